@@ -1,0 +1,95 @@
+"""Seeded synthetic inputs for the mHC forward.
+
+This module only draws random numbers and casts them; it holds none of the
+method's arithmetic.  Both the HIP path (through its Python binding) and the
+CPU oracle are fed from the same tensors it returns, so both sides see the
+identical bf16 bytes.
+
+Workloads (shapes follow the dimensions defined in [mHC-cutile] section 2:
+B rows = batch x sequence, n streams, hidden size C; page [mHC-cutile] is
+"mHC 算法分析 & cutile 高效实现"):
+
+  name      n  C     B      X distribution
+  tiny      4  256   64     N(0, 1)
+  prefill   4  4096  4096   N(0, 1)            (batch 1 x sequence 4096)
+  decode    4  7168  64     N(0, 1)
+  large     4  7168  16384  Student-t, 4 dof   (rows carry outliers)
+  wide      8  4096  8192   N(0, 1)
+
+For every workload: phi ~ N(0, sigma = 1/sqrt(nC)) so logits are O(1);
+alpha_pre = alpha_post = alpha_res = 0.01; b_pre, b_post ~ N(0, sigma = 0.1);
+b_res = 2 * I_n (flattened row-major) + N(0, sigma = 0.1); F_out ~ N(0, 1).
+X, phi and F_out are drawn in fp32 and rounded to bf16 (round-to-nearest-even);
+biases stay fp32.  The Student-t(4) draw is z / sqrt(chi2_4 / 4) with chi2_4 the
+sum of four squared standard normals.
+"""
+
+import math
+
+import numpy as np
+import torch
+
+CONFIGS = {
+    "tiny": dict(n=4, C=256, B=64, x_dist="normal", seed=1000),
+    "prefill": dict(n=4, C=4096, B=4096, x_dist="normal", seed=1001),
+    "decode": dict(n=4, C=7168, B=64, x_dist="normal", seed=1002),
+    "large": dict(n=4, C=7168, B=16384, x_dist="student_t4", seed=1003),
+    "wide": dict(n=8, C=4096, B=8192, x_dist="normal", seed=1004),
+}
+
+ALPHA = 0.01
+
+
+def _draw_rows(gen, rows, cols, dist, device):
+    z = torch.randn(rows, cols, generator=gen, device=device, dtype=torch.float32)
+    if dist == "normal":
+        return z
+    if dist == "student_t4":
+        chi2 = torch.zeros_like(z)
+        for _ in range(4):
+            w = torch.randn(rows, cols, generator=gen, device=device, dtype=torch.float32)
+            chi2.addcmul_(w, w)
+        return z / torch.sqrt(chi2 / 4.0)
+    raise ValueError(f"unknown distribution {dist!r}")
+
+
+def make_inputs(n, C, B, x_dist="normal", seed=0, device="cpu", row_chunk=512):
+    """Draw one seeded input set.  Returns a dict of torch tensors on `device`
+    (X bf16 [B, nC], phi bf16 [nC, N], F_out bf16 [B, C], b_pre/b_post fp32 [n],
+    b_res fp32 [n*n]) plus the python floats alpha_pre/post/res and the sizes."""
+    device = torch.device(device)
+    K = n * C
+    N = n * n + 2 * n
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    X = torch.empty(B, K, dtype=torch.bfloat16, device=device)
+    for lo in range(0, B, row_chunk):
+        hi = min(B, lo + row_chunk)
+        X[lo:hi] = _draw_rows(gen, hi - lo, K, x_dist, device).to(torch.bfloat16)
+    phi = (torch.randn(K, N, generator=gen, device=device) / math.sqrt(K)).to(torch.bfloat16)
+    b_pre = 0.1 * torch.randn(n, generator=gen, device=device)
+    b_post = 0.1 * torch.randn(n, generator=gen, device=device)
+    b_res = (2.0 * torch.eye(n, device=device).reshape(-1)
+             + 0.1 * torch.randn(n * n, generator=gen, device=device))
+    F_out = torch.empty(B, C, dtype=torch.bfloat16, device=device)
+    for lo in range(0, B, row_chunk * 4):
+        hi = min(B, lo + row_chunk * 4)
+        F_out[lo:hi] = torch.randn(hi - lo, C, generator=gen, device=device).to(torch.bfloat16)
+    return {
+        "n": n, "C": C, "B": B, "seed": int(seed), "x_dist": x_dist,
+        "X": X, "phi": phi, "F_out": F_out,
+        "b_pre": b_pre.float().contiguous(), "b_post": b_post.float().contiguous(),
+        "b_res": b_res.float().contiguous(),
+        "alpha_pre": ALPHA, "alpha_post": ALPHA, "alpha_res": ALPHA,
+    }
+
+
+def make_config(name, device="cpu"):
+    """Inputs for one named workload of CONFIGS."""
+    cfg = CONFIGS[name]
+    return make_inputs(cfg["n"], cfg["C"], cfg["B"], cfg["x_dist"], cfg["seed"], device)
+
+
+def bf16_bits(t):
+    """Raw bf16 bit patterns of a bf16 tensor as a numpy uint16 array (host copy)."""
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
