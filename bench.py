@@ -1,0 +1,267 @@
+"""Benchmark of the mHC residual-stream forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload large]
+
+One step = one pass of the whole forward (mhc_coeffs, mhc_pre, mhc_post_res)
+over one batch of synthetic input already resident in HBM.  Prints ONE JSON
+line with tokens/s, per-call times, achieved HBM bandwidth against the
+algorithmic byte count, the roofline of the dominant kernel and the fp64
+oracle's throughput on the host as a CPU baseline.
+
+Algorithmic bytes per forward (bf16 X_t, F_out, F_pre, X_next; fp32 coefficients):
+  mhc_coeffs    X_t + phi + biases + logits + r + H
+  mhc_pre       X_t + H_pre + F_pre
+  mhc_post_res  2 X_t + F_out + (H_post, H_res)
+The split-K workspace is implementation traffic and is not counted.
+
+Other modes:
+  --copy-probe   time a plain device-to-device copy of known size (the
+                 reference against which rocprofv3 FETCH_SIZE / WRITE_SIZE are
+                 scaled);
+  --kernel-only  run only the timed forward loop (for rocprofv3 runs).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "mHC fwd tokens/sec + achieved HBM GB/s (% of peak), n=4 C=7168 B=16384"
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+DEFAULT_WORKLOAD = "large"
+
+
+def path_bytes(B, n, C):
+    """Algorithmic bytes moved by each of the three calls for one forward."""
+    N = n * n + 2 * n
+    K = n * C
+    x = B * K * 2
+    return {
+        "mhc_coeffs": x + K * N * 2 + N * 4 + B * N * 4 + B * 4 + B * N * 4,
+        "mhc_pre": x + B * n * 4 + B * C * 2,
+        "mhc_post_res": 2 * x + B * C * 2 + B * (n + n * n) * 4,
+    }
+
+
+def path_flops(B, n, C):
+    """Algorithmic flops of one forward (product, sum of squares, pre, post/res)."""
+    N = n * n + 2 * n
+    K = n * C
+    return B * (2 * K * N + 2 * K + 2 * K + 2 * (n * n + n) * C)
+
+
+# dominant-kernel bookkeeping: kernel symbol substring -> call it belongs to
+KERNEL_OF_CALL = {"mhc_post_res": "post_res_kernel", "mhc_pre": "pre_kernel",
+                  "mhc_coeffs": "gemm_rms_kernel"}
+
+
+def _kernel_source_sha():
+    csrc = os.path.join(ROOT, "manifold_constrained_hyper_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def _recorded_traffic(call, workload):
+    """HBM bytes per launch measured by rocprofv3 counters, from the committed
+    summary in profiles/, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{call}_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    sha = re.search(r"kernel_source_sha:\s*([0-9a-f]+)", text)
+    val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not sha or not val or sha.group(1) != _kernel_source_sha():
+        return None
+    return float(val.group(1))
+
+
+def _cpu_baseline(inp, rows_wanted, budget_s):
+    """Time the fp64 oracle (as it stands) on the first rows of the workload."""
+    import numpy as np
+    import oracle
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        blas_threads = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        blas_threads = 1
+    n, C = inp["n"], inp["C"]
+    rows = min(rows_wanted, inp["B"])
+    # exact widening bf16 -> fp32 on the device side copy; the oracle widens to fp64
+    x = inp["X"][:rows].float().cpu().numpy()
+    f = inp["F_out"][:rows].float().cpu().numpy()
+    phi = inp["phi"].float().cpu().numpy()
+    bp, bq, br = (inp[k].double().cpu().numpy() for k in ("b_pre", "b_post", "b_res"))
+    done = 0
+    t0 = time.perf_counter()
+    while done < rows:
+        step = min(256, rows - done)
+        oracle.forward(x[done:done + step], phi, inp["alpha_pre"], inp["alpha_post"],
+                       inp["alpha_res"], bp, bq, br, f[done:done + step], n, C)
+        done += step
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": done / dt, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"first {done} of {inp['B']} rows of the same workload, fp64 numpy oracle, "
+                      f"{dt:.1f} s wall; BLAS threads={blas_threads} (elementwise numpy is "
+                      f"single-threaded); host cores visible={len(os.sched_getaffinity(0))}; "
+                      f"cpu={cpu_model}"}
+
+
+def copy_probe(args):
+    import torch
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    print(json.dumps({"copy_probe_bytes_read": nbytes, "copy_probe_bytes_written": nbytes,
+                      "launches": args.steps + args.warmup, "ms_per_copy": ms,
+                      "gbps_read_plus_write": 2 * nbytes / ms / 1e6}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-rows", type=int, default=4096)
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--kernel-only", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the mHC forward shards by rows (tokens) with no "
+              "exchange between GPUs, so a multi-GPU figure would be N independent copies of this "
+              "one; run with --gpus 1.", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    import manifold_constrained_hyper_amd as mhc
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_probe:
+        copy_probe(args)
+        return
+
+    mhc.load()  # raises if the HIP library is not built
+    cfg = synth.CONFIGS[args.workload]
+    inp = synth.make_config(args.workload, device="cuda")
+    B, n, C = inp["B"], inp["n"], inp["C"]
+    out = mhc.alloc_outputs(B, n, C)
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    calls = ("mhc_coeffs", "mhc_pre", "mhc_post_res")
+
+    def step(marks=None):
+        if marks is not None:
+            marks[0].record(stream)
+        mhc.mhc_coeffs(B, n, C, inp["X"], inp["phi"], inp["alpha_pre"], inp["alpha_post"],
+                       inp["alpha_res"], inp["b_pre"], inp["b_post"], inp["b_res"],
+                       out["logits"], out["r"], out["H"], out["workspace"], stream=stream)
+        if marks is not None:
+            marks[1].record(stream)
+        mhc.mhc_pre(B, n, C, inp["X"], out["H"], out["F_pre"], stream=stream)
+        if marks is not None:
+            marks[2].record(stream)
+        mhc.mhc_post_res(B, n, C, inp["X"], inp["F_out"], out["H"], out["X_next"], stream=stream)
+        if marks is not None:
+            marks[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    marks = [[ev() for _ in range(4)] for _ in range(args.steps)]
+    t_start, t_end = ev(), ev()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for k in range(args.steps):
+        step(marks[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    if args.kernel_only:
+        print(json.dumps({"kernel_only": True, "steps": args.steps}), flush=True)
+        return
+
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    per_call_ms = {c: sum(marks[k][i].elapsed_time(marks[k][i + 1]) for k in range(args.steps)) / args.steps
+                   for i, c in enumerate(calls)}
+    bytes_call = path_bytes(B, n, C)
+    total_bytes = sum(bytes_call.values())
+    gbps = total_bytes / (ms_step * 1e-3) / 1e9
+    tokens_per_s = B / (ms_step * 1e-3)
+
+    dom = max(calls, key=lambda c: per_call_ms[c])
+    dom_gbps = bytes_call[dom] / (per_call_ms[dom] * 1e-3) / 1e9
+    traffic = _recorded_traffic(dom, args.workload)
+    roofline = {"bound": "hbm", "kernel": KERNEL_OF_CALL[dom], "call": dom,
+                "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "algorithmic_bytes_per_launch": bytes_call[dom],
+                "avg_launch_us": round(per_call_ms[dom] * 1e3, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = _cpu_baseline(inp, args.cpu_rows, args.cpu_budget_s)
+
+    line = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; X Student-t(4) for the large workload)",
+        "config": {"workload": f"{args.workload}: n={n} C={C} B={B}", "n": n, "C": C, "B": B,
+                   "x_dist": cfg["x_dist"], "seed": cfg["seed"],
+                   "split_k": mhc.mhc_coeffs_split_k(B, n, C)},
+        "hbm_gbps": round(gbps, 1), "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_step": total_bytes,
+        "per_call_us": {c: round(v * 1e3, 2) for c, v in per_call_ms.items()},
+        "per_call_gbps": {c: round(bytes_call[c] / (per_call_ms[c] * 1e-3) / 1e9, 1) for c in calls},
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernel_source_sha": _kernel_source_sha(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

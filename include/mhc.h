@@ -1,0 +1,141 @@
+/*
+ * mhc.h -- C ABI of libmhc: the mHC (manifold-constrained hyper-connections)
+ * residual-stream forward on one AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one stated in section 2 of the blog page
+ * "mHC 算法分析 & cutile 高效实现" (edward-lyz, 2026-02-10), cited below as
+ * [mHC-cutile].  Three calls cover the forward of one mHC layer:
+ *
+ *   mhc_coeffs    steps (1)-(3): logits = X_t . phi and r = RMS(X_t) in one
+ *                 pass over X_t, then the alpha/r + bias correction, the
+ *                 sigmoid / 2*sigmoid gates and 20 Sinkhorn-Knopp iterations;
+ *   mhc_pre       step (4a): F_pre = sum_i H_pre[i] X_t[i]   (n streams -> 1);
+ *   mhc_post_res  step (4b): X_next[i] = sum_j H_res[i,j] X_t[j] + H_post[i] F_out.
+ *
+ * Between mhc_pre and mhc_post_res the caller runs its own layer F
+ * (attention / FFN) to turn F_pre into F_out; that layer is not part of mHC.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  B   number of rows (tokens = batch x sequence), B >= 0;
+ *  n   expansion rate (number of residual streams), one of 1, 2, 4, 8;
+ *  C   hidden size, C >= 8 and C % 8 == 0;
+ *  N   = n*n + 2n coefficients per row, K = n*C.
+ *
+ *  bf16 tensors are raw bfloat16 bit patterns (uint16), row-major.  X_t is
+ *  [B, n*C] stream-major: stream j occupies columns [j*C, (j+1)*C) of a row
+ *  ([mHC-cutile] sections 2 and 5.4).  A coefficient row is laid out
+ *  [pre (n) | post (n) | res (n*n, row-major (i, j))], the column order of the
+ *  single product in [mHC-cutile] section 2.1.
+ *
+ *  All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *  allocates and frees nothing and keeps no pointer after a call returns.
+ *  bf16 tensors and the workspace must be 16-byte aligned; fp32 tensors
+ *  4-byte aligned.  `stream` is a hipStream_t (NULL = the null stream).
+ *
+ *  Every call only enqueues work on `stream` and returns; it never
+ *  synchronises the host or the device.  Inputs must stay valid until the
+ *  stream has passed the call.  Calls are stateless and thread-safe.
+ *
+ *  Errors: every call returns an mhc_status value and never aborts, throws or
+ *  prints.  Arguments are checked on the host before anything is launched:
+ *    - a required pointer is NULL, B < 0, n < 1 or C < 1     -> MHC_ERR_INVALID_ARG
+ *    - an output overlaps an input or another output        -> MHC_ERR_INVALID_ARG
+ *    - n not in {1,2,4,8}, C % 8 != 0, misaligned pointer   -> MHC_ERR_UNSUPPORTED
+ *    - workspace smaller than mhc_coeffs_workspace_size()    -> MHC_ERR_WORKSPACE
+ *    - the HIP runtime reports a launch error                -> MHC_ERR_HIP
+ *  B == 0 is valid and launches nothing.  Faults during asynchronous
+ *  execution surface at the caller's next synchronisation, as in HIP.
+ */
+#ifndef MHC_H
+#define MHC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Sinkhorn-Knopp (row, column) normalisation pairs: [mHC-cutile] section 2.4
+ * gives about 20; its kernels in sections 4.3 and 5.3 fix exactly 20. */
+#define MHC_SINKHORN_ITERS 20
+
+enum mhc_status {
+  MHC_OK = 0,
+  MHC_ERR_INVALID_ARG = 1,
+  MHC_ERR_UNSUPPORTED = 2,
+  MHC_ERR_WORKSPACE = 3,
+  MHC_ERR_HIP = 4
+};
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *mhc_status_string(int status);
+
+/* Bytes of device workspace mhc_coeffs needs for (B, n, C): the split-K
+ * partial sums, fp32 [S, B, N+1].  Returns 0 for B == 0 or for arguments
+ * mhc_coeffs would reject.  Pure host function. */
+size_t mhc_coeffs_workspace_size(int64_t B, int32_t n, int64_t C);
+
+/* Number S of K-slices mhc_coeffs splits the reduction over K = n*C into for
+ * (B, n, C); 0 for arguments mhc_coeffs would reject.  Pure host function,
+ * for introspection. */
+int32_t mhc_coeffs_split_k(int64_t B, int32_t n, int64_t C);
+
+/* Steps (1)-(3) of the forward.
+ *
+ * [mHC-cutile] section 2.1: logits = X_t . phi (one product for all N
+ * columns); section 2.2: r = sqrt(sum(X_t^2) / (n C)) per row, no epsilon;
+ * section 2.3: h = alpha_x * logit / r + b_x; section 2.4: H_pre = sigmoid(h),
+ * H_post = 2 sigmoid(h), H_res = Sinkhorn-Knopp(exp(h)) with 20 row-then-
+ * column normalisations.  [mHC-cutile] sections 3.1 and 5.1-5.3 motivate the
+ * fusion: one pass over X_t gives both the product and the sum of squares
+ * (applying 1/r after the product is the row-scaling identity of section 2 of
+ * "Towards Free Normalization: Fusing Normalization into GEMM and Attention
+ * Kernels").
+ *
+ *   X_t       in  bf16 [B, n*C]
+ *   phi       in  bf16 [n*C, N], row-major
+ *   alpha_*   in  host fp32 scalars
+ *   b_pre     in  fp32 [n];  b_post in fp32 [n];  b_res in fp32 [n*n] row-major
+ *   logits    out fp32 [B, N]  raw X_t . phi
+ *   r         out fp32 [B]
+ *   H         out fp32 [B, N]  [H_pre | H_post | H_res]
+ *   workspace scratch, >= mhc_coeffs_workspace_size(B, n, C) bytes; its
+ *             contents on entry are ignored and on exit undefined.
+ *
+ * The result is deterministic: the split-K partials are combined in a fixed
+ * order, without atomics. */
+int mhc_coeffs(int64_t B, int32_t n, int64_t C,
+               const void *X_t, const void *phi,
+               float alpha_pre, float alpha_post, float alpha_res,
+               const float *b_pre, const float *b_post, const float *b_res,
+               float *logits, float *r, float *H,
+               void *workspace, size_t workspace_bytes, void *stream);
+
+/* Step (4a), [mHC-cutile] section 2.5: F_pre[b, c] = sum_i H_pre[b, i] *
+ * X_t[b, i*C + c], accumulated in fp32 and rounded to bf16 (nearest even).
+ *
+ *   X_t    in  bf16 [B, n*C]
+ *   H      in  fp32 [B, N] (only the pre block is read)
+ *   F_pre  out bf16 [B, C] */
+int mhc_pre(int64_t B, int32_t n, int64_t C, const void *X_t, const float *H,
+            void *F_pre, void *stream);
+
+/* Step (4b), [mHC-cutile] sections 2.5 and 3.4: X_next[b, i*C + c] =
+ * sum_j H_res[b, i, j] * X_t[b, j*C + c] + H_post[b, i] * F_out[b, c],
+ * accumulated in fp32 and rounded to bf16 (nearest even).  X_t is read once
+ * and X_next written once.
+ *
+ *   X_t     in  bf16 [B, n*C]
+ *   F_out   in  bf16 [B, C]
+ *   H       in  fp32 [B, N] (the post and res blocks are read)
+ *   X_next  out bf16 [B, n*C]; must not overlap X_t */
+int mhc_post_res(int64_t B, int32_t n, int64_t C, const void *X_t,
+                 const void *F_out, const float *H, void *X_next, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHC_H */

@@ -1,0 +1,140 @@
+// C ABI of libmhc (declared in include/mhc.h): host-side argument checks,
+// then the kernel launches.  Nothing here allocates, synchronises or prints.
+#include "mhc.h"
+#include "mhc_launch.h"
+
+#include <stdint.h>
+
+namespace {
+
+// Largest problem accepted: B*n*C elements below 2^40 and K = n*C below 2^30
+// keep every byte offset and every 32-bit kernel index in range.
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+constexpr int64_t kMaxK = int64_t(1) << 30;
+constexpr int64_t kMaxB = (int64_t(1) << 31) - 1;
+
+struct Span {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Span span(const void *p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Span{a, a + bytes};
+}
+
+bool overlaps(Span a, Span b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool supported_n(int32_t n) { return n == 1 || n == 2 || n == 4 || n == 8; }
+
+// Shape checks common to every call.  Returns MHC_OK when the shape is
+// acceptable (B may be 0).
+int check_shape(int64_t B, int32_t n, int64_t C) {
+  if (B < 0 || n < 1 || C < 1) return MHC_ERR_INVALID_ARG;
+  if (!supported_n(n) || C % 8 != 0) return MHC_ERR_UNSUPPORTED;
+  if (B > kMaxB || (int64_t)n * C > kMaxK || (B > 0 && B > kMaxElems / ((int64_t)n * C)))
+    return MHC_ERR_UNSUPPORTED;
+  return MHC_OK;
+}
+
+int64_t ncoef(int32_t n) { return (int64_t)n * n + 2 * (int64_t)n; }
+
+int from_hip(hipError_t e) { return e == hipSuccess ? MHC_OK : MHC_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *mhc_status_string(int status) {
+  switch (status) {
+    case MHC_OK: return "MHC_OK";
+    case MHC_ERR_INVALID_ARG: return "MHC_ERR_INVALID_ARG: null pointer, negative size or overlapping buffers";
+    case MHC_ERR_UNSUPPORTED: return "MHC_ERR_UNSUPPORTED: n not in {1,2,4,8}, C % 8 != 0, size too large or misaligned pointer";
+    case MHC_ERR_WORKSPACE: return "MHC_ERR_WORKSPACE: workspace smaller than mhc_coeffs_workspace_size()";
+    case MHC_ERR_HIP: return "MHC_ERR_HIP: the HIP runtime reported an error";
+    default: return "MHC_ERR_UNKNOWN";
+  }
+}
+
+size_t mhc_coeffs_workspace_size(int64_t B, int32_t n, int64_t C) {
+  if (check_shape(B, n, C) != MHC_OK || B == 0) return 0;
+  return mhc::gemm_workspace_bytes(mhc::plan_gemm(B, n, C), B, n);
+}
+
+int32_t mhc_coeffs_split_k(int64_t B, int32_t n, int64_t C) {
+  if (check_shape(B, n, C) != MHC_OK || B == 0) return 0;
+  return mhc::plan_gemm(B, n, C).split;
+}
+
+int mhc_coeffs(int64_t B, int32_t n, int64_t C, const void *X_t, const void *phi,
+               float alpha_pre, float alpha_post, float alpha_res, const float *b_pre,
+               const float *b_post, const float *b_res, float *logits, float *r, float *H,
+               void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_shape(B, n, C);
+  if (st != MHC_OK) return st;
+  if (B == 0) return MHC_OK;
+  if (!X_t || !phi || !b_pre || !b_post || !b_res || !logits || !r || !H || !workspace)
+    return MHC_ERR_INVALID_ARG;
+  if (!aligned(X_t, 16) || !aligned(phi, 16) || !aligned(workspace, 16) || !aligned(b_pre, 4) ||
+      !aligned(b_post, 4) || !aligned(b_res, 4) || !aligned(logits, 4) || !aligned(r, 4) ||
+      !aligned(H, 4))
+    return MHC_ERR_UNSUPPORTED;
+
+  const mhc::GemmPlan plan = mhc::plan_gemm(B, n, C);
+  const size_t ws_need = mhc::gemm_workspace_bytes(plan, B, n);
+  const int64_t N = ncoef(n), K = (int64_t)n * C;
+  const Span in[] = {span(X_t, (size_t)B * K * 2), span(phi, (size_t)K * N * 2),
+                     span(b_pre, (size_t)n * 4), span(b_post, (size_t)n * 4),
+                     span(b_res, (size_t)n * n * 4)};
+  const Span out[] = {span(logits, (size_t)B * N * 4), span(r, (size_t)B * 4),
+                      span(H, (size_t)B * N * 4), span(workspace, ws_need)};
+  for (const Span &o : out) {
+    for (const Span &i : in)
+      if (overlaps(o, i)) return MHC_ERR_INVALID_ARG;
+  }
+  for (int a = 0; a < 4; ++a)
+    for (int b = a + 1; b < 4; ++b)
+      if (overlaps(out[a], out[b])) return MHC_ERR_INVALID_ARG;
+  if (workspace_bytes < ws_need) return MHC_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float *ws = static_cast<float *>(workspace);
+  st = from_hip(mhc::launch_gemm_rms(plan, n, B, C, X_t, phi, ws, s));
+  if (st != MHC_OK) return st;
+  return from_hip(mhc::launch_coeff_sinkhorn(n, B, C, plan.split, ws, alpha_pre, alpha_post,
+                                             alpha_res, b_pre, b_post, b_res, logits, r, H, s));
+}
+
+int mhc_pre(int64_t B, int32_t n, int64_t C, const void *X_t, const float *H, void *F_pre,
+            void *stream) {
+  int st = check_shape(B, n, C);
+  if (st != MHC_OK) return st;
+  if (B == 0) return MHC_OK;
+  if (!X_t || !H || !F_pre) return MHC_ERR_INVALID_ARG;
+  if (!aligned(X_t, 16) || !aligned(F_pre, 16) || !aligned(H, 4)) return MHC_ERR_UNSUPPORTED;
+  const int64_t N = ncoef(n);
+  const Span o = span(F_pre, (size_t)B * C * 2);
+  if (overlaps(o, span(X_t, (size_t)B * n * C * 2)) || overlaps(o, span(H, (size_t)B * N * 4)))
+    return MHC_ERR_INVALID_ARG;
+  return from_hip(mhc::launch_pre(n, B, C, X_t, H, F_pre, static_cast<hipStream_t>(stream)));
+}
+
+int mhc_post_res(int64_t B, int32_t n, int64_t C, const void *X_t, const void *F_out,
+                 const float *H, void *X_next, void *stream) {
+  int st = check_shape(B, n, C);
+  if (st != MHC_OK) return st;
+  if (B == 0) return MHC_OK;
+  if (!X_t || !F_out || !H || !X_next) return MHC_ERR_INVALID_ARG;
+  if (!aligned(X_t, 16) || !aligned(F_out, 16) || !aligned(X_next, 16) || !aligned(H, 4))
+    return MHC_ERR_UNSUPPORTED;
+  const int64_t N = ncoef(n);
+  const Span o = span(X_next, (size_t)B * n * C * 2);
+  if (overlaps(o, span(X_t, (size_t)B * n * C * 2)) || overlaps(o, span(F_out, (size_t)B * C * 2)) ||
+      overlaps(o, span(H, (size_t)B * N * 4)))
+    return MHC_ERR_INVALID_ARG;
+  return from_hip(mhc::launch_post_res(n, B, C, X_t, F_out, H, X_next,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// Device-side helpers shared by the libmhc kernels (gfx950 / CDNA4).
+//
+// bf16 values travel as raw 16-bit patterns packed two per 32-bit word
+// (element 2i in the low half, 2i+1 in the high half, little endian), eight
+// per 16-byte vector.  Widening bf16 -> fp32 is exact (a 16-bit shift);
+// narrowing fp32 -> bf16 uses the hardware round-to-nearest-even conversion
+// (v_cvt_pk_bf16_f32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mhc {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 -> one word of two bf16 (round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// 16-byte global load / store.  Streaming data is touched once, so stores
+// carry the non-temporal hint.
+__device__ __forceinline__ u32x4 load16(const void *p) {
+  return *reinterpret_cast<const u32x4 *>(p);
+}
+__device__ __forceinline__ void store16_nt(void *p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+}
+
+// Wave-uniform value (lets the compiler keep row-derived addresses in SGPRs
+// and read per-row coefficients with scalar loads).
+__device__ __forceinline__ int64_t uniform(int64_t v) {
+  uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+  uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+}  // namespace mhc

@@ -1,0 +1,37 @@
+// Host-side launch interface between the C-ABI layer (mhc_abi.hip) and the
+// kernel translation units.  Arguments are validated by the caller; these
+// functions only pick launch shapes and enqueue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mhc {
+
+// Split-K plan of the fused product + sum-of-squares pass.
+struct GemmPlan {
+  int mb;             // 16-row MFMA blocks per wavefront (rows per workgroup = 64 * mb)
+  int kc;             // K elements staged per LDS chunk
+  int split;          // S: number of K-slices (partials in the workspace)
+  int64_t kslice;     // K elements per slice (multiple of kc)
+  int64_t row_tiles;  // workgroups along B
+};
+
+GemmPlan plan_gemm(int64_t B, int n, int64_t C);
+size_t gemm_workspace_bytes(const GemmPlan &p, int64_t B, int n);
+
+hipError_t launch_gemm_rms(const GemmPlan &p, int n, int64_t B, int64_t C,
+                           const void *X, const void *phi, float *ws, hipStream_t st);
+
+hipError_t launch_coeff_sinkhorn(int n, int64_t B, int64_t C, int split, const float *ws,
+                                 float alpha_pre, float alpha_post, float alpha_res,
+                                 const float *b_pre, const float *b_post, const float *b_res,
+                                 float *logits, float *r, float *H, hipStream_t st);
+
+hipError_t launch_pre(int n, int64_t B, int64_t C, const void *X, const float *H,
+                      void *F_pre, hipStream_t st);
+
+hipError_t launch_post_res(int n, int64_t B, int64_t C, const void *X, const void *F_out,
+                           const float *H, void *X_next, hipStream_t st);
+
+}  // namespace mhc

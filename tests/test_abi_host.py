@@ -1,0 +1,112 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+include/mhc.h declares, and rejects bad arguments before launching anything.
+
+No call here reaches a kernel launch: every call either fails validation or
+has B == 0, so these run without a GPU.  Pointers are fake addresses; the
+library never dereferences them on the host.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import manifold_constrained_hyper_amd as mhc
+
+pytestmark = pytest.mark.cpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mhc.h")
+
+A = 0x10000000  # fake, 16-byte aligned device addresses, far apart
+STEP = 0x10000000
+
+
+def _addrs(k):
+    return [A + i * STEP for i in range(k)]
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mhc_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert _declared_functions() == sorted(mhc.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(mhc.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), f"libmhc.so does not export {name}"
+
+
+def test_status_strings():
+    for code in range(5):
+        assert mhc.mhc_status_string(code).startswith("MHC_")
+    assert mhc.mhc_status_string(99) == "MHC_ERR_UNKNOWN"
+
+
+def test_workspace_and_split_host_functions():
+    for (B, n, C) in ((64, 4, 256), (4096, 4, 4096), (64, 4, 7168), (16384, 4, 7168),
+                      (8192, 8, 4096), (77, 1, 24), (5, 2, 8)):
+        S = mhc.mhc_coeffs_split_k(B, n, C)
+        N = n * n + 2 * n
+        assert 1 <= S <= max(1, (n * C + 127) // 128)
+        assert mhc.mhc_coeffs_workspace_size(B, n, C) == S * B * (N + 1) * 4
+    assert mhc.mhc_coeffs_workspace_size(0, 4, 256) == 0
+    assert mhc.mhc_coeffs_workspace_size(10, 3, 256) == 0
+    assert mhc.mhc_coeffs_split_k(10, 4, 12) == 0
+
+
+def _coeffs(B=16, n=4, C=64, ptrs=None, ws_bytes=None, **over):
+    p = dict(zip(["X", "phi", "bp", "bq", "br", "logits", "r", "H", "ws"], ptrs or _addrs(9)))
+    p.update(over)
+    if ws_bytes is None:
+        ws_bytes = max(mhc.mhc_coeffs_workspace_size(B, n, C), 16)
+    return mhc.mhc_coeffs(B, n, C, p["X"], p["phi"], 0.01, 0.01, 0.01, p["bp"], p["bq"], p["br"],
+                          p["logits"], p["r"], p["H"], p["ws"], ws_bytes, stream=0, check=False)
+
+
+def test_coeffs_validation():
+    assert _coeffs(B=0) == mhc.MHC_OK                                   # empty: nothing launched
+    assert _coeffs(B=0, X=None, H=None, ws=None) == mhc.MHC_OK          # pointers not inspected at B == 0
+    assert _coeffs(B=-1) == mhc.MHC_ERR_INVALID_ARG
+    assert _coeffs(n=0) == mhc.MHC_ERR_INVALID_ARG
+    assert _coeffs(C=0) == mhc.MHC_ERR_INVALID_ARG
+    assert _coeffs(n=3) == mhc.MHC_ERR_UNSUPPORTED
+    assert _coeffs(C=12) == mhc.MHC_ERR_UNSUPPORTED
+    for k in ("X", "phi", "bp", "bq", "br", "logits", "r", "H", "ws"):
+        assert _coeffs(**{k: None}) == mhc.MHC_ERR_INVALID_ARG, k
+    assert _coeffs(X=A + 8) == mhc.MHC_ERR_UNSUPPORTED                  # bf16 needs 16-byte alignment
+    assert _coeffs(ws=A + 8 * STEP + 4) == mhc.MHC_ERR_UNSUPPORTED
+    assert _coeffs(H=A + 7 * STEP + 2) == mhc.MHC_ERR_UNSUPPORTED       # fp32 needs 4-byte alignment
+    assert _coeffs(H=A) == mhc.MHC_ERR_INVALID_ARG                      # output overlaps X
+    assert _coeffs(r=A + 5 * STEP + 64) == mhc.MHC_ERR_INVALID_ARG      # r inside logits
+    assert _coeffs(ws=A + 7 * STEP) == mhc.MHC_ERR_INVALID_ARG          # workspace overlaps H
+    need = mhc.mhc_coeffs_workspace_size(16, 4, 64)
+    assert _coeffs(ws_bytes=need - 1) == mhc.MHC_ERR_WORKSPACE
+
+
+def test_pre_and_post_res_validation():
+    X, H, F, Y = _addrs(4)
+    ok_shape = (16, 4, 64)
+    assert mhc.mhc_pre(0, 4, 64, None, None, None, stream=0, check=False) == mhc.MHC_OK
+    assert mhc.mhc_pre(*ok_shape, None, H, F, stream=0, check=False) == mhc.MHC_ERR_INVALID_ARG
+    assert mhc.mhc_pre(16, 5, 64, X, H, F, stream=0, check=False) == mhc.MHC_ERR_UNSUPPORTED
+    assert mhc.mhc_pre(*ok_shape, X, H, F + 2, stream=0, check=False) == mhc.MHC_ERR_UNSUPPORTED
+    assert mhc.mhc_pre(*ok_shape, X, H, X + 256, stream=0, check=False) == mhc.MHC_ERR_INVALID_ARG
+    assert mhc.mhc_post_res(0, 4, 64, None, None, None, None, stream=0, check=False) == mhc.MHC_OK
+    assert mhc.mhc_post_res(*ok_shape, X, F, H, None, stream=0, check=False) == mhc.MHC_ERR_INVALID_ARG
+    assert mhc.mhc_post_res(*ok_shape, X, F, H, X, stream=0, check=False) == mhc.MHC_ERR_INVALID_ARG
+    assert mhc.mhc_post_res(*ok_shape, X, F, H, F + 16, stream=0, check=False) == mhc.MHC_ERR_INVALID_ARG
+    assert mhc.mhc_post_res(16, 4, 60, X, F, H, Y, stream=0, check=False) == mhc.MHC_ERR_UNSUPPORTED
+    assert mhc.mhc_post_res(-3, 4, 64, X, F, H, Y, stream=0, check=False) == mhc.MHC_ERR_INVALID_ARG
+
+
+def test_binding_raises_on_error_status():
+    with pytest.raises(mhc.MhcError) as ei:
+        mhc.mhc_pre(16, 3, 64, *_addrs(3), stream=0)
+    assert ei.value.status == mhc.MHC_ERR_UNSUPPORTED
