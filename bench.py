@@ -62,10 +62,19 @@ KERNEL_OF_CALL = {"mhc_post_res": "post_res_kernel", "mhc_pre": "pre_kernel",
                   "mhc_coeffs": "gemm_rms_kernel"}
 
 
-def _kernel_source_sha():
+# source files that make up each call's kernels (for the counter-freshness check)
+CALL_SOURCES = {
+    "mhc_coeffs": ("mhc_gemm_rms.hip", "mhc_coeff_sinkhorn.hip", "mhc_device.h"),
+    "mhc_pre": ("mhc_stream.hip", "mhc_device.h"),
+    "mhc_post_res": ("mhc_stream.hip", "mhc_device.h"),
+}
+
+
+def kernel_source_sha(call):
+    """Short hash of the sources of one call's kernels."""
     csrc = os.path.join(ROOT, "manifold_constrained_hyper_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(csrc)):
+    for f in CALL_SOURCES[call]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
@@ -80,7 +89,7 @@ def _recorded_traffic(call, workload):
     text = open(path).read()
     sha = re.search(r"kernel_source_sha:\s*([0-9a-f]+)", text)
     val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not sha or not val or sha.group(1) != _kernel_source_sha():
+    if not sha or not val or sha.group(1) != kernel_source_sha(call):
         return None
     return float(val.group(1))
 
@@ -154,8 +163,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--cpu-rows", type=int, default=4096)
-    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--cpu-rows", type=int, default=16384)
+    ap.add_argument("--cpu-budget-s", type=float, default=30.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--kernel-only", action="store_true")
@@ -258,7 +267,7 @@ def main():
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "kernel_source_sha": _kernel_source_sha(),
+        "kernel_source_sha": {c: kernel_source_sha(c) for c in calls},
     }
     print(json.dumps(line), flush=True)
 

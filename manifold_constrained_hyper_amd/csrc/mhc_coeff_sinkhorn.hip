@@ -47,8 +47,17 @@ __global__ __launch_bounds__(256) void coeff_sinkhorn_kernel(
     const size_t slice = (size_t)B * NP;
     const float *base = ws + (size_t)row0 * NP;
     for (int e = tid; e < rows * NP; e += 256) {
+      // batches of 8 independent loads, added in slice order
       float a = 0.f;
-      for (int s = 0; s < split; ++s) a += base[(size_t)s * slice + e];
+      int s = 0;
+      for (; s + 8 <= split; s += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = base[(size_t)(s + u) * slice + e];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) a += v[u];
+      }
+      for (; s < split; ++s) a += base[(size_t)s * slice + e];
       sums[e] = a;
       const int rr = e / NP, cc = e - rr * NP;
       if (cc < N) logits[(size_t)(row0 + rr) * N + cc] = a;

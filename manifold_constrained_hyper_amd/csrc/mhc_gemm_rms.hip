@@ -17,7 +17,11 @@
 //  * phi does not fit in LDS (1.4 MB at n=4, C=7168), so it is staged per K
 //    chunk, transposed to n-major / k-contiguous, so a lane's B operand
 //    (8 consecutive k of one column) is a single 16-byte LDS read.  All four
-//    wavefronts of a workgroup share one staged chunk.
+//    wavefronts of a workgroup share one staged chunk.  The chunk's phi loads
+//    are issued before its X loads, so waiting for phi never waits for X.
+//  * With PIPE, the X (and phi) loads of chunk i+1 are issued before the
+//    MFMAs of chunk i, so each wave keeps requests in flight while it
+//    computes (two register buffers).
 //  * The sum of squares rides on the matrix core too: the product of the A
 //    operand with itself (the same registers as the B operand) is the 16 x 16
 //    Gram block of the rows, whose diagonal is sum_k x^2 accumulated in fp32.
@@ -33,17 +37,115 @@ namespace mhc {
 namespace {
 
 template <int NS, int MB, int KC>
+struct GemmTile {
+  static constexpr int N = NS * NS + 2 * NS;
+  static constexpr int NP = N + 1;
+  static constexpr int NB = (N + 15) / 16;
+  static constexpr int LDK = KC + 8;                    // padded LDS row (elements)
+  static constexpr int T = KC / 32;                     // MFMA k-steps per chunk
+  static constexpr int PHI_VEC = (KC * N) / 8;          // 16-byte vectors of phi per chunk
+  static constexpr int PV = (PHI_VEC + 255) / 256;      // ... per thread
+  static_assert((KC * N) % 8 == 0, "chunk must be whole 16-byte vectors");
+};
+
+template <bool NTL>
+__device__ __forceinline__ u32x4 ldx(const uint16_t *p) {
+  return NTL ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p)) : load16(p);
+}
+
+// Loads of one K chunk: phi vectors (per thread) and the A operands of the wave.
+template <int NS, int MB, int KC, bool NTL, bool XFIRST = false>
+struct ChunkRegs {
+  using G = GemmTile<NS, MB, KC>;
+  u32x4 pw[G::PV];
+  bf16x8 xa[MB][G::T];
+
+  __device__ __forceinline__ void load_phi(const uint16_t *phi, int k0, int k_end, int tid) {
+    const int valid_vec = (min(KC, k_end - k0) * G::N) / 8;
+    const uint16_t *src = phi + (size_t)k0 * G::N;
+#pragma unroll
+    for (int p = 0; p < G::PV; ++p) {
+      const int v = tid + p * 256;
+      pw[p] = u32x4{0u, 0u, 0u, 0u};
+      if (v < valid_vec) pw[p] = load16(src + (size_t)v * 8);
+    }
+  }
+
+  __device__ __forceinline__ void load(const uint16_t *phi, const uint16_t *const *xrow, int k0,
+                                       int k_end, int tid, int g) {
+    if (!XFIRST) load_phi(phi, k0, k_end, tid);
+    load_x(xrow, k0, k_end, g);
+    if (XFIRST) load_phi(phi, k0, k_end, tid);
+  }
+
+  __device__ __forceinline__ void load_x(const uint16_t *const *xrow, int k0, int k_end, int g) {
+    if (k0 + KC <= k_end) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int t = 0; t < G::T; ++t)
+          xa[mb][t] = __builtin_bit_cast(bf16x8, ldx<NTL>(xrow[mb] + k0 + 32 * t + 8 * g));
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int t = 0; t < G::T; ++t) {
+          const int k = k0 + 32 * t + 8 * g;
+          u32x4 w = {0u, 0u, 0u, 0u};
+          if (k < k_end) w = ldx<NTL>(xrow[mb] + k);
+          xa[mb][t] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
+  }
+
+  // Transposed store of the phi chunk: element (kk, nn) -> phiT[nn][kk].
+  __device__ __forceinline__ void stage(uint16_t *phiT, int tid) const {
+#pragma unroll
+    for (int p = 0; p < G::PV; ++p) {
+      const int v = tid + p * 256;
+      if (v < G::PHI_VEC) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int e = v * 8 + q;
+          const int kk = e / G::N, nn = e - kk * G::N;
+          const uint32_t word = pw[p][q >> 1];
+          phiT[nn * G::LDK + kk] = (uint16_t)((q & 1) ? (word >> 16) : (word & 0xffffu));
+        }
+      }
+    }
+  }
+};
+
+template <int NS, int MB, int KC, bool NTL, bool XFIRST>
+__device__ __forceinline__ void chunk_mfma(const ChunkRegs<NS, MB, KC, NTL, XFIRST> &c,
+                                           const uint16_t *phiT, int m, int g,
+                                           f32x4 (&acc)[MB][GemmTile<NS, MB, KC>::NB],
+                                           f32x4 (&gram)[MB]) {
+  using G = GemmTile<NS, MB, KC>;
+#pragma unroll
+  for (int t = 0; t < G::T; ++t) {
+    bf16x8 b[G::NB];
+#pragma unroll
+    for (int nb = 0; nb < G::NB; ++nb)
+      b[nb] = *reinterpret_cast<const bf16x8 *>(&phiT[(nb * 16 + m) * G::LDK + 32 * t + 8 * g]);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.xa[mb][t], b[nb], acc[mb][nb], 0, 0, 0);
+      gram[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.xa[mb][t], c.xa[mb][t], gram[mb], 0, 0, 0);
+    }
+  }
+}
+
+template <int NS, int MB, int KC, bool NTL, bool PIPE, bool XFIRST = false>
 __global__ __launch_bounds__(256) void gemm_rms_kernel(const uint16_t *__restrict__ X,
                                                        const uint16_t *__restrict__ phi,
                                                        float *__restrict__ ws, int B, int K,
                                                        int kslice) {
-  constexpr int N = NS * NS + 2 * NS;
-  constexpr int NP = N + 1;
-  constexpr int NB = (N + 15) / 16;
-  constexpr int LDK = KC + 8;  // padded LDS row, in elements (keeps 16-byte alignment)
-  constexpr int T = KC / 32;   // MFMA k-steps per chunk
-  static_assert((KC * N) % 8 == 0, "chunk must be whole 16-byte vectors");
-  __shared__ __attribute__((aligned(16))) uint16_t phiT[NB * 16 * LDK];
+  using G = GemmTile<NS, MB, KC>;
+  using Regs = ChunkRegs<NS, MB, KC, NTL, XFIRST>;
+  __shared__ __attribute__((aligned(16))) uint16_t phiT[G::NB * 16 * G::LDK];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -55,7 +157,7 @@ __global__ __launch_bounds__(256) void gemm_rms_kernel(const uint16_t *__restric
 
   // Columns N..NB*16 of the last block are padding; their outputs are never
   // stored, but keep them finite.
-  for (int e = tid; e < (NB * 16 - N) * LDK; e += 256) phiT[N * LDK + e] = 0;
+  for (int e = tid; e < (G::NB * 16 - G::N) * G::LDK; e += 256) phiT[G::N * G::LDK + e] = 0;
 
   const uint16_t *xrow[MB];
 #pragma unroll
@@ -64,115 +166,100 @@ __global__ __launch_bounds__(256) void gemm_rms_kernel(const uint16_t *__restric
     xrow[mb] = X + (size_t)r * K;
   }
 
-  f32x4 acc[MB][NB], gram[MB];
+  f32x4 acc[MB][G::NB], gram[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     gram[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < G::NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int k0 = k_begin; k0 < k_end; k0 += KC) {
-    // A operands of the whole chunk first, so the HBM requests are in flight
-    // while the workgroup stages phi.
-    bf16x8 xa[MB][T];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const int k = k0 + 32 * t + 8 * g;
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (k < k_end) w = load16(xrow[mb] + k);
-        xa[mb][t] = __builtin_bit_cast(bf16x8, w);
-      }
+  if constexpr (!PIPE) {
+    Regs c;
+    for (int k0 = k_begin; k0 < k_end; k0 += KC) {
+      c.load(phi, xrow, k0, k_end, tid, g);
+      __syncthreads();  // previous chunk's LDS reads are done
+      c.stage(phiT, tid);
+      __syncthreads();
+      chunk_mfma<NS, MB, KC, NTL, XFIRST>(c, phiT, m, g, acc, gram);
     }
-
-    __syncthreads();  // previous chunk's LDS reads are done
-    {
-      const int valid_vec = (min(KC, k_end - k0) * N) / 8;
-      const uint16_t *src = phi + (size_t)k0 * N;
-      for (int v = tid; v < (KC * N) / 8; v += 256) {
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (v < valid_vec) w = load16(src + (size_t)v * 8);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int e = v * 8 + q;
-          const int kk = e / N, nn = e - kk * N;
-          const uint32_t word = w[q >> 1];
-          phiT[nn * LDK + kk] = (uint16_t)((q & 1) ? (word >> 16) : (word & 0xffffu));
-        }
-      }
-    }
-    __syncthreads();
-
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      bf16x8 b[NB];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        b[nb] = *reinterpret_cast<const bf16x8 *>(&phiT[(nb * 16 + m) * LDK + 32 * t + 8 * g]);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[mb][t], b[nb], acc[mb][nb], 0, 0, 0);
-        gram[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[mb][t], xa[mb][t], gram[mb], 0, 0, 0);
-      }
+  } else {
+    Regs c0, c1;
+    int k0 = k_begin;
+    c0.load(phi, xrow, k0, k_end, tid, g);
+    while (k0 < k_end) {
+      // chunk in c0; prefetch the next one into c1
+      __syncthreads();
+      c0.stage(phiT, tid);
+      __syncthreads();
+      const int k1 = k0 + KC;
+      if (k1 < k_end) c1.load(phi, xrow, k1, k_end, tid, g);
+      chunk_mfma<NS, MB, KC, NTL, XFIRST>(c0, phiT, m, g, acc, gram);
+      if (k1 >= k_end) break;
+      __syncthreads();
+      c1.stage(phiT, tid);
+      __syncthreads();
+      const int k2 = k1 + KC;
+      if (k2 < k_end) c0.load(phi, xrow, k2, k_end, tid, g);
+      chunk_mfma<NS, MB, KC, NTL, XFIRST>(c1, phiT, m, g, acc, gram);
+      k0 = k2;
     }
   }
 
   // D layout of the 16x16 MFMA: lane (m, g) holds rows 4g..4g+3 of column m.
-  float *wsl = ws + (size_t)s * B * NP;
+  float *wsl = ws + (size_t)s * B * G::NP;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
+    for (int nb = 0; nb < G::NB; ++nb) {
       const int col = nb * 16 + m;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = row_base + mb * 16 + 4 * g + v;
-        if (row < B && col < N) wsl[(size_t)row * NP + col] = acc[mb][nb][v];
+        if (row < B && col < G::N) wsl[(size_t)row * G::NP + col] = acc[mb][nb][v];
       }
     }
     // Gram diagonal (m, m) sits in lane (m, g = m/4), element m%4.
     if (g == (m >> 2)) {
       const int row = row_base + mb * 16 + m;
-      if (row < B) wsl[(size_t)row * NP + N] = gram[mb][m & 3];
+      if (row < B) wsl[(size_t)row * G::NP + G::N] = gram[mb][m & 3];
     }
   }
 }
 
-template <int NS, int MB>
-void launch_typed(const GemmPlan &p, int64_t B, int64_t C, const void *X, const void *phi,
-                  float *ws, hipStream_t st) {
-  constexpr int KC = (NS == 8) ? 128 : 256;
+template <int NS, int MB, int KC, bool NTL, bool PIPE, bool XFIRST = false>
+hipError_t launch_typed(const GemmPlan &p, int64_t B, int64_t C, const void *X, const void *phi,
+                        float *ws, hipStream_t st) {
   const dim3 grid((uint32_t)p.row_tiles, (uint32_t)p.split);
-  gemm_rms_kernel<NS, MB, KC><<<grid, 256, 0, st>>>(
+  gemm_rms_kernel<NS, MB, KC, NTL, PIPE, XFIRST><<<grid, 256, 0, st>>>(
       static_cast<const uint16_t *>(X), static_cast<const uint16_t *>(phi), ws, (int)B,
       (int)(NS * C), (int)p.kslice);
+  return hipGetLastError();
 }
 
+// Chosen by measurement on MI355X at n=4, C=7168, B=16384: 128-k chunks,
+// software-pipelined loads, plain (cache-allocating) loads of X, about two
+// workgroups per CU.  Fewer concurrent workgroups means fewer concurrently
+// streamed rows, which the HBM serves more efficiently than many short runs.
+constexpr int kGemmKC = 128;
+constexpr int64_t kGemmTargetWGs = 512;
+
 template <int NS>
-void launch_n(const GemmPlan &p, int64_t B, int64_t C, const void *X, const void *phi, float *ws,
-              hipStream_t st) {
-  if (p.mb == 2)
-    launch_typed<NS, 2>(p, B, C, X, phi, ws, st);
-  else
-    launch_typed<NS, 1>(p, B, C, X, phi, ws, st);
+hipError_t launch_n(const GemmPlan &p, int64_t B, int64_t C, const void *X, const void *phi,
+                    float *ws, hipStream_t st) {
+  if (p.mb == 2) return launch_typed<NS, 2, kGemmKC, false, true>(p, B, C, X, phi, ws, st);
+  return launch_typed<NS, 1, kGemmKC, false, true>(p, B, C, X, phi, ws, st);
 }
 
 }  // namespace
 
-GemmPlan plan_gemm(int64_t B, int n, int64_t C) {
+GemmPlan plan_gemm_custom(int64_t B, int n, int64_t C, int mb, int kc, int64_t target_wgs) {
   GemmPlan p;
   const int64_t K = (int64_t)n * C;
-  p.kc = (n == 8) ? 128 : 256;
-  p.mb = (B >= 1024) ? 2 : 1;
+  p.kc = kc;
+  p.mb = mb;
   p.row_tiles = (B + 64 * p.mb - 1) / (64 * p.mb);
   const int64_t kchunks = (K + p.kc - 1) / p.kc;
-  // Enough workgroups to cover the 256 CUs several times over, but no more
-  // K-slices than needed: every slice adds (N+1)*4 bytes of partials per row.
-  const int64_t target_wgs = 1024;
   int64_t want = (target_wgs + p.row_tiles - 1) / p.row_tiles;
   if (const char *e = getenv("MHC_SPLIT_K")) {  // tuning override
     const long v = strtol(e, nullptr, 10);
@@ -186,6 +273,12 @@ GemmPlan plan_gemm(int64_t B, int n, int64_t C) {
   return p;
 }
 
+GemmPlan plan_gemm(int64_t B, int n, int64_t C) {
+  // Enough workgroups to cover the 256 CUs several times over, but no more
+  // K-slices than needed: every slice adds (N+1)*4 bytes of partials per row.
+  return plan_gemm_custom(B, n, C, (B >= 1024) ? 2 : 1, kGemmKC, kGemmTargetWGs);
+}
+
 size_t gemm_workspace_bytes(const GemmPlan &p, int64_t B, int n) {
   const int64_t N = (int64_t)n * n + 2 * n;
   return (size_t)p.split * (size_t)B * (size_t)(N + 1) * sizeof(float);
@@ -194,13 +287,12 @@ size_t gemm_workspace_bytes(const GemmPlan &p, int64_t B, int n) {
 hipError_t launch_gemm_rms(const GemmPlan &p, int n, int64_t B, int64_t C, const void *X,
                            const void *phi, float *ws, hipStream_t st) {
   switch (n) {
-    case 1: launch_n<1>(p, B, C, X, phi, ws, st); break;
-    case 2: launch_n<2>(p, B, C, X, phi, ws, st); break;
-    case 4: launch_n<4>(p, B, C, X, phi, ws, st); break;
-    case 8: launch_n<8>(p, B, C, X, phi, ws, st); break;
+    case 1: return launch_n<1>(p, B, C, X, phi, ws, st);
+    case 2: return launch_n<2>(p, B, C, X, phi, ws, st);
+    case 4: return launch_n<4>(p, B, C, X, phi, ws, st);
+    case 8: return launch_n<8>(p, B, C, X, phi, ws, st);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace mhc

@@ -18,6 +18,8 @@ struct GemmPlan {
 };
 
 GemmPlan plan_gemm(int64_t B, int n, int64_t C);
+// Plan with explicit rows-per-wave blocks, chunk size and target workgroup count.
+GemmPlan plan_gemm_custom(int64_t B, int n, int64_t C, int mb, int kc, int64_t target_wgs);
 size_t gemm_workspace_bytes(const GemmPlan &p, int64_t B, int n);
 
 hipError_t launch_gemm_rms(const GemmPlan &p, int n, int64_t B, int64_t C,

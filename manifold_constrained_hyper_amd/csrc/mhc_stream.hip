@@ -10,7 +10,8 @@
 //    read once per wave with scalar loads and live in SGPRs;
 //  * all loads of a task are issued before any arithmetic, keeping
 //    (n+1) * VPL 16-byte requests per lane in flight;
-//  * outputs are written once with non-temporal stores.
+//  * inputs are read once, with the non-temporal hint; outputs are written
+//    once (the launchers below pick the store hint per kernel).
 //
 // Math ([mHC-cutile] = page "mHC 算法分析 & cutile 高效实现", section 2.5 and
 // the fused apply of section 3.4): fp32 accumulation of bf16 inputs, one
@@ -22,16 +23,26 @@ namespace mhc {
 
 namespace {
 
-constexpr int kWavesPerBlock = 4;
+template <bool NT>
+__device__ __forceinline__ u32x4 ld(const void *p) {
+  return NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p)) : load16(p);
+}
+template <bool NT>
+__device__ __forceinline__ void st(void *p, u32x4 v) {
+  if (NT)
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+  else
+    *reinterpret_cast<u32x4 *>(p) = v;
+}
 
 // F_pre[row, c] = sum_i H_pre[row, i] * X[row, i*C + c]
-template <int NS, int VPL>
-__global__ __launch_bounds__(256) void pre_kernel(const uint16_t *__restrict__ X,
+template <int NS, int VPL, int WPB, bool NTL, bool NTS>
+__global__ __launch_bounds__(64 * WPB) void pre_kernel(const uint16_t *__restrict__ X,
                                                   const float *__restrict__ H,
                                                   uint16_t *__restrict__ F, uint32_t cvec,
                                                   uint32_t chunks_per_row, uint32_t tasks) {
   constexpr int N = NS * NS + 2 * NS;
-  const uint32_t task = (uint32_t)uniform((int)(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6)));
+  const uint32_t task = (uint32_t)uniform((int)(blockIdx.x * WPB + (threadIdx.x >> 6)));
   if (task >= tasks) return;
   const uint32_t row = task / chunks_per_row;
   const uint32_t chunk = task - row * chunks_per_row;
@@ -50,7 +61,7 @@ __global__ __launch_bounds__(256) void pre_kernel(const uint16_t *__restrict__ X
     const uint32_t v = v0 + 64u * u;
     if (v < cvec) {
 #pragma unroll
-      for (int j = 0; j < NS; ++j) xv[u][j] = load16(xr + ((size_t)j * cvec + v) * 16);
+      for (int j = 0; j < NS; ++j) xv[u][j] = ld<NTL>(xr + ((size_t)j * cvec + v) * 16);
     }
   }
 #pragma unroll
@@ -68,20 +79,20 @@ __global__ __launch_bounds__(256) void pre_kernel(const uint16_t *__restrict__ X
         }
         out[w] = pack_bf16x2(a0, a1);
       }
-      store16_nt(fr + (size_t)v * 16, out);
+      st<NTS>(fr + (size_t)v * 16, out);
     }
   }
 }
 
 // X_next[row, i*C + c] = sum_j H_res[row, i, j] * X[row, j*C + c] + H_post[row, i] * F_out[row, c]
-template <int NS, int VPL>
-__global__ __launch_bounds__(256) void post_res_kernel(const uint16_t *__restrict__ X,
+template <int NS, int VPL, int WPB, bool NTL, bool NTS>
+__global__ __launch_bounds__(64 * WPB) void post_res_kernel(const uint16_t *__restrict__ X,
                                                        const uint16_t *__restrict__ F,
                                                        const float *__restrict__ H,
                                                        uint16_t *__restrict__ Y, uint32_t cvec,
                                                        uint32_t chunks_per_row, uint32_t tasks) {
   constexpr int N = NS * NS + 2 * NS;
-  const uint32_t task = (uint32_t)uniform((int)(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6)));
+  const uint32_t task = (uint32_t)uniform((int)(blockIdx.x * WPB + (threadIdx.x >> 6)));
   if (task >= tasks) return;
   const uint32_t row = task / chunks_per_row;
   const uint32_t chunk = task - row * chunks_per_row;
@@ -106,8 +117,8 @@ __global__ __launch_bounds__(256) void post_res_kernel(const uint16_t *__restric
     const uint32_t v = v0 + 64u * u;
     if (v < cvec) {
 #pragma unroll
-      for (int j = 0; j < NS; ++j) xv[u][j] = load16(xr + ((size_t)j * cvec + v) * 16);
-      fv[u] = load16(fr + (size_t)v * 16);
+      for (int j = 0; j < NS; ++j) xv[u][j] = ld<NTL>(xr + ((size_t)j * cvec + v) * 16);
+      fv[u] = ld<NTL>(fr + (size_t)v * 16);
     }
   }
 #pragma unroll
@@ -136,66 +147,63 @@ __global__ __launch_bounds__(256) void post_res_kernel(const uint16_t *__restric
         }
       }
 #pragma unroll
-      for (int i = 0; i < NS; ++i) store16_nt(yr + ((size_t)i * cvec + v) * 16, out[i]);
+      for (int i = 0; i < NS; ++i) st<NTS>(yr + ((size_t)i * cvec + v) * 16, out[i]);
     }
   }
 }
 
-// Vectors per lane: the candidate that wastes the fewest lanes on the ragged
-// end of a row, preferring 2 (two tasks' worth of requests in flight).
-int pick_vpl(uint32_t cvec) {
-  const int cand[3] = {2, 4, 1};
-  int best = 2;
-  double best_waste = 2.0;
-  for (int c : cand) {
-    const uint32_t chunk = 64u * c;
-    const uint32_t chunks = (cvec + chunk - 1) / chunk;
-    const double waste = double(chunks * chunk - cvec) / double(chunks * chunk);
-    if (waste < best_waste - 1e-12) {
-      best_waste = waste;
-      best = c;
-    }
-  }
-  return best;
+// Launch shape shared by both kernels: one wave per (row, chunk) task.
+struct StreamShape {
+  uint32_t cvec, chunks, tasks;
+  dim3 grid;
+};
+
+template <int VPL, int WPB>
+bool stream_shape(int64_t B, int64_t C, StreamShape &sh) {
+  sh.cvec = (uint32_t)(C / 8);
+  sh.chunks = (sh.cvec + 64u * VPL - 1) / (64u * VPL);
+  const uint64_t tasks = (uint64_t)B * sh.chunks;
+  if (tasks >= (1ull << 31)) return false;
+  sh.tasks = (uint32_t)tasks;
+  sh.grid = dim3((uint32_t)((tasks + WPB - 1) / WPB));
+  return true;
 }
 
+template <int NS, int VPL, int WPB, bool NTL, bool NTS>
+hipError_t launch_pre_t(int64_t B, int64_t C, const void *X, const float *H, void *F,
+                        hipStream_t st) {
+  StreamShape sh;
+  if (!stream_shape<VPL, WPB>(B, C, sh)) return hipErrorInvalidValue;
+  pre_kernel<NS, VPL, WPB, NTL, NTS><<<sh.grid, 64 * WPB, 0, st>>>(
+      static_cast<const uint16_t *>(X), H, static_cast<uint16_t *>(F), sh.cvec, sh.chunks, sh.tasks);
+  return hipGetLastError();
+}
+
+template <int NS, int VPL, int WPB, bool NTL, bool NTS>
+hipError_t launch_post_res_t(int64_t B, int64_t C, const void *X, const void *F, const float *H,
+                             void *Y, hipStream_t st) {
+  StreamShape sh;
+  if (!stream_shape<VPL, WPB>(B, C, sh)) return hipErrorInvalidValue;
+  post_res_kernel<NS, VPL, WPB, NTL, NTS><<<sh.grid, 64 * WPB, 0, st>>>(
+      static_cast<const uint16_t *>(X), static_cast<const uint16_t *>(F), H,
+      static_cast<uint16_t *>(Y), sh.cvec, sh.chunks, sh.tasks);
+  return hipGetLastError();
+}
+
+// Launch shapes chosen by measurement on MI355X at n=4, C=7168, B=16384 (the
+// variants differ only in speed): one 16-byte vector per lane and one wave
+// per workgroup; X and F_out read with the non-temporal hint (touched once);
+// X_next stored non-temporally, F_pre with plain stores.
 template <int NS>
 hipError_t launch_pre_n(int64_t B, int64_t C, const void *X, const float *H, void *F,
                         hipStream_t st) {
-  const uint32_t cvec = (uint32_t)(C / 8);
-  const int vpl = pick_vpl(cvec);
-  const uint32_t chunks = (cvec + 64u * vpl - 1) / (64u * vpl);
-  const uint64_t tasks = (uint64_t)B * chunks;
-  if (tasks >= (1ull << 31)) return hipErrorInvalidValue;
-  const dim3 grid((uint32_t)((tasks + kWavesPerBlock - 1) / kWavesPerBlock));
-  const uint16_t *x = static_cast<const uint16_t *>(X);
-  uint16_t *f = static_cast<uint16_t *>(F);
-  switch (vpl) {
-    case 1: pre_kernel<NS, 1><<<grid, 256, 0, st>>>(x, H, f, cvec, chunks, (uint32_t)tasks); break;
-    case 2: pre_kernel<NS, 2><<<grid, 256, 0, st>>>(x, H, f, cvec, chunks, (uint32_t)tasks); break;
-    default: pre_kernel<NS, 4><<<grid, 256, 0, st>>>(x, H, f, cvec, chunks, (uint32_t)tasks); break;
-  }
-  return hipGetLastError();
+  return launch_pre_t<NS, 1, 1, true, false>(B, C, X, H, F, st);
 }
 
 template <int NS>
 hipError_t launch_post_res_n(int64_t B, int64_t C, const void *X, const void *F, const float *H,
                              void *Y, hipStream_t st) {
-  const uint32_t cvec = (uint32_t)(C / 8);
-  const int vpl = pick_vpl(cvec);
-  const uint32_t chunks = (cvec + 64u * vpl - 1) / (64u * vpl);
-  const uint64_t tasks = (uint64_t)B * chunks;
-  if (tasks >= (1ull << 31)) return hipErrorInvalidValue;
-  const dim3 grid((uint32_t)((tasks + kWavesPerBlock - 1) / kWavesPerBlock));
-  const uint16_t *x = static_cast<const uint16_t *>(X);
-  const uint16_t *f = static_cast<const uint16_t *>(F);
-  uint16_t *y = static_cast<uint16_t *>(Y);
-  switch (vpl) {
-    case 1: post_res_kernel<NS, 1><<<grid, 256, 0, st>>>(x, f, H, y, cvec, chunks, (uint32_t)tasks); break;
-    case 2: post_res_kernel<NS, 2><<<grid, 256, 0, st>>>(x, f, H, y, cvec, chunks, (uint32_t)tasks); break;
-    default: post_res_kernel<NS, 4><<<grid, 256, 0, st>>>(x, f, H, y, cvec, chunks, (uint32_t)tasks); break;
-  }
-  return hipGetLastError();
+  return launch_post_res_t<NS, 1, 1, true, true>(B, C, X, F, H, Y, st);
 }
 
 }  // namespace
