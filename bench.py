@@ -38,23 +38,36 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 DEFAULT_WORKLOAD = "large"
 
 
+def apply_stream_bytes(B, n, C, elem_bytes):
+    """Residual-stream bytes of the fused post/res apply: X_t read, F_out read,
+    X_next written (the convention of the apply figures printed in the mHC
+    CuTile page, section 4), without the coefficients."""
+    return B * (2 * n * C + C) * elem_bytes
+
+
+def product_flops(B, n, C):
+    """Flops of the fused product + sum of squares, 2 B K (N + 1) (the
+    convention of the page's gemm_rmsnorm TFLOPS figure)."""
+    N = n * n + 2 * n
+    return 2 * B * n * C * (N + 1)
+
+
 def path_bytes(B, n, C):
-    """Algorithmic bytes moved by each of the three calls for one forward."""
+    """Algorithmic bytes moved by each of the three calls for one forward
+    (bf16 streams, fp32 coefficients and biases)."""
     N = n * n + 2 * n
     K = n * C
     x = B * K * 2
     return {
         "mhc_coeffs": x + K * N * 2 + N * 4 + B * N * 4 + B * 4 + B * N * 4,
         "mhc_pre": x + B * n * 4 + B * C * 2,
-        "mhc_post_res": 2 * x + B * C * 2 + B * (n + n * n) * 4,
+        "mhc_post_res": apply_stream_bytes(B, n, C, 2) + B * (n + n * n) * 4,
     }
 
 
 def path_flops(B, n, C):
     """Algorithmic flops of one forward (product, sum of squares, pre, post/res)."""
-    N = n * n + 2 * n
-    K = n * C
-    return B * (2 * K * N + 2 * K + 2 * K + 2 * (n * n + n) * C)
+    return product_flops(B, n, C) + B * (2 * n * C + 2 * (n * n + n) * C)
 
 
 # dominant-kernel bookkeeping: kernel symbol substring -> call it belongs to
