@@ -9,15 +9,17 @@
 //   sections 3.2, 3.3, 5.2, 5.3  these steps are tiny per row, so they are
 //                fused after the split-K reduction in a single launch.
 //
-// Layout: a workgroup of 256 lanes owns R = 256 / (n*n) rows.
+// Layout: a workgroup of 256 lanes owns R = 256 / n rows; n consecutive lanes
+// serve one row, lane i holding row i of that row's n x n res matrix.
 //   phase 1  lanes sum the S partial slices [S, B, N+1] in slice order 0..S-1
 //            (fixed order: bitwise deterministic).  For each slice the
-//            workgroup's rows are one contiguous run, so the loads coalesce.
+//            workgroup's rows are one contiguous run, so the loads coalesce;
+//            all loads of a batch of slices are issued before they are added.
 //            Sums go to LDS and the raw logits to global memory.
-//   phase 2  each row is owned by n*n consecutive lanes; lane (i, j) holds
-//            element (i, j) of the res matrix.  Row sums reduce over the low
-//            log2(n) lane bits, column sums over the high bits, with xor
-//            butterflies (every lane of a group ends with the same bits).
+//   phase 2  lane i computes gate i of the pre block and of the post block,
+//            then the Sinkhorn iteration: a row normalisation is local to the
+//            lane; a column sum is a butterfly over the n lanes of the row
+//            (DPP lane moves, every lane ends with bitwise the same sum).
 #include "mhc_device.h"
 #include "mhc_launch.h"
 
@@ -27,16 +29,38 @@ namespace {
 
 constexpr int kIters = 20;
 
+// x + (x from the lane whose index differs in the given low bits), for the
+// butterfly over groups of 2, 4 or 8 aligned lanes.
+__device__ __forceinline__ float dpp_add_xor1(float x) {
+  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_add_xor2(float x) {
+  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+// lane l <- lane (7 - l) within each group of 8: pairs the two quads of an
+// aligned group of 8 once each quad holds its own sum.
+__device__ __forceinline__ float dpp_add_half_mirror(float x) {
+  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
+}
+
+template <int NS>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (NS >= 2) x = dpp_add_xor1(x);
+  if constexpr (NS >= 4) x = dpp_add_xor2(x);
+  if constexpr (NS >= 8) x = dpp_add_half_mirror(x);
+  return x;
+}
+
 template <int NS>
 __global__ __launch_bounds__(256) void coeff_sinkhorn_kernel(
     const float *__restrict__ ws, int split, int B, float inv_k, float alpha_pre,
     float alpha_post, float alpha_res, const float *__restrict__ b_pre,
     const float *__restrict__ b_post, const float *__restrict__ b_res,
     float *__restrict__ logits, float *__restrict__ r_out, float *__restrict__ H) {
+  static_assert(NS == 1 || NS == 2 || NS == 4 || NS == 8, "n");
   constexpr int N = NS * NS + 2 * NS;
   constexpr int NP = N + 1;
-  constexpr int L = NS * NS;   // lanes per row
-  constexpr int R = 256 / L;   // rows per workgroup
+  constexpr int R = 256 / NS;  // rows per workgroup
   __shared__ float sums[R * NP];
 
   const int tid = threadIdx.x;
@@ -44,66 +68,85 @@ __global__ __launch_bounds__(256) void coeff_sinkhorn_kernel(
   const int rows = min(R, B - row0);
 
   {
+    // Every thread owns EPT elements of the workgroup's [rows, N+1] block and
+    // issues the loads of SB slices for all of them before adding, so a
+    // thread has up to SB*EPT independent loads in flight.
+    constexpr int EPT = (R * NP + 255) / 256;
+    constexpr int SB = 4;
     const size_t slice = (size_t)B * NP;
     const float *base = ws + (size_t)row0 * NP;
-    for (int e = tid; e < rows * NP; e += 256) {
-      // batches of 8 independent loads, added in slice order
-      float a = 0.f;
-      int s = 0;
-      for (; s + 8 <= split; s += 8) {
-        float v[8];
+    const int nel = rows * NP;
+    float acc[EPT];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = base[(size_t)(s + u) * slice + e];
+    for (int q = 0; q < EPT; ++q) acc[q] = 0.f;
+    for (int s0 = 0; s0 < split; s0 += SB) {
+      float v[SB][EPT];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) a += v[u];
+      for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+        for (int q = 0; q < EPT; ++q) {
+          const int e = tid + q * 256;
+          v[sb][q] = (s0 + sb < split && e < nel) ? base[(size_t)(s0 + sb) * slice + e] : 0.f;
+        }
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+        for (int q = 0; q < EPT; ++q)
+          if (s0 + sb < split) acc[q] += v[sb][q];
+    }
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      const int e = tid + q * 256;
+      if (e < nel) {
+        sums[e] = acc[q];
+        const int rr = e / NP, cc = e - rr * NP;
+        if (cc < N) logits[(size_t)(row0 + rr) * N + cc] = acc[q];
       }
-      for (; s < split; ++s) a += base[(size_t)s * slice + e];
-      sums[e] = a;
-      const int rr = e / NP, cc = e - rr * NP;
-      if (cc < N) logits[(size_t)(row0 + rr) * N + cc] = a;
     }
   }
   __syncthreads();
 
-  const int lr = tid / L, sub = tid - (tid / L) * L;
+  const int lr = tid / NS, i = tid % NS;
   if (lr >= rows) return;  // whole row groups leave together
   const float *sm = sums + lr * NP;
   const int row = row0 + lr;
   const float r = sqrtf(sm[N] * inv_k);
   const float inv_r = 1.0f / r;
   float *h = H + (size_t)row * N;
-  if (sub == 0) r_out[row] = r;
-
-  for (int c = sub; c < 2 * NS; c += L) {
-    if (c < NS) {
-      const float z = alpha_pre * sm[c] * inv_r + b_pre[c];
-      h[c] = 1.0f / (1.0f + __expf(-z));
-    } else {
-      const float z = alpha_post * sm[c] * inv_r + b_post[c - NS];
-      h[c] = 2.0f / (1.0f + __expf(-z));
-    }
+  if (i == 0) r_out[row] = r;
+  {
+    const float zp = alpha_pre * sm[i] * inv_r + b_pre[i];
+    h[i] = 1.0f / (1.0f + __expf(-zp));
+    const float zq = alpha_post * sm[NS + i] * inv_r + b_post[i];
+    h[NS + i] = 2.0f / (1.0f + __expf(-zq));
   }
 
-  float v = __expf(alpha_res * sm[2 * NS + sub] * inv_r + b_res[sub]);
+  float m[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j)
+    m[j] = __expf(alpha_res * sm[2 * NS + i * NS + j] * inv_r + b_res[i * NS + j]);
+  // Each normalisation multiplies by the hardware reciprocal of the sum
+  // (v_rcp_f32, about 1 ulp) instead of dividing element by element.
 #pragma unroll 1
   for (int it = 0; it < kIters; ++it) {
-    float rs = v;
+    float rs = 0.f;
 #pragma unroll
-    for (int o = 1; o < NS; o <<= 1) rs += __shfl_xor(rs, o, 64);
-    v = v / rs;
-    float cs = v;
+    for (int j = 0; j < NS; ++j) rs += m[j];
+    const float inv_rs = __builtin_amdgcn_rcpf(rs);
 #pragma unroll
-    for (int o = NS; o < L; o <<= 1) cs += __shfl_xor(cs, o, 64);
-    v = v / cs;
+    for (int j = 0; j < NS; ++j) m[j] *= inv_rs;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) m[j] *= __builtin_amdgcn_rcpf(group_sum<NS>(m[j]));
   }
-  h[2 * NS + sub] = v;
+#pragma unroll
+  for (int j = 0; j < NS; ++j) h[2 * NS + i * NS + j] = m[j];
 }
 
 template <int NS>
 void launch_n(int64_t B, int64_t C, int split, const float *ws, float ap, float aq, float ar,
               const float *bp, const float *bq, const float *br, float *logits, float *r,
               float *H, hipStream_t st) {
-  constexpr int R = 256 / (NS * NS);
+  constexpr int R = 256 / NS;
   const dim3 grid((uint32_t)((B + R - 1) / R));
   const float inv_k = (float)(1.0 / (double)(NS * C));
   coeff_sinkhorn_kernel<NS><<<grid, 256, 0, st>>>(ws, split, (int)B, inv_k, ap, aq, ar, bp, bq,

@@ -37,6 +37,9 @@ __device__ __forceinline__ u32x4 load16(const void *p) {
 __device__ __forceinline__ void store16_nt(void *p, u32x4 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
 }
+__device__ __forceinline__ void store16_plain(void *p, u32x4 v) {
+  *reinterpret_cast<u32x4 *>(p) = v;
+}
 
 // Wave-uniform value (lets the compiler keep row-derived addresses in SGPRs
 // and read per-row coefficients with scalar loads).

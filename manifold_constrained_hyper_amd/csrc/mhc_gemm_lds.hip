@@ -1,0 +1,264 @@
+// Fused coefficient product and sum of squares with X staged through LDS.
+//
+// Same arithmetic as gemm_rms_kernel (mhc_gemm_rms.hip): per row tile and
+// K-slice, the partial logits X_t . phi ([mHC-cutile] = page "mHC 算法分析 &
+// cutile 高效实现", sections 2.1, 3.1, 5.1) and the partial sum of X_t^2
+// (section 2.2) are written as fp32 [S, B, N+1] for the combine kernel.
+//
+// What changes is how X reaches the matrix cores.  The MFMA A operand wants
+// 16 rows x 16 bytes per instruction, and reading HBM in that shape (16 rows x
+// 64 bytes per load instruction) leaves a good part of the bandwidth unused.
+// Here X is read row-contiguously instead, by the gfx950 direct-to-LDS load
+// (global_load_lds_dwordx4: each lane's 16 bytes land at LDS base + 16*lane),
+// into a ring of STAGES chunk buffers, and the A operands are read back from
+// LDS.  So that those reads are free of bank conflicts, the 16-byte pieces of
+// row r are stored XOR-swizzled (piece p at slot p ^ (r & 15)); the swizzle is
+// applied through the per-lane source addresses, so every load instruction
+// still covers whole contiguous row segments.
+//
+// phi is consumed in a packed copy, written by pack_phi_kernel into the
+// workspace at the start of every call: for each 32-k step and 16-column
+// block, the 64 lanes' B operands (8 consecutive k of one column) are one
+// contiguous KiB, so phi also moves by direct-to-LDS loads, one instruction
+// per KiB, with no transposition on the critical path.  Columns past N and k
+// past K are zero in the packed copy.  X pieces past K are read from a zeroed
+// 256-byte block of the workspace instead of past the end of the row.
+//
+// Pipeline per workgroup (4 waves, 64*MB rows): the loads of chunks
+// c+1 .. c+STAGES-1 are in flight while chunk c is multiplied.  Each wave
+// waits only for its own share of chunk c (s_waitcnt vmcnt), then one barrier
+// makes the whole chunk visible and frees the slot of chunk c-1 for refill.
+#include "mhc_device.h"
+#include "mhc_launch.h"
+
+namespace mhc {
+
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int NS, int MB, int KC, int STAGES>
+struct LdsTile {
+  static constexpr int N = NS * NS + 2 * NS;
+  static constexpr int NP = N + 1;
+  static constexpr int NB = (N + 15) / 16;
+  static constexpr int RT = 64 * MB;                 // rows per workgroup
+  static constexpr int T = KC / 32;                  // MFMA k-steps per chunk
+  static constexpr int PIECES = KC / 8;              // 16-byte pieces per row per chunk
+  static constexpr int RPI = 64 / PIECES;            // rows per load instruction
+  static constexpr int XI = RT * PIECES / 64;        // X load instructions per chunk
+  static constexpr int PI = T * NB;                  // phi load instructions per chunk
+  static constexpr int XI_W = XI / 4, PI_W = PI / 4; // ... per wave
+  static constexpr int VM_PER_CHUNK = XI_W + PI_W;
+  static constexpr int X_BYTES = RT * KC * 2;
+  static constexpr int P_BYTES = PI * 1024;
+  static constexpr int STAGE_BYTES = X_BYTES + P_BYTES;
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static_assert(PIECES >= 16 && PIECES <= 64, "swizzle needs 16..64 pieces per row");
+  static_assert(XI % 4 == 0 && PI % 4 == 0, "load instructions must split evenly over 4 waves");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
+};
+
+// s_waitcnt with only the vector-memory counter constrained (expcnt and
+// lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int NS, int MB, int KC, int STAGES>
+__device__ __forceinline__ void issue_chunk(char *lds, int slot, int wave, int lane,
+                                           const uint16_t *__restrict__ X,
+                                           const uint16_t *__restrict__ phip,
+                                           const uint16_t *__restrict__ zero, int row0, int B,
+                                           int K, int k0) {
+  using L = LdsTile<NS, MB, KC, STAGES>;
+  char *xs = lds + slot * L::STAGE_BYTES;
+  char *ps = xs + L::X_BYTES;
+  const int slot_in_row = lane % L::PIECES;
+#pragma unroll
+  for (int j = 0; j < L::XI_W; ++j) {
+    const int inst = wave * L::XI_W + j;
+    const int rr = inst * L::RPI + lane / L::PIECES;          // row within the tile
+    const int piece = slot_in_row ^ (rr & 15);
+    const int k = k0 + piece * 8;
+    const int row = min(row0 + rr, B - 1);
+    const uint16_t *src = (k < K) ? X + (size_t)row * K + k : zero;
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)(xs + inst * 1024), 16, 0, 0);
+  }
+  const int kstep0 = k0 / 32;
+#pragma unroll
+  for (int j = 0; j < L::PI_W; ++j) {
+    const int inst = wave * L::PI_W + j;                       // = t * NB + nb
+    const uint16_t *src = phip + ((size_t)(kstep0 * L::NB + inst) * 64 + lane) * 8;
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)(ps + inst * 1024), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
+// Wait until at most `later` chunks' loads of this wave are outstanding.
+template <int NS, int MB, int KC, int STAGES>
+__device__ __forceinline__ void wait_chunks(int later) {
+  using L = LdsTile<NS, MB, KC, STAGES>;
+  if (STAGES >= 4 && later >= 2) {
+    wait_vmcnt<(STAGES >= 4 ? 2 : 0) * L::VM_PER_CHUNK>();
+  } else if (later >= 1) {
+    wait_vmcnt<L::VM_PER_CHUNK>();
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
+template <int NS, int MB, int KC, int STAGES>
+__global__ __launch_bounds__(256) void gemm_rms_lds_kernel(const uint16_t *__restrict__ X,
+                                                           const uint16_t *__restrict__ phip,
+                                                           const uint16_t *__restrict__ zero,
+                                                           float *__restrict__ ws, int B, int K,
+                                                           int kslice) {
+  using L = LdsTile<NS, MB, KC, STAGES>;
+  __shared__ __attribute__((aligned(1024))) char lds[L::LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int m = lane & 15, g = lane >> 4;
+  const int s = blockIdx.y;
+  const int k_begin = s * kslice;
+  const int k_end = min(K, k_begin + kslice);
+  const int nchunks = (k_end - k_begin + KC - 1) / KC;
+  const int row0 = blockIdx.x * L::RT;
+
+  f32x4 acc[MB][L::NB], gram[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    gram[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nb = 0; nb < L::NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+#pragma unroll
+  for (int c = 0; c < STAGES - 1; ++c)
+    if (c < nchunks)
+      issue_chunk<NS, MB, KC, STAGES>(lds, c, wave, lane, X, phip, zero, row0, B, K,
+                                      k_begin + c * KC);
+
+  for (int c = 0; c < nchunks; ++c) {
+    // This wave's loads of chunk c have landed and its LDS reads of chunk
+    // c-1 have returned; after the barrier the same holds for every wave, so
+    // chunk c is complete and the slot of chunk c-1 may be refilled.  (A bare
+    // s_barrier: a fenced __syncthreads would also wait for the loads still
+    // in flight for the later chunks.)
+    wait_chunks<NS, MB, KC, STAGES>(min(STAGES - 2, nchunks - 1 - c));
+    wait_lgkmcnt0();
+    asm volatile("" ::: "memory");  // no memory access moves across the barrier
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const int cn = c + STAGES - 1;
+    if (cn < nchunks)
+      issue_chunk<NS, MB, KC, STAGES>(lds, cn % STAGES, wave, lane, X, phip, zero, row0, B, K,
+                                      k_begin + cn * KC);
+    const char *xs = lds + (c % STAGES) * L::STAGE_BYTES;
+    const char *ps = xs + L::X_BYTES;
+#pragma unroll
+    for (int t = 0; t < L::T; ++t) {
+      bf16x8 b[L::NB];
+#pragma unroll
+      for (int nb = 0; nb < L::NB; ++nb)
+        b[nb] = *reinterpret_cast<const bf16x8 *>(ps + (t * L::NB + nb) * 1024 + lane * 16);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int rr = wave * 16 * MB + mb * 16 + m;
+        const int slot = (4 * t + g) ^ m;  // rr & 15 == m
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(xs + rr * (KC * 2) + slot * 16);
+#pragma unroll
+        for (int nb = 0; nb < L::NB; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[nb], acc[mb][nb], 0, 0, 0);
+        gram[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, a, gram[mb], 0, 0, 0);
+      }
+    }
+  }
+
+  // D layout of the 16x16 MFMA: lane (m, g) holds rows 4g..4g+3 of column m.
+  float *wsl = ws + (size_t)s * B * L::NP;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int rbase = row0 + wave * 16 * MB + mb * 16;
+#pragma unroll
+    for (int nb = 0; nb < L::NB; ++nb) {
+      const int col = nb * 16 + m;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = rbase + 4 * g + v;
+        if (row < B && col < L::N) wsl[(size_t)row * L::NP + col] = acc[mb][nb][v];
+      }
+    }
+    if (g == (m >> 2)) {  // Gram diagonal (m, m): lane (m, m/4), element m%4
+      const int row = rbase + m;
+      if (row < B) wsl[(size_t)row * L::NP + L::N] = gram[mb][m & 3];
+    }
+  }
+}
+
+// phi [K, N] -> packed B operands: for 32-k step ks and column block nb, lane
+// (m, g) of the 1 KiB block holds phi[ks*32 + 8g + j][nb*16 + m], j = 0..7.
+// Also clears the 256-byte zero block.
+template <int NS>
+__global__ __launch_bounds__(256) void pack_phi_kernel(const uint16_t *__restrict__ phi,
+                                                       uint16_t *__restrict__ phip,
+                                                       uint16_t *__restrict__ zero, int K,
+                                                       int ksteps) {
+  constexpr int N = NS * NS + 2 * NS;
+  constexpr int NB = (N + 15) / 16;
+  const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (v < 16) store16_plain(zero + v * 8, u32x4{0u, 0u, 0u, 0u});
+  if (v >= (int64_t)ksteps * NB * 64) return;
+  const int lane = (int)(v & 63);
+  const int64_t blk = v >> 6;
+  const int nb = (int)(blk % NB);
+  const int64_t ks = blk / NB;
+  const int n = nb * 16 + (lane & 15);
+  const int64_t k0 = ks * 32 + 8 * (lane >> 4);
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t ka = k0 + 2 * q, kb = ka + 1;
+    const uint32_t lo = (n < N && ka < K) ? phi[ka * N + n] : 0u;
+    const uint32_t hi = (n < N && kb < K) ? phi[kb * N + n] : 0u;
+    w[q] = lo | (hi << 16);
+  }
+  store16_plain(phip + v * 8, u32x4{w[0], w[1], w[2], w[3]});
+}
+
+}  // namespace
+
+template <int NS, int MB, int KC, int STAGES>
+hipError_t launch_gemm_lds_typed(const GemmPlan &p, int64_t B, int64_t C, const void *X,
+                                 const void *phi, void *ws_base, hipStream_t st) {
+  using L = LdsTile<NS, MB, KC, STAGES>;
+  const int K = (int)(NS * C);
+  char *base = static_cast<char *>(ws_base);
+  uint16_t *phip = reinterpret_cast<uint16_t *>(base + p.phip_offset);
+  uint16_t *zero = reinterpret_cast<uint16_t *>(base + p.zero_offset);
+  const int ksteps = (int)(p.phip_bytes / ((size_t)L::NB * 1024));
+  const int64_t vecs = (int64_t)ksteps * L::NB * 64;
+  pack_phi_kernel<NS><<<dim3((uint32_t)((vecs + 255) / 256)), 256, 0, st>>>(
+      static_cast<const uint16_t *>(phi), phip, zero, K, ksteps);
+  const dim3 grid((uint32_t)p.row_tiles, (uint32_t)p.split);
+  gemm_rms_lds_kernel<NS, MB, KC, STAGES><<<grid, 256, 0, st>>>(
+      static_cast<const uint16_t *>(X), phip, zero, reinterpret_cast<float *>(base), (int)B, K,
+      (int)p.kslice);
+  return hipGetLastError();
+}
+
+// Instantiations used by the library (see plan_gemm in mhc_gemm_rms.hip).
+template hipError_t launch_gemm_lds_typed<1, 1, 256, 3>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<2, 1, 256, 3>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<4, 1, 256, 3>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<8, 1, 128, 4>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+
+}  // namespace mhc

@@ -237,27 +237,35 @@ hipError_t launch_typed(const GemmPlan &p, int64_t B, int64_t C, const void *X, 
   return hipGetLastError();
 }
 
-// Chosen by measurement on MI355X at n=4, C=7168, B=16384: 128-k chunks,
-// software-pipelined loads, plain (cache-allocating) loads of X, about two
-// workgroups per CU.  Fewer concurrent workgroups means fewer concurrently
-// streamed rows, which the HBM serves more efficiently than many short runs.
+// Register-path settings (algo 0), chosen by measurement on MI355X at n=4,
+// C=7168, B=16384: 128-k chunks, software-pipelined loads, plain
+// (cache-allocating) loads of X, about two workgroups per CU.
 constexpr int kGemmKC = 128;
 constexpr int64_t kGemmTargetWGs = 512;
 
 template <int NS>
 hipError_t launch_n(const GemmPlan &p, int64_t B, int64_t C, const void *X, const void *phi,
                     float *ws, hipStream_t st) {
+  if (p.algo == 1) {
+    if constexpr (NS == 8) return launch_gemm_lds_typed<NS, 1, 128, 4>(p, B, C, X, phi, ws, st);
+    else return launch_gemm_lds_typed<NS, 1, 256, 3>(p, B, C, X, phi, ws, st);
+  }
   if (p.mb == 2) return launch_typed<NS, 2, kGemmKC, false, true>(p, B, C, X, phi, ws, st);
   return launch_typed<NS, 1, kGemmKC, false, true>(p, B, C, X, phi, ws, st);
 }
 
 }  // namespace
 
-GemmPlan plan_gemm_custom(int64_t B, int n, int64_t C, int mb, int kc, int64_t target_wgs) {
+GemmPlan plan_gemm_custom(int64_t B, int n, int64_t C, int algo, int mb, int kc, int stages,
+                          int64_t target_wgs) {
   GemmPlan p;
   const int64_t K = (int64_t)n * C;
+  const int64_t N = (int64_t)n * n + 2 * n;
+  const int64_t NB = (N + 15) / 16;
+  p.algo = algo;
   p.kc = kc;
   p.mb = mb;
+  p.stages = stages;
   p.row_tiles = (B + 64 * p.mb - 1) / (64 * p.mb);
   const int64_t kchunks = (K + p.kc - 1) / p.kc;
   int64_t want = (target_wgs + p.row_tiles - 1) / p.row_tiles;
@@ -270,18 +278,41 @@ GemmPlan plan_gemm_custom(int64_t B, int n, int64_t C, int mb, int kc, int64_t t
   const int64_t chunks_per_slice = (kchunks + want - 1) / want;
   p.kslice = chunks_per_slice * p.kc;
   p.split = (int)((K + p.kslice - 1) / p.kslice);
+  p.partial_bytes = (size_t)p.split * (size_t)B * (size_t)(N + 1) * sizeof(float);
+  if (algo == 1) {
+    p.phip_offset = (p.partial_bytes + 1023) & ~(size_t)1023;
+    p.phip_bytes = (size_t)(kchunks * p.kc / 32) * (size_t)NB * 1024;
+    p.zero_offset = p.phip_offset + p.phip_bytes;
+    p.total_bytes = p.zero_offset + 256;
+  } else {
+    p.phip_offset = p.phip_bytes = p.zero_offset = 0;
+    p.total_bytes = p.partial_bytes;
+  }
   return p;
 }
 
 GemmPlan plan_gemm(int64_t B, int n, int64_t C) {
-  // Enough workgroups to cover the 256 CUs several times over, but no more
-  // K-slices than needed: every slice adds (N+1)*4 bytes of partials per row.
-  return plan_gemm_custom(B, n, C, (B >= 1024) ? 2 : 1, kGemmKC, kGemmTargetWGs);
+  // X staged through LDS (algo 1), one 4-wave workgroup per CU at a time
+  // (the LDS ring is ~144 KiB); enough workgroups to fill the 256 CUs, and no
+  // more K-slices than that needs, since every slice adds (N+1)*4 bytes of
+  // partials per row.
+  const int kc = (n == 8) ? 128 : 256;
+  const int stages = (n == 8) ? 4 : 3;
+  int64_t target = 256;
+  if (const char *e = getenv("MHC_GEMM_ALGO")) {  // tuning override: 0 = register path
+    if (strtol(e, nullptr, 10) == 0) return plan_gemm_custom(B, n, C, 0, (B >= 1024) ? 2 : 1, kGemmKC, 1, kGemmTargetWGs);
+  }
+  if (const char *e = getenv("MHC_GEMM_WGS")) {  // tuning override
+    const long v = strtol(e, nullptr, 10);
+    if (v > 0) target = v;
+  }
+  return plan_gemm_custom(B, n, C, 1, 1, kc, stages, target);
 }
 
 size_t gemm_workspace_bytes(const GemmPlan &p, int64_t B, int n) {
-  const int64_t N = (int64_t)n * n + 2 * n;
-  return (size_t)p.split * (size_t)B * (size_t)(N + 1) * sizeof(float);
+  (void)B;
+  (void)n;
+  return p.total_bytes;
 }
 
 hipError_t launch_gemm_rms(const GemmPlan &p, int n, int64_t B, int64_t C, const void *X,

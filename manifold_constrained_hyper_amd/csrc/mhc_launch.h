@@ -9,18 +9,32 @@
 namespace mhc {
 
 // Split-K plan of the fused product + sum-of-squares pass.
+//
+// Workspace layout (bytes from the start of the caller's workspace):
+//   [0, partial_bytes)                 fp32 partials [split, B, N+1]
+//   [phip_offset, +phip_bytes)         packed phi (algo 1 only)
+//   [zero_offset, +256)                zero block (algo 1 only)
 struct GemmPlan {
+  int algo;           // 0: MFMA A operands loaded from global memory; 1: X staged through LDS
   int mb;             // 16-row MFMA blocks per wavefront (rows per workgroup = 64 * mb)
-  int kc;             // K elements staged per LDS chunk
+  int kc;             // K elements per chunk
+  int stages;         // LDS ring depth (algo 1)
   int split;          // S: number of K-slices (partials in the workspace)
   int64_t kslice;     // K elements per slice (multiple of kc)
   int64_t row_tiles;  // workgroups along B
+  size_t partial_bytes, phip_offset, phip_bytes, zero_offset, total_bytes;
 };
 
 GemmPlan plan_gemm(int64_t B, int n, int64_t C);
-// Plan with explicit rows-per-wave blocks, chunk size and target workgroup count.
-GemmPlan plan_gemm_custom(int64_t B, int n, int64_t C, int mb, int kc, int64_t target_wgs);
+// Plan with explicit kernel, rows-per-wave blocks, chunk size, ring depth and
+// target workgroup count.
+GemmPlan plan_gemm_custom(int64_t B, int n, int64_t C, int algo, int mb, int kc, int stages,
+                          int64_t target_wgs);
 size_t gemm_workspace_bytes(const GemmPlan &p, int64_t B, int n);
+
+template <int NS, int MB, int KC, int STAGES>
+hipError_t launch_gemm_lds_typed(const GemmPlan &p, int64_t B, int64_t C, const void *X,
+                                 const void *phi, void *ws_base, hipStream_t st);
 
 hipError_t launch_gemm_rms(const GemmPlan &p, int n, int64_t B, int64_t C,
                            const void *X, const void *phi, float *ws, hipStream_t st);

@@ -55,7 +55,11 @@ def test_workspace_and_split_host_functions():
         S = mhc.mhc_coeffs_split_k(B, n, C)
         N = n * n + 2 * n
         assert 1 <= S <= max(1, (n * C + 127) // 128)
-        assert mhc.mhc_coeffs_workspace_size(B, n, C) == S * B * (N + 1) * 4
+        # fp32 partials [S, B, N+1] plus, for the LDS-staged product, a packed
+        # copy of phi and a small zero block
+        ws = mhc.mhc_coeffs_workspace_size(B, n, C)
+        assert ws >= S * B * (N + 1) * 4
+        assert ws <= S * B * (N + 1) * 4 + 1024 + ((n * C + 255) // 32 + 8) * ((N + 15) // 16) * 1024 + 256
     assert mhc.mhc_coeffs_workspace_size(0, 4, 256) == 0
     assert mhc.mhc_coeffs_workspace_size(10, 3, 256) == 0
     assert mhc.mhc_coeffs_split_k(10, 4, 12) == 0

@@ -40,6 +40,21 @@ def _gpu():
     yield
 
 
+# The product kernel has two implementations: X staged through LDS by
+# direct-to-LDS loads (the default) and MFMA operands loaded straight from
+# global memory (selected with MHC_GEMM_ALGO=0).  Both must meet the bar.
+GEMM_ALGOS = ["lds", "reg"]
+
+
+@pytest.fixture(params=GEMM_ALGOS)
+def gemm_algo(request, monkeypatch):
+    if request.param == "reg":
+        monkeypatch.setenv("MHC_GEMM_ALGO", "0")
+    else:
+        monkeypatch.delenv("MHC_GEMM_ALGO", raising=False)
+    return request.param
+
+
 def run_forward(inp, out=None):
     B, n, C = inp["B"], inp["n"], inp["C"]
     o = out if out is not None else mhc.alloc_outputs(B, n, C)
@@ -122,8 +137,8 @@ def sample_rows(B, k=64, seed=0):
 # ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name", ["tiny", "decode"])
-def test_parity_full(name):
-    _say(f"parity full {name}")
+def test_parity_full(name, gemm_algo):
+    _say(f"parity full {name} gemm={gemm_algo}")
     inp = synth.make_config(name, device="cuda")
     o = run_forward(inp)
     rows = list(range(inp["B"]))
@@ -133,8 +148,8 @@ def test_parity_full(name):
 
 
 @pytest.mark.parametrize("name", ["prefill", "large", "wide"])
-def test_parity_sampled_and_properties(name):
-    _say(f"parity sampled {name}")
+def test_parity_sampled_and_properties(name, gemm_algo):
+    _say(f"parity sampled {name} gemm={gemm_algo}")
     inp = synth.make_config(name, device="cuda")
     o = run_forward(inp)
     B, n, C = inp["B"], inp["n"], inp["C"]
@@ -174,8 +189,8 @@ RAGGED = [(77, 4, 264), (1, 4, 8), (130, 8, 72), (33, 1, 24), (65, 2, 40), (200,
 
 
 @pytest.mark.parametrize("B,n,C", RAGGED, ids=[f"B{b}n{n}C{c}" for b, n, c in RAGGED])
-def test_parity_ragged(B, n, C):
-    _say(f"parity ragged B={B} n={n} C={C}")
+def test_parity_ragged(B, n, C, gemm_algo):
+    _say(f"parity ragged B={B} n={n} C={C} gemm={gemm_algo}")
     inp = synth.make_inputs(n, C, B, "student_t4" if B % 2 else "normal", seed=B * 31 + C,
                             device="cuda")
     o = run_forward(inp)
@@ -247,8 +262,8 @@ def test_bitwise_deterministic():
         assert torch.equal(a[k].view(torch.int8), b[k].view(torch.int8)), k
 
 
-def test_split_k_invariance(monkeypatch):
-    _say("split-K invariance decode")
+def test_split_k_invariance(monkeypatch, gemm_algo):
+    _say(f"split-K invariance decode gemm={gemm_algo}")
     inp = synth.make_config("decode", device="cuda")
     ref = None
     for s in ("1", "3", "17", "112"):
