@@ -2,23 +2,34 @@
 
     python bench.py [--steps K] [--warmup W] [--workload large]
 
-One step = one pass of the whole forward (mhc_coeffs, mhc_pre, mhc_post_res)
-over one batch of synthetic input already resident in HBM.  Prints ONE JSON
-line with tokens/s, per-call times, achieved HBM bandwidth against the
-algorithmic byte count, the roofline of the dominant kernel and the fp64
-oracle's throughput on the host as a CPU baseline.
+One step = one mHC layer over one batch of synthetic input already resident
+in HBM, run as a model runs it: `mhc_coeffs` once before the loop, then per
+layer `mhc_pre` (step 4a) and `mhc_post_res_coeffs` (step 4b of this layer
+fused with steps 1-3 of the next, so the residual stream is read twice per
+layer instead of three times).  The residual stream is chained through the
+layers (X_{t+1} of one step is X_t of the next); every layer uses the same
+synthetic phi and biases, and the layer F between the two calls is not mHC
+(F_out is a fixed synthetic input).  The three separate calls
+(`mhc_coeffs`, `mhc_pre`, `mhc_post_res` on a fixed X_t) are timed as well
+and reported under "three_call".
 
-Algorithmic bytes per forward (bf16 X_t, F_out, F_pre, X_next; fp32 coefficients):
-  mhc_coeffs    X_t + phi + biases + logits + r + H
-  mhc_pre       X_t + H_pre + F_pre
-  mhc_post_res  2 X_t + F_out + (H_post, H_res)
-The split-K workspace is implementation traffic and is not counted.
+Prints ONE JSON line with tokens/s, achieved HBM bandwidth against the
+algorithmic byte count, per-call times, the roofline of the dominant call and
+the fp64 oracle's throughput on the host as a CPU baseline.
+
+Algorithmic bytes (bf16 X_t, F_out, F_pre, X_next; fp32 coefficients):
+  mhc_coeffs           X_t + phi + biases + logits + r + H
+  mhc_pre              X_t + H_pre + F_pre
+  mhc_post_res         2 X_t + F_out + (H_post, H_res)
+  mhc_post_res_coeffs  mhc_post_res + phi_next + biases + logits + r + H (next layer)
+Split-K partials and the packed copy of phi are implementation traffic and
+are not counted.
 
 Other modes:
   --copy-probe   time a plain device-to-device copy of known size (the
                  reference against which rocprofv3 FETCH_SIZE / WRITE_SIZE are
                  scaled);
-  --kernel-only  run only the timed forward loop (for rocprofv3 runs).
+  --kernel-only  run only the timed headline loop (for rocprofv3 runs).
 """
 
 import argparse
@@ -53,15 +64,18 @@ def product_flops(B, n, C):
 
 
 def path_bytes(B, n, C):
-    """Algorithmic bytes moved by each of the three calls for one forward
-    (bf16 streams, fp32 coefficients and biases)."""
+    """Algorithmic bytes moved by each call for one layer (bf16 streams, fp32
+    coefficients and biases)."""
     N = n * n + 2 * n
     K = n * C
     x = B * K * 2
+    coeff_out = N * 4 + B * N * 4 + B * 4 + B * N * 4   # biases in, logits, H, r out
+    post_res = apply_stream_bytes(B, n, C, 2) + B * (n + n * n) * 4
     return {
-        "mhc_coeffs": x + K * N * 2 + N * 4 + B * N * 4 + B * 4 + B * N * 4,
+        "mhc_coeffs": x + K * N * 2 + coeff_out,
         "mhc_pre": x + B * n * 4 + B * C * 2,
-        "mhc_post_res": apply_stream_bytes(B, n, C, 2) + B * (n + n * n) * 4,
+        "mhc_post_res": post_res,
+        "mhc_post_res_coeffs": post_res + K * N * 2 + coeff_out,
     }
 
 
@@ -70,16 +84,19 @@ def path_flops(B, n, C):
     return product_flops(B, n, C) + B * (2 * n * C + 2 * (n * n + n) * C)
 
 
-# dominant-kernel bookkeeping: kernel symbol substring -> call it belongs to
-KERNEL_OF_CALL = {"mhc_post_res": "post_res_kernel", "mhc_pre": "pre_kernel",
-                  "mhc_coeffs": "gemm_rms_kernel"}
+# kernels launched by each call (for the roofline record)
+KERNELS_OF_CALL = {"mhc_post_res": "post_res_kernel", "mhc_pre": "pre_kernel",
+                   "mhc_coeffs": "pack_phi_kernel + gemm_rms_lds_kernel + coeff_sinkhorn_kernel",
+                   "mhc_post_res_coeffs": "pack_phi_kernel + post_res_next_kernel + coeff_sinkhorn_kernel"}
 
 
 # source files that make up each call's kernels (for the counter-freshness check)
 CALL_SOURCES = {
-    "mhc_coeffs": ("mhc_gemm_rms.hip", "mhc_coeff_sinkhorn.hip", "mhc_device.h"),
+    "mhc_coeffs": ("mhc_gemm_rms.hip", "mhc_gemm_lds.hip", "mhc_coeff_sinkhorn.hip", "mhc_device.h"),
     "mhc_pre": ("mhc_stream.hip", "mhc_device.h"),
     "mhc_post_res": ("mhc_stream.hip", "mhc_device.h"),
+    "mhc_post_res_coeffs": ("mhc_post_res_fused.hip", "mhc_gemm_lds.hip", "mhc_coeff_sinkhorn.hip",
+                            "mhc_device.h"),
 }
 
 
@@ -205,17 +222,79 @@ def main():
     cfg = synth.CONFIGS[args.workload]
     inp = synth.make_config(args.workload, device="cuda")
     B, n, C = inp["B"], inp["n"], inp["C"]
-    out = mhc.alloc_outputs(B, n, C)
+    N = n * n + 2 * n
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    calls = ("mhc_coeffs", "mhc_pre", "mhc_post_res")
 
-    def step(marks=None):
+    # The CPU baseline samples the input before the chained loop overwrites it.
+    cpu = None
+    if not args.no_cpu_baseline and not args.kernel_only:
+        cpu = _cpu_baseline(inp, args.cpu_rows, args.cpu_budget_s)
+
+    # ---- headline: per-layer pipeline, residual stream chained through layers
+    X = [inp["X"], torch.empty_like(inp["X"])]
+    Hs = [torch.empty(B, N, device="cuda") for _ in range(2)]
+    logits = torch.empty(B, N, device="cuda")
+    r = torch.empty(B, device="cuda")
+    F_pre = torch.empty(B, C, dtype=torch.bfloat16, device="cuda")
+    ws_c = torch.empty(max(mhc.mhc_coeffs_workspace_size(B, n, C), 16), dtype=torch.uint8, device="cuda")
+    ws_f = torch.empty(max(mhc.mhc_post_res_coeffs_workspace_size(B, n, C), 16), dtype=torch.uint8,
+                       device="cuda")
+    ab = (inp["alpha_pre"], inp["alpha_post"], inp["alpha_res"], inp["b_pre"], inp["b_post"], inp["b_res"])
+    mhc.mhc_coeffs(B, n, C, X[0], inp["phi"], *ab, logits, r, Hs[0], ws_c, stream=stream)
+    cur = [0]
+
+    def layer(marks=None):
+        a = cur[0]
         if marks is not None:
             marks[0].record(stream)
-        mhc.mhc_coeffs(B, n, C, inp["X"], inp["phi"], inp["alpha_pre"], inp["alpha_post"],
-                       inp["alpha_res"], inp["b_pre"], inp["b_post"], inp["b_res"],
-                       out["logits"], out["r"], out["H"], out["workspace"], stream=stream)
+        mhc.mhc_pre(B, n, C, X[a], Hs[a], F_pre, stream=stream)
+        if marks is not None:
+            marks[1].record(stream)
+        mhc.mhc_post_res_coeffs(B, n, C, X[a], inp["F_out"], Hs[a], X[1 - a], inp["phi"], *ab,
+                                logits, r, Hs[1 - a], ws_f, stream=stream)
+        if marks is not None:
+            marks[2].record(stream)
+        cur[0] = 1 - a
+
+    for _ in range(args.warmup):
+        layer()
+    torch.cuda.synchronize()
+    # Timed region 1 (the headline number): K back-to-back layers bracketed by
+    # two events and a device synchronisation on both sides; no event sits
+    # between calls (each recorded event idles the stream a few microseconds).
+    t0, t1 = ev(), ev()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(args.steps):
+        layer()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    if args.kernel_only:
+        print(json.dumps({"kernel_only": True, "steps": args.steps}), flush=True)
+        return
+    ms_step = t0.elapsed_time(t1) / args.steps
+
+    # Timed region 2: the same layers with an event before and after each call
+    # (per-call durations, on the stream the kernels run on).
+    marks = [[ev() for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        layer(marks[k])
+    torch.cuda.synchronize()
+    pipe_calls = ("mhc_pre", "mhc_post_res_coeffs")
+    per_call_ms = {c: sum(marks[k][i].elapsed_time(marks[k][i + 1]) for k in range(args.steps)) / args.steps
+                   for i, c in enumerate(pipe_calls)}
+
+    # Timed region 3: the three separate calls on a fixed X_t.
+    out = mhc.alloc_outputs(B, n, C)
+
+    def three(marks=None):
+        if marks is not None:
+            marks[0].record(stream)
+        mhc.mhc_coeffs(B, n, C, inp["X"], inp["phi"], *ab, out["logits"], out["r"], out["H"],
+                       out["workspace"], stream=stream)
         if marks is not None:
             marks[1].record(stream)
         mhc.mhc_pre(B, n, C, inp["X"], out["H"], out["F_pre"], stream=stream)
@@ -226,55 +305,36 @@ def main():
             marks[3].record(stream)
 
     for _ in range(args.warmup):
-        step()
+        three()
     torch.cuda.synchronize()
-
-    # Timed region 1 (the headline number): K back-to-back steps bracketed by
-    # two events and a device synchronisation on both sides.  No event sits
-    # between the calls, since every recorded event costs the stream a few
-    # microseconds of idle time.
-    t_start, t_end = ev(), ev()
+    t2, t3 = ev(), ev()
+    t2.record(stream)
+    for _ in range(args.steps):
+        three()
+    t3.record(stream)
     torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
+    ms_three = t2.elapsed_time(t3) / args.steps
+    marks3 = [[ev() for _ in range(4)] for _ in range(args.steps)]
     for k in range(args.steps):
-        step()
-    t_end.record(stream)
+        three(marks3[k])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    if args.kernel_only:
-        print(json.dumps({"kernel_only": True, "steps": args.steps}), flush=True)
-        return
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / args.steps
+    three_calls = ("mhc_coeffs", "mhc_pre", "mhc_post_res")
+    per_call3 = {c: sum(marks3[k][i].elapsed_time(marks3[k][i + 1]) for k in range(args.steps)) / args.steps
+                 for i, c in enumerate(three_calls)}
 
-    # Timed region 2 (per-call breakdown and the dominant kernel's launch
-    # duration): the same K steps with an event before and after every call,
-    # all on the stream the kernels are launched on.
-    marks = [[ev() for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for k in range(args.steps):
-        step(marks[k])
-    torch.cuda.synchronize()
-    per_call_ms = {c: sum(marks[k][i].elapsed_time(marks[k][i + 1]) for k in range(args.steps)) / args.steps
-                   for i, c in enumerate(calls)}
     bytes_call = path_bytes(B, n, C)
-    total_bytes = sum(bytes_call.values())
-    gbps = total_bytes / (ms_step * 1e-3) / 1e9
+    pipe_bytes = bytes_call["mhc_pre"] + bytes_call["mhc_post_res_coeffs"]
+    three_bytes = sum(bytes_call[c] for c in three_calls)
+    gbps = pipe_bytes / (ms_step * 1e-3) / 1e9
     tokens_per_s = B / (ms_step * 1e-3)
 
-    dom = max(calls, key=lambda c: per_call_ms[c])
+    dom = max(pipe_calls, key=lambda c: per_call_ms[c])
     dom_gbps = bytes_call[dom] / (per_call_ms[dom] * 1e-3) / 1e9
-    traffic = _recorded_traffic(dom, args.workload)
-    roofline = {"bound": "hbm", "kernel": KERNEL_OF_CALL[dom], "call": dom,
+    roofline = {"bound": "hbm", "call": dom, "kernel": KERNELS_OF_CALL[dom],
                 "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": _recorded_traffic(dom, args.workload),
                 "algorithmic_bytes_per_launch": bytes_call[dom],
                 "avg_launch_us": round(per_call_ms[dom] * 1e3, 2)}
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = _cpu_baseline(inp, args.cpu_rows, args.cpu_budget_s)
 
     line = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -283,18 +343,23 @@ def main():
         "data": "synthetic (seeded; X Student-t(4) for the large workload)",
         "config": {"workload": f"{args.workload}: n={n} C={C} B={B}", "n": n, "C": C, "B": B,
                    "x_dist": cfg["x_dist"], "seed": cfg["seed"],
-                   "split_k": mhc.mhc_coeffs_split_k(B, n, C)},
+                   "path": "per layer: mhc_pre + mhc_post_res_coeffs (mhc_coeffs once before the loop)"},
         "hbm_gbps": round(gbps, 1), "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
-        "algorithmic_bytes_per_step": total_bytes,
+        "algorithmic_bytes_per_step": pipe_bytes,
+        "three_call_equivalent_gbps": round(three_bytes / (ms_step * 1e-3) / 1e9, 1),
         "per_call_us": {c: round(v * 1e3, 2) for c, v in per_call_ms.items()},
-        "per_call_gbps": {c: round(bytes_call[c] / (per_call_ms[c] * 1e-3) / 1e9, 1) for c in calls},
+        "per_call_gbps": {c: round(bytes_call[c] / (per_call_ms[c] * 1e-3) / 1e9, 1) for c in pipe_calls},
+        "three_call": {"ms_per_step": round(ms_three, 5), "tokens_per_s": round(B / (ms_three * 1e-3), 1),
+                       "hbm_gbps": round(three_bytes / (ms_three * 1e-3) / 1e9, 1),
+                       "algorithmic_bytes_per_step": three_bytes,
+                       "per_call_us": {c: round(v * 1e3, 2) for c, v in per_call3.items()},
+                       "split_k": mhc.mhc_coeffs_split_k(B, n, C)},
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "kernel_source_sha": {c: kernel_source_sha(c) for c in calls},
+        "kernel_source_sha": {c: kernel_source_sha(c) for c in CALL_SOURCES},
     }
     print(json.dumps(line), flush=True)
-
 
 if __name__ == "__main__":
     main()

@@ -14,6 +14,8 @@
  *
  * Between mhc_pre and mhc_post_res the caller runs its own layer F
  * (attention / FFN) to turn F_pre into F_out; that layer is not part of mHC.
+ * mhc_post_res_coeffs fuses a layer's apply with the next layer's
+ * coefficients (one pass over the residual stream instead of two).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -133,6 +135,35 @@ int mhc_pre(int64_t B, int32_t n, int64_t C, const void *X_t, const float *H,
  *   X_next  out bf16 [B, n*C]; must not overlap X_t */
 int mhc_post_res(int64_t B, int32_t n, int64_t C, const void *X_t,
                  const void *F_out, const float *H, void *X_next, void *stream);
+
+/* Step (4b) of this layer fused with steps (1)-(3) of the next one.
+ *
+ * The apply of [mHC-cutile] sections 2.5 and 3.4 writes X_next, which is the
+ * next layer's input X_t; section 2.1 then begins the next layer with the
+ * product X_next . phi_next (and section 2.2 with the row sums of X_next^2).
+ * This call performs both in one pass over the residual stream, so X_next is
+ * written once and never read back for the next layer's coefficients:
+ *
+ *   X_next       = exactly what mhc_post_res(X_t, F_out, H) writes (bitwise);
+ *   logits_next, r_next, H_next
+ *                = what mhc_coeffs(X_next, phi_next, alpha_*, b_*) computes,
+ *                  up to fp32 summation order (deterministic, no atomics).
+ *
+ * A model runs mhc_coeffs once for its first layer and then, per layer,
+ * mhc_pre, its layer F, and this call.  Arguments as in mhc_post_res
+ * (X_t, F_out, H, X_next) and mhc_coeffs (phi_next, alpha_*, b_*, logits_next,
+ * r_next, H_next, workspace).  Additionally requires C % 32 == 0
+ * (else MHC_ERR_UNSUPPORTED); the workspace must hold
+ * mhc_post_res_coeffs_workspace_size(B, n, C) bytes. */
+size_t mhc_post_res_coeffs_workspace_size(int64_t B, int32_t n, int64_t C);
+
+int mhc_post_res_coeffs(int64_t B, int32_t n, int64_t C,
+                        const void *X_t, const void *F_out, const float *H, void *X_next,
+                        const void *phi_next,
+                        float alpha_pre, float alpha_post, float alpha_res,
+                        const float *b_pre, const float *b_post, const float *b_res,
+                        float *logits_next, float *r_next, float *H_next,
+                        void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,8 @@ MHC_ERR_HIP = 4
 MHC_SINKHORN_ITERS = 20
 
 EXPORTED = ("mhc_status_string", "mhc_coeffs_workspace_size", "mhc_coeffs_split_k",
-            "mhc_coeffs", "mhc_pre", "mhc_post_res")
+            "mhc_coeffs", "mhc_pre", "mhc_post_res", "mhc_post_res_coeffs_workspace_size",
+            "mhc_post_res_coeffs")
 
 _lib = None
 
@@ -53,6 +54,11 @@ def load():
     lib.mhc_pre.restype = ctypes.c_int
     lib.mhc_post_res.argtypes = [i64, i32, i64, vp, vp, vp, vp, vp]
     lib.mhc_post_res.restype = ctypes.c_int
+    lib.mhc_post_res_coeffs_workspace_size.argtypes = [i64, i32, i64]
+    lib.mhc_post_res_coeffs_workspace_size.restype = sz
+    lib.mhc_post_res_coeffs.argtypes = [i64, i32, i64, vp, vp, vp, vp, vp, f32, f32, f32,
+                                        vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.mhc_post_res_coeffs.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -123,6 +129,26 @@ def mhc_post_res(B, n, C, X_t, F_out, H, X_next, stream=None, check=True):
                              _ptr(X_next), _stream(stream))
     if check:
         _check(st, "mhc_post_res")
+    return st
+
+
+def mhc_post_res_coeffs_workspace_size(B, n, C):
+    return int(load().mhc_post_res_coeffs_workspace_size(int(B), int(n), int(C)))
+
+
+def mhc_post_res_coeffs(B, n, C, X_t, F_out, H, X_next, phi_next, alpha_pre, alpha_post,
+                        alpha_res, b_pre, b_post, b_res, logits_next, r_next, H_next, workspace,
+                        workspace_bytes=None, stream=None, check=True):
+    """Step (4b) of this layer fused with steps (1)-(3) of the next (see include/mhc.h)."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().mhc_post_res_coeffs(int(B), int(n), int(C), _ptr(X_t), _ptr(F_out), _ptr(H),
+                                    _ptr(X_next), _ptr(phi_next), float(alpha_pre),
+                                    float(alpha_post), float(alpha_res), _ptr(b_pre), _ptr(b_post),
+                                    _ptr(b_res), _ptr(logits_next), _ptr(r_next), _ptr(H_next),
+                                    _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if check:
+        _check(st, "mhc_post_res_coeffs")
     return st
 
 

@@ -137,4 +137,51 @@ int mhc_post_res(int64_t B, int32_t n, int64_t C, const void *X_t, const void *F
                                        static_cast<hipStream_t>(stream)));
 }
 
+size_t mhc_post_res_coeffs_workspace_size(int64_t B, int32_t n, int64_t C) {
+  if (check_shape(B, n, C) != MHC_OK || B == 0 || C % 32 != 0) return 0;
+  return mhc::plan_post_res_next(B, n, C).total_bytes;
+}
+
+int mhc_post_res_coeffs(int64_t B, int32_t n, int64_t C, const void *X_t, const void *F_out,
+                        const float *H, void *X_next, const void *phi_next, float alpha_pre,
+                        float alpha_post, float alpha_res, const float *b_pre, const float *b_post,
+                        const float *b_res, float *logits_next, float *r_next, float *H_next,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_shape(B, n, C);
+  if (st != MHC_OK) return st;
+  if (C % 32 != 0) return MHC_ERR_UNSUPPORTED;
+  if (B == 0) return MHC_OK;
+  if (!X_t || !F_out || !H || !X_next || !phi_next || !b_pre || !b_post || !b_res ||
+      !logits_next || !r_next || !H_next || !workspace)
+    return MHC_ERR_INVALID_ARG;
+  if (!aligned(X_t, 16) || !aligned(F_out, 16) || !aligned(X_next, 16) || !aligned(phi_next, 16) ||
+      !aligned(workspace, 16) || !aligned(H, 4) || !aligned(b_pre, 4) || !aligned(b_post, 4) ||
+      !aligned(b_res, 4) || !aligned(logits_next, 4) || !aligned(r_next, 4) || !aligned(H_next, 4))
+    return MHC_ERR_UNSUPPORTED;
+  const mhc::FusedPlan plan = mhc::plan_post_res_next(B, n, C);
+  const int64_t N = ncoef(n), K = (int64_t)n * C;
+  const Span in[] = {span(X_t, (size_t)B * K * 2), span(F_out, (size_t)B * C * 2),
+                     span(H, (size_t)B * N * 4), span(phi_next, (size_t)K * N * 2),
+                     span(b_pre, (size_t)n * 4), span(b_post, (size_t)n * 4),
+                     span(b_res, (size_t)n * n * 4)};
+  const Span out[] = {span(X_next, (size_t)B * K * 2), span(logits_next, (size_t)B * N * 4),
+                      span(r_next, (size_t)B * 4), span(H_next, (size_t)B * N * 4),
+                      span(workspace, plan.total_bytes)};
+  for (const Span &o : out)
+    for (const Span &i : in)
+      if (overlaps(o, i)) return MHC_ERR_INVALID_ARG;
+  for (int a = 0; a < 5; ++a)
+    for (int b = a + 1; b < 5; ++b)
+      if (overlaps(out[a], out[b])) return MHC_ERR_INVALID_ARG;
+  if (workspace_bytes < plan.total_bytes) return MHC_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = from_hip(mhc::launch_post_res_next(plan, n, B, C, X_t, F_out, H, X_next, phi_next,
+                                          workspace, s));
+  if (st != MHC_OK) return st;
+  return from_hip(mhc::launch_coeff_sinkhorn(n, B, C, plan.split, static_cast<const float *>(workspace),
+                                             alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res,
+                                             logits_next, r_next, H_next, s));
+}
+
 }  // extern "C"

@@ -244,14 +244,31 @@ hipError_t launch_gemm_lds_typed(const GemmPlan &p, int64_t B, int64_t C, const 
   char *base = static_cast<char *>(ws_base);
   uint16_t *phip = reinterpret_cast<uint16_t *>(base + p.phip_offset);
   uint16_t *zero = reinterpret_cast<uint16_t *>(base + p.zero_offset);
-  const int ksteps = (int)(p.phip_bytes / ((size_t)L::NB * 1024));
-  const int64_t vecs = (int64_t)ksteps * L::NB * 64;
-  pack_phi_kernel<NS><<<dim3((uint32_t)((vecs + 255) / 256)), 256, 0, st>>>(
-      static_cast<const uint16_t *>(phi), phip, zero, K, ksteps);
+  const int64_t ksteps = (int64_t)(p.phip_bytes / ((size_t)L::NB * 1024));
+  hipError_t e = launch_pack_phi(NS, K, ksteps, phi, phip, zero, st);
+  if (e != hipSuccess) return e;
   const dim3 grid((uint32_t)p.row_tiles, (uint32_t)p.split);
   gemm_rms_lds_kernel<NS, MB, KC, STAGES><<<grid, 256, 0, st>>>(
       static_cast<const uint16_t *>(X), phip, zero, reinterpret_cast<float *>(base), (int)B, K,
       (int)p.kslice);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_phi(int n, int64_t K, int64_t ksteps, const void *phi, void *phip,
+                           void *zero, hipStream_t st) {
+  const int N = n * n + 2 * n;
+  const int NB = (N + 15) / 16;
+  const int64_t vecs = ksteps * NB * 64;
+  const dim3 grid((uint32_t)((vecs + 255) / 256));
+  const uint16_t *src = static_cast<const uint16_t *>(phi);
+  uint16_t *dst = static_cast<uint16_t *>(phip), *z = static_cast<uint16_t *>(zero);
+  switch (n) {
+    case 1: pack_phi_kernel<1><<<grid, 256, 0, st>>>(src, dst, z, (int)K, (int)ksteps); break;
+    case 2: pack_phi_kernel<2><<<grid, 256, 0, st>>>(src, dst, z, (int)K, (int)ksteps); break;
+    case 4: pack_phi_kernel<4><<<grid, 256, 0, st>>>(src, dst, z, (int)K, (int)ksteps); break;
+    case 8: pack_phi_kernel<8><<<grid, 256, 0, st>>>(src, dst, z, (int)K, (int)ksteps); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

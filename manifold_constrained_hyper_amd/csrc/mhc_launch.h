@@ -39,6 +39,27 @@ hipError_t launch_gemm_lds_typed(const GemmPlan &p, int64_t B, int64_t C, const 
 hipError_t launch_gemm_rms(const GemmPlan &p, int n, int64_t B, int64_t C,
                            const void *X, const void *phi, float *ws, hipStream_t st);
 
+// phi [K, N] -> packed MFMA B operands ([ksteps][NB][64 lanes][8] bf16, zero
+// past K and past N) plus a 256-byte zero block.
+hipError_t launch_pack_phi(int n, int64_t K, int64_t ksteps, const void *phi, void *phip,
+                           void *zero, hipStream_t st);
+
+// Fused apply of this layer + coefficient product of the next (one pass).
+//
+// Workspace layout: [0, partial_bytes) fp32 partials [split, B, N+1];
+// [phip_offset, +phip_bytes) packed phi of the next layer; [zero_offset, +256).
+struct FusedPlan {
+  int split;          // channel slices (K-slices of n*cw)
+  int cw;             // channels per slice (multiple of 512)
+  int64_t row_tiles;  // 16-row tiles
+  int64_t ksteps;     // packed phi 32-k steps
+  size_t partial_bytes, phip_offset, phip_bytes, zero_offset, total_bytes;
+};
+FusedPlan plan_post_res_next(int64_t B, int n, int64_t C);
+hipError_t launch_post_res_next(const FusedPlan &p, int n, int64_t B, int64_t C, const void *X,
+                                const void *F, const float *H, void *Y, const void *phi_next,
+                                void *ws_base, hipStream_t st);
+
 hipError_t launch_coeff_sinkhorn(int n, int64_t B, int64_t C, int split, const float *ws,
                                  float alpha_pre, float alpha_post, float alpha_res,
                                  const float *b_pre, const float *b_post, const float *b_res,

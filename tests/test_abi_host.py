@@ -110,6 +110,33 @@ def test_pre_and_post_res_validation():
     assert mhc.mhc_post_res(-3, 4, 64, X, F, H, Y, stream=0, check=False) == mhc.MHC_ERR_INVALID_ARG
 
 
+def _fused(B=16, n=4, C=64, ws_bytes=None, **over):
+    names = ["X", "F", "H", "Y", "phi", "bp", "bq", "br", "logits", "r", "Hn", "ws"]
+    p = dict(zip(names, _addrs(len(names))))
+    p.update(over)
+    if ws_bytes is None:
+        ws_bytes = max(mhc.mhc_post_res_coeffs_workspace_size(B, n, C), 16)
+    return mhc.mhc_post_res_coeffs(B, n, C, p["X"], p["F"], p["H"], p["Y"], p["phi"], 0.01, 0.01,
+                                   0.01, p["bp"], p["bq"], p["br"], p["logits"], p["r"], p["Hn"],
+                                   p["ws"], ws_bytes, stream=0, check=False)
+
+
+def test_fused_validation():
+    assert _fused(B=0) == mhc.MHC_OK
+    assert _fused(C=40) == mhc.MHC_ERR_UNSUPPORTED                     # needs C % 32 == 0
+    assert mhc.mhc_post_res_coeffs_workspace_size(16, 4, 40) == 0
+    assert _fused(n=3) == mhc.MHC_ERR_UNSUPPORTED
+    assert _fused(B=-2) == mhc.MHC_ERR_INVALID_ARG
+    for k in ("X", "F", "H", "Y", "phi", "bp", "bq", "br", "logits", "r", "Hn", "ws"):
+        assert _fused(**{k: None}) == mhc.MHC_ERR_INVALID_ARG, k
+    assert _fused(Y=A) == mhc.MHC_ERR_INVALID_ARG                      # X_next overlaps X_t
+    assert _fused(Hn=A + 2 * STEP) == mhc.MHC_ERR_INVALID_ARG          # H_next overlaps H
+    assert _fused(ws=A + 3 * STEP) == mhc.MHC_ERR_INVALID_ARG          # workspace overlaps X_next
+    assert _fused(phi=A + 4 * STEP + 8) == mhc.MHC_ERR_UNSUPPORTED
+    need = mhc.mhc_post_res_coeffs_workspace_size(16, 4, 64)
+    assert need > 0 and _fused(ws_bytes=need - 1) == mhc.MHC_ERR_WORKSPACE
+
+
 def test_binding_raises_on_error_status():
     with pytest.raises(mhc.MhcError) as ei:
         mhc.mhc_pre(16, 3, 64, *_addrs(3), stream=0)

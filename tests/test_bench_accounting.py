@@ -47,8 +47,12 @@ def test_scale_sigmoid_bytes_convention_matches_page():
 
 def test_path_bytes_large_workload():
     b = bench.path_bytes(16384, 4, 7168)
-    assert b == {"mhc_coeffs": 944111712, "mhc_pre": 1174667264, "mhc_post_res": 2115239936}
-    assert sum(b.values()) == 4234018912
+    assert (b["mhc_coeffs"], b["mhc_pre"], b["mhc_post_res"]) == (944111712, 1174667264, 2115239936)
+    assert b["mhc_coeffs"] + b["mhc_pre"] + b["mhc_post_res"] == 4234018912
+    # the fused call moves the apply's bytes plus the next layer's coefficient
+    # inputs/outputs, but not X_next a second time
+    assert b["mhc_post_res_coeffs"] == b["mhc_post_res"] + (b["mhc_coeffs"] - 16384 * 4 * 7168 * 2)
+    assert b["mhc_pre"] + b["mhc_post_res_coeffs"] == 3294494816
     # post_res = page's apply convention at bf16 + the fp32 coefficients it reads
     assert b["mhc_post_res"] == bench.apply_stream_bytes(16384, 4, 7168, 2) + 16384 * 20 * 4
 
