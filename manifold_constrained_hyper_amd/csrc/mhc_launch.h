@@ -53,7 +53,7 @@ struct FusedPlan {
   int cw;             // channels per slice (multiple of 512)
   int64_t row_tiles;  // 16-row tiles
   int64_t ksteps;     // packed phi 32-k steps
-  size_t partial_bytes, phip_offset, phip_bytes, zero_offset, total_bytes;
+  size_t partial_bytes, dummy_offset, dummy_bytes, phip_offset, phip_bytes, zero_offset, total_bytes;
 };
 FusedPlan plan_post_res_next(int64_t B, int n, int64_t C);
 hipError_t launch_post_res_next(const FusedPlan &p, int n, int64_t B, int64_t C, const void *X,

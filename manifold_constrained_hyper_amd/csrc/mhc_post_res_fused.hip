@@ -9,9 +9,21 @@
 // read back for the product.  Per layer this removes one full read of the
 // residual stream from HBM.
 //
-// A workgroup is 16 waves and owns a tile of 16 rows; it walks the hidden
-// dimension in steps of 512 channels (its K-slice: a channel range of all n
-// streams).  Per step:
+// Work decomposition.  A unit is a 16-row tile times a slice of `spu`
+// consecutive 512-channel steps (all n streams of those channels); the S
+// slices of a row range cover the hidden size, and unit u is (tile u / S,
+// slice u % S).  A persistent grid of G 16-wave workgroups (one per CU)
+// takes units round-robin: round j of workgroup g is unit j*G + p(g), where
+// p deals each XCD (workgroups are dispatched to the 8 XCDs in turn) a
+// contiguous run of units.  At any moment the workgroups are thus working on
+// about G consecutive units, i.e. G/S consecutive row tiles: the set of HBM
+// pages being streamed stays as compact as in a plain row-major elementwise
+// pass.  (With one workgroup per tile sweeping its whole hidden size, 256
+// tiles spread over hundreds of MiB are live at once, and the same traffic
+// runs about 20 % slower on MI355X.)
+//
+// Per step (512 channels of one unit), with the loads two steps ahead
+// (one step ahead for n = 8, where two register sets do not fit):
 //   apply    wave w computes row w of the tile exactly like post_res_kernel
 //            (one 16-byte vector = 8 channels per lane and stream, 1 KiB
 //            contiguous per load/store instruction), stores X_{t+1} to HBM
@@ -22,11 +34,17 @@
 //            are split over the 16 waves; each reads its A operands (16 rows x
 //            8 channels per lane) from LDS and its B operands from the packed
 //            copy of phi_{t+1} (see mhc_gemm_lds.hip) and accumulates
-//            v_mfma_f32_16x16x32_bf16 plus the Gram block for sum of squares.
-// The loads of step c+1 are issued before the product of step c.  At the end
-// the 16 waves' accumulators are summed through LDS in wave order (fixed:
-// deterministic) into the workspace partials fp32 [S, B, N+1], which the
-// combine kernel turns into the next layer's logits, r and H.
+//            v_mfma_f32_16x16x32_bf16 plus the Gram block for sum of squares;
+//   flush    the 16 waves' accumulators are summed through LDS in wave order
+//            (fixed: deterministic) into the unit's partials fp32 [S, B, N+1]
+//            of the workspace, which the combine kernel turns into the next
+//            layer's logits, r and H.  Every step rewrites its unit's running
+//            sum (same thread, same address), so the last write is the unit's
+//            total and no memory operation depends on a branch.
+// Every wave issues the same memory operations on every step (out-of-range
+// lanes and rows use clamped addresses; stores that have no target go to a
+// dummy workspace area), which keeps the compiler's memory-counter waits
+// exact: the apply of step s waits only for the loads of step s.
 //
 // The apply arithmetic is that of post_res_kernel (fp32 FMA chain from
 // H_post * F_out, one round-to-nearest-even to bf16), so X_{t+1} is bitwise
@@ -35,11 +53,15 @@
 #include "mhc_device.h"
 #include "mhc_launch.h"
 
+#include <atomic>
+#include <cstdlib>
+
 namespace mhc {
 
 namespace {
 
-constexpr int kStepCh = 512;  // channels per step: 64 lanes x 8
+constexpr int kStepCh = 512;          // channels per step: 64 lanes x 8
+constexpr int kLdsMax = 160 * 1024;   // LDS of one CU
 
 template <int NS>
 struct FusedTile {
@@ -47,47 +69,56 @@ struct FusedTile {
   static constexpr int NP = N + 1;
   static constexpr int NB = (N + 15) / 16;
   static constexpr int ROW_BYTES = NS * kStepCh * 2;   // one tile row in LDS
-  static constexpr int LDS_BYTES = 16 * ROW_BYTES;     // 64 KiB at n=4, 128 KiB at n=8
+  static constexpr int TILE_BYTES = 16 * ROW_BYTES;    // 64 KiB at n=4, 128 KiB at n=8
   static constexpr int KSTEPS = 16 * NS;               // 32-channel MFMA steps per step
   static constexpr int KPW = KSTEPS / 16;              // ... per wave (= NS)
   static constexpr int KB = NS >= 8 ? 2 : (KPW < 4 ? KPW : 4);  // k-steps whose B operands are held at once
-  static_assert(16 * 16 * NP * 4 <= LDS_BYTES, "reduction scratch fits in the tile buffer");
+  static constexpr int NH = NS + NS * NS;              // H_post and H_res of one row
+  static constexpr int HV = (NH + 63) / 64;            // dwords per lane that hold them
+  static constexpr int RS = NB * 16 + 1;               // reduction row stride; Gram sum at NB*16
+  static constexpr int RED_BYTES = 16 * 16 * RS * 4;   // [16 waves][16 rows][RS] fp32
+  // The reduction buffer sits beside the tile when both fit (then the flush
+  // of step s-1 overlaps step s); otherwise it reuses the tile buffer.
+  static constexpr bool SEPARATE = TILE_BYTES + RED_BYTES <= kLdsMax;
+  static constexpr int LDS_BYTES = SEPARATE ? TILE_BYTES + RED_BYTES
+                                            : (TILE_BYTES > RED_BYTES ? TILE_BYTES : RED_BYTES);
+  static constexpr int OPT = (16 * NP + 1023) / 1024;  // flushed sums per thread
+  static_assert(LDS_BYTES <= kLdsMax, "LDS budget");
+};
+
+struct Step {
+  int row0, c0, c_end, slot;
 };
 
 template <int NS>
 __global__ __launch_bounds__(1024) void post_res_next_kernel(
     const uint16_t *__restrict__ X, const uint16_t *__restrict__ F, const float *__restrict__ H,
-    uint16_t *__restrict__ Y, const uint16_t *__restrict__ phip, float *__restrict__ ws, int B,
-    int C, int cw) {
+    uint16_t *__restrict__ Y, const uint16_t *__restrict__ phip, float *__restrict__ ws,
+    float *__restrict__ dummy, int B, int C, int spu, int S, int U) {
   using T = FusedTile<NS>;
   __shared__ __attribute__((aligned(1024))) char lds[T::LDS_BYTES];
+  float *red = reinterpret_cast<float *>(lds + (T::SEPARATE ? T::TILE_BYTES : 0));
 
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = uniform(tid >> 6);
   const int lane = tid & 63;
   const int m = lane & 15, g = lane >> 4;
-  const int s = blockIdx.y;
-  const int c_begin = s * cw;
-  const int c_end = min(C, c_begin + cw);
-  const int row0 = blockIdx.x * 16;
+  const int cw = spu * kStepCh;
 
-  // apply role: wave `wave` owns tile row `wave`
-  const int my_row = row0 + wave;
-  const bool live = my_row < B;
-  const int rr = uniform(min(my_row, B - 1));
-  const uint16_t *xr = X + (size_t)rr * NS * C;
-  const uint16_t *fr = F + (size_t)rr * C;
-  uint16_t *yr = Y + (size_t)rr * NS * C;
-  float hpost[NS], hres[NS][NS];
-  {
-    const float *h = H + (size_t)rr * T::N;
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      hpost[i] = h[NS + i];
-#pragma unroll
-      for (int j = 0; j < NS; ++j) hres[i][j] = h[2 * NS + i * NS + j];
-    }
-  }
+  // This workgroup's units: p(g) + j*G, j = 0, 1, ...
+  const int G = gridDim.x, gi = blockIdx.x;
+  const int pg = (gi & 7) * (G >> 3) + min(gi & 7, G & 7) + (gi >> 3);
+  if (pg >= U) return;
+  const int nsteps = ((U - pg + G - 1) / G) * spu;
+
+  auto step_at = [&](int t) {
+    const int j = t / spu, p = t - j * spu;
+    const int u = j * G + pg;
+    const int tile = u / S, s = u - tile * S;
+    const int cb = s * cw;
+    return Step{uniform(tile * 16), uniform(cb + p * kStepCh), uniform(min(C, cb + cw)), uniform(s)};
+  };
+
   char *my_lds_row = lds + wave * T::ROW_BYTES;
   const int wslot = (lane ^ (wave & 15)) * 16;  // swizzled 16-byte slot of this lane
 
@@ -96,86 +127,167 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
 #pragma unroll
   for (int nb = 0; nb < T::NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Loads of one step.  Lanes past the range read an in-range address
-  // instead (their values are never stored and enter the tile as zeros), so
-  // every wave issues the same loads on every step and the waits before the
-  // product only ever cover the operand loads, never the prefetch.
-  u32x4 xv[NS], fv;
-  auto load_step = [&](int c0) {
-    const int c = min(c0 + 8 * lane, c_end - 8);
+  // Loads of one step: this wave's row of X_t and F_out and the row's
+  // H_post / H_res (lane k holds coefficient k).  Lanes past the slice, and
+  // rows past B, read the nearest in-range address instead: they then
+  // compute exactly the values the owning lane writes, so their (duplicate)
+  // stores rewrite identical bytes, and they enter the LDS tile as zeros.
+  auto load_set = [&](u32x4 (&xv)[NS], u32x4 &fv, uint32_t (&hv)[T::HV], const Step &sp) {
+    const int rr = uniform(min(sp.row0 + wave, B - 1));
+    const float *hr = H + (size_t)rr * T::N + NS;
+#pragma unroll
+    for (int k = 0; k < T::HV; ++k) hv[k] = __builtin_bit_cast(uint32_t, hr[min(k * 64 + lane, T::NH - 1)]);
+    const int c = min(sp.c0 + 8 * lane, sp.c_end - 8);
+    const uint16_t *xr = X + (size_t)rr * NS * C;
 #pragma unroll
     for (int j = 0; j < NS; ++j)
       xv[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xr + (size_t)j * C + c));
-    fv = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(fr + c));
+    fv = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(F + (size_t)rr * C + c));
   };
 
-  load_step(c_begin);
-  for (int c0 = c_begin; c0 < c_end; c0 += kStepCh) {
-    const int c = c0 + 8 * lane;
-    // apply (row `wave`, channels c .. c+7 of every stream)
+  // Sum the 16 waves' accumulators of step `sp` (in wave order) into its
+  // unit's partials.  Threads without a target write the dummy area.
+  auto flush = [&](const Step &sp) {
+#pragma unroll
+    for (int q = 0; q < T::OPT; ++q) {
+      const int e = tid + q * 1024;
+      const int ec = min(e, 16 * T::NP - 1);
+      const int r = ec / T::NP, col = ec - r * T::NP;
+      const int rcol = col < T::N ? col : T::NB * 16;
+      float a = 0.f;
+#pragma unroll
+      for (int w = 0; w < 16; ++w) a += red[(w * 16 + r) * T::RS + rcol];
+      const int row = sp.row0 + r;
+      float *dst = (e < 16 * T::NP && row < B) ? ws + ((size_t)sp.slot * B + row) * T::NP + col
+                                               : dummy + e;
+      *dst = a;
+    }
+  };
+
+  auto write_red = [&]() {
+    float *rw = red + wave * 16 * T::RS;
+#pragma unroll
+    for (int nb = 0; nb < T::NB; ++nb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) rw[(4 * g + v) * T::RS + nb * 16 + m] = acc[nb][v];
+    if (g == (m >> 2)) rw[m * T::RS + T::NB * 16] = gram[m & 3];
+  };
+
+  // One step on the loads in (xv, fv, hv); refills them with step t_pref.
+  auto step = [&](int t, u32x4 (&xv)[NS], u32x4 &fv, uint32_t (&hv)[T::HV], int t_pref) {
+    const Step sp = step_at(t);
+    const int row = sp.row0 + wave;
+    const bool live = row < B;
+    const int rr = uniform(min(row, B - 1));
+    const int c = sp.c0 + 8 * lane;
+    const bool in_range = c < sp.c_end;
+    const int cst = min(c, sp.c_end - 8);
+
+    // apply (row `rr`, channels c .. c+7 of every stream); the coefficients
+    // are broadcast from the lanes of hv.
+    auto coef = [&](int k) {
+      return __builtin_bit_cast(float, __builtin_amdgcn_readlane((int)hv[k / 64], k % 64));
+    };
     u32x4 out[NS];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float f0 = bf16_lo(fv[w]), f1 = bf16_hi(fv[w]);
-      float x0[NS], x1[NS];
-#pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        x0[j] = bf16_lo(xv[j][w]);
-        x1[j] = bf16_hi(xv[j][w]);
-      }
+    if constexpr (NS <= 4) {
+      float hpost[NS], hres[NS][NS];
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
-        float a0 = hpost[i] * f0, a1 = hpost[i] * f1;
+        hpost[i] = coef(i);
+#pragma unroll
+        for (int j = 0; j < NS; ++j) hres[i][j] = coef(NS + i * NS + j);
+      }
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f0 = bf16_lo(fv[w]), f1 = bf16_hi(fv[w]);
+        float x0[NS], x1[NS];
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-          a0 = fmaf(hres[i][j], x0[j], a0);
-          a1 = fmaf(hres[i][j], x1[j], a1);
+          x0[j] = bf16_lo(xv[j][w]);
+          x1[j] = bf16_hi(xv[j][w]);
         }
-        out[i][w] = pack_bf16x2(a0, a1);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          float a0 = hpost[i] * f0, a1 = hpost[i] * f1;
+#pragma unroll
+          for (int j = 0; j < NS; ++j) {
+            a0 = fmaf(hres[i][j], x0[j], a0);
+            a1 = fmaf(hres[i][j], x1[j], a1);
+          }
+          out[i][w] = pack_bf16x2(a0, a1);
+        }
+      }
+    } else {
+      // n = 8: output stream by output stream, so that only that stream's
+      // nine coefficients are held in scalar registers at a time (the same
+      // FMA chain per element as above).
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const float hp = coef(i);
+        float hr[NS];
+#pragma unroll
+        for (int j = 0; j < NS; ++j) hr[j] = coef(NS + i * NS + j);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          float a0 = hp * bf16_lo(fv[w]), a1 = hp * bf16_hi(fv[w]);
+#pragma unroll
+          for (int j = 0; j < NS; ++j) {
+            a0 = fmaf(hr[j], bf16_lo(xv[j][w]), a0);
+            a1 = fmaf(hr[j], bf16_hi(xv[j][w]), a1);
+          }
+          out[i][w] = pack_bf16x2(a0, a1);
+        }
       }
     }
-    const bool in_range = c < c_end;
-    if (live && in_range) {
-#pragma unroll
-      for (int i = 0; i < NS; ++i)
-        __builtin_nontemporal_store(out[i], reinterpret_cast<u32x4 *>(yr + (size_t)i * C + c));
-    }
-    // B operands of this wave's k-steps (global, L2-resident), issued before
-    // the prefetch so that waiting for them never waits for the prefetch.
-    // They are held in groups of KB k-steps (all of them for n <= 4; for n = 8
-    // the later groups are loaded after the earlier ones are consumed).
+    // B operands of this wave's k-steps (global, L2-resident), in groups of
+    // KB k-steps (all of them for n <= 4; for n = 8 the later groups are
+    // loaded after the earlier ones are consumed).
     bf16x8 b[T::KB][T::NB];
     auto load_b = [&](int q0) {
 #pragma unroll
       for (int q = 0; q < T::KB; ++q) {
         const int ks = wave * T::KPW + q0 + q;       // 0 .. 16*NS-1 within the step
-        const int i = ks >> 4, t = ks & 15;          // stream, 32-channel sub-step
-        const int cs = c0 + 32 * t;
+        const int i = ks >> 4, ts = ks & 15;         // stream, 32-channel sub-step
+        const int cs = sp.c0 + 32 * ts;
         const int kstep = (i * C + min(cs, C - 32)) >> 5;  // clamped in range; such steps add zero
 #pragma unroll
         for (int nb = 0; nb < T::NB; ++nb)
           b[q][nb] = __builtin_bit_cast(bf16x8, load16(phip + ((size_t)(kstep * T::NB + nb) * 64 + lane) * 8));
       }
     };
-    load_b(0);
-    __syncthreads();  // the previous step's product is done reading the tile
+    uint16_t *yr = Y + (size_t)rr * NS * C;
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+      __builtin_nontemporal_store(out[i], reinterpret_cast<u32x4 *>(yr + (size_t)i * C + cst));
+    // The first B group is issued before the refill (waiting for it then
+    // never waits for the refill), except for n = 8, where holding it across
+    // the refill would not fit the register budget.
+    if constexpr (NS < 8) load_b(0);
+
+    __syncthreads();  // the previous step's product is done with the tile (and has written red)
+    if constexpr (T::SEPARATE) flush(step_at(t > 0 ? t - 1 : 0));
 #pragma unroll
     for (int i = 0; i < NS; ++i)
       *reinterpret_cast<u32x4 *>(my_lds_row + i * (kStepCh * 2) + wslot) =
-          in_range ? out[i] : u32x4{0u, 0u, 0u, 0u};
-    load_step(min(c0 + kStepCh, c_end - 8));  // prefetch the next step (a harmless reload after the last)
-    __syncthreads();  // the tile is complete
+          (in_range && live) ? out[i] : u32x4{0u, 0u, 0u, 0u};
+    load_set(xv, fv, hv, step_at(t_pref));
+    if constexpr (NS >= 8) load_b(0);
+    __syncthreads();  // the tile is complete (and the flush has read red)
 
-    // k-steps past the range read zeros from the tile (those lanes stored
-    // zeros), so they add nothing; no branch is needed.
+    // A unit's sums start from zero at its first step.
+    const bool first = (t % spu) == 0;
+#pragma unroll
+    for (int nb = 0; nb < T::NB; ++nb) acc[nb] = first ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[nb];
+    gram = first ? f32x4{0.f, 0.f, 0.f, 0.f} : gram;
+    // k-steps past the range read zeros from the tile, so they add nothing.
 #pragma unroll
     for (int q0 = 0; q0 < T::KPW; q0 += T::KB) {
       if (q0 > 0) load_b(q0);
 #pragma unroll
       for (int q = 0; q < T::KB; ++q) {
         const int ks = wave * T::KPW + q0 + q;
-        const int i = ks >> 4, t = ks & 15;
-        const int piece = (4 * t + g) ^ m;
+        const int i = ks >> 4, ts = ks & 15;
+        const int piece = (4 * ts + g) ^ m;
         const bf16x8 a = *reinterpret_cast<const bf16x8 *>(lds + m * T::ROW_BYTES + i * (kStepCh * 2) + piece * 16);
 #pragma unroll
         for (int nb = 0; nb < T::NB; ++nb)
@@ -183,39 +295,73 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
         gram = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, a, gram, 0, 0, 0);
       }
     }
-  }
+    if constexpr (T::SEPARATE) {
+      write_red();  // flushed after the next step's first barrier
+    } else {
+      __syncthreads();  // every wave is done with the tile, which now holds red
+      write_red();
+      __syncthreads();
+      flush(sp);        // the next step's first barrier orders it before the tile is rewritten
+    }
+  };
 
-  // Reduce the 16 waves' accumulators through LDS, in wave order.
-  __syncthreads();
-  float *red = reinterpret_cast<float *>(lds);  // [16 waves][16 rows][NP]
-#pragma unroll
-  for (int nb = 0; nb < T::NB; ++nb) {
-    const int col = nb * 16 + m;
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-      if (col < T::N) red[(wave * 16 + 4 * g + v) * T::NP + col] = acc[nb][v];
+  const int tl = nsteps - 1;
+  if constexpr (NS >= 8) {
+    // n = 8: one register set (two would not fit 128 VGPRs).
+    u32x4 xa[NS], fa;
+    uint32_t ha[T::HV];
+    load_set(xa, fa, ha, step_at(0));
+    for (int t = 0; t < nsteps; ++t) step(t, xa, fa, ha, min(t + 1, tl));
+  } else {
+    // Two register sets: the loads of step t+2 are issued while step t is
+    // applied and multiplied, so each wave has two steps of loads in flight.
+    // The loop always runs both steps (an odd last step runs after it), so
+    // the waits at the top of each step only cover the set used there.
+    u32x4 xa[NS], fa, xb[NS], fb;
+    uint32_t ha[T::HV], hb[T::HV];
+    load_set(xa, fa, ha, step_at(0));
+    load_set(xb, fb, hb, step_at(min(1, tl)));
+    int t = 0;
+    for (; t + 1 < nsteps; t += 2) {
+      step(t, xa, fa, ha, min(t + 2, tl));
+      step(t + 1, xb, fb, hb, min(t + 3, tl));
+    }
+    if (t < nsteps) step(t, xa, fa, ha, tl);
   }
-  if (g == (m >> 2)) red[(wave * 16 + m) * T::NP + T::N] = gram[m & 3];
-  __syncthreads();
-  float *wsl = ws + (size_t)s * B * T::NP;
-  for (int e = tid; e < 16 * T::NP; e += 1024) {
-    const int r = e / T::NP, col = e - r * T::NP;
-    float a = 0.f;
-    for (int w = 0; w < 16; ++w) a += red[(w * 16 + r) * T::NP + col];
-    if (row0 + r < B) wsl[(size_t)(row0 + r) * T::NP + col] = a;
+  if constexpr (T::SEPARATE) {
+    __syncthreads();
+    flush(step_at(tl));
   }
+}
+
+// Compute units of the current device (cached per device id).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < 64) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
 
 }  // namespace
 
 template <int NS>
-hipError_t launch_post_res_next_typed(int64_t B, int64_t C, int cw, int split, const void *X,
-                                      const void *F, const float *H, void *Y, const void *phip,
-                                      float *ws, hipStream_t st) {
-  const dim3 grid((uint32_t)((B + 15) / 16), (uint32_t)split);
-  post_res_next_kernel<NS><<<grid, 1024, 0, st>>>(
+hipError_t launch_post_res_next_typed(int64_t B, int64_t C, int spu, int split, int grid_cap,
+                                      const void *X, const void *F, const float *H, void *Y,
+                                      const void *phip, float *ws, float *dummy, hipStream_t st) {
+  const int64_t U = ((B + 15) / 16) * (int64_t)split;
+  const int G = (int)(U < grid_cap ? U : grid_cap);
+  post_res_next_kernel<NS><<<dim3((uint32_t)G), 1024, 0, st>>>(
       static_cast<const uint16_t *>(X), static_cast<const uint16_t *>(F), H,
-      static_cast<uint16_t *>(Y), static_cast<const uint16_t *>(phip), ws, (int)B, (int)C, cw);
+      static_cast<uint16_t *>(Y), static_cast<const uint16_t *>(phip), ws, dummy, (int)B, (int)C,
+      spu, split, (int)U);
   return hipGetLastError();
 }
 
@@ -223,18 +369,28 @@ FusedPlan plan_post_res_next(int64_t B, int n, int64_t C) {
   FusedPlan p;
   const int64_t N = (int64_t)n * n + 2 * n, NB = (N + 15) / 16, K = (int64_t)n * C;
   p.row_tiles = (B + 15) / 16;
-  // One slice of the whole hidden size when there are enough row tiles to
-  // fill the machine (one 16-wave workgroup per CU at a time); otherwise
-  // split the channels so that about 512 workgroups exist.
+  // Steps per unit: the largest divisor of the row's step count that still
+  // leaves at least 7 slices (fewer when the row is shorter), so that the
+  // ~256 resident workgroups cover at most ~37 row tiles at a time while the
+  // partial sums stay small (7 x B x (N+1) fp32).  MHC_FUSED_SPU overrides
+  // (any value >= 1; one that does not divide the step count leaves empty
+  // steps at the end of the last slice, which add nothing).
   const int64_t steps = (C + kStepCh - 1) / kStepCh;
-  int64_t want = (512 + p.row_tiles - 1) / p.row_tiles;
-  if (want < 1) want = 1;
-  if (want > steps) want = steps;
-  p.cw = (int)(((steps + want - 1) / want) * kStepCh);
-  p.split = (int)((C + p.cw - 1) / p.cw);
+  const int64_t want = steps < 7 ? steps : 7;
+  int64_t spu = 1;
+  for (int64_t d = 1; d <= steps; ++d)
+    if (steps % d == 0 && steps / d >= want) spu = d;
+  if (const char *e = std::getenv("MHC_FUSED_SPU")) {
+    const long v = std::strtol(e, nullptr, 10);
+    if (v >= 1 && v <= steps) spu = v;
+  }
+  p.cw = (int)(spu * kStepCh);
+  p.split = (int)((steps + spu - 1) / spu);
   p.partial_bytes = (size_t)p.split * (size_t)B * (size_t)(N + 1) * sizeof(float);
   p.ksteps = (K + 31) / 32;
-  p.phip_offset = (p.partial_bytes + 1023) & ~(size_t)1023;
+  p.dummy_offset = (p.partial_bytes + 1023) & ~(size_t)1023;
+  p.dummy_bytes = (size_t)((16 * (N + 1) + 1023) / 1024) * 1024 * sizeof(float);
+  p.phip_offset = p.dummy_offset + p.dummy_bytes;
   p.phip_bytes = (size_t)p.ksteps * (size_t)NB * 1024;
   p.zero_offset = p.phip_offset + p.phip_bytes;
   p.total_bytes = p.zero_offset + 256;
@@ -249,11 +405,18 @@ hipError_t launch_post_res_next(const FusedPlan &p, int n, int64_t B, int64_t C,
   hipError_t e = launch_pack_phi(n, (int64_t)n * C, p.ksteps, phi_next, phip, base + p.zero_offset, st);
   if (e != hipSuccess) return e;
   float *ws = reinterpret_cast<float *>(base);
+  float *dummy = reinterpret_cast<float *>(base + p.dummy_offset);
+  const int spu = p.cw / kStepCh;
+  int cap = device_cus();
+  if (const char *env = std::getenv("MHC_FUSED_WGS")) {
+    const long v = std::strtol(env, nullptr, 10);
+    if (v >= 1 && v <= 65535) cap = (int)v;
+  }
   switch (n) {
-    case 1: return launch_post_res_next_typed<1>(B, C, p.cw, p.split, X, F, H, Y, phip, ws, st);
-    case 2: return launch_post_res_next_typed<2>(B, C, p.cw, p.split, X, F, H, Y, phip, ws, st);
-    case 4: return launch_post_res_next_typed<4>(B, C, p.cw, p.split, X, F, H, Y, phip, ws, st);
-    case 8: return launch_post_res_next_typed<8>(B, C, p.cw, p.split, X, F, H, Y, phip, ws, st);
+    case 1: return launch_post_res_next_typed<1>(B, C, spu, p.split, cap, X, F, H, Y, phip, ws, dummy, st);
+    case 2: return launch_post_res_next_typed<2>(B, C, spu, p.split, cap, X, F, H, Y, phip, ws, dummy, st);
+    case 4: return launch_post_res_next_typed<4>(B, C, spu, p.split, cap, X, F, H, Y, phip, ws, dummy, st);
+    case 8: return launch_post_res_next_typed<8>(B, C, spu, p.split, cap, X, F, H, Y, phip, ws, dummy, st);
     default: return hipErrorInvalidValue;
   }
 }
