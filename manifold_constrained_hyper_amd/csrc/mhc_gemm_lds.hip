@@ -212,26 +212,46 @@ __global__ __launch_bounds__(256) void pack_phi_kernel(const uint16_t *__restric
                                                        uint16_t *__restrict__ phip,
                                                        uint16_t *__restrict__ zero, int K,
                                                        int ksteps) {
+  // One wave per 32-row k-step.  The step's rows of phi are one contiguous
+  // block of 64*N bytes; the wave copies it to LDS with 16-byte loads, then
+  // each lane gathers its 8 consecutive k of one column per 16-column block.
   constexpr int N = NS * NS + 2 * NS;
   constexpr int NB = (N + 15) / 16;
-  const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (v < 16) store16_plain(zero + v * 8, u32x4{0u, 0u, 0u, 0u});
-  if (v >= (int64_t)ksteps * NB * 64) return;
-  const int lane = (int)(v & 63);
-  const int64_t blk = v >> 6;
-  const int nb = (int)(blk % NB);
-  const int64_t ks = blk / NB;
-  const int n = nb * 16 + (lane & 15);
-  const int64_t k0 = ks * 32 + 8 * (lane >> 4);
-  uint32_t w[4];
+  constexpr int PIECES = 4 * N;                // 16-byte pieces per k-step (32 rows x 2N bytes)
+  constexpr int PPL = (PIECES + 63) / 64;      // ... per lane
+  __shared__ __attribute__((aligned(16))) uint16_t buf[4][32 * N];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (blockIdx.x == 0 && threadIdx.x < 16) store16_plain(zero + threadIdx.x * 8, u32x4{0u, 0u, 0u, 0u});
+  const int ks_raw = blockIdx.x * 4 + wave;
+  const int ks = min(ks_raw, ksteps - 1);      // surplus waves redo the last step and store nothing
+  const int64_t k0 = (int64_t)ks * 32;
+  const int64_t valid_bytes = (min((int64_t)K, k0 + 32) - k0) * (2 * N);  // a multiple of 16 (K % 8 == 0)
+  const char *src = reinterpret_cast<const char *>(phi) + k0 * (2 * N);
+  char *dst = reinterpret_cast<char *>(buf[wave]);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int64_t ka = k0 + 2 * q, kb = ka + 1;
-    const uint32_t lo = (n < N && ka < K) ? phi[ka * N + n] : 0u;
-    const uint32_t hi = (n < N && kb < K) ? phi[kb * N + n] : 0u;
-    w[q] = lo | (hi << 16);
+  for (int q = 0; q < PPL; ++q) {
+    const int p = lane + 64 * q;
+    if (p < PIECES) {
+      const u32x4 v = (int64_t)p * 16 < valid_bytes ? load16(reinterpret_cast<const uint16_t *>(src + p * 16))
+                                                    : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4 *>(dst + p * 16) = v;
+    }
   }
-  store16_plain(phip + v * 8, u32x4{w[0], w[1], w[2], w[3]});
+  __syncthreads();
+  if (ks_raw >= ksteps) return;
+  const int kk = 8 * (lane >> 4);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = nb * 16 + (lane & 15);
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t lo = n < N ? buf[wave][(kk + 2 * q) * N + n] : 0u;
+      const uint32_t hi = n < N ? buf[wave][(kk + 2 * q + 1) * N + n] : 0u;
+      w[q] = lo | (hi << 16);
+    }
+    store16_plain(phip + ((int64_t)(ks * NB + nb) * 64 + lane) * 8, u32x4{w[0], w[1], w[2], w[3]});
+  }
 }
 
 }  // namespace
@@ -256,10 +276,7 @@ hipError_t launch_gemm_lds_typed(const GemmPlan &p, int64_t B, int64_t C, const 
 
 hipError_t launch_pack_phi(int n, int64_t K, int64_t ksteps, const void *phi, void *phip,
                            void *zero, hipStream_t st) {
-  const int N = n * n + 2 * n;
-  const int NB = (N + 15) / 16;
-  const int64_t vecs = ksteps * NB * 64;
-  const dim3 grid((uint32_t)((vecs + 255) / 256));
+  const dim3 grid((uint32_t)((ksteps + 3) / 4));  // one wave per 32-row k-step
   const uint16_t *src = static_cast<const uint16_t *>(phi);
   uint16_t *dst = static_cast<uint16_t *>(phip), *z = static_cast<uint16_t *>(zero);
   switch (n) {
