@@ -9,13 +9,19 @@
 //   sections 3.2, 3.3, 5.2, 5.3  these steps are tiny per row, so they are
 //                fused after the split-K reduction in a single launch.
 //
-// Layout: a workgroup of 256 lanes owns R = 256 / n rows; n consecutive lanes
-// serve one row, lane i holding row i of that row's n x n res matrix.
-//   phase 1  lanes sum the S partial slices [S, B, N+1] in slice order 0..S-1
-//            (fixed order: bitwise deterministic).  For each slice the
-//            workgroup's rows are one contiguous run, so the loads coalesce;
-//            all loads of a batch of slices are issued before they are added.
-//            Sums go to LDS and the raw logits to global memory.
+// Layout: a workgroup of 256 lanes owns RB rows (RB = 256 / n, or 1 row when
+// B is small); n consecutive lanes serve one row, lane i holding row i of
+// that row's n x n res matrix.
+//   phase 1  lanes sum the S partial slices [S, B, N+1] in a fixed order
+//            (bitwise deterministic).  With RB = 256 / n every lane owns a few
+//            elements of the block and adds all slices in order 0..S-1; for
+//            each slice the workgroup's rows are one contiguous run, so the
+//            loads coalesce, and all loads of a batch of slices are issued
+//            before they are added.  With one row per workgroup (small B,
+//            typically many slices) the 256 lanes form G = 256 / (N+1) groups;
+//            group g adds slices g, g+G, g+2G, ... in order and the G group
+//            sums are then added in group order.  Sums go to LDS and the raw
+//            logits to global memory.
 //   phase 2  lane i computes gate i of the pre block and of the post block,
 //            then the Sinkhorn iteration: a row normalisation is local to the
 //            lane; a column sum is a butterfly over the n lanes of the row
@@ -28,6 +34,7 @@ namespace mhc {
 namespace {
 
 constexpr int kIters = 20;
+constexpr int64_t kOneRowMaxB = 512;  // up to this many rows, one row per workgroup
 
 // x + (x from the lane whose index differs in the given low bits), for the
 // butterfly over groups of 2, 4 or 8 aligned lanes.
@@ -51,7 +58,7 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-template <int NS>
+template <int NS, bool ONE_ROW>
 __global__ __launch_bounds__(256) void coeff_sinkhorn_kernel(
     const float *__restrict__ ws, int split, int B, float inv_k, float alpha_pre,
     float alpha_post, float alpha_res, const float *__restrict__ b_pre,
@@ -60,14 +67,40 @@ __global__ __launch_bounds__(256) void coeff_sinkhorn_kernel(
   static_assert(NS == 1 || NS == 2 || NS == 4 || NS == 8, "n");
   constexpr int N = NS * NS + 2 * NS;
   constexpr int NP = N + 1;
-  constexpr int R = 256 / NS;  // rows per workgroup
+  constexpr int R = ONE_ROW ? 1 : 256 / NS;  // rows per workgroup
+  constexpr int G = ONE_ROW ? 256 / NP : 1;   // slice groups (one-row mode)
   __shared__ float sums[R * NP];
+  __shared__ float gsum[ONE_ROW ? G * NP : 1];
 
   const int tid = threadIdx.x;
   const int row0 = blockIdx.x * R;
   const int rows = min(R, B - row0);
 
-  {
+  if constexpr (ONE_ROW) {
+    const size_t slice = (size_t)B * NP;
+    const float *base = ws + (size_t)row0 * NP;
+    const int g = tid / NP, e = tid - g * NP;
+    if (g < G) {
+      float acc = 0.f;
+      for (int s0 = g; s0 < split; s0 += 4 * G) {
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = (s0 + q * G < split) ? base[(size_t)(s0 + q * G) * slice + e] : 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (s0 + q * G < split) acc += v[q];
+      }
+      gsum[g * NP + e] = acc;
+    }
+    __syncthreads();
+    if (tid < NP) {
+      float a = 0.f;
+#pragma unroll
+      for (int q = 0; q < G; ++q) a += gsum[q * NP + tid];
+      sums[tid] = a;
+      if (tid < N) logits[(size_t)row0 * N + tid] = a;
+    }
+  } else {
     // Every thread owns EPT elements of the workgroup's [rows, N+1] block and
     // issues the loads of SB slices for all of them before adding, so a
     // thread has up to SB*EPT independent loads in flight.
@@ -146,11 +179,17 @@ template <int NS>
 void launch_n(int64_t B, int64_t C, int split, const float *ws, float ap, float aq, float ar,
               const float *bp, const float *bq, const float *br, float *logits, float *r,
               float *H, hipStream_t st) {
-  constexpr int R = 256 / NS;
-  const dim3 grid((uint32_t)((B + R - 1) / R));
   const float inv_k = (float)(1.0 / (double)(NS * C));
-  coeff_sinkhorn_kernel<NS><<<grid, 256, 0, st>>>(ws, split, (int)B, inv_k, ap, aq, ar, bp, bq,
-                                                  br, logits, r, H);
+  // Small B: one row per workgroup, so that the slices are summed by many
+  // lanes and many workgroups at once.
+  if (B <= kOneRowMaxB) {
+    coeff_sinkhorn_kernel<NS, true><<<dim3((uint32_t)B), 256, 0, st>>>(
+        ws, split, (int)B, inv_k, ap, aq, ar, bp, bq, br, logits, r, H);
+  } else {
+    constexpr int R = 256 / NS;
+    coeff_sinkhorn_kernel<NS, false><<<dim3((uint32_t)((B + R - 1) / R)), 256, 0, st>>>(
+        ws, split, (int)B, inv_k, ap, aq, ar, bp, bq, br, logits, r, H);
+  }
 }
 
 }  // namespace
