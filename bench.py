@@ -92,10 +92,12 @@ KERNELS_OF_CALL = {"mhc_post_res": "post_res_kernel", "mhc_pre": "pre_kernel",
 
 # source files that make up each call's kernels (for the counter-freshness check)
 CALL_SOURCES = {
-    "mhc_coeffs": ("mhc_gemm_rms.hip", "mhc_gemm_lds.hip", "mhc_coeff_sinkhorn.hip", "mhc_device.h"),
+    "mhc_coeffs": ("mhc_gemm_rms.hip", "mhc_gemm_lds.hip", "mhc_coeff_sinkhorn.hip",
+                   "mhc_coeffs_small.hip", "mhc_finish.h", "mhc_device.h"),
     "mhc_pre": ("mhc_stream.hip", "mhc_device.h"),
     "mhc_post_res": ("mhc_stream.hip", "mhc_device.h"),
     "mhc_post_res_coeffs": ("mhc_post_res_fused.hip", "mhc_gemm_lds.hip", "mhc_coeff_sinkhorn.hip",
+                            "mhc_coeffs_small.hip", "mhc_stream.hip", "mhc_finish.h",
                             "mhc_device.h"),
 }
 

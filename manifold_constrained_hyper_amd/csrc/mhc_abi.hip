@@ -59,11 +59,13 @@ const char *mhc_status_string(int status) {
 
 size_t mhc_coeffs_workspace_size(int64_t B, int32_t n, int64_t C) {
   if (check_shape(B, n, C) != MHC_OK || B == 0) return 0;
+  if (mhc::use_coeffs_small(B, n, C)) return mhc::plan_coeffs_small(B, n, C).total_bytes;
   return mhc::gemm_workspace_bytes(mhc::plan_gemm(B, n, C), B, n);
 }
 
 int32_t mhc_coeffs_split_k(int64_t B, int32_t n, int64_t C) {
   if (check_shape(B, n, C) != MHC_OK || B == 0) return 0;
+  if (mhc::use_coeffs_small(B, n, C)) return mhc::plan_coeffs_small(B, n, C).split;
   return mhc::plan_gemm(B, n, C).split;
 }
 
@@ -81,8 +83,10 @@ int mhc_coeffs(int64_t B, int32_t n, int64_t C, const void *X_t, const void *phi
       !aligned(H, 4))
     return MHC_ERR_UNSUPPORTED;
 
+  const bool small = mhc::use_coeffs_small(B, n, C);
   const mhc::GemmPlan plan = mhc::plan_gemm(B, n, C);
-  const size_t ws_need = mhc::gemm_workspace_bytes(plan, B, n);
+  const mhc::SmallPlan splan = mhc::plan_coeffs_small(B, n, C);
+  const size_t ws_need = small ? splan.total_bytes : mhc::gemm_workspace_bytes(plan, B, n);
   const int64_t N = ncoef(n), K = (int64_t)n * C;
   const Span in[] = {span(X_t, (size_t)B * K * 2), span(phi, (size_t)K * N * 2),
                      span(b_pre, (size_t)n * 4), span(b_post, (size_t)n * 4),
@@ -99,6 +103,10 @@ int mhc_coeffs(int64_t B, int32_t n, int64_t C, const void *X_t, const void *phi
   if (workspace_bytes < ws_need) return MHC_ERR_WORKSPACE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (small)
+    return from_hip(mhc::launch_coeffs_small(splan, n, B, C, X_t, phi, alpha_pre, alpha_post,
+                                             alpha_res, b_pre, b_post, b_res, logits, r, H,
+                                             workspace, s));
   float *ws = static_cast<float *>(workspace);
   st = from_hip(mhc::launch_gemm_rms(plan, n, B, C, X_t, phi, ws, s));
   if (st != MHC_OK) return st;
@@ -139,6 +147,7 @@ int mhc_post_res(int64_t B, int32_t n, int64_t C, const void *X_t, const void *F
 
 size_t mhc_post_res_coeffs_workspace_size(int64_t B, int32_t n, int64_t C) {
   if (check_shape(B, n, C) != MHC_OK || B == 0 || C % 32 != 0) return 0;
+  if (mhc::use_coeffs_small(B, n, C)) return mhc::plan_coeffs_small(B, n, C).total_bytes;
   return mhc::plan_post_res_next(B, n, C).total_bytes;
 }
 
@@ -158,7 +167,11 @@ int mhc_post_res_coeffs(int64_t B, int32_t n, int64_t C, const void *X_t, const 
       !aligned(workspace, 16) || !aligned(H, 4) || !aligned(b_pre, 4) || !aligned(b_post, 4) ||
       !aligned(b_res, 4) || !aligned(logits_next, 4) || !aligned(r_next, 4) || !aligned(H_next, 4))
     return MHC_ERR_UNSUPPORTED;
+  // Small B: the apply, then the one-launch coefficient kernel on X_next (at
+  // decode sizes re-reading X_next costs less than the fused kernel's setup).
+  const bool small = mhc::use_coeffs_small(B, n, C);
   const mhc::FusedPlan plan = mhc::plan_post_res_next(B, n, C);
+  const size_t ws_need = small ? mhc::plan_coeffs_small(B, n, C).total_bytes : plan.total_bytes;
   const int64_t N = ncoef(n), K = (int64_t)n * C;
   const Span in[] = {span(X_t, (size_t)B * K * 2), span(F_out, (size_t)B * C * 2),
                      span(H, (size_t)B * N * 4), span(phi_next, (size_t)K * N * 2),
@@ -166,16 +179,24 @@ int mhc_post_res_coeffs(int64_t B, int32_t n, int64_t C, const void *X_t, const 
                      span(b_res, (size_t)n * n * 4)};
   const Span out[] = {span(X_next, (size_t)B * K * 2), span(logits_next, (size_t)B * N * 4),
                       span(r_next, (size_t)B * 4), span(H_next, (size_t)B * N * 4),
-                      span(workspace, plan.total_bytes)};
+                      span(workspace, ws_need)};
   for (const Span &o : out)
     for (const Span &i : in)
       if (overlaps(o, i)) return MHC_ERR_INVALID_ARG;
   for (int a = 0; a < 5; ++a)
     for (int b = a + 1; b < 5; ++b)
       if (overlaps(out[a], out[b])) return MHC_ERR_INVALID_ARG;
-  if (workspace_bytes < plan.total_bytes) return MHC_ERR_WORKSPACE;
+  if (workspace_bytes < ws_need) return MHC_ERR_WORKSPACE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (small) {
+    st = from_hip(mhc::launch_post_res(n, B, C, X_t, F_out, H, X_next, s));
+    if (st != MHC_OK) return st;
+    return from_hip(mhc::launch_coeffs_small(mhc::plan_coeffs_small(B, n, C), n, B, C, X_next,
+                                             phi_next, alpha_pre, alpha_post, alpha_res, b_pre,
+                                             b_post, b_res, logits_next, r_next, H_next,
+                                             workspace, s));
+  }
   st = from_hip(mhc::launch_post_res_next(plan, n, B, C, X_t, F_out, H, X_next, phi_next,
                                           workspace, s));
   if (st != MHC_OK) return st;

@@ -22,41 +22,18 @@
 //            group g adds slices g, g+G, g+2G, ... in order and the G group
 //            sums are then added in group order.  Sums go to LDS and the raw
 //            logits to global memory.
-//   phase 2  lane i computes gate i of the pre block and of the post block,
-//            then the Sinkhorn iteration: a row normalisation is local to the
-//            lane; a column sum is a butterfly over the n lanes of the row
-//            (DPP lane moves, every lane ends with bitwise the same sum).
+//   phase 2  finish_row (mhc_finish.h): lane i computes gate i of the pre
+//            and post blocks, then the Sinkhorn iteration on row i of the res
+//            matrix, with column sums by a DPP butterfly over the row's lanes.
 #include "mhc_device.h"
+#include "mhc_finish.h"
 #include "mhc_launch.h"
 
 namespace mhc {
 
 namespace {
 
-constexpr int kIters = 20;
 constexpr int64_t kOneRowMaxB = 512;  // up to this many rows, one row per workgroup
-
-// x + (x from the lane whose index differs in the given low bits), for the
-// butterfly over groups of 2, 4 or 8 aligned lanes.
-__device__ __forceinline__ float dpp_add_xor1(float x) {
-  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float dpp_add_xor2(float x) {
-  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
-}
-// lane l <- lane (7 - l) within each group of 8: pairs the two quads of an
-// aligned group of 8 once each quad holds its own sum.
-__device__ __forceinline__ float dpp_add_half_mirror(float x) {
-  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
-}
-
-template <int NS>
-__device__ __forceinline__ float group_sum(float x) {
-  if constexpr (NS >= 2) x = dpp_add_xor1(x);
-  if constexpr (NS >= 4) x = dpp_add_xor2(x);
-  if constexpr (NS >= 8) x = dpp_add_half_mirror(x);
-  return x;
-}
 
 template <int NS, bool ONE_ROW>
 __global__ __launch_bounds__(256) void coeff_sinkhorn_kernel(
@@ -141,38 +118,8 @@ __global__ __launch_bounds__(256) void coeff_sinkhorn_kernel(
 
   const int lr = tid / NS, i = tid % NS;
   if (lr >= rows) return;  // whole row groups leave together
-  const float *sm = sums + lr * NP;
-  const int row = row0 + lr;
-  const float r = sqrtf(sm[N] * inv_k);
-  const float inv_r = 1.0f / r;
-  float *h = H + (size_t)row * N;
-  if (i == 0) r_out[row] = r;
-  {
-    const float zp = alpha_pre * sm[i] * inv_r + b_pre[i];
-    h[i] = 1.0f / (1.0f + __expf(-zp));
-    const float zq = alpha_post * sm[NS + i] * inv_r + b_post[i];
-    h[NS + i] = 2.0f / (1.0f + __expf(-zq));
-  }
-
-  float m[NS];
-#pragma unroll
-  for (int j = 0; j < NS; ++j)
-    m[j] = __expf(alpha_res * sm[2 * NS + i * NS + j] * inv_r + b_res[i * NS + j]);
-  // Each normalisation multiplies by the hardware reciprocal of the sum
-  // (v_rcp_f32, about 1 ulp) instead of dividing element by element.
-#pragma unroll 1
-  for (int it = 0; it < kIters; ++it) {
-    float rs = 0.f;
-#pragma unroll
-    for (int j = 0; j < NS; ++j) rs += m[j];
-    const float inv_rs = __builtin_amdgcn_rcpf(rs);
-#pragma unroll
-    for (int j = 0; j < NS; ++j) m[j] *= inv_rs;
-#pragma unroll
-    for (int j = 0; j < NS; ++j) m[j] *= __builtin_amdgcn_rcpf(group_sum<NS>(m[j]));
-  }
-#pragma unroll
-  for (int j = 0; j < NS; ++j) h[2 * NS + i * NS + j] = m[j];
+  finish_row<NS>(sums + lr * NP, row0 + lr, i, inv_k, alpha_pre, alpha_post, alpha_res, b_pre,
+                 b_post, b_res, r_out, H);
 }
 
 template <int NS>

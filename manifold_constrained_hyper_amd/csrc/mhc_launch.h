@@ -60,6 +60,29 @@ hipError_t launch_post_res_next(const FusedPlan &p, int n, int64_t B, int64_t C,
                                 const void *F, const float *H, void *Y, const void *phi_next,
                                 void *ws_base, hipStream_t st);
 
+// Small-B (decode) path of mhc_coeffs: product, split-K reduction and finish
+// in one launch (mhc_coeffs_small.hip).
+//
+// Workspace layout: [0, partial_bytes) fp32 partials [split, B, N+1];
+// [ctr_offset, +8 * row_tiles * split) one 64-bit arrival flag per 16-row
+// tile and K-slice (any initial contents).
+template <int NS>
+constexpr int kSmallKSlice() { return NS >= 8 ? 256 : 1024; }  // K per slice: phi slice <= 48 KiB of LDS
+constexpr int64_t kSmallMaxB = 256;     // rows up to which mhc_coeffs takes this path
+constexpr int64_t kSmallMaxSplit = 64;  // ... and K-slices up to which
+struct SmallPlan {
+  int split;
+  int64_t kslice, row_tiles;
+  size_t partial_bytes, ctr_offset, total_bytes;
+};
+SmallPlan plan_coeffs_small(int64_t B, int n, int64_t C);
+bool use_coeffs_small(int64_t B, int n, int64_t C);
+hipError_t launch_coeffs_small(const SmallPlan &p, int n, int64_t B, int64_t C, const void *X,
+                               const void *phi, float alpha_pre, float alpha_post,
+                               float alpha_res, const float *b_pre, const float *b_post,
+                               const float *b_res, float *logits, float *r, float *H, void *ws,
+                               hipStream_t st);
+
 hipError_t launch_coeff_sinkhorn(int n, int64_t B, int64_t C, int split, const float *ws,
                                  float alpha_pre, float alpha_post, float alpha_res,
                                  const float *b_pre, const float *b_post, const float *b_res,

@@ -34,6 +34,18 @@ def _gpu():
     yield
 
 
+# Up to 256 rows mhc_post_res_coeffs runs the stand-alone apply and the
+# one-launch small-B coefficient kernel; "fused" forces the fused kernel at
+# every size.
+@pytest.fixture(params=["default", "fused"])
+def route(request, monkeypatch):
+    if request.param == "fused":
+        monkeypatch.setenv("MHC_SMALL_MAX_B", "0")
+    else:
+        monkeypatch.delenv("MHC_SMALL_MAX_B", raising=False)
+    return request.param
+
+
 def _f64(t):
     return oracle.bf16_bits_to_f64(synth.bf16_bits(t))
 
@@ -93,8 +105,10 @@ def _check(cur, nxt, o, ref, f, rows, label):
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "large", "wide"])
-def test_fused_named(name):
-    _say(f"fused {name}")
+def test_fused_named(name, route):
+    if route == "fused" and synth.CONFIGS[name]["B"] > 256:
+        pytest.skip("above 256 rows the default route is the fused kernel")
+    _say(f"fused {name} route={route}")
     cfg = synth.CONFIGS[name]
     cur, nxt = _layers(cfg["n"], cfg["C"], cfg["B"], cfg["x_dist"], cfg["seed"])
     o, ref, f = _run(cur, nxt)
@@ -109,8 +123,8 @@ FUSED_RAGGED = [(77, 4, 544), (1, 4, 32), (130, 8, 96), (33, 1, 64), (65, 2, 208
 
 
 @pytest.mark.parametrize("B,n,C", FUSED_RAGGED, ids=[f"B{b}n{n}C{c}" for b, n, c in FUSED_RAGGED])
-def test_fused_ragged(B, n, C):
-    _say(f"fused ragged B={B} n={n} C={C}")
+def test_fused_ragged(B, n, C, route):
+    _say(f"fused ragged B={B} n={n} C={C} route={route}")
     cur, nxt = _layers(n, C, B, "student_t4" if B % 2 else "normal", B * 13 + C)
     o, ref, f = _run(cur, nxt)
     _check(cur, nxt, o, ref, f, list(range(B)), f"B{B}n{n}C{C}")
@@ -126,8 +140,8 @@ def test_fused_deterministic():
         assert torch.equal(a[k].view(torch.int8), b[k].view(torch.int8)), k
 
 
-def test_fused_guard_bands():
-    _say("fused guard bands")
+def test_fused_guard_bands(route):
+    _say(f"fused guard bands route={route}")
     B, n, C = 77, 4, 544
     N = n * n + 2 * n
     cur, nxt = _layers(n, C, B, "normal", 11)

@@ -40,18 +40,25 @@ def _gpu():
     yield
 
 
-# The product kernel has two implementations: X staged through LDS by
-# direct-to-LDS loads (the default) and MFMA operands loaded straight from
-# global memory (selected with MHC_GEMM_ALGO=0).  Both must meet the bar.
-GEMM_ALGOS = ["lds", "reg"]
+# mhc_coeffs has three implementations, and every one must meet the bar:
+#   lds    split-K product with X staged through LDS by direct-to-LDS loads,
+#          then the combine kernel (the default above 256 rows);
+#   reg    the same with MFMA operands loaded straight from global memory
+#          (MHC_GEMM_ALGO=0);
+#   small  the one-launch small-B kernel (the default up to 256 rows; forced
+#          here for every size it supports with MHC_SMALL_MAX_B).
+GEMM_ALGOS = ["lds", "reg", "small"]
 
 
 @pytest.fixture(params=GEMM_ALGOS)
 def gemm_algo(request, monkeypatch):
-    if request.param == "reg":
-        monkeypatch.setenv("MHC_GEMM_ALGO", "0")
+    monkeypatch.delenv("MHC_GEMM_ALGO", raising=False)
+    if request.param == "small":
+        monkeypatch.setenv("MHC_SMALL_MAX_B", str(1 << 30))
     else:
-        monkeypatch.delenv("MHC_GEMM_ALGO", raising=False)
+        monkeypatch.setenv("MHC_SMALL_MAX_B", "0")
+        if request.param == "reg":
+            monkeypatch.setenv("MHC_GEMM_ALGO", "0")
     return request.param
 
 
@@ -260,6 +267,55 @@ def test_bitwise_deterministic():
     b = run_forward(inp)
     for k in ("logits", "r", "H", "F_pre", "X_next"):
         assert torch.equal(a[k].view(torch.int8), b[k].view(torch.int8)), k
+
+
+def test_small_path_deterministic_and_matches_split(monkeypatch):
+    _say("small path vs split path, decode")
+    inp = synth.make_config("decode", device="cuda")
+    monkeypatch.setenv("MHC_SMALL_MAX_B", str(1 << 30))
+    a = run_forward(inp)
+    b = run_forward(inp)
+    for k in ("logits", "r", "H"):
+        assert torch.equal(a[k].view(torch.int8), b[k].view(torch.int8)), k
+    monkeypatch.setenv("MHC_SMALL_MAX_B", "0")
+    c = run_forward(inp)
+    rel = (a["logits"] - c["logits"]).abs().max() / c["logits"].abs().max()
+    assert rel.item() < 1e-5
+    assert ((a["r"] - c["r"]).abs() / c["r"]).max().item() < 1e-5
+    assert (a["H"] - c["H"]).abs().max().item() < 1e-5
+
+
+@pytest.mark.parametrize("fill", ["zeros", "ones", "random", "near_done"])
+def test_small_path_any_workspace_contents(monkeypatch, fill):
+    """The small-B kernel keeps per-tile counters in the workspace; whatever
+    the workspace held before the call, the result is the same bits."""
+    _say(f"small path, workspace filled with {fill}")
+    monkeypatch.setenv("MHC_SMALL_MAX_B", str(1 << 30))
+    inp = synth.make_inputs(4, 1024, 77, "normal", seed=4242, device="cuda")
+    ref = run_forward(inp)
+    B, n, C = inp["B"], inp["n"], inp["C"]
+    o = mhc.alloc_outputs(B, n, C)
+    ws = o["workspace"]
+    if fill == "zeros":
+        ws.zero_()
+    elif fill == "ones":
+        ws.fill_(-1)
+    elif fill == "random":
+        g = torch.Generator(device="cpu").manual_seed(5)
+        ws.copy_(torch.randint(-128, 128, ws.shape, generator=g, dtype=torch.int8).to(ws.device))
+    else:
+        # every 64-bit word holds an arbitrary epoch with a count one short of a
+        # full tile, the worst case for a counter that is not reset
+        w64 = ws[: ws.numel() // 8 * 8].view(torch.int64)
+        S = mhc.mhc_coeffs_split_k(B, n, C)
+        w64.fill_((0x123456789A << 16) | (S - 1))
+    for _ in range(2):
+        mhc.mhc_coeffs(B, n, C, inp["X"], inp["phi"], inp["alpha_pre"], inp["alpha_post"],
+                       inp["alpha_res"], inp["b_pre"], inp["b_post"], inp["b_res"],
+                       o["logits"], o["r"], o["H"], ws)
+        torch.cuda.synchronize()
+        for k in ("logits", "r", "H"):
+            assert torch.equal(o[k].view(torch.int8), ref[k].view(torch.int8)), (fill, k)
 
 
 def test_split_k_invariance(monkeypatch, gemm_algo):
