@@ -75,8 +75,10 @@ enum mhc_status {
 const char *mhc_status_string(int status);
 
 /* Bytes of device workspace mhc_coeffs needs for (B, n, C): the split-K
- * partial sums, fp32 [S, B, N+1].  Returns 0 for B == 0 or for arguments
- * mhc_coeffs would reject.  Pure host function. */
+ * partial sums, fp32 [S, B, N+1], plus (up to 256 rows) one 8-byte arrival
+ * flag per 16-row tile and K-slice, or (above) a packed copy of phi.  Returns
+ * 0 for B == 0 or for arguments mhc_coeffs would reject.  Pure host
+ * function. */
 size_t mhc_coeffs_workspace_size(int64_t B, int32_t n, int64_t C);
 
 /* Number S of K-slices mhc_coeffs splits the reduction over K = n*C into for
@@ -107,7 +109,12 @@ int32_t mhc_coeffs_split_k(int64_t B, int32_t n, int64_t C);
  *             contents on entry are ignored and on exit undefined.
  *
  * The result is deterministic: the split-K partials are combined in a fixed
- * order, without atomics. */
+ * order.  Up to 256 rows the call is a single kernel (the decode sizes of
+ * [mHC-cutile] section 3.2, where launches dominate): the K-slices of each
+ * 16-row tile publish their partials and arrival flags in the workspace, and
+ * whichever slice finds all flags set adds the partials in slice order and
+ * finishes the tile.  The flags carry a per-call tag, so the workspace needs
+ * no initialisation in either case. */
 int mhc_coeffs(int64_t B, int32_t n, int64_t C,
                const void *X_t, const void *phi,
                float alpha_pre, float alpha_post, float alpha_res,
