@@ -32,3 +32,5 @@ from .mhc_oracle import (  # noqa: F401
     forward,
     split_h,
 )
+
+from . import fp8  # noqa: F401,E402  (E4M3 encode / decode for the FP8 variant)
