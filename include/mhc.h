@@ -172,6 +172,65 @@ int mhc_post_res_coeffs(int64_t B, int32_t n, int64_t C,
                         float *logits_next, float *r_next, float *H_next,
                         void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * FP8 residual-stream variant.
+ *
+ * [mHC-cutile] runs its first benchmark (the performance section after its
+ * section 4 kernels) with every tensor in torch.float8_e4m3fn.  These calls
+ * are the three above (and the fused call) with the residual-stream tensors
+ * X_t, F_out, F_pre and X_next in FP8 E4M3 -- the OCP "fn" encoding: 1 sign,
+ * 4 exponent (bias 7) and 3 mantissa bits, subnormals, no infinities, NaN =
+ * S.1111.111, largest finite value 448 -- stored unscaled, one byte per
+ * element, same layouts as the bf16 calls.  phi stays bf16 and H, logits, r
+ * stay fp32.
+ *
+ * Readings (the page gives no conversion rules): values are used as they are
+ * (no scale factors, as in the page's benchmark); inputs are widened exactly;
+ * arithmetic is fp32 as in the bf16 calls; F_pre and X_next are rounded once
+ * to E4M3, to nearest even, saturating at +-448 (torch's own cast returns NaN
+ * past the range).  The product widens the E4M3 X exactly to bf16 for the
+ * matrix core, so logits, r and H carry the bf16 calls' accuracy.
+ *
+ * Arguments, ownership, errors and workspace rules are those of the bf16
+ * calls, with E4M3 in place of bf16 and the additional requirement
+ * C % 16 == 0 (16-byte vectors of 16 elements), else MHC_ERR_UNSUPPORTED.
+ * Workspace sizes come from the *_fp8_workspace_size functions.
+ * ------------------------------------------------------------------------ */
+
+size_t mhc_coeffs_fp8_workspace_size(int64_t B, int32_t n, int64_t C);
+
+/* Steps (1)-(3) on an E4M3 X_t [B, n*C]; as mhc_coeffs otherwise.  Above 256
+ * rows the product runs in the persistent kernel of mhc_post_res_coeffs
+ * (product only), then the combine kernel. */
+int mhc_coeffs_fp8(int64_t B, int32_t n, int64_t C,
+                   const void *X_t, const void *phi,
+                   float alpha_pre, float alpha_post, float alpha_res,
+                   const float *b_pre, const float *b_post, const float *b_res,
+                   float *logits, float *r, float *H,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Step (4a): F_pre (E4M3 [B, C]) = sum_i H_pre[b, i] * X_t[b, i*C + c]. */
+int mhc_pre_fp8(int64_t B, int32_t n, int64_t C, const void *X_t, const float *H,
+                void *F_pre, void *stream);
+
+/* Step (4b): X_next (E4M3 [B, n*C]) from X_t and F_out (both E4M3). */
+int mhc_post_res_fp8(int64_t B, int32_t n, int64_t C, const void *X_t,
+                     const void *F_out, const float *H, void *X_next, void *stream);
+
+/* mhc_post_res_coeffs on the E4M3 residual stream: X_next is bitwise what
+ * mhc_post_res_fp8 writes; logits_next, r_next, H_next are what
+ * mhc_coeffs_fp8(X_next, ...) computes, up to fp32 summation order.
+ * Requires C % 32 == 0. */
+size_t mhc_post_res_coeffs_fp8_workspace_size(int64_t B, int32_t n, int64_t C);
+
+int mhc_post_res_coeffs_fp8(int64_t B, int32_t n, int64_t C,
+                            const void *X_t, const void *F_out, const float *H, void *X_next,
+                            const void *phi_next,
+                            float alpha_pre, float alpha_post, float alpha_res,
+                            const float *b_pre, const float *b_post, const float *b_res,
+                            float *logits_next, float *r_next, float *H_next,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

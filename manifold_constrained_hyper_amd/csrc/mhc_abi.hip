@@ -4,6 +4,7 @@
 #include "mhc_launch.h"
 
 #include <stdint.h>
+#include <cstdlib>
 
 namespace {
 
@@ -42,38 +43,50 @@ int64_t ncoef(int32_t n) { return (int64_t)n * n + 2 * (int64_t)n; }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? MHC_OK : MHC_ERR_HIP; }
 
-}  // namespace
+// The residual-stream element type of a call: bf16 (2 bytes) or E4M3 (1 byte,
+// the *_fp8 entry points, which need C % 16 == 0 for 16-byte vectors).
+struct Elt {
+  bool fp8;
+  size_t bytes() const { return fp8 ? 1 : 2; }
+};
 
-extern "C" {
+int check_shape_elt(int64_t B, int32_t n, int64_t C, Elt e) {
+  const int st = check_shape(B, n, C);
+  if (st != MHC_OK) return st;
+  if (e.fp8 && C % 16 != 0) return MHC_ERR_UNSUPPORTED;
+  return MHC_OK;
+}
 
-const char *mhc_status_string(int status) {
-  switch (status) {
-    case MHC_OK: return "MHC_OK";
-    case MHC_ERR_INVALID_ARG: return "MHC_ERR_INVALID_ARG: null pointer, negative size or overlapping buffers";
-    case MHC_ERR_UNSUPPORTED: return "MHC_ERR_UNSUPPORTED: n not in {1,2,4,8}, C % 8 != 0, size too large or misaligned pointer";
-    case MHC_ERR_WORKSPACE: return "MHC_ERR_WORKSPACE: workspace smaller than mhc_coeffs_workspace_size()";
-    case MHC_ERR_HIP: return "MHC_ERR_HIP: the HIP runtime reported an error";
-    default: return "MHC_ERR_UNKNOWN";
+// Which kernels mhc_coeffs(_fp8) runs: the one-launch small-B kernel, the
+// split-K product + combine (bf16), or the persistent product kernel of
+// mhc_post_res_fused.hip + combine (E4M3, or bf16 with MHC_GEMM_ALGO=2).  The
+// persistent kernel walks each stream in 32-channel k-steps, so it needs
+// C % 32 == 0; other hidden sizes take the small-B kernel at any B (it is
+// correct for every shape, only slower at large B).
+enum class CoeffsPath { kSmall, kSplitK, kPersistent };
+
+CoeffsPath coeffs_path(int64_t B, int32_t n, int64_t C, Elt e) {
+  if (mhc::use_coeffs_small(B, n, C)) return CoeffsPath::kSmall;
+  bool persistent = e.fp8;
+  if (const char *v = std::getenv("MHC_GEMM_ALGO"))
+    if (std::strtol(v, nullptr, 10) == 2) persistent = true;
+  if (!persistent) return CoeffsPath::kSplitK;
+  return C % 32 == 0 ? CoeffsPath::kPersistent : CoeffsPath::kSmall;
+}
+
+size_t coeffs_ws_bytes(int64_t B, int32_t n, int64_t C, Elt e) {
+  switch (coeffs_path(B, n, C, e)) {
+    case CoeffsPath::kSmall: return mhc::plan_coeffs_small(B, n, C).total_bytes;
+    case CoeffsPath::kPersistent: return mhc::plan_post_res_next(B, n, C).total_bytes;
+    default: return mhc::gemm_workspace_bytes(mhc::plan_gemm(B, n, C), B, n);
   }
 }
 
-size_t mhc_coeffs_workspace_size(int64_t B, int32_t n, int64_t C) {
-  if (check_shape(B, n, C) != MHC_OK || B == 0) return 0;
-  if (mhc::use_coeffs_small(B, n, C)) return mhc::plan_coeffs_small(B, n, C).total_bytes;
-  return mhc::gemm_workspace_bytes(mhc::plan_gemm(B, n, C), B, n);
-}
-
-int32_t mhc_coeffs_split_k(int64_t B, int32_t n, int64_t C) {
-  if (check_shape(B, n, C) != MHC_OK || B == 0) return 0;
-  if (mhc::use_coeffs_small(B, n, C)) return mhc::plan_coeffs_small(B, n, C).split;
-  return mhc::plan_gemm(B, n, C).split;
-}
-
-int mhc_coeffs(int64_t B, int32_t n, int64_t C, const void *X_t, const void *phi,
-               float alpha_pre, float alpha_post, float alpha_res, const float *b_pre,
-               const float *b_post, const float *b_res, float *logits, float *r, float *H,
-               void *workspace, size_t workspace_bytes, void *stream) {
-  int st = check_shape(B, n, C);
+int coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t, const void *phi,
+                float alpha_pre, float alpha_post, float alpha_res, const float *b_pre,
+                const float *b_post, const float *b_res, float *logits, float *r, float *H,
+                void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_shape_elt(B, n, C, e);
   if (st != MHC_OK) return st;
   if (B == 0) return MHC_OK;
   if (!X_t || !phi || !b_pre || !b_post || !b_res || !logits || !r || !H || !workspace)
@@ -83,12 +96,10 @@ int mhc_coeffs(int64_t B, int32_t n, int64_t C, const void *X_t, const void *phi
       !aligned(H, 4))
     return MHC_ERR_UNSUPPORTED;
 
-  const bool small = mhc::use_coeffs_small(B, n, C);
-  const mhc::GemmPlan plan = mhc::plan_gemm(B, n, C);
-  const mhc::SmallPlan splan = mhc::plan_coeffs_small(B, n, C);
-  const size_t ws_need = small ? splan.total_bytes : mhc::gemm_workspace_bytes(plan, B, n);
+  const CoeffsPath path = coeffs_path(B, n, C, e);
+  const size_t ws_need = coeffs_ws_bytes(B, n, C, e);
   const int64_t N = ncoef(n), K = (int64_t)n * C;
-  const Span in[] = {span(X_t, (size_t)B * K * 2), span(phi, (size_t)K * N * 2),
+  const Span in[] = {span(X_t, (size_t)B * K * e.bytes()), span(phi, (size_t)K * N * 2),
                      span(b_pre, (size_t)n * 4), span(b_post, (size_t)n * 4),
                      span(b_res, (size_t)n * n * 4)};
   const Span out[] = {span(logits, (size_t)B * N * 4), span(r, (size_t)B * 4),
@@ -103,10 +114,20 @@ int mhc_coeffs(int64_t B, int32_t n, int64_t C, const void *X_t, const void *phi
   if (workspace_bytes < ws_need) return MHC_ERR_WORKSPACE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (small)
-    return from_hip(mhc::launch_coeffs_small(splan, n, B, C, X_t, phi, alpha_pre, alpha_post,
-                                             alpha_res, b_pre, b_post, b_res, logits, r, H,
-                                             workspace, s));
+  if (path == CoeffsPath::kSmall)
+    return from_hip(mhc::launch_coeffs_small(mhc::plan_coeffs_small(B, n, C), n, e.fp8, B, C, X_t,
+                                             phi, alpha_pre, alpha_post, alpha_res, b_pre, b_post,
+                                             b_res, logits, r, H, workspace, s));
+  if (path == CoeffsPath::kPersistent) {
+    const mhc::FusedPlan plan = mhc::plan_post_res_next(B, n, C);
+    st = from_hip(mhc::launch_post_res_next(plan, n, e.fp8 ? mhc::kFusedCoeffsFp8 : mhc::kFusedCoeffsBf16,
+                                            B, C, X_t, nullptr, nullptr, nullptr, phi, workspace, s));
+    if (st != MHC_OK) return st;
+    return from_hip(mhc::launch_coeff_sinkhorn(n, B, C, plan.split, static_cast<const float *>(workspace),
+                                               alpha_pre, alpha_post, alpha_res, b_pre, b_post,
+                                               b_res, logits, r, H, s));
+  }
+  const mhc::GemmPlan plan = mhc::plan_gemm(B, n, C);
   float *ws = static_cast<float *>(workspace);
   st = from_hip(mhc::launch_gemm_rms(plan, n, B, C, X_t, phi, ws, s));
   if (st != MHC_OK) return st;
@@ -114,49 +135,53 @@ int mhc_coeffs(int64_t B, int32_t n, int64_t C, const void *X_t, const void *phi
                                              alpha_res, b_pre, b_post, b_res, logits, r, H, s));
 }
 
-int mhc_pre(int64_t B, int32_t n, int64_t C, const void *X_t, const float *H, void *F_pre,
-            void *stream) {
-  int st = check_shape(B, n, C);
+int pre_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t, const float *H,
+             void *F_pre, void *stream) {
+  int st = check_shape_elt(B, n, C, e);
   if (st != MHC_OK) return st;
   if (B == 0) return MHC_OK;
   if (!X_t || !H || !F_pre) return MHC_ERR_INVALID_ARG;
   if (!aligned(X_t, 16) || !aligned(F_pre, 16) || !aligned(H, 4)) return MHC_ERR_UNSUPPORTED;
   const int64_t N = ncoef(n);
-  const Span o = span(F_pre, (size_t)B * C * 2);
-  if (overlaps(o, span(X_t, (size_t)B * n * C * 2)) || overlaps(o, span(H, (size_t)B * N * 4)))
+  const Span o = span(F_pre, (size_t)B * C * e.bytes());
+  if (overlaps(o, span(X_t, (size_t)B * n * C * e.bytes())) || overlaps(o, span(H, (size_t)B * N * 4)))
     return MHC_ERR_INVALID_ARG;
-  return from_hip(mhc::launch_pre(n, B, C, X_t, H, F_pre, static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return from_hip(e.fp8 ? mhc::launch_pre_fp8(n, B, C, X_t, H, F_pre, s)
+                        : mhc::launch_pre(n, B, C, X_t, H, F_pre, s));
 }
 
-int mhc_post_res(int64_t B, int32_t n, int64_t C, const void *X_t, const void *F_out,
-                 const float *H, void *X_next, void *stream) {
-  int st = check_shape(B, n, C);
+int post_res_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t, const void *F_out,
+                  const float *H, void *X_next, void *stream) {
+  int st = check_shape_elt(B, n, C, e);
   if (st != MHC_OK) return st;
   if (B == 0) return MHC_OK;
   if (!X_t || !F_out || !H || !X_next) return MHC_ERR_INVALID_ARG;
   if (!aligned(X_t, 16) || !aligned(F_out, 16) || !aligned(X_next, 16) || !aligned(H, 4))
     return MHC_ERR_UNSUPPORTED;
   const int64_t N = ncoef(n);
-  const Span o = span(X_next, (size_t)B * n * C * 2);
-  if (overlaps(o, span(X_t, (size_t)B * n * C * 2)) || overlaps(o, span(F_out, (size_t)B * C * 2)) ||
-      overlaps(o, span(H, (size_t)B * N * 4)))
+  const Span o = span(X_next, (size_t)B * n * C * e.bytes());
+  if (overlaps(o, span(X_t, (size_t)B * n * C * e.bytes())) ||
+      overlaps(o, span(F_out, (size_t)B * C * e.bytes())) || overlaps(o, span(H, (size_t)B * N * 4)))
     return MHC_ERR_INVALID_ARG;
-  return from_hip(mhc::launch_post_res(n, B, C, X_t, F_out, H, X_next,
-                                       static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return from_hip(e.fp8 ? mhc::launch_post_res_fp8(n, B, C, X_t, F_out, H, X_next, s)
+                        : mhc::launch_post_res(n, B, C, X_t, F_out, H, X_next, s));
 }
 
-size_t mhc_post_res_coeffs_workspace_size(int64_t B, int32_t n, int64_t C) {
-  if (check_shape(B, n, C) != MHC_OK || B == 0 || C % 32 != 0) return 0;
+size_t post_res_coeffs_ws_bytes(int64_t B, int32_t n, int64_t C, Elt e) {
+  if (check_shape_elt(B, n, C, e) != MHC_OK || B == 0 || C % 32 != 0) return 0;
   if (mhc::use_coeffs_small(B, n, C)) return mhc::plan_coeffs_small(B, n, C).total_bytes;
   return mhc::plan_post_res_next(B, n, C).total_bytes;
 }
 
-int mhc_post_res_coeffs(int64_t B, int32_t n, int64_t C, const void *X_t, const void *F_out,
-                        const float *H, void *X_next, const void *phi_next, float alpha_pre,
-                        float alpha_post, float alpha_res, const float *b_pre, const float *b_post,
-                        const float *b_res, float *logits_next, float *r_next, float *H_next,
-                        void *workspace, size_t workspace_bytes, void *stream) {
-  int st = check_shape(B, n, C);
+int post_res_coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t,
+                         const void *F_out, const float *H, void *X_next, const void *phi_next,
+                         float alpha_pre, float alpha_post, float alpha_res, const float *b_pre,
+                         const float *b_post, const float *b_res, float *logits_next,
+                         float *r_next, float *H_next, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+  int st = check_shape_elt(B, n, C, e);
   if (st != MHC_OK) return st;
   if (C % 32 != 0) return MHC_ERR_UNSUPPORTED;
   if (B == 0) return MHC_OK;
@@ -171,13 +196,14 @@ int mhc_post_res_coeffs(int64_t B, int32_t n, int64_t C, const void *X_t, const 
   // decode sizes re-reading X_next costs less than the fused kernel's setup).
   const bool small = mhc::use_coeffs_small(B, n, C);
   const mhc::FusedPlan plan = mhc::plan_post_res_next(B, n, C);
-  const size_t ws_need = small ? mhc::plan_coeffs_small(B, n, C).total_bytes : plan.total_bytes;
+  const size_t ws_need = post_res_coeffs_ws_bytes(B, n, C, e);
   const int64_t N = ncoef(n), K = (int64_t)n * C;
-  const Span in[] = {span(X_t, (size_t)B * K * 2), span(F_out, (size_t)B * C * 2),
+  const size_t eb = e.bytes();
+  const Span in[] = {span(X_t, (size_t)B * K * eb), span(F_out, (size_t)B * C * eb),
                      span(H, (size_t)B * N * 4), span(phi_next, (size_t)K * N * 2),
                      span(b_pre, (size_t)n * 4), span(b_post, (size_t)n * 4),
                      span(b_res, (size_t)n * n * 4)};
-  const Span out[] = {span(X_next, (size_t)B * K * 2), span(logits_next, (size_t)B * N * 4),
+  const Span out[] = {span(X_next, (size_t)B * K * eb), span(logits_next, (size_t)B * N * 4),
                       span(r_next, (size_t)B * 4), span(H_next, (size_t)B * N * 4),
                       span(workspace, ws_need)};
   for (const Span &o : out)
@@ -190,19 +216,121 @@ int mhc_post_res_coeffs(int64_t B, int32_t n, int64_t C, const void *X_t, const 
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (small) {
-    st = from_hip(mhc::launch_post_res(n, B, C, X_t, F_out, H, X_next, s));
+    st = from_hip(e.fp8 ? mhc::launch_post_res_fp8(n, B, C, X_t, F_out, H, X_next, s)
+                        : mhc::launch_post_res(n, B, C, X_t, F_out, H, X_next, s));
     if (st != MHC_OK) return st;
-    return from_hip(mhc::launch_coeffs_small(mhc::plan_coeffs_small(B, n, C), n, B, C, X_next,
-                                             phi_next, alpha_pre, alpha_post, alpha_res, b_pre,
-                                             b_post, b_res, logits_next, r_next, H_next,
+    return from_hip(mhc::launch_coeffs_small(mhc::plan_coeffs_small(B, n, C), n, e.fp8, B, C,
+                                             X_next, phi_next, alpha_pre, alpha_post, alpha_res,
+                                             b_pre, b_post, b_res, logits_next, r_next, H_next,
                                              workspace, s));
   }
-  st = from_hip(mhc::launch_post_res_next(plan, n, B, C, X_t, F_out, H, X_next, phi_next,
-                                          workspace, s));
+  st = from_hip(mhc::launch_post_res_next(plan, n, e.fp8 ? mhc::kFusedApplyFp8 : mhc::kFusedApplyBf16,
+                                          B, C, X_t, F_out, H, X_next, phi_next, workspace, s));
   if (st != MHC_OK) return st;
   return from_hip(mhc::launch_coeff_sinkhorn(n, B, C, plan.split, static_cast<const float *>(workspace),
                                              alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res,
                                              logits_next, r_next, H_next, s));
+}
+
+constexpr Elt kBf16{false}, kFp8{true};
+
+}  // namespace
+
+extern "C" {
+
+const char *mhc_status_string(int status) {
+  switch (status) {
+    case MHC_OK: return "MHC_OK";
+    case MHC_ERR_INVALID_ARG: return "MHC_ERR_INVALID_ARG: null pointer, negative size or overlapping buffers";
+    case MHC_ERR_UNSUPPORTED: return "MHC_ERR_UNSUPPORTED: n not in {1,2,4,8}, C % 8 != 0 (C % 16 for E4M3, C % 32 for the fused call), size too large or misaligned pointer";
+    case MHC_ERR_WORKSPACE: return "MHC_ERR_WORKSPACE: workspace smaller than the call's workspace-size function returns";
+    case MHC_ERR_HIP: return "MHC_ERR_HIP: the HIP runtime reported an error";
+    default: return "MHC_ERR_UNKNOWN";
+  }
+}
+
+size_t mhc_coeffs_workspace_size(int64_t B, int32_t n, int64_t C) {
+  if (check_shape(B, n, C) != MHC_OK || B == 0) return 0;
+  return coeffs_ws_bytes(B, n, C, kBf16);
+}
+
+int32_t mhc_coeffs_split_k(int64_t B, int32_t n, int64_t C) {
+  if (check_shape(B, n, C) != MHC_OK || B == 0) return 0;
+  switch (coeffs_path(B, n, C, kBf16)) {
+    case CoeffsPath::kSmall: return mhc::plan_coeffs_small(B, n, C).split;
+    case CoeffsPath::kPersistent: return mhc::plan_post_res_next(B, n, C).split;
+    default: return mhc::plan_gemm(B, n, C).split;
+  }
+}
+
+int mhc_coeffs(int64_t B, int32_t n, int64_t C, const void *X_t, const void *phi,
+               float alpha_pre, float alpha_post, float alpha_res, const float *b_pre,
+               const float *b_post, const float *b_res, float *logits, float *r, float *H,
+               void *workspace, size_t workspace_bytes, void *stream) {
+  return coeffs_impl(kBf16, B, n, C, X_t, phi, alpha_pre, alpha_post, alpha_res, b_pre, b_post,
+                     b_res, logits, r, H, workspace, workspace_bytes, stream);
+}
+
+int mhc_pre(int64_t B, int32_t n, int64_t C, const void *X_t, const float *H, void *F_pre,
+            void *stream) {
+  return pre_impl(kBf16, B, n, C, X_t, H, F_pre, stream);
+}
+
+int mhc_post_res(int64_t B, int32_t n, int64_t C, const void *X_t, const void *F_out,
+                 const float *H, void *X_next, void *stream) {
+  return post_res_impl(kBf16, B, n, C, X_t, F_out, H, X_next, stream);
+}
+
+size_t mhc_post_res_coeffs_workspace_size(int64_t B, int32_t n, int64_t C) {
+  return post_res_coeffs_ws_bytes(B, n, C, kBf16);
+}
+
+int mhc_post_res_coeffs(int64_t B, int32_t n, int64_t C, const void *X_t, const void *F_out,
+                        const float *H, void *X_next, const void *phi_next, float alpha_pre,
+                        float alpha_post, float alpha_res, const float *b_pre, const float *b_post,
+                        const float *b_res, float *logits_next, float *r_next, float *H_next,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+  return post_res_coeffs_impl(kBf16, B, n, C, X_t, F_out, H, X_next, phi_next, alpha_pre,
+                              alpha_post, alpha_res, b_pre, b_post, b_res, logits_next, r_next,
+                              H_next, workspace, workspace_bytes, stream);
+}
+
+size_t mhc_coeffs_fp8_workspace_size(int64_t B, int32_t n, int64_t C) {
+  if (check_shape_elt(B, n, C, kFp8) != MHC_OK || B == 0) return 0;
+  return coeffs_ws_bytes(B, n, C, kFp8);
+}
+
+int mhc_coeffs_fp8(int64_t B, int32_t n, int64_t C, const void *X_t, const void *phi,
+                   float alpha_pre, float alpha_post, float alpha_res, const float *b_pre,
+                   const float *b_post, const float *b_res, float *logits, float *r, float *H,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+  return coeffs_impl(kFp8, B, n, C, X_t, phi, alpha_pre, alpha_post, alpha_res, b_pre, b_post,
+                     b_res, logits, r, H, workspace, workspace_bytes, stream);
+}
+
+int mhc_pre_fp8(int64_t B, int32_t n, int64_t C, const void *X_t, const float *H, void *F_pre,
+                void *stream) {
+  return pre_impl(kFp8, B, n, C, X_t, H, F_pre, stream);
+}
+
+int mhc_post_res_fp8(int64_t B, int32_t n, int64_t C, const void *X_t, const void *F_out,
+                     const float *H, void *X_next, void *stream) {
+  return post_res_impl(kFp8, B, n, C, X_t, F_out, H, X_next, stream);
+}
+
+size_t mhc_post_res_coeffs_fp8_workspace_size(int64_t B, int32_t n, int64_t C) {
+  return post_res_coeffs_ws_bytes(B, n, C, kFp8);
+}
+
+int mhc_post_res_coeffs_fp8(int64_t B, int32_t n, int64_t C, const void *X_t, const void *F_out,
+                            const float *H, void *X_next, const void *phi_next, float alpha_pre,
+                            float alpha_post, float alpha_res, const float *b_pre,
+                            const float *b_post, const float *b_res, float *logits_next,
+                            float *r_next, float *H_next, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  return post_res_coeffs_impl(kFp8, B, n, C, X_t, F_out, H, X_next, phi_next, alpha_pre,
+                              alpha_post, alpha_res, b_pre, b_post, b_res, logits_next, r_next,
+                              H_next, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

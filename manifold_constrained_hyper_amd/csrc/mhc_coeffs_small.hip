@@ -1,4 +1,5 @@
-// Small-B (decode) path of mhc_coeffs: steps (1)-(3) in one launch.
+// Small-B (decode) path of mhc_coeffs (and mhc_coeffs_fp8): steps (1)-(3) in
+// one launch.
 //
 // [mHC-cutile] (page "mHC 算法分析 & cutile 高效实现") section 2.1: one
 // product logits = X_t . phi for all N columns; section 2.2: the row sums of
@@ -61,9 +62,9 @@ struct SmallTile {
   static_assert(KS % 128 == 0, "slice splits evenly over 4 waves");
 };
 
-template <int NS>
+template <int NS, bool FP8X>
 __global__ __launch_bounds__(256) void coeffs_small_kernel(
-    const uint16_t *__restrict__ X, const uint16_t *__restrict__ phi, int B, int K, int S,
+    const uint8_t *__restrict__ X, const uint16_t *__restrict__ phi, int B, int K, int S,
     float inv_k, float alpha_pre, float alpha_post, float alpha_res,
     const float *__restrict__ b_pre, const float *__restrict__ b_post,
     const float *__restrict__ b_res, float *__restrict__ logits, float *__restrict__ r_out,
@@ -86,12 +87,18 @@ __global__ __launch_bounds__(256) void coeffs_small_kernel(
   // A operands of this wave's k-steps: row row0+m (rows past B read row
   // B-1; their results are not written), k = step*32 + 8g .. +7 (zero past
   // the slice).
-  const uint16_t *xr = X + (size_t)min(row0 + m, B - 1) * K;
+  // X in E4M3 (FP8X) is widened exactly to bf16 for the matrix core.
+  constexpr int EB = FP8X ? 1 : 2;
+  const uint8_t *xr = X + (size_t)min(row0 + m, B - 1) * K * EB;
   bf16x8 a[T::KSW];
 #pragma unroll
   for (int q = 0; q < T::KSW; ++q) {
     const int k = k_lo + (wave * T::KSW + q) * 32 + 8 * g;
-    const u32x4 v = load16(xr + min(k, K - 8));
+    u32x4 v;
+    if constexpr (FP8X)
+      v = fp8x8_to_bf16(*reinterpret_cast<const u32x2 *>(xr + min(k, K - 8)));
+    else
+      v = load16(xr + (size_t)min(k, K - 8) * 2);
     a[q] = __builtin_bit_cast(bf16x8, k < k_hi ? v : u32x4{0u, 0u, 0u, 0u});
   }
 
@@ -246,7 +253,7 @@ unsigned long long next_epoch() {
   return e;
 }
 
-template <int NS>
+template <int NS, bool FP8X>
 hipError_t launch_small_n(const SmallPlan &p, int64_t B, int64_t C, const void *X,
                           const void *phi, float ap, float aq, float ar, const float *bp,
                           const float *bq, const float *br, float *logits, float *r, float *H,
@@ -254,8 +261,8 @@ hipError_t launch_small_n(const SmallPlan &p, int64_t B, int64_t C, const void *
   char *base = static_cast<char *>(ws_base);
   const dim3 grid((uint32_t)p.row_tiles, (uint32_t)p.split);
   const float inv_k = (float)(1.0 / (double)(NS * C));
-  coeffs_small_kernel<NS><<<grid, 256, 0, st>>>(
-      static_cast<const uint16_t *>(X), static_cast<const uint16_t *>(phi), (int)B,
+  coeffs_small_kernel<NS, FP8X><<<grid, 256, 0, st>>>(
+      static_cast<const uint8_t *>(X), static_cast<const uint16_t *>(phi), (int)B,
       (int)(NS * C), p.split, inv_k, ap, aq, ar, bp, bq, br, logits, r, H,
       reinterpret_cast<float *>(base), reinterpret_cast<unsigned long long *>(base + p.ctr_offset),
       next_epoch());
@@ -292,17 +299,26 @@ bool use_coeffs_small(int64_t B, int n, int64_t C) {
   return B <= max_b && plan_coeffs_small(B, n, C).split <= kSmallMaxSplit;
 }
 
-hipError_t launch_coeffs_small(const SmallPlan &p, int n, int64_t B, int64_t C, const void *X,
-                               const void *phi, float ap, float aq, float ar, const float *bp,
-                               const float *bq, const float *br, float *logits, float *r,
-                               float *H, void *ws, hipStream_t st) {
+template <bool FP8X>
+hipError_t launch_small_x(const SmallPlan &p, int n, int64_t B, int64_t C, const void *X,
+                          const void *phi, float ap, float aq, float ar, const float *bp,
+                          const float *bq, const float *br, float *logits, float *r, float *H,
+                          void *ws, hipStream_t st) {
   switch (n) {
-    case 1: return launch_small_n<1>(p, B, C, X, phi, ap, aq, ar, bp, bq, br, logits, r, H, ws, st);
-    case 2: return launch_small_n<2>(p, B, C, X, phi, ap, aq, ar, bp, bq, br, logits, r, H, ws, st);
-    case 4: return launch_small_n<4>(p, B, C, X, phi, ap, aq, ar, bp, bq, br, logits, r, H, ws, st);
-    case 8: return launch_small_n<8>(p, B, C, X, phi, ap, aq, ar, bp, bq, br, logits, r, H, ws, st);
+    case 1: return launch_small_n<1, FP8X>(p, B, C, X, phi, ap, aq, ar, bp, bq, br, logits, r, H, ws, st);
+    case 2: return launch_small_n<2, FP8X>(p, B, C, X, phi, ap, aq, ar, bp, bq, br, logits, r, H, ws, st);
+    case 4: return launch_small_n<4, FP8X>(p, B, C, X, phi, ap, aq, ar, bp, bq, br, logits, r, H, ws, st);
+    case 8: return launch_small_n<8, FP8X>(p, B, C, X, phi, ap, aq, ar, bp, bq, br, logits, r, H, ws, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_coeffs_small(const SmallPlan &p, int n, bool fp8_x, int64_t B, int64_t C,
+                               const void *X, const void *phi, float ap, float aq, float ar,
+                               const float *bp, const float *bq, const float *br, float *logits,
+                               float *r, float *H, void *ws, hipStream_t st) {
+  return fp8_x ? launch_small_x<true>(p, n, B, C, X, phi, ap, aq, ar, bp, bq, br, logits, r, H, ws, st)
+               : launch_small_x<false>(p, n, B, C, X, phi, ap, aq, ar, bp, bq, br, logits, r, H, ws, st);
 }
 
 }  // namespace mhc

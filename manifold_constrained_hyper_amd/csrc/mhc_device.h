@@ -17,6 +17,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -27,6 +28,29 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   f32x2 v = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// FP8 E4M3 (the OCP "fn" encoding: bias 7, max 448, no infinities), four
+// values per 32-bit word, byte k holding element k.  gfx950's conversions use
+// this encoding and round to nearest even; narrowing would give NaN from
+// +-464 up, so values are clamped to +-448 first (saturation).  Widening to
+// fp32 (and from there to bf16) is exact.
+__device__ __forceinline__ f32x2 fp8_lo2(uint32_t w) {  // elements 0, 1
+  return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+}
+__device__ __forceinline__ f32x2 fp8_hi2(uint32_t w) {  // elements 2, 3
+  return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+}
+__device__ __forceinline__ float sat_e4m3(float x) { return __builtin_amdgcn_fmed3f(x, -448.0f, 448.0f); }
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+  const int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(a), sat_e4m3(b), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(c), sat_e4m3(d), w, true);
+}
+// Eight E4M3 values (two words) -> the same eight values as bf16 (exact).
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(u32x2 w) {
+  const f32x2 a = fp8_lo2(w[0]), b = fp8_hi2(w[0]), c = fp8_lo2(w[1]), d = fp8_hi2(w[1]);
+  return u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1]), pack_bf16x2(c[0], c[1]),
+               pack_bf16x2(d[0], d[1])};
 }
 
 // 16-byte global load / store.  Streaming data is touched once, so stores

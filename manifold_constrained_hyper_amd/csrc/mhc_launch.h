@@ -56,9 +56,22 @@ struct FusedPlan {
   size_t partial_bytes, dummy_offset, dummy_bytes, phip_offset, phip_bytes, zero_offset, total_bytes;
 };
 FusedPlan plan_post_res_next(int64_t B, int n, int64_t C);
-hipError_t launch_post_res_next(const FusedPlan &p, int n, int64_t B, int64_t C, const void *X,
-                                const void *F, const float *H, void *Y, const void *phi_next,
-                                void *ws_base, hipStream_t st);
+// What the persistent kernel of mhc_post_res_fused.hip does per step.
+enum FusedMode : int {
+  kFusedApplyBf16 = 0,   // bf16 X_t, F_out -> bf16 X_next, plus X_next . phi_next
+  kFusedApplyFp8 = 1,    // E4M3 X_t, F_out -> E4M3 X_next, plus X_next . phi_next
+  kFusedCoeffsFp8 = 2,   // X . phi only, X in E4M3
+  kFusedCoeffsBf16 = 3,  // X . phi only, X in bf16
+};
+hipError_t launch_post_res_next(const FusedPlan &p, int n, int mode, int64_t B, int64_t C,
+                                const void *X, const void *F, const float *H, void *Y,
+                                const void *phi_next, void *ws_base, hipStream_t st);
+
+// FP8 (E4M3) streaming kernels (mhc_stream_fp8.hip).
+hipError_t launch_pre_fp8(int n, int64_t B, int64_t C, const void *X, const float *H,
+                          void *F_pre, hipStream_t st);
+hipError_t launch_post_res_fp8(int n, int64_t B, int64_t C, const void *X, const void *F_out,
+                               const float *H, void *X_next, hipStream_t st);
 
 // Small-B (decode) path of mhc_coeffs: product, split-K reduction and finish
 // in one launch (mhc_coeffs_small.hip).
@@ -77,8 +90,9 @@ struct SmallPlan {
 };
 SmallPlan plan_coeffs_small(int64_t B, int n, int64_t C);
 bool use_coeffs_small(int64_t B, int n, int64_t C);
-hipError_t launch_coeffs_small(const SmallPlan &p, int n, int64_t B, int64_t C, const void *X,
-                               const void *phi, float alpha_pre, float alpha_post,
+// fp8_x: X holds E4M3 values (widened exactly to bf16 for the product).
+hipError_t launch_coeffs_small(const SmallPlan &p, int n, bool fp8_x, int64_t B, int64_t C,
+                               const void *X, const void *phi, float alpha_pre, float alpha_post,
                                float alpha_res, const float *b_pre, const float *b_post,
                                const float *b_res, float *logits, float *r, float *H, void *ws,
                                hipStream_t st);

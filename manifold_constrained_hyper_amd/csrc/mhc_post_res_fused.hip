@@ -55,6 +55,7 @@
 
 #include <atomic>
 #include <cstdlib>
+#include <type_traits>
 
 namespace mhc {
 
@@ -90,12 +91,23 @@ struct Step {
   int row0, c0, c_end, slot;
 };
 
-template <int NS>
+// What the kernel reads, writes and multiplies (FusedMode, mhc_launch.h).
+template <int MODE>
+struct FusedIO {
+  static constexpr bool FP8 = MODE == kFusedApplyFp8 || MODE == kFusedCoeffsFp8;
+  static constexpr bool APPLY = MODE == kFusedApplyBf16 || MODE == kFusedApplyFp8;
+  static constexpr int EB = FP8 ? 1 : 2;  // bytes per element
+  using vec = typename std::conditional<FP8, u32x2, u32x4>::type;  // 8 elements per lane
+};
+
+template <int NS, int MODE>
 __global__ __launch_bounds__(1024) void post_res_next_kernel(
-    const uint16_t *__restrict__ X, const uint16_t *__restrict__ F, const float *__restrict__ H,
-    uint16_t *__restrict__ Y, const uint16_t *__restrict__ phip, float *__restrict__ ws,
+    const uint8_t *__restrict__ X, const uint8_t *__restrict__ F, const float *__restrict__ H,
+    uint8_t *__restrict__ Y, const uint16_t *__restrict__ phip, float *__restrict__ ws,
     float *__restrict__ dummy, int B, int C, int spu, int S, int U) {
   using T = FusedTile<NS>;
+  using IO = FusedIO<MODE>;
+  using vec = typename IO::vec;
   __shared__ __attribute__((aligned(1024))) char lds[T::LDS_BYTES];
   float *red = reinterpret_cast<float *>(lds + (T::SEPARATE ? T::TILE_BYTES : 0));
 
@@ -132,17 +144,20 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
   // rows past B, read the nearest in-range address instead: they then
   // compute exactly the values the owning lane writes, so their (duplicate)
   // stores rewrite identical bytes, and they enter the LDS tile as zeros.
-  auto load_set = [&](u32x4 (&xv)[NS], u32x4 &fv, uint32_t (&hv)[T::HV], const Step &sp) {
+  auto load_set = [&](vec (&xv)[NS], vec &fv, uint32_t (&hv)[T::HV], const Step &sp) {
     const int rr = uniform(min(sp.row0 + wave, B - 1));
-    const float *hr = H + (size_t)rr * T::N + NS;
+    if constexpr (IO::APPLY) {
+      const float *hr = H + (size_t)rr * T::N + NS;
 #pragma unroll
-    for (int k = 0; k < T::HV; ++k) hv[k] = __builtin_bit_cast(uint32_t, hr[min(k * 64 + lane, T::NH - 1)]);
+      for (int k = 0; k < T::HV; ++k) hv[k] = __builtin_bit_cast(uint32_t, hr[min(k * 64 + lane, T::NH - 1)]);
+    }
     const int c = min(sp.c0 + 8 * lane, sp.c_end - 8);
-    const uint16_t *xr = X + (size_t)rr * NS * C;
+    const uint8_t *xr = X + (size_t)rr * NS * C * IO::EB;
 #pragma unroll
     for (int j = 0; j < NS; ++j)
-      xv[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xr + (size_t)j * C + c));
-    fv = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(F + (size_t)rr * C + c));
+      xv[j] = __builtin_nontemporal_load(reinterpret_cast<const vec *>(xr + ((size_t)j * C + c) * IO::EB));
+    if constexpr (IO::APPLY)
+      fv = __builtin_nontemporal_load(reinterpret_cast<const vec *>(F + ((size_t)rr * C + c) * IO::EB));
   };
 
   // Sum the 16 waves' accumulators of step `sp` (in wave order) into its
@@ -174,7 +189,7 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
   };
 
   // One step on the loads in (xv, fv, hv); refills them with step t_pref.
-  auto step = [&](int t, u32x4 (&xv)[NS], u32x4 &fv, uint32_t (&hv)[T::HV], int t_pref) {
+  auto step = [&](int t, vec (&xv)[NS], vec &fv, uint32_t (&hv)[T::HV], int t_pref) {
     const Step sp = step_at(t);
     const int row = sp.row0 + wave;
     const bool live = row < B;
@@ -184,61 +199,133 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
     const int cst = min(c, sp.c_end - 8);
 
     // apply (row `rr`, channels c .. c+7 of every stream); the coefficients
-    // are broadcast from the lanes of hv.
+    // are broadcast from the lanes of hv.  `out` goes to HBM; the LDS tile
+    // gets the same values as bf16 (tile_vec below).
     auto coef = [&](int k) {
       return __builtin_bit_cast(float, __builtin_amdgcn_readlane((int)hv[k / 64], k % 64));
     };
-    u32x4 out[NS];
-    if constexpr (NS <= 4) {
-      float hpost[NS], hres[NS][NS];
-#pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        hpost[i] = coef(i);
-#pragma unroll
-        for (int j = 0; j < NS; ++j) hres[i][j] = coef(NS + i * NS + j);
-      }
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float f0 = bf16_lo(fv[w]), f1 = bf16_hi(fv[w]);
-        float x0[NS], x1[NS];
-#pragma unroll
-        for (int j = 0; j < NS; ++j) {
-          x0[j] = bf16_lo(xv[j][w]);
-          x1[j] = bf16_hi(xv[j][w]);
-        }
+    vec out[NS];
+    if constexpr (MODE == kFusedApplyBf16) {
+      if constexpr (NS <= 4) {
+        float hpost[NS], hres[NS][NS];
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
-          float a0 = hpost[i] * f0, a1 = hpost[i] * f1;
+          hpost[i] = coef(i);
 #pragma unroll
-          for (int j = 0; j < NS; ++j) {
-            a0 = fmaf(hres[i][j], x0[j], a0);
-            a1 = fmaf(hres[i][j], x1[j], a1);
-          }
-          out[i][w] = pack_bf16x2(a0, a1);
+          for (int j = 0; j < NS; ++j) hres[i][j] = coef(NS + i * NS + j);
         }
-      }
-    } else {
-      // n = 8: output stream by output stream, so that only that stream's
-      // nine coefficients are held in scalar registers at a time (the same
-      // FMA chain per element as above).
-#pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        const float hp = coef(i);
-        float hr[NS];
-#pragma unroll
-        for (int j = 0; j < NS; ++j) hr[j] = coef(NS + i * NS + j);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          float a0 = hp * bf16_lo(fv[w]), a1 = hp * bf16_hi(fv[w]);
+          const float f0 = bf16_lo(fv[w]), f1 = bf16_hi(fv[w]);
+          float x0[NS], x1[NS];
 #pragma unroll
           for (int j = 0; j < NS; ++j) {
-            a0 = fmaf(hr[j], bf16_lo(xv[j][w]), a0);
-            a1 = fmaf(hr[j], bf16_hi(xv[j][w]), a1);
+            x0[j] = bf16_lo(xv[j][w]);
+            x1[j] = bf16_hi(xv[j][w]);
           }
-          out[i][w] = pack_bf16x2(a0, a1);
+#pragma unroll
+          for (int i = 0; i < NS; ++i) {
+            float a0 = hpost[i] * f0, a1 = hpost[i] * f1;
+#pragma unroll
+            for (int j = 0; j < NS; ++j) {
+              a0 = fmaf(hres[i][j], x0[j], a0);
+              a1 = fmaf(hres[i][j], x1[j], a1);
+            }
+            out[i][w] = pack_bf16x2(a0, a1);
+          }
+        }
+      } else {
+        // n = 8: output stream by output stream, so that only that stream's
+        // nine coefficients are held in scalar registers at a time (the same
+        // FMA chain per element as above).
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          const float hp = coef(i);
+          float hr[NS];
+#pragma unroll
+          for (int j = 0; j < NS; ++j) hr[j] = coef(NS + i * NS + j);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            float a0 = hp * bf16_lo(fv[w]), a1 = hp * bf16_hi(fv[w]);
+#pragma unroll
+            for (int j = 0; j < NS; ++j) {
+              a0 = fmaf(hr[j], bf16_lo(xv[j][w]), a0);
+              a1 = fmaf(hr[j], bf16_hi(xv[j][w]), a1);
+            }
+            out[i][w] = pack_bf16x2(a0, a1);
+          }
+        }
+      }
+    } else if constexpr (MODE == kFusedApplyFp8) {
+      // E4M3: each 8-byte vector is two words of four channels; the same FMA
+      // chain per element as post_res_fp8_kernel, then the E4M3 result is
+      // widened (exactly) for the tile.
+      if constexpr (NS <= 4) {
+        float hpost[NS], hres[NS][NS];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          hpost[i] = coef(i);
+#pragma unroll
+          for (int j = 0; j < NS; ++j) hres[i][j] = coef(NS + i * NS + j);
+        }
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          const f32x2 fl = fp8_lo2(fv[d]), fh = fp8_hi2(fv[d]);
+          const float f[4] = {fl[0], fl[1], fh[0], fh[1]};
+          float x[NS][4];
+#pragma unroll
+          for (int j = 0; j < NS; ++j) {
+            const f32x2 xl = fp8_lo2(xv[j][d]), xh = fp8_hi2(xv[j][d]);
+            x[j][0] = xl[0];
+            x[j][1] = xl[1];
+            x[j][2] = xh[0];
+            x[j][3] = xh[1];
+          }
+#pragma unroll
+          for (int i = 0; i < NS; ++i) {
+            float a[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              a[k] = hpost[i] * f[k];
+#pragma unroll
+              for (int j = 0; j < NS; ++j) a[k] = fmaf(hres[i][j], x[j][k], a[k]);
+            }
+            out[i][d] = pack_fp8x4(a[0], a[1], a[2], a[3]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          const float hp = coef(i);
+          float hr[NS];
+#pragma unroll
+          for (int j = 0; j < NS; ++j) hr[j] = coef(NS + i * NS + j);
+#pragma unroll
+          for (int d = 0; d < 2; ++d) {
+            const f32x2 fl = fp8_lo2(fv[d]), fh = fp8_hi2(fv[d]);
+            float a[4] = {hp * fl[0], hp * fl[1], hp * fh[0], hp * fh[1]};
+#pragma unroll
+            for (int j = 0; j < NS; ++j) {
+              const f32x2 xl = fp8_lo2(xv[j][d]), xh = fp8_hi2(xv[j][d]);
+              a[0] = fmaf(hr[j], xl[0], a[0]);
+              a[1] = fmaf(hr[j], xl[1], a[1]);
+              a[2] = fmaf(hr[j], xh[0], a[2]);
+              a[3] = fmaf(hr[j], xh[1], a[3]);
+            }
+            out[i][d] = pack_fp8x4(a[0], a[1], a[2], a[3]);
+          }
         }
       }
     }
+    // Stream i of the LDS tile (bf16): the apply's output, or X itself; the
+    // E4M3 values widen exactly.  Taken at the LDS write, before the refill
+    // overwrites xv, so no second copy is held across the stores.
+    auto tile_vec = [&](int i) -> u32x4 {
+      if constexpr (MODE == kFusedApplyBf16) return out[i];
+      else if constexpr (MODE == kFusedApplyFp8) return fp8x8_to_bf16(out[i]);
+      else if constexpr (MODE == kFusedCoeffsFp8) return fp8x8_to_bf16(xv[i]);
+      else return xv[i];
+    };
     // B operands of this wave's k-steps (global, L2-resident), in groups of
     // KB k-steps (all of them for n <= 4; for n = 8 the later groups are
     // loaded after the earlier ones are consumed).
@@ -255,10 +342,12 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
           b[q][nb] = __builtin_bit_cast(bf16x8, load16(phip + ((size_t)(kstep * T::NB + nb) * 64 + lane) * 8));
       }
     };
-    uint16_t *yr = Y + (size_t)rr * NS * C;
+    if constexpr (IO::APPLY) {
+      uint8_t *yr = Y + (size_t)rr * NS * C * IO::EB;
 #pragma unroll
-    for (int i = 0; i < NS; ++i)
-      __builtin_nontemporal_store(out[i], reinterpret_cast<u32x4 *>(yr + (size_t)i * C + cst));
+      for (int i = 0; i < NS; ++i)
+        __builtin_nontemporal_store(out[i], reinterpret_cast<vec *>(yr + ((size_t)i * C + cst) * IO::EB));
+    }
     // The first B group is issued before the refill (waiting for it then
     // never waits for the refill), except for n = 8, where holding it across
     // the refill would not fit the register budget.
@@ -269,7 +358,7 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
 #pragma unroll
     for (int i = 0; i < NS; ++i)
       *reinterpret_cast<u32x4 *>(my_lds_row + i * (kStepCh * 2) + wslot) =
-          (in_range && live) ? out[i] : u32x4{0u, 0u, 0u, 0u};
+          (in_range && live) ? tile_vec(i) : u32x4{0u, 0u, 0u, 0u};
     load_set(xv, fv, hv, step_at(t_pref));
     if constexpr (NS >= 8) load_b(0);
     __syncthreads();  // the tile is complete (and the flush has read red)
@@ -308,7 +397,7 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
   const int tl = nsteps - 1;
   if constexpr (NS >= 8) {
     // n = 8: one register set (two would not fit 128 VGPRs).
-    u32x4 xa[NS], fa;
+    vec xa[NS], fa;
     uint32_t ha[T::HV];
     load_set(xa, fa, ha, step_at(0));
     for (int t = 0; t < nsteps; ++t) step(t, xa, fa, ha, min(t + 1, tl));
@@ -317,7 +406,7 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
     // applied and multiplied, so each wave has two steps of loads in flight.
     // The loop always runs both steps (an odd last step runs after it), so
     // the waits at the top of each step only cover the set used there.
-    u32x4 xa[NS], fa, xb[NS], fb;
+    vec xa[NS], fa, xb[NS], fb;
     uint32_t ha[T::HV], hb[T::HV];
     load_set(xa, fa, ha, step_at(0));
     load_set(xb, fb, hb, step_at(min(1, tl)));
@@ -352,17 +441,30 @@ int device_cus() {
 
 }  // namespace
 
-template <int NS>
+template <int NS, int MODE>
 hipError_t launch_post_res_next_typed(int64_t B, int64_t C, int spu, int split, int grid_cap,
                                       const void *X, const void *F, const float *H, void *Y,
                                       const void *phip, float *ws, float *dummy, hipStream_t st) {
   const int64_t U = ((B + 15) / 16) * (int64_t)split;
   const int G = (int)(U < grid_cap ? U : grid_cap);
-  post_res_next_kernel<NS><<<dim3((uint32_t)G), 1024, 0, st>>>(
-      static_cast<const uint16_t *>(X), static_cast<const uint16_t *>(F), H,
-      static_cast<uint16_t *>(Y), static_cast<const uint16_t *>(phip), ws, dummy, (int)B, (int)C,
+  post_res_next_kernel<NS, MODE><<<dim3((uint32_t)G), 1024, 0, st>>>(
+      static_cast<const uint8_t *>(X), static_cast<const uint8_t *>(F), H,
+      static_cast<uint8_t *>(Y), static_cast<const uint16_t *>(phip), ws, dummy, (int)B, (int)C,
       spu, split, (int)U);
   return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_mode(int n, int64_t B, int64_t C, int spu, int split, int cap, const void *X,
+                       const void *F, const float *H, void *Y, const void *phip, float *ws,
+                       float *dummy, hipStream_t st) {
+  switch (n) {
+    case 1: return launch_post_res_next_typed<1, MODE>(B, C, spu, split, cap, X, F, H, Y, phip, ws, dummy, st);
+    case 2: return launch_post_res_next_typed<2, MODE>(B, C, spu, split, cap, X, F, H, Y, phip, ws, dummy, st);
+    case 4: return launch_post_res_next_typed<4, MODE>(B, C, spu, split, cap, X, F, H, Y, phip, ws, dummy, st);
+    case 8: return launch_post_res_next_typed<8, MODE>(B, C, spu, split, cap, X, F, H, Y, phip, ws, dummy, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 FusedPlan plan_post_res_next(int64_t B, int n, int64_t C) {
@@ -397,9 +499,9 @@ FusedPlan plan_post_res_next(int64_t B, int n, int64_t C) {
   return p;
 }
 
-hipError_t launch_post_res_next(const FusedPlan &p, int n, int64_t B, int64_t C, const void *X,
-                                const void *F, const float *H, void *Y, const void *phi_next,
-                                void *ws_base, hipStream_t st) {
+hipError_t launch_post_res_next(const FusedPlan &p, int n, int mode, int64_t B, int64_t C,
+                                const void *X, const void *F, const float *H, void *Y,
+                                const void *phi_next, void *ws_base, hipStream_t st) {
   char *base = static_cast<char *>(ws_base);
   void *phip = base + p.phip_offset;
   hipError_t e = launch_pack_phi(n, (int64_t)n * C, p.ksteps, phi_next, phip, base + p.zero_offset, st);
@@ -412,11 +514,11 @@ hipError_t launch_post_res_next(const FusedPlan &p, int n, int64_t B, int64_t C,
     const long v = std::strtol(env, nullptr, 10);
     if (v >= 1 && v <= 65535) cap = (int)v;
   }
-  switch (n) {
-    case 1: return launch_post_res_next_typed<1>(B, C, spu, p.split, cap, X, F, H, Y, phip, ws, dummy, st);
-    case 2: return launch_post_res_next_typed<2>(B, C, spu, p.split, cap, X, F, H, Y, phip, ws, dummy, st);
-    case 4: return launch_post_res_next_typed<4>(B, C, spu, p.split, cap, X, F, H, Y, phip, ws, dummy, st);
-    case 8: return launch_post_res_next_typed<8>(B, C, spu, p.split, cap, X, F, H, Y, phip, ws, dummy, st);
+  switch (mode) {
+    case kFusedApplyBf16: return launch_mode<kFusedApplyBf16>(n, B, C, spu, p.split, cap, X, F, H, Y, phip, ws, dummy, st);
+    case kFusedApplyFp8: return launch_mode<kFusedApplyFp8>(n, B, C, spu, p.split, cap, X, F, H, Y, phip, ws, dummy, st);
+    case kFusedCoeffsFp8: return launch_mode<kFusedCoeffsFp8>(n, B, C, spu, p.split, cap, X, F, H, Y, phip, ws, dummy, st);
+    case kFusedCoeffsBf16: return launch_mode<kFusedCoeffsBf16>(n, B, C, spu, p.split, cap, X, F, H, Y, phip, ws, dummy, st);
     default: return hipErrorInvalidValue;
   }
 }

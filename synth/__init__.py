@@ -93,3 +93,35 @@ def make_config(name, device="cpu"):
 def bf16_bits(t):
     """Raw bf16 bit patterns of a bf16 tensor as a numpy uint16 array (host copy)."""
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def to_e4m3(t):
+    """Round a tensor to FP8 E4M3 (the OCP "fn" encoding, round to nearest
+    even) after clamping to +-448; returns the raw codes as a uint8 tensor on
+    the same device."""
+    return t.float().clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def make_inputs_fp8(n, C, B, x_dist="normal", seed=0, device="cpu", row_chunk=512):
+    """make_inputs with X and F_out rounded to E4M3 (uint8 codes), for the FP8
+    residual-stream variant; phi and the biases are unchanged."""
+    inp = make_inputs(n, C, B, x_dist, seed, device, row_chunk)
+    for k in ("X", "F_out"):
+        src = inp[k]
+        out = torch.empty(src.shape, dtype=torch.uint8, device=src.device)
+        for lo in range(0, src.shape[0], row_chunk):
+            out[lo:lo + row_chunk] = to_e4m3(src[lo:lo + row_chunk])
+        inp[k] = out
+    inp["fp8"] = True
+    return inp
+
+
+def make_config_fp8(name, device="cpu"):
+    """FP8 inputs for one named workload of CONFIGS."""
+    cfg = CONFIGS[name]
+    return make_inputs_fp8(cfg["n"], cfg["C"], cfg["B"], cfg["x_dist"], cfg["seed"], device)
+
+
+def e4m3_codes(t):
+    """Raw E4M3 codes of a uint8 (or float8_e4m3fn) tensor as a numpy uint8 array."""
+    return t.detach().contiguous().view(torch.uint8).cpu().numpy()

@@ -141,3 +141,48 @@ def test_binding_raises_on_error_status():
     with pytest.raises(mhc.MhcError) as ei:
         mhc.mhc_pre(16, 3, 64, *_addrs(3), stream=0)
     assert ei.value.status == mhc.MHC_ERR_UNSUPPORTED
+
+
+def test_fp8_validation():
+    """The E4M3 calls: same rules as the bf16 ones, with one-byte elements
+    (overlap checks in bytes) and C % 16 == 0."""
+    X, H, F, Y = _addrs(4)
+    assert mhc.mhc_pre_fp8(0, 4, 64, None, None, None, stream=0, check=False) == mhc.MHC_OK
+    assert mhc.mhc_pre_fp8(16, 4, 24, X, H, F, stream=0, check=False) == mhc.MHC_ERR_UNSUPPORTED
+    assert mhc.mhc_pre_fp8(16, 4, 64, X, H, None, stream=0, check=False) == mhc.MHC_ERR_INVALID_ARG
+    # F_pre right after X_t's 16*4*64 bytes does not overlap; one byte earlier does
+    assert mhc.mhc_pre_fp8(16, 4, 64, X, H, X + 16 * 4 * 64 - 16, stream=0, check=False) == mhc.MHC_ERR_INVALID_ARG
+    assert mhc.mhc_post_res_fp8(16, 4, 40, X, F, H, Y, stream=0, check=False) == mhc.MHC_ERR_UNSUPPORTED
+    assert mhc.mhc_post_res_fp8(16, 4, 64, X, F, H, X, stream=0, check=False) == mhc.MHC_ERR_INVALID_ARG
+    assert mhc.mhc_post_res_fp8(16, 4, 64, X, F, H, Y + 8, stream=0, check=False) == mhc.MHC_ERR_UNSUPPORTED
+    assert mhc.mhc_coeffs_fp8_workspace_size(16, 4, 24) == 0
+    assert mhc.mhc_coeffs_fp8_workspace_size(16, 4, 64) > 0
+    names = ["X", "phi", "bp", "bq", "br", "logits", "r", "H", "ws"]
+    p = dict(zip(names, _addrs(len(names))))
+
+    def coeffs(C=64, ws_bytes=None, **over):
+        q = dict(p, **over)
+        wb = ws_bytes if ws_bytes is not None else max(mhc.mhc_coeffs_fp8_workspace_size(16, 4, C), 16)
+        return mhc.mhc_coeffs_fp8(16, 4, C, q["X"], q["phi"], 0.01, 0.01, 0.01, q["bp"], q["bq"],
+                                  q["br"], q["logits"], q["r"], q["H"], q["ws"], wb, stream=0,
+                                  check=False)
+
+    assert coeffs(C=24) == mhc.MHC_ERR_UNSUPPORTED
+    assert coeffs(X=None) == mhc.MHC_ERR_INVALID_ARG
+    assert coeffs(H=A + 1024) == mhc.MHC_ERR_INVALID_ARG               # inside X's 4096 bytes
+    assert coeffs(ws_bytes=mhc.mhc_coeffs_fp8_workspace_size(16, 4, 64) - 1) == mhc.MHC_ERR_WORKSPACE
+    fnames = ["X", "F", "H", "Y", "phi", "bp", "bq", "br", "logits", "r", "Hn", "ws"]
+    f = dict(zip(fnames, _addrs(len(fnames))))
+
+    def fused(C=64, ws_bytes=None, **over):
+        q = dict(f, **over)
+        wb = ws_bytes if ws_bytes is not None else max(mhc.mhc_post_res_coeffs_fp8_workspace_size(16, 4, C), 16)
+        return mhc.mhc_post_res_coeffs_fp8(16, 4, C, q["X"], q["F"], q["H"], q["Y"], q["phi"], 0.01,
+                                           0.01, 0.01, q["bp"], q["bq"], q["br"], q["logits"],
+                                           q["r"], q["Hn"], q["ws"], wb, stream=0, check=False)
+
+    assert fused(C=48) == mhc.MHC_ERR_UNSUPPORTED                      # C % 32 for the fused call
+    assert mhc.mhc_post_res_coeffs_fp8_workspace_size(16, 4, 48) == 0
+    assert fused(Y=A) == mhc.MHC_ERR_INVALID_ARG
+    need = mhc.mhc_post_res_coeffs_fp8_workspace_size(16, 4, 64)
+    assert need > 0 and fused(ws_bytes=need - 1) == mhc.MHC_ERR_WORKSPACE

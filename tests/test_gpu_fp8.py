@@ -1,0 +1,244 @@
+"""GPU parity of the FP8 (E4M3) residual-stream variant against the fp64 oracle.
+
+The oracle decodes the same E4M3 bytes exactly (oracle.fp8.e4m3_decode) and
+computes in fp64.  Tolerances:
+  logits, r, H           as for the bf16 calls (the E4M3 inputs widen exactly):
+                         logits row-normwise 2e-3, r relative 2e-3, H absolute 1e-3
+  F_pre, X_next (E4M3)   tight: with the GPU's own H fed to the oracle's apply,
+                         every code equals the E4M3 rounding (nearest even,
+                         saturating) of the exact fp64 value, except within fp32
+                         rounding of a midpoint, where either neighbour is
+                         accepted (oracle.fp8.e4m3_neighbors_ok);
+                         loose: against the oracle's own coefficients,
+                         |decoded - exact| <= 0.07 |exact| + 2^-9 (half a code
+                         plus the H tolerance).
+Full-size workloads are checked on sampled rows (rows are independent).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import manifold_constrained_hyper_amd as mhc
+import oracle
+import synth
+from oracle import fp8 as F8
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a HIP device")
+    mhc.load()
+    yield
+
+
+# mhc_coeffs_fp8 has two implementations: the one-launch small-B kernel and,
+# above 256 rows, the persistent product kernel + combine.  Both must meet
+# the bar at every size they support.
+@pytest.fixture(params=["default", "small", "persistent"])
+def path(request, monkeypatch):
+    if request.param == "small":
+        monkeypatch.setenv("MHC_SMALL_MAX_B", str(1 << 30))
+    elif request.param == "persistent":
+        monkeypatch.setenv("MHC_SMALL_MAX_B", "0")
+    else:
+        monkeypatch.delenv("MHC_SMALL_MAX_B", raising=False)
+    return request.param
+
+
+def _alloc(B, n, C):
+    N = n * n + 2 * n
+    ws = max(mhc.mhc_coeffs_fp8_workspace_size(B, n, C),
+             mhc.mhc_post_res_coeffs_fp8_workspace_size(B, n, C), 16)
+    return {"logits": torch.empty(B, N, device="cuda"), "r": torch.empty(B, device="cuda"),
+            "H": torch.empty(B, N, device="cuda"),
+            "F_pre": torch.empty(B, C, dtype=torch.uint8, device="cuda"),
+            "X_next": torch.empty(B, n * C, dtype=torch.uint8, device="cuda"),
+            "workspace": torch.empty(ws, dtype=torch.uint8, device="cuda")}
+
+
+def run_three_calls(inp):
+    B, n, C = inp["B"], inp["n"], inp["C"]
+    o = _alloc(B, n, C)
+    mhc.mhc_coeffs_fp8(B, n, C, inp["X"], inp["phi"], inp["alpha_pre"], inp["alpha_post"],
+                       inp["alpha_res"], inp["b_pre"], inp["b_post"], inp["b_res"],
+                       o["logits"], o["r"], o["H"], o["workspace"])
+    mhc.mhc_pre_fp8(B, n, C, inp["X"], o["H"], o["F_pre"])
+    mhc.mhc_post_res_fp8(B, n, C, inp["X"], inp["F_out"], o["H"], o["X_next"])
+    torch.cuda.synchronize()
+    return o
+
+
+def _rows_f64(t, rows):
+    idx = torch.as_tensor(rows, device=t.device, dtype=torch.long)
+    return F8.e4m3_decode(synth.e4m3_codes(t.index_select(0, idx)))
+
+
+def check(inp, o, rows, label):
+    n, C = inp["n"], inp["C"]
+    x = _rows_f64(inp["X"], rows)
+    f = _rows_f64(inp["F_out"], rows)
+    phi = oracle.bf16_bits_to_f64(synth.bf16_bits(inp["phi"]))
+    bp, bq, br = (inp[k].double().cpu().numpy() for k in ("b_pre", "b_post", "b_res"))
+    co = oracle.coefficients(x, phi, inp["alpha_pre"], inp["alpha_post"], inp["alpha_res"],
+                             bp, bq, br, n, C)
+    idx = torch.as_tensor(rows, device="cuda", dtype=torch.long)
+    g = {k: o[k].index_select(0, idx).double().cpu().numpy() for k in ("logits", "r", "H")}
+    row_err = np.abs(g["logits"] - co["logits"]).max(1)
+    assert np.all(row_err <= 2e-3 * np.abs(co["logits"]).max(1)), f"{label}: logits"
+    assert np.all(np.abs(g["r"] - co["r"]) <= 2e-3 * co["r"]), f"{label}: r"
+    assert np.abs(g["H"] - co["H"]).max() <= 1e-3, f"{label}: H"
+    # apply steps with the GPU's own coefficients: exact E4M3 rounding rule
+    pre_g, post_g, res_g = oracle.split_h(g["H"], n)
+    fpre_exact = oracle.pre_mix(x, pre_g, n, C)
+    xnext_exact = oracle.post_res(x, f, post_g, res_g, n, C)
+    fpre_codes = synth.e4m3_codes(o["F_pre"].index_select(0, idx))
+    xnext_codes = synth.e4m3_codes(o["X_next"].index_select(0, idx))
+    bad = ~F8.e4m3_neighbors_ok(fpre_codes, fpre_exact)
+    assert not bad.any(), f"{label}: F_pre codes off at {np.argwhere(bad)[:5].tolist()}"
+    bad = ~F8.e4m3_neighbors_ok(xnext_codes, xnext_exact)
+    assert not bad.any(), f"{label}: X_next codes off at {np.argwhere(bad)[:5].tolist()}"
+    # against the oracle's own coefficients
+    pre_o, post_o, res_o = oracle.split_h(co["H"], n)
+    for name, codes, exact in (("F_pre", fpre_codes, oracle.pre_mix(x, pre_o, n, C)),
+                               ("X_next", xnext_codes, oracle.post_res(x, f, post_o, res_o, n, C))):
+        err = np.abs(F8.e4m3_decode(codes) - exact)
+        assert np.all(err <= 0.07 * np.abs(exact) + 2.0 ** -9), f"{label}: {name} vs oracle"
+
+
+def _sample(B):
+    if B <= 64:
+        return list(range(B))
+    return sorted(set([0, 1, B // 2, B - 1] + np.random.default_rng(B).choice(B, 40, replace=False).tolist()))
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "large", "wide"])
+def test_fp8_named(name):
+    _say(f"fp8 three calls {name}")
+    inp = synth.make_config_fp8(name, device="cuda")
+    o = run_three_calls(inp)
+    check(inp, o, _sample(inp["B"]), name)
+
+
+FP8_RAGGED = [(77, 4, 272), (1, 4, 16), (130, 8, 96), (33, 1, 48), (65, 2, 2064), (300, 4, 1040),
+              (3, 8, 16), (257, 4, 528)]
+
+
+@pytest.mark.parametrize("B,n,C", FP8_RAGGED, ids=[f"B{b}n{n}C{c}" for b, n, c in FP8_RAGGED])
+def test_fp8_ragged(B, n, C, path):
+    _say(f"fp8 ragged B={B} n={n} C={C} path={path}")
+    inp = synth.make_inputs_fp8(n, C, B, "student_t4" if B % 2 else "normal", seed=B * 17 + C,
+                                device="cuda")
+    o = run_three_calls(inp)
+    check(inp, o, list(range(B)), f"B{B}n{n}C{C}")
+
+
+def test_fp8_saturates():
+    """Outputs past the E4M3 range saturate to +-448 (the variant's reading)."""
+    _say("fp8 saturation")
+    B, n, C = 32, 4, 64
+    inp = synth.make_inputs_fp8(n, C, B, "normal", seed=9, device="cuda")
+    big = synth.to_e4m3(torch.full((B, n * C), 400.0, device="cuda"))
+    fbig = synth.to_e4m3(torch.full((B, C), 448.0, device="cuda"))
+    N = n * n + 2 * n
+    H = torch.zeros(B, N, device="cuda")
+    H[:, n:2 * n] = 2.0                                          # H_post = 2
+    H[:, 2 * n:] = torch.eye(n, device="cuda").reshape(-1)      # H_res = I
+    H[:, :n] = 1.0                                               # H_pre = 1: F_pre = n * 400
+    o = _alloc(B, n, C)
+    mhc.mhc_post_res_fp8(B, n, C, big, fbig, H, o["X_next"])     # 400 + 2 * 448 = 1296 -> 448
+    mhc.mhc_pre_fp8(B, n, C, big, H, o["F_pre"])
+    torch.cuda.synchronize()
+    assert (synth.e4m3_codes(o["X_next"]) == 0x7E).all()
+    assert (synth.e4m3_codes(o["F_pre"]) == 0x7E).all()
+    neg = synth.to_e4m3(torch.full((B, n * C), -400.0, device="cuda"))
+    mhc.mhc_post_res_fp8(B, n, C, neg, synth.to_e4m3(-torch.full((B, C), 448.0, device="cuda")), H,
+                         o["X_next"])
+    torch.cuda.synchronize()
+    assert (synth.e4m3_codes(o["X_next"]) == 0xFE).all()
+
+
+# ----------------------------------------------------------------------------
+# fused: mhc_post_res_coeffs_fp8
+# ----------------------------------------------------------------------------
+
+def _fused(inp, nxt):
+    B, n, C = inp["B"], inp["n"], inp["C"]
+    o = run_three_calls(inp)
+    ref = _alloc(B, n, C)
+    mhc.mhc_coeffs_fp8(B, n, C, o["X_next"], nxt["phi"], nxt["alpha_pre"], nxt["alpha_post"],
+                       nxt["alpha_res"], nxt["b_pre"], nxt["b_post"], nxt["b_res"],
+                       ref["logits"], ref["r"], ref["H"], ref["workspace"])
+    f = _alloc(B, n, C)
+    mhc.mhc_post_res_coeffs_fp8(B, n, C, inp["X"], inp["F_out"], o["H"], f["X_next"], nxt["phi"],
+                                nxt["alpha_pre"], nxt["alpha_post"], nxt["alpha_res"],
+                                nxt["b_pre"], nxt["b_post"], nxt["b_res"], f["logits"], f["r"],
+                                f["H"], f["workspace"])
+    torch.cuda.synchronize()
+    return o, ref, f
+
+
+def _check_fused(inp, nxt, o, ref, f, rows, label):
+    n, C = inp["n"], inp["C"]
+    assert torch.equal(f["X_next"], o["X_next"]), f"{label}: fused X_next differs from mhc_post_res_fp8"
+    xn = _rows_f64(f["X_next"], rows)
+    co = oracle.coefficients(xn, oracle.bf16_bits_to_f64(synth.bf16_bits(nxt["phi"])),
+                             nxt["alpha_pre"], nxt["alpha_post"], nxt["alpha_res"],
+                             nxt["b_pre"].double().cpu().numpy(), nxt["b_post"].double().cpu().numpy(),
+                             nxt["b_res"].double().cpu().numpy(), n, C)
+    idx = torch.as_tensor(rows, device="cuda", dtype=torch.long)
+    g = {k: f[k].index_select(0, idx).double().cpu().numpy() for k in ("logits", "r", "H")}
+    row_err = np.abs(g["logits"] - co["logits"]).max(1)
+    assert np.all(row_err <= 2e-3 * np.abs(co["logits"]).max(1)), f"{label}: logits"
+    assert np.all(np.abs(g["r"] - co["r"]) <= 2e-3 * co["r"]), f"{label}: r"
+    assert np.abs(g["H"] - co["H"]).max() <= 1e-3, f"{label}: H"
+    rel = ((f["logits"] - ref["logits"]).abs().max() / ref["logits"].abs().max()).item()
+    assert rel < 1e-4, f"{label}: logits vs mhc_coeffs_fp8 {rel}"
+    assert (f["H"] - ref["H"]).abs().max().item() < 1e-4, f"{label}: H vs mhc_coeffs_fp8"
+
+
+def _layers(n, C, B, dist, seed):
+    cur = synth.make_inputs_fp8(n, C, B, dist, seed=seed, device="cuda")
+    nxt = synth.make_inputs(n, C, 1, "normal", seed=seed + 7919, device="cuda")
+    return cur, nxt
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "large", "wide"])
+def test_fp8_fused_named(name):
+    _say(f"fp8 fused {name}")
+    cfg = synth.CONFIGS[name]
+    cur, nxt = _layers(cfg["n"], cfg["C"], cfg["B"], cfg["x_dist"], cfg["seed"])
+    o, ref, f = _fused(cur, nxt)
+    _check_fused(cur, nxt, o, ref, f, _sample(cfg["B"]), name)
+
+
+FP8_FUSED_RAGGED = [(77, 4, 544), (1, 4, 32), (130, 8, 96), (33, 1, 64), (300, 4, 1536),
+                    (17, 8, 32), (65, 2, 2080)]
+
+
+@pytest.mark.parametrize("B,n,C", FP8_FUSED_RAGGED, ids=[f"B{b}n{n}C{c}" for b, n, c in FP8_FUSED_RAGGED])
+def test_fp8_fused_ragged(B, n, C, path):
+    _say(f"fp8 fused ragged B={B} n={n} C={C} path={path}")
+    cur, nxt = _layers(n, C, B, "student_t4" if B % 2 else "normal", B * 29 + C)
+    o, ref, f = _fused(cur, nxt)
+    _check_fused(cur, nxt, o, ref, f, list(range(B)), f"B{B}n{n}C{C}")
+
+
+def test_fp8_fused_deterministic():
+    _say("fp8 fused determinism")
+    cfg = synth.CONFIGS["prefill"]
+    cur, nxt = _layers(cfg["n"], cfg["C"], cfg["B"], cfg["x_dist"], cfg["seed"])
+    _, _, a = _fused(cur, nxt)
+    _, _, b = _fused(cur, nxt)
+    for k in ("X_next", "logits", "r", "H"):
+        assert torch.equal(a[k].view(torch.int8), b[k].view(torch.int8)), k

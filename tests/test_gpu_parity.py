@@ -46,8 +46,10 @@ def _gpu():
 #   reg    the same with MFMA operands loaded straight from global memory
 #          (MHC_GEMM_ALGO=0);
 #   small  the one-launch small-B kernel (the default up to 256 rows; forced
-#          here for every size it supports with MHC_SMALL_MAX_B).
-GEMM_ALGOS = ["lds", "reg", "small"]
+#          here for every size it supports with MHC_SMALL_MAX_B);
+#   persist  the product in the persistent kernel of mhc_post_res_coeffs
+#          (product only, MHC_GEMM_ALGO=2), then the combine kernel.
+GEMM_ALGOS = ["lds", "reg", "small", "persist"]
 
 
 @pytest.fixture(params=GEMM_ALGOS)
@@ -59,6 +61,8 @@ def gemm_algo(request, monkeypatch):
         monkeypatch.setenv("MHC_SMALL_MAX_B", "0")
         if request.param == "reg":
             monkeypatch.setenv("MHC_GEMM_ALGO", "0")
+        elif request.param == "persist":
+            monkeypatch.setenv("MHC_GEMM_ALGO", "2")
     return request.param
 
 
