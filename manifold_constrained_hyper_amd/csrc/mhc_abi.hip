@@ -58,8 +58,9 @@ int check_shape_elt(int64_t B, int32_t n, int64_t C, Elt e) {
 }
 
 // Which kernels mhc_coeffs(_fp8) runs: the one-launch small-B kernel, the
-// split-K product + combine (bf16), or the persistent product kernel of
-// mhc_post_res_fused.hip + combine (E4M3, or bf16 with MHC_GEMM_ALGO=2).  The
+// split-K product (X staged through LDS, bf16 or E4M3) + combine, or (with
+// MHC_GEMM_ALGO=2) the persistent product kernel of mhc_post_res_fused.hip +
+// combine.  The
 // persistent kernel walks each stream in 32-channel k-steps, so it needs
 // C % 32 == 0; other hidden sizes take the small-B kernel at any B (it is
 // correct for every shape, only slower at large B).
@@ -67,18 +68,22 @@ enum class CoeffsPath { kSmall, kSplitK, kPersistent };
 
 CoeffsPath coeffs_path(int64_t B, int32_t n, int64_t C, Elt e) {
   if (mhc::use_coeffs_small(B, n, C)) return CoeffsPath::kSmall;
-  bool persistent = e.fp8;
+  bool persistent = false;
   if (const char *v = std::getenv("MHC_GEMM_ALGO"))
     if (std::strtol(v, nullptr, 10) == 2) persistent = true;
   if (!persistent) return CoeffsPath::kSplitK;
   return C % 32 == 0 ? CoeffsPath::kPersistent : CoeffsPath::kSmall;
 }
 
+mhc::GemmPlan split_plan(int64_t B, int32_t n, int64_t C, Elt e) {
+  return mhc::plan_gemm(B, n, C, e.fp8);
+}
+
 size_t coeffs_ws_bytes(int64_t B, int32_t n, int64_t C, Elt e) {
   switch (coeffs_path(B, n, C, e)) {
     case CoeffsPath::kSmall: return mhc::plan_coeffs_small(B, n, C).total_bytes;
     case CoeffsPath::kPersistent: return mhc::plan_post_res_next(B, n, C).total_bytes;
-    default: return mhc::gemm_workspace_bytes(mhc::plan_gemm(B, n, C), B, n);
+    default: return mhc::gemm_workspace_bytes(split_plan(B, n, C, e), B, n);
   }
 }
 
@@ -127,7 +132,7 @@ int coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t, const v
                                                alpha_pre, alpha_post, alpha_res, b_pre, b_post,
                                                b_res, logits, r, H, s));
   }
-  const mhc::GemmPlan plan = mhc::plan_gemm(B, n, C);
+  const mhc::GemmPlan plan = split_plan(B, n, C, e);
   float *ws = static_cast<float *>(workspace);
   st = from_hip(mhc::launch_gemm_rms(plan, n, B, C, X_t, phi, ws, s));
   if (st != MHC_OK) return st;
@@ -169,10 +174,26 @@ int post_res_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t, const
                         : mhc::launch_post_res(n, B, C, X_t, F_out, H, X_next, s));
 }
 
+// How mhc_post_res_coeffs(_fp8) runs: small B -> the apply, then the
+// one-launch small-B coefficient kernel on X_next; n = 8 -> the apply, then
+// the split-K product on X_next (at n = 8 the fused kernel re-reads phi from
+// L2 for every 16 rows, 80 columns wide, and loses to the two passes; set
+// MHC_FUSED_N8=1 to run it anyway); otherwise the fused kernel.
+enum class FusedRoute { kSmall, kTwoPass, kFused };
+
+FusedRoute fused_route(int64_t B, int32_t n, int64_t C) {
+  if (mhc::use_coeffs_small(B, n, C)) return FusedRoute::kSmall;
+  if (n == 8 && !std::getenv("MHC_FUSED_N8")) return FusedRoute::kTwoPass;
+  return FusedRoute::kFused;
+}
+
 size_t post_res_coeffs_ws_bytes(int64_t B, int32_t n, int64_t C, Elt e) {
   if (check_shape_elt(B, n, C, e) != MHC_OK || B == 0 || C % 32 != 0) return 0;
-  if (mhc::use_coeffs_small(B, n, C)) return mhc::plan_coeffs_small(B, n, C).total_bytes;
-  return mhc::plan_post_res_next(B, n, C).total_bytes;
+  switch (fused_route(B, n, C)) {
+    case FusedRoute::kSmall: return mhc::plan_coeffs_small(B, n, C).total_bytes;
+    case FusedRoute::kTwoPass: return mhc::gemm_workspace_bytes(split_plan(B, n, C, e), B, n);
+    default: return mhc::plan_post_res_next(B, n, C).total_bytes;
+  }
 }
 
 int post_res_coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t,
@@ -192,9 +213,7 @@ int post_res_coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t
       !aligned(workspace, 16) || !aligned(H, 4) || !aligned(b_pre, 4) || !aligned(b_post, 4) ||
       !aligned(b_res, 4) || !aligned(logits_next, 4) || !aligned(r_next, 4) || !aligned(H_next, 4))
     return MHC_ERR_UNSUPPORTED;
-  // Small B: the apply, then the one-launch coefficient kernel on X_next (at
-  // decode sizes re-reading X_next costs less than the fused kernel's setup).
-  const bool small = mhc::use_coeffs_small(B, n, C);
+  const FusedRoute route = fused_route(B, n, C);
   const mhc::FusedPlan plan = mhc::plan_post_res_next(B, n, C);
   const size_t ws_need = post_res_coeffs_ws_bytes(B, n, C, e);
   const int64_t N = ncoef(n), K = (int64_t)n * C;
@@ -215,14 +234,22 @@ int post_res_coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t
   if (workspace_bytes < ws_need) return MHC_ERR_WORKSPACE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (small) {
+  if (route != FusedRoute::kFused) {
     st = from_hip(e.fp8 ? mhc::launch_post_res_fp8(n, B, C, X_t, F_out, H, X_next, s)
                         : mhc::launch_post_res(n, B, C, X_t, F_out, H, X_next, s));
     if (st != MHC_OK) return st;
-    return from_hip(mhc::launch_coeffs_small(mhc::plan_coeffs_small(B, n, C), n, e.fp8, B, C,
-                                             X_next, phi_next, alpha_pre, alpha_post, alpha_res,
-                                             b_pre, b_post, b_res, logits_next, r_next, H_next,
-                                             workspace, s));
+    if (route == FusedRoute::kSmall)
+      return from_hip(mhc::launch_coeffs_small(mhc::plan_coeffs_small(B, n, C), n, e.fp8, B, C,
+                                               X_next, phi_next, alpha_pre, alpha_post, alpha_res,
+                                               b_pre, b_post, b_res, logits_next, r_next, H_next,
+                                               workspace, s));
+    const mhc::GemmPlan gp = split_plan(B, n, C, e);
+    float *ws = static_cast<float *>(workspace);
+    st = from_hip(mhc::launch_gemm_rms(gp, n, B, C, X_next, phi_next, ws, s));
+    if (st != MHC_OK) return st;
+    return from_hip(mhc::launch_coeff_sinkhorn(n, B, C, gp.split, ws, alpha_pre, alpha_post,
+                                               alpha_res, b_pre, b_post, b_res, logits_next,
+                                               r_next, H_next, s));
   }
   st = from_hip(mhc::launch_post_res_next(plan, n, e.fp8 ? mhc::kFusedApplyFp8 : mhc::kFusedApplyBf16,
                                           B, C, X_t, F_out, H, X_next, phi_next, workspace, s));

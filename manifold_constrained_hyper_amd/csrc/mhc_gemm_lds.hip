@@ -37,20 +37,22 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int NS, int MB, int KC, int STAGES>
+template <int NS, int MB, int KC, int STAGES, int XB>
 struct LdsTile {
   static constexpr int N = NS * NS + 2 * NS;
   static constexpr int NP = N + 1;
   static constexpr int NB = (N + 15) / 16;
   static constexpr int RT = 64 * MB;                 // rows per workgroup
   static constexpr int T = KC / 32;                  // MFMA k-steps per chunk
-  static constexpr int PIECES = KC / 8;              // 16-byte pieces per row per chunk
+  static constexpr int EPP = 16 / XB;                // X elements per 16-byte piece
+  static constexpr int ROW_BYTES = KC * XB;          // one row of a chunk in LDS
+  static constexpr int PIECES = KC / EPP;            // 16-byte pieces per row per chunk
   static constexpr int RPI = 64 / PIECES;            // rows per load instruction
   static constexpr int XI = RT * PIECES / 64;        // X load instructions per chunk
   static constexpr int PI = T * NB;                  // phi load instructions per chunk
   static constexpr int XI_W = XI / 4, PI_W = PI / 4; // ... per wave
   static constexpr int VM_PER_CHUNK = XI_W + PI_W;
-  static constexpr int X_BYTES = RT * KC * 2;
+  static constexpr int X_BYTES = RT * ROW_BYTES;
   static constexpr int P_BYTES = PI * 1024;
   static constexpr int STAGE_BYTES = X_BYTES + P_BYTES;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
@@ -68,13 +70,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int NS, int MB, int KC, int STAGES>
+template <int NS, int MB, int KC, int STAGES, int XB>
 __device__ __forceinline__ void issue_chunk(char *lds, int slot, int wave, int lane,
-                                           const uint16_t *__restrict__ X,
+                                           const uint8_t *__restrict__ X,
                                            const uint16_t *__restrict__ phip,
                                            const uint16_t *__restrict__ zero, int row0, int B,
                                            int K, int k0) {
-  using L = LdsTile<NS, MB, KC, STAGES>;
+  using L = LdsTile<NS, MB, KC, STAGES, XB>;
   char *xs = lds + slot * L::STAGE_BYTES;
   char *ps = xs + L::X_BYTES;
   const int slot_in_row = lane % L::PIECES;
@@ -83,9 +85,10 @@ __device__ __forceinline__ void issue_chunk(char *lds, int slot, int wave, int l
     const int inst = wave * L::XI_W + j;
     const int rr = inst * L::RPI + lane / L::PIECES;          // row within the tile
     const int piece = slot_in_row ^ (rr & 15);
-    const int k = k0 + piece * 8;
+    const int k = k0 + piece * L::EPP;
     const int row = min(row0 + rr, B - 1);
-    const uint16_t *src = (k < K) ? X + (size_t)row * K + k : zero;
+    const void *src = (k < K) ? static_cast<const void *>(X + ((size_t)row * K + k) * XB)
+                              : static_cast<const void *>(zero);
     __builtin_amdgcn_global_load_lds(src, (lds_void *)(xs + inst * 1024), 16, 0, 0);
   }
   const int kstep0 = k0 / 32;
@@ -102,9 +105,9 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
 }
 
 // Wait until at most `later` chunks' loads of this wave are outstanding.
-template <int NS, int MB, int KC, int STAGES>
+template <int NS, int MB, int KC, int STAGES, int XB>
 __device__ __forceinline__ void wait_chunks(int later) {
-  using L = LdsTile<NS, MB, KC, STAGES>;
+  using L = LdsTile<NS, MB, KC, STAGES, XB>;
   if (STAGES >= 4 && later >= 2) {
     wait_vmcnt<(STAGES >= 4 ? 2 : 0) * L::VM_PER_CHUNK>();
   } else if (later >= 1) {
@@ -114,13 +117,13 @@ __device__ __forceinline__ void wait_chunks(int later) {
   }
 }
 
-template <int NS, int MB, int KC, int STAGES>
-__global__ __launch_bounds__(256) void gemm_rms_lds_kernel(const uint16_t *__restrict__ X,
+template <int NS, int MB, int KC, int STAGES, int XB>
+__global__ __launch_bounds__(256) void gemm_rms_lds_kernel(const uint8_t *__restrict__ X,
                                                            const uint16_t *__restrict__ phip,
                                                            const uint16_t *__restrict__ zero,
                                                            float *__restrict__ ws, int B, int K,
                                                            int kslice) {
-  using L = LdsTile<NS, MB, KC, STAGES>;
+  using L = LdsTile<NS, MB, KC, STAGES, XB>;
   __shared__ __attribute__((aligned(1024))) char lds[L::LDS_BYTES];
 
   const int tid = threadIdx.x;
@@ -144,7 +147,7 @@ __global__ __launch_bounds__(256) void gemm_rms_lds_kernel(const uint16_t *__res
 #pragma unroll
   for (int c = 0; c < STAGES - 1; ++c)
     if (c < nchunks)
-      issue_chunk<NS, MB, KC, STAGES>(lds, c, wave, lane, X, phip, zero, row0, B, K,
+      issue_chunk<NS, MB, KC, STAGES, XB>(lds, c, wave, lane, X, phip, zero, row0, B, K,
                                       k_begin + c * KC);
 
   for (int c = 0; c < nchunks; ++c) {
@@ -153,14 +156,14 @@ __global__ __launch_bounds__(256) void gemm_rms_lds_kernel(const uint16_t *__res
     // chunk c is complete and the slot of chunk c-1 may be refilled.  (A bare
     // s_barrier: a fenced __syncthreads would also wait for the loads still
     // in flight for the later chunks.)
-    wait_chunks<NS, MB, KC, STAGES>(min(STAGES - 2, nchunks - 1 - c));
+    wait_chunks<NS, MB, KC, STAGES, XB>(min(STAGES - 2, nchunks - 1 - c));
     wait_lgkmcnt0();
     asm volatile("" ::: "memory");  // no memory access moves across the barrier
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     const int cn = c + STAGES - 1;
     if (cn < nchunks)
-      issue_chunk<NS, MB, KC, STAGES>(lds, cn % STAGES, wave, lane, X, phip, zero, row0, B, K,
+      issue_chunk<NS, MB, KC, STAGES, XB>(lds, cn % STAGES, wave, lane, X, phip, zero, row0, B, K,
                                       k_begin + cn * KC);
     const char *xs = lds + (c % STAGES) * L::STAGE_BYTES;
     const char *ps = xs + L::X_BYTES;
@@ -173,8 +176,17 @@ __global__ __launch_bounds__(256) void gemm_rms_lds_kernel(const uint16_t *__res
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const int rr = wave * 16 * MB + mb * 16 + m;
-        const int slot = (4 * t + g) ^ m;  // rr & 15 == m
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(xs + rr * (KC * 2) + slot * 16);
+        bf16x8 a;
+        if constexpr (XB == 2) {
+          const int slot = (4 * t + g) ^ m;  // rr & 15 == m
+          a = *reinterpret_cast<const bf16x8 *>(xs + rr * L::ROW_BYTES + slot * 16);
+        } else {
+          // E4M3: k = 32t + 8g .. +7 is the (g & 1) half of piece 2t + g/2;
+          // it widens exactly to bf16.
+          const int slot = (2 * t + (g >> 1)) ^ m;
+          const u32x2 v = *reinterpret_cast<const u32x2 *>(xs + rr * L::ROW_BYTES + slot * 16 + (g & 1) * 8);
+          a = __builtin_bit_cast(bf16x8, fp8x8_to_bf16(v));
+        }
 #pragma unroll
         for (int nb = 0; nb < L::NB; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[nb], acc[mb][nb], 0, 0, 0);
@@ -256,10 +268,10 @@ __global__ __launch_bounds__(256) void pack_phi_kernel(const uint16_t *__restric
 
 }  // namespace
 
-template <int NS, int MB, int KC, int STAGES>
+template <int NS, int MB, int KC, int STAGES, int XB>
 hipError_t launch_gemm_lds_typed(const GemmPlan &p, int64_t B, int64_t C, const void *X,
                                  const void *phi, void *ws_base, hipStream_t st) {
-  using L = LdsTile<NS, MB, KC, STAGES>;
+  using L = LdsTile<NS, MB, KC, STAGES, XB>;
   const int K = (int)(NS * C);
   char *base = static_cast<char *>(ws_base);
   uint16_t *phip = reinterpret_cast<uint16_t *>(base + p.phip_offset);
@@ -268,8 +280,8 @@ hipError_t launch_gemm_lds_typed(const GemmPlan &p, int64_t B, int64_t C, const 
   hipError_t e = launch_pack_phi(NS, K, ksteps, phi, phip, zero, st);
   if (e != hipSuccess) return e;
   const dim3 grid((uint32_t)p.row_tiles, (uint32_t)p.split);
-  gemm_rms_lds_kernel<NS, MB, KC, STAGES><<<grid, 256, 0, st>>>(
-      static_cast<const uint16_t *>(X), phip, zero, reinterpret_cast<float *>(base), (int)B, K,
+  gemm_rms_lds_kernel<NS, MB, KC, STAGES, XB><<<grid, 256, 0, st>>>(
+      static_cast<const uint8_t *>(X), phip, zero, reinterpret_cast<float *>(base), (int)B, K,
       (int)p.kslice);
   return hipGetLastError();
 }
@@ -290,9 +302,13 @@ hipError_t launch_pack_phi(int n, int64_t K, int64_t ksteps, const void *phi, vo
 }
 
 // Instantiations used by the library (see plan_gemm in mhc_gemm_rms.hip).
-template hipError_t launch_gemm_lds_typed<1, 1, 256, 3>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
-template hipError_t launch_gemm_lds_typed<2, 1, 256, 3>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
-template hipError_t launch_gemm_lds_typed<4, 1, 256, 3>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
-template hipError_t launch_gemm_lds_typed<8, 1, 128, 4>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<1, 1, 256, 3, 2>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<2, 1, 256, 3, 2>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<4, 1, 256, 3, 2>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<8, 1, 128, 4, 2>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<1, 1, 256, 4, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<2, 1, 256, 4, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<4, 1, 256, 4, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<8, 1, 256, 2, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
 
 }  // namespace mhc

@@ -246,9 +246,13 @@ constexpr int64_t kGemmTargetWGs = 512;
 template <int NS>
 hipError_t launch_n(const GemmPlan &p, int64_t B, int64_t C, const void *X, const void *phi,
                     float *ws, hipStream_t st) {
+  if (p.algo == 1 && p.xb == 1) {
+    if constexpr (NS == 8) return launch_gemm_lds_typed<NS, 1, 256, 2, 1>(p, B, C, X, phi, ws, st);
+    else return launch_gemm_lds_typed<NS, 1, 256, 4, 1>(p, B, C, X, phi, ws, st);
+  }
   if (p.algo == 1) {
-    if constexpr (NS == 8) return launch_gemm_lds_typed<NS, 1, 128, 4>(p, B, C, X, phi, ws, st);
-    else return launch_gemm_lds_typed<NS, 1, 256, 3>(p, B, C, X, phi, ws, st);
+    if constexpr (NS == 8) return launch_gemm_lds_typed<NS, 1, 128, 4, 2>(p, B, C, X, phi, ws, st);
+    else return launch_gemm_lds_typed<NS, 1, 256, 3, 2>(p, B, C, X, phi, ws, st);
   }
   if (p.mb == 2) return launch_typed<NS, 2, kGemmKC, false, true>(p, B, C, X, phi, ws, st);
   return launch_typed<NS, 1, kGemmKC, false, true>(p, B, C, X, phi, ws, st);
@@ -263,6 +267,7 @@ GemmPlan plan_gemm_custom(int64_t B, int n, int64_t C, int algo, int mb, int kc,
   const int64_t N = (int64_t)n * n + 2 * n;
   const int64_t NB = (N + 15) / 16;
   p.algo = algo;
+  p.xb = 2;
   p.kc = kc;
   p.mb = mb;
   p.stages = stages;
@@ -291,11 +296,22 @@ GemmPlan plan_gemm_custom(int64_t B, int n, int64_t C, int algo, int mb, int kc,
   return p;
 }
 
-GemmPlan plan_gemm(int64_t B, int n, int64_t C) {
+GemmPlan plan_gemm(int64_t B, int n, int64_t C, bool fp8_x) {
   // X staged through LDS (algo 1), one 4-wave workgroup per CU at a time
   // (the LDS ring is ~144 KiB); enough workgroups to fill the 256 CUs, and no
   // more K-slices than that needs, since every slice adds (N+1)*4 bytes of
-  // partials per row.
+  // partials per row.  E4M3 X: 256-k chunks (16 pieces of 16 bytes per row),
+  // four stages (two at n = 8, whose phi blocks are larger).
+  if (fp8_x) {
+    int64_t target = 256;
+    if (const char *e = getenv("MHC_GEMM_WGS")) {
+      const long v = strtol(e, nullptr, 10);
+      if (v > 0) target = v;
+    }
+    GemmPlan p = plan_gemm_custom(B, n, C, 1, 1, 256, n == 8 ? 2 : 4, target);
+    p.xb = 1;
+    return p;
+  }
   const int kc = (n == 8) ? 128 : 256;
   const int stages = (n == 8) ? 4 : 3;
   int64_t target = 256;

@@ -19,20 +19,21 @@ struct GemmPlan {
   int mb;             // 16-row MFMA blocks per wavefront (rows per workgroup = 64 * mb)
   int kc;             // K elements per chunk
   int stages;         // LDS ring depth (algo 1)
+  int xb;             // bytes per X element: 2 (bf16) or 1 (E4M3, algo 1 only)
   int split;          // S: number of K-slices (partials in the workspace)
   int64_t kslice;     // K elements per slice (multiple of kc)
   int64_t row_tiles;  // workgroups along B
   size_t partial_bytes, phip_offset, phip_bytes, zero_offset, total_bytes;
 };
 
-GemmPlan plan_gemm(int64_t B, int n, int64_t C);
+GemmPlan plan_gemm(int64_t B, int n, int64_t C, bool fp8_x = false);
 // Plan with explicit kernel, rows-per-wave blocks, chunk size, ring depth and
 // target workgroup count.
 GemmPlan plan_gemm_custom(int64_t B, int n, int64_t C, int algo, int mb, int kc, int stages,
                           int64_t target_wgs);
 size_t gemm_workspace_bytes(const GemmPlan &p, int64_t B, int n);
 
-template <int NS, int MB, int KC, int STAGES>
+template <int NS, int MB, int KC, int STAGES, int XB>
 hipError_t launch_gemm_lds_typed(const GemmPlan &p, int64_t B, int64_t C, const void *X,
                                  const void *phi, void *ws_base, hipStream_t st);
 

@@ -42,17 +42,23 @@ def _gpu():
     yield
 
 
-# mhc_coeffs_fp8 has two implementations: the one-launch small-B kernel and,
-# above 256 rows, the persistent product kernel + combine.  Both must meet
-# the bar at every size they support.
-@pytest.fixture(params=["default", "small", "persistent"])
+# mhc_coeffs_fp8 has three implementations: the one-launch small-B kernel
+# (default up to 256 rows), the split-K product with X staged through LDS
+# (default above), and the persistent product kernel (MHC_GEMM_ALGO=2).  The
+# fused call also has its fused kernel (forced at n = 8 with MHC_FUSED_N8).
+# Every one must meet the bar at every size it supports.
+@pytest.fixture(params=["default", "small", "split", "persistent"])
 def path(request, monkeypatch):
+    for k in ("MHC_SMALL_MAX_B", "MHC_GEMM_ALGO", "MHC_FUSED_N8"):
+        monkeypatch.delenv(k, raising=False)
     if request.param == "small":
         monkeypatch.setenv("MHC_SMALL_MAX_B", str(1 << 30))
+    elif request.param == "split":
+        monkeypatch.setenv("MHC_SMALL_MAX_B", "0")
     elif request.param == "persistent":
         monkeypatch.setenv("MHC_SMALL_MAX_B", "0")
-    else:
-        monkeypatch.delenv("MHC_SMALL_MAX_B", raising=False)
+        monkeypatch.setenv("MHC_GEMM_ALGO", "2")
+        monkeypatch.setenv("MHC_FUSED_N8", "1")
     return request.param
 
 

@@ -35,14 +35,16 @@ def _gpu():
 
 
 # Up to 256 rows mhc_post_res_coeffs runs the stand-alone apply and the
-# one-launch small-B coefficient kernel; "fused" forces the fused kernel at
-# every size.
+# one-launch small-B coefficient kernel, and at n = 8 the apply and the
+# split-K product; "fused" forces the fused kernel at every size and n.
 @pytest.fixture(params=["default", "fused"])
 def route(request, monkeypatch):
     if request.param == "fused":
         monkeypatch.setenv("MHC_SMALL_MAX_B", "0")
+        monkeypatch.setenv("MHC_FUSED_N8", "1")
     else:
         monkeypatch.delenv("MHC_SMALL_MAX_B", raising=False)
+        monkeypatch.delenv("MHC_FUSED_N8", raising=False)
     return request.param
 
 
@@ -106,8 +108,8 @@ def _check(cur, nxt, o, ref, f, rows, label):
 
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "large", "wide"])
 def test_fused_named(name, route):
-    if route == "fused" and synth.CONFIGS[name]["B"] > 256:
-        pytest.skip("above 256 rows the default route is the fused kernel")
+    if route == "fused" and synth.CONFIGS[name]["B"] > 256 and synth.CONFIGS[name]["n"] != 8:
+        pytest.skip("above 256 rows (n < 8) the default route is the fused kernel")
     _say(f"fused {name} route={route}")
     cfg = synth.CONFIGS[name]
     cur, nxt = _layers(cfg["n"], cfg["C"], cfg["B"], cfg["x_dist"], cfg["seed"])
