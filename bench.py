@@ -25,6 +25,11 @@ Algorithmic bytes (bf16 X_t, F_out, F_pre, X_next; fp32 coefficients):
 Split-K partials and the packed copy of phi are implementation traffic and
 are not counted.
 
+Also reported: the same pipeline on the E4M3 residual stream ("fp8", the
+*_fp8 entry points, one byte per stream element in the byte count) and, for
+the other workloads (tiny, decode, prefill, wide), both dtypes' per-layer and
+three-call times ("workloads"; decode also cold, after a 512 MB write).
+
 Other modes:
   --copy-probe   time a plain device-to-device copy of known size (the
                  reference against which rocprofv3 FETCH_SIZE / WRITE_SIZE are
@@ -63,17 +68,18 @@ def product_flops(B, n, C):
     return 2 * B * n * C * (N + 1)
 
 
-def path_bytes(B, n, C):
-    """Algorithmic bytes moved by each call for one layer (bf16 streams, fp32
-    coefficients and biases)."""
+def path_bytes(B, n, C, eb=2):
+    """Algorithmic bytes moved by each call for one layer: residual-stream
+    tensors (X_t, F_out, F_pre, X_next) of eb bytes per element (2 for bf16, 1
+    for the E4M3 calls), bf16 phi, fp32 coefficients and biases."""
     N = n * n + 2 * n
     K = n * C
-    x = B * K * 2
+    x = B * K * eb
     coeff_out = N * 4 + B * N * 4 + B * 4 + B * N * 4   # biases in, logits, H, r out
-    post_res = apply_stream_bytes(B, n, C, 2) + B * (n + n * n) * 4
+    post_res = apply_stream_bytes(B, n, C, eb) + B * (n + n * n) * 4
     return {
         "mhc_coeffs": x + K * N * 2 + coeff_out,
-        "mhc_pre": x + B * n * 4 + B * C * 2,
+        "mhc_pre": x + B * n * 4 + B * C * eb,
         "mhc_post_res": post_res,
         "mhc_post_res_coeffs": post_res + K * N * 2 + coeff_out,
     }
@@ -88,6 +94,109 @@ def path_flops(B, n, C):
 KERNELS_OF_CALL = {"mhc_post_res": "post_res_kernel", "mhc_pre": "pre_kernel",
                    "mhc_coeffs": "pack_phi_kernel + gemm_rms_lds_kernel + coeff_sinkhorn_kernel",
                    "mhc_post_res_coeffs": "pack_phi_kernel + post_res_next_kernel + coeff_sinkhorn_kernel"}
+
+
+class Pipeline:
+    """The per-layer pipeline (mhc_pre + mhc_post_res_coeffs, X chained through
+    the layers) and the three separate calls, for one input set, in bf16 or
+    E4M3 (fp8=True: the *_fp8 entry points)."""
+
+    def __init__(self, mhc, torch, inp, fp8=False):
+        self.torch, self.inp = torch, inp
+        B, n, C = inp["B"], inp["n"], inp["C"]
+        self.B, self.n, self.C = B, n, C
+        N = n * n + 2 * n
+        sfx = "_fp8" if fp8 else ""
+        self.coeffs = getattr(mhc, "mhc_coeffs" + sfx)
+        self.pre = getattr(mhc, "mhc_pre" + sfx)
+        self.post_res = getattr(mhc, "mhc_post_res" + sfx)
+        self.fused = getattr(mhc, "mhc_post_res_coeffs" + sfx)
+        ws_c = getattr(mhc, "mhc_coeffs" + sfx + "_workspace_size")(B, n, C)
+        ws_f = getattr(mhc, "mhc_post_res_coeffs" + sfx + "_workspace_size")(B, n, C)
+        dev, st = "cuda", torch.uint8 if fp8 else torch.bfloat16
+        self.X = [inp["X"], torch.empty_like(inp["X"])]
+        self.H = [torch.empty(B, N, device=dev) for _ in range(2)]
+        self.logits = torch.empty(B, N, device=dev)
+        self.r = torch.empty(B, device=dev)
+        self.F_pre = torch.empty(B, C, dtype=st, device=dev)
+        self.X_out = torch.empty_like(inp["X"])
+        self.ws_c = torch.empty(max(ws_c, 16), dtype=torch.uint8, device=dev)
+        self.ws_f = torch.empty(max(ws_f, 16), dtype=torch.uint8, device=dev)
+        self.ab = (inp["alpha_pre"], inp["alpha_post"], inp["alpha_res"], inp["b_pre"],
+                   inp["b_post"], inp["b_res"])
+        self.stream = torch.cuda.current_stream()
+        self.coeffs(B, n, C, self.X[0], inp["phi"], *self.ab, self.logits, self.r, self.H[0],
+                    self.ws_c, stream=self.stream)
+        self.cur = 0
+
+    def layer(self, marks=None):
+        B, n, C, a, s = self.B, self.n, self.C, self.cur, self.stream
+        if marks is not None:
+            marks[0].record(s)
+        self.pre(B, n, C, self.X[a], self.H[a], self.F_pre, stream=s)
+        if marks is not None:
+            marks[1].record(s)
+        self.fused(B, n, C, self.X[a], self.inp["F_out"], self.H[a], self.X[1 - a], self.inp["phi"],
+                   *self.ab, self.logits, self.r, self.H[1 - a], self.ws_f, stream=s)
+        if marks is not None:
+            marks[2].record(s)
+        self.cur = 1 - a
+
+    def three(self, marks=None):
+        B, n, C, s, inp = self.B, self.n, self.C, self.stream, self.inp
+        if marks is not None:
+            marks[0].record(s)
+        self.coeffs(B, n, C, inp["X"], inp["phi"], *self.ab, self.logits, self.r, self.H[0],
+                    self.ws_c, stream=s)
+        if marks is not None:
+            marks[1].record(s)
+        self.pre(B, n, C, inp["X"], self.H[0], self.F_pre, stream=s)
+        if marks is not None:
+            marks[2].record(s)
+        self.post_res(B, n, C, inp["X"], inp["F_out"], self.H[0], self.X_out, stream=s)
+        if marks is not None:
+            marks[3].record(s)
+
+    def time_loop(self, fn, steps, warmup):
+        """Mean ms per call of fn over `steps` back-to-back calls between two
+        events (no event between calls)."""
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(self.stream)
+        for _ in range(steps):
+            fn()
+        t1.record(self.stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    def per_call(self, fn, names, steps):
+        """Mean ms of each call, from events around every call."""
+        torch = self.torch
+        marks = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for k in range(steps):
+            fn(marks[k])
+        torch.cuda.synchronize()
+        return {c: sum(marks[k][i].elapsed_time(marks[k][i + 1]) for k in range(steps)) / steps
+                for i, c in enumerate(names)}
+
+
+def _summary(B, n, C, eb, ms_layer, ms_three, per_pipe=None, per_three=None):
+    b = path_bytes(B, n, C, eb)
+    pipe = b["mhc_pre"] + b["mhc_post_res_coeffs"]
+    three = b["mhc_coeffs"] + b["mhc_pre"] + b["mhc_post_res"]
+    out = {"us_per_layer": round(ms_layer * 1e3, 2), "tokens_per_s": round(B / (ms_layer * 1e-3), 1),
+           "hbm_gbps": round(pipe / (ms_layer * 1e-3) / 1e9, 1), "algorithmic_bytes_per_layer": pipe,
+           "three_call_us": round(ms_three * 1e3, 2),
+           "three_call_hbm_gbps": round(three / (ms_three * 1e-3) / 1e9, 1)}
+    if per_pipe:
+        out["per_call_us"] = {c: round(v * 1e3, 2) for c, v in per_pipe.items()}
+    if per_three:
+        out["three_call_per_call_us"] = {c: round(v * 1e3, 2) for c, v in per_three.items()}
+    return out
 
 
 # source files that make up each call's kernels (for the counter-freshness check)
@@ -324,6 +433,50 @@ def main():
     per_call3 = {c: sum(marks3[k][i].elapsed_time(marks3[k][i + 1]) for k in range(args.steps)) / args.steps
                  for i, c in enumerate(three_calls)}
 
+    # ---- the E4M3 residual-stream variant on the same workload (same shapes
+    # and draws, X and F_out rounded to E4M3)
+    del X, Hs, out
+    fp8_inp = synth.make_config_fp8(args.workload, device="cuda")
+    pf = Pipeline(mhc, torch, fp8_inp, fp8=True)
+    fp8_line = _summary(
+        B, n, C, 1, pf.time_loop(pf.layer, args.steps, args.warmup),
+        pf.time_loop(pf.three, args.steps, args.warmup),
+        pf.per_call(pf.layer, ("mhc_pre_fp8", "mhc_post_res_coeffs_fp8"), args.steps),
+        pf.per_call(pf.three, ("mhc_coeffs_fp8", "mhc_pre_fp8", "mhc_post_res_fp8"), args.steps))
+    del pf, fp8_inp
+
+    # ---- the other workloads (parity-test shapes), both dtypes: mean over 50
+    # back-to-back layers (launch-bound at tiny and decode sizes); decode also
+    # "cold", with a 512 MB write between layers and events around each layer.
+    workloads = {}
+    for wname in synth.CONFIGS:
+        if wname == args.workload:
+            continue
+        wcfg = synth.CONFIGS[wname]
+        wsteps = 50
+        res = {"shape": f"n={wcfg['n']} C={wcfg['C']} B={wcfg['B']}"}
+        for dname, fp8 in (("bf16", False), ("fp8", True)):
+            winp = (synth.make_config_fp8 if fp8 else synth.make_config)(wname, device="cuda")
+            pw = Pipeline(mhc, torch, winp, fp8=fp8)
+            res[dname] = _summary(wcfg["B"], wcfg["n"], wcfg["C"], 1 if fp8 else 2,
+                                  pw.time_loop(pw.layer, wsteps, 10), pw.time_loop(pw.three, wsteps, 10))
+            if wname == "decode":
+                scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+                cold = []
+                for _ in range(20):
+                    scratch.fill_(1)
+                    e0, e1 = ev(), ev()
+                    e0.record(stream)
+                    pw.layer()
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    cold.append(e0.elapsed_time(e1))
+                cold.sort()
+                res[dname]["cold_us_per_layer_median"] = round(cold[len(cold) // 2] * 1e3, 2)
+                del scratch
+            del pw, winp
+        workloads[wname] = res
+
     bytes_call = path_bytes(B, n, C)
     pipe_bytes = bytes_call["mhc_pre"] + bytes_call["mhc_post_res_coeffs"]
     three_bytes = sum(bytes_call[c] for c in three_calls)
@@ -359,6 +512,9 @@ def main():
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "fp8": dict(fp8_line, note="E4M3 residual stream (X_t, F_out, F_pre, X_next), same workload; "
+                                  "the *_fp8 entry points"),
+        "workloads": workloads,
         "kernel_source_sha": {c: kernel_source_sha(c) for c in CALL_SOURCES},
     }
     print(json.dumps(line), flush=True)

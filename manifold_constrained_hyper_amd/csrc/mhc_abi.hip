@@ -175,21 +175,26 @@ int post_res_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t, const
 }
 
 // How mhc_post_res_coeffs(_fp8) runs: small B -> the apply, then the
-// one-launch small-B coefficient kernel on X_next; n = 8 -> the apply, then
-// the split-K product on X_next (at n = 8 the fused kernel re-reads phi from
-// L2 for every 16 rows, 80 columns wide, and loses to the two passes; set
-// MHC_FUSED_N8=1 to run it anyway); otherwise the fused kernel.
+// one-launch small-B coefficient kernel on X_next; otherwise the fused kernel,
+// except where the apply followed by the split-K product on X_next measured
+// faster (chained layers on MI355X):
+//   n = 8: the fused kernel re-reads 80-column phi blocks from L2 for every 16
+//          rows (501 vs 321 us bf16 at B=8192, C=4096); MHC_FUSED_N8=1 forces it;
+//   E4M3:  half the bytes per step leave the fused kernel's fixed per-step
+//          cost (barriers, flush, phi from L2) in front (407 vs 370 us per
+//          layer at n=4, C=7168, B=16384); MHC_FUSED_FP8=1 forces it.
 enum class FusedRoute { kSmall, kTwoPass, kFused };
 
-FusedRoute fused_route(int64_t B, int32_t n, int64_t C) {
+FusedRoute fused_route(int64_t B, int32_t n, int64_t C, Elt e) {
   if (mhc::use_coeffs_small(B, n, C)) return FusedRoute::kSmall;
   if (n == 8 && !std::getenv("MHC_FUSED_N8")) return FusedRoute::kTwoPass;
+  if (e.fp8 && !std::getenv("MHC_FUSED_FP8")) return FusedRoute::kTwoPass;
   return FusedRoute::kFused;
 }
 
 size_t post_res_coeffs_ws_bytes(int64_t B, int32_t n, int64_t C, Elt e) {
   if (check_shape_elt(B, n, C, e) != MHC_OK || B == 0 || C % 32 != 0) return 0;
-  switch (fused_route(B, n, C)) {
+  switch (fused_route(B, n, C, e)) {
     case FusedRoute::kSmall: return mhc::plan_coeffs_small(B, n, C).total_bytes;
     case FusedRoute::kTwoPass: return mhc::gemm_workspace_bytes(split_plan(B, n, C, e), B, n);
     default: return mhc::plan_post_res_next(B, n, C).total_bytes;
@@ -213,7 +218,7 @@ int post_res_coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t
       !aligned(workspace, 16) || !aligned(H, 4) || !aligned(b_pre, 4) || !aligned(b_post, 4) ||
       !aligned(b_res, 4) || !aligned(logits_next, 4) || !aligned(r_next, 4) || !aligned(H_next, 4))
     return MHC_ERR_UNSUPPORTED;
-  const FusedRoute route = fused_route(B, n, C);
+  const FusedRoute route = fused_route(B, n, C, e);
   const mhc::FusedPlan plan = mhc::plan_post_res_next(B, n, C);
   const size_t ws_need = post_res_coeffs_ws_bytes(B, n, C, e);
   const int64_t N = ncoef(n), K = (int64_t)n * C;

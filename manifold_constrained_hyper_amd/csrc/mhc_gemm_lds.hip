@@ -310,5 +310,8 @@ template hipError_t launch_gemm_lds_typed<1, 1, 256, 4, 1>(const GemmPlan &, int
 template hipError_t launch_gemm_lds_typed<2, 1, 256, 4, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
 template hipError_t launch_gemm_lds_typed<4, 1, 256, 4, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
 template hipError_t launch_gemm_lds_typed<8, 1, 256, 2, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<1, 2, 256, 3, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<2, 2, 256, 3, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<4, 2, 256, 3, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
 
 }  // namespace mhc

@@ -248,6 +248,7 @@ hipError_t launch_n(const GemmPlan &p, int64_t B, int64_t C, const void *X, cons
                     float *ws, hipStream_t st) {
   if (p.algo == 1 && p.xb == 1) {
     if constexpr (NS == 8) return launch_gemm_lds_typed<NS, 1, 256, 2, 1>(p, B, C, X, phi, ws, st);
+    else if (p.mb == 2) return launch_gemm_lds_typed<NS, 2, 256, 3, 1>(p, B, C, X, phi, ws, st);
     else return launch_gemm_lds_typed<NS, 1, 256, 4, 1>(p, B, C, X, phi, ws, st);
   }
   if (p.algo == 1) {
@@ -308,7 +309,12 @@ GemmPlan plan_gemm(int64_t B, int n, int64_t C, bool fp8_x) {
       const long v = strtol(e, nullptr, 10);
       if (v > 0) target = v;
     }
-    GemmPlan p = plan_gemm_custom(B, n, C, 1, 1, 256, n == 8 ? 2 : 4, target);
+    int mb = n == 8 ? 1 : 2;  // 128-row tiles: phi per X byte as for bf16 with 64 rows
+    if (const char *e = getenv("MHC_GEMM_MB")) {
+      const long v = strtol(e, nullptr, 10);
+      if (v == 1 || (v == 2 && n != 8)) mb = (int)v;
+    }
+    GemmPlan p = plan_gemm_custom(B, n, C, 1, mb, 256, n == 8 ? 2 : (mb == 2 ? 3 : 4), target);
     p.xb = 1;
     return p;
   }

@@ -45,7 +45,8 @@ def _gpu():
 # mhc_coeffs_fp8 has three implementations: the one-launch small-B kernel
 # (default up to 256 rows), the split-K product with X staged through LDS
 # (default above), and the persistent product kernel (MHC_GEMM_ALGO=2).  The
-# fused call also has its fused kernel (forced at n = 8 with MHC_FUSED_N8).
+# fused call is the apply + product by default and the fused kernel with
+# MHC_FUSED_FP8 (and MHC_FUSED_N8 at n = 8), both exercised here.
 # Every one must meet the bar at every size it supports.
 @pytest.fixture(params=["default", "small", "split", "persistent"])
 def path(request, monkeypatch):
@@ -59,6 +60,7 @@ def path(request, monkeypatch):
         monkeypatch.setenv("MHC_SMALL_MAX_B", "0")
         monkeypatch.setenv("MHC_GEMM_ALGO", "2")
         monkeypatch.setenv("MHC_FUSED_N8", "1")
+        monkeypatch.setenv("MHC_FUSED_FP8", "1")
     return request.param
 
 
@@ -219,9 +221,13 @@ def _layers(n, C, B, dist, seed):
     return cur, nxt
 
 
+@pytest.mark.parametrize("kernel", ["default", "fused"])
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "large", "wide"])
-def test_fp8_fused_named(name):
-    _say(f"fp8 fused {name}")
+def test_fp8_fused_named(name, kernel, monkeypatch):
+    if kernel == "fused":
+        monkeypatch.setenv("MHC_FUSED_FP8", "1")
+        monkeypatch.setenv("MHC_FUSED_N8", "1")
+    _say(f"fp8 fused {name} kernel={kernel}")
     cfg = synth.CONFIGS[name]
     cur, nxt = _layers(cfg["n"], cfg["C"], cfg["B"], cfg["x_dist"], cfg["seed"])
     o, ref, f = _fused(cur, nxt)
@@ -240,8 +246,11 @@ def test_fp8_fused_ragged(B, n, C, path):
     _check_fused(cur, nxt, o, ref, f, list(range(B)), f"B{B}n{n}C{C}")
 
 
-def test_fp8_fused_deterministic():
-    _say("fp8 fused determinism")
+@pytest.mark.parametrize("kernel", ["default", "fused"])
+def test_fp8_fused_deterministic(kernel, monkeypatch):
+    if kernel == "fused":
+        monkeypatch.setenv("MHC_FUSED_FP8", "1")
+    _say(f"fp8 fused determinism kernel={kernel}")
     cfg = synth.CONFIGS["prefill"]
     cur, nxt = _layers(cfg["n"], cfg["C"], cfg["B"], cfg["x_dist"], cfg["seed"])
     _, _, a = _fused(cur, nxt)
