@@ -298,6 +298,54 @@ def copy_probe(args):
                       "gbps_read_plus_write": 2 * nbytes / ms / 1e6}), flush=True)
 
 
+def _variants(args, mhc, torch, synth, stream, ev):
+    """The E4M3 pipeline on the headline workload and both dtypes on the
+    other workloads (see the module docstring)."""
+    B, n, C = (synth.CONFIGS[args.workload][k] for k in ("B", "n", "C"))
+    fp8_inp = synth.make_config_fp8(args.workload, device="cuda")
+    pf = Pipeline(mhc, torch, fp8_inp, fp8=True)
+    fp8_line = _summary(
+        B, n, C, 1, pf.time_loop(pf.layer, args.steps, args.warmup),
+        pf.time_loop(pf.three, args.steps, args.warmup),
+        pf.per_call(pf.layer, ("mhc_pre_fp8", "mhc_post_res_coeffs_fp8"), args.steps),
+        pf.per_call(pf.three, ("mhc_coeffs_fp8", "mhc_pre_fp8", "mhc_post_res_fp8"), args.steps))
+    del pf, fp8_inp
+
+    # ---- the other workloads (parity-test shapes), both dtypes: mean over 50
+    # back-to-back layers (launch-bound at tiny and decode sizes); decode also
+    # "cold", with a 512 MB write between layers and events around each layer.
+    workloads = {}
+    for wname in synth.CONFIGS:
+        if wname == args.workload:
+            continue
+        wcfg = synth.CONFIGS[wname]
+        wsteps = 50
+        res = {"shape": f"n={wcfg['n']} C={wcfg['C']} B={wcfg['B']}"}
+        for dname, fp8 in (("bf16", False), ("fp8", True)):
+            winp = (synth.make_config_fp8 if fp8 else synth.make_config)(wname, device="cuda")
+            pw = Pipeline(mhc, torch, winp, fp8=fp8)
+            res[dname] = _summary(wcfg["B"], wcfg["n"], wcfg["C"], 1 if fp8 else 2,
+                                  pw.time_loop(pw.layer, wsteps, 10), pw.time_loop(pw.three, wsteps, 10))
+            if wname == "decode":
+                scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+                cold = []
+                for _ in range(20):
+                    scratch.fill_(1)
+                    e0, e1 = ev(), ev()
+                    e0.record(stream)
+                    pw.layer()
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    cold.append(e0.elapsed_time(e1))
+                cold.sort()
+                res[dname]["cold_us_per_layer_median"] = round(cold[len(cold) // 2] * 1e3, 2)
+                del scratch
+            del pw, winp
+        workloads[wname] = res
+
+    return fp8_line, workloads
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -309,6 +357,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--kernel-only", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the E4M3 and other-workload sections (profiling runs of one workload)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -436,46 +486,9 @@ def main():
     # ---- the E4M3 residual-stream variant on the same workload (same shapes
     # and draws, X and F_out rounded to E4M3)
     del X, Hs, out
-    fp8_inp = synth.make_config_fp8(args.workload, device="cuda")
-    pf = Pipeline(mhc, torch, fp8_inp, fp8=True)
-    fp8_line = _summary(
-        B, n, C, 1, pf.time_loop(pf.layer, args.steps, args.warmup),
-        pf.time_loop(pf.three, args.steps, args.warmup),
-        pf.per_call(pf.layer, ("mhc_pre_fp8", "mhc_post_res_coeffs_fp8"), args.steps),
-        pf.per_call(pf.three, ("mhc_coeffs_fp8", "mhc_pre_fp8", "mhc_post_res_fp8"), args.steps))
-    del pf, fp8_inp
-
-    # ---- the other workloads (parity-test shapes), both dtypes: mean over 50
-    # back-to-back layers (launch-bound at tiny and decode sizes); decode also
-    # "cold", with a 512 MB write between layers and events around each layer.
-    workloads = {}
-    for wname in synth.CONFIGS:
-        if wname == args.workload:
-            continue
-        wcfg = synth.CONFIGS[wname]
-        wsteps = 50
-        res = {"shape": f"n={wcfg['n']} C={wcfg['C']} B={wcfg['B']}"}
-        for dname, fp8 in (("bf16", False), ("fp8", True)):
-            winp = (synth.make_config_fp8 if fp8 else synth.make_config)(wname, device="cuda")
-            pw = Pipeline(mhc, torch, winp, fp8=fp8)
-            res[dname] = _summary(wcfg["B"], wcfg["n"], wcfg["C"], 1 if fp8 else 2,
-                                  pw.time_loop(pw.layer, wsteps, 10), pw.time_loop(pw.three, wsteps, 10))
-            if wname == "decode":
-                scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-                cold = []
-                for _ in range(20):
-                    scratch.fill_(1)
-                    e0, e1 = ev(), ev()
-                    e0.record(stream)
-                    pw.layer()
-                    e1.record(stream)
-                    torch.cuda.synchronize()
-                    cold.append(e0.elapsed_time(e1))
-                cold.sort()
-                res[dname]["cold_us_per_layer_median"] = round(cold[len(cold) // 2] * 1e3, 2)
-                del scratch
-            del pw, winp
-        workloads[wname] = res
+    fp8_line, workloads = None, None
+    if not args.headline_only:
+        fp8_line, workloads = _variants(args, mhc, torch, synth, stream, ev)
 
     bytes_call = path_bytes(B, n, C)
     pipe_bytes = bytes_call["mhc_pre"] + bytes_call["mhc_post_res_coeffs"]
@@ -512,8 +525,9 @@ def main():
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "fp8": dict(fp8_line, note="E4M3 residual stream (X_t, F_out, F_pre, X_next), same workload; "
-                                  "the *_fp8 entry points"),
+        "fp8": None if fp8_line is None else dict(
+            fp8_line, note="E4M3 residual stream (X_t, F_out, F_pre, X_next), same workload; "
+                           "the *_fp8 entry points"),
         "workloads": workloads,
         "kernel_source_sha": {c: kernel_source_sha(c) for c in CALL_SOURCES},
     }
