@@ -34,3 +34,4 @@ from .mhc_oracle import (  # noqa: F401
 )
 
 from . import fp8  # noqa: F401,E402  (E4M3 encode / decode for the FP8 variant)
+from . import lazy_prenorm  # noqa: F401,E402  (the Lazy Pre-Norm GEMM of [FreeNorm] section 2)
