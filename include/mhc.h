@@ -231,6 +231,32 @@ int mhc_post_res_coeffs_fp8(int64_t B, int32_t n, int64_t C,
                             float *logits_next, float *r_next, float *H_next,
                             void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Lazy Pre-Norm GEMM (a second workload on the same machinery).
+ *
+ * Section 2 of the page "Towards Free Normalization: Fusing Normalization
+ * into GEMM and Attention Kernels" ([FreeNorm]) defines
+ *     C = rmsnorm(A) @ B,  rmsnorm(A) = A * rstd[:, None],
+ *     rstd = rsqrt(sum(A^2, dim=-1) / K + eps)   (eps = 1e-5 on the page,
+ * no element-wise affine weight), and computes it lazily: the product runs on
+ * the raw A, the row sums of squares accumulate in the same k-loop, and each
+ * output row is scaled by rstd at the end (a row scaling commutes with the
+ * product).  [mHC-cutile] section 2.2's r is the same statistic without eps.
+ *
+ *   A     in  bf16 [M, K] row-major
+ *   W     in  bf16 [N, K] row-major: B passed as its transpose, the layout of a
+ *             linear layer's weight (both operands then have K contiguous)
+ *   eps   host fp32 (1e-5 in [FreeNorm])
+ *   C     out bf16 [M, N] row-major, fp32 accumulation, one round-to-nearest-
+ *             even at the end
+ *   rstd  out fp32 [M], or NULL if not wanted
+ *
+ * Requires K % 8 == 0 and N % 8 == 0 (16-byte rows), else
+ * MHC_ERR_UNSUPPORTED; M == 0 launches nothing; N < 1 or K < 1 is
+ * MHC_ERR_INVALID_ARG.  No workspace.  Other rules as for the calls above. */
+int mhc_lazy_prenorm_gemm(int64_t M, int64_t N, int64_t K, const void *A, const void *W,
+                          float eps, void *C, float *rstd, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

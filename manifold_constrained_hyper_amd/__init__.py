@@ -8,5 +8,5 @@ from .binding import (  # noqa: F401
     mhc_status_string, mhc_coeffs_workspace_size, mhc_coeffs_split_k,
     mhc_coeffs, mhc_pre, mhc_post_res, mhc_post_res_coeffs_workspace_size, mhc_post_res_coeffs,
     mhc_coeffs_fp8_workspace_size, mhc_coeffs_fp8, mhc_pre_fp8, mhc_post_res_fp8,
-    mhc_post_res_coeffs_fp8_workspace_size, mhc_post_res_coeffs_fp8,
+    mhc_post_res_coeffs_fp8_workspace_size, mhc_post_res_coeffs_fp8, mhc_lazy_prenorm_gemm,
 )

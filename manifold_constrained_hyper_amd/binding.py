@@ -24,7 +24,7 @@ EXPORTED = ("mhc_status_string", "mhc_coeffs_workspace_size", "mhc_coeffs_split_
             "mhc_coeffs", "mhc_pre", "mhc_post_res", "mhc_post_res_coeffs_workspace_size",
             "mhc_post_res_coeffs", "mhc_coeffs_fp8_workspace_size", "mhc_coeffs_fp8",
             "mhc_pre_fp8", "mhc_post_res_fp8", "mhc_post_res_coeffs_fp8_workspace_size",
-            "mhc_post_res_coeffs_fp8")
+            "mhc_post_res_coeffs_fp8", "mhc_lazy_prenorm_gemm")
 
 _lib = None
 
@@ -75,6 +75,8 @@ def load():
     lib.mhc_coeffs_fp8_workspace_size.restype = sz
     lib.mhc_post_res_coeffs_fp8_workspace_size.argtypes = [i64, i32, i64]
     lib.mhc_post_res_coeffs_fp8_workspace_size.restype = sz
+    lib.mhc_lazy_prenorm_gemm.argtypes = [i64, i64, i64, vp, vp, f32, vp, vp, vp]
+    lib.mhc_lazy_prenorm_gemm.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -224,6 +226,16 @@ def mhc_post_res_coeffs_fp8(B, n, C, X_t, F_out, H, X_next, phi_next, alpha_pre,
                                         _stream(stream))
     if check:
         _check(st, "mhc_post_res_coeffs_fp8")
+    return st
+
+
+def mhc_lazy_prenorm_gemm(M, N, K, A, W, C, rstd=None, eps=1e-5, stream=None, check=True):
+    """C = rmsnorm(A) @ W^T (A bf16 [M, K], W bf16 [N, K], C bf16 [M, N]); rstd
+    fp32 [M] if given (see include/mhc.h)."""
+    st = load().mhc_lazy_prenorm_gemm(int(M), int(N), int(K), _ptr(A), _ptr(W), float(eps), _ptr(C),
+                                      _ptr(rstd), _stream(stream))
+    if check:
+        _check(st, "mhc_lazy_prenorm_gemm")
     return st
 
 

@@ -365,4 +365,27 @@ int mhc_post_res_coeffs_fp8(int64_t B, int32_t n, int64_t C, const void *X_t, co
                               H_next, workspace, workspace_bytes, stream);
 }
 
+int mhc_lazy_prenorm_gemm(int64_t M, int64_t N, int64_t K, const void *A, const void *W,
+                          float eps, void *C, float *rstd, void *stream) {
+  if (M < 0 || N < 1 || K < 1) return MHC_ERR_INVALID_ARG;
+  if (K % 8 != 0 || N % 8 != 0) return MHC_ERR_UNSUPPORTED;
+  constexpr int64_t kMaxDim = (int64_t(1) << 31) - 256;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim ||
+      (M > 0 && (M * K > kMaxElems || N * K > kMaxElems || M * N > kMaxElems)))
+    return MHC_ERR_UNSUPPORTED;
+  if (M == 0) return MHC_OK;
+  if (!A || !W || !C) return MHC_ERR_INVALID_ARG;
+  if (!aligned(A, 16) || !aligned(W, 16) || !aligned(C, 16) || (rstd && !aligned(rstd, 4)))
+    return MHC_ERR_UNSUPPORTED;
+  const Span sa = span(A, (size_t)(M * K * 2)), sw = span(W, (size_t)(N * K * 2));
+  const Span sc = span(C, (size_t)(M * N * 2));
+  if (overlaps(sc, sa) || overlaps(sc, sw)) return MHC_ERR_INVALID_ARG;
+  if (rstd) {
+    const Span sr = span(rstd, (size_t)M * 4);
+    if (overlaps(sr, sa) || overlaps(sr, sw) || overlaps(sr, sc)) return MHC_ERR_INVALID_ARG;
+  }
+  return from_hip(mhc::launch_lazy_prenorm_gemm(M, N, K, A, W, eps, C, rstd,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -68,6 +68,10 @@ hipError_t launch_post_res_next(const FusedPlan &p, int n, int mode, int64_t B, 
                                 const void *X, const void *F, const float *H, void *Y,
                                 const void *phi_next, void *ws_base, hipStream_t st);
 
+// Lazy Pre-Norm GEMM C = rmsnorm(A) W^T (mhc_lazy_prenorm.hip).
+hipError_t launch_lazy_prenorm_gemm(int64_t M, int64_t N, int64_t K, const void *A, const void *W,
+                                    float eps, void *C, float *rstd, hipStream_t st);
+
 // FP8 (E4M3) streaming kernels (mhc_stream_fp8.hip).
 hipError_t launch_pre_fp8(int n, int64_t B, int64_t C, const void *X, const float *H,
                           void *F_pre, hipStream_t st);

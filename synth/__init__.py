@@ -125,3 +125,31 @@ def make_config_fp8(name, device="cpu"):
 def e4m3_codes(t):
     """Raw E4M3 codes of a uint8 (or float8_e4m3fn) tensor as a numpy uint8 array."""
     return t.detach().contiguous().view(torch.uint8).cpu().numpy()
+
+
+# Lazy Pre-Norm GEMM workloads (C = rmsnorm(A) @ W^T): A is the pre-mixed
+# layer input of the large workload (rows of a fixed scale spread, so rstd
+# varies), W a linear layer's weight [N, K].
+LPN_CONFIGS = {
+    "lpn_proj": dict(M=16384, N=1536, K=7168, seed=2001),
+    "lpn_square": dict(M=16384, N=7168, K=7168, seed=2002),
+}
+
+
+def make_lpn_inputs(M, N, K, seed=0, device="cpu", row_chunk=2048):
+    """A bf16 [M, K] = z * s_row (z ~ N(0, 1), s_row = 2^u, u ~ U(-2, 2) per
+    row); W bf16 [N, K] ~ N(0, sigma = 1/sqrt(K))."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    A = torch.empty(M, K, dtype=torch.bfloat16, device=device)
+    for lo in range(0, M, row_chunk):
+        hi = min(M, lo + row_chunk)
+        z = torch.randn(hi - lo, K, generator=gen, device=device)
+        u = torch.rand(hi - lo, 1, generator=gen, device=device) * 4.0 - 2.0
+        A[lo:hi] = (z * torch.exp2(u)).to(torch.bfloat16)
+    W = torch.empty(N, K, dtype=torch.bfloat16, device=device)
+    for lo in range(0, N, row_chunk):
+        hi = min(N, lo + row_chunk)
+        W[lo:hi] = (torch.randn(hi - lo, K, generator=gen, device=device) / math.sqrt(K)).to(torch.bfloat16)
+    return {"M": M, "N": N, "K": K, "A": A, "W": W, "seed": int(seed)}

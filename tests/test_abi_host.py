@@ -186,3 +186,30 @@ def test_fp8_validation():
     assert fused(Y=A) == mhc.MHC_ERR_INVALID_ARG
     need = mhc.mhc_post_res_coeffs_fp8_workspace_size(16, 4, 64)
     assert need > 0 and fused(ws_bytes=need - 1) == mhc.MHC_ERR_WORKSPACE
+
+
+def test_lazy_prenorm_validation():
+    """mhc_lazy_prenorm_gemm: K and N multiples of 8, 16-byte aligned operands,
+    C and rstd disjoint from the inputs and each other; M == 0 is a no-op."""
+    Ap, Wp, Cp, Rp = _addrs(4)
+
+    def call(M=32, N=64, K=64, a=Ap, w=Wp, c=Cp, r=Rp):
+        return mhc.mhc_lazy_prenorm_gemm(M, N, K, a, w, c, r, stream=0, check=False)
+
+    assert call(M=0) == mhc.MHC_OK
+    assert call(M=0, a=None, w=None, c=None, r=None) == mhc.MHC_OK
+    assert call(M=-1) == mhc.MHC_ERR_INVALID_ARG
+    assert call(N=0) == mhc.MHC_ERR_INVALID_ARG
+    assert call(K=0) == mhc.MHC_ERR_INVALID_ARG
+    assert call(K=60) == mhc.MHC_ERR_UNSUPPORTED
+    assert call(N=60) == mhc.MHC_ERR_UNSUPPORTED
+    for k in ("a", "w", "c"):
+        assert call(**{k: None}) == mhc.MHC_ERR_INVALID_ARG, k
+    assert call(a=Ap + 8) == mhc.MHC_ERR_UNSUPPORTED
+    assert call(c=Cp + 4) == mhc.MHC_ERR_UNSUPPORTED
+    assert call(r=Rp + 2) == mhc.MHC_ERR_UNSUPPORTED
+    # C right after A's 32*64*2 bytes is fine; one piece earlier overlaps
+    assert call(c=Ap + 32 * 64 * 2 - 16) == mhc.MHC_ERR_INVALID_ARG
+    assert call(c=Wp + 16) == mhc.MHC_ERR_INVALID_ARG
+    assert call(r=Cp + 64) == mhc.MHC_ERR_INVALID_ARG                  # rstd inside C
+    assert call(M=1 << 31) == mhc.MHC_ERR_UNSUPPORTED
