@@ -251,9 +251,10 @@ int mhc_post_res_coeffs_fp8(int64_t B, int32_t n, int64_t C,
  *             even at the end
  *   rstd  out fp32 [M], or NULL if not wanted
  *
- * Requires K % 8 == 0 and N % 8 == 0 (16-byte rows), else
- * MHC_ERR_UNSUPPORTED; M == 0 launches nothing; N < 1 or K < 1 is
- * MHC_ERR_INVALID_ARG.  No workspace.  Other rules as for the calls above. */
+ * Requires K % 8 == 0 and N % 8 == 0 (16-byte rows), K <= 2^22 and
+ * M * N, M * K, N * K <= 2^40, else MHC_ERR_UNSUPPORTED; M == 0 launches
+ * nothing; N < 1 or K < 1 is MHC_ERR_INVALID_ARG.  No workspace.  Other
+ * rules as for the calls above. */
 int mhc_lazy_prenorm_gemm(int64_t M, int64_t N, int64_t K, const void *A, const void *W,
                           float eps, void *C, float *rstd, void *stream);
 

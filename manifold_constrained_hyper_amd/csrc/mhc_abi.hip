@@ -370,7 +370,8 @@ int mhc_lazy_prenorm_gemm(int64_t M, int64_t N, int64_t K, const void *A, const 
   if (M < 0 || N < 1 || K < 1) return MHC_ERR_INVALID_ARG;
   if (K % 8 != 0 || N % 8 != 0) return MHC_ERR_UNSUPPORTED;
   constexpr int64_t kMaxDim = (int64_t(1) << 31) - 256;
-  if (M > kMaxDim || N > kMaxDim || K > kMaxDim ||
+  constexpr int64_t kMaxLpnK = int64_t(1) << 22;  // 32-bit in-tile byte offsets
+  if (M > kMaxDim || N > kMaxDim || K > kMaxLpnK ||
       (M > 0 && (M * K > kMaxElems || N * K > kMaxElems || M * N > kMaxElems)))
     return MHC_ERR_UNSUPPORTED;
   if (M == 0) return MHC_OK;

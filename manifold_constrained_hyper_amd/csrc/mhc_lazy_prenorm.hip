@@ -9,26 +9,32 @@
 // transpose W [N, K] (a linear layer's weight), so both operands are
 // K-contiguous rows.
 //
-// gfx950 design (the page's kernel is TLX/Blackwell; this is written for
-// CDNA4):
-//  * workgroup tile 256 x 256 of C, 4 waves, each 128 x 128 (8 x 8 blocks of
-//    v_mfma_f32_16x16x32_bf16: 256 accumulator registers per wave, one wave
-//    per SIMD);
-//  * A and W tiles move to LDS by direct-to-LDS loads (global_load_lds_dwordx4,
-//    each instruction 1 KiB = 8 rows of a 64-k chunk), two stages of 64 KiB;
-//    within a 128-byte row the 16-byte pieces are XOR-swizzled by
-//    ((row >> 1) & 7), which makes the operand ds_read_b128 of 16 rows
-//    bank-conflict-free;
-//  * each block computes C^T = W A^T (W as the MFMA A operand), so a lane ends
-//    with 4 consecutive output columns of one row: the epilogue scales them
-//    by that row's rstd and stores 8 bytes;
+// gfx950 design (the page's kernel is written for another GPU; this one is
+// laid out for CDNA4):
+//  * workgroup tile 256 x 256 of C, 8 waves (two per SIMD, so one wave's LDS
+//    reads and barrier waits hide behind the other's matrix work); each wave
+//    owns 128 A rows x 64 W rows as 4 x 2 blocks of v_mfma_f32_32x32x16_bf16
+//    (128 accumulator registers);
+//  * A and W move to LDS in 64-wide k-chunks by direct-to-LDS loads
+//    (global_load_lds_dwordx4: one instruction fills 8 rows of 128 bytes),
+//    two stages of 64 KiB; the loads are issued from inline asm with an
+//    SGPR tile base and per-lane 32-bit row offsets, and waited for with an
+//    explicit vmcnt before the chunk's barrier (the compiler would otherwise
+//    wait for every outstanding LDS DMA before each LDS read);
+//  * within a 128-byte row the 16-byte pieces are XOR-swizzled by
+//    ((row >> 1) & 7), so 16 consecutive rows read at one piece index hit 16
+//    distinct bank groups (LDS serves 256 bytes per clock);
+//  * operands of k-step t+1 are read while the MFMAs of step t run (two
+//    register sets of 24 VGPRs); scheduling barriers keep the compiler from
+//    sinking those reads next to their use;
+//  * each block computes C^T = W A^T (W as the MFMA A operand), so a lane
+//    ends with runs of 4 consecutive output columns of one row: the epilogue
+//    scales them by that row's rstd and stores 8 bytes;
 //  * the row sums of squares run on the vector unit beside the matrix core:
-//    thread t adds the squares of row t of every A chunk in LDS (the matrix
-//    core's accumulators fill the 256 AGPRs, so a Gram block there would
-//    spill);
-//  * tiles are walked in groups of 16 tile rows (so the ~256 resident
-//    workgroups share A and W tiles in L2 / MALL), each XCD taking a
-//    contiguous run of the order.
+//    thread t adds the squares of half of row t >> 1 of every A chunk (four
+//    independent partial sums);
+//  * tiles are walked in groups of 4 tile rows, each XCD taking a contiguous
+//    run of the order.
 #include "mhc_device.h"
 #include "mhc_launch.h"
 
@@ -36,84 +42,60 @@ namespace mhc {
 
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void_t;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kTM = 256, kTN = 256;  // workgroup tile
-constexpr int kKC = 64;              // k per chunk
-constexpr int kRowBytes = kKC * 2;   // 128 bytes: 8 pieces of 16 bytes
-constexpr int kTileBytes = 256 * kRowBytes;         // 32 KiB per operand tile
-constexpr int kStageBytes = 2 * kTileBytes;          // A + W
+constexpr int kTile = 256;             // workgroup tile (rows of A and of W)
+constexpr int kKC = 64;                // k per chunk
+constexpr int kRB = kKC * 2;           // 128 bytes per tile row per chunk
+constexpr int kPieces = kKC / 8;       // 16-byte pieces per row
+constexpr int kTileBytes = kTile * kRB;
+constexpr int kStageBytes = 2 * kTileBytes;  // A tile + W tile
 constexpr int kStages = 2;
-constexpr int kGroupM = 16;          // tile rows per group of the walk
+constexpr int kRowsPerInst = 1024 / kRB;                // 8 rows per DMA instruction
+constexpr int kWaves = 8;
+constexpr int kInstPerWave = kTile / kRowsPerInst / kWaves;  // 4 per operand
+constexpr int kLoadsPerWave = 2 * kInstPerWave;         // vmcnt per chunk
+constexpr int kSteps = kKC / 16;                        // MFMA k-steps per chunk
+constexpr int kGroupM = 4;
 
 // Zero source for pieces past K (global loads must come from somewhere).
 __device__ __attribute__((aligned(256))) uint32_t g_lpn_zero[64];
 
-__device__ __forceinline__ void wait_vm(int n) {
-  // s_waitcnt vmcnt(n) with expcnt / lgkmcnt at their maxima; n is 0 or 16.
-  if (n == 0)
-    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8) | (0 << 14));
-  else
-    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8) | (1 << 14));  // vmcnt = 16
-}
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-__device__ __forceinline__ void wait_lgkm0() {
-  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+// Direct-to-LDS 16-byte loads: lane i's data lands at M0 + 16 i.
+__device__ __forceinline__ void dma_saddr(const void *sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory");
 }
+__device__ __forceinline__ void dma_vaddr(const void *vaddr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(vaddr), "s"(lds_addr) : "memory");
+}
+template <int N> __device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
 
-// Per-lane part of a chunk load: lane l of an instruction covers tile row
-// 8*inst + (l >> 3) and the 16-byte piece (l & 7) ^ ((row >> 1) & 7).  Since
-// (row >> 1) & 7 = ((inst & 1) * 4 + (l >> 4)) & 7, the piece depends only on
-// the lane and the parity of the instruction.
-struct LoadLane {
-  int rsub;        // row within the instruction's 8 rows
-  int piece[2];    // piece for even / odd instructions
+struct Operands {
+  bf16x8 a[4], w[2];
 };
 
-__device__ __forceinline__ LoadLane load_lane(int lane) {
-  LoadLane L;
-  L.rsub = lane >> 3;
-  const int slot = lane & 7;
-  L.piece[0] = slot ^ ((lane >> 4) & 7);
-  L.piece[1] = slot ^ ((4 + (lane >> 4)) & 7);
-  return L;
-}
-
-// Issue the 16 direct-to-LDS loads of this wave for one chunk: 8 of A's 32
-// instructions and 8 of W's.  Rows past M (N) read the last row; pieces past
-// K read the zero block.
-__device__ __forceinline__ void issue(char *stage, int wave, const LoadLane &L,
-                                      const uint16_t *__restrict__ A,
-                                      const uint16_t *__restrict__ W, int m0, int n0, int M,
-                                      int N, int K, int k0) {
-  const uint16_t *zero = reinterpret_cast<const uint16_t *>(g_lpn_zero);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int inst = wave * 8 + j;  // 0..31, wave-uniform
-    const int r = inst * 8 + L.rsub;
-    const int k = k0 + L.piece[j & 1] * 8;
-    const uint16_t *pa = A + ((size_t)(unsigned)min(m0 + r, M - 1) * (unsigned)K + (unsigned)k);
-    const uint16_t *pw = W + ((size_t)(unsigned)min(n0 + r, N - 1) * (unsigned)K + (unsigned)k);
-    __builtin_amdgcn_global_load_lds(k < K ? pa : zero, (lds_void_t *)(stage + inst * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(k < K ? pw : zero, (lds_void_t *)(stage + kTileBytes + inst * 1024), 16, 0, 0);
-  }
-}
-
-__global__ __launch_bounds__(256, 1) void lazy_prenorm_gemm_kernel(
+__global__ __launch_bounds__(512, 1) void lazy_prenorm_gemm_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, uint16_t *__restrict__ Cout,
-    float *__restrict__ rstd_out, int M, int N, int K, float inv_k, float eps, int tiles_m,
-    int tiles_n) {
+    float *__restrict__ rstd_out, int M, int N, int K, float inv_k, float eps, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageBytes];
-  __shared__ float rs_lds[kTM];
+  __shared__ float rs_lds[kTile];
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int m = lane & 15, g = lane >> 4;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int j32 = lane & 31, g = lane >> 5;
+  const int wm = wave & 1, wn = wave >> 1;  // 2 x 4 waves
 
-  // Tile of this workgroup: each XCD (workgroups are dealt to the 8 XCDs in
-  // turn) walks a contiguous run of the grouped order.
+  // Tile of this workgroup: workgroups are dealt to the 8 XCDs in turn; each
+  // XCD walks a contiguous run of the grouped order.
   const int T = tiles_m * tiles_n;
   const int bid = blockIdx.x;
   const int q = T >> 3, rr8 = T & 7, x = bid & 7;
@@ -124,85 +106,165 @@ __global__ __launch_bounds__(256, 1) void lazy_prenorm_gemm_kernel(
   const int within = lin - group * kGroupM * tiles_n;
   const int tm = gm0 + within % gsz;
   const int tn = within / gsz;
-  const int m0 = tm * kTM, n0 = tn * kTN;
+  const int m0 = tm * kTile, n0 = tn * kTile;
 
-  f32x4 acc[8][8];
+  // DMA: this wave issues instructions kInstPerWave*wave + jj of each operand;
+  // instruction i fills tile rows 8 i .. 8 i + 7, lane l row 8 i + (l >> 3),
+  // slot l & 7, which holds piece slot ^ swz(row).  Rows past M (N) repeat the
+  // last row (their outputs are not stored).
+  const uint32_t rowK2 = (uint32_t)K * 2u;
+  const int rsub = lane / kPieces, slot = lane % kPieces;
+  uint32_t voa[kInstPerWave], vow[kInstPerWave];
+  int pce[kInstPerWave];
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+  for (int jj = 0; jj < kInstPerWave; ++jj) {
+    const int r = kRowsPerInst * (kInstPerWave * wave + jj) + rsub;
+    pce[jj] = slot ^ swz(r);
+    voa[jj] = (uint32_t)(min(m0 + r, M - 1) - m0) * rowK2 + pce[jj] * 16;
+    vow[jj] = (uint32_t)(min(n0 + r, N - 1) - n0) * rowK2 + pce[jj] * 16;
+  }
+  const char *Ab = reinterpret_cast<const char *>(A) + (size_t)m0 * rowK2;
+  const char *Wb = reinterpret_cast<const char *>(W) + (size_t)n0 * rowK2;
+  auto issue = [&](int stage, int k0) {
+    const uint32_t sb = lds_base + stage * kStageBytes + kInstPerWave * wave * 1024;
+    const char *ab = Ab + (size_t)k0 * 2, *wb = Wb + (size_t)k0 * 2;
+    if (k0 + kKC <= K) {
 #pragma unroll
-    for (int b = 0; b < 8; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float sumsq = 0.f;  // thread t: row t of the tile
+      for (int jj = 0; jj < kInstPerWave; ++jj) {
+        dma_saddr(ab, voa[jj], sb + jj * 1024);
+        dma_saddr(wb, vow[jj], sb + kTileBytes + jj * 1024);
+      }
+    } else {  // ragged last chunk: pieces past K read the zero block
+      const char *zero = reinterpret_cast<const char *>(g_lpn_zero);
+#pragma unroll
+      for (int jj = 0; jj < kInstPerWave; ++jj) {
+        const bool in = k0 + pce[jj] * 8 < K;
+        dma_vaddr(in ? ab + voa[jj] : zero, sb + jj * 1024);
+        dma_vaddr(in ? wb + vow[jj] : zero, sb + kTileBytes + jj * 1024);
+      }
+    }
+  };
+
+  // Operand reads: k-step t of a chunk uses piece 2t + g of row j32 of each
+  // 32-row block (the 32x32x16 operand layout: lane l supplies k 8 (l >> 5)
+  // .. +7 of row l & 31).
+  const int sw = swz(j32);
+  const int offa = (wm * 128 + j32) * kRB, offw = kTileBytes + (wn * 64 + j32) * kRB;
+  auto read_ops = [&](Operands &o, int stage, int t) {
+    const char *st = lds + stage * kStageBytes;
+    const int sl = ((2 * t + g) ^ sw) * 16;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) o.a[b] = *reinterpret_cast<const bf16x8 *>(st + offa + b * 32 * kRB + sl);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) o.w[b] = *reinterpret_cast<const bf16x8 *>(st + offw + b * 32 * kRB + sl);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Row sums of squares: thread t takes row t >> 1, pieces 4 (t & 1) .. +3.
+  const int srow = tid >> 1, sh = tid & 1;
+  u32x4 sq[kPieces / 2];
+  auto read_sq = [&](int stage) {
+    const char *st = lds + stage * kStageBytes + srow * kRB;
+#pragma unroll
+    for (int p = 0; p < kPieces / 2; ++p)
+      sq[p] = *reinterpret_cast<const u32x4 *>(st + ((((kPieces / 2) * sh + p) ^ swz(srow)) * 16));
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  float ssp[4] = {0.f, 0.f, 0.f, 0.f};
+  auto add_sq = [&]() {
+#pragma unroll
+    for (int p = 0; p < kPieces / 2; ++p)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float lo = bf16_lo(sq[p][w]), hi = bf16_hi(sq[p][w]);
+        ssp[w] = fmaf(lo, lo, ssp[w]);
+        ssp[w] = fmaf(hi, hi, ssp[w]);
+      }
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+  auto mfma = [&](const Operands &o) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+        acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.w[cb], o.a[rb], acc[rb][cb], 0, 0, 0);
+  };
 
   const int nchunks = (K + kKC - 1) / kKC;
-  const LoadLane L = load_lane(lane);
-  issue(lds, wave, L, A, W, m0, n0, M, N, K, 0);
-  const int swz = (m >> 1) & 7;  // ((row >> 1) & 7) of every row this lane reads
+#pragma unroll
+  for (int s = 0; s < kStages; ++s)
+    if (s < nchunks) issue(s, s * kKC);
+  if (nchunks >= kStages) wait_vm<(kStages - 1) * kLoadsPerWave>();
+  else wait_vm<0>();
+  __builtin_amdgcn_s_barrier();
+  Operands o0, o1;
+  read_ops(o0, 0, 0);
+  read_sq(0);
+
   for (int c = 0; c < nchunks; ++c) {
-    // This wave's loads of chunk c have landed and its reads of chunk c-1 have
-    // returned; after the barrier the same holds for all waves, so chunk c is
-    // complete and the other stage may be refilled.
-    wait_vm(0);
+    const int st = c % kStages;
+    // k-steps 0 .. kSteps-2 of this chunk, each reading the next step's operands
+#pragma unroll
+    for (int t = 0; t + 1 < kSteps; t += 2) {
+      read_ops(o1, st, t + 1);
+      mfma(o0);
+      if (t == 0) add_sq();
+      if (t + 2 < kSteps) {
+        read_ops(o0, st, t + 2);
+        mfma(o1);
+      }
+    }
+    // Chunk c+1 has landed (this wave's loads, then the barrier for all
+    // waves) and every read of chunk c has returned, so its stage may be
+    // refilled with chunk c + kStages.
+    if (c + kStages - 1 < nchunks) wait_vm<(kStages - 2) * kLoadsPerWave>();
+    else wait_vm<0>();
     wait_lgkm0();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (c + 1 < nchunks)
-      issue(lds + ((c + 1) & 1) * kStageBytes, wave, L, A, W, m0, n0, M, N, K, (c + 1) * kKC);
-    const char *sa = lds + (c & 1) * kStageBytes;
-    const char *sw = sa + kTileBytes;
-#pragma unroll
-    for (int t = 0; t < kKC / 32; ++t) {
-      const int slot = ((4 * t + g) ^ swz) * 16;
-      bf16x8 aop[8], wop[8];
-#pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        aop[b] = *reinterpret_cast<const bf16x8 *>(sa + (wm * 128 + b * 16 + m) * kRowBytes + slot);
-        wop[b] = *reinterpret_cast<const bf16x8 *>(sw + (wn * 128 + b * 16 + m) * kRowBytes + slot);
-      }
-#pragma unroll
-      for (int rb = 0; rb < 8; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wop[cb], aop[rb], acc[rb][cb], 0, 0, 0);
-    }
-    // Row sums of squares on the vector unit: thread t adds the squares of
-    // row t of this chunk (its 8 pieces, wherever the swizzle put them).
-    {
-      const int srow = (tid >> 1) & 7;
-#pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(sa + tid * kRowBytes + ((p ^ srow) * 16));
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float lo = bf16_lo(v[w]), hi = bf16_hi(v[w]);
-          sumsq = fmaf(lo, lo, sumsq);
-          sumsq = fmaf(hi, hi, sumsq);
-        }
-      }
-    }
+    if (c + kStages < nchunks) issue(st, (c + kStages) * kKC);
+    // last k-step; read step 0 of the next chunk (past the end: stale, unused)
+    const int sn = (c + 1) % kStages;
+    read_ops(o0, sn, 0);
+    read_sq(sn);
+    mfma(o1);
   }
 
-  // rstd of the tile's 256 rows.
-  {
-    const float r = 1.0f / sqrtf(sumsq * inv_k + eps);
-    rs_lds[tid] = r;
+  float ss = (ssp[0] + ssp[1]) + (ssp[2] + ssp[3]);
+  ss += __shfl_xor(ss, 1);
+  if (sh == 0) rs_lds[srow] = ss;
+  __syncthreads();
+  if (tid < kTile) {
+    const float r = 1.0f / sqrtf(rs_lds[tid] * inv_k + eps);
     if (tn == 0 && rstd_out != nullptr && m0 + tid < M) rstd_out[m0 + tid] = r;
+    rs_lds[tid] = r;  // each thread reads and rewrites only its own row
   }
   __syncthreads();
 
-  // Epilogue: block (rb, cb) of C^T: lane (m, g) holds C[row][4g .. 4g+3] of
-  // row = m0 + wm*128 + rb*16 + m, columns n0 + wn*128 + cb*16 + 4g ...
+  // Epilogue: block (rb, cb) of C^T: lane holds row j32 of A block rb and
+  // columns 8 q + 4 g .. +3 (q = 0..3) of W block cb.
+  const bool interior = (m0 + kTile <= M) && (n0 + kTile <= N);
 #pragma unroll
-  for (int rb = 0; rb < 8; ++rb) {
-    const int lr = wm * 128 + rb * 16 + m;
+  for (int rb = 0; rb < 4; ++rb) {
+    const int lr = wm * 128 + rb * 32 + j32;
     const int row = m0 + lr;
-    const float s = rs_lds[lr];
+    const float sc = rs_lds[lr];
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) {
-      const int col = n0 + wn * 128 + cb * 16 + 4 * g;
-      const f32x4 v = acc[rb][cb];
-      const u32x2 o = {pack_bf16x2(v[0] * s, v[1] * s), pack_bf16x2(v[2] * s, v[3] * s)};
-      if (row < M && col < N) *reinterpret_cast<u32x2 *>(Cout + (size_t)row * N + col) = o;
+    for (int cb = 0; cb < 2; ++cb) {
+      const f32x16 v = acc[rb][cb];
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int col = n0 + wn * 64 + cb * 32 + 8 * qq + 4 * g;
+        const u32x2 ov = {pack_bf16x2(v[4 * qq] * sc, v[4 * qq + 1] * sc),
+                          pack_bf16x2(v[4 * qq + 2] * sc, v[4 * qq + 3] * sc)};
+        if (interior || (row < M && col < N)) *reinterpret_cast<u32x2 *>(Cout + (size_t)row * N + col) = ov;
+      }
     }
   }
 }
@@ -211,9 +273,9 @@ __global__ __launch_bounds__(256, 1) void lazy_prenorm_gemm_kernel(
 
 hipError_t launch_lazy_prenorm_gemm(int64_t M, int64_t N, int64_t K, const void *A, const void *W,
                                     float eps, void *C, float *rstd, hipStream_t st) {
-  const int tiles_m = (int)((M + kTM - 1) / kTM), tiles_n = (int)((N + kTN - 1) / kTN);
+  const int tiles_m = (int)((M + kTile - 1) / kTile), tiles_n = (int)((N + kTile - 1) / kTile);
   const int64_t tiles = (int64_t)tiles_m * tiles_n;
-  lazy_prenorm_gemm_kernel<<<dim3((uint32_t)tiles), 256, 0, st>>>(
+  lazy_prenorm_gemm_kernel<<<dim3((uint32_t)tiles), kWaves * 64, 0, st>>>(
       static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(W), static_cast<uint16_t *>(C),
       rstd, (int)M, (int)N, (int)K, (float)(1.0 / (double)K), eps, tiles_m, tiles_n);
   return hipGetLastError();

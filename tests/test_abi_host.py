@@ -213,3 +213,4 @@ def test_lazy_prenorm_validation():
     assert call(c=Wp + 16) == mhc.MHC_ERR_INVALID_ARG
     assert call(r=Cp + 64) == mhc.MHC_ERR_INVALID_ARG                  # rstd inside C
     assert call(M=1 << 31) == mhc.MHC_ERR_UNSUPPORTED
+    assert call(K=(1 << 22) + 8) == mhc.MHC_ERR_UNSUPPORTED
