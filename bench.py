@@ -30,11 +30,17 @@ Also reported: the same pipeline on the E4M3 residual stream ("fp8", the
 the other workloads (tiny, decode, prefill, wide), both dtypes' per-layer and
 three-call times ("workloads"; decode also cold, after a 512 MB write).
 
+Also reported ("lazy_prenorm"): the Lazy Pre-Norm GEMM C = rmsnorm(A) W^T
+(mhc_lazy_prenorm_gemm) on its two synthetic workloads, with TFLOP/s
+(2 M N K per call; the sums of squares are not counted) against MI355X's
+dense bf16 MFMA peak.
+
 Other modes:
   --copy-probe   time a plain device-to-device copy of known size (the
                  reference against which rocprofv3 FETCH_SIZE / WRITE_SIZE are
                  scaled);
-  --kernel-only  run only the timed headline loop (for rocprofv3 runs).
+  --kernel-only  run only the timed headline loop (for rocprofv3 runs);
+  --lazy-prenorm-only  time only the Lazy Pre-Norm GEMM workloads.
 """
 
 import argparse
@@ -51,6 +57,7 @@ if ROOT not in sys.path:
 
 METRIC = "mHC fwd tokens/sec + achieved HBM GB/s (% of peak), n=4 C=7168 B=16384"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 DEFAULT_WORKLOAD = "large"
 
 
@@ -208,6 +215,7 @@ CALL_SOURCES = {
     "mhc_post_res_coeffs": ("mhc_post_res_fused.hip", "mhc_gemm_lds.hip", "mhc_coeff_sinkhorn.hip",
                             "mhc_coeffs_small.hip", "mhc_stream.hip", "mhc_finish.h",
                             "mhc_device.h"),
+    "mhc_lazy_prenorm_gemm": ("mhc_lazy_prenorm.hip", "mhc_device.h"),
 }
 
 
@@ -346,6 +354,41 @@ def _variants(args, mhc, torch, synth, stream, ev):
     return fp8_line, workloads
 
 
+def _lazy_prenorm(mhc, torch, synth, stream, ev, steps=20, warmup=5):
+    """mhc_lazy_prenorm_gemm on its synthetic workloads: mean time of
+    back-to-back calls (HIP events on the launch stream), TFLOP/s against the
+    dense bf16 MFMA peak, and the algorithmic bytes (A, W, C, rstd) for context."""
+    out = {}
+    for name, cfg in synth.LPN_CONFIGS.items():
+        M, N, K = cfg["M"], cfg["N"], cfg["K"]
+        d = synth.make_lpn_inputs(M, N, K, seed=cfg["seed"], device="cuda")
+        C = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        r = torch.empty(M, dtype=torch.float32, device="cuda")
+
+        def call():
+            mhc.mhc_lazy_prenorm_gemm(M, N, K, d["A"], d["W"], C, r, stream=stream)
+
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(steps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        tflops = 2.0 * M * N * K / (us * 1e-6) / 1e12
+        nbytes = 2 * (M * K + N * K + M * N) + 4 * M
+        out[name] = {"shape": f"M={M} N={N} K={K}", "us_per_call": round(us, 2),
+                     "tflops": round(tflops, 1), "bound": "mfma",
+                     "frac_of_bf16_peak": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "algorithmic_bytes": nbytes,
+                     "hbm_gbps_at_algorithmic_bytes": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        del d, C, r
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -359,6 +402,8 @@ def main():
     ap.add_argument("--kernel-only", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the E4M3 and other-workload sections (profiling runs of one workload)")
+    ap.add_argument("--lazy-prenorm-only", action="store_true",
+                    help="time only mhc_lazy_prenorm_gemm on its workloads (profiling runs)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -380,6 +425,11 @@ def main():
         return
 
     mhc.load()  # raises if the HIP library is not built
+    if args.lazy_prenorm_only:
+        lpn = _lazy_prenorm(mhc, torch, synth, torch.cuda.current_stream(),
+                            lambda: torch.cuda.Event(enable_timing=True), args.steps, args.warmup)
+        print(json.dumps({"lazy_prenorm": lpn}), flush=True)
+        return
     cfg = synth.CONFIGS[args.workload]
     inp = synth.make_config(args.workload, device="cuda")
     B, n, C = inp["B"], inp["n"], inp["C"]
@@ -486,9 +536,10 @@ def main():
     # ---- the E4M3 residual-stream variant on the same workload (same shapes
     # and draws, X and F_out rounded to E4M3)
     del X, Hs, out
-    fp8_line, workloads = None, None
+    fp8_line, workloads, lpn = None, None, None
     if not args.headline_only:
         fp8_line, workloads = _variants(args, mhc, torch, synth, stream, ev)
+        lpn = _lazy_prenorm(mhc, torch, synth, stream, ev)
 
     bytes_call = path_bytes(B, n, C)
     pipe_bytes = bytes_call["mhc_pre"] + bytes_call["mhc_post_res_coeffs"]
@@ -529,6 +580,7 @@ def main():
             fp8_line, note="E4M3 residual stream (X_t, F_out, F_pre, X_next), same workload; "
                            "the *_fp8 entry points"),
         "workloads": workloads,
+        "lazy_prenorm": lpn,
         "kernel_source_sha": {c: kernel_source_sha(c) for c in CALL_SOURCES},
     }
     print(json.dumps(line), flush=True)

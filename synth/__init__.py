@@ -133,6 +133,7 @@ def e4m3_codes(t):
 LPN_CONFIGS = {
     "lpn_proj": dict(M=16384, N=1536, K=7168, seed=2001),
     "lpn_square": dict(M=16384, N=7168, K=7168, seed=2002),
+    "lpn_ads": dict(M=262144, N=512, K=512, seed=2003),
 }
 
 
