@@ -30,6 +30,9 @@ Also reported: the same pipeline on the E4M3 residual stream ("fp8", the
 the other workloads (tiny, decode, prefill, wide), both dtypes' per-layer and
 three-call times ("workloads"; decode also cold, after a 512 MB write).
 
+Also reported ("phi32_coeffs"): mhc_coeffs_phi32 (fp32 phi) beside mhc_coeffs
+on the same X, decode and headline workloads, mean call time.
+
 Also reported ("lazy_prenorm"): the Lazy Pre-Norm GEMM C = rmsnorm(A) W^T
 (mhc_lazy_prenorm_gemm) on its two synthetic workloads, with TFLOP/s
 (2 M N K per call; the sums of squares are not counted) against MI355X's
@@ -216,6 +219,8 @@ CALL_SOURCES = {
                             "mhc_coeffs_small.hip", "mhc_stream.hip", "mhc_finish.h",
                             "mhc_device.h"),
     "mhc_lazy_prenorm_gemm": ("mhc_lazy_prenorm.hip", "mhc_device.h"),
+    "mhc_coeffs_phi32": ("mhc_gemm_lds.hip", "mhc_coeffs_small.hip", "mhc_coeff_sinkhorn.hip",
+                         "mhc_finish.h", "mhc_device.h"),
 }
 
 
@@ -352,6 +357,41 @@ def _variants(args, mhc, torch, synth, stream, ev):
         workloads[wname] = res
 
     return fp8_line, workloads
+
+
+def _phi32(mhc, torch, synth, stream, ev, names, steps=50, warmup=10):
+    """mhc_coeffs_phi32 (fp32 phi, hi + lo bf16 product) beside mhc_coeffs on
+    the same X: mean time of back-to-back calls, HIP events on the stream."""
+    out = {}
+    for name in names:
+        inp = synth.make_config_phi32(name, device="cuda")
+        B, n, C = inp["B"], inp["n"], inp["C"]
+        N = n * n + 2 * n
+        phi16 = inp["phi"].to(torch.bfloat16)
+        lg, r, H = (torch.empty(B, N, device="cuda"), torch.empty(B, device="cuda"),
+                    torch.empty(B, N, device="cuda"))
+        ws = torch.empty(max(mhc.mhc_coeffs_phi32_workspace_size(B, n, C),
+                             mhc.mhc_coeffs_workspace_size(B, n, C), 16), dtype=torch.uint8, device="cuda")
+        args = (inp["alpha_pre"], inp["alpha_post"], inp["alpha_res"], inp["b_pre"], inp["b_post"],
+                inp["b_res"], lg, r, H, ws)
+        res = {"shape": f"n={n} C={C} B={B}"}
+        for label, fn in (("phi32_us", lambda: mhc.mhc_coeffs_phi32(B, n, C, inp["X"], inp["phi"], *args,
+                                                                    stream=stream)),
+                          ("bf16_phi_us", lambda: mhc.mhc_coeffs(B, n, C, inp["X"], phi16, *args,
+                                                                 stream=stream))):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            for _ in range(steps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res[label] = round(e0.elapsed_time(e1) * 1e3 / steps, 2)
+        out[name] = res
+        del inp, phi16, lg, r, H, ws
+    return out
 
 
 def _lazy_prenorm(mhc, torch, synth, stream, ev, steps=20, warmup=5):
@@ -536,10 +576,11 @@ def main():
     # ---- the E4M3 residual-stream variant on the same workload (same shapes
     # and draws, X and F_out rounded to E4M3)
     del X, Hs, out
-    fp8_line, workloads, lpn = None, None, None
+    fp8_line, workloads, lpn, phi32 = None, None, None, None
     if not args.headline_only:
         fp8_line, workloads = _variants(args, mhc, torch, synth, stream, ev)
         lpn = _lazy_prenorm(mhc, torch, synth, stream, ev)
+        phi32 = _phi32(mhc, torch, synth, stream, ev, ("decode", args.workload))
 
     bytes_call = path_bytes(B, n, C)
     pipe_bytes = bytes_call["mhc_pre"] + bytes_call["mhc_post_res_coeffs"]
@@ -581,6 +622,7 @@ def main():
                            "the *_fp8 entry points"),
         "workloads": workloads,
         "lazy_prenorm": lpn,
+        "phi32_coeffs": phi32,
         "kernel_source_sha": {c: kernel_source_sha(c) for c in CALL_SOURCES},
     }
     print(json.dumps(line), flush=True)

@@ -232,6 +232,45 @@ int mhc_post_res_coeffs_fp8(int64_t B, int32_t n, int64_t C,
                             void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * fp32 phi variant.
+ *
+ * The tuned benchmark of [mHC-cutile] section 5 keeps X in bf16, phi (its W)
+ * in fp32 and every other input in fp32, and the product of section 5.1
+ * multiplies in TF32 when either operand is fp32.  These calls take phi as
+ * fp32 [n*C, N] row-major (16-byte aligned) and compute the product at
+ * higher precision than TF32: phi is split into phi_hi = bf16(phi) and
+ * phi_lo = bf16(phi - phi_hi), which together are within 2^-16 of phi
+ * (relative), and the product is X . phi_hi + X . phi_lo accumulated in fp32
+ * (bf16 X times either part is exact in fp32).  Everything else -- arguments,
+ * outputs, ownership, errors, determinism -- is as for mhc_coeffs and
+ * mhc_post_res_coeffs with a bf16 residual stream.  Workspace sizes come from
+ * the *_phi32_workspace_size functions.  The product runs in the one-launch
+ * small-B kernel up to 256 rows, otherwise in the split-K product staged
+ * through LDS; mhc_post_res_coeffs_phi32 is then the apply followed by that
+ * product on X_next (the fused kernel takes bf16 phi only).
+ * ------------------------------------------------------------------------ */
+
+size_t mhc_coeffs_phi32_workspace_size(int64_t B, int32_t n, int64_t C);
+
+int mhc_coeffs_phi32(int64_t B, int32_t n, int64_t C,
+                     const void *X_t, const float *phi,
+                     float alpha_pre, float alpha_post, float alpha_res,
+                     const float *b_pre, const float *b_post, const float *b_res,
+                     float *logits, float *r, float *H,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Requires C % 32 == 0, as mhc_post_res_coeffs. */
+size_t mhc_post_res_coeffs_phi32_workspace_size(int64_t B, int32_t n, int64_t C);
+
+int mhc_post_res_coeffs_phi32(int64_t B, int32_t n, int64_t C,
+                              const void *X_t, const void *F_out, const float *H, void *X_next,
+                              const float *phi_next,
+                              float alpha_pre, float alpha_post, float alpha_res,
+                              const float *b_pre, const float *b_post, const float *b_res,
+                              float *logits_next, float *r_next, float *H_next,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * Lazy Pre-Norm GEMM (a second workload on the same machinery).
  *
  * Section 2 of the page "Towards Free Normalization: Fusing Normalization

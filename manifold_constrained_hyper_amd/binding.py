@@ -24,7 +24,9 @@ EXPORTED = ("mhc_status_string", "mhc_coeffs_workspace_size", "mhc_coeffs_split_
             "mhc_coeffs", "mhc_pre", "mhc_post_res", "mhc_post_res_coeffs_workspace_size",
             "mhc_post_res_coeffs", "mhc_coeffs_fp8_workspace_size", "mhc_coeffs_fp8",
             "mhc_pre_fp8", "mhc_post_res_fp8", "mhc_post_res_coeffs_fp8_workspace_size",
-            "mhc_post_res_coeffs_fp8", "mhc_lazy_prenorm_gemm")
+            "mhc_post_res_coeffs_fp8", "mhc_coeffs_phi32_workspace_size", "mhc_coeffs_phi32",
+            "mhc_post_res_coeffs_phi32_workspace_size", "mhc_post_res_coeffs_phi32",
+            "mhc_lazy_prenorm_gemm")
 
 _lib = None
 
@@ -61,20 +63,25 @@ def load():
     lib.mhc_post_res_coeffs.argtypes = [i64, i32, i64, vp, vp, vp, vp, vp, f32, f32, f32,
                                         vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.mhc_post_res_coeffs.restype = ctypes.c_int
-    for suffix in ("", "_fp8"):
+    for suffix in ("", "_fp8", "_phi32"):
         if suffix:
             getattr(lib, "mhc_coeffs" + suffix).argtypes = lib.mhc_coeffs.argtypes
             getattr(lib, "mhc_coeffs" + suffix).restype = ctypes.c_int
-            getattr(lib, "mhc_pre" + suffix).argtypes = lib.mhc_pre.argtypes
-            getattr(lib, "mhc_pre" + suffix).restype = ctypes.c_int
-            getattr(lib, "mhc_post_res" + suffix).argtypes = lib.mhc_post_res.argtypes
-            getattr(lib, "mhc_post_res" + suffix).restype = ctypes.c_int
+            if suffix == "_fp8":
+                getattr(lib, "mhc_pre" + suffix).argtypes = lib.mhc_pre.argtypes
+                getattr(lib, "mhc_pre" + suffix).restype = ctypes.c_int
+                getattr(lib, "mhc_post_res" + suffix).argtypes = lib.mhc_post_res.argtypes
+                getattr(lib, "mhc_post_res" + suffix).restype = ctypes.c_int
             getattr(lib, "mhc_post_res_coeffs" + suffix).argtypes = lib.mhc_post_res_coeffs.argtypes
             getattr(lib, "mhc_post_res_coeffs" + suffix).restype = ctypes.c_int
     lib.mhc_coeffs_fp8_workspace_size.argtypes = [i64, i32, i64]
     lib.mhc_coeffs_fp8_workspace_size.restype = sz
     lib.mhc_post_res_coeffs_fp8_workspace_size.argtypes = [i64, i32, i64]
     lib.mhc_post_res_coeffs_fp8_workspace_size.restype = sz
+    lib.mhc_coeffs_phi32_workspace_size.argtypes = [i64, i32, i64]
+    lib.mhc_coeffs_phi32_workspace_size.restype = sz
+    lib.mhc_post_res_coeffs_phi32_workspace_size.argtypes = [i64, i32, i64]
+    lib.mhc_post_res_coeffs_phi32_workspace_size.restype = sz
     lib.mhc_lazy_prenorm_gemm.argtypes = [i64, i64, i64, vp, vp, f32, vp, vp, vp]
     lib.mhc_lazy_prenorm_gemm.restype = ctypes.c_int
     _lib = lib
@@ -226,6 +233,45 @@ def mhc_post_res_coeffs_fp8(B, n, C, X_t, F_out, H, X_next, phi_next, alpha_pre,
                                         _stream(stream))
     if check:
         _check(st, "mhc_post_res_coeffs_fp8")
+    return st
+
+
+def mhc_coeffs_phi32_workspace_size(B, n, C):
+    return int(load().mhc_coeffs_phi32_workspace_size(int(B), int(n), int(C)))
+
+
+def mhc_coeffs_phi32(B, n, C, X_t, phi, alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res,
+                     logits, r, H, workspace, workspace_bytes=None, stream=None, check=True):
+    """Steps (1)-(3) with an fp32 phi (see include/mhc.h)."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().mhc_coeffs_phi32(int(B), int(n), int(C), _ptr(X_t), _ptr(phi), float(alpha_pre),
+                                 float(alpha_post), float(alpha_res), _ptr(b_pre), _ptr(b_post),
+                                 _ptr(b_res), _ptr(logits), _ptr(r), _ptr(H), _ptr(workspace),
+                                 int(workspace_bytes), _stream(stream))
+    if check:
+        _check(st, "mhc_coeffs_phi32")
+    return st
+
+
+def mhc_post_res_coeffs_phi32_workspace_size(B, n, C):
+    return int(load().mhc_post_res_coeffs_phi32_workspace_size(int(B), int(n), int(C)))
+
+
+def mhc_post_res_coeffs_phi32(B, n, C, X_t, F_out, H, X_next, phi_next, alpha_pre, alpha_post,
+                              alpha_res, b_pre, b_post, b_res, logits_next, r_next, H_next,
+                              workspace, workspace_bytes=None, stream=None, check=True):
+    """mhc_post_res_coeffs with an fp32 phi_next (see include/mhc.h)."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().mhc_post_res_coeffs_phi32(int(B), int(n), int(C), _ptr(X_t), _ptr(F_out), _ptr(H),
+                                          _ptr(X_next), _ptr(phi_next), float(alpha_pre),
+                                          float(alpha_post), float(alpha_res), _ptr(b_pre),
+                                          _ptr(b_post), _ptr(b_res), _ptr(logits_next), _ptr(r_next),
+                                          _ptr(H_next), _ptr(workspace), int(workspace_bytes),
+                                          _stream(stream))
+    if check:
+        _check(st, "mhc_post_res_coeffs_phi32")
     return st
 
 

@@ -43,11 +43,14 @@ int64_t ncoef(int32_t n) { return (int64_t)n * n + 2 * (int64_t)n; }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? MHC_OK : MHC_ERR_HIP; }
 
-// The residual-stream element type of a call: bf16 (2 bytes) or E4M3 (1 byte,
-// the *_fp8 entry points, which need C % 16 == 0 for 16-byte vectors).
+// The element types of a call: the residual stream in bf16 (2 bytes) or E4M3
+// (1 byte, the *_fp8 entry points, which need C % 16 == 0 for 16-byte
+// vectors); phi in bf16 or fp32 (the *_phi32 entry points, bf16 stream).
 struct Elt {
   bool fp8;
+  bool phi32;
   size_t bytes() const { return fp8 ? 1 : 2; }
+  size_t phi_bytes() const { return phi32 ? 4 : 2; }
 };
 
 int check_shape_elt(int64_t B, int32_t n, int64_t C, Elt e) {
@@ -68,6 +71,7 @@ enum class CoeffsPath { kSmall, kSplitK, kPersistent };
 
 CoeffsPath coeffs_path(int64_t B, int32_t n, int64_t C, Elt e) {
   if (mhc::use_coeffs_small(B, n, C)) return CoeffsPath::kSmall;
+  if (e.phi32) return CoeffsPath::kSplitK;  // fp32 phi: small-B kernel or split-K through LDS
   bool persistent = false;
   if (const char *v = std::getenv("MHC_GEMM_ALGO"))
     if (std::strtol(v, nullptr, 10) == 2) persistent = true;
@@ -76,7 +80,7 @@ CoeffsPath coeffs_path(int64_t B, int32_t n, int64_t C, Elt e) {
 }
 
 mhc::GemmPlan split_plan(int64_t B, int32_t n, int64_t C, Elt e) {
-  return mhc::plan_gemm(B, n, C, e.fp8);
+  return mhc::plan_gemm(B, n, C, e.fp8, e.phi32);
 }
 
 size_t coeffs_ws_bytes(int64_t B, int32_t n, int64_t C, Elt e) {
@@ -104,7 +108,7 @@ int coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t, const v
   const CoeffsPath path = coeffs_path(B, n, C, e);
   const size_t ws_need = coeffs_ws_bytes(B, n, C, e);
   const int64_t N = ncoef(n), K = (int64_t)n * C;
-  const Span in[] = {span(X_t, (size_t)B * K * e.bytes()), span(phi, (size_t)K * N * 2),
+  const Span in[] = {span(X_t, (size_t)B * K * e.bytes()), span(phi, (size_t)K * N * e.phi_bytes()),
                      span(b_pre, (size_t)n * 4), span(b_post, (size_t)n * 4),
                      span(b_res, (size_t)n * n * 4)};
   const Span out[] = {span(logits, (size_t)B * N * 4), span(r, (size_t)B * 4),
@@ -122,7 +126,7 @@ int coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t, const v
   if (path == CoeffsPath::kSmall)
     return from_hip(mhc::launch_coeffs_small(mhc::plan_coeffs_small(B, n, C), n, e.fp8, B, C, X_t,
                                              phi, alpha_pre, alpha_post, alpha_res, b_pre, b_post,
-                                             b_res, logits, r, H, workspace, s));
+                                             b_res, logits, r, H, workspace, s, e.phi32));
   if (path == CoeffsPath::kPersistent) {
     const mhc::FusedPlan plan = mhc::plan_post_res_next(B, n, C);
     st = from_hip(mhc::launch_post_res_next(plan, n, e.fp8 ? mhc::kFusedCoeffsFp8 : mhc::kFusedCoeffsBf16,
@@ -187,6 +191,7 @@ enum class FusedRoute { kSmall, kTwoPass, kFused };
 
 FusedRoute fused_route(int64_t B, int32_t n, int64_t C, Elt e) {
   if (mhc::use_coeffs_small(B, n, C)) return FusedRoute::kSmall;
+  if (e.phi32) return FusedRoute::kTwoPass;  // the fused kernel takes bf16 phi only
   if (n == 8 && !std::getenv("MHC_FUSED_N8")) return FusedRoute::kTwoPass;
   if (e.fp8 && !std::getenv("MHC_FUSED_FP8")) return FusedRoute::kTwoPass;
   return FusedRoute::kFused;
@@ -224,7 +229,7 @@ int post_res_coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t
   const int64_t N = ncoef(n), K = (int64_t)n * C;
   const size_t eb = e.bytes();
   const Span in[] = {span(X_t, (size_t)B * K * eb), span(F_out, (size_t)B * C * eb),
-                     span(H, (size_t)B * N * 4), span(phi_next, (size_t)K * N * 2),
+                     span(H, (size_t)B * N * 4), span(phi_next, (size_t)K * N * e.phi_bytes()),
                      span(b_pre, (size_t)n * 4), span(b_post, (size_t)n * 4),
                      span(b_res, (size_t)n * n * 4)};
   const Span out[] = {span(X_next, (size_t)B * K * eb), span(logits_next, (size_t)B * N * 4),
@@ -247,7 +252,7 @@ int post_res_coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t
       return from_hip(mhc::launch_coeffs_small(mhc::plan_coeffs_small(B, n, C), n, e.fp8, B, C,
                                                X_next, phi_next, alpha_pre, alpha_post, alpha_res,
                                                b_pre, b_post, b_res, logits_next, r_next, H_next,
-                                               workspace, s));
+                                               workspace, s, e.phi32));
     const mhc::GemmPlan gp = split_plan(B, n, C, e);
     float *ws = static_cast<float *>(workspace);
     st = from_hip(mhc::launch_gemm_rms(gp, n, B, C, X_next, phi_next, ws, s));
@@ -264,7 +269,7 @@ int post_res_coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t
                                              logits_next, r_next, H_next, s));
 }
 
-constexpr Elt kBf16{false}, kFp8{true};
+constexpr Elt kBf16{false, false}, kFp8{true, false}, kPhi32{false, true};
 
 }  // namespace
 
@@ -361,6 +366,34 @@ int mhc_post_res_coeffs_fp8(int64_t B, int32_t n, int64_t C, const void *X_t, co
                             float *r_next, float *H_next, void *workspace, size_t workspace_bytes,
                             void *stream) {
   return post_res_coeffs_impl(kFp8, B, n, C, X_t, F_out, H, X_next, phi_next, alpha_pre,
+                              alpha_post, alpha_res, b_pre, b_post, b_res, logits_next, r_next,
+                              H_next, workspace, workspace_bytes, stream);
+}
+
+size_t mhc_coeffs_phi32_workspace_size(int64_t B, int32_t n, int64_t C) {
+  if (check_shape(B, n, C) != MHC_OK || B == 0) return 0;
+  return coeffs_ws_bytes(B, n, C, kPhi32);
+}
+
+int mhc_coeffs_phi32(int64_t B, int32_t n, int64_t C, const void *X_t, const float *phi,
+                     float alpha_pre, float alpha_post, float alpha_res, const float *b_pre,
+                     const float *b_post, const float *b_res, float *logits, float *r, float *H,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+  return coeffs_impl(kPhi32, B, n, C, X_t, phi, alpha_pre, alpha_post, alpha_res, b_pre, b_post,
+                     b_res, logits, r, H, workspace, workspace_bytes, stream);
+}
+
+size_t mhc_post_res_coeffs_phi32_workspace_size(int64_t B, int32_t n, int64_t C) {
+  return post_res_coeffs_ws_bytes(B, n, C, kPhi32);
+}
+
+int mhc_post_res_coeffs_phi32(int64_t B, int32_t n, int64_t C, const void *X_t, const void *F_out,
+                              const float *H, void *X_next, const float *phi_next, float alpha_pre,
+                              float alpha_post, float alpha_res, const float *b_pre,
+                              const float *b_post, const float *b_res, float *logits_next,
+                              float *r_next, float *H_next, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+  return post_res_coeffs_impl(kPhi32, B, n, C, X_t, F_out, H, X_next, phi_next, alpha_pre,
                               alpha_post, alpha_res, b_pre, b_post, b_res, logits_next, r_next,
                               H_next, workspace, workspace_bytes, stream);
 }

@@ -31,6 +31,10 @@
 //            see them, both write the same bits.  No counter, no atomic
 //            read-modify-write, no fence that writes back the L2.
 //
+// fp32 phi (the *_phi32 calls): the slice is split while it is staged into
+// two bf16 arrays, phi_hi = bf16(phi) and phi_lo = bf16(phi - phi_hi), and
+// every block takes two MFMAs, X.phi_hi + X.phi_lo, into one accumulator.
+//
 // The epoch is a process-wide 64-bit counter from a start that differs
 // between runs, so flags left in a workspace by earlier calls (or any other
 // contents) never match the current call: the workspace needs no
@@ -62,15 +66,15 @@ struct SmallTile {
   static_assert(KS % 128 == 0, "slice splits evenly over 4 waves");
 };
 
-template <int NS, bool FP8X>
+template <int NS, bool FP8X, bool P32>
 __global__ __launch_bounds__(256) void coeffs_small_kernel(
-    const uint8_t *__restrict__ X, const uint16_t *__restrict__ phi, int B, int K, int S,
+    const uint8_t *__restrict__ X, const void *__restrict__ phi_v, int B, int K, int S,
     float inv_k, float alpha_pre, float alpha_post, float alpha_res,
     const float *__restrict__ b_pre, const float *__restrict__ b_post,
     const float *__restrict__ b_res, float *__restrict__ logits, float *__restrict__ r_out,
     float *__restrict__ H, float *ws, unsigned long long *flags, unsigned long long epoch) {
   using T = SmallTile<NS>;
-  __shared__ __attribute__((aligned(16))) uint16_t phs[T::KS * T::N];
+  __shared__ __attribute__((aligned(16))) uint16_t phs[P32 ? 2 : 1][T::KS * T::N];
   __shared__ float red[4 * 16 * T::RS];
   __shared__ float sums[16 * T::NP];
   __shared__ int is_last;
@@ -105,10 +109,10 @@ __global__ __launch_bounds__(256) void coeffs_small_kernel(
   // phi rows [k_lo, k_hi) into LDS, zero past k_hi.  (k_hi - k_lo) is a
   // multiple of 8, so the valid bytes are a whole number of 16-byte pieces.
   // All of a thread's loads are issued before the first LDS store.
-  {
+  if constexpr (!P32) {
     const int valid = (k_hi - k_lo) * T::N * 2;
-    const char *src = reinterpret_cast<const char *>(phi + (size_t)k_lo * T::N);
-    char *dst = reinterpret_cast<char *>(phs);
+    const char *src = reinterpret_cast<const char *>(static_cast<const uint16_t *>(phi_v) + (size_t)k_lo * T::N);
+    char *dst = reinterpret_cast<char *>(phs[0]);
     u32x4 v[T::PPT];
 #pragma unroll
     for (int q = 0; q < T::PPT; ++q) {
@@ -119,6 +123,37 @@ __global__ __launch_bounds__(256) void coeffs_small_kernel(
     for (int q = 0; q < T::PPT; ++q) {
       const int p = tid + 256 * q;
       if (p < T::PIECES) *reinterpret_cast<u32x4 *>(dst + p * 16) = p * 16 < valid ? v[q] : u32x4{0u, 0u, 0u, 0u};
+    }
+  } else {
+    // fp32 phi: 16-byte pieces of 4 values, split into hi and lo halves of 8
+    // bytes each; loads issued in batches of 8 pieces per thread.
+    constexpr int PIECES32 = T::KS * T::N / 4;
+    constexpr int PPT32 = (PIECES32 + 255) / 256;
+    constexpr int BATCH = 8;
+    const int valid = (k_hi - k_lo) * T::N * 4;
+    const char *src = reinterpret_cast<const char *>(static_cast<const float *>(phi_v) + (size_t)k_lo * T::N);
+#pragma unroll
+    for (int q0 = 0; q0 < PPT32; q0 += BATCH) {
+      u32x4 v[BATCH];
+#pragma unroll
+      for (int q = 0; q < BATCH; ++q) {
+        const int p = tid + 256 * (q0 + q);
+        if (q0 + q < PPT32) v[q] = load16(src + (size_t)min(p * 16, valid - 16));
+      }
+#pragma unroll
+      for (int q = 0; q < BATCH; ++q) {
+        const int p = tid + 256 * (q0 + q);
+        if (q0 + q < PPT32 && p < PIECES32) {
+          const u32x4 w = p * 16 < valid ? v[q] : u32x4{0u, 0u, 0u, 0u};
+          const float f0 = __uint_as_float(w[0]), f1 = __uint_as_float(w[1]);
+          const float f2 = __uint_as_float(w[2]), f3 = __uint_as_float(w[3]);
+          const uint32_t h01 = pack_bf16x2(f0, f1), h23 = pack_bf16x2(f2, f3);
+          const uint32_t l01 = pack_bf16x2(f0 - bf16_lo(h01), f1 - bf16_hi(h01));  // exact differences
+          const uint32_t l23 = pack_bf16x2(f2 - bf16_lo(h23), f3 - bf16_hi(h23));
+          *reinterpret_cast<u32x2 *>(phs[0] + p * 4) = u32x2{h01, h23};
+          *reinterpret_cast<u32x2 *>(phs[1] + p * 4) = u32x2{l01, l23};
+        }
+      }
     }
   }
   __syncthreads();
@@ -132,15 +167,18 @@ __global__ __launch_bounds__(256) void coeffs_small_kernel(
 #pragma unroll
     for (int nb = 0; nb < T::NB; ++nb) {
       const int col = nb * 16 + m;
-      uint32_t w[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t lo = col < T::N ? phs[(kk + 2 * j) * T::N + col] : 0u;
-        const uint32_t hi = col < T::N ? phs[(kk + 2 * j + 1) * T::N + col] : 0u;
-        w[j] = lo | (hi << 16);
+      for (int part = 0; part < (P32 ? 2 : 1); ++part) {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t lo = col < T::N ? phs[part][(kk + 2 * j) * T::N + col] : 0u;
+          const uint32_t hi = col < T::N ? phs[part][(kk + 2 * j + 1) * T::N + col] : 0u;
+          w[j] = lo | (hi << 16);
+        }
+        const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q], b, acc[nb], 0, 0, 0);
       }
-      const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q], b, acc[nb], 0, 0, 0);
     }
     gram = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q], a[q], gram, 0, 0, 0);
   }
@@ -253,7 +291,7 @@ unsigned long long next_epoch() {
   return e;
 }
 
-template <int NS, bool FP8X>
+template <int NS, bool FP8X, bool P32>
 hipError_t launch_small_n(const SmallPlan &p, int64_t B, int64_t C, const void *X,
                           const void *phi, float ap, float aq, float ar, const float *bp,
                           const float *bq, const float *br, float *logits, float *r, float *H,
@@ -261,8 +299,8 @@ hipError_t launch_small_n(const SmallPlan &p, int64_t B, int64_t C, const void *
   char *base = static_cast<char *>(ws_base);
   const dim3 grid((uint32_t)p.row_tiles, (uint32_t)p.split);
   const float inv_k = (float)(1.0 / (double)(NS * C));
-  coeffs_small_kernel<NS, FP8X><<<grid, 256, 0, st>>>(
-      static_cast<const uint8_t *>(X), static_cast<const uint16_t *>(phi), (int)B,
+  coeffs_small_kernel<NS, FP8X, P32><<<grid, 256, 0, st>>>(
+      static_cast<const uint8_t *>(X), phi, (int)B,
       (int)(NS * C), p.split, inv_k, ap, aq, ar, bp, bq, br, logits, r, H,
       reinterpret_cast<float *>(base), reinterpret_cast<unsigned long long *>(base + p.ctr_offset),
       next_epoch());
@@ -299,16 +337,16 @@ bool use_coeffs_small(int64_t B, int n, int64_t C) {
   return B <= max_b && plan_coeffs_small(B, n, C).split <= kSmallMaxSplit;
 }
 
-template <bool FP8X>
+template <bool FP8X, bool P32>
 hipError_t launch_small_x(const SmallPlan &p, int n, int64_t B, int64_t C, const void *X,
                           const void *phi, float ap, float aq, float ar, const float *bp,
                           const float *bq, const float *br, float *logits, float *r, float *H,
                           void *ws, hipStream_t st) {
   switch (n) {
-    case 1: return launch_small_n<1, FP8X>(p, B, C, X, phi, ap, aq, ar, bp, bq, br, logits, r, H, ws, st);
-    case 2: return launch_small_n<2, FP8X>(p, B, C, X, phi, ap, aq, ar, bp, bq, br, logits, r, H, ws, st);
-    case 4: return launch_small_n<4, FP8X>(p, B, C, X, phi, ap, aq, ar, bp, bq, br, logits, r, H, ws, st);
-    case 8: return launch_small_n<8, FP8X>(p, B, C, X, phi, ap, aq, ar, bp, bq, br, logits, r, H, ws, st);
+    case 1: return launch_small_n<1, FP8X, P32>(p, B, C, X, phi, ap, aq, ar, bp, bq, br, logits, r, H, ws, st);
+    case 2: return launch_small_n<2, FP8X, P32>(p, B, C, X, phi, ap, aq, ar, bp, bq, br, logits, r, H, ws, st);
+    case 4: return launch_small_n<4, FP8X, P32>(p, B, C, X, phi, ap, aq, ar, bp, bq, br, logits, r, H, ws, st);
+    case 8: return launch_small_n<8, FP8X, P32>(p, B, C, X, phi, ap, aq, ar, bp, bq, br, logits, r, H, ws, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -316,9 +354,12 @@ hipError_t launch_small_x(const SmallPlan &p, int n, int64_t B, int64_t C, const
 hipError_t launch_coeffs_small(const SmallPlan &p, int n, bool fp8_x, int64_t B, int64_t C,
                                const void *X, const void *phi, float ap, float aq, float ar,
                                const float *bp, const float *bq, const float *br, float *logits,
-                               float *r, float *H, void *ws, hipStream_t st) {
-  return fp8_x ? launch_small_x<true>(p, n, B, C, X, phi, ap, aq, ar, bp, bq, br, logits, r, H, ws, st)
-               : launch_small_x<false>(p, n, B, C, X, phi, ap, aq, ar, bp, bq, br, logits, r, H, ws, st);
+                               float *r, float *H, void *ws, hipStream_t st, bool phi32) {
+  if (phi32)  // fp32 phi is offered with bf16 X only
+    return fp8_x ? hipErrorInvalidValue
+                 : launch_small_x<false, true>(p, n, B, C, X, phi, ap, aq, ar, bp, bq, br, logits, r, H, ws, st);
+  return fp8_x ? launch_small_x<true, false>(p, n, B, C, X, phi, ap, aq, ar, bp, bq, br, logits, r, H, ws, st)
+               : launch_small_x<false, false>(p, n, B, C, X, phi, ap, aq, ar, bp, bq, br, logits, r, H, ws, st);
 }
 
 }  // namespace mhc

@@ -24,6 +24,13 @@
 // past K are zero in the packed copy.  X pieces past K are read from a zeroed
 // 256-byte block of the workspace instead of past the end of the row.
 //
+// fp32 phi (the *_phi32 calls): pack_phi32_kernel splits each value into
+// phi_hi = bf16(phi) and phi_lo = bf16(phi - phi_hi) (together within 2^-16
+// of phi, relative) and writes, per 32-k step, the NB hi blocks followed by
+// the NB lo blocks; the product then runs two MFMAs per block,
+// X.phi_hi + X.phi_lo, into the same fp32 accumulator (bf16 X times either
+// part is exact in fp32).
+//
 // Pipeline per workgroup (4 waves, 64*MB rows): the loads of chunks
 // c+1 .. c+STAGES-1 are in flight while chunk c is multiplied.  Each wave
 // waits only for its own share of chunk c (s_waitcnt vmcnt), then one barrier
@@ -37,11 +44,12 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int NS, int MB, int KC, int STAGES, int XB>
+template <int NS, int MB, int KC, int STAGES, int XB, int P2 = 1>
 struct LdsTile {
   static constexpr int N = NS * NS + 2 * NS;
   static constexpr int NP = N + 1;
   static constexpr int NB = (N + 15) / 16;
+  static constexpr int PB = NB * P2;                 // packed phi blocks per 32-k step
   static constexpr int RT = 64 * MB;                 // rows per workgroup
   static constexpr int T = KC / 32;                  // MFMA k-steps per chunk
   static constexpr int EPP = 16 / XB;                // X elements per 16-byte piece
@@ -49,7 +57,7 @@ struct LdsTile {
   static constexpr int PIECES = KC / EPP;            // 16-byte pieces per row per chunk
   static constexpr int RPI = 64 / PIECES;            // rows per load instruction
   static constexpr int XI = RT * PIECES / 64;        // X load instructions per chunk
-  static constexpr int PI = T * NB;                  // phi load instructions per chunk
+  static constexpr int PI = T * PB;                  // phi load instructions per chunk
   static constexpr int XI_W = XI / 4, PI_W = PI / 4; // ... per wave
   static constexpr int VM_PER_CHUNK = XI_W + PI_W;
   static constexpr int X_BYTES = RT * ROW_BYTES;
@@ -70,13 +78,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int NS, int MB, int KC, int STAGES, int XB>
+template <int NS, int MB, int KC, int STAGES, int XB, int P2>
 __device__ __forceinline__ void issue_chunk(char *lds, int slot, int wave, int lane,
                                            const uint8_t *__restrict__ X,
                                            const uint16_t *__restrict__ phip,
                                            const uint16_t *__restrict__ zero, int row0, int B,
                                            int K, int k0) {
-  using L = LdsTile<NS, MB, KC, STAGES, XB>;
+  using L = LdsTile<NS, MB, KC, STAGES, XB, P2>;
   char *xs = lds + slot * L::STAGE_BYTES;
   char *ps = xs + L::X_BYTES;
   const int slot_in_row = lane % L::PIECES;
@@ -94,8 +102,8 @@ __device__ __forceinline__ void issue_chunk(char *lds, int slot, int wave, int l
   const int kstep0 = k0 / 32;
 #pragma unroll
   for (int j = 0; j < L::PI_W; ++j) {
-    const int inst = wave * L::PI_W + j;                       // = t * NB + nb
-    const uint16_t *src = phip + ((size_t)(kstep0 * L::NB + inst) * 64 + lane) * 8;
+    const int inst = wave * L::PI_W + j;                       // = t * PB + block
+    const uint16_t *src = phip + ((size_t)(kstep0 * L::PB + inst) * 64 + lane) * 8;
     __builtin_amdgcn_global_load_lds(src, (lds_void *)(ps + inst * 1024), 16, 0, 0);
   }
 }
@@ -105,9 +113,9 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
 }
 
 // Wait until at most `later` chunks' loads of this wave are outstanding.
-template <int NS, int MB, int KC, int STAGES, int XB>
+template <int NS, int MB, int KC, int STAGES, int XB, int P2>
 __device__ __forceinline__ void wait_chunks(int later) {
-  using L = LdsTile<NS, MB, KC, STAGES, XB>;
+  using L = LdsTile<NS, MB, KC, STAGES, XB, P2>;
   if (STAGES >= 4 && later >= 2) {
     wait_vmcnt<(STAGES >= 4 ? 2 : 0) * L::VM_PER_CHUNK>();
   } else if (later >= 1) {
@@ -117,13 +125,13 @@ __device__ __forceinline__ void wait_chunks(int later) {
   }
 }
 
-template <int NS, int MB, int KC, int STAGES, int XB>
+template <int NS, int MB, int KC, int STAGES, int XB, int P2>
 __global__ __launch_bounds__(256) void gemm_rms_lds_kernel(const uint8_t *__restrict__ X,
                                                            const uint16_t *__restrict__ phip,
                                                            const uint16_t *__restrict__ zero,
                                                            float *__restrict__ ws, int B, int K,
                                                            int kslice) {
-  using L = LdsTile<NS, MB, KC, STAGES, XB>;
+  using L = LdsTile<NS, MB, KC, STAGES, XB, P2>;
   __shared__ __attribute__((aligned(1024))) char lds[L::LDS_BYTES];
 
   const int tid = threadIdx.x;
@@ -147,7 +155,7 @@ __global__ __launch_bounds__(256) void gemm_rms_lds_kernel(const uint8_t *__rest
 #pragma unroll
   for (int c = 0; c < STAGES - 1; ++c)
     if (c < nchunks)
-      issue_chunk<NS, MB, KC, STAGES, XB>(lds, c, wave, lane, X, phip, zero, row0, B, K,
+      issue_chunk<NS, MB, KC, STAGES, XB, P2>(lds, c, wave, lane, X, phip, zero, row0, B, K,
                                       k_begin + c * KC);
 
   for (int c = 0; c < nchunks; ++c) {
@@ -156,23 +164,23 @@ __global__ __launch_bounds__(256) void gemm_rms_lds_kernel(const uint8_t *__rest
     // chunk c is complete and the slot of chunk c-1 may be refilled.  (A bare
     // s_barrier: a fenced __syncthreads would also wait for the loads still
     // in flight for the later chunks.)
-    wait_chunks<NS, MB, KC, STAGES, XB>(min(STAGES - 2, nchunks - 1 - c));
+    wait_chunks<NS, MB, KC, STAGES, XB, P2>(min(STAGES - 2, nchunks - 1 - c));
     wait_lgkmcnt0();
     asm volatile("" ::: "memory");  // no memory access moves across the barrier
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     const int cn = c + STAGES - 1;
     if (cn < nchunks)
-      issue_chunk<NS, MB, KC, STAGES, XB>(lds, cn % STAGES, wave, lane, X, phip, zero, row0, B, K,
+      issue_chunk<NS, MB, KC, STAGES, XB, P2>(lds, cn % STAGES, wave, lane, X, phip, zero, row0, B, K,
                                       k_begin + cn * KC);
     const char *xs = lds + (c % STAGES) * L::STAGE_BYTES;
     const char *ps = xs + L::X_BYTES;
 #pragma unroll
     for (int t = 0; t < L::T; ++t) {
-      bf16x8 b[L::NB];
+      bf16x8 b[L::PB];
 #pragma unroll
-      for (int nb = 0; nb < L::NB; ++nb)
-        b[nb] = *reinterpret_cast<const bf16x8 *>(ps + (t * L::NB + nb) * 1024 + lane * 16);
+      for (int j = 0; j < L::PB; ++j)
+        b[j] = *reinterpret_cast<const bf16x8 *>(ps + (t * L::PB + j) * 1024 + lane * 16);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const int rr = wave * 16 * MB + mb * 16 + m;
@@ -188,8 +196,11 @@ __global__ __launch_bounds__(256) void gemm_rms_lds_kernel(const uint8_t *__rest
           a = __builtin_bit_cast(bf16x8, fp8x8_to_bf16(v));
         }
 #pragma unroll
-        for (int nb = 0; nb < L::NB; ++nb)
+        for (int nb = 0; nb < L::NB; ++nb) {
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[nb], acc[mb][nb], 0, 0, 0);
+          if constexpr (P2 == 2)  // the low part of an fp32 phi
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[L::NB + nb], acc[mb][nb], 0, 0, 0);
+        }
         gram[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, a, gram[mb], 0, 0, 0);
       }
     }
@@ -266,21 +277,77 @@ __global__ __launch_bounds__(256) void pack_phi_kernel(const uint16_t *__restric
   }
 }
 
+// fp32 phi [K, N] -> packed hi and lo bf16 B operands: for 32-k step ks the
+// NB hi blocks (phi_hi = bf16(phi)), then the NB lo blocks (phi_lo =
+// bf16(phi - phi_hi)); block layout as in pack_phi_kernel.  Also clears the
+// zero block.
+template <int NS>
+__global__ __launch_bounds__(256) void pack_phi32_kernel(const float *__restrict__ phi,
+                                                         uint16_t *__restrict__ phip,
+                                                         uint16_t *__restrict__ zero, int K,
+                                                         int ksteps) {
+  constexpr int N = NS * NS + 2 * NS;
+  constexpr int NB = (N + 15) / 16;
+  constexpr int PIECES = 8 * N;                // 16-byte pieces per k-step (32 rows x 4N bytes)
+  constexpr int PPL = (PIECES + 63) / 64;
+  __shared__ __attribute__((aligned(16))) float buf[4][32 * N];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (blockIdx.x == 0 && threadIdx.x < 16) store16_plain(zero + threadIdx.x * 8, u32x4{0u, 0u, 0u, 0u});
+  const int ks_raw = blockIdx.x * 4 + wave;
+  const int ks = min(ks_raw, ksteps - 1);
+  const int64_t k0 = (int64_t)ks * 32;
+  const int64_t valid_bytes = (min((int64_t)K, k0 + 32) - k0) * (4 * N);  // a multiple of 16
+  const char *src = reinterpret_cast<const char *>(phi) + k0 * (4 * N);
+  char *dst = reinterpret_cast<char *>(buf[wave]);
+#pragma unroll
+  for (int q = 0; q < PPL; ++q) {
+    const int p = lane + 64 * q;
+    if (p < PIECES) {
+      const u32x4 v = (int64_t)p * 16 < valid_bytes ? load16(src + p * 16) : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4 *>(dst + p * 16) = v;
+    }
+  }
+  __syncthreads();
+  if (ks_raw >= ksteps) return;
+  const int kk = 8 * (lane >> 4);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = nb * 16 + (lane & 15);
+    uint32_t wh[4], wl[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float f0 = n < N ? buf[wave][(kk + 2 * q) * N + n] : 0.f;
+      const float f1 = n < N ? buf[wave][(kk + 2 * q + 1) * N + n] : 0.f;
+      wh[q] = pack_bf16x2(f0, f1);
+      wl[q] = pack_bf16x2(f0 - bf16_lo(wh[q]), f1 - bf16_hi(wh[q]));  // differences exact in fp32
+    }
+    store16_plain(phip + ((int64_t)(ks * 2 * NB + nb) * 64 + lane) * 8, u32x4{wh[0], wh[1], wh[2], wh[3]});
+    store16_plain(phip + ((int64_t)(ks * 2 * NB + NB + nb) * 64 + lane) * 8, u32x4{wl[0], wl[1], wl[2], wl[3]});
+  }
+}
+
 }  // namespace
 
-template <int NS, int MB, int KC, int STAGES, int XB>
+template <int NS, int MB, int KC, int STAGES, int XB, int P2>
 hipError_t launch_gemm_lds_typed(const GemmPlan &p, int64_t B, int64_t C, const void *X,
                                  const void *phi, void *ws_base, hipStream_t st) {
-  using L = LdsTile<NS, MB, KC, STAGES, XB>;
+  using L = LdsTile<NS, MB, KC, STAGES, XB, P2>;
   const int K = (int)(NS * C);
   char *base = static_cast<char *>(ws_base);
   uint16_t *phip = reinterpret_cast<uint16_t *>(base + p.phip_offset);
   uint16_t *zero = reinterpret_cast<uint16_t *>(base + p.zero_offset);
-  const int64_t ksteps = (int64_t)(p.phip_bytes / ((size_t)L::NB * 1024));
-  hipError_t e = launch_pack_phi(NS, K, ksteps, phi, phip, zero, st);
+  const int64_t ksteps = (int64_t)(p.phip_bytes / ((size_t)L::PB * 1024));
+  hipError_t e;
+  if constexpr (P2 == 2) {
+    pack_phi32_kernel<NS><<<dim3((uint32_t)((ksteps + 3) / 4)), 256, 0, st>>>(
+        static_cast<const float *>(phi), phip, zero, K, (int)ksteps);
+    e = hipGetLastError();
+  } else {
+    e = launch_pack_phi(NS, K, ksteps, phi, phip, zero, st);
+  }
   if (e != hipSuccess) return e;
   const dim3 grid((uint32_t)p.row_tiles, (uint32_t)p.split);
-  gemm_rms_lds_kernel<NS, MB, KC, STAGES, XB><<<grid, 256, 0, st>>>(
+  gemm_rms_lds_kernel<NS, MB, KC, STAGES, XB, P2><<<grid, 256, 0, st>>>(
       static_cast<const uint8_t *>(X), phip, zero, reinterpret_cast<float *>(base), (int)B, K,
       (int)p.kslice);
   return hipGetLastError();
@@ -302,16 +369,21 @@ hipError_t launch_pack_phi(int n, int64_t K, int64_t ksteps, const void *phi, vo
 }
 
 // Instantiations used by the library (see plan_gemm in mhc_gemm_rms.hip).
-template hipError_t launch_gemm_lds_typed<1, 1, 256, 3, 2>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
-template hipError_t launch_gemm_lds_typed<2, 1, 256, 3, 2>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
-template hipError_t launch_gemm_lds_typed<4, 1, 256, 3, 2>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
-template hipError_t launch_gemm_lds_typed<8, 1, 128, 4, 2>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
-template hipError_t launch_gemm_lds_typed<1, 1, 256, 4, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
-template hipError_t launch_gemm_lds_typed<2, 1, 256, 4, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
-template hipError_t launch_gemm_lds_typed<4, 1, 256, 4, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
-template hipError_t launch_gemm_lds_typed<8, 1, 256, 2, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
-template hipError_t launch_gemm_lds_typed<1, 2, 256, 3, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
-template hipError_t launch_gemm_lds_typed<2, 2, 256, 3, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
-template hipError_t launch_gemm_lds_typed<4, 2, 256, 3, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<1, 1, 256, 3, 2, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<2, 1, 256, 3, 2, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<4, 1, 256, 3, 2, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<8, 1, 128, 4, 2, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<1, 1, 256, 4, 1, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<2, 1, 256, 4, 1, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<4, 1, 256, 4, 1, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<8, 1, 256, 2, 1, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<1, 2, 256, 3, 1, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<2, 2, 256, 3, 1, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<4, 2, 256, 3, 1, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+// fp32 phi (hi + lo parts)
+template hipError_t launch_gemm_lds_typed<1, 1, 128, 4, 2, 2>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<2, 1, 128, 4, 2, 2>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<4, 1, 128, 4, 2, 2>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<8, 1, 128, 2, 2, 2>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
 
 }  // namespace mhc

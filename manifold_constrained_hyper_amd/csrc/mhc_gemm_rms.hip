@@ -246,14 +246,18 @@ constexpr int64_t kGemmTargetWGs = 512;
 template <int NS>
 hipError_t launch_n(const GemmPlan &p, int64_t B, int64_t C, const void *X, const void *phi,
                     float *ws, hipStream_t st) {
+  if (p.algo == 1 && p.phi_parts == 2) {
+    if constexpr (NS == 8) return launch_gemm_lds_typed<NS, 1, 128, 2, 2, 2>(p, B, C, X, phi, ws, st);
+    else return launch_gemm_lds_typed<NS, 1, 128, 4, 2, 2>(p, B, C, X, phi, ws, st);
+  }
   if (p.algo == 1 && p.xb == 1) {
-    if constexpr (NS == 8) return launch_gemm_lds_typed<NS, 1, 256, 2, 1>(p, B, C, X, phi, ws, st);
-    else if (p.mb == 2) return launch_gemm_lds_typed<NS, 2, 256, 3, 1>(p, B, C, X, phi, ws, st);
-    else return launch_gemm_lds_typed<NS, 1, 256, 4, 1>(p, B, C, X, phi, ws, st);
+    if constexpr (NS == 8) return launch_gemm_lds_typed<NS, 1, 256, 2, 1, 1>(p, B, C, X, phi, ws, st);
+    else if (p.mb == 2) return launch_gemm_lds_typed<NS, 2, 256, 3, 1, 1>(p, B, C, X, phi, ws, st);
+    else return launch_gemm_lds_typed<NS, 1, 256, 4, 1, 1>(p, B, C, X, phi, ws, st);
   }
   if (p.algo == 1) {
-    if constexpr (NS == 8) return launch_gemm_lds_typed<NS, 1, 128, 4, 2>(p, B, C, X, phi, ws, st);
-    else return launch_gemm_lds_typed<NS, 1, 256, 3, 2>(p, B, C, X, phi, ws, st);
+    if constexpr (NS == 8) return launch_gemm_lds_typed<NS, 1, 128, 4, 2, 1>(p, B, C, X, phi, ws, st);
+    else return launch_gemm_lds_typed<NS, 1, 256, 3, 2, 1>(p, B, C, X, phi, ws, st);
   }
   if (p.mb == 2) return launch_typed<NS, 2, kGemmKC, false, true>(p, B, C, X, phi, ws, st);
   return launch_typed<NS, 1, kGemmKC, false, true>(p, B, C, X, phi, ws, st);
@@ -269,6 +273,7 @@ GemmPlan plan_gemm_custom(int64_t B, int n, int64_t C, int algo, int mb, int kc,
   const int64_t NB = (N + 15) / 16;
   p.algo = algo;
   p.xb = 2;
+  p.phi_parts = 1;
   p.kc = kc;
   p.mb = mb;
   p.stages = stages;
@@ -297,7 +302,22 @@ GemmPlan plan_gemm_custom(int64_t B, int n, int64_t C, int algo, int mb, int kc,
   return p;
 }
 
-GemmPlan plan_gemm(int64_t B, int n, int64_t C, bool fp8_x) {
+GemmPlan plan_gemm(int64_t B, int n, int64_t C, bool fp8_x, bool phi32) {
+  // fp32 phi (bf16 X): X staged through LDS in 128-k chunks, so that the
+  // doubled (hi + lo) phi blocks fit the ring: four stages, two at n = 8.
+  if (phi32) {
+    int64_t target = 256;
+    if (const char *e = getenv("MHC_GEMM_WGS")) {
+      const long v = strtol(e, nullptr, 10);
+      if (v > 0) target = v;
+    }
+    GemmPlan p = plan_gemm_custom(B, n, C, 1, 1, 128, n == 8 ? 2 : 4, target);
+    p.phi_parts = 2;
+    p.phip_bytes *= 2;
+    p.zero_offset = p.phip_offset + p.phip_bytes;
+    p.total_bytes = p.zero_offset + 256;
+    return p;
+  }
   // X staged through LDS (algo 1), one 4-wave workgroup per CU at a time
   // (the LDS ring is ~144 KiB); enough workgroups to fill the 256 CUs, and no
   // more K-slices than that needs, since every slice adds (N+1)*4 bytes of

@@ -20,20 +20,21 @@ struct GemmPlan {
   int kc;             // K elements per chunk
   int stages;         // LDS ring depth (algo 1)
   int xb;             // bytes per X element: 2 (bf16) or 1 (E4M3, algo 1 only)
+  int phi_parts;      // 1: bf16 phi; 2: fp32 phi packed as hi + lo bf16 parts (algo 1 only)
   int split;          // S: number of K-slices (partials in the workspace)
   int64_t kslice;     // K elements per slice (multiple of kc)
   int64_t row_tiles;  // workgroups along B
   size_t partial_bytes, phip_offset, phip_bytes, zero_offset, total_bytes;
 };
 
-GemmPlan plan_gemm(int64_t B, int n, int64_t C, bool fp8_x = false);
+GemmPlan plan_gemm(int64_t B, int n, int64_t C, bool fp8_x = false, bool phi32 = false);
 // Plan with explicit kernel, rows-per-wave blocks, chunk size, ring depth and
 // target workgroup count.
 GemmPlan plan_gemm_custom(int64_t B, int n, int64_t C, int algo, int mb, int kc, int stages,
                           int64_t target_wgs);
 size_t gemm_workspace_bytes(const GemmPlan &p, int64_t B, int n);
 
-template <int NS, int MB, int KC, int STAGES, int XB>
+template <int NS, int MB, int KC, int STAGES, int XB, int P2>
 hipError_t launch_gemm_lds_typed(const GemmPlan &p, int64_t B, int64_t C, const void *X,
                                  const void *phi, void *ws_base, hipStream_t st);
 
@@ -100,7 +101,8 @@ hipError_t launch_coeffs_small(const SmallPlan &p, int n, bool fp8_x, int64_t B,
                                const void *X, const void *phi, float alpha_pre, float alpha_post,
                                float alpha_res, const float *b_pre, const float *b_post,
                                const float *b_res, float *logits, float *r, float *H, void *ws,
-                               hipStream_t st);
+                               hipStream_t st,
+                               bool phi32 = false);
 
 hipError_t launch_coeff_sinkhorn(int n, int64_t B, int64_t C, int split, const float *ws,
                                  float alpha_pre, float alpha_post, float alpha_res,

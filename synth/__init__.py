@@ -53,10 +53,11 @@ def _draw_rows(gen, rows, cols, dist, device):
     raise ValueError(f"unknown distribution {dist!r}")
 
 
-def make_inputs(n, C, B, x_dist="normal", seed=0, device="cpu", row_chunk=512):
+def make_inputs(n, C, B, x_dist="normal", seed=0, device="cpu", row_chunk=512, phi32=False):
     """Draw one seeded input set.  Returns a dict of torch tensors on `device`
     (X bf16 [B, nC], phi bf16 [nC, N], F_out bf16 [B, C], b_pre/b_post fp32 [n],
-    b_res fp32 [n*n]) plus the python floats alpha_pre/post/res and the sizes."""
+    b_res fp32 [n*n]) plus the python floats alpha_pre/post/res and the sizes.
+    phi32=True keeps phi in fp32 (the same draw, not rounded to bf16)."""
     device = torch.device(device)
     K = n * C
     N = n * n + 2 * n
@@ -66,7 +67,8 @@ def make_inputs(n, C, B, x_dist="normal", seed=0, device="cpu", row_chunk=512):
     for lo in range(0, B, row_chunk):
         hi = min(B, lo + row_chunk)
         X[lo:hi] = _draw_rows(gen, hi - lo, K, x_dist, device).to(torch.bfloat16)
-    phi = (torch.randn(K, N, generator=gen, device=device) / math.sqrt(K)).to(torch.bfloat16)
+    phi = torch.randn(K, N, generator=gen, device=device) / math.sqrt(K)
+    phi = phi.contiguous() if phi32 else phi.to(torch.bfloat16)
     b_pre = 0.1 * torch.randn(n, generator=gen, device=device)
     b_post = 0.1 * torch.randn(n, generator=gen, device=device)
     b_res = (2.0 * torch.eye(n, device=device).reshape(-1)
@@ -88,6 +90,13 @@ def make_config(name, device="cpu"):
     """Inputs for one named workload of CONFIGS."""
     cfg = CONFIGS[name]
     return make_inputs(cfg["n"], cfg["C"], cfg["B"], cfg["x_dist"], cfg["seed"], device)
+
+
+def make_config_phi32(name, device="cpu"):
+    """Inputs for one named workload of CONFIGS with phi kept in fp32 (the
+    bf16 config's phi is this phi rounded to bf16)."""
+    cfg = CONFIGS[name]
+    return make_inputs(cfg["n"], cfg["C"], cfg["B"], cfg["x_dist"], cfg["seed"], device, phi32=True)
 
 
 def bf16_bits(t):

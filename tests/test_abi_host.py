@@ -214,3 +214,46 @@ def test_lazy_prenorm_validation():
     assert call(r=Cp + 64) == mhc.MHC_ERR_INVALID_ARG                  # rstd inside C
     assert call(M=1 << 31) == mhc.MHC_ERR_UNSUPPORTED
     assert call(K=(1 << 22) + 8) == mhc.MHC_ERR_UNSUPPORTED
+
+
+def test_phi32_validation():
+    """The fp32-phi calls: the bf16 calls' rules, with phi 4 bytes per element
+    (its overlap span is K*N*4 bytes)."""
+    B, n, C = 16, 4, 64
+    K, N = n * C, n * n + 2 * n
+    names = ["X", "phi", "bp", "bq", "br", "logits", "r", "H", "ws"]
+    p = dict(zip(names, _addrs(len(names))))
+
+    def coeffs(ws_bytes=None, **over):
+        q = dict(p, **over)
+        wb = ws_bytes if ws_bytes is not None else max(mhc.mhc_coeffs_phi32_workspace_size(B, n, C), 16)
+        return mhc.mhc_coeffs_phi32(B, n, C, q["X"], q["phi"], 0.01, 0.01, 0.01, q["bp"], q["bq"],
+                                    q["br"], q["logits"], q["r"], q["H"], q["ws"], wb, stream=0,
+                                    check=False)
+
+    assert mhc.mhc_coeffs_phi32_workspace_size(B, n, C) > 0
+    assert mhc.mhc_coeffs_phi32_workspace_size(B, 3, C) == 0
+    assert mhc.mhc_coeffs_phi32(0, n, C, None, None, 0.01, 0.01, 0.01, None, None, None, None, None,
+                                None, None, 0, stream=0, check=False) == mhc.MHC_OK
+    assert coeffs(phi=None) == mhc.MHC_ERR_INVALID_ARG
+    assert coeffs(phi=p["phi"] + 8) == mhc.MHC_ERR_UNSUPPORTED
+    # logits placed after the bf16 size of phi but inside its fp32 size
+    assert coeffs(logits=p["phi"] + K * N * 2) == mhc.MHC_ERR_INVALID_ARG
+    need = mhc.mhc_coeffs_phi32_workspace_size(B, n, C)
+    assert coeffs(ws_bytes=need - 1) == mhc.MHC_ERR_WORKSPACE
+    fnames = ["X", "F", "H", "Y", "phi", "bp", "bq", "br", "logits", "r", "Hn", "ws"]
+    f = dict(zip(fnames, _addrs(len(fnames))))
+
+    def fused(Cc=C, ws_bytes=None, **over):
+        q = dict(f, **over)
+        wb = ws_bytes if ws_bytes is not None else max(mhc.mhc_post_res_coeffs_phi32_workspace_size(B, n, Cc), 16)
+        return mhc.mhc_post_res_coeffs_phi32(B, n, Cc, q["X"], q["F"], q["H"], q["Y"], q["phi"], 0.01,
+                                             0.01, 0.01, q["bp"], q["bq"], q["br"], q["logits"],
+                                             q["r"], q["Hn"], q["ws"], wb, stream=0, check=False)
+
+    assert fused(Cc=48) == mhc.MHC_ERR_UNSUPPORTED                     # C % 32
+    assert mhc.mhc_post_res_coeffs_phi32_workspace_size(B, n, 48) == 0
+    assert fused(Y=A) == mhc.MHC_ERR_INVALID_ARG
+    assert fused(logits=f["phi"] + K * N * 2) == mhc.MHC_ERR_INVALID_ARG
+    need = mhc.mhc_post_res_coeffs_phi32_workspace_size(B, n, C)
+    assert need > 0 and fused(ws_bytes=need - 1) == mhc.MHC_ERR_WORKSPACE
