@@ -3,27 +3,29 @@
     python bench.py [--steps K] [--warmup W] [--workload large]
 
 One step = one mHC layer over one batch of synthetic input already resident
-in HBM, run as a model runs it: `mhc_coeffs` once before the loop, then per
-layer `mhc_pre` (step 4a) and `mhc_post_res_coeffs` (step 4b of this layer
-fused with steps 1-3 of the next, so the residual stream is read twice per
-layer instead of three times).  The residual stream is chained through the
+in HBM, run as a model runs it: `mhc_coeffs` and `mhc_pre` once before the
+loop, then per layer one `mhc_post_res_coeffs_pre` (step 4b of this layer,
+then steps 1-3 and 4a of the next, in one pass: the residual stream is read
+once and written once per layer).  The residual stream is chained through the
 layers (X_{t+1} of one step is X_t of the next); every layer uses the same
-synthetic phi and biases, and the layer F between the two calls is not mHC
-(F_out is a fixed synthetic input).  The three separate calls
-(`mhc_coeffs`, `mhc_pre`, `mhc_post_res` on a fixed X_t) are timed as well
-and reported under "three_call".
+synthetic phi and biases, and the layer F between two calls is not mHC
+(F_out is a fixed synthetic input).  Also timed: the two-call pipeline
+(`mhc_pre` + `mhc_post_res_coeffs` per layer, "two_call_pipeline") and the
+three separate calls (`mhc_coeffs`, `mhc_pre`, `mhc_post_res` on a fixed
+X_t, "three_call").
 
 Prints ONE JSON line with tokens/s, achieved HBM bandwidth against the
 algorithmic byte count, per-call times, the roofline of the dominant call and
 the fp64 oracle's throughput on the host as a CPU baseline.
 
 Algorithmic bytes (bf16 X_t, F_out, F_pre, X_next; fp32 coefficients):
-  mhc_coeffs           X_t + phi + biases + logits + r + H
-  mhc_pre              X_t + H_pre + F_pre
-  mhc_post_res         2 X_t + F_out + (H_post, H_res)
-  mhc_post_res_coeffs  mhc_post_res + phi_next + biases + logits + r + H (next layer)
-Split-K partials and the packed copy of phi are implementation traffic and
-are not counted.
+  mhc_coeffs               X_t + phi + biases + logits + r + H
+  mhc_pre                  X_t + H_pre + F_pre
+  mhc_post_res             2 X_t + F_out + (H_post, H_res)
+  mhc_post_res_coeffs      mhc_post_res + phi_next + biases + logits + r + H (next layer)
+  mhc_post_res_coeffs_pre  mhc_post_res_coeffs + F_pre (next layer)
+Split-K partials, the hand-off records of the one-pass call and the packed
+copy of phi are implementation traffic and are not counted.
 
 Also reported: the same pipeline on the E4M3 residual stream ("fp8", the
 *_fp8 entry points, one byte per stream element in the byte count) and, for
@@ -92,6 +94,7 @@ def path_bytes(B, n, C, eb=2):
         "mhc_pre": x + B * n * 4 + B * C * eb,
         "mhc_post_res": post_res,
         "mhc_post_res_coeffs": post_res + K * N * 2 + coeff_out,
+        "mhc_post_res_coeffs_pre": post_res + K * N * 2 + coeff_out + B * C * eb,
     }
 
 
@@ -103,13 +106,17 @@ def path_flops(B, n, C):
 # kernels launched by each call (for the roofline record)
 KERNELS_OF_CALL = {"mhc_post_res": "post_res_kernel", "mhc_pre": "pre_kernel",
                    "mhc_coeffs": "pack_phi_kernel + gemm_rms_lds_kernel + coeff_sinkhorn_kernel",
-                   "mhc_post_res_coeffs": "pack_phi_kernel + post_res_next_kernel + coeff_sinkhorn_kernel"}
+                   "mhc_post_res_coeffs": "pack_phi_kernel + post_res_next_kernel + coeff_sinkhorn_kernel",
+                   "mhc_post_res_coeffs_pre": "pack_phi_kernel + post_res_next_kernel<n, 4> (pre-mix mode) "
+                                              "+ coeff_sinkhorn_kernel (tree order)"}
 
 
 class Pipeline:
-    """The per-layer pipeline (mhc_pre + mhc_post_res_coeffs, X chained through
-    the layers) and the three separate calls, for one input set, in bf16 or
-    E4M3 (fp8=True: the *_fp8 entry points)."""
+    """The per-layer pipelines for one input set (X chained through the
+    layers): `layer` = mhc_pre + mhc_post_res_coeffs, `onepass` =
+    mhc_post_res_coeffs_pre (bf16 only); and `three` = the three separate
+    calls on a fixed X_t; in bf16 or E4M3 (fp8=True: the *_fp8 entry
+    points)."""
 
     def __init__(self, mhc, torch, inp, fp8=False):
         self.torch, self.inp = torch, inp
@@ -123,6 +130,9 @@ class Pipeline:
         self.fused = getattr(mhc, "mhc_post_res_coeffs" + sfx)
         ws_c = getattr(mhc, "mhc_coeffs" + sfx + "_workspace_size")(B, n, C)
         ws_f = getattr(mhc, "mhc_post_res_coeffs" + sfx + "_workspace_size")(B, n, C)
+        if not fp8:
+            self.fused_pre = mhc.mhc_post_res_coeffs_pre
+            ws_f = max(ws_f, mhc.mhc_post_res_coeffs_pre_workspace_size(B, n, C))
         dev, st = "cuda", torch.uint8 if fp8 else torch.bfloat16
         self.X = [inp["X"], torch.empty_like(inp["X"])]
         self.H = [torch.empty(B, N, device=dev) for _ in range(2)]
@@ -150,6 +160,16 @@ class Pipeline:
                    *self.ab, self.logits, self.r, self.H[1 - a], self.ws_f, stream=s)
         if marks is not None:
             marks[2].record(s)
+        self.cur = 1 - a
+
+    def onepass(self, marks=None):
+        B, n, C, a, s = self.B, self.n, self.C, self.cur, self.stream
+        if marks is not None:
+            marks[0].record(s)
+        self.fused_pre(B, n, C, self.X[a], self.inp["F_out"], self.H[a], self.X[1 - a], self.inp["phi"],
+                       *self.ab, self.logits, self.r, self.H[1 - a], self.F_pre, self.ws_f, stream=s)
+        if marks is not None:
+            marks[1].record(s)
         self.cur = 1 - a
 
     def three(self, marks=None):
@@ -194,14 +214,21 @@ class Pipeline:
                 for i, c in enumerate(names)}
 
 
-def _summary(B, n, C, eb, ms_layer, ms_three, per_pipe=None, per_three=None):
+def _summary(B, n, C, eb, ms_layer, ms_three, per_pipe=None, per_three=None, ms_onepass=None):
     b = path_bytes(B, n, C, eb)
     pipe = b["mhc_pre"] + b["mhc_post_res_coeffs"]
     three = b["mhc_coeffs"] + b["mhc_pre"] + b["mhc_post_res"]
-    out = {"us_per_layer": round(ms_layer * 1e3, 2), "tokens_per_s": round(B / (ms_layer * 1e-3), 1),
-           "hbm_gbps": round(pipe / (ms_layer * 1e-3) / 1e9, 1), "algorithmic_bytes_per_layer": pipe,
-           "three_call_us": round(ms_three * 1e3, 2),
-           "three_call_hbm_gbps": round(three / (ms_three * 1e-3) / 1e9, 1)}
+    out = {}
+    if ms_onepass is not None:
+        one = b["mhc_post_res_coeffs_pre"]
+        out.update({"onepass_us_per_layer": round(ms_onepass * 1e3, 2),
+                    "onepass_tokens_per_s": round(B / (ms_onepass * 1e-3), 1),
+                    "onepass_hbm_gbps": round(one / (ms_onepass * 1e-3) / 1e9, 1),
+                    "onepass_algorithmic_bytes_per_layer": one})
+    out.update({"us_per_layer": round(ms_layer * 1e3, 2), "tokens_per_s": round(B / (ms_layer * 1e-3), 1),
+                "hbm_gbps": round(pipe / (ms_layer * 1e-3) / 1e9, 1), "algorithmic_bytes_per_layer": pipe,
+                "three_call_us": round(ms_three * 1e3, 2),
+                "three_call_hbm_gbps": round(three / (ms_three * 1e-3) / 1e9, 1)})
     if per_pipe:
         out["per_call_us"] = {c: round(v * 1e3, 2) for c, v in per_pipe.items()}
     if per_three:
@@ -218,6 +245,9 @@ CALL_SOURCES = {
     "mhc_post_res_coeffs": ("mhc_post_res_fused.hip", "mhc_gemm_lds.hip", "mhc_coeff_sinkhorn.hip",
                             "mhc_coeffs_small.hip", "mhc_stream.hip", "mhc_finish.h",
                             "mhc_device.h"),
+    "mhc_post_res_coeffs_pre": ("mhc_post_res_fused.hip", "mhc_gemm_lds.hip", "mhc_coeff_sinkhorn.hip",
+                                "mhc_coeffs_small.hip", "mhc_stream.hip", "mhc_finish.h",
+                                "mhc_device.h"),
     "mhc_lazy_prenorm_gemm": ("mhc_lazy_prenorm.hip", "mhc_device.h"),
     "mhc_coeffs_phi32": ("mhc_gemm_lds.hip", "mhc_coeffs_small.hip", "mhc_coeff_sinkhorn.hip",
                          "mhc_finish.h", "mhc_device.h"),
@@ -338,7 +368,11 @@ def _variants(args, mhc, torch, synth, stream, ev):
             winp = (synth.make_config_fp8 if fp8 else synth.make_config)(wname, device="cuda")
             pw = Pipeline(mhc, torch, winp, fp8=fp8)
             res[dname] = _summary(wcfg["B"], wcfg["n"], wcfg["C"], 1 if fp8 else 2,
-                                  pw.time_loop(pw.layer, wsteps, 10), pw.time_loop(pw.three, wsteps, 10))
+                                  pw.time_loop(pw.layer, wsteps, 10), pw.time_loop(pw.three, wsteps, 10),
+                                  ms_onepass=None if fp8 else pw.time_loop(pw.onepass, wsteps, 10))
+            if not fp8:
+                res[dname]["onepass_route"] = ("one pass" if mhc.mhc_post_res_coeffs_pre_one_pass(
+                    wcfg["B"], wcfg["n"], wcfg["C"]) else "mhc_post_res_coeffs + mhc_pre")
             if wname == "decode":
                 scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
                 cold = []
@@ -346,7 +380,7 @@ def _variants(args, mhc, torch, synth, stream, ev):
                     scratch.fill_(1)
                     e0, e1 = ev(), ev()
                     e0.record(stream)
-                    pw.layer()
+                    (pw.layer if fp8 else pw.onepass)()
                     e1.record(stream)
                     torch.cuda.synchronize()
                     cold.append(e0.elapsed_time(e1))
@@ -482,20 +516,32 @@ def main():
     if not args.no_cpu_baseline and not args.kernel_only:
         cpu = _cpu_baseline(inp, args.cpu_rows, args.cpu_budget_s)
 
-    # ---- headline: per-layer pipeline, residual stream chained through layers
+    # ---- headline: one call per layer, residual stream chained through layers
     X = [inp["X"], torch.empty_like(inp["X"])]
     Hs = [torch.empty(B, N, device="cuda") for _ in range(2)]
     logits = torch.empty(B, N, device="cuda")
     r = torch.empty(B, device="cuda")
     F_pre = torch.empty(B, C, dtype=torch.bfloat16, device="cuda")
     ws_c = torch.empty(max(mhc.mhc_coeffs_workspace_size(B, n, C), 16), dtype=torch.uint8, device="cuda")
-    ws_f = torch.empty(max(mhc.mhc_post_res_coeffs_workspace_size(B, n, C), 16), dtype=torch.uint8,
-                       device="cuda")
+    ws_f = torch.empty(max(mhc.mhc_post_res_coeffs_workspace_size(B, n, C),
+                           mhc.mhc_post_res_coeffs_pre_workspace_size(B, n, C), 16),
+                       dtype=torch.uint8, device="cuda")
     ab = (inp["alpha_pre"], inp["alpha_post"], inp["alpha_res"], inp["b_pre"], inp["b_post"], inp["b_res"])
     mhc.mhc_coeffs(B, n, C, X[0], inp["phi"], *ab, logits, r, Hs[0], ws_c, stream=stream)
+    mhc.mhc_pre(B, n, C, X[0], Hs[0], F_pre, stream=stream)
     cur = [0]
 
     def layer(marks=None):
+        a = cur[0]
+        if marks is not None:
+            marks[0].record(stream)
+        mhc.mhc_post_res_coeffs_pre(B, n, C, X[a], inp["F_out"], Hs[a], X[1 - a], inp["phi"], *ab,
+                                    logits, r, Hs[1 - a], F_pre, ws_f, stream=stream)
+        if marks is not None:
+            marks[1].record(stream)
+        cur[0] = 1 - a
+
+    def two_call_layer(marks=None):
         a = cur[0]
         if marks is not None:
             marks[0].record(stream)
@@ -508,35 +554,45 @@ def main():
             marks[2].record(stream)
         cur[0] = 1 - a
 
-    for _ in range(args.warmup):
-        layer()
-    torch.cuda.synchronize()
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        w0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps, time.perf_counter() - w0
+
+    def per_call(fn, names):
+        marks = [[ev() for _ in range(len(names) + 1)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for k in range(args.steps):
+            fn(marks[k])
+        torch.cuda.synchronize()
+        return {c: sum(marks[k][i].elapsed_time(marks[k][i + 1]) for k in range(args.steps)) / args.steps
+                for i, c in enumerate(names)}
+
     # Timed region 1 (the headline number): K back-to-back layers bracketed by
     # two events and a device synchronisation on both sides; no event sits
     # between calls (each recorded event idles the stream a few microseconds).
-    t0, t1 = ev(), ev()
-    wall0 = time.perf_counter()
-    t0.record(stream)
-    for _ in range(args.steps):
-        layer()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
+    ms_step, wall = timed(layer)
     if args.kernel_only:
         print(json.dumps({"kernel_only": True, "steps": args.steps}), flush=True)
         return
-    ms_step = t0.elapsed_time(t1) / args.steps
 
     # Timed region 2: the same layers with an event before and after each call
     # (per-call durations, on the stream the kernels run on).
-    marks = [[ev() for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for k in range(args.steps):
-        layer(marks[k])
-    torch.cuda.synchronize()
-    pipe_calls = ("mhc_pre", "mhc_post_res_coeffs")
-    per_call_ms = {c: sum(marks[k][i].elapsed_time(marks[k][i + 1]) for k in range(args.steps)) / args.steps
-                   for i, c in enumerate(pipe_calls)}
+    pipe_calls = ("mhc_post_res_coeffs_pre",)
+    per_call_ms = per_call(layer, pipe_calls)
+
+    # The two-call pipeline (mhc_pre + mhc_post_res_coeffs per layer).
+    mhc.mhc_pre(B, n, C, X[cur[0]], Hs[cur[0]], F_pre, stream=stream)
+    ms_two, _ = timed(two_call_layer)
+    per_two = per_call(two_call_layer, ("mhc_pre", "mhc_post_res_coeffs"))
 
     # Timed region 3: the three separate calls on a fixed X_t.
     out = mhc.alloc_outputs(B, n, C)
@@ -583,7 +639,8 @@ def main():
         phi32 = _phi32(mhc, torch, synth, stream, ev, ("decode", args.workload))
 
     bytes_call = path_bytes(B, n, C)
-    pipe_bytes = bytes_call["mhc_pre"] + bytes_call["mhc_post_res_coeffs"]
+    pipe_bytes = bytes_call["mhc_post_res_coeffs_pre"]
+    two_bytes = bytes_call["mhc_pre"] + bytes_call["mhc_post_res_coeffs"]
     three_bytes = sum(bytes_call[c] for c in three_calls)
     gbps = pipe_bytes / (ms_step * 1e-3) / 1e9
     tokens_per_s = B / (ms_step * 1e-3)
@@ -603,12 +660,17 @@ def main():
         "data": "synthetic (seeded; X Student-t(4) for the large workload)",
         "config": {"workload": f"{args.workload}: n={n} C={C} B={B}", "n": n, "C": C, "B": B,
                    "x_dist": cfg["x_dist"], "seed": cfg["seed"],
-                   "path": "per layer: mhc_pre + mhc_post_res_coeffs (mhc_coeffs once before the loop)"},
+                   "path": "per layer: mhc_post_res_coeffs_pre (mhc_coeffs and mhc_pre once before the loop)",
+                   "one_pass": mhc.mhc_post_res_coeffs_pre_one_pass(B, n, C)},
         "hbm_gbps": round(gbps, 1), "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": pipe_bytes,
         "three_call_equivalent_gbps": round(three_bytes / (ms_step * 1e-3) / 1e9, 1),
         "per_call_us": {c: round(v * 1e3, 2) for c, v in per_call_ms.items()},
         "per_call_gbps": {c: round(bytes_call[c] / (per_call_ms[c] * 1e-3) / 1e9, 1) for c in pipe_calls},
+        "two_call_pipeline": {"ms_per_step": round(ms_two, 5), "tokens_per_s": round(B / (ms_two * 1e-3), 1),
+                              "hbm_gbps": round(two_bytes / (ms_two * 1e-3) / 1e9, 1),
+                              "algorithmic_bytes_per_step": two_bytes,
+                              "per_call_us": {c: round(v * 1e3, 2) for c, v in per_two.items()}},
         "three_call": {"ms_per_step": round(ms_three, 5), "tokens_per_s": round(B / (ms_three * 1e-3), 1),
                        "hbm_gbps": round(three_bytes / (ms_three * 1e-3) / 1e9, 1),
                        "algorithmic_bytes_per_step": three_bytes,

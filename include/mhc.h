@@ -172,6 +172,50 @@ int mhc_post_res_coeffs(int64_t B, int32_t n, int64_t C,
                         float *logits_next, float *r_next, float *H_next,
                         void *workspace, size_t workspace_bytes, void *stream);
 
+/* The whole per-layer mHC forward after the layer F, in one pass: step (4b)
+ * of this layer, then steps (1)-(3) and step (4a) of the next.
+ *
+ * [mHC-cutile] section 2.5 (first step) forms the next layer's input
+ * F_pre = sum_i H_pre[i] X_next[i] once the next layer's H_pre is known
+ * (sections 2.1-2.4).  This call returns everything mhc_post_res_coeffs
+ * returns and, in addition,
+ *
+ *   F_pre_next   out bf16 [B, C] = exactly what mhc_pre(X_next, H_next) writes
+ *                (bitwise).
+ *
+ * A model runs mhc_coeffs and mhc_pre once for its first layer and then, per
+ * layer, its layer F and this call: the residual stream is read once and
+ * written once per layer (X_t and F_out in, X_next and F_pre_next out).
+ *
+ * Where the shape allows (n <= 4, B above 256, C % 32 == 0 and at most
+ * 2*floor(64/(n+1)) 512-channel steps per row, i.e. C <= 12288 at n = 4)
+ * this runs as one persistent pass whose workgroups exchange each row's
+ * partial sums through the workspace; mhc_post_res_coeffs_pre_one_pass()
+ * reports whether a shape takes that route.  That pass needs its whole grid
+ * (one workgroup per compute unit) resident at once: it shares the device
+ * poorly with kernels running concurrently on other streams, and if a wait
+ * for another workgroup cannot complete within about a second it gives up and
+ * writes NaN to the affected F_pre_next vectors.  Other shapes run
+ * mhc_post_res_coeffs followed by mhc_pre on X_next, with the same results.
+ *
+ * Arguments as mhc_post_res_coeffs, plus F_pre_next (16-byte aligned, must
+ * not overlap any other argument).  The workspace must hold
+ * mhc_post_res_coeffs_pre_workspace_size(B, n, C) bytes; its contents on
+ * entry do not matter. */
+size_t mhc_post_res_coeffs_pre_workspace_size(int64_t B, int32_t n, int64_t C);
+
+int mhc_post_res_coeffs_pre(int64_t B, int32_t n, int64_t C,
+                            const void *X_t, const void *F_out, const float *H, void *X_next,
+                            const void *phi_next,
+                            float alpha_pre, float alpha_post, float alpha_res,
+                            const float *b_pre, const float *b_post, const float *b_res,
+                            float *logits_next, float *r_next, float *H_next, void *F_pre_next,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* 1 if mhc_post_res_coeffs_pre runs this shape as one pass, 0 if it runs the
+ * two calls (or the shape is invalid). */
+int32_t mhc_post_res_coeffs_pre_one_pass(int64_t B, int32_t n, int64_t C);
+
 /* ------------------------------------------------------------------------
  * FP8 residual-stream variant.
  *

@@ -22,6 +22,10 @@
 //            group g adds slices g, g+G, g+2G, ... in order and the G group
 //            sums are then added in group order.  Sums go to LDS and the raw
 //            logits to global memory.
+//            With TREE (at most 16 slices) the slices are instead added as
+//            the balanced binary tree over 16 slots, zero past S
+//            (tree16_sum_serial), the order in which the pre-mix mode of the
+//            fused kernel sums the same partials for its H_pre.
 //   phase 2  finish_row (mhc_finish.h): lane i computes gate i of the pre
 //            and post blocks, then the Sinkhorn iteration on row i of the res
 //            matrix, with column sums by a DPP butterfly over the row's lanes.
@@ -35,7 +39,7 @@ namespace {
 
 constexpr int64_t kOneRowMaxB = 512;  // up to this many rows, one row per workgroup
 
-template <int NS, bool ONE_ROW>
+template <int NS, bool ONE_ROW, bool TREE = false>
 __global__ __launch_bounds__(256) void coeff_sinkhorn_kernel(
     const float *__restrict__ ws, int split, int B, float inv_k, float alpha_pre,
     float alpha_post, float alpha_res, const float *__restrict__ b_pre,
@@ -89,7 +93,18 @@ __global__ __launch_bounds__(256) void coeff_sinkhorn_kernel(
     float acc[EPT];
 #pragma unroll
     for (int q = 0; q < EPT; ++q) acc[q] = 0.f;
-    for (int s0 = 0; s0 < split; s0 += SB) {
+    if constexpr (TREE) {
+#pragma unroll
+      for (int q = 0; q < EPT; ++q) {
+        const int e = tid + q * 256;
+        float v[16];
+#pragma unroll
+        for (int sb = 0; sb < 16; ++sb)
+          v[sb] = (sb < split && e < nel) ? base[(size_t)min(sb, split - 1) * slice + min(e, nel - 1)] : 0.f;
+        acc[q] = tree16_sum_serial(v);
+      }
+    }
+    for (int s0 = 0; s0 < (TREE ? 0 : split); s0 += SB) {
       float v[SB][EPT];
 #pragma unroll
       for (int sb = 0; sb < SB; ++sb)
@@ -125,8 +140,14 @@ __global__ __launch_bounds__(256) void coeff_sinkhorn_kernel(
 template <int NS>
 void launch_n(int64_t B, int64_t C, int split, const float *ws, float ap, float aq, float ar,
               const float *bp, const float *bq, const float *br, float *logits, float *r,
-              float *H, hipStream_t st) {
+              float *H, hipStream_t st, bool tree) {
   const float inv_k = (float)(1.0 / (double)(NS * C));
+  if (tree) {
+    constexpr int R = 256 / NS;
+    coeff_sinkhorn_kernel<NS, false, true><<<dim3((uint32_t)((B + R - 1) / R)), 256, 0, st>>>(
+        ws, split, (int)B, inv_k, ap, aq, ar, bp, bq, br, logits, r, H);
+    return;
+  }
   // Small B: one row per workgroup, so that the slices are summed by many
   // lanes and many workgroups at once.
   if (B <= kOneRowMaxB) {
@@ -144,12 +165,13 @@ void launch_n(int64_t B, int64_t C, int split, const float *ws, float ap, float 
 hipError_t launch_coeff_sinkhorn(int n, int64_t B, int64_t C, int split, const float *ws,
                                  float alpha_pre, float alpha_post, float alpha_res,
                                  const float *b_pre, const float *b_post, const float *b_res,
-                                 float *logits, float *r, float *H, hipStream_t st) {
+                                 float *logits, float *r, float *H, hipStream_t st, bool tree) {
+  if (tree && (split > 16 || n == 8)) return hipErrorInvalidValue;
   switch (n) {
-    case 1: launch_n<1>(B, C, split, ws, alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res, logits, r, H, st); break;
-    case 2: launch_n<2>(B, C, split, ws, alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res, logits, r, H, st); break;
-    case 4: launch_n<4>(B, C, split, ws, alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res, logits, r, H, st); break;
-    case 8: launch_n<8>(B, C, split, ws, alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res, logits, r, H, st); break;
+    case 1: launch_n<1>(B, C, split, ws, alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res, logits, r, H, st, tree); break;
+    case 2: launch_n<2>(B, C, split, ws, alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res, logits, r, H, st, tree); break;
+    case 4: launch_n<4>(B, C, split, ws, alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res, logits, r, H, st, tree); break;
+    case 8: launch_n<8>(B, C, split, ws, alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res, logits, r, H, st, tree); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -34,12 +34,44 @@ __device__ __forceinline__ float dpp_add_half_mirror(float x) {
   return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
 }
 
+// Sum over each aligned group of 16 lanes as the balanced binary tree
+// ((x0+x1)+(x2+x3)) + ... in slot order; every lane of the group ends with
+// the same bits (each level adds two equal-shaped subtrees, and + commutes).
+__device__ __forceinline__ float dpp_add_mirror(float x) {  // lane l <- lane 15 - l in its row of 16
+  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float tree16_sum(float x) {
+  return dpp_add_mirror(dpp_add_half_mirror(dpp_add_xor2(dpp_add_xor1(x))));
+}
+
+// The same tree over 16 values held by one thread (slot order, zeros past the
+// last slice): bitwise tree16_sum of those values.
+__device__ __forceinline__ float tree16_sum_serial(const float (&x)[16]) {
+  float y[8], z[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = x[2 * i] + x[2 * i + 1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) z[i] = y[2 * i] + y[2 * i + 1];
+  return (z[0] + z[1]) + (z[2] + z[3]);
+}
+
 template <int NS>
 __device__ __forceinline__ float group_sum(float x) {
   if constexpr (NS >= 2) x = dpp_add_xor1(x);
   if constexpr (NS >= 4) x = dpp_add_xor2(x);
   if constexpr (NS >= 8) x = dpp_add_half_mirror(x);
   return x;
+}
+
+// r of a row from its sum of squares (section 2.2, no epsilon) and 1/r.
+__device__ __forceinline__ float row_rms(float sumsq, float inv_k) { return sqrtf(sumsq * inv_k); }
+__device__ __forceinline__ float recip_exact(float r) { return 1.0f / r; }
+
+// Gate i of the pre block (sections 2.3-2.4): sigmoid(alpha_pre * logit / r + b).
+// Every kernel that forms H_pre calls this, so equal sums give equal bits.
+__device__ __forceinline__ float pre_gate(float logit, float inv_r, float alpha_pre, float b) {
+  const float z = alpha_pre * logit * inv_r + b;
+  return 1.0f / (1.0f + __expf(-z));
 }
 
 // sm: the row's N+1 sums (N logits, then the sum of squares); lane i of the
@@ -52,13 +84,12 @@ __device__ __forceinline__ void finish_row(const float *sm, int row, int i, floa
                                            const float *__restrict__ b_res,
                                            float *__restrict__ r_out, float *__restrict__ H) {
   constexpr int N = NS * NS + 2 * NS;
-  const float r = sqrtf(sm[N] * inv_k);
-  const float inv_r = 1.0f / r;
+  const float r = row_rms(sm[N], inv_k);
+  const float inv_r = recip_exact(r);
   float *h = H + (size_t)row * N;
   if (i == 0) r_out[row] = r;
   {
-    const float zp = alpha_pre * sm[i] * inv_r + b_pre[i];
-    h[i] = 1.0f / (1.0f + __expf(-zp));
+    h[i] = pre_gate(sm[i], inv_r, alpha_pre, b_pre[i]);
     const float zq = alpha_post * sm[NS + i] * inv_r + b_post[i];
     h[NS + i] = 2.0f / (1.0f + __expf(-zq));
   }

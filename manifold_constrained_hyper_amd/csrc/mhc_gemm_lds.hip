@@ -234,10 +234,13 @@ template <int NS>
 __global__ __launch_bounds__(256) void pack_phi_kernel(const uint16_t *__restrict__ phi,
                                                        uint16_t *__restrict__ phip,
                                                        uint16_t *__restrict__ zero, int K,
-                                                       int ksteps) {
+                                                       int ksteps, u32x4 *__restrict__ clr,
+                                                       int64_t clr_vecs) {
   // One wave per 32-row k-step.  The step's rows of phi are one contiguous
   // block of 64*N bytes; the wave copies it to LDS with 16-byte loads, then
   // each lane gathers its 8 consecutive k of one column per 16-column block.
+  // The grid also zero-fills clr[0, clr_vecs) (16-byte vectors; none when
+  // clr_vecs is 0).
   constexpr int N = NS * NS + 2 * NS;
   constexpr int NB = (N + 15) / 16;
   constexpr int PIECES = 4 * N;                // 16-byte pieces per k-step (32 rows x 2N bytes)
@@ -245,6 +248,8 @@ __global__ __launch_bounds__(256) void pack_phi_kernel(const uint16_t *__restric
   __shared__ __attribute__((aligned(16))) uint16_t buf[4][32 * N];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (blockIdx.x == 0 && threadIdx.x < 16) store16_plain(zero + threadIdx.x * 8, u32x4{0u, 0u, 0u, 0u});
+  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < clr_vecs; v += (int64_t)gridDim.x * 256)
+    store16_plain(clr + v, u32x4{0u, 0u, 0u, 0u});
   const int ks_raw = blockIdx.x * 4 + wave;
   const int ks = min(ks_raw, ksteps - 1);      // surplus waves redo the last step and store nothing
   const int64_t k0 = (int64_t)ks * 32;
@@ -354,15 +359,17 @@ hipError_t launch_gemm_lds_typed(const GemmPlan &p, int64_t B, int64_t C, const 
 }
 
 hipError_t launch_pack_phi(int n, int64_t K, int64_t ksteps, const void *phi, void *phip,
-                           void *zero, hipStream_t st) {
+                           void *zero, hipStream_t st, void *clear, size_t clear_bytes) {
   const dim3 grid((uint32_t)((ksteps + 3) / 4));  // one wave per 32-row k-step
   const uint16_t *src = static_cast<const uint16_t *>(phi);
   uint16_t *dst = static_cast<uint16_t *>(phip), *z = static_cast<uint16_t *>(zero);
+  u32x4 *clr = static_cast<u32x4 *>(clear);
+  const int64_t cv = clear ? (int64_t)(clear_bytes / 16) : 0;
   switch (n) {
-    case 1: pack_phi_kernel<1><<<grid, 256, 0, st>>>(src, dst, z, (int)K, (int)ksteps); break;
-    case 2: pack_phi_kernel<2><<<grid, 256, 0, st>>>(src, dst, z, (int)K, (int)ksteps); break;
-    case 4: pack_phi_kernel<4><<<grid, 256, 0, st>>>(src, dst, z, (int)K, (int)ksteps); break;
-    case 8: pack_phi_kernel<8><<<grid, 256, 0, st>>>(src, dst, z, (int)K, (int)ksteps); break;
+    case 1: pack_phi_kernel<1><<<grid, 256, 0, st>>>(src, dst, z, (int)K, (int)ksteps, clr, cv); break;
+    case 2: pack_phi_kernel<2><<<grid, 256, 0, st>>>(src, dst, z, (int)K, (int)ksteps, clr, cv); break;
+    case 4: pack_phi_kernel<4><<<grid, 256, 0, st>>>(src, dst, z, (int)K, (int)ksteps, clr, cv); break;
+    case 8: pack_phi_kernel<8><<<grid, 256, 0, st>>>(src, dst, z, (int)K, (int)ksteps, clr, cv); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -42,32 +42,67 @@ hipError_t launch_gemm_rms(const GemmPlan &p, int n, int64_t B, int64_t C,
                            const void *X, const void *phi, float *ws, hipStream_t st);
 
 // phi [K, N] -> packed MFMA B operands ([ksteps][NB][64 lanes][8] bf16, zero
-// past K and past N) plus a 256-byte zero block.
+// past K and past N) plus a 256-byte zero block.  The same launch zero-fills
+// clear[0, clear_bytes) when clear is given (clear_bytes a multiple of 16).
 hipError_t launch_pack_phi(int n, int64_t K, int64_t ksteps, const void *phi, void *phip,
-                           void *zero, hipStream_t st);
+                           void *zero, hipStream_t st, void *clear = nullptr,
+                           size_t clear_bytes = 0);
 
 // Fused apply of this layer + coefficient product of the next (one pass).
 //
 // Workspace layout: [0, partial_bytes) fp32 partials [split, B, N+1];
 // [phip_offset, +phip_bytes) packed phi of the next layer; [zero_offset, +256).
+//
+// The pre-mix mode (pre = true in the plan) adds, after the zero block:
+// [rec_offset, +rec_bytes) hand-off records [B, split, PW] (4 bytes each,
+// PW = n+1 rounded up to even; zero-filled by the launch before the kernel
+// runs).
 struct FusedPlan {
   int split;          // channel slices (K-slices of n*cw)
   int cw;             // channels per slice (multiple of 512)
   int64_t row_tiles;  // 16-row tiles
   int64_t ksteps;     // packed phi 32-k steps
-  size_t partial_bytes, dummy_offset, dummy_bytes, phip_offset, phip_bytes, zero_offset, total_bytes;
+  bool pre;           // pre-mix mode layout
+  size_t partial_bytes, dummy_offset, dummy_bytes, phip_offset, phip_bytes, zero_offset;
+  size_t rec_offset, rec_bytes, total_bytes;
 };
-FusedPlan plan_post_res_next(int64_t B, int n, int64_t C);
+FusedPlan plan_post_res_next(int64_t B, int n, int64_t C, bool pre = false);
 // What the persistent kernel of mhc_post_res_fused.hip does per step.
 enum FusedMode : int {
-  kFusedApplyBf16 = 0,   // bf16 X_t, F_out -> bf16 X_next, plus X_next . phi_next
-  kFusedApplyFp8 = 1,    // E4M3 X_t, F_out -> E4M3 X_next, plus X_next . phi_next
-  kFusedCoeffsFp8 = 2,   // X . phi only, X in E4M3
-  kFusedCoeffsBf16 = 3,  // X . phi only, X in bf16
+  kFusedApplyBf16 = 0,     // bf16 X_t, F_out -> bf16 X_next, plus X_next . phi_next
+  kFusedApplyFp8 = 1,      // E4M3 X_t, F_out -> E4M3 X_next, plus X_next . phi_next
+  kFusedCoeffsFp8 = 2,     // X . phi only, X in E4M3
+  kFusedCoeffsBf16 = 3,    // X . phi only, X in bf16
+  kFusedApplyPreBf16 = 4,  // kFusedApplyBf16, plus the next layer's F_pre (n <= 4)
+};
+// Kernel-side arguments of the pre-mix mode.  Its stores of partials,
+// records and F_pre, and its record loads, go through buffer resources, so a
+// store without a target is given an offset past the buffer and dropped by
+// the hardware: no dummy area, no branch, no memory traffic.
+struct PreArgs {
+  uint16_t *F_pre;                // bf16 [B, C]
+  uint32_t *rec;                  // records [B, split, PW]: fp32 bits, 0 = not yet written
+  uint32_t rec_bytes;             // split * B * PW * 4 (< 2^31); PW = n+1 rounded up to even
+  uint32_t partial_bytes;         // split * B * (N+1) * 4 (< 2^31)
+  const float *b_pre;             // fp32 [n]
+  float alpha_pre, inv_k;         // alpha_pre; 1 / (n C)
+};
+// Whether the pre-mix mode can run this shape: n <= 4, at most 16
+// 512-channel steps per row (the record gather), a grid of whole row tiles
+// (a multiple of S workgroups) that fits the device, and partials and
+// records addressable by 32-bit buffer offsets.
+bool pre_mode_fits(int64_t B, int n, int64_t C);
+// pre_out: F_pre (bf16 [B, C]) and the next layer's b_pre / alpha_pre for the
+// pre-mix mode, else null.
+struct PreOut {
+  void *F_pre;
+  const float *b_pre;
+  float alpha_pre;
 };
 hipError_t launch_post_res_next(const FusedPlan &p, int n, int mode, int64_t B, int64_t C,
                                 const void *X, const void *F, const float *H, void *Y,
-                                const void *phi_next, void *ws_base, hipStream_t st);
+                                const void *phi_next, void *ws_base, hipStream_t st,
+                                const PreOut *pre_out = nullptr);
 
 // Lazy Pre-Norm GEMM C = rmsnorm(A) W^T (mhc_lazy_prenorm.hip).
 hipError_t launch_lazy_prenorm_gemm(int64_t M, int64_t N, int64_t K, const void *A, const void *W,
@@ -104,10 +139,13 @@ hipError_t launch_coeffs_small(const SmallPlan &p, int n, bool fp8_x, int64_t B,
                                hipStream_t st,
                                bool phi32 = false);
 
+// tree: add the split partials as the 16-slot balanced tree (split <= 16,
+// n <= 4), the order of the fused kernel's pre-mix mode.
 hipError_t launch_coeff_sinkhorn(int n, int64_t B, int64_t C, int split, const float *ws,
                                  float alpha_pre, float alpha_post, float alpha_res,
                                  const float *b_pre, const float *b_post, const float *b_res,
-                                 float *logits, float *r, float *H, hipStream_t st);
+                                 float *logits, float *r, float *H, hipStream_t st,
+                                 bool tree = false);
 
 hipError_t launch_pre(int n, int64_t B, int64_t C, const void *X, const float *H,
                       void *F_pre, hipStream_t st);

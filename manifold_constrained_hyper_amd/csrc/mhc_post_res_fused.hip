@@ -51,6 +51,7 @@
 // what the stand-alone apply writes, and the product consumes those rounded
 // values, exactly what a separate product pass would read back.
 #include "mhc_device.h"
+#include "mhc_finish.h"
 #include "mhc_launch.h"
 
 #include <atomic>
@@ -64,27 +65,53 @@ namespace {
 constexpr int kStepCh = 512;          // channels per step: 64 lanes x 8
 constexpr int kLdsMax = 160 * 1024;   // LDS of one CU
 
-template <int NS>
+// Pre-mix mode: a hand-off record is one fp32 value in 4 bytes.  The records
+// are zero-filled before every launch and a stored value is never the zero
+// word (+0.0 is stored as -0.0), so a record holds either zero (not yet
+// written) or its value, written by one single-copy-atomic store.
+constexpr uint32_t kRecNegZero = 0x80000000u;
+// Bound on the polls of one wait for records (each poll sleeps ~0.2 us and
+// reads memory): a wait that cannot end, e.g. when the grid is not fully
+// resident, gives up after well under a second and poisons its outputs.
+constexpr int kSpinLimit = 1 << 17;
+// Word 3 of a gfx9 buffer resource for raw (untyped) access, and the cache
+// policy bit SC1 of a buffer access (agent-scope coherence, as the compiler
+// gives agent-scope atomic loads and stores).
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kSc1 = 16;
+
+template <int NS, bool PRE = false>
 struct FusedTile {
   static constexpr int N = NS * NS + 2 * NS;
   static constexpr int NP = N + 1;
   static constexpr int NB = (N + 15) / 16;
   static constexpr int ROW_BYTES = NS * kStepCh * 2;   // one tile row in LDS
   static constexpr int TILE_BYTES = 16 * ROW_BYTES;    // 64 KiB at n=4, 128 KiB at n=8
+  static constexpr int NT = PRE ? 2 : 1;               // tiles (pre-mix: this step's and the one before)
   static constexpr int KSTEPS = 16 * NS;               // 32-channel MFMA steps per step
   static constexpr int KPW = KSTEPS / 16;              // ... per wave (= NS)
   static constexpr int KB = NS >= 8 ? 2 : (KPW < 4 ? KPW : 4);  // k-steps whose B operands are held at once
   static constexpr int NH = NS + NS * NS;              // H_post and H_res of one row
   static constexpr int HV = (NH + 63) / 64;            // dwords per lane that hold them
-  static constexpr int RS = NB * 16 + 1;               // reduction row stride; Gram sum at NB*16
+  // Reduction rows: the NB*16 product columns, then the Gram sum; the
+  // pre-mix mode puts the Gram sum in the last padding column (N < NB*16)
+  // so that the two tiles and the buffer fit 160 KiB at n = 4.
+  static constexpr int GRAM_COL = PRE ? NB * 16 - 1 : NB * 16;
+  static constexpr int RS = PRE ? NB * 16 : NB * 16 + 1;
   static constexpr int RED_BYTES = 16 * 16 * RS * 4;   // [16 waves][16 rows][RS] fp32
   // The reduction buffer sits beside the tile when both fit (then the flush
   // of step s-1 overlaps step s); otherwise it reuses the tile buffer.
-  static constexpr bool SEPARATE = TILE_BYTES + RED_BYTES <= kLdsMax;
-  static constexpr int LDS_BYTES = SEPARATE ? TILE_BYTES + RED_BYTES
+  static constexpr bool SEPARATE = NT * TILE_BYTES + RED_BYTES <= kLdsMax;
+  static constexpr int LDS_BYTES = SEPARATE ? NT * TILE_BYTES + RED_BYTES
                                             : (TILE_BYTES > RED_BYTES ? TILE_BYTES : RED_BYTES);
   static constexpr int OPT = (16 * NP + 1023) / 1024;  // flushed sums per thread
+  // Pre-mix hand-off: per (row, slice) the n pre logits and the sum of
+  // squares, padded to an even count PW of 4-byte records; one 8-byte load
+  // per lane reads a row's records for up to 16 slices (16 * PW <= 128).
+  static constexpr int PW = (NS + 2) & ~1;
+  static constexpr int RB = NS >= 4 ? 2 : 1;  // 16-lane column groups needed: n + 1 columns
   static_assert(LDS_BYTES <= kLdsMax, "LDS budget");
+  static_assert(!PRE || (SEPARATE && N < NB * 16), "pre-mix mode needs n <= 4");
 };
 
 struct Step {
@@ -95,7 +122,8 @@ struct Step {
 template <int MODE>
 struct FusedIO {
   static constexpr bool FP8 = MODE == kFusedApplyFp8 || MODE == kFusedCoeffsFp8;
-  static constexpr bool APPLY = MODE == kFusedApplyBf16 || MODE == kFusedApplyFp8;
+  static constexpr bool PRE = MODE == kFusedApplyPreBf16;
+  static constexpr bool APPLY = MODE == kFusedApplyBf16 || MODE == kFusedApplyFp8 || PRE;
   static constexpr int EB = FP8 ? 1 : 2;  // bytes per element
   using vec = typename std::conditional<FP8, u32x2, u32x4>::type;  // 8 elements per lane
 };
@@ -104,12 +132,12 @@ template <int NS, int MODE>
 __global__ __launch_bounds__(1024) void post_res_next_kernel(
     const uint8_t *__restrict__ X, const uint8_t *__restrict__ F, const float *__restrict__ H,
     uint8_t *__restrict__ Y, const uint16_t *__restrict__ phip, float *__restrict__ ws,
-    float *__restrict__ dummy, int B, int C, int spu, int S, int U) {
-  using T = FusedTile<NS>;
+    float *__restrict__ dummy, int B, int C, int spu, int S, int U, const PreArgs pa) {
   using IO = FusedIO<MODE>;
+  using T = FusedTile<NS, IO::PRE>;
   using vec = typename IO::vec;
   __shared__ __attribute__((aligned(1024))) char lds[T::LDS_BYTES];
-  float *red = reinterpret_cast<float *>(lds + (T::SEPARATE ? T::TILE_BYTES : 0));
+  float *red = reinterpret_cast<float *>(lds + (T::SEPARATE ? T::NT * T::TILE_BYTES : 0));
 
   const int tid = threadIdx.x;
   const int wave = uniform(tid >> 6);
@@ -123,16 +151,33 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
   if (pg >= U) return;
   const int nsteps = ((U - pg + G - 1) / G) * spu;
 
+  // The pre-mix mode has one step per unit and a grid of whole row tiles
+  // (G % S == 0), so a workgroup keeps one slice and its row tile advances
+  // by G/S tiles per step: no division per step.
+  [[maybe_unused]] const int pre_slot = uniform(pg % S), pre_tile0 = uniform(pg / S), pre_gs = uniform(G / S);
   auto step_at = [&](int t) {
-    const int j = t / spu, p = t - j * spu;
-    const int u = j * G + pg;
-    const int tile = u / S, s = u - tile * S;
-    const int cb = s * cw;
-    return Step{uniform(tile * 16), uniform(cb + p * kStepCh), uniform(min(C, cb + cw)), uniform(s)};
+    if constexpr (IO::PRE) {
+      const int cb = pre_slot * kStepCh;
+      return Step{uniform((t * pre_gs + pre_tile0) * 16), cb, uniform(min(C, cb + kStepCh)), pre_slot};
+    } else {
+      const int j = t / spu, p = t - j * spu;
+      const int u = j * G + pg;
+      const int tile = u / S, s = u - tile * S;
+      const int cb = s * cw;
+      return Step{uniform(tile * 16), uniform(cb + p * kStepCh), uniform(min(C, cb + cw)), uniform(s)};
+    }
   };
 
-  char *my_lds_row = lds + wave * T::ROW_BYTES;
+  // The tile of step t (the pre-mix mode alternates two).
+  auto tile_of = [&](int t) -> char * { return lds + (IO::PRE ? (t & 1) * T::TILE_BYTES : 0); };
   const int wslot = (lane ^ (wave & 15)) * 16;  // swizzled 16-byte slot of this lane
+  // Buffer resources of the pre-mix mode (gfx9 raw buffers: stride 0, the
+  // size in bytes as the record count; accesses past it are dropped).
+  [[maybe_unused]] __amdgpu_buffer_rsrc_t ws_rsrc, rec_rsrc;
+  if constexpr (IO::PRE) {
+    ws_rsrc = __builtin_amdgcn_make_buffer_rsrc(ws, (short)0, (int)pa.partial_bytes, kRsrcWord3);
+    rec_rsrc = __builtin_amdgcn_make_buffer_rsrc(pa.rec, (short)0, (int)pa.rec_bytes, kRsrcWord3);
+  }
 
   f32x4 acc[T::NB], gram;
   gram = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -161,21 +206,40 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
   };
 
   // Sum the 16 waves' accumulators of step `sp` (in wave order) into its
-  // unit's partials.  Threads without a target write the dummy area.
-  auto flush = [&](const Step &sp) {
+  // unit's partials.  Threads without a target write the dummy area; so
+  // does everything when `real` is false (the flush before the first step).
+  // The pre-mix mode also publishes the n pre logits and the sum of squares
+  // as tagged records: one 8-byte store each, value and tag together, which
+  // another workgroup can read without any ordering between stores.
+  auto flush = [&](const Step &sp, bool real) {
 #pragma unroll
     for (int q = 0; q < T::OPT; ++q) {
       const int e = tid + q * 1024;
       const int ec = min(e, 16 * T::NP - 1);
       const int r = ec / T::NP, col = ec - r * T::NP;
-      const int rcol = col < T::N ? col : T::NB * 16;
+      const int rcol = col < T::N ? col : T::GRAM_COL;
       float a = 0.f;
 #pragma unroll
       for (int w = 0; w < 16; ++w) a += red[(w * 16 + r) * T::RS + rcol];
       const int row = sp.row0 + r;
-      float *dst = (e < 16 * T::NP && row < B) ? ws + ((size_t)sp.slot * B + row) * T::NP + col
-                                               : dummy + e;
-      *dst = a;
+      const bool tgt = real && e < 16 * T::NP && row < B;
+      if constexpr (!IO::PRE) {
+        float *dst = tgt ? ws + ((size_t)sp.slot * B + row) * T::NP + col : dummy + e;
+        *dst = a;
+      } else {
+        // Buffer stores: a thread without a target stores past the buffer
+        // (dropped).  The record is one 8-byte store with the SC1 bit (the
+        // agent-scope coherence of the gfx950 memory model), value and tag
+        // together.
+        constexpr uint32_t kNone = 0x80000000u;
+        const uint32_t poff = tgt ? (uint32_t)((sp.slot * B + row) * T::NP + col) * 4u : kNone;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a), ws_rsrc, poff, 0, 0);
+        const bool rec = tgt && (col < NS || col == T::N);
+        const int rc = col < NS ? col : NS;
+        const uint32_t roff = rec ? (uint32_t)((row * S + sp.slot) * T::PW + rc) * 4u : kNone;
+        const uint32_t bits = __float_as_uint(a);
+        __builtin_amdgcn_raw_buffer_store_b32(bits == 0u ? kRecNegZero : bits, rec_rsrc, roff, 0, kSc1);
+      }
     }
   };
 
@@ -185,12 +249,127 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
     for (int nb = 0; nb < T::NB; ++nb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) rw[(4 * g + v) * T::RS + nb * 16 + m] = acc[nb][v];
-    if (g == (m >> 2)) rw[m * T::RS + T::NB * 16] = gram[m & 3];
+    // (In the pre-mix mode this lands on a padding column written just above
+    // by the same wave; the later write wins.)  The empty asm makes the lane
+    // index opaque, so the address is formed here rather than hoisted out of
+    // the step loop (where, in the pre-mix mode, it was spilled to scratch,
+    // and reloading it waited for every load in flight).
+    int mm = m;
+    if constexpr (IO::PRE) asm volatile("" : "+v"(mm));
+    if (g == (mm >> 2)) rw[mm * T::RS + T::GRAM_COL] = gram[mm & 3];
+  };
+
+  // ---- pre-mix mode: F_pre of the next layer, two steps behind the apply.
+  // Step q's X_{t+1} rows stay in their LDS tile until step q+2 (or the end)
+  // rewrites it.  By then every slice of q's row tile has (normally) been
+  // flushed by its workgroup, so the row's n pre logits and sum of squares
+  // can be summed in slice order 0..S-1 -- the order of the combine kernel,
+  // hence the same H_pre bits -- and F_pre[row, chunk] = sum_i H_pre[i]
+  // X_{t+1}[i, chunk] is formed from the tile exactly as pre_kernel forms it.
+  // b_pre of the gate lane 16i forms (lanes past the n columns: any valid one)
+  [[maybe_unused]] float bpre_lane = 0.f;
+  if constexpr (IO::PRE) bpre_lane = pa.b_pre[min(lane >> 4, NS - 1)];
+  // Records of step q's row for this wave ([B][S][PW] words: a row's records
+  // are contiguous): lane l reads words 2l, 2l+1, i.e. slice 2l / PW; lanes
+  // past the row read past the buffer (zeros, never checked).  Agent scope
+  // (SC1): served past this XCD's L2, where another XCD's stores land.
+  using rec_t = u32x2;
+  auto rec_load = [&](rec_t &rv, int q) {
+    const Step sp = step_at(q);
+    const int rr = uniform(min(sp.row0 + wave, B - 1));
+    const uint32_t off = 2 * lane < S * T::PW ? (uint32_t)(rr * S * T::PW + 2 * lane) * 4u : 0x80000000u;
+    rv = __builtin_amdgcn_raw_buffer_load_b64(rec_rsrc, off, 0, kSc1);
+  };
+  auto rec_ready = [&](const rec_t &rv) -> bool {
+    const int w = 2 * lane;                       // first word of this lane
+    const bool lo_used = w < S * T::PW && (w % T::PW) <= NS;
+    const bool hi_used = w + 1 < S * T::PW && ((w + 1) % T::PW) <= NS;
+    const bool ok = (!lo_used || rv[0] != 0u) && (!hi_used || rv[1] != 0u);
+    return __builtin_amdgcn_ballot_w64(!ok) == 0;
+  };
+  // Poll until every record is there; true if the wait gave up.
+  auto rec_wait = [&](rec_t &rv, int q) -> bool {
+    if (rec_ready(rv)) return false;
+    bool ready = false;
+    int tries = 0;
+    do {
+      __builtin_amdgcn_s_sleep(8);
+      rec_load(rv, q);
+      ready = rec_ready(rv);
+    } while (!ready && ++tries < kSpinLimit);
+    return !ready;
+  };
+  // H_pre of the row from its records.  Lane 16c + s gathers column c of
+  // slice s (word s*PW + c, in lane (s*PW + c)/2, half c&1; zero past S) and
+  // each 16-lane group sums its column over the 16 slice slots as a
+  // balanced binary tree (tree16_sum), the order the combine kernel uses in
+  // this mode: equal sums, equal H_pre bits.  Lane 16i then forms gate i.
+  auto pre_coeffs = [&](const rec_t &rv, float (&hp)[NS]) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // keep the gather addresses out of the loop's live registers
+    const int sl = ln & 15;
+    float t[T::RB];
+#pragma unroll
+    for (int b = 0; b < T::RB; ++b) {
+      const int c = b == 0 ? min(ln >> 4, NS) : NS;  // column of this lane's group
+      const int src = (sl * T::PW + c) >> 1;
+      const int lo = __builtin_amdgcn_ds_bpermute(src * 4, (int)rv[0]);
+      const int hi = __builtin_amdgcn_ds_bpermute(src * 4, (int)rv[1]);
+      const float v = __int_as_float((c & 1) ? hi : lo);
+      t[b] = tree16_sum(sl < S ? v : 0.f);
+    }
+    const float sq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t[T::RB - 1]), NS < 4 ? 16 * NS : 0));
+    const float inv_r = recip_exact(row_rms(sq, pa.inv_k));
+    const float gate = pre_gate(t[0], inv_r, pa.alpha_pre, bpre_lane);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) hp[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gate), 16 * i));
+  };
+  // F_pre of this wave's row of step q from its tile; `real` false or a
+  // given-up wait send the vector to the dummy area / poison it with NaN.
+  // Lanes past the slice take the last in-range vector's tile slot, so they
+  // store the owning lane's bytes to the owning lane's address.
+  auto emit = [&](int q, const float (&hp)[NS], bool poison, bool real) {
+    const Step sp = step_at(q);
+    const int row = sp.row0 + wave;
+    const int cst = min(sp.c0 + 8 * lane, sp.c_end - 8);
+    const int slot = (((cst - sp.c0) >> 3) ^ (wave & 15)) * 16;
+    const char *src = tile_of(q) + wave * T::ROW_BYTES;
+    u32x4 xv[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) xv[i] = *reinterpret_cast<const u32x4 *>(src + i * (kStepCh * 2) + slot);
+    u32x4 o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        a0 = fmaf(hp[j], bf16_lo(xv[j][w]), a0);
+        a1 = fmaf(hp[j], bf16_hi(xv[j][w]), a1);
+      }
+      o[w] = pack_bf16x2(a0, a1);
+    }
+    if (poison) o = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+    // The row's own buffer; a row without a target (past B, or before the
+    // first step) gets an empty one, so the store is dropped.
+    const bool tgt = real && row < B;  // wave-uniform
+    const __amdgpu_buffer_rsrc_t frow = __builtin_amdgcn_make_buffer_rsrc(
+        pa.F_pre + (size_t)min(row, B - 1) * C, (short)0, tgt ? C * 2 : 0, kRsrcWord3);
+    __builtin_amdgcn_raw_buffer_store_b128(o, frow, (uint32_t)cst * 2u, 0, 0);
   };
 
   // One step on the loads in (xv, fv, hv); refills them with step t_pref.
   auto step = [&](int t, vec (&xv)[NS], vec &fv, uint32_t (&hv)[T::HV], int t_pref) {
     const Step sp = step_at(t);
+    [[maybe_unused]] u32x2 rv;
+    if constexpr (IO::PRE) {
+      // The pre-mix mode publishes step t-1's sums first thing, a whole step
+      // before any workgroup reads them (at step t+1), and issues the reads
+      // of step t-2's records ahead of its own stores, so checking them after
+      // the apply waits for no store of this step.
+      __syncthreads();  // red holds step t-1's sums
+      rec_load(rv, t >= 2 ? t - 2 : 0);
+      flush(step_at(t > 0 ? t - 1 : 0), t > 0);
+    }
     const int row = sp.row0 + wave;
     const bool live = row < B;
     const int rr = uniform(min(row, B - 1));
@@ -205,7 +384,7 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
       return __builtin_bit_cast(float, __builtin_amdgcn_readlane((int)hv[k / 64], k % 64));
     };
     vec out[NS];
-    if constexpr (MODE == kFusedApplyBf16) {
+    if constexpr (MODE == kFusedApplyBf16 || IO::PRE) {
       if constexpr (NS <= 4) {
         float hpost[NS], hres[NS][NS];
 #pragma unroll
@@ -321,7 +500,7 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
     // E4M3 values widen exactly.  Taken at the LDS write, before the refill
     // overwrites xv, so no second copy is held across the stores.
     auto tile_vec = [&](int i) -> u32x4 {
-      if constexpr (MODE == kFusedApplyBf16) return out[i];
+      if constexpr (MODE == kFusedApplyBf16 || IO::PRE) return out[i];
       else if constexpr (MODE == kFusedApplyFp8) return fp8x8_to_bf16(out[i]);
       else if constexpr (MODE == kFusedCoeffsFp8) return fp8x8_to_bf16(xv[i]);
       else return xv[i];
@@ -342,7 +521,31 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
           b[q][nb] = __builtin_bit_cast(bf16x8, load16(phip + ((size_t)(kstep * T::NB + nb) * 64 + lane) * 8));
       }
     };
-    if constexpr (IO::APPLY) {
+    char *my_lds_row = tile_of(t) + wave * T::ROW_BYTES;
+    if constexpr (IO::PRE) {
+      uint8_t *yr = Y + (size_t)rr * NS * C * IO::EB;
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+        __builtin_nontemporal_store(out[i], reinterpret_cast<vec *>(yr + ((size_t)i * C + cst) * IO::EB));
+      // Keep the record check below the stores: the check's wait then covers
+      // only loads issued at least a step ago (and the step's own stores).
+      asm volatile("" ::: "memory");
+      // F_pre of step t-2 from this wave's row of tile t&1, then this step's
+      // row into the same place (the wave's own row: program order suffices;
+      // every wave finished reading tile t&1 for step t-2's product before
+      // the barriers of step t-1).
+      const bool have = t >= 2;
+      bool poison = false;
+      if (have) poison = rec_wait(rv, t - 2);
+      float hp[NS];
+      pre_coeffs(rv, hp);
+      emit(have ? t - 2 : 0, hp, poison, have);
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+        *reinterpret_cast<u32x4 *>(my_lds_row + i * (kStepCh * 2) + wslot) =
+            (in_range && live) ? tile_vec(i) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if constexpr (IO::APPLY && !IO::PRE) {
       uint8_t *yr = Y + (size_t)rr * NS * C * IO::EB;
 #pragma unroll
       for (int i = 0; i < NS; ++i)
@@ -353,18 +556,22 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
     // the refill would not fit the register budget.
     if constexpr (NS < 8) load_b(0);
 
-    __syncthreads();  // the previous step's product is done with the tile (and has written red)
-    if constexpr (T::SEPARATE) flush(step_at(t > 0 ? t - 1 : 0));
+    if constexpr (!IO::PRE) {
+      __syncthreads();  // the previous step's product is done with the tile (and has written red)
+      if constexpr (T::SEPARATE) flush(step_at(t > 0 ? t - 1 : 0), t > 0);
 #pragma unroll
-    for (int i = 0; i < NS; ++i)
-      *reinterpret_cast<u32x4 *>(my_lds_row + i * (kStepCh * 2) + wslot) =
-          (in_range && live) ? tile_vec(i) : u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < NS; ++i)
+        *reinterpret_cast<u32x4 *>(my_lds_row + i * (kStepCh * 2) + wslot) =
+            (in_range && live) ? tile_vec(i) : u32x4{0u, 0u, 0u, 0u};
+    }
     load_set(xv, fv, hv, step_at(t_pref));
     if constexpr (NS >= 8) load_b(0);
     __syncthreads();  // the tile is complete (and the flush has read red)
 
-    // A unit's sums start from zero at its first step.
-    const bool first = (t % spu) == 0;
+    // A unit's sums start from zero at its first step (every step in the
+    // pre-mix mode, which has one step per unit: the sums then live only
+    // within the step).
+    const bool first = IO::PRE || (t % spu) == 0;
 #pragma unroll
     for (int nb = 0; nb < T::NB; ++nb) acc[nb] = first ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[nb];
     gram = first ? f32x4{0.f, 0.f, 0.f, 0.f} : gram;
@@ -377,7 +584,7 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
         const int ks = wave * T::KPW + q0 + q;
         const int i = ks >> 4, ts = ks & 15;
         const int piece = (4 * ts + g) ^ m;
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(lds + m * T::ROW_BYTES + i * (kStepCh * 2) + piece * 16);
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(tile_of(t) + m * T::ROW_BYTES + i * (kStepCh * 2) + piece * 16);
 #pragma unroll
         for (int nb = 0; nb < T::NB; ++nb)
           acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[q][nb], acc[nb], 0, 0, 0);
@@ -390,7 +597,7 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
       __syncthreads();  // every wave is done with the tile, which now holds red
       write_red();
       __syncthreads();
-      flush(sp);        // the next step's first barrier orders it before the tile is rewritten
+      flush(sp, true);  // the next step's first barrier orders it before the tile is rewritten
     }
   };
 
@@ -419,7 +626,19 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
   }
   if constexpr (T::SEPARATE) {
     __syncthreads();
-    flush(step_at(tl));
+    flush(step_at(tl), true);
+  }
+  if constexpr (IO::PRE) {
+    // The last two steps' F_pre (their tiles are intact: nothing rewrote them).
+#pragma unroll 1
+    for (int q = tl >= 1 ? tl - 1 : tl; q <= tl; ++q) {
+      u32x2 rv;
+      rec_load(rv, q);
+      const bool poison = rec_wait(rv, q);
+      float hp[NS];
+      pre_coeffs(rv, hp);
+      emit(q, hp, poison, true);
+    }
   }
 }
 
@@ -439,52 +658,70 @@ int device_cus() {
   return cus;
 }
 
-}  // namespace
 
 template <int NS, int MODE>
-hipError_t launch_post_res_next_typed(int64_t B, int64_t C, int spu, int split, int grid_cap,
+hipError_t launch_post_res_next_typed(int64_t B, int64_t C, int spu, int split, int G,
                                       const void *X, const void *F, const float *H, void *Y,
-                                      const void *phip, float *ws, float *dummy, hipStream_t st) {
+                                      const void *phip, float *ws, float *dummy,
+                                      const PreArgs &pa, hipStream_t st) {
   const int64_t U = ((B + 15) / 16) * (int64_t)split;
-  const int G = (int)(U < grid_cap ? U : grid_cap);
   post_res_next_kernel<NS, MODE><<<dim3((uint32_t)G), 1024, 0, st>>>(
       static_cast<const uint8_t *>(X), static_cast<const uint8_t *>(F), H,
       static_cast<uint8_t *>(Y), static_cast<const uint16_t *>(phip), ws, dummy, (int)B, (int)C,
-      spu, split, (int)U);
+      spu, split, (int)U, pa);
   return hipGetLastError();
 }
 
 template <int MODE>
-hipError_t launch_mode(int n, int64_t B, int64_t C, int spu, int split, int cap, const void *X,
+hipError_t launch_mode(int n, int64_t B, int64_t C, int spu, int split, int G, const void *X,
                        const void *F, const float *H, void *Y, const void *phip, float *ws,
-                       float *dummy, hipStream_t st) {
+                       float *dummy, const PreArgs &pa, hipStream_t st) {
   switch (n) {
-    case 1: return launch_post_res_next_typed<1, MODE>(B, C, spu, split, cap, X, F, H, Y, phip, ws, dummy, st);
-    case 2: return launch_post_res_next_typed<2, MODE>(B, C, spu, split, cap, X, F, H, Y, phip, ws, dummy, st);
-    case 4: return launch_post_res_next_typed<4, MODE>(B, C, spu, split, cap, X, F, H, Y, phip, ws, dummy, st);
-    case 8: return launch_post_res_next_typed<8, MODE>(B, C, spu, split, cap, X, F, H, Y, phip, ws, dummy, st);
+    case 1: return launch_post_res_next_typed<1, MODE>(B, C, spu, split, G, X, F, H, Y, phip, ws, dummy, pa, st);
+    case 2: return launch_post_res_next_typed<2, MODE>(B, C, spu, split, G, X, F, H, Y, phip, ws, dummy, pa, st);
+    case 4: return launch_post_res_next_typed<4, MODE>(B, C, spu, split, G, X, F, H, Y, phip, ws, dummy, pa, st);
+    case 8:
+      if constexpr (MODE == kFusedApplyPreBf16) return hipErrorInvalidValue;  // n <= 4 only
+      else return launch_post_res_next_typed<8, MODE>(B, C, spu, split, G, X, F, H, Y, phip, ws, dummy, pa, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-FusedPlan plan_post_res_next(int64_t B, int n, int64_t C) {
+constexpr int kRecordSlices = 16;  // slices one record gather covers
+
+}  // namespace
+
+bool pre_mode_fits(int64_t B, int n, int64_t C) {
+  if (n != 1 && n != 2 && n != 4) return false;
+  const int64_t steps = (C + kStepCh - 1) / kStepCh;
+  const int64_t N = (int64_t)n * n + 2 * n;
+  const int64_t lim = int64_t(1) << 31;
+  return steps <= kRecordSlices && steps <= device_cus() && C * 2 < lim &&
+         steps * B * ((n + 2) & ~1) * 4 < lim && steps * B * (N + 1) * 4 < lim;
+}
+
+FusedPlan plan_post_res_next(int64_t B, int n, int64_t C, bool pre) {
   FusedPlan p;
   const int64_t N = (int64_t)n * n + 2 * n, NB = (N + 15) / 16, K = (int64_t)n * C;
   p.row_tiles = (B + 15) / 16;
+  p.pre = pre;
   // Steps per unit: the largest divisor of the row's step count that still
   // leaves at least 7 slices (fewer when the row is shorter), so that the
   // ~256 resident workgroups cover at most ~37 row tiles at a time while the
   // partial sums stay small (7 x B x (N+1) fp32).  MHC_FUSED_SPU overrides
   // (any value >= 1; one that does not divide the step count leaves empty
-  // steps at the end of the last slice, which add nothing).
+  // steps at the end of the last slice, which add nothing).  The pre-mix
+  // mode takes one step per unit: a unit's flush is then its total.
   const int64_t steps = (C + kStepCh - 1) / kStepCh;
   const int64_t want = steps < 7 ? steps : 7;
   int64_t spu = 1;
-  for (int64_t d = 1; d <= steps; ++d)
-    if (steps % d == 0 && steps / d >= want) spu = d;
-  if (const char *e = std::getenv("MHC_FUSED_SPU")) {
-    const long v = std::strtol(e, nullptr, 10);
-    if (v >= 1 && v <= steps) spu = v;
+  if (!pre) {
+    for (int64_t d = 1; d <= steps; ++d)
+      if (steps % d == 0 && steps / d >= want) spu = d;
+    if (const char *e = std::getenv("MHC_FUSED_SPU")) {
+      const long v = std::strtol(e, nullptr, 10);
+      if (v >= 1 && v <= steps) spu = v;
+    }
   }
   p.cw = (int)(spu * kStepCh);
   p.split = (int)((steps + spu - 1) / spu);
@@ -495,30 +732,55 @@ FusedPlan plan_post_res_next(int64_t B, int n, int64_t C) {
   p.phip_offset = p.dummy_offset + p.dummy_bytes;
   p.phip_bytes = (size_t)p.ksteps * (size_t)NB * 1024;
   p.zero_offset = p.phip_offset + p.phip_bytes;
-  p.total_bytes = p.zero_offset + 256;
+  p.rec_offset = p.zero_offset + 256;
+  p.rec_bytes = pre ? (size_t)p.split * (size_t)B * (size_t)((n + 2) & ~1) * 4 : 0;
+  p.total_bytes = p.rec_offset + ((p.rec_bytes + 15) & ~(size_t)15);
   return p;
 }
 
 hipError_t launch_post_res_next(const FusedPlan &p, int n, int mode, int64_t B, int64_t C,
                                 const void *X, const void *F, const float *H, void *Y,
-                                const void *phi_next, void *ws_base, hipStream_t st) {
+                                const void *phi_next, void *ws_base, hipStream_t st,
+                                const PreOut *pre_out) {
+  const bool pre = mode == kFusedApplyPreBf16;
+  if (pre != p.pre || (pre && !pre_out)) return hipErrorInvalidValue;
   char *base = static_cast<char *>(ws_base);
   void *phip = base + p.phip_offset;
-  hipError_t e = launch_pack_phi(n, (int64_t)n * C, p.ksteps, phi_next, phip, base + p.zero_offset, st);
+  // The pre-mix mode's records start from zero: the packing launch clears them.
+  hipError_t e = launch_pack_phi(n, (int64_t)n * C, p.ksteps, phi_next, phip, base + p.zero_offset, st,
+                                 pre ? base + p.rec_offset : nullptr, (p.rec_bytes + 15) & ~(size_t)15);
   if (e != hipSuccess) return e;
   float *ws = reinterpret_cast<float *>(base);
   float *dummy = reinterpret_cast<float *>(base + p.dummy_offset);
   const int spu = p.cw / kStepCh;
+  const int64_t U = p.row_tiles * (int64_t)p.split;
   int cap = device_cus();
-  if (const char *env = std::getenv("MHC_FUSED_WGS")) {
+  PreArgs pa{};
+  if (pre) {
+    // Workgroups of one row tile wait for each other's records, so the whole
+    // grid must be resident at once: one workgroup per CU (the mode's LDS
+    // admits no second), in whole row tiles (a multiple of S) so that the S
+    // slices of a tile are always taken in the same round.
+    cap = (cap / p.split) * p.split;
+    pa.F_pre = static_cast<uint16_t *>(pre_out->F_pre);
+    pa.rec = reinterpret_cast<uint32_t *>(base + p.rec_offset);
+    pa.rec_bytes = (uint32_t)p.rec_bytes;
+    pa.partial_bytes = (uint32_t)p.partial_bytes;
+    pa.b_pre = pre_out->b_pre;
+    pa.alpha_pre = pre_out->alpha_pre;
+    pa.inv_k = (float)(1.0 / (double)((int64_t)n * C));
+  } else if (const char *env = std::getenv("MHC_FUSED_WGS")) {
     const long v = std::strtol(env, nullptr, 10);
     if (v >= 1 && v <= 65535) cap = (int)v;
   }
+  if (cap < 1) return hipErrorInvalidValue;
+  const int G = (int)(U < cap ? U : cap);
   switch (mode) {
-    case kFusedApplyBf16: return launch_mode<kFusedApplyBf16>(n, B, C, spu, p.split, cap, X, F, H, Y, phip, ws, dummy, st);
-    case kFusedApplyFp8: return launch_mode<kFusedApplyFp8>(n, B, C, spu, p.split, cap, X, F, H, Y, phip, ws, dummy, st);
-    case kFusedCoeffsFp8: return launch_mode<kFusedCoeffsFp8>(n, B, C, spu, p.split, cap, X, F, H, Y, phip, ws, dummy, st);
-    case kFusedCoeffsBf16: return launch_mode<kFusedCoeffsBf16>(n, B, C, spu, p.split, cap, X, F, H, Y, phip, ws, dummy, st);
+    case kFusedApplyBf16: return launch_mode<kFusedApplyBf16>(n, B, C, spu, p.split, G, X, F, H, Y, phip, ws, dummy, pa, st);
+    case kFusedApplyFp8: return launch_mode<kFusedApplyFp8>(n, B, C, spu, p.split, G, X, F, H, Y, phip, ws, dummy, pa, st);
+    case kFusedCoeffsFp8: return launch_mode<kFusedCoeffsFp8>(n, B, C, spu, p.split, G, X, F, H, Y, phip, ws, dummy, pa, st);
+    case kFusedCoeffsBf16: return launch_mode<kFusedCoeffsBf16>(n, B, C, spu, p.split, G, X, F, H, Y, phip, ws, dummy, pa, st);
+    case kFusedApplyPreBf16: return launch_mode<kFusedApplyPreBf16>(n, B, C, spu, p.split, G, X, F, H, Y, phip, ws, dummy, pa, st);
     default: return hipErrorInvalidValue;
   }
 }
