@@ -84,6 +84,7 @@ struct PreArgs {
   uint32_t *rec;                  // records [B, split, PW]: fp32 bits, 0 = not yet written
   uint32_t rec_bytes;             // split * B * PW * 4 (< 2^31); PW = n+1 rounded up to even
   uint32_t partial_bytes;         // split * B * (N+1) * 4 (< 2^31)
+  uint32_t phip_bytes;            // packed phi (< 2^31)
   const float *b_pre;             // fp32 [n]
   float alpha_pre, inv_k;         // alpha_pre; 1 / (n C)
 };

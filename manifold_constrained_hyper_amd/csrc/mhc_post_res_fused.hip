@@ -50,6 +50,35 @@
 // H_post * F_out, one round-to-nearest-even to bf16), so X_{t+1} is bitwise
 // what the stand-alone apply writes, and the product consumes those rounded
 // values, exactly what a separate product pass would read back.
+//
+// Pre-mix mode (kFusedApplyPreBf16, n <= 4, mhc_post_res_coeffs_pre).  The
+// next layer also needs F_pre = sum_i H_pre[i] X_{t+1}[i] (section 2.5,
+// first step), and H_pre needs the whole row's product (sections 2.1-2.4),
+// which S workgroups compute slice by slice.  This mode forms F_pre in the
+// same pass, so X_{t+1} is written once and never read back at all:
+//   * one step per unit (a unit's flush is its total) and a grid of whole
+//     row tiles (G % S == 0): the S slices of a row tile are always taken
+//     in the same round by S co-resident workgroups;
+//   * two LDS tiles: step t's X_{t+1} rows stay on chip until step t+2
+//     rewrites their tile;
+//   * at the start of step t+1 each workgroup publishes, per row of step t,
+//     the n pre logits and the sum of squares of its slice as 4-byte
+//     records in the workspace (buffer stores with the SC1 bit, which the
+//     gfx950 memory model uses for agent-scope coherence across XCDs; a
+//     record is zero until written, and a written value is never the zero
+//     word: +0.0 is stored as -0.0);
+//   * at step t+2 each wave reads its row's records for all S slices (one
+//     8-byte load per lane, issued at the start of the step, checked after
+//     the apply; a rare miss is polled with a bounded wait), sums each
+//     column over 16 slice slots as a balanced tree (the order the combine
+//     kernel uses in this mode, so H_pre comes out bitwise as in H_next),
+//     forms the n gates and emits its row of F_pre from the tile exactly as
+//     pre_kernel would from X_{t+1} in HBM.
+// No workgroup waits for one that has not started: a wait at step t+2 needs
+// only records published at the start of step t+1 by workgroups of the same
+// round, and every workgroup publishes before it waits (induction over t;
+// all G workgroups are resident at once: one per CU).  A wait that cannot
+// end within about a second gives up and writes NaN to its F_pre vector.
 #include "mhc_device.h"
 #include "mhc_finish.h"
 #include "mhc_launch.h"
@@ -79,17 +108,24 @@ constexpr int kSpinLimit = 1 << 17;
 // gives agent-scope atomic loads and stores).
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kSc1 = 16;
+constexpr int kNt = 2;  // non-temporal (streaming) buffer access
 
 template <int NS, bool PRE = false>
 struct FusedTile {
   static constexpr int N = NS * NS + 2 * NS;
   static constexpr int NP = N + 1;
   static constexpr int NB = (N + 15) / 16;
+  // Rows per tile = waves per workgroup (one workgroup per CU).  A tile of
+  // R < 16 rows would repeat its rows in the upper MFMA rows (results there
+  // unused); 8-row tiles with two workgroups per CU measured slower for the
+  // pre-mix mode (twice the phi operand traffic per row).
+  static constexpr int R = 16;
+  static constexpr int THREADS = 64 * R;
   static constexpr int ROW_BYTES = NS * kStepCh * 2;   // one tile row in LDS
-  static constexpr int TILE_BYTES = 16 * ROW_BYTES;    // 64 KiB at n=4, 128 KiB at n=8
+  static constexpr int TILE_BYTES = R * ROW_BYTES;     // 64 KiB at n=4, 128 KiB at n=8 (R = 16)
   static constexpr int NT = PRE ? 2 : 1;               // tiles (pre-mix: this step's and the one before)
   static constexpr int KSTEPS = 16 * NS;               // 32-channel MFMA steps per step
-  static constexpr int KPW = KSTEPS / 16;              // ... per wave (= NS)
+  static constexpr int KPW = KSTEPS / R;               // ... per wave
   static constexpr int KB = NS >= 8 ? 2 : (KPW < 4 ? KPW : 4);  // k-steps whose B operands are held at once
   static constexpr int NH = NS + NS * NS;              // H_post and H_res of one row
   static constexpr int HV = (NH + 63) / 64;            // dwords per lane that hold them
@@ -98,13 +134,13 @@ struct FusedTile {
   // so that the two tiles and the buffer fit 160 KiB at n = 4.
   static constexpr int GRAM_COL = PRE ? NB * 16 - 1 : NB * 16;
   static constexpr int RS = PRE ? NB * 16 : NB * 16 + 1;
-  static constexpr int RED_BYTES = 16 * 16 * RS * 4;   // [16 waves][16 rows][RS] fp32
+  static constexpr int RED_BYTES = R * 16 * RS * 4;    // [R waves][16 MFMA rows][RS] fp32
   // The reduction buffer sits beside the tile when both fit (then the flush
   // of step s-1 overlaps step s); otherwise it reuses the tile buffer.
   static constexpr bool SEPARATE = NT * TILE_BYTES + RED_BYTES <= kLdsMax;
   static constexpr int LDS_BYTES = SEPARATE ? NT * TILE_BYTES + RED_BYTES
                                             : (TILE_BYTES > RED_BYTES ? TILE_BYTES : RED_BYTES);
-  static constexpr int OPT = (16 * NP + 1023) / 1024;  // flushed sums per thread
+  static constexpr int OPT = (R * NP + THREADS - 1) / THREADS;  // flushed sums per thread
   // Pre-mix hand-off: per (row, slice) the n pre logits and the sum of
   // squares, padded to an even count PW of 4-byte records; one 8-byte load
   // per lane reads a row's records for up to 16 slices (16 * PW <= 128).
@@ -158,13 +194,13 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
   auto step_at = [&](int t) {
     if constexpr (IO::PRE) {
       const int cb = pre_slot * kStepCh;
-      return Step{uniform((t * pre_gs + pre_tile0) * 16), cb, uniform(min(C, cb + kStepCh)), pre_slot};
+      return Step{uniform((t * pre_gs + pre_tile0) * T::R), cb, uniform(min(C, cb + kStepCh)), pre_slot};
     } else {
       const int j = t / spu, p = t - j * spu;
       const int u = j * G + pg;
       const int tile = u / S, s = u - tile * S;
       const int cb = s * cw;
-      return Step{uniform(tile * 16), uniform(cb + p * kStepCh), uniform(min(C, cb + cw)), uniform(s)};
+      return Step{uniform(tile * T::R), uniform(cb + p * kStepCh), uniform(min(C, cb + cw)), uniform(s)};
     }
   };
 
@@ -173,8 +209,10 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
   const int wslot = (lane ^ (wave & 15)) * 16;  // swizzled 16-byte slot of this lane
   // Buffer resources of the pre-mix mode (gfx9 raw buffers: stride 0, the
   // size in bytes as the record count; accesses past it are dropped).
-  [[maybe_unused]] __amdgpu_buffer_rsrc_t ws_rsrc, rec_rsrc;
+  [[maybe_unused]] __amdgpu_buffer_rsrc_t ws_rsrc, rec_rsrc, phi_rsrc;
+  [[maybe_unused]] const uint32_t lane_off16 = (uint32_t)lane * 16u;
   if constexpr (IO::PRE) {
+    phi_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(phip), (short)0, (int)pa.phip_bytes, kRsrcWord3);
     ws_rsrc = __builtin_amdgcn_make_buffer_rsrc(ws, (short)0, (int)pa.partial_bytes, kRsrcWord3);
     rec_rsrc = __builtin_amdgcn_make_buffer_rsrc(pa.rec, (short)0, (int)pa.rec_bytes, kRsrcWord3);
   }
@@ -214,15 +252,15 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
   auto flush = [&](const Step &sp, bool real) {
 #pragma unroll
     for (int q = 0; q < T::OPT; ++q) {
-      const int e = tid + q * 1024;
-      const int ec = min(e, 16 * T::NP - 1);
+      const int e = tid + q * T::THREADS;
+      const int ec = min(e, T::R * T::NP - 1);
       const int r = ec / T::NP, col = ec - r * T::NP;
       const int rcol = col < T::N ? col : T::GRAM_COL;
       float a = 0.f;
 #pragma unroll
-      for (int w = 0; w < 16; ++w) a += red[(w * 16 + r) * T::RS + rcol];
+      for (int w = 0; w < T::R; ++w) a += red[(w * 16 + r) * T::RS + rcol];
       const int row = sp.row0 + r;
-      const bool tgt = real && e < 16 * T::NP && row < B;
+      const bool tgt = real && e < T::R * T::NP && row < B;
       if constexpr (!IO::PRE) {
         float *dst = tgt ? ws + ((size_t)sp.slot * B + row) * T::NP + col : dummy + e;
         *dst = a;
@@ -354,7 +392,7 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
     const bool tgt = real && row < B;  // wave-uniform
     const __amdgpu_buffer_rsrc_t frow = __builtin_amdgcn_make_buffer_rsrc(
         pa.F_pre + (size_t)min(row, B - 1) * C, (short)0, tgt ? C * 2 : 0, kRsrcWord3);
-    __builtin_amdgcn_raw_buffer_store_b128(o, frow, (uint32_t)cst * 2u, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(o, frow, (uint32_t)cst * 2u, 0, kNt);
   };
 
   // One step on the loads in (xv, fv, hv); refills them with step t_pref.
@@ -517,8 +555,13 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
         const int cs = sp.c0 + 32 * ts;
         const int kstep = (i * C + min(cs, C - 32)) >> 5;  // clamped in range; such steps add zero
 #pragma unroll
-        for (int nb = 0; nb < T::NB; ++nb)
-          b[q][nb] = __builtin_bit_cast(bf16x8, load16(phip + ((size_t)(kstep * T::NB + nb) * 64 + lane) * 8));
+        for (int nb = 0; nb < T::NB; ++nb) {
+          if constexpr (IO::PRE)  // scalar block offset + the lane's 16 bytes: one offset register
+            b[q][nb] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                phi_rsrc, lane_off16, uniform((kstep * T::NB + nb) * 1024), 0));
+          else
+            b[q][nb] = __builtin_bit_cast(bf16x8, load16(phip + ((size_t)(kstep * T::NB + nb) * 64 + lane) * 8));
+        }
       }
     };
     char *my_lds_row = tile_of(t) + wave * T::ROW_BYTES;
@@ -529,6 +572,9 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
         __builtin_nontemporal_store(out[i], reinterpret_cast<vec *>(yr + ((size_t)i * C + cst) * IO::EB));
       // Keep the record check below the stores: the check's wait then covers
       // only loads issued at least a step ago (and the step's own stores).
+      // The phi operands of this step's product are issued here, so that
+      // their L2 latency passes during the emission.
+      load_b(0);
       asm volatile("" ::: "memory");
       // F_pre of step t-2 from this wave's row of tile t&1, then this step's
       // row into the same place (the wave's own row: program order suffices;
@@ -554,7 +600,7 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
     // The first B group is issued before the refill (waiting for it then
     // never waits for the refill), except for n = 8, where holding it across
     // the refill would not fit the register budget.
-    if constexpr (NS < 8) load_b(0);
+    if constexpr (NS < 8 && !IO::PRE) load_b(0);
 
     if constexpr (!IO::PRE) {
       __syncthreads();  // the previous step's product is done with the tile (and has written red)
@@ -583,8 +629,9 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
       for (int q = 0; q < T::KB; ++q) {
         const int ks = wave * T::KPW + q0 + q;
         const int i = ks >> 4, ts = ks & 15;
-        const int piece = (4 * ts + g) ^ m;
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(tile_of(t) + m * T::ROW_BYTES + i * (kStepCh * 2) + piece * 16);
+        const int rm = m & (T::R - 1);  // tile row of MFMA row m
+        const int piece = (4 * ts + g) ^ rm;
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(tile_of(t) + rm * T::ROW_BYTES + i * (kStepCh * 2) + piece * 16);
 #pragma unroll
         for (int nb = 0; nb < T::NB; ++nb)
           acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[q][nb], acc[nb], 0, 0, 0);
@@ -664,8 +711,9 @@ hipError_t launch_post_res_next_typed(int64_t B, int64_t C, int spu, int split, 
                                       const void *X, const void *F, const float *H, void *Y,
                                       const void *phip, float *ws, float *dummy,
                                       const PreArgs &pa, hipStream_t st) {
-  const int64_t U = ((B + 15) / 16) * (int64_t)split;
-  post_res_next_kernel<NS, MODE><<<dim3((uint32_t)G), 1024, 0, st>>>(
+  using T = FusedTile<NS, FusedIO<MODE>::PRE>;
+  const int64_t U = ((B + T::R - 1) / T::R) * (int64_t)split;
+  post_res_next_kernel<NS, MODE><<<dim3((uint32_t)G), T::THREADS, 0, st>>>(
       static_cast<const uint8_t *>(X), static_cast<const uint8_t *>(F), H,
       static_cast<uint8_t *>(Y), static_cast<const uint16_t *>(phip), ws, dummy, (int)B, (int)C,
       spu, split, (int)U, pa);
@@ -688,6 +736,8 @@ hipError_t launch_mode(int n, int64_t B, int64_t C, int spu, int split, int G, c
 }
 
 constexpr int kRecordSlices = 16;  // slices one record gather covers
+constexpr int kPreWgsPerCu = 1;    // resident pre-mix workgroups per CU (its LDS admits no second)
+constexpr int kPreRows = 16;       // rows per tile of the pre-mix mode (FusedTile::R)
 
 }  // namespace
 
@@ -696,14 +746,15 @@ bool pre_mode_fits(int64_t B, int n, int64_t C) {
   const int64_t steps = (C + kStepCh - 1) / kStepCh;
   const int64_t N = (int64_t)n * n + 2 * n;
   const int64_t lim = int64_t(1) << 31;
-  return steps <= kRecordSlices && steps <= device_cus() && C * 2 < lim &&
+  const int64_t phip_bytes = ((int64_t)n * C + 31) / 32 * ((N + 15) / 16) * 1024;
+  return steps <= kRecordSlices && steps <= kPreWgsPerCu * device_cus() && C * 2 < lim && phip_bytes < lim &&
          steps * B * ((n + 2) & ~1) * 4 < lim && steps * B * (N + 1) * 4 < lim;
 }
 
 FusedPlan plan_post_res_next(int64_t B, int n, int64_t C, bool pre) {
   FusedPlan p;
   const int64_t N = (int64_t)n * n + 2 * n, NB = (N + 15) / 16, K = (int64_t)n * C;
-  p.row_tiles = (B + 15) / 16;
+  p.row_tiles = pre ? (B + kPreRows - 1) / kPreRows : (B + 15) / 16;
   p.pre = pre;
   // Steps per unit: the largest divisor of the row's step count that still
   // leaves at least 7 slices (fewer when the row is shorter), so that the
@@ -761,11 +812,17 @@ hipError_t launch_post_res_next(const FusedPlan &p, int n, int mode, int64_t B, 
     // grid must be resident at once: one workgroup per CU (the mode's LDS
     // admits no second), in whole row tiles (a multiple of S) so that the S
     // slices of a tile are always taken in the same round.
+    cap *= kPreWgsPerCu;
+    if (const char *env = std::getenv("MHC_FUSED_WGS")) {  // tuning: fewer workgroups (never more)
+      const long v = std::strtol(env, nullptr, 10);
+      if (v >= 1 && v < cap) cap = (int)v;
+    }
     cap = (cap / p.split) * p.split;
     pa.F_pre = static_cast<uint16_t *>(pre_out->F_pre);
     pa.rec = reinterpret_cast<uint32_t *>(base + p.rec_offset);
     pa.rec_bytes = (uint32_t)p.rec_bytes;
     pa.partial_bytes = (uint32_t)p.partial_bytes;
+    pa.phip_bytes = (uint32_t)p.phip_bytes;
     pa.b_pre = pre_out->b_pre;
     pa.alpha_pre = pre_out->alpha_pre;
     pa.inv_k = (float)(1.0 / (double)((int64_t)n * C));
