@@ -137,6 +137,58 @@ def test_fused_validation():
     assert need > 0 and _fused(ws_bytes=need - 1) == mhc.MHC_ERR_WORKSPACE
 
 
+def _fused_pre(B=16, n=4, C=64, ws_bytes=None, **over):
+    names = ["X", "F", "H", "Y", "phi", "bp", "bq", "br", "logits", "r", "Hn", "Fp", "ws"]
+    p = dict(zip(names, _addrs(len(names))))
+    p.update(over)
+    if ws_bytes is None:
+        ws_bytes = max(mhc.mhc_post_res_coeffs_pre_workspace_size(B, n, C), 16)
+    return mhc.mhc_post_res_coeffs_pre(B, n, C, p["X"], p["F"], p["H"], p["Y"], p["phi"], 0.01, 0.01,
+                                       0.01, p["bp"], p["bq"], p["br"], p["logits"], p["r"], p["Hn"],
+                                       p["Fp"], p["ws"], ws_bytes, stream=0, check=False)
+
+
+def test_fused_pre_validation():
+    assert _fused_pre(B=0) == mhc.MHC_OK
+    assert _fused_pre(B=0, X=None, Fp=None, ws=None) == mhc.MHC_OK
+    assert _fused_pre(C=40) == mhc.MHC_ERR_UNSUPPORTED                 # needs C % 32 == 0
+    assert mhc.mhc_post_res_coeffs_pre_workspace_size(16, 4, 40) == 0
+    assert _fused_pre(n=3) == mhc.MHC_ERR_UNSUPPORTED
+    assert _fused_pre(B=-2) == mhc.MHC_ERR_INVALID_ARG
+    for k in ("X", "F", "H", "Y", "phi", "bp", "bq", "br", "logits", "r", "Hn", "Fp", "ws"):
+        assert _fused_pre(**{k: None}) == mhc.MHC_ERR_INVALID_ARG, k
+    assert _fused_pre(Fp=A) == mhc.MHC_ERR_INVALID_ARG                 # F_pre overlaps X_t
+    assert _fused_pre(Fp=A + 3 * STEP + 256) == mhc.MHC_ERR_INVALID_ARG   # F_pre inside X_next
+    assert _fused_pre(Fp=A + 10 * STEP) == mhc.MHC_ERR_INVALID_ARG     # F_pre overlaps H_next
+    assert _fused_pre(ws=A + 11 * STEP) == mhc.MHC_ERR_INVALID_ARG     # workspace overlaps F_pre
+    assert _fused_pre(Fp=A + 11 * STEP + 8) == mhc.MHC_ERR_UNSUPPORTED  # F_pre needs 16-byte alignment
+    need = mhc.mhc_post_res_coeffs_pre_workspace_size(16, 4, 64)
+    assert need > 0 and _fused_pre(ws_bytes=need - 1) == mhc.MHC_ERR_WORKSPACE
+
+
+def test_fused_pre_route_and_workspace(monkeypatch):
+    monkeypatch.delenv("MHC_FUSED_PRE", raising=False)
+    monkeypatch.delenv("MHC_SMALL_MAX_B", raising=False)
+    one = mhc.mhc_post_res_coeffs_pre_one_pass
+    assert one(16384, 4, 7168) and one(4096, 4, 4096) and one(1000, 2, 4096) and one(300, 1, 1024)
+    assert not one(64, 4, 7168)          # small B: the two calls
+    assert not one(8192, 8, 4096)        # n = 8: two tiles do not fit LDS
+    assert not one(4096, 4, 8704)        # 17 steps of 512 channels per row
+    assert not one(0, 4, 7168) and not one(16, 4, 40)
+    # one pass: partials [S, B, N+1] fp32 + packed phi + records [B, S, PW] of 4 bytes
+    B, n, C = 16384, 4, 7168
+    S, N, PW = C // 512, n * n + 2 * n, (n + 2) & ~1
+    ws = mhc.mhc_post_res_coeffs_pre_workspace_size(B, n, C)
+    assert ws >= S * B * (N + 1) * 4 + S * B * PW * 4
+    assert ws <= S * B * (N + 1) * 4 + S * B * PW * 4 + (n * C // 32) * 2 * 1024 + 8192
+    # the two-call routes need what mhc_post_res_coeffs needs
+    assert mhc.mhc_post_res_coeffs_pre_workspace_size(8192, 8, 4096) == \
+        mhc.mhc_post_res_coeffs_workspace_size(8192, 8, 4096)
+    monkeypatch.setenv("MHC_FUSED_PRE", "0")
+    assert not one(16384, 4, 7168)
+    assert mhc.mhc_post_res_coeffs_pre_workspace_size(B, n, C) == mhc.mhc_post_res_coeffs_workspace_size(B, n, C)
+
+
 def test_binding_raises_on_error_status():
     with pytest.raises(mhc.MhcError) as ei:
         mhc.mhc_pre(16, 3, 64, *_addrs(3), stream=0)

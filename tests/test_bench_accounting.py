@@ -53,6 +53,9 @@ def test_path_bytes_large_workload():
     # inputs/outputs, but not X_next a second time
     assert b["mhc_post_res_coeffs"] == b["mhc_post_res"] + (b["mhc_coeffs"] - 16384 * 4 * 7168 * 2)
     assert b["mhc_pre"] + b["mhc_post_res_coeffs"] == 3294494816
+    # the one-pass call adds only the next layer's F_pre write: X read once, written once
+    assert b["mhc_post_res_coeffs_pre"] == b["mhc_post_res_coeffs"] + 16384 * 7168 * 2
+    assert b["mhc_post_res_coeffs_pre"] == 2354708576
     # post_res = page's apply convention at bf16 + the fp32 coefficients it reads
     assert b["mhc_post_res"] == bench.apply_stream_bytes(16384, 4, 7168, 2) + 16384 * 20 * 4
 
