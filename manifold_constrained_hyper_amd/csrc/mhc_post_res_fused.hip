@@ -217,6 +217,26 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
     rec_rsrc = __builtin_amdgcn_make_buffer_rsrc(pa.rec, (short)0, (int)pa.rec_bytes, kRsrcWord3);
   }
 
+  // The pre-mix mode keeps one slice for the whole run (and KB = KPW at
+  // n <= 4), so the phi operands of each wave's k-steps are the same on
+  // every step: loaded once here (scalar block offset + the lane's 16 bytes)
+  // and held in registers.
+  [[maybe_unused]] bf16x8 bfix[IO::PRE ? T::KB : 1][T::NB];
+  if constexpr (IO::PRE) {
+    static_assert(!IO::PRE || T::KB == T::KPW, "pre-mix mode holds every k-step's operands");
+    const int cb = pre_slot * kStepCh;
+#pragma unroll
+    for (int q = 0; q < T::KB; ++q) {
+      const int ks = wave * T::KPW + q;
+      const int i = ks >> 4, ts = ks & 15;
+      const int kstep = (i * C + min(cb + 32 * ts, C - 32)) >> 5;  // clamped in range; such steps add zero
+#pragma unroll
+      for (int nb = 0; nb < T::NB; ++nb)
+        bfix[q][nb] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+            phi_rsrc, lane_off16, uniform((kstep * T::NB + nb) * 1024), 0));
+    }
+  }
+
   f32x4 acc[T::NB], gram;
   gram = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -556,9 +576,8 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
         const int kstep = (i * C + min(cs, C - 32)) >> 5;  // clamped in range; such steps add zero
 #pragma unroll
         for (int nb = 0; nb < T::NB; ++nb) {
-          if constexpr (IO::PRE)  // scalar block offset + the lane's 16 bytes: one offset register
-            b[q][nb] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                phi_rsrc, lane_off16, uniform((kstep * T::NB + nb) * 1024), 0));
+          if constexpr (IO::PRE)
+            b[q][nb] = bfix[q][nb];
           else
             b[q][nb] = __builtin_bit_cast(bf16x8, load16(phip + ((size_t)(kstep * T::NB + nb) * 64 + lane) * 8));
         }
@@ -572,8 +591,6 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
         __builtin_nontemporal_store(out[i], reinterpret_cast<vec *>(yr + ((size_t)i * C + cst) * IO::EB));
       // Keep the record check below the stores: the check's wait then covers
       // only loads issued at least a step ago (and the step's own stores).
-      // The phi operands of this step's product are issued here, so that
-      // their L2 latency passes during the emission.
       load_b(0);
       asm volatile("" ::: "memory");
       // F_pre of step t-2 from this wave's row of tile t&1, then this step's
