@@ -86,7 +86,7 @@ mhc::GemmPlan split_plan(int64_t B, int32_t n, int64_t C, Elt e) {
 size_t coeffs_ws_bytes(int64_t B, int32_t n, int64_t C, Elt e) {
   switch (coeffs_path(B, n, C, e)) {
     case CoeffsPath::kSmall: return mhc::plan_coeffs_small(B, n, C).total_bytes;
-    case CoeffsPath::kPersistent: return mhc::plan_post_res_next(B, n, C).total_bytes;
+    case CoeffsPath::kPersistent: return mhc::plan_post_res_next(B, n, C, false, true).total_bytes;
     default: return mhc::gemm_workspace_bytes(split_plan(B, n, C, e), B, n);
   }
 }
@@ -128,7 +128,7 @@ int coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t, const v
                                              phi, alpha_pre, alpha_post, alpha_res, b_pre, b_post,
                                              b_res, logits, r, H, workspace, s, e.phi32));
   if (path == CoeffsPath::kPersistent) {
-    const mhc::FusedPlan plan = mhc::plan_post_res_next(B, n, C);
+    const mhc::FusedPlan plan = mhc::plan_post_res_next(B, n, C, false, true);
     st = from_hip(mhc::launch_post_res_next(plan, n, e.fp8 ? mhc::kFusedCoeffsFp8 : mhc::kFusedCoeffsBf16,
                                             B, C, X_t, nullptr, nullptr, nullptr, phi, workspace, s));
     if (st != MHC_OK) return st;
@@ -181,19 +181,26 @@ int post_res_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t, const
 // How mhc_post_res_coeffs(_fp8) runs: small B -> the apply, then the
 // one-launch small-B coefficient kernel on X_next; otherwise the fused kernel,
 // except where the apply followed by the split-K product on X_next measured
-// faster (chained layers on MI355X):
+// faster (MI355X):
 //   n = 8: the fused kernel re-reads 80-column phi blocks from L2 for every 16
 //          rows (501 vs 321 us bf16 at B=8192, C=4096); MHC_FUSED_N8=1 forces it;
-//   E4M3:  half the bytes per step leave the fused kernel's fixed per-step
-//          cost (barriers, flush, phi from L2) in front (407 vs 370 us per
-//          layer at n=4, C=7168, B=16384); MHC_FUSED_FP8=1 forces it.
+//   E4M3:  outside the fixed-slice layout (phi operands held in registers)
+//          the fused kernel's per-step phi reads from L2 cost more than the
+//          second pass saves; in it the fused kernel wins (243 vs 288 us per
+//          call, 371 vs 383 us per layer with pre_fp8, chained layers at
+//          n=4, C=7168, B=16384).  MHC_FUSED_FP8=1 forces the fused kernel,
+//          MHC_FUSED_FP8=0 the two passes.
 enum class FusedRoute { kSmall, kTwoPass, kFused };
 
 FusedRoute fused_route(int64_t B, int32_t n, int64_t C, Elt e) {
   if (mhc::use_coeffs_small(B, n, C)) return FusedRoute::kSmall;
   if (e.phi32) return FusedRoute::kTwoPass;  // the fused kernel takes bf16 phi only
   if (n == 8 && !std::getenv("MHC_FUSED_N8")) return FusedRoute::kTwoPass;
-  if (e.fp8 && !std::getenv("MHC_FUSED_FP8")) return FusedRoute::kTwoPass;
+  if (e.fp8) {
+    if (const char *v = std::getenv("MHC_FUSED_FP8"))
+      return std::strtol(v, nullptr, 10) == 0 ? FusedRoute::kTwoPass : FusedRoute::kFused;
+    if (!mhc::plan_post_res_next(B, n, C, false, true).fixed) return FusedRoute::kTwoPass;
+  }
   return FusedRoute::kFused;
 }
 
@@ -202,7 +209,7 @@ size_t post_res_coeffs_ws_bytes(int64_t B, int32_t n, int64_t C, Elt e) {
   switch (fused_route(B, n, C, e)) {
     case FusedRoute::kSmall: return mhc::plan_coeffs_small(B, n, C).total_bytes;
     case FusedRoute::kTwoPass: return mhc::gemm_workspace_bytes(split_plan(B, n, C, e), B, n);
-    default: return mhc::plan_post_res_next(B, n, C).total_bytes;
+    default: return mhc::plan_post_res_next(B, n, C, false, e.fp8).total_bytes;
   }
 }
 
@@ -246,7 +253,7 @@ int post_res_coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t
     return MHC_ERR_UNSUPPORTED;
   const FusedRoute route = fused_route(B, n, C, e);
   const bool one_pass = with_pre && pre_fused(B, n, C);
-  const mhc::FusedPlan plan = mhc::plan_post_res_next(B, n, C, one_pass);
+  const mhc::FusedPlan plan = mhc::plan_post_res_next(B, n, C, one_pass, e.fp8);
   const size_t ws_need = with_pre ? post_res_coeffs_pre_ws_bytes(B, n, C) : post_res_coeffs_ws_bytes(B, n, C, e);
   const int64_t N = ncoef(n), K = (int64_t)n * C;
   const size_t eb = e.bytes();
@@ -335,7 +342,7 @@ int32_t mhc_coeffs_split_k(int64_t B, int32_t n, int64_t C) {
   if (check_shape(B, n, C) != MHC_OK || B == 0) return 0;
   switch (coeffs_path(B, n, C, kBf16)) {
     case CoeffsPath::kSmall: return mhc::plan_coeffs_small(B, n, C).split;
-    case CoeffsPath::kPersistent: return mhc::plan_post_res_next(B, n, C).split;
+    case CoeffsPath::kPersistent: return mhc::plan_post_res_next(B, n, C, false, true).split;
     default: return mhc::plan_gemm(B, n, C).split;
   }
 }

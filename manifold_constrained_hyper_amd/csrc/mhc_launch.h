@@ -63,10 +63,16 @@ struct FusedPlan {
   int64_t row_tiles;  // 16-row tiles
   int64_t ksteps;     // packed phi 32-k steps
   bool pre;           // pre-mix mode layout
+  bool fixed;         // fixed-slice layout: one step per unit, whole row tiles per round
   size_t partial_bytes, dummy_offset, dummy_bytes, phip_offset, phip_bytes, zero_offset;
   size_t rec_offset, rec_bytes, total_bytes;
 };
-FusedPlan plan_post_res_next(int64_t B, int n, int64_t C, bool pre = false);
+// prefer_fixed: take the fixed-slice layout where it fits (n <= 4) unless
+// MHC_FUSED_FIXED=0; without it, only with MHC_FUSED_FIXED=1.  The pre-mix
+// mode always takes it.  Measured on MI355X (n=4, C=7168, B=16384, chained
+// layers): the E4M3 apply and both product-only modes run faster in it; the
+// bf16 apply after mhc_pre runs slower (393 vs 381 us).
+FusedPlan plan_post_res_next(int64_t B, int n, int64_t C, bool pre = false, bool prefer_fixed = false);
 // What the persistent kernel of mhc_post_res_fused.hip does per step.
 enum FusedMode : int {
   kFusedApplyBf16 = 0,     // bf16 X_t, F_out -> bf16 X_next, plus X_next . phi_next
@@ -84,7 +90,7 @@ struct PreArgs {
   uint32_t *rec;                  // records [B, split, PW]: fp32 bits, 0 = not yet written
   uint32_t rec_bytes;             // split * B * PW * 4 (< 2^31); PW = n+1 rounded up to even
   uint32_t partial_bytes;         // split * B * (N+1) * 4 (< 2^31)
-  uint32_t phip_bytes;            // packed phi (< 2^31)
+  uint32_t phip_bytes;            // packed phi (< 2^31; also set in the fixed-slice layout)
   const float *b_pre;             // fp32 [n]
   float alpha_pre, inv_k;         // alpha_pre; 1 / (n C)
 };

@@ -164,7 +164,10 @@ struct FusedIO {
   using vec = typename std::conditional<FP8, u32x2, u32x4>::type;  // 8 elements per lane
 };
 
-template <int NS, int MODE>
+// FIX: the fixed-slice layout (one step per unit, a grid of whole row tiles,
+// n <= 4; always so in the pre-mix mode), in which a workgroup keeps one
+// slice for its whole run.
+template <int NS, int MODE, bool FIX>
 __global__ __launch_bounds__(1024) void post_res_next_kernel(
     const uint8_t *__restrict__ X, const uint8_t *__restrict__ F, const float *__restrict__ H,
     uint8_t *__restrict__ Y, const uint16_t *__restrict__ phip, float *__restrict__ ws,
@@ -172,6 +175,8 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
   using IO = FusedIO<MODE>;
   using T = FusedTile<NS, IO::PRE>;
   using vec = typename IO::vec;
+  static_assert(!IO::PRE || FIX, "the pre-mix mode runs the fixed-slice layout");
+  static_assert(!FIX || T::KB == T::KPW, "the fixed-slice layout holds every k-step's operands");
   __shared__ __attribute__((aligned(1024))) char lds[T::LDS_BYTES];
   float *red = reinterpret_cast<float *>(lds + (T::SEPARATE ? T::NT * T::TILE_BYTES : 0));
 
@@ -187,12 +192,12 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
   if (pg >= U) return;
   const int nsteps = ((U - pg + G - 1) / G) * spu;
 
-  // The pre-mix mode has one step per unit and a grid of whole row tiles
-  // (G % S == 0), so a workgroup keeps one slice and its row tile advances
-  // by G/S tiles per step: no division per step.
+  // The fixed-slice layout has one step per unit and a grid of whole row
+  // tiles (G % S == 0), so a workgroup keeps one slice and its row tile
+  // advances by G/S tiles per step: no division per step.
   [[maybe_unused]] const int pre_slot = uniform(pg % S), pre_tile0 = uniform(pg / S), pre_gs = uniform(G / S);
   auto step_at = [&](int t) {
-    if constexpr (IO::PRE) {
+    if constexpr (FIX) {
       const int cb = pre_slot * kStepCh;
       return Step{uniform((t * pre_gs + pre_tile0) * T::R), cb, uniform(min(C, cb + kStepCh)), pre_slot};
     } else {
@@ -211,19 +216,18 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
   // size in bytes as the record count; accesses past it are dropped).
   [[maybe_unused]] __amdgpu_buffer_rsrc_t ws_rsrc, rec_rsrc, phi_rsrc;
   [[maybe_unused]] const uint32_t lane_off16 = (uint32_t)lane * 16u;
-  if constexpr (IO::PRE) {
+  if constexpr (FIX)
     phi_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(phip), (short)0, (int)pa.phip_bytes, kRsrcWord3);
+  if constexpr (IO::PRE) {
     ws_rsrc = __builtin_amdgcn_make_buffer_rsrc(ws, (short)0, (int)pa.partial_bytes, kRsrcWord3);
     rec_rsrc = __builtin_amdgcn_make_buffer_rsrc(pa.rec, (short)0, (int)pa.rec_bytes, kRsrcWord3);
   }
 
-  // The pre-mix mode keeps one slice for the whole run (and KB = KPW at
-  // n <= 4), so the phi operands of each wave's k-steps are the same on
-  // every step: loaded once here (scalar block offset + the lane's 16 bytes)
-  // and held in registers.
-  [[maybe_unused]] bf16x8 bfix[IO::PRE ? T::KB : 1][T::NB];
-  if constexpr (IO::PRE) {
-    static_assert(!IO::PRE || T::KB == T::KPW, "pre-mix mode holds every k-step's operands");
+  // In the fixed-slice layout (KB = KPW at n <= 4) the phi operands of each
+  // wave's k-steps are the same on every step: loaded once here (scalar
+  // block offset + the lane's 16 bytes) and held in registers.
+  [[maybe_unused]] bf16x8 bfix[FIX ? T::KB : 1][T::NB];
+  if constexpr (FIX) {
     const int cb = pre_slot * kStepCh;
 #pragma unroll
     for (int q = 0; q < T::KB; ++q) {
@@ -576,7 +580,7 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
         const int kstep = (i * C + min(cs, C - 32)) >> 5;  // clamped in range; such steps add zero
 #pragma unroll
         for (int nb = 0; nb < T::NB; ++nb) {
-          if constexpr (IO::PRE)
+          if constexpr (FIX)
             b[q][nb] = bfix[q][nb];
           else
             b[q][nb] = __builtin_bit_cast(bf16x8, load16(phip + ((size_t)(kstep * T::NB + nb) * 64 + lane) * 8));
@@ -632,9 +636,9 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
     __syncthreads();  // the tile is complete (and the flush has read red)
 
     // A unit's sums start from zero at its first step (every step in the
-    // pre-mix mode, which has one step per unit: the sums then live only
-    // within the step).
-    const bool first = IO::PRE || (t % spu) == 0;
+    // fixed-slice layout, which has one step per unit: the sums then live
+    // only within the step).
+    const bool first = FIX || (t % spu) == 0;
 #pragma unroll
     for (int nb = 0; nb < T::NB; ++nb) acc[nb] = first ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[nb];
     gram = first ? f32x4{0.f, 0.f, 0.f, 0.f} : gram;
@@ -723,31 +727,47 @@ int device_cus() {
 }
 
 
-template <int NS, int MODE>
+template <int NS, int MODE, bool FIX>
 hipError_t launch_post_res_next_typed(int64_t B, int64_t C, int spu, int split, int G,
                                       const void *X, const void *F, const float *H, void *Y,
                                       const void *phip, float *ws, float *dummy,
                                       const PreArgs &pa, hipStream_t st) {
   using T = FusedTile<NS, FusedIO<MODE>::PRE>;
   const int64_t U = ((B + T::R - 1) / T::R) * (int64_t)split;
-  post_res_next_kernel<NS, MODE><<<dim3((uint32_t)G), T::THREADS, 0, st>>>(
+  post_res_next_kernel<NS, MODE, FIX><<<dim3((uint32_t)G), T::THREADS, 0, st>>>(
       static_cast<const uint8_t *>(X), static_cast<const uint8_t *>(F), H,
       static_cast<uint8_t *>(Y), static_cast<const uint16_t *>(phip), ws, dummy, (int)B, (int)C,
       spu, split, (int)U, pa);
   return hipGetLastError();
 }
 
+template <int NS, int MODE>
+hipError_t launch_layout(bool fixed, int64_t B, int64_t C, int spu, int split, int G, const void *X,
+                         const void *F, const float *H, void *Y, const void *phip, float *ws,
+                         float *dummy, const PreArgs &pa, hipStream_t st) {
+  if constexpr (MODE == kFusedApplyPreBf16) {
+    if (!fixed) return hipErrorInvalidValue;
+    return launch_post_res_next_typed<NS, MODE, true>(B, C, spu, split, G, X, F, H, Y, phip, ws, dummy, pa, st);
+  } else if constexpr (NS >= 8) {
+    if (fixed) return hipErrorInvalidValue;  // n = 8 holds its operands in two groups
+    return launch_post_res_next_typed<NS, MODE, false>(B, C, spu, split, G, X, F, H, Y, phip, ws, dummy, pa, st);
+  } else {
+    return fixed ? launch_post_res_next_typed<NS, MODE, true>(B, C, spu, split, G, X, F, H, Y, phip, ws, dummy, pa, st)
+                 : launch_post_res_next_typed<NS, MODE, false>(B, C, spu, split, G, X, F, H, Y, phip, ws, dummy, pa, st);
+  }
+}
+
 template <int MODE>
-hipError_t launch_mode(int n, int64_t B, int64_t C, int spu, int split, int G, const void *X,
+hipError_t launch_mode(int n, bool fixed, int64_t B, int64_t C, int spu, int split, int G, const void *X,
                        const void *F, const float *H, void *Y, const void *phip, float *ws,
                        float *dummy, const PreArgs &pa, hipStream_t st) {
   switch (n) {
-    case 1: return launch_post_res_next_typed<1, MODE>(B, C, spu, split, G, X, F, H, Y, phip, ws, dummy, pa, st);
-    case 2: return launch_post_res_next_typed<2, MODE>(B, C, spu, split, G, X, F, H, Y, phip, ws, dummy, pa, st);
-    case 4: return launch_post_res_next_typed<4, MODE>(B, C, spu, split, G, X, F, H, Y, phip, ws, dummy, pa, st);
+    case 1: return launch_layout<1, MODE>(fixed, B, C, spu, split, G, X, F, H, Y, phip, ws, dummy, pa, st);
+    case 2: return launch_layout<2, MODE>(fixed, B, C, spu, split, G, X, F, H, Y, phip, ws, dummy, pa, st);
+    case 4: return launch_layout<4, MODE>(fixed, B, C, spu, split, G, X, F, H, Y, phip, ws, dummy, pa, st);
     case 8:
       if constexpr (MODE == kFusedApplyPreBf16) return hipErrorInvalidValue;  // n <= 4 only
-      else return launch_post_res_next_typed<8, MODE>(B, C, spu, split, G, X, F, H, Y, phip, ws, dummy, pa, st);
+      else return launch_layout<8, MODE>(fixed, B, C, spu, split, G, X, F, H, Y, phip, ws, dummy, pa, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -768,11 +788,29 @@ bool pre_mode_fits(int64_t B, int n, int64_t C) {
          steps * B * ((n + 2) & ~1) * 4 < lim && steps * B * (N + 1) * 4 < lim;
 }
 
-FusedPlan plan_post_res_next(int64_t B, int n, int64_t C, bool pre) {
+// The fixed-slice layout: one 512-channel step per unit and a grid of whole
+// row tiles, so that each workgroup keeps one slice and holds its phi
+// operands in registers for the whole run (n <= 4; n = 8 needs its
+// registers for two groups of operands).  It needs one workgroup per slice
+// at least and phi addressable by 32-bit buffer offsets.
+bool fixed_layout_fits(int n, int64_t C) {
+  if (n != 1 && n != 2 && n != 4) return false;
+  const int64_t steps = (C + kStepCh - 1) / kStepCh;
+  const int64_t N = (int64_t)n * n + 2 * n;
+  const int64_t phip_bytes = ((int64_t)n * C + 31) / 32 * ((N + 15) / 16) * 1024;
+  return steps <= device_cus() && phip_bytes < (int64_t(1) << 31);
+}
+
+FusedPlan plan_post_res_next(int64_t B, int n, int64_t C, bool pre, bool prefer_fixed) {
   FusedPlan p;
   const int64_t N = (int64_t)n * n + 2 * n, NB = (N + 15) / 16, K = (int64_t)n * C;
   p.row_tiles = pre ? (B + kPreRows - 1) / kPreRows : (B + 15) / 16;
   p.pre = pre;
+  p.fixed = pre;
+  if (!pre && fixed_layout_fits(n, C)) {
+    p.fixed = prefer_fixed;
+    if (const char *e = std::getenv("MHC_FUSED_FIXED")) p.fixed = std::strtol(e, nullptr, 10) != 0;
+  }
   // Steps per unit: the largest divisor of the row's step count that still
   // leaves at least 7 slices (fewer when the row is shorter), so that the
   // ~256 resident workgroups cover at most ~37 row tiles at a time while the
@@ -783,7 +821,7 @@ FusedPlan plan_post_res_next(int64_t B, int n, int64_t C, bool pre) {
   const int64_t steps = (C + kStepCh - 1) / kStepCh;
   const int64_t want = steps < 7 ? steps : 7;
   int64_t spu = 1;
-  if (!pre) {
+  if (!p.fixed) {
     for (int64_t d = 1; d <= steps; ++d)
       if (steps % d == 0 && steps / d >= want) spu = d;
     if (const char *e = std::getenv("MHC_FUSED_SPU")) {
@@ -834,12 +872,10 @@ hipError_t launch_post_res_next(const FusedPlan &p, int n, int mode, int64_t B, 
       const long v = std::strtol(env, nullptr, 10);
       if (v >= 1 && v < cap) cap = (int)v;
     }
-    cap = (cap / p.split) * p.split;
     pa.F_pre = static_cast<uint16_t *>(pre_out->F_pre);
     pa.rec = reinterpret_cast<uint32_t *>(base + p.rec_offset);
     pa.rec_bytes = (uint32_t)p.rec_bytes;
     pa.partial_bytes = (uint32_t)p.partial_bytes;
-    pa.phip_bytes = (uint32_t)p.phip_bytes;
     pa.b_pre = pre_out->b_pre;
     pa.alpha_pre = pre_out->alpha_pre;
     pa.inv_k = (float)(1.0 / (double)((int64_t)n * C));
@@ -847,14 +883,19 @@ hipError_t launch_post_res_next(const FusedPlan &p, int n, int mode, int64_t B, 
     const long v = std::strtol(env, nullptr, 10);
     if (v >= 1 && v <= 65535) cap = (int)v;
   }
+  if (p.fixed) {
+    // Whole row tiles per round (each workgroup keeps slice p(g) mod S).
+    cap = (cap / p.split) * p.split;
+    pa.phip_bytes = (uint32_t)p.phip_bytes;
+  }
   if (cap < 1) return hipErrorInvalidValue;
   const int G = (int)(U < cap ? U : cap);
   switch (mode) {
-    case kFusedApplyBf16: return launch_mode<kFusedApplyBf16>(n, B, C, spu, p.split, G, X, F, H, Y, phip, ws, dummy, pa, st);
-    case kFusedApplyFp8: return launch_mode<kFusedApplyFp8>(n, B, C, spu, p.split, G, X, F, H, Y, phip, ws, dummy, pa, st);
-    case kFusedCoeffsFp8: return launch_mode<kFusedCoeffsFp8>(n, B, C, spu, p.split, G, X, F, H, Y, phip, ws, dummy, pa, st);
-    case kFusedCoeffsBf16: return launch_mode<kFusedCoeffsBf16>(n, B, C, spu, p.split, G, X, F, H, Y, phip, ws, dummy, pa, st);
-    case kFusedApplyPreBf16: return launch_mode<kFusedApplyPreBf16>(n, B, C, spu, p.split, G, X, F, H, Y, phip, ws, dummy, pa, st);
+    case kFusedApplyBf16: return launch_mode<kFusedApplyBf16>(n, p.fixed, B, C, spu, p.split, G, X, F, H, Y, phip, ws, dummy, pa, st);
+    case kFusedApplyFp8: return launch_mode<kFusedApplyFp8>(n, p.fixed, B, C, spu, p.split, G, X, F, H, Y, phip, ws, dummy, pa, st);
+    case kFusedCoeffsFp8: return launch_mode<kFusedCoeffsFp8>(n, p.fixed, B, C, spu, p.split, G, X, F, H, Y, phip, ws, dummy, pa, st);
+    case kFusedCoeffsBf16: return launch_mode<kFusedCoeffsBf16>(n, p.fixed, B, C, spu, p.split, G, X, F, H, Y, phip, ws, dummy, pa, st);
+    case kFusedApplyPreBf16: return launch_mode<kFusedApplyPreBf16>(n, p.fixed, B, C, spu, p.split, G, X, F, H, Y, phip, ws, dummy, pa, st);
     default: return hipErrorInvalidValue;
   }
 }

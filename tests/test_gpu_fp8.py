@@ -45,8 +45,9 @@ def _gpu():
 # mhc_coeffs_fp8 has three implementations: the one-launch small-B kernel
 # (default up to 256 rows), the split-K product with X staged through LDS
 # (default above), and the persistent product kernel (MHC_GEMM_ALGO=2).  The
-# fused call is the apply + product by default and the fused kernel with
-# MHC_FUSED_FP8 (and MHC_FUSED_N8 at n = 8), both exercised here.
+# fused call is the fused kernel by default at n <= 4 (MHC_FUSED_FP8=0 gives
+# the apply + product instead, MHC_FUSED_FP8=1 the fused kernel also at n = 8
+# with MHC_FUSED_N8), all exercised here.
 # Every one must meet the bar at every size it supports.
 @pytest.fixture(params=["default", "small", "split", "persistent"])
 def path(request, monkeypatch):
@@ -221,12 +222,18 @@ def _layers(n, C, B, dist, seed):
     return cur, nxt
 
 
-@pytest.mark.parametrize("kernel", ["default", "fused"])
+@pytest.mark.parametrize("kernel", ["default", "fused", "twopass", "fused_spu"])
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "large", "wide"])
 def test_fp8_fused_named(name, kernel, monkeypatch):
-    if kernel == "fused":
+    if kernel in ("fused", "fused_spu"):
         monkeypatch.setenv("MHC_FUSED_FP8", "1")
         monkeypatch.setenv("MHC_FUSED_N8", "1")
+        if kernel == "fused_spu":
+            if synth.CONFIGS[name]["n"] == 8:
+                pytest.skip("n = 8 always runs this layout (kernel 'fused')")
+            monkeypatch.setenv("MHC_FUSED_FIXED", "0")
+    elif kernel == "twopass":
+        monkeypatch.setenv("MHC_FUSED_FP8", "0")
     _say(f"fp8 fused {name} kernel={kernel}")
     cfg = synth.CONFIGS[name]
     cur, nxt = _layers(cfg["n"], cfg["C"], cfg["B"], cfg["x_dist"], cfg["seed"])
@@ -246,10 +253,12 @@ def test_fp8_fused_ragged(B, n, C, path):
     _check_fused(cur, nxt, o, ref, f, list(range(B)), f"B{B}n{n}C{C}")
 
 
-@pytest.mark.parametrize("kernel", ["default", "fused"])
+@pytest.mark.parametrize("kernel", ["default", "fused", "twopass"])
 def test_fp8_fused_deterministic(kernel, monkeypatch):
     if kernel == "fused":
         monkeypatch.setenv("MHC_FUSED_FP8", "1")
+    elif kernel == "twopass":
+        monkeypatch.setenv("MHC_FUSED_FP8", "0")
     _say(f"fp8 fused determinism kernel={kernel}")
     cfg = synth.CONFIGS["prefill"]
     cur, nxt = _layers(cfg["n"], cfg["C"], cfg["B"], cfg["x_dist"], cfg["seed"])

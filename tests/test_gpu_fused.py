@@ -36,12 +36,18 @@ def _gpu():
 
 # Up to 256 rows mhc_post_res_coeffs runs the stand-alone apply and the
 # one-launch small-B coefficient kernel, and at n = 8 the apply and the
-# split-K product; "fused" forces the fused kernel at every size and n.
-@pytest.fixture(params=["default", "fused"])
+# split-K product; "fused" forces the fused kernel at every size and n (in
+# its default layout: several 512-channel steps per unit, slices changing
+# from round to round), and "fused_fixed" the same kernel in its fixed-slice
+# layout (n <= 4: one step per unit, each workgroup keeping one slice).
+@pytest.fixture(params=["default", "fused", "fused_fixed"])
 def route(request, monkeypatch):
-    if request.param == "fused":
+    monkeypatch.delenv("MHC_FUSED_FIXED", raising=False)
+    if request.param in ("fused", "fused_fixed"):
         monkeypatch.setenv("MHC_SMALL_MAX_B", "0")
         monkeypatch.setenv("MHC_FUSED_N8", "1")
+        if request.param == "fused_fixed":
+            monkeypatch.setenv("MHC_FUSED_FIXED", "1")
     else:
         monkeypatch.delenv("MHC_SMALL_MAX_B", raising=False)
         monkeypatch.delenv("MHC_FUSED_N8", raising=False)
@@ -110,6 +116,8 @@ def _check(cur, nxt, o, ref, f, rows, label):
 def test_fused_named(name, route):
     if route == "fused" and synth.CONFIGS[name]["B"] > 256 and synth.CONFIGS[name]["n"] != 8:
         pytest.skip("above 256 rows (n < 8) the default route is the fused kernel")
+    if route == "fused_fixed" and synth.CONFIGS[name]["n"] == 8:
+        pytest.skip("the fixed-slice layout is for n <= 4")
     _say(f"fused {name} route={route}")
     cfg = synth.CONFIGS[name]
     cur, nxt = _layers(cfg["n"], cfg["C"], cfg["B"], cfg["x_dist"], cfg["seed"])
