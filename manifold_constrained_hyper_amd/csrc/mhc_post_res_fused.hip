@@ -108,7 +108,6 @@ constexpr int kSpinLimit = 1 << 17;
 // gives agent-scope atomic loads and stores).
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kSc1 = 16;
-constexpr int kNt = 2;  // non-temporal (streaming) buffer access
 
 template <int NS, bool PRE = false>
 struct FusedTile {
@@ -416,7 +415,9 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
     const bool tgt = real && row < B;  // wave-uniform
     const __amdgpu_buffer_rsrc_t frow = __builtin_amdgcn_make_buffer_rsrc(
         pa.F_pre + (size_t)min(row, B - 1) * C, (short)0, tgt ? C * 2 : 0, kRsrcWord3);
-    __builtin_amdgcn_raw_buffer_store_b128(o, frow, (uint32_t)cst * 2u, 0, kNt);
+    // A plain store (default cache policy): measured 412-417 against 439-442
+    // us per call with the non-temporal bit at n=4, C=7168, B=16384.
+    __builtin_amdgcn_raw_buffer_store_b128(o, frow, (uint32_t)cst * 2u, 0, 0);
   };
 
   // One step on the loads in (xv, fv, hv); refills them with step t_pref.
