@@ -27,10 +27,11 @@ Algorithmic bytes (bf16 X_t, F_out, F_pre, X_next; fp32 coefficients):
 Split-K partials, the hand-off records of the one-pass call and the packed
 copy of phi are implementation traffic and are not counted.
 
-Also reported: the same pipeline on the E4M3 residual stream ("fp8", the
+Also reported: the same pipelines on the E4M3 residual stream ("fp8", the
 *_fp8 entry points, one byte per stream element in the byte count) and, for
-the other workloads (tiny, decode, prefill, wide), both dtypes' per-layer and
-three-call times ("workloads"; decode also cold, after a 512 MB write).
+the other workloads (tiny, decode, prefill, wide), both dtypes' one-pass,
+two-call and three-call times ("workloads"; decode also cold: the one-pass
+call after a 512 MB write).
 
 Also reported ("phi32_coeffs"): mhc_coeffs_phi32 (fp32 phi) beside mhc_coeffs
 on the same X, decode and headline workloads, mean call time.
@@ -114,9 +115,8 @@ KERNELS_OF_CALL = {"mhc_post_res": "post_res_kernel", "mhc_pre": "pre_kernel",
 class Pipeline:
     """The per-layer pipelines for one input set (X chained through the
     layers): `layer` = mhc_pre + mhc_post_res_coeffs, `onepass` =
-    mhc_post_res_coeffs_pre (bf16 only); and `three` = the three separate
-    calls on a fixed X_t; in bf16 or E4M3 (fp8=True: the *_fp8 entry
-    points)."""
+    mhc_post_res_coeffs_pre; and `three` = the three separate calls on a
+    fixed X_t; in bf16 or E4M3 (fp8=True: the *_fp8 entry points)."""
 
     def __init__(self, mhc, torch, inp, fp8=False):
         self.torch, self.inp = torch, inp
@@ -130,9 +130,8 @@ class Pipeline:
         self.fused = getattr(mhc, "mhc_post_res_coeffs" + sfx)
         ws_c = getattr(mhc, "mhc_coeffs" + sfx + "_workspace_size")(B, n, C)
         ws_f = getattr(mhc, "mhc_post_res_coeffs" + sfx + "_workspace_size")(B, n, C)
-        if not fp8:
-            self.fused_pre = mhc.mhc_post_res_coeffs_pre
-            ws_f = max(ws_f, mhc.mhc_post_res_coeffs_pre_workspace_size(B, n, C))
+        self.fused_pre = getattr(mhc, "mhc_post_res_coeffs_pre" + sfx)
+        ws_f = max(ws_f, getattr(mhc, "mhc_post_res_coeffs_pre" + sfx + "_workspace_size")(B, n, C))
         dev, st = "cuda", torch.uint8 if fp8 else torch.bfloat16
         self.X = [inp["X"], torch.empty_like(inp["X"])]
         self.H = [torch.empty(B, N, device=dev) for _ in range(2)]
@@ -351,7 +350,10 @@ def _variants(args, mhc, torch, synth, stream, ev):
         B, n, C, 1, pf.time_loop(pf.layer, args.steps, args.warmup),
         pf.time_loop(pf.three, args.steps, args.warmup),
         pf.per_call(pf.layer, ("mhc_pre_fp8", "mhc_post_res_coeffs_fp8"), args.steps),
-        pf.per_call(pf.three, ("mhc_coeffs_fp8", "mhc_pre_fp8", "mhc_post_res_fp8"), args.steps))
+        pf.per_call(pf.three, ("mhc_coeffs_fp8", "mhc_pre_fp8", "mhc_post_res_fp8"), args.steps),
+        ms_onepass=pf.time_loop(pf.onepass, args.steps, args.warmup))
+    fp8_line["onepass_route"] = ("one pass" if mhc.mhc_post_res_coeffs_pre_fp8_one_pass(B, n, C)
+                                 else "mhc_post_res_coeffs_fp8 + mhc_pre_fp8")
     del pf, fp8_inp
 
     # ---- the other workloads (parity-test shapes), both dtypes: mean over 50
@@ -369,10 +371,11 @@ def _variants(args, mhc, torch, synth, stream, ev):
             pw = Pipeline(mhc, torch, winp, fp8=fp8)
             res[dname] = _summary(wcfg["B"], wcfg["n"], wcfg["C"], 1 if fp8 else 2,
                                   pw.time_loop(pw.layer, wsteps, 10), pw.time_loop(pw.three, wsteps, 10),
-                                  ms_onepass=None if fp8 else pw.time_loop(pw.onepass, wsteps, 10))
-            if not fp8:
-                res[dname]["onepass_route"] = ("one pass" if mhc.mhc_post_res_coeffs_pre_one_pass(
-                    wcfg["B"], wcfg["n"], wcfg["C"]) else "mhc_post_res_coeffs + mhc_pre")
+                                  ms_onepass=pw.time_loop(pw.onepass, wsteps, 10))
+            sfx = "_fp8" if fp8 else ""
+            one = getattr(mhc, "mhc_post_res_coeffs_pre" + sfx + "_one_pass")(wcfg["B"], wcfg["n"], wcfg["C"])
+            res[dname]["onepass_route"] = ("one pass" if one else
+                                           f"mhc_post_res_coeffs{sfx} + mhc_pre{sfx}")
             if wname == "decode":
                 scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
                 cold = []
@@ -380,7 +383,7 @@ def _variants(args, mhc, torch, synth, stream, ev):
                     scratch.fill_(1)
                     e0, e1 = ev(), ev()
                     e0.record(stream)
-                    (pw.layer if fp8 else pw.onepass)()
+                    pw.onepass()
                     e1.record(stream)
                     torch.cuda.synchronize()
                     cold.append(e0.elapsed_time(e1))

@@ -187,9 +187,8 @@ int mhc_post_res_coeffs(int64_t B, int32_t n, int64_t C,
  * layer, its layer F and this call: the residual stream is read once and
  * written once per layer (X_t and F_out in, X_next and F_pre_next out).
  *
- * Where the shape allows (n <= 4, B above 256, C % 32 == 0 and at most
- * 2*floor(64/(n+1)) 512-channel steps per row, i.e. C <= 12288 at n = 4)
- * this runs as one persistent pass whose workgroups exchange each row's
+ * Where the shape allows (n <= 4, B above 256, C % 32 == 0 and at most 16
+ * 512-channel steps per row, i.e. C <= 8192) this runs as one persistent pass whose workgroups exchange each row's
  * partial sums through the workspace; mhc_post_res_coeffs_pre_one_pass()
  * reports whether a shape takes that route.  That pass needs its whole grid
  * (one workgroup per compute unit) resident at once: it shares the device
@@ -243,9 +242,9 @@ int32_t mhc_post_res_coeffs_pre_one_pass(int64_t B, int32_t n, int64_t C);
 
 size_t mhc_coeffs_fp8_workspace_size(int64_t B, int32_t n, int64_t C);
 
-/* Steps (1)-(3) on an E4M3 X_t [B, n*C]; as mhc_coeffs otherwise.  Above 256
- * rows the product runs in the persistent kernel of mhc_post_res_coeffs
- * (product only), then the combine kernel. */
+/* Steps (1)-(3) on an E4M3 X_t [B, n*C]; as mhc_coeffs otherwise (up to 256
+ * rows one kernel, above that the split-K product with X staged through LDS,
+ * then the combine kernel). */
 int mhc_coeffs_fp8(int64_t B, int32_t n, int64_t C,
                    const void *X_t, const void *phi,
                    float alpha_pre, float alpha_post, float alpha_res,
@@ -274,6 +273,35 @@ int mhc_post_res_coeffs_fp8(int64_t B, int32_t n, int64_t C,
                             const float *b_pre, const float *b_post, const float *b_res,
                             float *logits_next, float *r_next, float *H_next,
                             void *workspace, size_t workspace_bytes, void *stream);
+
+/* mhc_post_res_coeffs_pre on the E4M3 residual stream ([mHC-cutile] section
+ * 2.5 for F_pre, sections 2.1-2.4 for the coefficients it needs): everything
+ * mhc_post_res_coeffs_fp8 returns, plus
+ *
+ *   F_pre_next   out E4M3 [B, C] = exactly what mhc_pre_fp8(X_next, H_next)
+ *                writes (bitwise).
+ *
+ * Route, residency caveat and give-up behaviour (NaN, here the E4M3 code
+ * 0x7F, in the affected F_pre_next bytes) as for mhc_post_res_coeffs_pre; the
+ * one-pass route also needs the fused E4M3 route (the default at n <= 4;
+ * MHC_FUSED_FP8=0 turns it off), else the call runs mhc_post_res_coeffs_fp8
+ * followed by mhc_pre_fp8 on X_next, with the same results.  Requires
+ * C % 32 == 0; F_pre_next 16-byte aligned and not overlapping any other
+ * argument; the workspace must hold mhc_post_res_coeffs_pre_fp8_workspace_size
+ * bytes. */
+size_t mhc_post_res_coeffs_pre_fp8_workspace_size(int64_t B, int32_t n, int64_t C);
+
+int mhc_post_res_coeffs_pre_fp8(int64_t B, int32_t n, int64_t C,
+                                const void *X_t, const void *F_out, const float *H,
+                                void *X_next, const void *phi_next,
+                                float alpha_pre, float alpha_post, float alpha_res,
+                                const float *b_pre, const float *b_post, const float *b_res,
+                                float *logits_next, float *r_next, float *H_next,
+                                void *F_pre_next, void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+/* 1 if mhc_post_res_coeffs_pre_fp8 runs this shape as one pass, else 0. */
+int32_t mhc_post_res_coeffs_pre_fp8_one_pass(int64_t B, int32_t n, int64_t C);
 
 /* ------------------------------------------------------------------------
  * fp32 phi variant.

@@ -11,5 +11,6 @@ from .binding import (  # noqa: F401
     mhc_post_res_coeffs_fp8_workspace_size, mhc_post_res_coeffs_fp8, mhc_lazy_prenorm_gemm,
     mhc_coeffs_phi32_workspace_size, mhc_coeffs_phi32, mhc_post_res_coeffs_phi32_workspace_size,
     mhc_post_res_coeffs_phi32, mhc_post_res_coeffs_pre_workspace_size, mhc_post_res_coeffs_pre,
-    mhc_post_res_coeffs_pre_one_pass,
+    mhc_post_res_coeffs_pre_one_pass, mhc_post_res_coeffs_pre_fp8_workspace_size,
+    mhc_post_res_coeffs_pre_fp8, mhc_post_res_coeffs_pre_fp8_one_pass,
 )

@@ -27,7 +27,9 @@ EXPORTED = ("mhc_status_string", "mhc_coeffs_workspace_size", "mhc_coeffs_split_
             "mhc_post_res_coeffs_fp8", "mhc_coeffs_phi32_workspace_size", "mhc_coeffs_phi32",
             "mhc_post_res_coeffs_phi32_workspace_size", "mhc_post_res_coeffs_phi32",
             "mhc_lazy_prenorm_gemm", "mhc_post_res_coeffs_pre_workspace_size",
-            "mhc_post_res_coeffs_pre", "mhc_post_res_coeffs_pre_one_pass")
+            "mhc_post_res_coeffs_pre", "mhc_post_res_coeffs_pre_one_pass",
+            "mhc_post_res_coeffs_pre_fp8_workspace_size", "mhc_post_res_coeffs_pre_fp8",
+            "mhc_post_res_coeffs_pre_fp8_one_pass")
 
 _lib = None
 
@@ -92,6 +94,13 @@ def load():
     lib.mhc_post_res_coeffs_pre.restype = ctypes.c_int
     lib.mhc_post_res_coeffs_pre_one_pass.argtypes = [i64, i32, i64]
     lib.mhc_post_res_coeffs_pre_one_pass.restype = i32
+    lib.mhc_post_res_coeffs_pre_fp8_workspace_size.argtypes = [i64, i32, i64]
+    lib.mhc_post_res_coeffs_pre_fp8_workspace_size.restype = sz
+    lib.mhc_post_res_coeffs_pre_fp8.argtypes = [i64, i32, i64, vp, vp, vp, vp, vp, f32, f32, f32,
+                                                vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.mhc_post_res_coeffs_pre_fp8.restype = ctypes.c_int
+    lib.mhc_post_res_coeffs_pre_fp8_one_pass.argtypes = [i64, i32, i64]
+    lib.mhc_post_res_coeffs_pre_fp8_one_pass.restype = i32
     _lib = lib
     return lib
 
@@ -208,6 +217,32 @@ def mhc_post_res_coeffs_pre(B, n, C, X_t, F_out, H, X_next, phi_next, alpha_pre,
                                         int(workspace_bytes), _stream(stream))
     if check:
         _check(st, "mhc_post_res_coeffs_pre")
+    return st
+
+
+def mhc_post_res_coeffs_pre_fp8_workspace_size(B, n, C):
+    return int(load().mhc_post_res_coeffs_pre_fp8_workspace_size(int(B), int(n), int(C)))
+
+
+def mhc_post_res_coeffs_pre_fp8_one_pass(B, n, C):
+    return bool(load().mhc_post_res_coeffs_pre_fp8_one_pass(int(B), int(n), int(C)))
+
+
+def mhc_post_res_coeffs_pre_fp8(B, n, C, X_t, F_out, H, X_next, phi_next, alpha_pre, alpha_post,
+                                alpha_res, b_pre, b_post, b_res, logits_next, r_next, H_next,
+                                F_pre_next, workspace, workspace_bytes=None, stream=None,
+                                check=True):
+    """mhc_post_res_coeffs_pre on the E4M3 residual stream (see include/mhc.h)."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().mhc_post_res_coeffs_pre_fp8(int(B), int(n), int(C), _ptr(X_t), _ptr(F_out), _ptr(H),
+                                            _ptr(X_next), _ptr(phi_next), float(alpha_pre),
+                                            float(alpha_post), float(alpha_res), _ptr(b_pre),
+                                            _ptr(b_post), _ptr(b_res), _ptr(logits_next),
+                                            _ptr(r_next), _ptr(H_next), _ptr(F_pre_next),
+                                            _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if check:
+        _check(st, "mhc_post_res_coeffs_pre_fp8")
     return st
 
 

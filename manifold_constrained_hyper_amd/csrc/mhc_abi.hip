@@ -213,26 +213,26 @@ size_t post_res_coeffs_ws_bytes(int64_t B, int32_t n, int64_t C, Elt e) {
   }
 }
 
-// mhc_post_res_coeffs_pre: the fused kernel's pre-mix mode (one pass that
-// also writes the next layer's F_pre) wherever mhc_post_res_coeffs would run
-// the fused kernel and the mode fits the shape (bf16, n <= 4, at most
-// 2*floor(64/(n+1)) 512-channel steps per row); otherwise mhc_post_res_coeffs
-// followed by mhc_pre on X_next.  MHC_FUSED_PRE=0 forces the latter.
-bool pre_fused(int64_t B, int32_t n, int64_t C) {
+// mhc_post_res_coeffs_pre(_fp8): the fused kernel's pre-mix mode (one pass
+// that also writes the next layer's F_pre) wherever mhc_post_res_coeffs(_fp8)
+// would run the fused kernel and the mode fits the shape (n <= 4, at most 16
+// 512-channel steps per row); otherwise mhc_post_res_coeffs(_fp8) followed by
+// mhc_pre(_fp8) on X_next.  MHC_FUSED_PRE=0 forces the latter.
+bool pre_fused(int64_t B, int32_t n, int64_t C, Elt e) {
+  if (e.phi32) return false;
   if (const char *v = std::getenv("MHC_FUSED_PRE"))
     if (std::strtol(v, nullptr, 10) == 0) return false;
-  return fused_route(B, n, C, Elt{false, false}) == FusedRoute::kFused && mhc::pre_mode_fits(B, n, C);
+  return fused_route(B, n, C, e) == FusedRoute::kFused && mhc::pre_mode_fits(B, n, C);
 }
 
-size_t post_res_coeffs_pre_ws_bytes(int64_t B, int32_t n, int64_t C) {
-  const Elt e{false, false};
+size_t post_res_coeffs_pre_ws_bytes(int64_t B, int32_t n, int64_t C, Elt e) {
   if (check_shape_elt(B, n, C, e) != MHC_OK || B == 0 || C % 32 != 0) return 0;
-  if (pre_fused(B, n, C)) return mhc::plan_post_res_next(B, n, C, true).total_bytes;
+  if (pre_fused(B, n, C, e)) return mhc::plan_post_res_next(B, n, C, true).total_bytes;
   return post_res_coeffs_ws_bytes(B, n, C, e);
 }
 
 // F_pre_next: null for mhc_post_res_coeffs(_fp8, _phi32); the output of
-// mhc_post_res_coeffs_pre (bf16 only) otherwise.
+// mhc_post_res_coeffs_pre(_fp8) otherwise.
 int post_res_coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t,
                          const void *F_out, const float *H, void *X_next, const void *phi_next,
                          float alpha_pre, float alpha_post, float alpha_res, const float *b_pre,
@@ -252,9 +252,9 @@ int post_res_coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t
       (with_pre && !aligned(F_pre_next, 16)))
     return MHC_ERR_UNSUPPORTED;
   const FusedRoute route = fused_route(B, n, C, e);
-  const bool one_pass = with_pre && pre_fused(B, n, C);
+  const bool one_pass = with_pre && pre_fused(B, n, C, e);
   const mhc::FusedPlan plan = mhc::plan_post_res_next(B, n, C, one_pass, e.fp8);
-  const size_t ws_need = with_pre ? post_res_coeffs_pre_ws_bytes(B, n, C) : post_res_coeffs_ws_bytes(B, n, C, e);
+  const size_t ws_need = with_pre ? post_res_coeffs_pre_ws_bytes(B, n, C, e) : post_res_coeffs_ws_bytes(B, n, C, e);
   const int64_t N = ncoef(n), K = (int64_t)n * C;
   const size_t eb = e.bytes();
   const Span in[] = {span(X_t, (size_t)B * K * eb), span(F_out, (size_t)B * C * eb),
@@ -276,8 +276,8 @@ int post_res_coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (one_pass) {
     const mhc::PreOut po{F_pre_next, b_pre, alpha_pre};
-    st = from_hip(mhc::launch_post_res_next(plan, n, mhc::kFusedApplyPreBf16, B, C, X_t, F_out, H,
-                                            X_next, phi_next, workspace, s, &po));
+    st = from_hip(mhc::launch_post_res_next(plan, n, e.fp8 ? mhc::kFusedApplyPreFp8 : mhc::kFusedApplyPreBf16,
+                                            B, C, X_t, F_out, H, X_next, phi_next, workspace, s, &po));
     if (st != MHC_OK) return st;
     return from_hip(mhc::launch_coeff_sinkhorn(n, B, C, plan.split, static_cast<const float *>(workspace),
                                                alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res,
@@ -289,7 +289,8 @@ int post_res_coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t
                               alpha_res, b_pre, b_post, b_res, logits_next, r_next, H_next,
                               workspace, workspace_bytes, stream);
     if (st != MHC_OK) return st;
-    return from_hip(mhc::launch_pre(n, B, C, X_next, H_next, F_pre_next, s));
+    return from_hip(e.fp8 ? mhc::launch_pre_fp8(n, B, C, X_next, H_next, F_pre_next, s)
+                          : mhc::launch_pre(n, B, C, X_next, H_next, F_pre_next, s));
   }
   if (route != FusedRoute::kFused) {
     st = from_hip(e.fp8 ? mhc::launch_post_res_fp8(n, B, C, X_t, F_out, H, X_next, s)
@@ -380,7 +381,7 @@ int mhc_post_res_coeffs(int64_t B, int32_t n, int64_t C, const void *X_t, const 
 }
 
 size_t mhc_post_res_coeffs_pre_workspace_size(int64_t B, int32_t n, int64_t C) {
-  return post_res_coeffs_pre_ws_bytes(B, n, C);
+  return post_res_coeffs_pre_ws_bytes(B, n, C, kBf16);
 }
 
 int mhc_post_res_coeffs_pre(int64_t B, int32_t n, int64_t C, const void *X_t, const void *F_out,
@@ -396,7 +397,7 @@ int mhc_post_res_coeffs_pre(int64_t B, int32_t n, int64_t C, const void *X_t, co
 
 int32_t mhc_post_res_coeffs_pre_one_pass(int64_t B, int32_t n, int64_t C) {
   if (check_shape(B, n, C) != MHC_OK || B == 0 || C % 32 != 0) return 0;
-  return pre_fused(B, n, C) ? 1 : 0;
+  return pre_fused(B, n, C, kBf16) ? 1 : 0;
 }
 
 size_t mhc_coeffs_fp8_workspace_size(int64_t B, int32_t n, int64_t C) {
@@ -435,6 +436,27 @@ int mhc_post_res_coeffs_fp8(int64_t B, int32_t n, int64_t C, const void *X_t, co
   return post_res_coeffs_impl(kFp8, B, n, C, X_t, F_out, H, X_next, phi_next, alpha_pre,
                               alpha_post, alpha_res, b_pre, b_post, b_res, logits_next, r_next,
                               H_next, workspace, workspace_bytes, stream);
+}
+
+size_t mhc_post_res_coeffs_pre_fp8_workspace_size(int64_t B, int32_t n, int64_t C) {
+  return post_res_coeffs_pre_ws_bytes(B, n, C, kFp8);
+}
+
+int mhc_post_res_coeffs_pre_fp8(int64_t B, int32_t n, int64_t C, const void *X_t,
+                                const void *F_out, const float *H, void *X_next,
+                                const void *phi_next, float alpha_pre, float alpha_post,
+                                float alpha_res, const float *b_pre, const float *b_post,
+                                const float *b_res, float *logits_next, float *r_next,
+                                float *H_next, void *F_pre_next, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  return post_res_coeffs_impl(kFp8, B, n, C, X_t, F_out, H, X_next, phi_next, alpha_pre,
+                              alpha_post, alpha_res, b_pre, b_post, b_res, logits_next, r_next,
+                              H_next, workspace, workspace_bytes, stream, true, F_pre_next);
+}
+
+int32_t mhc_post_res_coeffs_pre_fp8_one_pass(int64_t B, int32_t n, int64_t C) {
+  if (check_shape_elt(B, n, C, kFp8) != MHC_OK || B == 0 || C % 32 != 0) return 0;
+  return pre_fused(B, n, C, kFp8) ? 1 : 0;
 }
 
 size_t mhc_coeffs_phi32_workspace_size(int64_t B, int32_t n, int64_t C) {

@@ -80,13 +80,15 @@ enum FusedMode : int {
   kFusedCoeffsFp8 = 2,     // X . phi only, X in E4M3
   kFusedCoeffsBf16 = 3,    // X . phi only, X in bf16
   kFusedApplyPreBf16 = 4,  // kFusedApplyBf16, plus the next layer's F_pre (n <= 4)
+  kFusedApplyPreFp8 = 5,   // kFusedApplyFp8, plus the next layer's F_pre in E4M3 (n <= 4)
 };
+constexpr bool is_pre_mode(int mode) { return mode == kFusedApplyPreBf16 || mode == kFusedApplyPreFp8; }
 // Kernel-side arguments of the pre-mix mode.  Its stores of partials,
 // records and F_pre, and its record loads, go through buffer resources, so a
 // store without a target is given an offset past the buffer and dropped by
 // the hardware: no dummy area, no branch, no memory traffic.
 struct PreArgs {
-  uint16_t *F_pre;                // bf16 [B, C]
+  void *F_pre;                    // bf16 or E4M3 [B, C]
   uint32_t *rec;                  // records [B, split, PW]: fp32 bits, 0 = not yet written
   uint32_t rec_bytes;             // split * B * PW * 4 (< 2^31); PW = n+1 rounded up to even
   uint32_t partial_bytes;         // split * B * (N+1) * 4 (< 2^31)
@@ -99,8 +101,8 @@ struct PreArgs {
 // (a multiple of S workgroups) that fits the device, and partials and
 // records addressable by 32-bit buffer offsets.
 bool pre_mode_fits(int64_t B, int n, int64_t C);
-// pre_out: F_pre (bf16 [B, C]) and the next layer's b_pre / alpha_pre for the
-// pre-mix mode, else null.
+// pre_out: F_pre (bf16 or E4M3 [B, C], the element type of the mode) and the
+// next layer's b_pre / alpha_pre for the pre-mix modes, else null.
 struct PreOut {
   void *F_pre;
   const float *b_pre;

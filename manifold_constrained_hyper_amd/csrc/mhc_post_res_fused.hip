@@ -51,7 +51,8 @@
 // what the stand-alone apply writes, and the product consumes those rounded
 // values, exactly what a separate product pass would read back.
 //
-// Pre-mix mode (kFusedApplyPreBf16, n <= 4, mhc_post_res_coeffs_pre).  The
+// Pre-mix mode (kFusedApplyPreBf16 / kFusedApplyPreFp8, n <= 4,
+// mhc_post_res_coeffs_pre / mhc_post_res_coeffs_pre_fp8).  The
 // next layer also needs F_pre = sum_i H_pre[i] X_{t+1}[i] (section 2.5,
 // first step), and H_pre needs the whole row's product (sections 2.1-2.4),
 // which S workgroups compute slice by slice.  This mode forms F_pre in the
@@ -156,9 +157,11 @@ struct Step {
 // What the kernel reads, writes and multiplies (FusedMode, mhc_launch.h).
 template <int MODE>
 struct FusedIO {
-  static constexpr bool FP8 = MODE == kFusedApplyFp8 || MODE == kFusedCoeffsFp8;
-  static constexpr bool PRE = MODE == kFusedApplyPreBf16;
-  static constexpr bool APPLY = MODE == kFusedApplyBf16 || MODE == kFusedApplyFp8 || PRE;
+  static constexpr bool FP8 = MODE == kFusedApplyFp8 || MODE == kFusedCoeffsFp8 || MODE == kFusedApplyPreFp8;
+  static constexpr bool PRE = is_pre_mode(MODE);
+  static constexpr bool APPLY_BF16 = MODE == kFusedApplyBf16 || MODE == kFusedApplyPreBf16;
+  static constexpr bool APPLY_FP8 = MODE == kFusedApplyFp8 || MODE == kFusedApplyPreFp8;
+  static constexpr bool APPLY = APPLY_BF16 || APPLY_FP8;
   static constexpr int EB = FP8 ? 1 : 2;  // bytes per element
   using vec = typename std::conditional<FP8, u32x2, u32x4>::type;  // 8 elements per lane
 };
@@ -398,7 +401,10 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
     u32x4 xv[NS];
 #pragma unroll
     for (int i = 0; i < NS; ++i) xv[i] = *reinterpret_cast<const u32x4 *>(src + i * (kStepCh * 2) + slot);
-    u32x4 o;
+    // fp32 FMA chain over the streams in stream order from zero, one rounding
+    // at the end: pre_kernel's arithmetic (pre_fp8_kernel's for E4M3, whose
+    // tile values are the E4M3 results widened exactly).
+    float a[8];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       float a0 = 0.f, a1 = 0.f;
@@ -407,17 +413,28 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
         a0 = fmaf(hp[j], bf16_lo(xv[j][w]), a0);
         a1 = fmaf(hp[j], bf16_hi(xv[j][w]), a1);
       }
-      o[w] = pack_bf16x2(a0, a1);
+      a[2 * w] = a0;
+      a[2 * w + 1] = a1;
     }
-    if (poison) o = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
     // The row's own buffer; a row without a target (past B, or before the
-    // first step) gets an empty one, so the store is dropped.
+    // first step) gets an empty one, so the store is dropped.  Stores use
+    // the default cache policy: measured 412-417 against 439-442 us per call
+    // with the non-temporal bit (bf16, n=4, C=7168, B=16384).
     const bool tgt = real && row < B;  // wave-uniform
     const __amdgpu_buffer_rsrc_t frow = __builtin_amdgcn_make_buffer_rsrc(
-        pa.F_pre + (size_t)min(row, B - 1) * C, (short)0, tgt ? C * 2 : 0, kRsrcWord3);
-    // A plain store (default cache policy): measured 412-417 against 439-442
-    // us per call with the non-temporal bit at n=4, C=7168, B=16384.
-    __builtin_amdgcn_raw_buffer_store_b128(o, frow, (uint32_t)cst * 2u, 0, 0);
+        static_cast<uint8_t *>(pa.F_pre) + (size_t)min(row, B - 1) * C * IO::EB, (short)0,
+        tgt ? C * IO::EB : 0, kRsrcWord3);
+    if constexpr (IO::FP8) {
+      u32x2 o{pack_fp8x4(a[0], a[1], a[2], a[3]), pack_fp8x4(a[4], a[5], a[6], a[7])};
+      if (poison) o = u32x2{0x7f7f7f7fu, 0x7f7f7f7fu};  // E4M3 NaN
+      __builtin_amdgcn_raw_buffer_store_b64(o, frow, (uint32_t)cst, 0, 0);
+    } else {
+      u32x4 o;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) o[w] = pack_bf16x2(a[2 * w], a[2 * w + 1]);
+      if (poison) o = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+      __builtin_amdgcn_raw_buffer_store_b128(o, frow, (uint32_t)cst * 2u, 0, 0);
+    }
   };
 
   // One step on the loads in (xv, fv, hv); refills them with step t_pref.
@@ -447,7 +464,7 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
       return __builtin_bit_cast(float, __builtin_amdgcn_readlane((int)hv[k / 64], k % 64));
     };
     vec out[NS];
-    if constexpr (MODE == kFusedApplyBf16 || IO::PRE) {
+    if constexpr (IO::APPLY_BF16) {
       if constexpr (NS <= 4) {
         float hpost[NS], hres[NS][NS];
 #pragma unroll
@@ -498,7 +515,7 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
           }
         }
       }
-    } else if constexpr (MODE == kFusedApplyFp8) {
+    } else if constexpr (IO::APPLY_FP8) {
       // E4M3: each 8-byte vector is two words of four channels; the same FMA
       // chain per element as post_res_fp8_kernel, then the E4M3 result is
       // widened (exactly) for the tile.
@@ -563,8 +580,8 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
     // E4M3 values widen exactly.  Taken at the LDS write, before the refill
     // overwrites xv, so no second copy is held across the stores.
     auto tile_vec = [&](int i) -> u32x4 {
-      if constexpr (MODE == kFusedApplyBf16 || IO::PRE) return out[i];
-      else if constexpr (MODE == kFusedApplyFp8) return fp8x8_to_bf16(out[i]);
+      if constexpr (IO::APPLY_BF16) return out[i];
+      else if constexpr (IO::APPLY_FP8) return fp8x8_to_bf16(out[i]);
       else if constexpr (MODE == kFusedCoeffsFp8) return fp8x8_to_bf16(xv[i]);
       else return xv[i];
     };
@@ -746,7 +763,7 @@ template <int NS, int MODE>
 hipError_t launch_layout(bool fixed, int64_t B, int64_t C, int spu, int split, int G, const void *X,
                          const void *F, const float *H, void *Y, const void *phip, float *ws,
                          float *dummy, const PreArgs &pa, hipStream_t st) {
-  if constexpr (MODE == kFusedApplyPreBf16) {
+  if constexpr (is_pre_mode(MODE)) {
     if (!fixed) return hipErrorInvalidValue;
     return launch_post_res_next_typed<NS, MODE, true>(B, C, spu, split, G, X, F, H, Y, phip, ws, dummy, pa, st);
   } else if constexpr (NS >= 8) {
@@ -767,7 +784,7 @@ hipError_t launch_mode(int n, bool fixed, int64_t B, int64_t C, int spu, int spl
     case 2: return launch_layout<2, MODE>(fixed, B, C, spu, split, G, X, F, H, Y, phip, ws, dummy, pa, st);
     case 4: return launch_layout<4, MODE>(fixed, B, C, spu, split, G, X, F, H, Y, phip, ws, dummy, pa, st);
     case 8:
-      if constexpr (MODE == kFusedApplyPreBf16) return hipErrorInvalidValue;  // n <= 4 only
+      if constexpr (is_pre_mode(MODE)) return hipErrorInvalidValue;  // n <= 4 only
       else return launch_layout<8, MODE>(fixed, B, C, spu, split, G, X, F, H, Y, phip, ws, dummy, pa, st);
     default: return hipErrorInvalidValue;
   }
@@ -849,7 +866,7 @@ hipError_t launch_post_res_next(const FusedPlan &p, int n, int mode, int64_t B, 
                                 const void *X, const void *F, const float *H, void *Y,
                                 const void *phi_next, void *ws_base, hipStream_t st,
                                 const PreOut *pre_out) {
-  const bool pre = mode == kFusedApplyPreBf16;
+  const bool pre = is_pre_mode(mode);
   if (pre != p.pre || (pre && !pre_out)) return hipErrorInvalidValue;
   char *base = static_cast<char *>(ws_base);
   void *phip = base + p.phip_offset;
@@ -873,7 +890,7 @@ hipError_t launch_post_res_next(const FusedPlan &p, int n, int mode, int64_t B, 
       const long v = std::strtol(env, nullptr, 10);
       if (v >= 1 && v < cap) cap = (int)v;
     }
-    pa.F_pre = static_cast<uint16_t *>(pre_out->F_pre);
+    pa.F_pre = pre_out->F_pre;
     pa.rec = reinterpret_cast<uint32_t *>(base + p.rec_offset);
     pa.rec_bytes = (uint32_t)p.rec_bytes;
     pa.partial_bytes = (uint32_t)p.partial_bytes;
@@ -897,6 +914,7 @@ hipError_t launch_post_res_next(const FusedPlan &p, int n, int mode, int64_t B, 
     case kFusedCoeffsFp8: return launch_mode<kFusedCoeffsFp8>(n, p.fixed, B, C, spu, p.split, G, X, F, H, Y, phip, ws, dummy, pa, st);
     case kFusedCoeffsBf16: return launch_mode<kFusedCoeffsBf16>(n, p.fixed, B, C, spu, p.split, G, X, F, H, Y, phip, ws, dummy, pa, st);
     case kFusedApplyPreBf16: return launch_mode<kFusedApplyPreBf16>(n, p.fixed, B, C, spu, p.split, G, X, F, H, Y, phip, ws, dummy, pa, st);
+    case kFusedApplyPreFp8: return launch_mode<kFusedApplyPreFp8>(n, p.fixed, B, C, spu, p.split, G, X, F, H, Y, phip, ws, dummy, pa, st);
     default: return hipErrorInvalidValue;
   }
 }

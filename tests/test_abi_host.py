@@ -189,6 +189,59 @@ def test_fused_pre_route_and_workspace(monkeypatch):
     assert mhc.mhc_post_res_coeffs_pre_workspace_size(B, n, C) == mhc.mhc_post_res_coeffs_workspace_size(B, n, C)
 
 
+def _fused_pre_fp8(B=16, n=4, C=64, ws_bytes=None, **over):
+    names = ["X", "F", "H", "Y", "phi", "bp", "bq", "br", "logits", "r", "Hn", "Fp", "ws"]
+    p = dict(zip(names, _addrs(len(names))))
+    p.update(over)
+    if ws_bytes is None:
+        ws_bytes = max(mhc.mhc_post_res_coeffs_pre_fp8_workspace_size(B, n, C), 16)
+    return mhc.mhc_post_res_coeffs_pre_fp8(B, n, C, p["X"], p["F"], p["H"], p["Y"], p["phi"], 0.01,
+                                           0.01, 0.01, p["bp"], p["bq"], p["br"], p["logits"], p["r"],
+                                           p["Hn"], p["Fp"], p["ws"], ws_bytes, stream=0, check=False)
+
+
+def test_fused_pre_fp8_validation():
+    """The E4M3 one-pass call: the bf16 call's rules with one-byte stream
+    elements (overlaps in bytes)."""
+    assert _fused_pre_fp8(B=0) == mhc.MHC_OK
+    assert _fused_pre_fp8(B=0, X=None, Fp=None, ws=None) == mhc.MHC_OK
+    assert _fused_pre_fp8(C=48) == mhc.MHC_ERR_UNSUPPORTED             # C % 16 == 0 but not % 32
+    assert mhc.mhc_post_res_coeffs_pre_fp8_workspace_size(16, 4, 48) == 0
+    assert _fused_pre_fp8(n=3) == mhc.MHC_ERR_UNSUPPORTED
+    assert _fused_pre_fp8(B=-2) == mhc.MHC_ERR_INVALID_ARG
+    for k in ("X", "F", "H", "Y", "phi", "bp", "bq", "br", "logits", "r", "Hn", "Fp", "ws"):
+        assert _fused_pre_fp8(**{k: None}) == mhc.MHC_ERR_INVALID_ARG, k
+    # F_pre (16 * 64 bytes) starting 16 bytes before the end of X_t's
+    # 16 * 4 * 64 bytes overlaps it
+    assert _fused_pre_fp8(Fp=A + 16 * 4 * 64 - 16) == mhc.MHC_ERR_INVALID_ARG
+    assert _fused_pre_fp8(Fp=A + 3 * STEP + 16 * 4 * 64 - 16) == mhc.MHC_ERR_INVALID_ARG  # inside X_next
+    assert _fused_pre_fp8(ws=A + 11 * STEP + 16 * 64 - 16) == mhc.MHC_ERR_INVALID_ARG     # overlaps F_pre
+    assert _fused_pre_fp8(Fp=A + 11 * STEP + 8) == mhc.MHC_ERR_UNSUPPORTED                 # alignment
+    need = mhc.mhc_post_res_coeffs_pre_fp8_workspace_size(16, 4, 64)
+    assert need > 0 and _fused_pre_fp8(ws_bytes=need - 1) == mhc.MHC_ERR_WORKSPACE
+
+
+def test_fused_pre_fp8_route_and_workspace(monkeypatch):
+    for k in ("MHC_FUSED_PRE", "MHC_SMALL_MAX_B", "MHC_FUSED_FP8", "MHC_FUSED_FIXED"):
+        monkeypatch.delenv(k, raising=False)
+    one = mhc.mhc_post_res_coeffs_pre_fp8_one_pass
+    assert one(16384, 4, 7168) and one(4096, 4, 4096) and one(1000, 2, 4096) and one(300, 1, 1024)
+    assert not one(64, 4, 7168)          # small B: the two calls
+    assert not one(8192, 8, 4096)        # n = 8
+    assert not one(4096, 4, 8704)        # 17 steps of 512 channels per row
+    assert not one(0, 4, 7168) and not one(16, 4, 48)
+    # one pass: the bf16 call's workspace (partials, packed phi, records)
+    assert mhc.mhc_post_res_coeffs_pre_fp8_workspace_size(16384, 4, 7168) == \
+        mhc.mhc_post_res_coeffs_pre_workspace_size(16384, 4, 7168)
+    # two calls: what mhc_post_res_coeffs_fp8 needs
+    assert mhc.mhc_post_res_coeffs_pre_fp8_workspace_size(8192, 8, 4096) == \
+        mhc.mhc_post_res_coeffs_fp8_workspace_size(8192, 8, 4096)
+    monkeypatch.setenv("MHC_FUSED_FP8", "0")       # E4M3 fused call as apply + product
+    assert not one(16384, 4, 7168)
+    assert mhc.mhc_post_res_coeffs_pre_fp8_workspace_size(16384, 4, 7168) == \
+        mhc.mhc_post_res_coeffs_fp8_workspace_size(16384, 4, 7168)
+
+
 def test_binding_raises_on_error_status():
     with pytest.raises(mhc.MhcError) as ei:
         mhc.mhc_pre(16, 3, 64, *_addrs(3), stream=0)
