@@ -9,15 +9,17 @@
 //   sections 3.2, 3.3, 5.2, 5.3  these steps are tiny per row, so they are
 //                fused after the split-K reduction in a single launch.
 //
-// Layout: a workgroup of 256 lanes owns RB rows (RB = 256 / n, or 1 row when
-// B is small); n consecutive lanes serve one row, lane i holding row i of
-// that row's n x n res matrix.
+// Layout: a workgroup owns RB rows (RB = 256 / n, or 1 row when B is small);
+// in phase 2, n consecutive lanes serve one row, lane i holding row i of that
+// row's n x n res matrix.
 //   phase 1  lanes sum the S partial slices [S, B, N+1] in a fixed order
-//            (bitwise deterministic).  With RB = 256 / n every lane owns a few
-//            elements of the block and adds all slices in order 0..S-1; for
-//            each slice the workgroup's rows are one contiguous run, so the
-//            loads coalesce, and all loads of a batch of slices are issued
-//            before they are added.  With one row per workgroup (small B,
+//            (bitwise deterministic).  With RB = 256 / n the workgroup has
+//            1024 lanes (16 waves: enough loads in flight per CU to stream
+//            the partials), every lane owns one to three elements of the
+//            block and adds all slices in order 0..S-1; for each slice the
+//            workgroup's rows are one contiguous run, so the loads coalesce,
+//            and all loads of a batch of slices are issued before they are
+//            added.  With one row per workgroup (small B,
 //            typically many slices) the 256 lanes form G = 256 / (N+1) groups;
 //            group g adds slices g, g+G, g+2G, ... in order and the G group
 //            sums are then added in group order.  Sums go to LDS and the raw
@@ -39,8 +41,10 @@ namespace {
 
 constexpr int64_t kOneRowMaxB = 512;  // up to this many rows, one row per workgroup
 
+constexpr int kMultiRowThreads = 1024;  // lanes per workgroup of the multi-row layout
+
 template <int NS, bool ONE_ROW, bool TREE = false>
-__global__ __launch_bounds__(256) void coeff_sinkhorn_kernel(
+__global__ __launch_bounds__(ONE_ROW ? 256 : kMultiRowThreads) void coeff_sinkhorn_kernel(
     const float *__restrict__ ws, int split, int B, float inv_k, float alpha_pre,
     float alpha_post, float alpha_res, const float *__restrict__ b_pre,
     const float *__restrict__ b_post, const float *__restrict__ b_res,
@@ -85,7 +89,8 @@ __global__ __launch_bounds__(256) void coeff_sinkhorn_kernel(
     // Every thread owns EPT elements of the workgroup's [rows, N+1] block and
     // issues the loads of SB slices for all of them before adding, so a
     // thread has up to SB*EPT independent loads in flight.
-    constexpr int EPT = (R * NP + 255) / 256;
+    constexpr int TH = kMultiRowThreads;
+    constexpr int EPT = (R * NP + TH - 1) / TH;
     constexpr int SB = 4;
     const size_t slice = (size_t)B * NP;
     const float *base = ws + (size_t)row0 * NP;
@@ -94,13 +99,18 @@ __global__ __launch_bounds__(256) void coeff_sinkhorn_kernel(
 #pragma unroll
     for (int q = 0; q < EPT; ++q) acc[q] = 0.f;
     if constexpr (TREE) {
+      // Slots past S are zero (no load); the tree is the same for any S.
 #pragma unroll
       for (int q = 0; q < EPT; ++q) {
-        const int e = tid + q * 256;
+        const int e = tid + q * TH;
         float v[16];
 #pragma unroll
-        for (int sb = 0; sb < 16; ++sb)
-          v[sb] = (sb < split && e < nel) ? base[(size_t)min(sb, split - 1) * slice + min(e, nel - 1)] : 0.f;
+        for (int sb = 0; sb < 16; ++sb) v[sb] = 0.f;
+        if (e < nel) {
+#pragma unroll
+          for (int sb = 0; sb < 16; ++sb)
+            if (sb < split) v[sb] = base[(size_t)sb * slice + e];
+        }
         acc[q] = tree16_sum_serial(v);
       }
     }
@@ -110,7 +120,7 @@ __global__ __launch_bounds__(256) void coeff_sinkhorn_kernel(
       for (int sb = 0; sb < SB; ++sb)
 #pragma unroll
         for (int q = 0; q < EPT; ++q) {
-          const int e = tid + q * 256;
+          const int e = tid + q * TH;
           v[sb][q] = (s0 + sb < split && e < nel) ? base[(size_t)(s0 + sb) * slice + e] : 0.f;
         }
 #pragma unroll
@@ -121,7 +131,7 @@ __global__ __launch_bounds__(256) void coeff_sinkhorn_kernel(
     }
 #pragma unroll
     for (int q = 0; q < EPT; ++q) {
-      const int e = tid + q * 256;
+      const int e = tid + q * TH;
       if (e < nel) {
         sums[e] = acc[q];
         const int rr = e / NP, cc = e - rr * NP;
@@ -144,7 +154,7 @@ void launch_n(int64_t B, int64_t C, int split, const float *ws, float ap, float 
   const float inv_k = (float)(1.0 / (double)(NS * C));
   if (tree) {
     constexpr int R = 256 / NS;
-    coeff_sinkhorn_kernel<NS, false, true><<<dim3((uint32_t)((B + R - 1) / R)), 256, 0, st>>>(
+    coeff_sinkhorn_kernel<NS, false, true><<<dim3((uint32_t)((B + R - 1) / R)), kMultiRowThreads, 0, st>>>(
         ws, split, (int)B, inv_k, ap, aq, ar, bp, bq, br, logits, r, H);
     return;
   }
@@ -155,7 +165,7 @@ void launch_n(int64_t B, int64_t C, int split, const float *ws, float ap, float 
         ws, split, (int)B, inv_k, ap, aq, ar, bp, bq, br, logits, r, H);
   } else {
     constexpr int R = 256 / NS;
-    coeff_sinkhorn_kernel<NS, false><<<dim3((uint32_t)((B + R - 1) / R)), 256, 0, st>>>(
+    coeff_sinkhorn_kernel<NS, false><<<dim3((uint32_t)((B + R - 1) / R)), kMultiRowThreads, 0, st>>>(
         ws, split, (int)B, inv_k, ap, aq, ar, bp, bq, br, logits, r, H);
   }
 }
