@@ -392,29 +392,51 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
   // given-up wait send the vector to the dummy area / poison it with NaN.
   // Lanes past the slice take the last in-range vector's tile slot, so they
   // store the owning lane's bytes to the owning lane's address.
-  auto emit = [&](int q, const float (&hp)[NS], bool poison, bool real) {
+  // kv: this lane's own E4M3 apply output of step q (kept in registers for
+  // two steps; E4M3 only).  Every lane that stores reads back exactly what it
+  // wrote to the tile: lanes past the slice computed the owning lane's values
+  // from clamped addresses, and rows past B store nothing.
+  auto emit = [&](int q, const float (&hp)[NS], bool poison, bool real, const vec (&kv)[NS]) {
     const Step sp = step_at(q);
     const int row = sp.row0 + wave;
     const int cst = min(sp.c0 + 8 * lane, sp.c_end - 8);
-    const int slot = (((cst - sp.c0) >> 3) ^ (wave & 15)) * 16;
-    const char *src = tile_of(q) + wave * T::ROW_BYTES;
-    u32x4 xv[NS];
-#pragma unroll
-    for (int i = 0; i < NS; ++i) xv[i] = *reinterpret_cast<const u32x4 *>(src + i * (kStepCh * 2) + slot);
     // fp32 FMA chain over the streams in stream order from zero, one rounding
-    // at the end: pre_kernel's arithmetic (pre_fp8_kernel's for E4M3, whose
-    // tile values are the E4M3 results widened exactly).
+    // at the end: pre_kernel's arithmetic (pre_fp8_kernel's for E4M3).
     float a[8];
+    if constexpr (IO::FP8) {
+      // The E4M3 values themselves, widened to fp32 (exact), two per instruction.
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      float a0 = 0.f, a1 = 0.f;
+      for (int d = 0; d < 2; ++d) {
+        float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        a0 = fmaf(hp[j], bf16_lo(xv[j][w]), a0);
-        a1 = fmaf(hp[j], bf16_hi(xv[j][w]), a1);
+        for (int j = 0; j < NS; ++j) {
+          const f32x2 lo = fp8_lo2(kv[j][d]), hi = fp8_hi2(kv[j][d]);
+          s4[0] = fmaf(hp[j], lo[0], s4[0]);
+          s4[1] = fmaf(hp[j], lo[1], s4[1]);
+          s4[2] = fmaf(hp[j], hi[0], s4[2]);
+          s4[3] = fmaf(hp[j], hi[1], s4[3]);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) a[4 * d + k] = s4[k];
       }
-      a[2 * w] = a0;
-      a[2 * w + 1] = a1;
+    } else {
+      // bf16: the lane's 16-byte slot of its row of the tile.
+      const int slot = (((cst - sp.c0) >> 3) ^ (wave & 15)) * 16;
+      const char *src = tile_of(q) + wave * T::ROW_BYTES;
+      u32x4 xv[NS];
+#pragma unroll
+      for (int i = 0; i < NS; ++i) xv[i] = *reinterpret_cast<const u32x4 *>(src + i * (kStepCh * 2) + slot);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          a0 = fmaf(hp[j], bf16_lo(xv[j][w]), a0);
+          a1 = fmaf(hp[j], bf16_hi(xv[j][w]), a1);
+        }
+        a[2 * w] = a0;
+        a[2 * w + 1] = a1;
+      }
     }
     // The row's own buffer; a row without a target (past B, or before the
     // first step) gets an empty one, so the store is dropped.  Stores use
@@ -438,7 +460,7 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
   };
 
   // One step on the loads in (xv, fv, hv); refills them with step t_pref.
-  auto step = [&](int t, vec (&xv)[NS], vec &fv, uint32_t (&hv)[T::HV], int t_pref) {
+  auto step = [&](int t, vec (&xv)[NS], vec &fv, uint32_t (&hv)[T::HV], int t_pref, vec (&kv)[NS]) {
     const Step sp = step_at(t);
     [[maybe_unused]] u32x2 rv;
     if constexpr (IO::PRE) {
@@ -624,7 +646,11 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
       if (have) poison = rec_wait(rv, t - 2);
       float hp[NS];
       pre_coeffs(rv, hp);
-      emit(have ? t - 2 : 0, hp, poison, have);
+      emit(have ? t - 2 : 0, hp, poison, have, kv);
+      if constexpr (IO::FP8) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i) kv[i] = out[i];  // this step's output, emitted two steps on
+      }
 #pragma unroll
       for (int i = 0; i < NS; ++i)
         *reinterpret_cast<u32x4 *>(my_lds_row + i * (kStepCh * 2) + wslot) =
@@ -688,12 +714,15 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
   };
 
   const int tl = nsteps - 1;
+  // The E4M3 pre-mix mode's own apply outputs of the last two steps, one set
+  // per register set (step t runs on set t & 1: ka for even t, kb for odd).
+  [[maybe_unused]] vec ka[NS], kb[NS];
   if constexpr (NS >= 8) {
     // n = 8: one register set (two would not fit 128 VGPRs).
     vec xa[NS], fa;
     uint32_t ha[T::HV];
     load_set(xa, fa, ha, step_at(0));
-    for (int t = 0; t < nsteps; ++t) step(t, xa, fa, ha, min(t + 1, tl));
+    for (int t = 0; t < nsteps; ++t) step(t, xa, fa, ha, min(t + 1, tl), ka);
   } else {
     // Two register sets: the loads of step t+2 are issued while step t is
     // applied and multiplied, so each wave has two steps of loads in flight.
@@ -705,25 +734,36 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
     load_set(xb, fb, hb, step_at(min(1, tl)));
     int t = 0;
     for (; t + 1 < nsteps; t += 2) {
-      step(t, xa, fa, ha, min(t + 2, tl));
-      step(t + 1, xb, fb, hb, min(t + 3, tl));
+      step(t, xa, fa, ha, min(t + 2, tl), ka);
+      step(t + 1, xb, fb, hb, min(t + 3, tl), kb);
     }
-    if (t < nsteps) step(t, xa, fa, ha, tl);
+    if (t < nsteps) step(t, xa, fa, ha, tl, ka);
   }
   if constexpr (T::SEPARATE) {
     __syncthreads();
     flush(step_at(tl), true);
   }
   if constexpr (IO::PRE) {
-    // The last two steps' F_pre (their tiles are intact: nothing rewrote them).
-#pragma unroll 1
-    for (int q = tl >= 1 ? tl - 1 : tl; q <= tl; ++q) {
+    // The last two steps' F_pre (their tiles are intact: nothing rewrote them;
+    // step q's own outputs are in ka or kb by the parity of q).
+    auto tail = [&](int q, const vec (&kv)[NS]) {
       u32x2 rv;
       rec_load(rv, q);
       const bool poison = rec_wait(rv, q);
       float hp[NS];
       pre_coeffs(rv, hp);
-      emit(q, hp, poison, true);
+      emit(q, hp, poison, true, kv);
+    };
+    if (tl >= 1) {
+      if (tl & 1) {
+        tail(tl - 1, ka);
+        tail(tl, kb);
+      } else {
+        tail(tl - 1, kb);
+        tail(tl, ka);
+      }
+    } else {
+      tail(tl, ka);
     }
   }
 }
