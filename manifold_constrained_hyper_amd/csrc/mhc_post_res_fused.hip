@@ -33,8 +33,10 @@
 //   product  the step's 16*n MFMA k-steps (32 channels of one stream each)
 //            are split over the 16 waves; each reads its A operands (16 rows x
 //            8 channels per lane) from LDS and its B operands from the packed
-//            copy of phi_{t+1} (see mhc_gemm_lds.hip) and accumulates
-//            v_mfma_f32_16x16x32_bf16 plus the Gram block for sum of squares;
+//            copy of phi_{t+1} (see mhc_gemm_lds.hip; in the fixed-slice
+//            layout loaded once per run and held in registers) and
+//            accumulates v_mfma_f32_16x16x32_bf16 plus the Gram block for the
+//            sum of squares;
 //   flush    the 16 waves' accumulators are summed through LDS in wave order
 //            (fixed: deterministic) into the unit's partials fp32 [S, B, N+1]
 //            of the workspace, which the combine kernel turns into the next
@@ -74,7 +76,8 @@
 //     column over 16 slice slots as a balanced tree (the order the combine
 //     kernel uses in this mode, so H_pre comes out bitwise as in H_next),
 //     forms the n gates and emits its row of F_pre from the tile exactly as
-//     pre_kernel would from X_{t+1} in HBM.
+//     pre_kernel would from X_{t+1} in HBM (E4M3: from the lane's own
+//     outputs of that step, kept in registers, as pre_fp8_kernel would).
 // No workgroup waits for one that has not started: a wait at step t+2 needs
 // only records published at the start of step t+1 by workgroups of the same
 // round, and every workgroup publishes before it waits (induction over t;
@@ -388,14 +391,14 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
 #pragma unroll
     for (int i = 0; i < NS; ++i) hp[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gate), 16 * i));
   };
-  // F_pre of this wave's row of step q from its tile; `real` false or a
-  // given-up wait send the vector to the dummy area / poison it with NaN.
-  // Lanes past the slice take the last in-range vector's tile slot, so they
-  // store the owning lane's bytes to the owning lane's address.
-  // kv: this lane's own E4M3 apply output of step q (kept in registers for
-  // two steps; E4M3 only).  Every lane that stores reads back exactly what it
-  // wrote to the tile: lanes past the slice computed the owning lane's values
-  // from clamped addresses, and rows past B store nothing.
+  // F_pre of this wave's row of step q: bf16 from the row's tile, E4M3 from
+  // kv, this lane's own apply output of step q (kept in registers for two
+  // steps).  `real` false (before the first step) or a row past B gives the
+  // store an empty buffer (dropped); a given-up wait poisons the vector with
+  // NaN.  Lanes past the slice take the last in-range vector's tile slot
+  // (bf16) or computed the owning lane's values from clamped addresses
+  // (E4M3), so they store the owning lane's bytes to the owning lane's
+  // address.
   auto emit = [&](int q, const float (&hp)[NS], bool poison, bool real, const vec (&kv)[NS]) {
     const Step sp = step_at(q);
     const int row = sp.row0 + wave;
