@@ -31,7 +31,8 @@ Also reported: the same pipelines on the E4M3 residual stream ("fp8", the
 *_fp8 entry points, one byte per stream element in the byte count) and, for
 the other workloads (tiny, decode, prefill, wide), both dtypes' one-pass,
 two-call and three-call times ("workloads"; decode also cold: the one-pass
-call after a 512 MB write).
+call after a 512 MB write; tiny, decode and prefill also with 16 chained
+one-pass layers captured in a HIP graph and replayed, "graph_*").
 
 Also reported ("phi32_coeffs"): mhc_coeffs_phi32 (fp32 phi) beside mhc_coeffs
 on the same X, decode and headline workloads, mean call time.
@@ -200,6 +201,39 @@ class Pipeline:
         t1.record(self.stream)
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / steps
+
+    def time_graph(self, fn, layers=16, reps=20):
+        """Mean ms per layer when `layers` chained calls of fn, captured once
+        in a HIP graph, are replayed `reps` times back to back (launch
+        overhead removed, as a serving loop would run them)."""
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        old = self.stream
+        with torch.cuda.stream(side):
+            self.stream = side
+            for _ in range(layers):
+                fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            self.stream = torch.cuda.current_stream()
+            for _ in range(layers):
+                fn()
+        self.stream = old
+        torch.cuda.synchronize()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        cur = torch.cuda.current_stream()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(cur)
+        for _ in range(reps):
+            g.replay()
+        t1.record(cur)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / (reps * layers)
 
     def per_call(self, fn, names, steps):
         """Mean ms of each call, from events around every call."""
@@ -372,6 +406,8 @@ def _variants(args, mhc, torch, synth, stream, ev):
             res[dname] = _summary(wcfg["B"], wcfg["n"], wcfg["C"], 1 if fp8 else 2,
                                   pw.time_loop(pw.layer, wsteps, 10), pw.time_loop(pw.three, wsteps, 10),
                                   ms_onepass=pw.time_loop(pw.onepass, wsteps, 10))
+            if wname in ("tiny", "decode", "prefill"):  # launch-bound sizes: the same layers replayed from a graph
+                res[dname]["graph_onepass_us_per_layer"] = round(pw.time_graph(pw.onepass) * 1e3, 2)
             sfx = "_fp8" if fp8 else ""
             one = getattr(mhc, "mhc_post_res_coeffs_pre" + sfx + "_one_pass")(wcfg["B"], wcfg["n"], wcfg["C"])
             res[dname]["onepass_route"] = ("one pass" if one else
