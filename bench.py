@@ -47,6 +47,8 @@ Other modes:
                  reference against which rocprofv3 FETCH_SIZE / WRITE_SIZE are
                  scaled);
   --kernel-only  run only the timed headline loop (for rocprofv3 runs);
+  --two-call-only  run only the two-call pipeline's loop (mhc_pre +
+                 mhc_post_res_coeffs; for rocprofv3 counter runs of their kernels);
   --lazy-prenorm-only  time only the Lazy Pre-Norm GEMM workloads.
 """
 
@@ -516,6 +518,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--kernel-only", action="store_true")
+    ap.add_argument("--two-call-only", action="store_true",
+                    help="run only the two-call pipeline's timed loop (counter runs of its kernels)")
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the E4M3 and other-workload sections (profiling runs of one workload)")
     ap.add_argument("--lazy-prenorm-only", action="store_true",
@@ -555,7 +559,7 @@ def main():
 
     # The CPU baseline samples the input before the chained loop overwrites it.
     cpu = None
-    if not args.no_cpu_baseline and not args.kernel_only:
+    if not args.no_cpu_baseline and not args.kernel_only and not args.two_call_only:
         cpu = _cpu_baseline(inp, args.cpu_rows, args.cpu_budget_s)
 
     # ---- headline: one call per layer, residual stream chained through layers
@@ -621,6 +625,11 @@ def main():
     # Timed region 1 (the headline number): K back-to-back layers bracketed by
     # two events and a device synchronisation on both sides; no event sits
     # between calls (each recorded event idles the stream a few microseconds).
+    if args.two_call_only:  # counter runs of the two-call pipeline's kernels
+        mhc.mhc_pre(B, n, C, X[cur[0]], Hs[cur[0]], F_pre, stream=stream)
+        timed(two_call_layer)
+        print(json.dumps({"two_call_only": True, "steps": args.steps}), flush=True)
+        return
     ms_step, wall = timed(layer)
     if args.kernel_only:
         print(json.dumps({"kernel_only": True, "steps": args.steps}), flush=True)
