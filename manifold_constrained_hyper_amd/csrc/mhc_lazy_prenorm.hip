@@ -25,14 +25,15 @@
 //    ((row >> 1) & 7), so 16 consecutive rows read at one piece index hit 16
 //    distinct bank groups (LDS serves 256 bytes per clock);
 //  * operands of k-step t+1 are read while the MFMAs of step t run (two
-//    register sets of 24 VGPRs); scheduling barriers keep the compiler from
-//    sinking those reads next to their use;
+//    register sets of 24 VGPRs), one LDS read after each MFMA (scheduling
+//    group barriers keep the compiler from sinking the reads next to their
+//    use);
 //  * each block computes C^T = W A^T (W as the MFMA A operand), so a lane
 //    ends with runs of 4 consecutive output columns of one row: the epilogue
 //    scales them by that row's rstd and stores 8 bytes;
 //  * the row sums of squares run on the vector unit beside the matrix core:
 //    thread t adds the squares of half of row t >> 1 of every A chunk (four
-//    independent partial sums);
+//    independent partial sums, one v_dot2_f32_bf16 per packed pair);
 //  * tiles are walked in groups of 4 tile rows, each XCD taking a contiguous
 //    run of the order.
 #include "mhc_device.h"
@@ -76,6 +77,14 @@ template <int N> __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
+
+// lo^2 + hi^2 + acc of a packed bf16 pair in one instruction (bf16 squares
+// are exact in fp32).  Written as inline asm: through the builtin, hipcc
+// passed element 0 of a 4-word vector for every element.
+__device__ __forceinline__ float dot2_sq_bf16(uint32_t v, float acc) {
+  asm("v_dot2_f32_bf16 %0, %1, %1, %0" : "+v"(acc) : "v"(v));
+  return acc;
+}
 
 struct Operands {
   bf16x8 a[4], w[2];
@@ -157,7 +166,6 @@ __global__ __launch_bounds__(512, 1) void lazy_prenorm_gemm_kernel(
     for (int b = 0; b < 4; ++b) o.a[b] = *reinterpret_cast<const bf16x8 *>(st + offa + b * 32 * kRB + sl);
 #pragma unroll
     for (int b = 0; b < 2; ++b) o.w[b] = *reinterpret_cast<const bf16x8 *>(st + offw + b * 32 * kRB + sl);
-    __builtin_amdgcn_sched_barrier(0);
   };
 
   // Row sums of squares: thread t takes row t >> 1, pieces 4 (t & 1) .. +3.
@@ -176,9 +184,7 @@ __global__ __launch_bounds__(512, 1) void lazy_prenorm_gemm_kernel(
     for (int p = 0; p < kPieces / 2; ++p)
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float lo = bf16_lo(sq[p][w]), hi = bf16_hi(sq[p][w]);
-        ssp[w] = fmaf(lo, lo, ssp[w]);
-        ssp[w] = fmaf(hi, hi, ssp[w]);
+        ssp[w] = dot2_sq_bf16(sq[p][w], ssp[w]);
       }
   };
 
@@ -193,6 +199,14 @@ __global__ __launch_bounds__(512, 1) void lazy_prenorm_gemm_kernel(
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
         acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.w[cb], o.a[rb], acc[rb][cb], 0, 0, 0);
+    // one LDS read of the next k-step after each of the first six MFMAs
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   const int nchunks = (K + kKC - 1) / kKC;
