@@ -8,6 +8,9 @@
 
 namespace mhc {
 
+// Compute units of the current device (queried once per device id).
+int device_cus();
+
 // Split-K plan of the fused product + sum-of-squares pass.
 //
 // Workspace layout (bytes from the start of the caller's workspace):

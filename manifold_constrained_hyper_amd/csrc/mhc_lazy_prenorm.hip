@@ -39,6 +39,8 @@
 #include "mhc_device.h"
 #include "mhc_launch.h"
 
+#include <algorithm>
+
 namespace mhc {
 
 namespace {
@@ -77,6 +79,14 @@ template <int N> __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
+// Workgroup barrier for LDS only: this wave's LDS accesses have completed;
+// outstanding global loads (the next tile's chunks) are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  wait_lgkm0();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // lo^2 + hi^2 + acc of a packed bf16 pair in one instruction (bf16 squares
 // are exact in fp32).  Written as inline asm: through the builtin, hipcc
@@ -103,37 +113,51 @@ __global__ __launch_bounds__(512, 1) void lazy_prenorm_gemm_kernel(
   const int j32 = lane & 31, g = lane >> 5;
   const int wm = wave & 1, wn = wave >> 1;  // 2 x 4 waves
 
-  // Tile of this workgroup: workgroups are dealt to the 8 XCDs in turn; each
-  // XCD walks a contiguous run of the grouped order.
+  // Tiles of this workgroup.  The grouped order (kGroupM tile rows at a time)
+  // is cut into 8 contiguous runs, one per XCD (workgroups are dealt to the
+  // XCDs in turn); the P workgroups of an XCD walk its run together, taking
+  // tiles j, j + P, j + 2 P, ... of it.
   const int T = tiles_m * tiles_n;
-  const int bid = blockIdx.x;
-  const int q = T >> 3, rr8 = T & 7, x = bid & 7;
-  const int lin = x * q + min(x, rr8) + (bid >> 3);
-  const int group = lin / (kGroupM * tiles_n);
-  const int gm0 = group * kGroupM;
-  const int gsz = min(kGroupM, tiles_m - gm0);
-  const int within = lin - group * kGroupM * tiles_n;
-  const int tm = gm0 + within % gsz;
-  const int tn = within / gsz;
-  const int m0 = tm * kTile, n0 = tn * kTile;
+  const int G = gridDim.x, bid = blockIdx.x;
+  const int x = bid & 7, jw = bid >> 3;
+  const int run0 = x * (T >> 3) + min(x, T & 7), runlen = (T >> 3) + (x < (T & 7) ? 1 : 0);
+  const int P = (G >> 3) + (x < (G & 7) ? 1 : 0);
+  const int ntiles = jw < runlen ? (runlen - 1 - jw) / P + 1 : 0;
+  auto tile_of = [&](int it, int &tm, int &tn) {
+    const int lin = run0 + jw + it * P;
+    const int group = lin / (kGroupM * tiles_n);
+    const int gm0 = group * kGroupM;
+    const int gsz = min(kGroupM, tiles_m - gm0);
+    const int within = lin - group * kGroupM * tiles_n;
+    tm = gm0 + within % gsz;
+    tn = within / gsz;
+  };
 
   // DMA: this wave issues instructions kInstPerWave*wave + jj of each operand;
   // instruction i fills tile rows 8 i .. 8 i + 7, lane l row 8 i + (l >> 3),
   // slot l & 7, which holds piece slot ^ swz(row).  Rows past M (N) repeat the
-  // last row (their outputs are not stored).
+  // last row (their outputs are not stored).  The chunks of all the
+  // workgroup's tiles form one stream: the first chunks of the next tile are
+  // loaded while the current tile's last chunks and its epilogue run.
   const uint32_t rowK2 = (uint32_t)K * 2u;
   const int rsub = lane / kPieces, slot = lane % kPieces;
   uint32_t voa[kInstPerWave], vow[kInstPerWave];
   int pce[kInstPerWave];
+  const char *Ab = nullptr, *Wb = nullptr;
+  auto dma_tile = [&](int it) {  // point the DMA at tile it
+    int tm, tn;
+    tile_of(it, tm, tn);
+    const int m0 = tm * kTile, n0 = tn * kTile;
 #pragma unroll
-  for (int jj = 0; jj < kInstPerWave; ++jj) {
-    const int r = kRowsPerInst * (kInstPerWave * wave + jj) + rsub;
-    pce[jj] = slot ^ swz(r);
-    voa[jj] = (uint32_t)(min(m0 + r, M - 1) - m0) * rowK2 + pce[jj] * 16;
-    vow[jj] = (uint32_t)(min(n0 + r, N - 1) - n0) * rowK2 + pce[jj] * 16;
-  }
-  const char *Ab = reinterpret_cast<const char *>(A) + (size_t)m0 * rowK2;
-  const char *Wb = reinterpret_cast<const char *>(W) + (size_t)n0 * rowK2;
+    for (int jj = 0; jj < kInstPerWave; ++jj) {
+      const int r = kRowsPerInst * (kInstPerWave * wave + jj) + rsub;
+      pce[jj] = slot ^ swz(r);
+      voa[jj] = (uint32_t)(min(m0 + r, M - 1) - m0) * rowK2 + pce[jj] * 16;
+      vow[jj] = (uint32_t)(min(n0 + r, N - 1) - n0) * rowK2 + pce[jj] * 16;
+    }
+    Ab = reinterpret_cast<const char *>(A) + (size_t)m0 * rowK2;
+    Wb = reinterpret_cast<const char *>(W) + (size_t)n0 * rowK2;
+  };
   auto issue = [&](int stage, int k0) {
     const uint32_t sb = lds_base + stage * kStageBytes + kInstPerWave * wave * 1024;
     const char *ab = Ab + (size_t)k0 * 2, *wb = Wb + (size_t)k0 * 2;
@@ -152,6 +176,17 @@ __global__ __launch_bounds__(512, 1) void lazy_prenorm_gemm_kernel(
         dma_vaddr(in ? wb + vow[jj] : zero, sb + kTileBytes + jj * 1024);
       }
     }
+  };
+  const int nchunks = (K + kKC - 1) / kKC;
+  const int total = ntiles * nchunks;  // chunks in this workgroup's stream
+  int dit = 0, dc = 0;                  // tile and chunk the next DMA fills
+  auto issue_next = [&](int stage) {
+    if (dc == nchunks) {
+      dc = 0;
+      dma_tile(++dit);
+    }
+    issue(stage, dc * kKC);
+    ++dc;
   };
 
   // Operand reads: k-step t of a chunk uses piece 2t + g of row j32 of each
@@ -209,77 +244,86 @@ __global__ __launch_bounds__(512, 1) void lazy_prenorm_gemm_kernel(
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  const int nchunks = (K + kKC - 1) / kKC;
+  if (total == 0) return;  // more workgroups than tiles (uniform per workgroup)
+  dma_tile(0);
 #pragma unroll
   for (int s = 0; s < kStages; ++s)
-    if (s < nchunks) issue(s, s * kKC);
-  if (nchunks >= kStages) wait_vm<(kStages - 1) * kLoadsPerWave>();
+    if (s < total) issue_next(s);
+  if (total >= kStages) wait_vm<(kStages - 1) * kLoadsPerWave>();
   else wait_vm<0>();
   __builtin_amdgcn_s_barrier();
   Operands o0, o1;
   read_ops(o0, 0, 0);
   read_sq(0);
 
-  for (int c = 0; c < nchunks; ++c) {
-    const int st = c % kStages;
-    // k-steps 0 .. kSteps-2 of this chunk, each reading the next step's operands
+  int gc = 0;  // position in the chunk stream
+  for (int it = 0; it < ntiles; ++it) {
+    for (int c = 0; c < nchunks; ++c, ++gc) {
+      const int st = gc % kStages;
+      // k-steps 0 .. kSteps-2 of this chunk, each reading the next step's operands
 #pragma unroll
-    for (int t = 0; t + 1 < kSteps; t += 2) {
-      read_ops(o1, st, t + 1);
-      mfma(o0);
-      if (t == 0) add_sq();
-      if (t + 2 < kSteps) {
-        read_ops(o0, st, t + 2);
-        mfma(o1);
+      for (int t = 0; t + 1 < kSteps; t += 2) {
+        read_ops(o1, st, t + 1);
+        mfma(o0);
+        if (t == 0) add_sq();
+        if (t + 2 < kSteps) {
+          read_ops(o0, st, t + 2);
+          mfma(o1);
+        }
+      }
+      // Chunk gc+1 of the stream has landed (this wave's loads, then the
+      // barrier for all waves) and every read of chunk gc has returned, so
+      // its stage may be refilled with chunk gc + kStages.
+      if (gc + kStages - 1 < total) wait_vm<(kStages - 2) * kLoadsPerWave>();
+      else wait_vm<0>();
+      lds_barrier();
+      if (gc + kStages < total) issue_next(st);
+      // last k-step; read step 0 of the next chunk (past the stream's end:
+      // stale, unused)
+      const int sn = (gc + 1) % kStages;
+      read_ops(o0, sn, 0);
+      read_sq(sn);
+      mfma(o1);
+    }
+
+    int tm, tn;
+    tile_of(it, tm, tn);
+    const int m0 = tm * kTile, n0 = tn * kTile;
+    float ss = (ssp[0] + ssp[1]) + (ssp[2] + ssp[3]);
+    ss += __shfl_xor(ss, 1);
+    if (sh == 0) rs_lds[srow] = ss;
+    lds_barrier();
+    if (tid < kTile) {
+      const float r = 1.0f / sqrtf(rs_lds[tid] * inv_k + eps);
+      if (tn == 0 && rstd_out != nullptr && m0 + tid < M) rstd_out[m0 + tid] = r;
+      rs_lds[tid] = r;  // each thread reads and rewrites only its own row
+    }
+    lds_barrier();
+
+    // Epilogue: block (rb, cb) of C^T: lane holds row j32 of A block rb and
+    // columns 8 q + 4 g .. +3 (q = 0..3) of W block cb.  rs_lds is next
+    // written after the next tile's first chunk barrier.
+    const bool interior = (m0 + kTile <= M) && (n0 + kTile <= N);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int lr = wm * 128 + rb * 32 + j32;
+      const int row = m0 + lr;
+      const float sc = rs_lds[lr];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const f32x16 v = acc[rb][cb];
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int col = n0 + wn * 64 + cb * 32 + 8 * qq + 4 * g;
+          const u32x2 ov = {pack_bf16x2(v[4 * qq] * sc, v[4 * qq + 1] * sc),
+                            pack_bf16x2(v[4 * qq + 2] * sc, v[4 * qq + 3] * sc)};
+          if (interior || (row < M && col < N)) *reinterpret_cast<u32x2 *>(Cout + (size_t)row * N + col) = ov;
+        }
+        acc[rb][cb] = f32x16{};
       }
     }
-    // Chunk c+1 has landed (this wave's loads, then the barrier for all
-    // waves) and every read of chunk c has returned, so its stage may be
-    // refilled with chunk c + kStages.
-    if (c + kStages - 1 < nchunks) wait_vm<(kStages - 2) * kLoadsPerWave>();
-    else wait_vm<0>();
-    wait_lgkm0();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (c + kStages < nchunks) issue(st, (c + kStages) * kKC);
-    // last k-step; read step 0 of the next chunk (past the end: stale, unused)
-    const int sn = (c + 1) % kStages;
-    read_ops(o0, sn, 0);
-    read_sq(sn);
-    mfma(o1);
-  }
-
-  float ss = (ssp[0] + ssp[1]) + (ssp[2] + ssp[3]);
-  ss += __shfl_xor(ss, 1);
-  if (sh == 0) rs_lds[srow] = ss;
-  __syncthreads();
-  if (tid < kTile) {
-    const float r = 1.0f / sqrtf(rs_lds[tid] * inv_k + eps);
-    if (tn == 0 && rstd_out != nullptr && m0 + tid < M) rstd_out[m0 + tid] = r;
-    rs_lds[tid] = r;  // each thread reads and rewrites only its own row
-  }
-  __syncthreads();
-
-  // Epilogue: block (rb, cb) of C^T: lane holds row j32 of A block rb and
-  // columns 8 q + 4 g .. +3 (q = 0..3) of W block cb.
-  const bool interior = (m0 + kTile <= M) && (n0 + kTile <= N);
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const int lr = wm * 128 + rb * 32 + j32;
-    const int row = m0 + lr;
-    const float sc = rs_lds[lr];
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const f32x16 v = acc[rb][cb];
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int col = n0 + wn * 64 + cb * 32 + 8 * qq + 4 * g;
-        const u32x2 ov = {pack_bf16x2(v[4 * qq] * sc, v[4 * qq + 1] * sc),
-                          pack_bf16x2(v[4 * qq + 2] * sc, v[4 * qq + 3] * sc)};
-        if (interior || (row < M && col < N)) *reinterpret_cast<u32x2 *>(Cout + (size_t)row * N + col) = ov;
-      }
-    }
+    for (int w = 0; w < 4; ++w) ssp[w] = 0.f;
   }
 }
 
@@ -289,7 +333,10 @@ hipError_t launch_lazy_prenorm_gemm(int64_t M, int64_t N, int64_t K, const void 
                                     float eps, void *C, float *rstd, hipStream_t st) {
   const int tiles_m = (int)((M + kTile - 1) / kTile), tiles_n = (int)((N + kTile - 1) / kTile);
   const int64_t tiles = (int64_t)tiles_m * tiles_n;
-  lazy_prenorm_gemm_kernel<<<dim3((uint32_t)tiles), kWaves * 64, 0, st>>>(
+  // persistent: one workgroup per compute unit (the LDS stages allow one);
+  // at least 8, so that each XCD run of the tile order has a workgroup
+  const int64_t grid = std::min<int64_t>(tiles, std::max(device_cus(), 8));
+  lazy_prenorm_gemm_kernel<<<dim3((uint32_t)grid), kWaves * 64, 0, st>>>(
       static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(W), static_cast<uint16_t *>(C),
       rstd, (int)M, (int)N, (int)K, (float)(1.0 / (double)K), eps, tiles_m, tiles_n);
   return hipGetLastError();

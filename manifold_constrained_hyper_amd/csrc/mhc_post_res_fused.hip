@@ -771,21 +771,6 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
   }
 }
 
-// Compute units of the current device (cached per device id).
-int device_cus() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  if (dev >= 0 && dev < 64) {
-    const int v = cache[dev].load(std::memory_order_relaxed);
-    if (v > 0) return v;
-  }
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
-  if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
-  return cus;
-}
 
 
 template <int NS, int MODE, bool FIX>
@@ -838,6 +823,23 @@ constexpr int kPreWgsPerCu = 1;    // resident pre-mix workgroups per CU (its LD
 constexpr int kPreRows = 16;       // rows per tile of the pre-mix mode (FusedTile::R)
 
 }  // namespace
+
+// Compute units of the current device (cached per device id); declared in
+// mhc_launch.h.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < 64) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
 
 bool pre_mode_fits(int64_t B, int n, int64_t C) {
   if (n != 1 && n != 2 && n != 4) return false;
