@@ -30,7 +30,8 @@
 //    use);
 //  * each block computes C^T = W A^T (W as the MFMA A operand), so a lane
 //    ends with runs of 4 consecutive output columns of one row: the epilogue
-//    scales them by that row's rstd and stores 8 bytes;
+//    scales them by that row's rstd, pairs runs across the two lane halves
+//    (v_permlane32_swap) and stores 16 bytes;
 //  * the row sums of squares run on the vector unit beside the matrix core:
 //    thread t adds the squares of half of row t >> 1 of every A chunk (four
 //    independent partial sums, one v_dot2_f32_bf16 per packed pair);
@@ -301,8 +302,11 @@ __global__ __launch_bounds__(512, 1) void lazy_prenorm_gemm_kernel(
     lds_barrier();
 
     // Epilogue: block (rb, cb) of C^T: lane holds row j32 of A block rb and
-    // columns 8 q + 4 g .. +3 (q = 0..3) of W block cb.  rs_lds is next
-    // written after the next tile's first chunk barrier.
+    // columns 8 q + 4 g .. +3 (q = 0..3) of W block cb.  For each pair of
+    // column groups (q, q + 1) one v_permlane32_swap per word gives lane g
+    // all 8 columns of group q + g (16 bytes): lanes 0-31 trade their group
+    // q + 1 half for lanes 32-63's group q half.  rs_lds is next written
+    // after the next tile's first chunk barrier.
     const bool interior = (m0 + kTile <= M) && (n0 + kTile <= N);
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
@@ -313,11 +317,16 @@ __global__ __launch_bounds__(512, 1) void lazy_prenorm_gemm_kernel(
       for (int cb = 0; cb < 2; ++cb) {
         const f32x16 v = acc[rb][cb];
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const int col = n0 + wn * 64 + cb * 32 + 8 * qq + 4 * g;
-          const u32x2 ov = {pack_bf16x2(v[4 * qq] * sc, v[4 * qq + 1] * sc),
-                            pack_bf16x2(v[4 * qq + 2] * sc, v[4 * qq + 3] * sc)};
-          if (interior || (row < M && col < N)) *reinterpret_cast<u32x2 *>(Cout + (size_t)row * N + col) = ov;
+        for (int qp = 0; qp < 4; qp += 2) {
+          const uint32_t a0 = pack_bf16x2(v[4 * qp] * sc, v[4 * qp + 1] * sc);
+          const uint32_t a1 = pack_bf16x2(v[4 * qp + 2] * sc, v[4 * qp + 3] * sc);
+          const uint32_t b0 = pack_bf16x2(v[4 * qp + 4] * sc, v[4 * qp + 5] * sc);
+          const uint32_t b1 = pack_bf16x2(v[4 * qp + 6] * sc, v[4 * qp + 7] * sc);
+          const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+          const u32x4 ov = {s0[0], s1[0], s0[1], s1[1]};
+          const int col = n0 + wn * 64 + cb * 32 + 8 * (qp + g);  // N % 8 == 0: all 8 in range or none
+          if (interior || (row < M && col < N)) *reinterpret_cast<u32x4 *>(Cout + (size_t)row * N + col) = ov;
         }
         acc[rb][cb] = f32x16{};
       }
