@@ -12,7 +12,8 @@ workspace with garbage; each replay must reproduce the eager run bitwise.
 Shapes: the decode workload (the two-call route: apply, one-launch small-B
 coefficient kernel with its arrival flags, pre-mix) and a prefill-sized shape
 on the one-pass kernel (hand-off records cleared in-graph by the packing
-kernel).
+kernel).  The Lazy Pre-Norm GEMM (one persistent launch) is replayed the same
+way.
 """
 
 import sys
@@ -129,3 +130,44 @@ def test_graph_replay_matches_eager(B, n, C, fp8):
         got = _outputs(bufs)
         for i, (a, b) in enumerate(zip(got, ref)):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep}: output {i} differs"
+
+
+def test_graph_replay_lazy_prenorm():
+    """mhc_lazy_prenorm_gemm is one persistent launch with no memset: captured
+    twice in a graph (two shapes, one the ragged case), replayed three times
+    with the outputs overwritten in between, bitwise equal to the eager run."""
+    _say("graph replay lazy_prenorm")
+    cases = []
+    for M, N, K, seed in ((1000, 776, 520, 31), (4096, 1536, 1024, 32)):
+        d = synth.make_lpn_inputs(M, N, K, seed=seed, device="cuda")
+        C = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        r = torch.empty(M, device="cuda")
+        cases.append((M, N, K, d["A"], d["W"], C, r))
+
+    def run():
+        for M, N, K, A, W, C, r in cases:
+            assert mhc.mhc_lazy_prenorm_gemm(M, N, K, A, W, C, r) == mhc.MHC_OK
+
+    run()
+    torch.cuda.synchronize()
+    ref = [(c[5].clone(), c[6].clone()) for c in cases]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for c in cases:
+            c[5].view(torch.uint8).fill_(0x7F)
+            c[6].view(torch.uint8).fill_(0x7F)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (c, (rc, rr)) in enumerate(zip(cases, ref)):
+            assert torch.equal(c[5].view(torch.int16), rc.view(torch.int16)), f"replay {rep}: C of case {i} differs"
+            assert torch.equal(c[6], rr), f"replay {rep}: rstd of case {i} differs"
