@@ -38,7 +38,7 @@ Also reported ("phi32_coeffs"): mhc_coeffs_phi32 (fp32 phi) beside mhc_coeffs
 on the same X, decode and headline workloads, mean call time.
 
 Also reported ("lazy_prenorm"): the Lazy Pre-Norm GEMM C = rmsnorm(A) W^T
-(mhc_lazy_prenorm_gemm) on its two synthetic workloads, with TFLOP/s
+(mhc_lazy_prenorm_gemm) on its three synthetic workloads, with TFLOP/s
 (2 M N K per call; the sums of squares are not counted) against MI355X's
 dense bf16 MFMA peak.
 
@@ -49,7 +49,10 @@ Other modes:
   --kernel-only  run only the timed headline loop (for rocprofv3 runs);
   --two-call-only  run only the two-call pipeline's loop (mhc_pre +
                  mhc_post_res_coeffs; for rocprofv3 counter runs of their kernels);
-  --lazy-prenorm-only  time only the Lazy Pre-Norm GEMM workloads.
+  --lazy-prenorm-only  time only the Lazy Pre-Norm GEMM workloads;
+  --shape-sweep  time the one-pass layer call (bf16 and E4M3) over a grid of
+                 shapes around the headline one, one JSON line per shape
+                 (steady state: ~60 ms of chained layers before ~60 ms timed).
 """
 
 import argparse
@@ -504,6 +507,64 @@ def _lazy_prenorm(mhc, torch, synth, stream, ev, steps=20, warmup=5):
     return out
 
 
+SWEEP_SHAPES = [(4, 2048, 16384), (4, 4096, 16384), (4, 7168, 1024), (4, 7168, 4096),
+                (4, 7168, 16384), (4, 7168, 32768), (4, 7168, 65536), (4, 8192, 16384),
+                (2, 7168, 16384), (1, 7168, 16384)]
+
+
+def _shape_sweep(mhc, torch, synth):
+    """mhc_post_res_coeffs_pre(_fp8) chained over layers at each shape of
+    SWEEP_SHAPES: mean us per layer and TB/s of its algorithmic bytes."""
+    for fp8 in (False, True):
+        for n, C, B in SWEEP_SHAPES:
+            make = synth.make_inputs_fp8 if fp8 else synth.make_inputs
+            inp = make(n, C, B, "normal", seed=7, device="cuda")
+            N = n * n + 2 * n
+            sfx = "_fp8" if fp8 else ""
+            ab = (inp["alpha_pre"], inp["alpha_post"], inp["alpha_res"], inp["b_pre"], inp["b_post"],
+                  inp["b_res"])
+            H0, lg = torch.empty(B, N, device="cuda"), torch.empty(B, N, device="cuda")
+            r = torch.empty(B, device="cuda")
+            wsc = torch.empty(max(getattr(mhc, f"mhc_coeffs{sfx}_workspace_size")(B, n, C), 16),
+                              dtype=torch.uint8, device="cuda")
+            getattr(mhc, f"mhc_coeffs{sfx}")(B, n, C, inp["X"], inp["phi"], *ab, lg, r, H0, wsc)
+            X, Hs = [inp["X"], torch.empty_like(inp["X"])], [H0, torch.empty_like(H0)]
+            F = torch.empty(B, C, dtype=torch.uint8 if fp8 else torch.bfloat16, device="cuda")
+            ws = torch.empty(max(getattr(mhc, f"mhc_post_res_coeffs_pre{sfx}_workspace_size")(B, n, C), 16),
+                             dtype=torch.uint8, device="cuda")
+            call = getattr(mhc, f"mhc_post_res_coeffs_pre{sfx}")
+            cur = [0]
+
+            def layer():
+                a = cur[0]
+                call(B, n, C, X[a], inp["F_out"], Hs[a], X[1 - a], inp["phi"], *ab, lg, r, Hs[1 - a], F, ws)
+                cur[0] = 1 - a
+
+            def timed(k):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(k):
+                    layer()
+                e1.record()
+                torch.cuda.synchronize()
+                return e0.elapsed_time(e1) * 1e3 / k
+
+            layer()
+            torch.cuda.synchronize()
+            k = max(20, int(60e3 / timed(4)))
+            timed(k)  # warm-up
+            us = timed(k)
+            nbytes = path_bytes(B, n, C, 1 if fp8 else 2)["mhc_post_res_coeffs_pre"]
+            one = getattr(mhc, f"mhc_post_res_coeffs_pre{sfx}_one_pass")(B, n, C)
+            print(json.dumps({"shape_sweep": {"n": n, "C": C, "B": B, "dtype": "e4m3" if fp8 else "bf16",
+                                              "route": "one pass" if one else "two calls", "layers": k,
+                                              "us_per_layer": round(us, 1),
+                                              "hbm_gbps": round(nbytes / us / 1e3, 1),
+                                              "tokens_per_s": round(B / us * 1e6, 1)}}), flush=True)
+            del inp, X, Hs, F, ws, wsc, H0, lg, r
+            torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -524,6 +585,8 @@ def main():
                     help="skip the E4M3 and other-workload sections (profiling runs of one workload)")
     ap.add_argument("--lazy-prenorm-only", action="store_true",
                     help="time only mhc_lazy_prenorm_gemm on its workloads (profiling runs)")
+    ap.add_argument("--shape-sweep", action="store_true",
+                    help="time the one-pass layer call over a grid of shapes (one JSON line each)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -545,6 +608,9 @@ def main():
         return
 
     mhc.load()  # raises if the HIP library is not built
+    if args.shape_sweep:
+        _shape_sweep(mhc, torch, synth)
+        return
     if args.lazy_prenorm_only:
         lpn = _lazy_prenorm(mhc, torch, synth, torch.cuda.current_stream(),
                             lambda: torch.cuda.Event(enable_timing=True), args.steps, args.warmup)
