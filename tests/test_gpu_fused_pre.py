@@ -207,11 +207,14 @@ def test_workspace_contents(B, n, C, fill, route):
     _check(cur, nxt, o, ref, f, pre_own, _rows(B), f"B{B}n{n}C{C}/{fill.__name__}")
 
 
-def test_two_routes_agree(monkeypatch):
+@pytest.mark.parametrize("B", [16384, 65536], ids=["large", "B65536"])
+def test_two_routes_agree(monkeypatch, B):
     """The one-pass kernel and the two calls it replaces: X_next bitwise,
-    coefficients up to summation order, F_pre within one bf16 step."""
-    _say("post_res_coeffs_pre one pass vs two calls (large)")
-    cfg = synth.CONFIGS["large"]
+    coefficients up to summation order, F_pre within one bf16 step.  At
+    B = 65536 every workgroup runs 228 steps of the record hand-off (57 at the
+    large workload)."""
+    _say(f"post_res_coeffs_pre one pass vs two calls (n=4 C=7168 B={B})")
+    cfg = dict(synth.CONFIGS["large"], B=B)
     cur, nxt = _layers(cfg["n"], cfg["C"], cfg["B"], cfg["x_dist"], cfg["seed"])
     o = mhc.alloc_outputs(cfg["B"], cfg["n"], cfg["C"])
     _coeffs(cur, cur["X"], o)

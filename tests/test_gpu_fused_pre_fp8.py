@@ -215,12 +215,14 @@ def test_workspace_contents(B, n, C):
     _check(cur, nxt, o, ref, f, pre_own, _rows(B), f"B{B}n{n}C{C}/random")
 
 
-def test_two_routes_agree(monkeypatch):
-    """The one-pass kernel and the two calls it replaces on the large
-    workload: X_next bitwise, coefficients up to summation order, F_pre codes
-    at most one E4M3 step apart (H_pre may differ in its last bits)."""
-    _say("post_res_coeffs_pre_fp8 one pass vs two calls (large)")
-    cfg = synth.CONFIGS["large"]
+@pytest.mark.parametrize("B", [16384, 65536], ids=["large", "B65536"])
+def test_two_routes_agree(monkeypatch, B):
+    """The one-pass kernel and the two calls it replaces at n=4, C=7168 (the
+    large workload, and B = 65536 for a long run of the record hand-off):
+    X_next bitwise, coefficients up to summation order, F_pre codes at most
+    one E4M3 step apart (H_pre may differ in its last bits)."""
+    _say(f"post_res_coeffs_pre_fp8 one pass vs two calls (n=4 C=7168 B={B})")
+    cfg = dict(synth.CONFIGS["large"], B=B)
     cur, nxt = _layers(cfg["n"], cfg["C"], cfg["B"], cfg["x_dist"], cfg["seed"])
     o = {}
     _coeffs(cur, cur["X"], o)
