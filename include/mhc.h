@@ -46,7 +46,8 @@
  *    - n not in {1,2,4,8}, C % 8 != 0, misaligned pointer   -> MHC_ERR_UNSUPPORTED
  *    - workspace smaller than mhc_coeffs_workspace_size()    -> MHC_ERR_WORKSPACE
  *    - the HIP runtime reports a launch error                -> MHC_ERR_HIP
- *  B == 0 is valid and launches nothing.  Faults during asynchronous
+ *  B == 0 is valid and launches nothing.  MHC_ERR_INCOMPLETE is returned only
+ *  by mhc_post_res_coeffs_pre_check (below).  Faults during asynchronous
  *  execution surface at the caller's next synchronisation, as in HIP.
  */
 #ifndef MHC_H
@@ -68,7 +69,8 @@ enum mhc_status {
   MHC_ERR_INVALID_ARG = 1,
   MHC_ERR_UNSUPPORTED = 2,
   MHC_ERR_WORKSPACE = 3,
-  MHC_ERR_HIP = 4
+  MHC_ERR_HIP = 4,
+  MHC_ERR_INCOMPLETE = 5
 };
 
 /* Human-readable name of a status code (static storage; never NULL). */
@@ -188,13 +190,19 @@ int mhc_post_res_coeffs(int64_t B, int32_t n, int64_t C,
  * written once per layer (X_t and F_out in, X_next and F_pre_next out).
  *
  * Where the shape allows (n <= 4, B above 256, C % 32 == 0 and at most 16
- * 512-channel steps per row, i.e. C <= 8192) this runs as one persistent pass whose workgroups exchange each row's
- * partial sums through the workspace; mhc_post_res_coeffs_pre_one_pass()
- * reports whether a shape takes that route.  That pass needs its whole grid
- * (one workgroup per compute unit) resident at once: it shares the device
- * poorly with kernels running concurrently on other streams, and if a wait
- * for another workgroup cannot complete within about a second it gives up and
- * writes NaN to the affected F_pre_next vectors.  Other shapes run
+ * 512-channel steps per row, i.e. C <= 8192) this runs as one persistent
+ * pass whose workgroups exchange each row's partial sums through the
+ * workspace; mhc_post_res_coeffs_pre_one_pass() reports whether a shape takes
+ * that route.  The workgroups of a round wait for each other, so the call
+ * sizes that pass's grid to what can be resident at once -- the occupancy
+ * the HIP runtime reports for the kernel (one workgroup per compute unit)
+ * times the compute units `stream` may use (its CU mask) -- and runs the two
+ * calls below instead when not even one row's slices fit together.  It
+ * cannot see kernels that other streams or processes run at the same time:
+ * if they hold compute units so long that a wait for another workgroup
+ * cannot complete within about a second, the wait gives up, writes NaN to the
+ * affected F_pre_next vectors and sets a word in the workspace, which
+ * mhc_post_res_coeffs_pre_check reads back.  Other shapes run
  * mhc_post_res_coeffs followed by mhc_pre on X_next, with the same results.
  *
  * Arguments as mhc_post_res_coeffs, plus F_pre_next (16-byte aligned, must
@@ -212,8 +220,23 @@ int mhc_post_res_coeffs_pre(int64_t B, int32_t n, int64_t C,
                             void *workspace, size_t workspace_bytes, void *stream);
 
 /* 1 if mhc_post_res_coeffs_pre runs this shape as one pass, 0 if it runs the
- * two calls (or the shape is invalid). */
+ * two calls (or the shape is invalid).  (A stream whose CU mask leaves too
+ * few compute units makes the call take the two calls even where this
+ * returns 1.) */
 int32_t mhc_post_res_coeffs_pre_one_pass(int64_t B, int32_t n, int64_t C);
+
+/* Whether the last mhc_post_res_coeffs_pre (fp8 == 0) or
+ * mhc_post_res_coeffs_pre_fp8 (fp8 != 0) call of shape (B, n, C) that used
+ * `workspace` completed every wait of its one-pass route.  Synchronises
+ * `stream` (the stream of that call) and reads one word of the workspace;
+ * the workspace must still be the one the call used, not yet reused.
+ * Returns MHC_OK when no wait gave up (always for shapes that run the two
+ * calls), MHC_ERR_INCOMPLETE when one did (F_pre_next then holds NaN -- the
+ * E4M3 code 0x7F in the fp8 call -- in the vectors of the rows it gave up
+ * on; X_next, logits_next, r_next and H_next are still complete), and the
+ * usual argument errors and MHC_ERR_HIP otherwise. */
+int mhc_post_res_coeffs_pre_check(int64_t B, int32_t n, int64_t C, int32_t fp8,
+                                  const void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * FP8 residual-stream variant.
@@ -281,8 +304,9 @@ int mhc_post_res_coeffs_fp8(int64_t B, int32_t n, int64_t C,
  *   F_pre_next   out E4M3 [B, C] = exactly what mhc_pre_fp8(X_next, H_next)
  *                writes (bitwise).
  *
- * Route, residency caveat and give-up behaviour (NaN, here the E4M3 code
- * 0x7F, in the affected F_pre_next bytes) as for mhc_post_res_coeffs_pre; the
+ * Route, residency handling and give-up behaviour (NaN, here the E4M3 code
+ * 0x7F, in the affected F_pre_next bytes; mhc_post_res_coeffs_pre_check with
+ * fp8 = 1 reads it back) as for mhc_post_res_coeffs_pre; the
  * one-pass route also needs the fused E4M3 route (the default at n <= 4;
  * MHC_FUSED_FP8=0 turns it off), else the call runs mhc_post_res_coeffs_fp8
  * followed by mhc_pre_fp8 on X_next, with the same results.  Requires
@@ -368,6 +392,31 @@ int mhc_post_res_coeffs_phi32(int64_t B, int32_t n, int64_t C,
  * rules as for the calls above. */
 int mhc_lazy_prenorm_gemm(int64_t M, int64_t N, int64_t K, const void *A, const void *W,
                           float eps, void *C, float *rstd, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Testing and tuning.
+ *
+ * Every call above picks its kernels and launch shapes by the sizes of the
+ * problem alone (the choices measured fastest on MI355X); the library reads
+ * no environment variable.  These functions override the choices for tests
+ * and tuning runs, process-wide, e.g. to run the register-path product or
+ * the small-B kernel at any B.  Keys (value < 0 restores the default):
+ *   MHC_SMALL_MAX_B  rows up to which the one-launch small-B coefficient
+ *                    kernel runs (0: never)
+ *   MHC_GEMM_ALGO    0: register-path product; 2: persistent product kernel
+ *   MHC_SPLIT_K, MHC_GEMM_WGS, MHC_GEMM_MB   split-K product shape
+ *   MHC_FUSED_N8     > 0: the fused kernel also at n = 8
+ *   MHC_FUSED_FP8    0: E4M3 fused call as apply + product; > 0: fused kernel
+ *   MHC_FUSED_FIXED  0 / 1: the fused kernel's fixed-slice layout off / on
+ *   MHC_FUSED_SPU, MHC_FUSED_WGS   fused kernel's steps per unit, grid cap
+ *   MHC_FUSED_PRE    0: mhc_post_res_coeffs_pre(_fp8) as two calls
+ * Every route computes the same results up to fp32 summation order (the
+ * fused calls' X_next and F_pre_next bitwise).  The workspace-size functions
+ * answer for the routes selected at the time they are called, so set
+ * overrides before sizing a workspace.  Not thread-safe against concurrent
+ * calls.  mhc_tuning_set returns MHC_ERR_INVALID_ARG for an unknown key. */
+int mhc_tuning_set(const char *name, int64_t value);
+void mhc_tuning_reset(void);
 
 #ifdef __cplusplus
 }

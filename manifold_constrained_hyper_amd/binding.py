@@ -18,6 +18,7 @@ MHC_ERR_INVALID_ARG = 1
 MHC_ERR_UNSUPPORTED = 2
 MHC_ERR_WORKSPACE = 3
 MHC_ERR_HIP = 4
+MHC_ERR_INCOMPLETE = 5
 MHC_SINKHORN_ITERS = 20
 
 EXPORTED = ("mhc_status_string", "mhc_coeffs_workspace_size", "mhc_coeffs_split_k",
@@ -29,7 +30,8 @@ EXPORTED = ("mhc_status_string", "mhc_coeffs_workspace_size", "mhc_coeffs_split_
             "mhc_lazy_prenorm_gemm", "mhc_post_res_coeffs_pre_workspace_size",
             "mhc_post_res_coeffs_pre", "mhc_post_res_coeffs_pre_one_pass",
             "mhc_post_res_coeffs_pre_fp8_workspace_size", "mhc_post_res_coeffs_pre_fp8",
-            "mhc_post_res_coeffs_pre_fp8_one_pass")
+            "mhc_post_res_coeffs_pre_fp8_one_pass", "mhc_post_res_coeffs_pre_check",
+            "mhc_tuning_set", "mhc_tuning_reset")
 
 _lib = None
 
@@ -101,21 +103,57 @@ def load():
     lib.mhc_post_res_coeffs_pre_fp8.restype = ctypes.c_int
     lib.mhc_post_res_coeffs_pre_fp8_one_pass.argtypes = [i64, i32, i64]
     lib.mhc_post_res_coeffs_pre_fp8_one_pass.restype = i32
+    lib.mhc_post_res_coeffs_pre_check.argtypes = [i64, i32, i64, i32, vp, sz, vp]
+    lib.mhc_post_res_coeffs_pre_check.restype = ctypes.c_int
+    lib.mhc_tuning_set.argtypes = [ctypes.c_char_p, i64]
+    lib.mhc_tuning_set.restype = ctypes.c_int
+    lib.mhc_tuning_reset.argtypes = []
+    lib.mhc_tuning_reset.restype = None
     _lib = lib
     return lib
 
 
-def _ptr(t):
-    """Device pointer of a tensor (None -> NULL).  Raises on host tensors."""
+def _ptr(t, nbytes=None, esize=None, name="tensor"):
+    """Device pointer of a tensor (None -> NULL; an int is taken as a raw
+    address).  Raises ValueError on host or non-contiguous tensors and, when
+    the call's sizes are given, on a tensor of another element size or
+    smaller than the nbytes the library will touch, before anything runs."""
     if t is None:
         return None
     if not isinstance(t, torch.Tensor):
         return int(t)  # raw address
-    if t.numel() > 0 and not t.is_cuda:
-        raise ValueError("libmhc takes device tensors")
+    if esize is not None and t.numel() > 0 and t.element_size() != esize:
+        raise ValueError(f"{name}: element size {t.element_size()} bytes, the call takes {esize}")
+    if nbytes is not None and t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name}: {t.numel() * t.element_size()} bytes, the call needs {nbytes}")
     if not t.is_contiguous():
         raise ValueError("libmhc takes contiguous tensors")
+    if t.numel() > 0 and not t.is_cuda:
+        raise ValueError("libmhc takes device tensors")
     return t.data_ptr() or None
+
+
+class _Sizes:
+    """Byte counts of the tensors of one (B, n, C) call: eb bytes per
+    residual-stream element (2 bf16, 1 E4M3), pb per phi element."""
+
+    def __init__(self, B, n, C, eb=2, pb=2):
+        B, n, C = int(B), int(n), int(C)
+        N = n * n + 2 * n
+        self.eb, self.pb = eb, pb
+        self.x = max(B, 0) * n * C * eb       # X_t, X_next
+        self.f = max(B, 0) * C * eb           # F_out, F_pre
+        self.phi = n * C * N * pb
+        self.coef = max(B, 0) * N * 4         # logits, H
+        self.r = max(B, 0) * 4
+        self.nb = n * 4                       # b_pre, b_post
+        self.nr = n * n * 4                   # b_res
+
+
+def _coeff_args(z, phi, b_pre, b_post, b_res, logits, r, H):
+    return (_ptr(phi, z.phi, z.pb, "phi"), _ptr(b_pre, z.nb, 4, "b_pre"), _ptr(b_post, z.nb, 4, "b_post"),
+            _ptr(b_res, z.nr, 4, "b_res"), _ptr(logits, z.coef, 4, "logits"), _ptr(r, z.r, 4, "r"),
+            _ptr(H, z.coef, 4, "H"))
 
 
 def _stream(stream):
@@ -135,6 +173,23 @@ def mhc_status_string(status):
     return load().mhc_status_string(int(status)).decode()
 
 
+def mhc_tuning_set(name, value):
+    """Override a route or launch-shape choice process-wide (tests and tuning;
+    value < 0 restores the default).  See include/mhc.h."""
+    _check(load().mhc_tuning_set(str(name).encode(), int(value)), f"mhc_tuning_set({name})")
+
+
+def mhc_tuning_reset():
+    """Restore every route and launch-shape choice to its default."""
+    load().mhc_tuning_reset()
+
+
+def _ws_bytes(workspace, workspace_bytes):
+    if workspace_bytes is not None:
+        return int(workspace_bytes)
+    return workspace.numel() * workspace.element_size() if isinstance(workspace, torch.Tensor) else 0
+
+
 def mhc_coeffs_workspace_size(B, n, C):
     return int(load().mhc_coeffs_workspace_size(int(B), int(n), int(C)))
 
@@ -143,34 +198,69 @@ def mhc_coeffs_split_k(B, n, C):
     return int(load().mhc_coeffs_split_k(int(B), int(n), int(C)))
 
 
+def _coeffs(fn, name, eb, pb, B, n, C, X_t, phi, alpha_pre, alpha_post, alpha_res, b_pre, b_post,
+            b_res, logits, r, H, workspace, workspace_bytes, stream, check):
+    z = _Sizes(B, n, C, eb, pb)
+    pp, bp, bq, br, lg, rr, hh = _coeff_args(z, phi, b_pre, b_post, b_res, logits, r, H)
+    wb = _ws_bytes(workspace, workspace_bytes)
+    st = fn(int(B), int(n), int(C), _ptr(X_t, z.x, eb, "X_t"), pp, float(alpha_pre), float(alpha_post),
+            float(alpha_res), bp, bq, br, lg, rr, hh, _ptr(workspace, wb, None, "workspace"), wb,
+            _stream(stream))
+    if check:
+        _check(st, name)
+    return st
+
+
 def mhc_coeffs(B, n, C, X_t, phi, alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res,
                logits, r, H, workspace, workspace_bytes=None, stream=None, check=True):
     """Steps (1)-(3): logits, r and H from X_t and phi (see include/mhc.h)."""
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = load().mhc_coeffs(int(B), int(n), int(C), _ptr(X_t), _ptr(phi), float(alpha_pre),
-                           float(alpha_post), float(alpha_res), _ptr(b_pre), _ptr(b_post),
-                           _ptr(b_res), _ptr(logits), _ptr(r), _ptr(H), _ptr(workspace),
-                           int(workspace_bytes), _stream(stream))
+    return _coeffs(load().mhc_coeffs, "mhc_coeffs", 2, 2, B, n, C, X_t, phi, alpha_pre, alpha_post,
+                   alpha_res, b_pre, b_post, b_res, logits, r, H, workspace, workspace_bytes, stream, check)
+
+
+def _pre(fn, name, eb, B, n, C, X_t, H, F_pre, stream, check):
+    z = _Sizes(B, n, C, eb)
+    st = fn(int(B), int(n), int(C), _ptr(X_t, z.x, eb, "X_t"), _ptr(H, z.coef, 4, "H"),
+            _ptr(F_pre, z.f, eb, "F_pre"), _stream(stream))
     if check:
-        _check(st, "mhc_coeffs")
+        _check(st, name)
     return st
 
 
 def mhc_pre(B, n, C, X_t, H, F_pre, stream=None, check=True):
     """Step (4a): F_pre = sum_i H_pre[i] X_t[i] (see include/mhc.h)."""
-    st = load().mhc_pre(int(B), int(n), int(C), _ptr(X_t), _ptr(H), _ptr(F_pre), _stream(stream))
+    return _pre(load().mhc_pre, "mhc_pre", 2, B, n, C, X_t, H, F_pre, stream, check)
+
+
+def _post_res(fn, name, eb, B, n, C, X_t, F_out, H, X_next, stream, check):
+    z = _Sizes(B, n, C, eb)
+    st = fn(int(B), int(n), int(C), _ptr(X_t, z.x, eb, "X_t"), _ptr(F_out, z.f, eb, "F_out"),
+            _ptr(H, z.coef, 4, "H"), _ptr(X_next, z.x, eb, "X_next"), _stream(stream))
     if check:
-        _check(st, "mhc_pre")
+        _check(st, name)
     return st
 
 
 def mhc_post_res(B, n, C, X_t, F_out, H, X_next, stream=None, check=True):
     """Step (4b): X_next = H_res X_t + H_post^T F_out (see include/mhc.h)."""
-    st = load().mhc_post_res(int(B), int(n), int(C), _ptr(X_t), _ptr(F_out), _ptr(H),
-                             _ptr(X_next), _stream(stream))
+    return _post_res(load().mhc_post_res, "mhc_post_res", 2, B, n, C, X_t, F_out, H, X_next, stream, check)
+
+
+def _fused(fn, name, eb, pb, B, n, C, X_t, F_out, H, X_next, phi_next, alpha_pre, alpha_post,
+           alpha_res, b_pre, b_post, b_res, logits_next, r_next, H_next, F_pre_next, workspace,
+           workspace_bytes, stream, check, with_pre):
+    z = _Sizes(B, n, C, eb, pb)
+    pp, bp, bq, br, lg, rr, hh = _coeff_args(z, phi_next, b_pre, b_post, b_res, logits_next, r_next, H_next)
+    wb = _ws_bytes(workspace, workspace_bytes)
+    args = [int(B), int(n), int(C), _ptr(X_t, z.x, eb, "X_t"), _ptr(F_out, z.f, eb, "F_out"),
+            _ptr(H, z.coef, 4, "H"), _ptr(X_next, z.x, eb, "X_next"), pp, float(alpha_pre),
+            float(alpha_post), float(alpha_res), bp, bq, br, lg, rr, hh]
+    if with_pre:
+        args.append(_ptr(F_pre_next, z.f, eb, "F_pre_next"))
+    args += [_ptr(workspace, wb, None, "workspace"), wb, _stream(stream)]
+    st = fn(*args)
     if check:
-        _check(st, "mhc_post_res")
+        _check(st, name)
     return st
 
 
@@ -182,16 +272,9 @@ def mhc_post_res_coeffs(B, n, C, X_t, F_out, H, X_next, phi_next, alpha_pre, alp
                         alpha_res, b_pre, b_post, b_res, logits_next, r_next, H_next, workspace,
                         workspace_bytes=None, stream=None, check=True):
     """Step (4b) of this layer fused with steps (1)-(3) of the next (see include/mhc.h)."""
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = load().mhc_post_res_coeffs(int(B), int(n), int(C), _ptr(X_t), _ptr(F_out), _ptr(H),
-                                    _ptr(X_next), _ptr(phi_next), float(alpha_pre),
-                                    float(alpha_post), float(alpha_res), _ptr(b_pre), _ptr(b_post),
-                                    _ptr(b_res), _ptr(logits_next), _ptr(r_next), _ptr(H_next),
-                                    _ptr(workspace), int(workspace_bytes), _stream(stream))
-    if check:
-        _check(st, "mhc_post_res_coeffs")
-    return st
+    return _fused(load().mhc_post_res_coeffs, "mhc_post_res_coeffs", 2, 2, B, n, C, X_t, F_out, H,
+                  X_next, phi_next, alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res,
+                  logits_next, r_next, H_next, None, workspace, workspace_bytes, stream, check, False)
 
 
 def mhc_post_res_coeffs_pre_workspace_size(B, n, C):
@@ -207,17 +290,20 @@ def mhc_post_res_coeffs_pre(B, n, C, X_t, F_out, H, X_next, phi_next, alpha_pre,
                             F_pre_next, workspace, workspace_bytes=None, stream=None, check=True):
     """Step (4b) of this layer, then steps (1)-(3) and (4a) of the next, in
     one pass where the shape allows (see include/mhc.h)."""
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = load().mhc_post_res_coeffs_pre(int(B), int(n), int(C), _ptr(X_t), _ptr(F_out), _ptr(H),
-                                        _ptr(X_next), _ptr(phi_next), float(alpha_pre),
-                                        float(alpha_post), float(alpha_res), _ptr(b_pre),
-                                        _ptr(b_post), _ptr(b_res), _ptr(logits_next), _ptr(r_next),
-                                        _ptr(H_next), _ptr(F_pre_next), _ptr(workspace),
-                                        int(workspace_bytes), _stream(stream))
-    if check:
-        _check(st, "mhc_post_res_coeffs_pre")
-    return st
+    return _fused(load().mhc_post_res_coeffs_pre, "mhc_post_res_coeffs_pre", 2, 2, B, n, C, X_t,
+                  F_out, H, X_next, phi_next, alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res,
+                  logits_next, r_next, H_next, F_pre_next, workspace, workspace_bytes, stream, check,
+                  True)
+
+
+def mhc_post_res_coeffs_pre_check(B, n, C, workspace, fp8=False, workspace_bytes=None, stream=None):
+    """Status of the last one-pass call of shape (B, n, C) on `workspace`:
+    MHC_OK, or MHC_ERR_INCOMPLETE if one of its waits gave up (synchronises
+    the stream; see include/mhc.h).  Returns the status, never raises on it."""
+    wb = _ws_bytes(workspace, workspace_bytes)
+    return int(load().mhc_post_res_coeffs_pre_check(int(B), int(n), int(C), 1 if fp8 else 0,
+                                                     _ptr(workspace, wb, None, "workspace"), wb,
+                                                     _stream(stream)))
 
 
 def mhc_post_res_coeffs_pre_fp8_workspace_size(B, n, C):
@@ -233,17 +319,10 @@ def mhc_post_res_coeffs_pre_fp8(B, n, C, X_t, F_out, H, X_next, phi_next, alpha_
                                 F_pre_next, workspace, workspace_bytes=None, stream=None,
                                 check=True):
     """mhc_post_res_coeffs_pre on the E4M3 residual stream (see include/mhc.h)."""
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = load().mhc_post_res_coeffs_pre_fp8(int(B), int(n), int(C), _ptr(X_t), _ptr(F_out), _ptr(H),
-                                            _ptr(X_next), _ptr(phi_next), float(alpha_pre),
-                                            float(alpha_post), float(alpha_res), _ptr(b_pre),
-                                            _ptr(b_post), _ptr(b_res), _ptr(logits_next),
-                                            _ptr(r_next), _ptr(H_next), _ptr(F_pre_next),
-                                            _ptr(workspace), int(workspace_bytes), _stream(stream))
-    if check:
-        _check(st, "mhc_post_res_coeffs_pre_fp8")
-    return st
+    return _fused(load().mhc_post_res_coeffs_pre_fp8, "mhc_post_res_coeffs_pre_fp8", 1, 2, B, n, C,
+                  X_t, F_out, H, X_next, phi_next, alpha_pre, alpha_post, alpha_res, b_pre, b_post,
+                  b_res, logits_next, r_next, H_next, F_pre_next, workspace, workspace_bytes, stream,
+                  check, True)
 
 
 # FP8 (E4M3) residual-stream variant: same arguments, with X_t, F_out, F_pre
@@ -256,32 +335,20 @@ def mhc_coeffs_fp8_workspace_size(B, n, C):
 def mhc_coeffs_fp8(B, n, C, X_t, phi, alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res,
                    logits, r, H, workspace, workspace_bytes=None, stream=None, check=True):
     """Steps (1)-(3) on an E4M3 X_t (see include/mhc.h)."""
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = load().mhc_coeffs_fp8(int(B), int(n), int(C), _ptr(X_t), _ptr(phi), float(alpha_pre),
-                               float(alpha_post), float(alpha_res), _ptr(b_pre), _ptr(b_post),
-                               _ptr(b_res), _ptr(logits), _ptr(r), _ptr(H), _ptr(workspace),
-                               int(workspace_bytes), _stream(stream))
-    if check:
-        _check(st, "mhc_coeffs_fp8")
-    return st
+    return _coeffs(load().mhc_coeffs_fp8, "mhc_coeffs_fp8", 1, 2, B, n, C, X_t, phi, alpha_pre,
+                   alpha_post, alpha_res, b_pre, b_post, b_res, logits, r, H, workspace,
+                   workspace_bytes, stream, check)
 
 
 def mhc_pre_fp8(B, n, C, X_t, H, F_pre, stream=None, check=True):
     """Step (4a) on the E4M3 residual stream (see include/mhc.h)."""
-    st = load().mhc_pre_fp8(int(B), int(n), int(C), _ptr(X_t), _ptr(H), _ptr(F_pre), _stream(stream))
-    if check:
-        _check(st, "mhc_pre_fp8")
-    return st
+    return _pre(load().mhc_pre_fp8, "mhc_pre_fp8", 1, B, n, C, X_t, H, F_pre, stream, check)
 
 
 def mhc_post_res_fp8(B, n, C, X_t, F_out, H, X_next, stream=None, check=True):
     """Step (4b) on the E4M3 residual stream (see include/mhc.h)."""
-    st = load().mhc_post_res_fp8(int(B), int(n), int(C), _ptr(X_t), _ptr(F_out), _ptr(H),
-                                 _ptr(X_next), _stream(stream))
-    if check:
-        _check(st, "mhc_post_res_fp8")
-    return st
+    return _post_res(load().mhc_post_res_fp8, "mhc_post_res_fp8", 1, B, n, C, X_t, F_out, H, X_next,
+                     stream, check)
 
 
 def mhc_post_res_coeffs_fp8_workspace_size(B, n, C):
@@ -292,17 +359,9 @@ def mhc_post_res_coeffs_fp8(B, n, C, X_t, F_out, H, X_next, phi_next, alpha_pre,
                             alpha_res, b_pre, b_post, b_res, logits_next, r_next, H_next,
                             workspace, workspace_bytes=None, stream=None, check=True):
     """mhc_post_res_coeffs on the E4M3 residual stream (see include/mhc.h)."""
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = load().mhc_post_res_coeffs_fp8(int(B), int(n), int(C), _ptr(X_t), _ptr(F_out), _ptr(H),
-                                        _ptr(X_next), _ptr(phi_next), float(alpha_pre),
-                                        float(alpha_post), float(alpha_res), _ptr(b_pre),
-                                        _ptr(b_post), _ptr(b_res), _ptr(logits_next), _ptr(r_next),
-                                        _ptr(H_next), _ptr(workspace), int(workspace_bytes),
-                                        _stream(stream))
-    if check:
-        _check(st, "mhc_post_res_coeffs_fp8")
-    return st
+    return _fused(load().mhc_post_res_coeffs_fp8, "mhc_post_res_coeffs_fp8", 1, 2, B, n, C, X_t, F_out,
+                  H, X_next, phi_next, alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res,
+                  logits_next, r_next, H_next, None, workspace, workspace_bytes, stream, check, False)
 
 
 def mhc_coeffs_phi32_workspace_size(B, n, C):
@@ -312,15 +371,9 @@ def mhc_coeffs_phi32_workspace_size(B, n, C):
 def mhc_coeffs_phi32(B, n, C, X_t, phi, alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res,
                      logits, r, H, workspace, workspace_bytes=None, stream=None, check=True):
     """Steps (1)-(3) with an fp32 phi (see include/mhc.h)."""
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = load().mhc_coeffs_phi32(int(B), int(n), int(C), _ptr(X_t), _ptr(phi), float(alpha_pre),
-                                 float(alpha_post), float(alpha_res), _ptr(b_pre), _ptr(b_post),
-                                 _ptr(b_res), _ptr(logits), _ptr(r), _ptr(H), _ptr(workspace),
-                                 int(workspace_bytes), _stream(stream))
-    if check:
-        _check(st, "mhc_coeffs_phi32")
-    return st
+    return _coeffs(load().mhc_coeffs_phi32, "mhc_coeffs_phi32", 2, 4, B, n, C, X_t, phi, alpha_pre,
+                   alpha_post, alpha_res, b_pre, b_post, b_res, logits, r, H, workspace,
+                   workspace_bytes, stream, check)
 
 
 def mhc_post_res_coeffs_phi32_workspace_size(B, n, C):
@@ -331,24 +384,19 @@ def mhc_post_res_coeffs_phi32(B, n, C, X_t, F_out, H, X_next, phi_next, alpha_pr
                               alpha_res, b_pre, b_post, b_res, logits_next, r_next, H_next,
                               workspace, workspace_bytes=None, stream=None, check=True):
     """mhc_post_res_coeffs with an fp32 phi_next (see include/mhc.h)."""
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = load().mhc_post_res_coeffs_phi32(int(B), int(n), int(C), _ptr(X_t), _ptr(F_out), _ptr(H),
-                                          _ptr(X_next), _ptr(phi_next), float(alpha_pre),
-                                          float(alpha_post), float(alpha_res), _ptr(b_pre),
-                                          _ptr(b_post), _ptr(b_res), _ptr(logits_next), _ptr(r_next),
-                                          _ptr(H_next), _ptr(workspace), int(workspace_bytes),
-                                          _stream(stream))
-    if check:
-        _check(st, "mhc_post_res_coeffs_phi32")
-    return st
+    return _fused(load().mhc_post_res_coeffs_phi32, "mhc_post_res_coeffs_phi32", 2, 4, B, n, C, X_t,
+                  F_out, H, X_next, phi_next, alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res,
+                  logits_next, r_next, H_next, None, workspace, workspace_bytes, stream, check, False)
 
 
 def mhc_lazy_prenorm_gemm(M, N, K, A, W, C, rstd=None, eps=1e-5, stream=None, check=True):
     """C = rmsnorm(A) @ W^T (A bf16 [M, K], W bf16 [N, K], C bf16 [M, N]); rstd
     fp32 [M] if given (see include/mhc.h)."""
-    st = load().mhc_lazy_prenorm_gemm(int(M), int(N), int(K), _ptr(A), _ptr(W), float(eps), _ptr(C),
-                                      _ptr(rstd), _stream(stream))
+    M, N, K = int(M), int(N), int(K)
+    m = max(M, 0)
+    st = load().mhc_lazy_prenorm_gemm(M, N, K, _ptr(A, m * K * 2, 2, "A"), _ptr(W, max(N, 0) * K * 2, 2, "W"),
+                                      float(eps), _ptr(C, m * max(N, 0) * 2, 2, "C"),
+                                      _ptr(rstd, m * 4, 4, "rstd"), _stream(stream))
     if check:
         _check(st, "mhc_lazy_prenorm_gemm")
     return st

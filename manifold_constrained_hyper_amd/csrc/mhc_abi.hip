@@ -4,7 +4,8 @@
 #include "mhc_launch.h"
 
 #include <stdint.h>
-#include <cstdlib>
+#include <atomic>
+#include <cstring>
 
 namespace {
 
@@ -72,10 +73,7 @@ enum class CoeffsPath { kSmall, kSplitK, kPersistent };
 CoeffsPath coeffs_path(int64_t B, int32_t n, int64_t C, Elt e) {
   if (mhc::use_coeffs_small(B, n, C)) return CoeffsPath::kSmall;
   if (e.phi32) return CoeffsPath::kSplitK;  // fp32 phi: small-B kernel or split-K through LDS
-  bool persistent = false;
-  if (const char *v = std::getenv("MHC_GEMM_ALGO"))
-    if (std::strtol(v, nullptr, 10) == 2) persistent = true;
-  if (!persistent) return CoeffsPath::kSplitK;
+  if (mhc::tune(mhc::kTuneGemmAlgo) != 2) return CoeffsPath::kSplitK;
   return C % 32 == 0 ? CoeffsPath::kPersistent : CoeffsPath::kSmall;
 }
 
@@ -195,10 +193,10 @@ enum class FusedRoute { kSmall, kTwoPass, kFused };
 FusedRoute fused_route(int64_t B, int32_t n, int64_t C, Elt e) {
   if (mhc::use_coeffs_small(B, n, C)) return FusedRoute::kSmall;
   if (e.phi32) return FusedRoute::kTwoPass;  // the fused kernel takes bf16 phi only
-  if (n == 8 && !std::getenv("MHC_FUSED_N8")) return FusedRoute::kTwoPass;
+  if (n == 8 && mhc::tune(mhc::kTuneFusedN8) <= 0) return FusedRoute::kTwoPass;
   if (e.fp8) {
-    if (const char *v = std::getenv("MHC_FUSED_FP8"))
-      return std::strtol(v, nullptr, 10) == 0 ? FusedRoute::kTwoPass : FusedRoute::kFused;
+    const int64_t v = mhc::tune(mhc::kTuneFusedFp8);
+    if (v >= 0) return v == 0 ? FusedRoute::kTwoPass : FusedRoute::kFused;
     if (!mhc::plan_post_res_next(B, n, C, false, true).fixed) return FusedRoute::kTwoPass;
   }
   return FusedRoute::kFused;
@@ -220,8 +218,7 @@ size_t post_res_coeffs_ws_bytes(int64_t B, int32_t n, int64_t C, Elt e) {
 // mhc_pre(_fp8) on X_next.  MHC_FUSED_PRE=0 forces the latter.
 bool pre_fused(int64_t B, int32_t n, int64_t C, Elt e) {
   if (e.phi32) return false;
-  if (const char *v = std::getenv("MHC_FUSED_PRE"))
-    if (std::strtol(v, nullptr, 10) == 0) return false;
+  if (mhc::tune(mhc::kTuneFusedPre) == 0) return false;
   return fused_route(B, n, C, e) == FusedRoute::kFused && mhc::pre_mode_fits(B, n, C);
 }
 
@@ -252,7 +249,7 @@ int post_res_coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t
       (with_pre && !aligned(F_pre_next, 16)))
     return MHC_ERR_UNSUPPORTED;
   const FusedRoute route = fused_route(B, n, C, e);
-  const bool one_pass = with_pre && pre_fused(B, n, C, e);
+  bool one_pass = with_pre && pre_fused(B, n, C, e);
   const mhc::FusedPlan plan = mhc::plan_post_res_next(B, n, C, one_pass, e.fp8);
   const size_t ws_need = with_pre ? post_res_coeffs_pre_ws_bytes(B, n, C, e) : post_res_coeffs_ws_bytes(B, n, C, e);
   const int64_t N = ncoef(n), K = (int64_t)n * C;
@@ -274,8 +271,22 @@ int post_res_coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t
   if (workspace_bytes < ws_need) return MHC_ERR_WORKSPACE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  int64_t grid = 0;
   if (one_pass) {
-    const mhc::PreOut po{F_pre_next, b_pre, alpha_pre};
+    // The pass needs every workgroup of a round resident at once: size the
+    // grid from what the device and the stream's CUs hold, and run the two
+    // calls instead when not even one row tile's slices fit together.
+    grid = mhc::pre_mode_grid(plan.row_tiles * plan.split, plan.split,
+                              mhc::pre_mode_resident(n, e.fp8, s), mhc::tune(mhc::kTuneFusedWgs));
+    if (grid == 0) {
+      one_pass = false;
+      // The give-up word then reports no give-up.
+      st = from_hip(mhc::launch_zero(static_cast<char *>(workspace) + plan.flag_offset, 16, s));
+      if (st != MHC_OK) return st;
+    }
+  }
+  if (one_pass) {
+    const mhc::PreOut po{F_pre_next, b_pre, alpha_pre, grid};
     st = from_hip(mhc::launch_post_res_next(plan, n, e.fp8 ? mhc::kFusedApplyPreFp8 : mhc::kFusedApplyPreBf16,
                                             B, C, X_t, F_out, H, X_next, phi_next, workspace, s, &po));
     if (st != MHC_OK) return st;
@@ -319,7 +330,43 @@ int post_res_coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t
 
 constexpr Elt kBf16{false, false}, kFp8{true, false}, kPhi32{false, true};
 
+// Route and launch-shape overrides (mhc_tuning_set): -1 = unset.
+std::atomic<int64_t> g_tune[mhc::kTuneCount] = {};
+std::atomic<bool> g_tune_init{false};
+
+struct TuneName {
+  const char *name;
+  mhc::TuneKey key;
+};
+constexpr TuneName kTuneNames[] = {
+    {"MHC_SMALL_MAX_B", mhc::kTuneSmallMaxB}, {"MHC_GEMM_ALGO", mhc::kTuneGemmAlgo},
+    {"MHC_SPLIT_K", mhc::kTuneSplitK},        {"MHC_GEMM_WGS", mhc::kTuneGemmWgs},
+    {"MHC_GEMM_MB", mhc::kTuneGemmMb},        {"MHC_FUSED_N8", mhc::kTuneFusedN8},
+    {"MHC_FUSED_FP8", mhc::kTuneFusedFp8},    {"MHC_FUSED_FIXED", mhc::kTuneFusedFixed},
+    {"MHC_FUSED_SPU", mhc::kTuneFusedSpu},    {"MHC_FUSED_WGS", mhc::kTuneFusedWgs},
+    {"MHC_FUSED_PRE", mhc::kTuneFusedPre},
+};
+static_assert(sizeof(kTuneNames) / sizeof(kTuneNames[0]) == mhc::kTuneCount, "one name per key");
+
+void tune_reset_all() {
+  for (auto &v : g_tune) v.store(-1, std::memory_order_relaxed);
+}
+
+void tune_init() {
+  if (!g_tune_init.load(std::memory_order_acquire)) {
+    tune_reset_all();
+    g_tune_init.store(true, std::memory_order_release);
+  }
+}
+
 }  // namespace
+
+namespace mhc {
+int64_t tune(TuneKey k) {
+  if (!g_tune_init.load(std::memory_order_acquire)) return -1;
+  return g_tune[k].load(std::memory_order_relaxed);
+}
+}  // namespace mhc
 
 extern "C" {
 
@@ -330,8 +377,25 @@ const char *mhc_status_string(int status) {
     case MHC_ERR_UNSUPPORTED: return "MHC_ERR_UNSUPPORTED: n not in {1,2,4,8}, C % 8 != 0 (C % 16 for E4M3, C % 32 for the fused call), size too large or misaligned pointer";
     case MHC_ERR_WORKSPACE: return "MHC_ERR_WORKSPACE: workspace smaller than the call's workspace-size function returns";
     case MHC_ERR_HIP: return "MHC_ERR_HIP: the HIP runtime reported an error";
+    case MHC_ERR_INCOMPLETE: return "MHC_ERR_INCOMPLETE: a one-pass call gave up waiting for another workgroup; its F_pre_next holds NaN where it gave up";
     default: return "MHC_ERR_UNKNOWN";
   }
+}
+
+int mhc_tuning_set(const char *name, int64_t value) {
+  if (!name) return MHC_ERR_INVALID_ARG;
+  tune_init();
+  for (const TuneName &t : kTuneNames)
+    if (std::strcmp(t.name, name) == 0) {
+      g_tune[t.key].store(value < 0 ? -1 : value, std::memory_order_relaxed);
+      return MHC_OK;
+    }
+  return MHC_ERR_INVALID_ARG;
+}
+
+void mhc_tuning_reset(void) {
+  tune_init();
+  tune_reset_all();
 }
 
 size_t mhc_coeffs_workspace_size(int64_t B, int32_t n, int64_t C) {
@@ -393,6 +457,25 @@ int mhc_post_res_coeffs_pre(int64_t B, int32_t n, int64_t C, const void *X_t, co
   return post_res_coeffs_impl(kBf16, B, n, C, X_t, F_out, H, X_next, phi_next, alpha_pre,
                               alpha_post, alpha_res, b_pre, b_post, b_res, logits_next, r_next,
                               H_next, workspace, workspace_bytes, stream, true, F_pre_next);
+}
+
+int mhc_post_res_coeffs_pre_check(int64_t B, int32_t n, int64_t C, int32_t fp8,
+                                  const void *workspace, size_t workspace_bytes, void *stream) {
+  const Elt e = fp8 ? kFp8 : kBf16;
+  const int st = check_shape_elt(B, n, C, e);
+  if (st != MHC_OK) return st;
+  if (C % 32 != 0) return MHC_ERR_UNSUPPORTED;
+  if (B == 0 || !pre_fused(B, n, C, e)) return MHC_OK;  // the two calls never give up
+  if (!workspace) return MHC_ERR_INVALID_ARG;
+  if (workspace_bytes < post_res_coeffs_pre_ws_bytes(B, n, C, e)) return MHC_ERR_WORKSPACE;
+  const mhc::FusedPlan plan = mhc::plan_post_res_next(B, n, C, true, e.fp8);
+  uint32_t word = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(&word, static_cast<const char *>(workspace) + plan.flag_offset, sizeof(word),
+                     hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return MHC_ERR_HIP;
+  return word == 0 ? MHC_OK : MHC_ERR_INCOMPLETE;
 }
 
 int32_t mhc_post_res_coeffs_pre_one_pass(int64_t B, int32_t n, int64_t C) {

@@ -329,11 +329,7 @@ SmallPlan plan_coeffs_small(int64_t B, int n, int64_t C) {
 }
 
 bool use_coeffs_small(int64_t B, int n, int64_t C) {
-  int64_t max_b = kSmallMaxB;
-  if (const char *e = std::getenv("MHC_SMALL_MAX_B")) {  // tuning / test override (0: never)
-    const long v = std::strtol(e, nullptr, 10);
-    if (v >= 0) max_b = v;
-  }
+  const int64_t max_b = tune(kTuneSmallMaxB) >= 0 ? tune(kTuneSmallMaxB) : kSmallMaxB;  // 0: never
   return B <= max_b && plan_coeffs_small(B, n, C).split <= kSmallMaxSplit;
 }
 

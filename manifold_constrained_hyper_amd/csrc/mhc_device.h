@@ -42,9 +42,22 @@ __device__ __forceinline__ f32x2 fp8_hi2(uint32_t w) {  // elements 2, 3
   return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
 }
 __device__ __forceinline__ float sat_e4m3(float x) { return __builtin_amdgcn_fmed3f(x, -448.0f, 448.0f); }
+// Byte k of w becomes the NaN code 0x7F where input k is NaN.
+__device__ __forceinline__ uint32_t fp8x4_nan_fix(uint32_t w, float a, float b, float c, float d) {
+  const uint32_t m = (a != a ? 0x000000ffu : 0u) | (b != b ? 0x0000ff00u : 0u) |
+                     (c != c ? 0x00ff0000u : 0u) | (d != d ? 0xff000000u : 0u);
+  return (w & ~m) | (0x7f7f7f7fu & m);
+}
 __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
   const int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(a), sat_e4m3(b), 0, false);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(c), sat_e4m3(d), w, true);
+  const uint32_t r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(c), sat_e4m3(d), w, true);
+  // The clamp takes a NaN to -448; a NaN keeps the NaN code 0x7F instead.
+  // The sum is NaN when one of the four is (or when infinities of both signs
+  // meet, which the per-value test then sorts out), so the common case costs
+  // three adds and a compare.
+  const float s = (a + b) + (c + d);
+  if (__builtin_expect(s != s, 0)) return fp8x4_nan_fix(r, a, b, c, d);
+  return r;
 }
 // Eight E4M3 values (two words) -> the same eight values as bf16 (exact).
 // gfx950's scaled OCP conversion with scale 1.0 widens a pair straight to

@@ -375,6 +375,21 @@ hipError_t launch_pack_phi(int n, int64_t K, int64_t ksteps, const void *phi, vo
   return hipGetLastError();
 }
 
+namespace {
+__global__ __launch_bounds__(256) void zero_kernel(u32x4 *__restrict__ p, int64_t nv) {
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < nv; i += (int64_t)gridDim.x * 256)
+    store16_plain(p + i, u32x4{0u, 0u, 0u, 0u});
+}
+}  // namespace
+
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t st) {
+  const int64_t nv = (int64_t)(bytes / 16);
+  if (nv <= 0) return hipSuccess;
+  const int64_t blocks = (nv + 255) / 256;
+  zero_kernel<<<dim3((uint32_t)(blocks < 1024 ? blocks : 1024)), 256, 0, st>>>(static_cast<u32x4 *>(p), nv);
+  return hipGetLastError();
+}
+
 // Instantiations used by the library (see plan_gemm in mhc_gemm_rms.hip).
 template hipError_t launch_gemm_lds_typed<1, 1, 256, 3, 2, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
 template hipError_t launch_gemm_lds_typed<2, 1, 256, 3, 2, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);

@@ -280,10 +280,7 @@ GemmPlan plan_gemm_custom(int64_t B, int n, int64_t C, int algo, int mb, int kc,
   p.row_tiles = (B + 64 * p.mb - 1) / (64 * p.mb);
   const int64_t kchunks = (K + p.kc - 1) / p.kc;
   int64_t want = (target_wgs + p.row_tiles - 1) / p.row_tiles;
-  if (const char *e = getenv("MHC_SPLIT_K")) {  // tuning override
-    const long v = strtol(e, nullptr, 10);
-    if (v > 0) want = v;
-  }
+  if (tune(kTuneSplitK) > 0) want = tune(kTuneSplitK);  // tuning override
   if (want < 1) want = 1;
   if (want > kchunks) want = kchunks;
   const int64_t chunks_per_slice = (kchunks + want - 1) / want;
@@ -306,11 +303,7 @@ GemmPlan plan_gemm(int64_t B, int n, int64_t C, bool fp8_x, bool phi32) {
   // fp32 phi (bf16 X): X staged through LDS in 128-k chunks, so that the
   // doubled (hi + lo) phi blocks fit the ring: four stages, two at n = 8.
   if (phi32) {
-    int64_t target = 256;
-    if (const char *e = getenv("MHC_GEMM_WGS")) {
-      const long v = strtol(e, nullptr, 10);
-      if (v > 0) target = v;
-    }
+    const int64_t target = tune(kTuneGemmWgs) > 0 ? tune(kTuneGemmWgs) : 256;
     GemmPlan p = plan_gemm_custom(B, n, C, 1, 1, 128, n == 8 ? 2 : 4, target);
     p.phi_parts = 2;
     p.phip_bytes *= 2;
@@ -324,30 +317,19 @@ GemmPlan plan_gemm(int64_t B, int n, int64_t C, bool fp8_x, bool phi32) {
   // partials per row.  E4M3 X: 256-k chunks (16 pieces of 16 bytes per row),
   // four stages (two at n = 8, whose phi blocks are larger).
   if (fp8_x) {
-    int64_t target = 256;
-    if (const char *e = getenv("MHC_GEMM_WGS")) {
-      const long v = strtol(e, nullptr, 10);
-      if (v > 0) target = v;
-    }
+    const int64_t target = tune(kTuneGemmWgs) > 0 ? tune(kTuneGemmWgs) : 256;
     int mb = n == 8 ? 1 : 2;  // 128-row tiles: phi per X byte as for bf16 with 64 rows
-    if (const char *e = getenv("MHC_GEMM_MB")) {
-      const long v = strtol(e, nullptr, 10);
-      if (v == 1 || (v == 2 && n != 8)) mb = (int)v;
-    }
+    const int64_t v = tune(kTuneGemmMb);
+    if (v == 1 || (v == 2 && n != 8)) mb = (int)v;
     GemmPlan p = plan_gemm_custom(B, n, C, 1, mb, 256, n == 8 ? 2 : (mb == 2 ? 3 : 4), target);
     p.xb = 1;
     return p;
   }
   const int kc = (n == 8) ? 128 : 256;
   const int stages = (n == 8) ? 4 : 3;
-  int64_t target = 256;
-  if (const char *e = getenv("MHC_GEMM_ALGO")) {  // tuning override: 0 = register path
-    if (strtol(e, nullptr, 10) == 0) return plan_gemm_custom(B, n, C, 0, (B >= 1024) ? 2 : 1, kGemmKC, 1, kGemmTargetWGs);
-  }
-  if (const char *e = getenv("MHC_GEMM_WGS")) {  // tuning override
-    const long v = strtol(e, nullptr, 10);
-    if (v > 0) target = v;
-  }
+  if (tune(kTuneGemmAlgo) == 0)  // tuning override: the register path
+    return plan_gemm_custom(B, n, C, 0, (B >= 1024) ? 2 : 1, kGemmKC, 1, kGemmTargetWGs);
+  const int64_t target = tune(kTuneGemmWgs) > 0 ? tune(kTuneGemmWgs) : 256;
   return plan_gemm_custom(B, n, C, 1, 1, kc, stages, target);
 }
 

@@ -8,6 +8,27 @@
 
 namespace mhc {
 
+// Route and launch-shape overrides for tests and tuning (mhc_tuning_set in
+// mhc.h).  Every key starts unset (-1), which selects the measured default;
+// the library never reads the environment, so nothing outside an explicit
+// mhc_tuning_set call changes which kernels run or in what order they sum.
+enum TuneKey : int {
+  kTuneSmallMaxB = 0,  // rows up to which the one-launch small-B kernel runs (0: never)
+  kTuneGemmAlgo,       // 0: register-path product; 2: persistent product kernel
+  kTuneSplitK,         // K-slices of the split-K product (> 0)
+  kTuneGemmWgs,        // target workgroup count of the split-K product (> 0)
+  kTuneGemmMb,         // 16-row blocks per wave of the E4M3 split-K product (1 or 2)
+  kTuneFusedN8,        // > 0: the fused kernel also at n = 8
+  kTuneFusedFp8,       // 0: E4M3 fused call as apply + product; > 0: fused kernel
+  kTuneFusedFixed,     // 0 / 1: fused kernel's fixed-slice layout off / on
+  kTuneFusedSpu,       // 512-channel steps per unit of the fused kernel (> 0)
+  kTuneFusedWgs,       // workgroups of the fused kernel (> 0; never above the resident count)
+  kTuneFusedPre,       // 0: mhc_post_res_coeffs_pre(_fp8) as two calls
+  kTuneCount
+};
+// Current value of a key; -1 when unset.
+int64_t tune(TuneKey k);
+
 // Compute units of the current device (queried once per device id).
 int device_cus();
 
@@ -58,8 +79,9 @@ hipError_t launch_pack_phi(int n, int64_t K, int64_t ksteps, const void *phi, vo
 //
 // The pre-mix mode (pre = true in the plan) adds, after the zero block:
 // [rec_offset, +rec_bytes) hand-off records [B, split, PW] (4 bytes each,
-// PW = n+1 rounded up to even; zero-filled by the launch before the kernel
-// runs).
+// PW = n+1 rounded up to even) and [flag_offset, +16) the give-up word (a
+// uint32, non-zero once a wait for records gave up); both zero-filled by the
+// launch before the kernel runs.
 struct FusedPlan {
   int split;          // channel slices (K-slices of n*cw)
   int cw;             // channels per slice (multiple of 512)
@@ -68,7 +90,7 @@ struct FusedPlan {
   bool pre;           // pre-mix mode layout
   bool fixed;         // fixed-slice layout: one step per unit, whole row tiles per round
   size_t partial_bytes, dummy_offset, dummy_bytes, phip_offset, phip_bytes, zero_offset;
-  size_t rec_offset, rec_bytes, total_bytes;
+  size_t rec_offset, rec_bytes, flag_offset, total_bytes;
 };
 // prefer_fixed: take the fixed-slice layout where it fits (n <= 4) unless
 // MHC_FUSED_FIXED=0; without it, only with MHC_FUSED_FIXED=1.  The pre-mix
@@ -98,23 +120,40 @@ struct PreArgs {
   uint32_t phip_bytes;            // packed phi (< 2^31; also set in the fixed-slice layout)
   const float *b_pre;             // fp32 [n]
   float alpha_pre, inv_k;         // alpha_pre; 1 / (n C)
+  uint32_t *giveup;               // set non-zero by a wave whose wait for records gave up
 };
 // Whether the pre-mix mode can run this shape: n <= 4, at most 16
 // 512-channel steps per row (the record gather), a grid of whole row tiles
 // (a multiple of S workgroups) that fits the device, and partials and
 // records addressable by 32-bit buffer offsets.
 bool pre_mode_fits(int64_t B, int n, int64_t C);
-// pre_out: F_pre (bf16 or E4M3 [B, C], the element type of the mode) and the
-// next layer's b_pre / alpha_pre for the pre-mix modes, else null.
+// Workgroups of the pre-mix kernel (n, E4M3 or bf16) that can be resident at
+// once for launches on `st`: the per-CU occupancy the runtime reports for the
+// kernel times the compute units the stream may use (its CU mask).  Cached
+// per device and kernel, except the mask, which is read per call.
+int64_t pre_mode_resident(int n, bool fp8, hipStream_t st);
+// Grid of the pre-mix mode: whole row tiles per round (a multiple of
+// `split`), at most `resident` workgroups (and at most `wgs_cap` when that is
+// positive), no more than the `units` there are; 0 when not even one row
+// tile's `split` workgroups can be resident together (the mode must not run).
+int64_t pre_mode_grid(int64_t units, int64_t split, int64_t resident, int64_t wgs_cap);
+// pre_out: F_pre (bf16 or E4M3 [B, C], the element type of the mode), the
+// next layer's b_pre / alpha_pre and the grid (pre_mode_grid) for the
+// pre-mix modes, else null.
 struct PreOut {
   void *F_pre;
   const float *b_pre;
   float alpha_pre;
+  int64_t grid;
 };
 hipError_t launch_post_res_next(const FusedPlan &p, int n, int mode, int64_t B, int64_t C,
                                 const void *X, const void *F, const float *H, void *Y,
                                 const void *phi_next, void *ws_base, hipStream_t st,
                                 const PreOut *pre_out = nullptr);
+
+// Zero-fill [p, p + bytes) (bytes a multiple of 16, p 16-byte aligned) with a
+// small kernel (no memset node if the caller captures a graph).
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t st);
 
 // Lazy Pre-Norm GEMM C = rmsnorm(A) W^T (mhc_lazy_prenorm.hip).
 hipError_t launch_lazy_prenorm_gemm(int64_t M, int64_t N, int64_t K, const void *A, const void *W,

@@ -81,8 +81,12 @@
 // No workgroup waits for one that has not started: a wait at step t+2 needs
 // only records published at the start of step t+1 by workgroups of the same
 // round, and every workgroup publishes before it waits (induction over t;
-// all G workgroups are resident at once: one per CU).  A wait that cannot
-// end within about a second gives up and writes NaN to its F_pre vector.
+// all G workgroups are resident at once: the host sizes G from the
+// occupancy the runtime reports and the compute units of the stream).  A
+// wait that still cannot end (e.g. kernels on other streams hold CUs) gives
+// up after about a second, writes NaN to its F_pre vector and sets the
+// give-up word of the workspace, which the caller can read back
+// (mhc_post_res_coeffs_pre_check).
 #include "mhc_device.h"
 #include "mhc_finish.h"
 #include "mhc_launch.h"
@@ -401,6 +405,12 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
   // address.
   auto emit = [&](int q, const float (&hp)[NS], bool poison, bool real, const vec (&kv)[NS]) {
     const Step sp = step_at(q);
+    if (poison) {
+      // Report the give-up (a vector buffer store, agent scope; every lane
+      // stores the same word).
+      const __amdgpu_buffer_rsrc_t frs = __builtin_amdgcn_make_buffer_rsrc(pa.giveup, (short)0, 4, kRsrcWord3);
+      __builtin_amdgcn_raw_buffer_store_b32(1u, frs, 0u, 0, kSc1);
+    }
     const int row = sp.row0 + wave;
     const int cst = min(sp.c0 + 8 * lane, sp.c_end - 8);
     // fp32 FMA chain over the streams in stream order from zero, one rounding
@@ -819,7 +829,6 @@ hipError_t launch_mode(int n, bool fixed, int64_t B, int64_t C, int spu, int spl
 }
 
 constexpr int kRecordSlices = 16;  // slices one record gather covers
-constexpr int kPreWgsPerCu = 1;    // resident pre-mix workgroups per CU (its LDS admits no second)
 constexpr int kPreRows = 16;       // rows per tile of the pre-mix mode (FusedTile::R)
 
 }  // namespace
@@ -847,7 +856,7 @@ bool pre_mode_fits(int64_t B, int n, int64_t C) {
   const int64_t N = (int64_t)n * n + 2 * n;
   const int64_t lim = int64_t(1) << 31;
   const int64_t phip_bytes = ((int64_t)n * C + 31) / 32 * ((N + 15) / 16) * 1024;
-  return steps <= kRecordSlices && steps <= kPreWgsPerCu * device_cus() && C * 2 < lim && phip_bytes < lim &&
+  return steps <= kRecordSlices && steps <= device_cus() && C * 2 < lim && phip_bytes < lim &&
          steps * B * ((n + 2) & ~1) * 4 < lim && steps * B * (N + 1) * 4 < lim;
 }
 
@@ -872,7 +881,7 @@ FusedPlan plan_post_res_next(int64_t B, int n, int64_t C, bool pre, bool prefer_
   p.fixed = pre;
   if (!pre && fixed_layout_fits(n, C)) {
     p.fixed = prefer_fixed;
-    if (const char *e = std::getenv("MHC_FUSED_FIXED")) p.fixed = std::strtol(e, nullptr, 10) != 0;
+    if (tune(kTuneFusedFixed) >= 0) p.fixed = tune(kTuneFusedFixed) != 0;
   }
   // Steps per unit: the largest divisor of the row's step count that still
   // leaves at least 7 slices (fewer when the row is shorter), so that the
@@ -887,10 +896,8 @@ FusedPlan plan_post_res_next(int64_t B, int n, int64_t C, bool pre, bool prefer_
   if (!p.fixed) {
     for (int64_t d = 1; d <= steps; ++d)
       if (steps % d == 0 && steps / d >= want) spu = d;
-    if (const char *e = std::getenv("MHC_FUSED_SPU")) {
-      const long v = std::strtol(e, nullptr, 10);
-      if (v >= 1 && v <= steps) spu = v;
-    }
+    const int64_t v = tune(kTuneFusedSpu);
+    if (v >= 1 && v <= steps) spu = v;
   }
   p.cw = (int)(spu * kStepCh);
   p.split = (int)((steps + spu - 1) / spu);
@@ -903,8 +910,60 @@ FusedPlan plan_post_res_next(int64_t B, int n, int64_t C, bool pre, bool prefer_
   p.zero_offset = p.phip_offset + p.phip_bytes;
   p.rec_offset = p.zero_offset + 256;
   p.rec_bytes = pre ? (size_t)p.split * (size_t)B * (size_t)((n + 2) & ~1) * 4 : 0;
-  p.total_bytes = p.rec_offset + ((p.rec_bytes + 15) & ~(size_t)15);
+  p.flag_offset = p.rec_offset + ((p.rec_bytes + 15) & ~(size_t)15);
+  p.total_bytes = p.flag_offset + (pre ? 16 : 0);
   return p;
+}
+
+int64_t pre_mode_grid(int64_t units, int64_t split, int64_t resident, int64_t wgs_cap) {
+  if (units < 1 || split < 1 || resident < 1) return 0;
+  int64_t cap = resident;
+  if (wgs_cap >= 1 && wgs_cap < cap) cap = wgs_cap;
+  cap = (cap / split) * split;  // whole row tiles per round
+  if (cap < split) return 0;
+  return units < cap ? units : cap;
+}
+
+int64_t pre_mode_resident(int n, bool fp8, hipStream_t st) {
+  // Per-CU occupancy of the pre-mix kernel, cached per device and variant.
+  static std::atomic<int> occ_cache[64][3][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  const int ni = n == 1 ? 0 : (n == 2 ? 1 : (n == 4 ? 2 : -1));
+  if (ni < 0) return 0;
+  int occ = (dev >= 0 && dev < 64) ? occ_cache[dev][ni][fp8].load(std::memory_order_relaxed) : 0;
+  if (occ <= 0) {
+    const void *fn = nullptr;
+    switch (ni * 2 + (fp8 ? 1 : 0)) {
+      case 0: fn = reinterpret_cast<const void *>(&post_res_next_kernel<1, kFusedApplyPreBf16, true>); break;
+      case 1: fn = reinterpret_cast<const void *>(&post_res_next_kernel<1, kFusedApplyPreFp8, true>); break;
+      case 2: fn = reinterpret_cast<const void *>(&post_res_next_kernel<2, kFusedApplyPreBf16, true>); break;
+      case 3: fn = reinterpret_cast<const void *>(&post_res_next_kernel<2, kFusedApplyPreFp8, true>); break;
+      case 4: fn = reinterpret_cast<const void *>(&post_res_next_kernel<4, kFusedApplyPreBf16, true>); break;
+      default: fn = reinterpret_cast<const void *>(&post_res_next_kernel<4, kFusedApplyPreFp8, true>); break;
+    }
+    int v = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, fn, FusedTile<4, true>::THREADS, 0) != hipSuccess) {
+      (void)hipGetLastError();  // leave no sticky error for the launch check
+      return 0;
+    }
+    occ = v;
+    if (occ > 0 && dev >= 0 && dev < 64) occ_cache[dev][ni][fp8].store(occ, std::memory_order_relaxed);
+  }
+  int64_t cus = device_cus();
+  if (st != nullptr) {
+    // A stream created with a CU mask runs on the masked CUs only.
+    uint32_t mask[32] = {};
+    const uint32_t words = (uint32_t)((cus + 31) / 32 <= 32 ? (cus + 31) / 32 : 32);
+    if (hipExtStreamGetCUMask(st, words, mask) == hipSuccess) {
+      int64_t on = 0;
+      for (uint32_t w = 0; w < words; ++w) on += __builtin_popcount(mask[w]);
+      if (on > 0 && on < cus) cus = on;
+    } else {
+      (void)hipGetLastError();
+    }
+  }
+  return (int64_t)occ * cus;
 }
 
 hipError_t launch_post_res_next(const FusedPlan &p, int n, int mode, int64_t B, int64_t C,
@@ -915,9 +974,10 @@ hipError_t launch_post_res_next(const FusedPlan &p, int n, int mode, int64_t B, 
   if (pre != p.pre || (pre && !pre_out)) return hipErrorInvalidValue;
   char *base = static_cast<char *>(ws_base);
   void *phip = base + p.phip_offset;
-  // The pre-mix mode's records start from zero: the packing launch clears them.
+  // The pre-mix mode's records and give-up word start from zero: the packing
+  // launch clears them.
   hipError_t e = launch_pack_phi(n, (int64_t)n * C, p.ksteps, phi_next, phip, base + p.zero_offset, st,
-                                 pre ? base + p.rec_offset : nullptr, (p.rec_bytes + 15) & ~(size_t)15);
+                                 pre ? base + p.rec_offset : nullptr, p.total_bytes - p.rec_offset);
   if (e != hipSuccess) return e;
   float *ws = reinterpret_cast<float *>(base);
   float *dummy = reinterpret_cast<float *>(base + p.dummy_offset);
@@ -927,24 +987,21 @@ hipError_t launch_post_res_next(const FusedPlan &p, int n, int mode, int64_t B, 
   PreArgs pa{};
   if (pre) {
     // Workgroups of one row tile wait for each other's records, so the whole
-    // grid must be resident at once: one workgroup per CU (the mode's LDS
-    // admits no second), in whole row tiles (a multiple of S) so that the S
-    // slices of a tile are always taken in the same round.
-    cap *= kPreWgsPerCu;
-    if (const char *env = std::getenv("MHC_FUSED_WGS")) {  // tuning: fewer workgroups (never more)
-      const long v = std::strtol(env, nullptr, 10);
-      if (v >= 1 && v < cap) cap = (int)v;
-    }
+    // grid must be resident at once; the caller sized it (pre_mode_grid:
+    // whole row tiles per round, within the resident count).
+    const int64_t G = pre_out->grid;
+    if (G < p.split || G % p.split != 0 || G > U) return hipErrorInvalidValue;
+    cap = (int)G;
     pa.F_pre = pre_out->F_pre;
+    pa.giveup = reinterpret_cast<uint32_t *>(base + p.flag_offset);
     pa.rec = reinterpret_cast<uint32_t *>(base + p.rec_offset);
     pa.rec_bytes = (uint32_t)p.rec_bytes;
     pa.partial_bytes = (uint32_t)p.partial_bytes;
     pa.b_pre = pre_out->b_pre;
     pa.alpha_pre = pre_out->alpha_pre;
     pa.inv_k = (float)(1.0 / (double)((int64_t)n * C));
-  } else if (const char *env = std::getenv("MHC_FUSED_WGS")) {
-    const long v = std::strtol(env, nullptr, 10);
-    if (v >= 1 && v <= 65535) cap = (int)v;
+  } else if (tune(kTuneFusedWgs) >= 1 && tune(kTuneFusedWgs) <= 65535) {
+    cap = (int)tune(kTuneFusedWgs);
   }
   if (p.fixed) {
     // Whole row tiles per round (each workgroup keeps slice p(g) mod S).

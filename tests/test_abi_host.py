@@ -1,9 +1,11 @@
 """Host-only checks of the C ABI: the library loads, exports every function
 include/mhc.h declares, and rejects bad arguments before launching anything.
 
-No call here reaches a kernel launch: every call either fails validation or
-has B == 0, so these run without a GPU.  Pointers are fake addresses; the
-library never dereferences them on the host.
+Almost every call here fails validation or has B == 0, so nothing is
+launched and the tests run without a GPU.  Pointers are fake addresses; the
+library never dereferences them on the host.  The one test that lets calls
+reach a launch (to see MHC_ERR_HIP without a device) runs only on a host with
+no HIP device.
 """
 
 import ctypes
@@ -11,6 +13,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import manifold_constrained_hyper_amd as mhc
 
@@ -44,7 +47,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(5):
+    for code in range(6):
         assert mhc.mhc_status_string(code).startswith("MHC_")
     assert mhc.mhc_status_string(99) == "MHC_ERR_UNKNOWN"
 
@@ -166,9 +169,9 @@ def test_fused_pre_validation():
     assert need > 0 and _fused_pre(ws_bytes=need - 1) == mhc.MHC_ERR_WORKSPACE
 
 
-def test_fused_pre_route_and_workspace(monkeypatch):
-    monkeypatch.delenv("MHC_FUSED_PRE", raising=False)
-    monkeypatch.delenv("MHC_SMALL_MAX_B", raising=False)
+def test_fused_pre_route_and_workspace(tune):
+    tune.delenv("MHC_FUSED_PRE", raising=False)
+    tune.delenv("MHC_SMALL_MAX_B", raising=False)
     one = mhc.mhc_post_res_coeffs_pre_one_pass
     assert one(16384, 4, 7168) and one(4096, 4, 4096) and one(1000, 2, 4096) and one(300, 1, 1024)
     assert not one(64, 4, 7168)          # small B: the two calls
@@ -184,7 +187,7 @@ def test_fused_pre_route_and_workspace(monkeypatch):
     # the two-call routes need what mhc_post_res_coeffs needs
     assert mhc.mhc_post_res_coeffs_pre_workspace_size(8192, 8, 4096) == \
         mhc.mhc_post_res_coeffs_workspace_size(8192, 8, 4096)
-    monkeypatch.setenv("MHC_FUSED_PRE", "0")
+    tune.setenv("MHC_FUSED_PRE", "0")
     assert not one(16384, 4, 7168)
     assert mhc.mhc_post_res_coeffs_pre_workspace_size(B, n, C) == mhc.mhc_post_res_coeffs_workspace_size(B, n, C)
 
@@ -221,9 +224,9 @@ def test_fused_pre_fp8_validation():
     assert need > 0 and _fused_pre_fp8(ws_bytes=need - 1) == mhc.MHC_ERR_WORKSPACE
 
 
-def test_fused_pre_fp8_route_and_workspace(monkeypatch):
+def test_fused_pre_fp8_route_and_workspace(tune):
     for k in ("MHC_FUSED_PRE", "MHC_SMALL_MAX_B", "MHC_FUSED_FP8", "MHC_FUSED_FIXED"):
-        monkeypatch.delenv(k, raising=False)
+        tune.delenv(k, raising=False)
     one = mhc.mhc_post_res_coeffs_pre_fp8_one_pass
     assert one(16384, 4, 7168) and one(4096, 4, 4096) and one(1000, 2, 4096) and one(300, 1, 1024)
     assert not one(64, 4, 7168)          # small B: the two calls
@@ -236,7 +239,7 @@ def test_fused_pre_fp8_route_and_workspace(monkeypatch):
     # two calls: what mhc_post_res_coeffs_fp8 needs
     assert mhc.mhc_post_res_coeffs_pre_fp8_workspace_size(8192, 8, 4096) == \
         mhc.mhc_post_res_coeffs_fp8_workspace_size(8192, 8, 4096)
-    monkeypatch.setenv("MHC_FUSED_FP8", "0")       # E4M3 fused call as apply + product
+    tune.setenv("MHC_FUSED_FP8", "0")       # E4M3 fused call as apply + product
     assert not one(16384, 4, 7168)
     assert mhc.mhc_post_res_coeffs_pre_fp8_workspace_size(16384, 4, 7168) == \
         mhc.mhc_post_res_coeffs_fp8_workspace_size(16384, 4, 7168)
@@ -362,3 +365,91 @@ def test_phi32_validation():
     assert fused(logits=f["phi"] + K * N * 2) == mhc.MHC_ERR_INVALID_ARG
     need = mhc.mhc_post_res_coeffs_phi32_workspace_size(B, n, C)
     assert need > 0 and fused(ws_bytes=need - 1) == mhc.MHC_ERR_WORKSPACE
+
+
+def test_tuning_keys_and_no_environment(tune, monkeypatch):
+    """Routes change only through mhc_tuning_set: the environment variables
+    that once selected them are ignored, and unknown keys are rejected."""
+    one = mhc.mhc_post_res_coeffs_pre_one_pass
+    ws = mhc.mhc_post_res_coeffs_pre_workspace_size
+    base = (one(16384, 4, 7168), ws(16384, 4, 7168), mhc.mhc_coeffs_split_k(16384, 4, 7168),
+            mhc.mhc_coeffs_workspace_size(64, 4, 7168))
+    for k, v in (("MHC_FUSED_PRE", "0"), ("MHC_SMALL_MAX_B", "0"), ("MHC_SPLIT_K", "5"),
+                 ("MHC_GEMM_ALGO", "0")):
+        monkeypatch.setenv(k, v)
+    assert (one(16384, 4, 7168), ws(16384, 4, 7168), mhc.mhc_coeffs_split_k(16384, 4, 7168),
+            mhc.mhc_coeffs_workspace_size(64, 4, 7168)) == base
+    tune.setenv("MHC_SPLIT_K", 5)
+    assert mhc.mhc_coeffs_split_k(16384, 4, 7168) == 5
+    tune.delenv("MHC_SPLIT_K")
+    assert mhc.mhc_coeffs_split_k(16384, 4, 7168) == base[2]
+    tune.setenv("MHC_FUSED_PRE", 0)
+    assert not one(16384, 4, 7168)
+    mhc.mhc_tuning_reset()
+    assert one(16384, 4, 7168)
+    with pytest.raises(mhc.MhcError) as ei:
+        mhc.mhc_tuning_set("MHC_NO_SUCH_KEY", 1)
+    assert ei.value.status == mhc.MHC_ERR_INVALID_ARG
+
+
+def test_binding_checks_tensor_sizes():
+    """The binding rejects a tensor of the wrong element size, or smaller
+    than the bytes the call touches, before anything reaches the library
+    (host tensors suffice: the size check comes before the device check;
+    the other arguments are raw addresses, which are passed through)."""
+    B, n, C = 16, 4, 64
+    X, H, F, Y, W = _addrs(5)
+    with pytest.raises(ValueError, match="F_pre: 1792 bytes, the call needs 2048"):
+        mhc.mhc_pre(B, n, C, X, H, torch.empty(B, C - 8, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="X_t: element size 1"):
+        mhc.mhc_pre(B, n, C, torch.empty(B, 2 * n * C, dtype=torch.uint8), H, F)
+    with pytest.raises(ValueError, match="X_t: element size 2"):  # a bf16 tensor to an E4M3 call
+        mhc.mhc_pre_fp8(B, n, C, torch.empty(B, n * C, dtype=torch.bfloat16), H, F)
+    with pytest.raises(ValueError, match="H: "):
+        mhc.mhc_post_res(B, n, C, X, F, torch.empty(B - 1, n * n + 2 * n), Y)
+    with pytest.raises(ValueError, match="phi: element size 4"):  # fp32 phi to the bf16-phi call
+        mhc.mhc_coeffs(B, n, C, X, torch.empty(n * C, 24), 0.01, 0.01, 0.01, *_addrs(6), W,
+                       workspace_bytes=1 << 20)
+    with pytest.raises(ValueError, match="workspace"):
+        mhc.mhc_coeffs(B, n, C, X, H, 0.01, 0.01, 0.01, *_addrs(6), torch.empty(64, dtype=torch.uint8),
+                       workspace_bytes=128)
+    with pytest.raises(ValueError, match="device tensors"):  # right sizes: then the host-tensor check
+        mhc.mhc_pre(B, n, C, X, H, torch.empty(B, C, dtype=torch.bfloat16))
+
+
+def test_one_pass_grid_and_check():
+    """The one-pass grid arithmetic (whole row tiles per round within what is
+    resident) is exercised through the route, and the give-up check answers
+    without a device where no one-pass kernel can have run."""
+    # the shapes that run two calls never give up: no device access needed
+    assert mhc.mhc_post_res_coeffs_pre_check(64, 4, 7168, A, workspace_bytes=1 << 20, stream=0) == mhc.MHC_OK
+    assert mhc.mhc_post_res_coeffs_pre_check(8192, 8, 4096, A, workspace_bytes=1 << 20, stream=0) == mhc.MHC_OK
+    assert mhc.mhc_post_res_coeffs_pre_check(0, 4, 7168, None, stream=0) == mhc.MHC_OK
+    # argument errors
+    assert mhc.mhc_post_res_coeffs_pre_check(16384, 3, 7168, A, stream=0) == mhc.MHC_ERR_UNSUPPORTED
+    assert mhc.mhc_post_res_coeffs_pre_check(16384, 4, 7168, None, fp8=True, stream=0) == mhc.MHC_ERR_INVALID_ARG
+    assert mhc.mhc_post_res_coeffs_pre_check(16384, 4, 7168, None, stream=0) == mhc.MHC_ERR_INVALID_ARG
+    need = mhc.mhc_post_res_coeffs_pre_workspace_size(16384, 4, 7168)
+    assert mhc.mhc_post_res_coeffs_pre_check(16384, 4, 7168, A, workspace_bytes=need - 1,
+                                             stream=0) == mhc.MHC_ERR_WORKSPACE
+    # the one-pass workspace holds partials, packed phi, records and the give-up word
+    assert need % 16 == 0
+
+
+def _no_device():
+    return torch.cuda.device_count() == 0
+
+
+@pytest.mark.skipif(not _no_device(), reason="needs a host without a HIP device (calls use fake addresses)")
+def test_no_device_is_mhc_err_hip():
+    """Calls that pass validation but cannot launch (no HIP device) report
+    MHC_ERR_HIP; nothing aborts."""
+    X, H, F, Y = _addrs(4)
+    assert mhc.mhc_pre(16, 4, 64, X, H, F, stream=0, check=False) == mhc.MHC_ERR_HIP
+    assert mhc.mhc_post_res(16, 4, 64, X, F, H, Y, stream=0, check=False) == mhc.MHC_ERR_HIP
+    assert _fused_pre(B=16384, n=4, C=7168, **dict(zip(
+        ["X", "F", "H", "Y", "phi", "bp", "bq", "br", "logits", "r", "Hn", "Fp", "ws"],
+        [A + k * (1 << 36) for k in range(13)]))) == mhc.MHC_ERR_HIP
+    need = mhc.mhc_post_res_coeffs_pre_workspace_size(16384, 4, 7168)
+    assert mhc.mhc_post_res_coeffs_pre_check(16384, 4, 7168, A, workspace_bytes=need,
+                                             stream=0) == mhc.MHC_ERR_HIP

@@ -50,18 +50,18 @@ def _gpu():
 # with MHC_FUSED_N8), all exercised here.
 # Every one must meet the bar at every size it supports.
 @pytest.fixture(params=["default", "small", "split", "persistent"])
-def path(request, monkeypatch):
+def path(request, tune):
     for k in ("MHC_SMALL_MAX_B", "MHC_GEMM_ALGO", "MHC_FUSED_N8"):
-        monkeypatch.delenv(k, raising=False)
+        tune.delenv(k, raising=False)
     if request.param == "small":
-        monkeypatch.setenv("MHC_SMALL_MAX_B", str(1 << 30))
+        tune.setenv("MHC_SMALL_MAX_B", str(1 << 30))
     elif request.param == "split":
-        monkeypatch.setenv("MHC_SMALL_MAX_B", "0")
+        tune.setenv("MHC_SMALL_MAX_B", "0")
     elif request.param == "persistent":
-        monkeypatch.setenv("MHC_SMALL_MAX_B", "0")
-        monkeypatch.setenv("MHC_GEMM_ALGO", "2")
-        monkeypatch.setenv("MHC_FUSED_N8", "1")
-        monkeypatch.setenv("MHC_FUSED_FP8", "1")
+        tune.setenv("MHC_SMALL_MAX_B", "0")
+        tune.setenv("MHC_GEMM_ALGO", "2")
+        tune.setenv("MHC_FUSED_N8", "1")
+        tune.setenv("MHC_FUSED_FP8", "1")
     return request.param
 
 
@@ -224,16 +224,16 @@ def _layers(n, C, B, dist, seed):
 
 @pytest.mark.parametrize("kernel", ["default", "fused", "twopass", "fused_spu"])
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "large", "wide"])
-def test_fp8_fused_named(name, kernel, monkeypatch):
+def test_fp8_fused_named(name, kernel, tune):
     if kernel in ("fused", "fused_spu"):
-        monkeypatch.setenv("MHC_FUSED_FP8", "1")
-        monkeypatch.setenv("MHC_FUSED_N8", "1")
+        tune.setenv("MHC_FUSED_FP8", "1")
+        tune.setenv("MHC_FUSED_N8", "1")
         if kernel == "fused_spu":
             if synth.CONFIGS[name]["n"] == 8:
                 pytest.skip("n = 8 always runs this layout (kernel 'fused')")
-            monkeypatch.setenv("MHC_FUSED_FIXED", "0")
+            tune.setenv("MHC_FUSED_FIXED", "0")
     elif kernel == "twopass":
-        monkeypatch.setenv("MHC_FUSED_FP8", "0")
+        tune.setenv("MHC_FUSED_FP8", "0")
     _say(f"fp8 fused {name} kernel={kernel}")
     cfg = synth.CONFIGS[name]
     cur, nxt = _layers(cfg["n"], cfg["C"], cfg["B"], cfg["x_dist"], cfg["seed"])
@@ -254,11 +254,11 @@ def test_fp8_fused_ragged(B, n, C, path):
 
 
 @pytest.mark.parametrize("kernel", ["default", "fused", "twopass"])
-def test_fp8_fused_deterministic(kernel, monkeypatch):
+def test_fp8_fused_deterministic(kernel, tune):
     if kernel == "fused":
-        monkeypatch.setenv("MHC_FUSED_FP8", "1")
+        tune.setenv("MHC_FUSED_FP8", "1")
     elif kernel == "twopass":
-        monkeypatch.setenv("MHC_FUSED_FP8", "0")
+        tune.setenv("MHC_FUSED_FP8", "0")
     _say(f"fp8 fused determinism kernel={kernel}")
     cfg = synth.CONFIGS["prefill"]
     cur, nxt = _layers(cfg["n"], cfg["C"], cfg["B"], cfg["x_dist"], cfg["seed"])
@@ -266,3 +266,40 @@ def test_fp8_fused_deterministic(kernel, monkeypatch):
     _, _, b = _fused(cur, nxt)
     for k in ("X_next", "logits", "r", "H"):
         assert torch.equal(a[k].view(torch.int8), b[k].view(torch.int8)), k
+
+
+def test_fp8_nan_codes():
+    """NaN inputs (E4M3 codes 0x7F and 0xFF) give the NaN code 0x7F in every
+    output they reach, as the oracle's encoding does (the saturating clamp
+    alone would turn them into -448), in the stand-alone apply and pre-mix;
+    every other code is the oracle's."""
+    _say("fp8 NaN codes")
+    B, n, C = 64, 4, 256
+    N = n * n + 2 * n
+    inp = synth.make_inputs_fp8(n, C, B, "normal", seed=21, device="cuda")
+    X, F = inp["X"].clone(), inp["F_out"].clone()
+    X[3, 5] = 0x7F
+    X[10, C + 17] = 0xFF
+    X[20, 3 * C + 100] = 0x7F
+    F[30, 7] = 0xFF
+    g = torch.Generator(device="cpu").manual_seed(5)
+    H = torch.rand(B, N, generator=g).to("cuda")
+    H[:, n:2 * n] *= 2.0
+    o = _alloc(B, n, C)
+    mhc.mhc_post_res_fp8(B, n, C, X, F, H, o["X_next"])
+    mhc.mhc_pre_fp8(B, n, C, X, H, o["F_pre"])
+    torch.cuda.synchronize()
+    x = F8.e4m3_decode(synth.e4m3_codes(X))
+    f = F8.e4m3_decode(synth.e4m3_codes(F))
+    pre, post, res = oracle.split_h(H.double().cpu().numpy(), n)
+    want_x = F8.e4m3_encode(oracle.post_res(x, f, post, res, n, C))
+    want_f = F8.e4m3_encode(oracle.pre_mix(x, pre, n, C))
+    got_x, got_f = synth.e4m3_codes(o["X_next"]), synth.e4m3_codes(o["F_pre"])
+    assert (want_x == 0x7F).sum() == 4 * 4 and (want_f == 0x7F).sum() == 3
+    nan_x, nan_f = want_x == 0x7F, want_f == 0x7F
+    assert np.array_equal(got_x[nan_x], want_x[nan_x]) and (got_x[~nan_x] != 0x7F).all()
+    assert np.array_equal(got_f[nan_f], want_f[nan_f]) and (got_f[~nan_f] != 0x7F).all()
+    exact_x = oracle.post_res(x, f, post, res, n, C)
+    exact_f = oracle.pre_mix(x, pre, n, C)
+    assert F8.e4m3_neighbors_ok(got_x[~nan_x], exact_x[~nan_x]).all()
+    assert F8.e4m3_neighbors_ok(got_f[~nan_f], exact_f[~nan_f]).all()

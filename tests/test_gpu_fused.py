@@ -41,16 +41,16 @@ def _gpu():
 # from round to round), and "fused_fixed" the same kernel in its fixed-slice
 # layout (n <= 4: one step per unit, each workgroup keeping one slice).
 @pytest.fixture(params=["default", "fused", "fused_fixed"])
-def route(request, monkeypatch):
-    monkeypatch.delenv("MHC_FUSED_FIXED", raising=False)
+def route(request, tune):
+    tune.delenv("MHC_FUSED_FIXED", raising=False)
     if request.param in ("fused", "fused_fixed"):
-        monkeypatch.setenv("MHC_SMALL_MAX_B", "0")
-        monkeypatch.setenv("MHC_FUSED_N8", "1")
+        tune.setenv("MHC_SMALL_MAX_B", "0")
+        tune.setenv("MHC_FUSED_N8", "1")
         if request.param == "fused_fixed":
-            monkeypatch.setenv("MHC_FUSED_FIXED", "1")
+            tune.setenv("MHC_FUSED_FIXED", "1")
     else:
-        monkeypatch.delenv("MHC_SMALL_MAX_B", raising=False)
-        monkeypatch.delenv("MHC_FUSED_N8", raising=False)
+        tune.delenv("MHC_SMALL_MAX_B", raising=False)
+        tune.delenv("MHC_FUSED_N8", raising=False)
     return request.param
 
 

@@ -45,12 +45,12 @@ def _gpu():
 
 
 @pytest.fixture(params=["default", "onepass"])
-def route(request, monkeypatch):
-    monkeypatch.delenv("MHC_FUSED_PRE", raising=False)
+def route(request, tune):
+    tune.delenv("MHC_FUSED_PRE", raising=False)
     if request.param == "onepass":
-        monkeypatch.setenv("MHC_SMALL_MAX_B", "0")
+        tune.setenv("MHC_SMALL_MAX_B", "0")
     else:
-        monkeypatch.delenv("MHC_SMALL_MAX_B", raising=False)
+        tune.delenv("MHC_SMALL_MAX_B", raising=False)
     return request.param
 
 
@@ -155,15 +155,15 @@ def test_named(name, route):
     _check(cur, nxt, o, ref, f, pre_own, _rows(cfg["B"]), name)
 
 
-def test_route_query(monkeypatch):
-    monkeypatch.delenv("MHC_SMALL_MAX_B", raising=False)
-    monkeypatch.delenv("MHC_FUSED_PRE", raising=False)
+def test_route_query(tune):
+    tune.delenv("MHC_SMALL_MAX_B", raising=False)
+    tune.delenv("MHC_FUSED_PRE", raising=False)
     assert mhc.mhc_post_res_coeffs_pre_one_pass(16384, 4, 7168)
     assert mhc.mhc_post_res_coeffs_pre_one_pass(4096, 4, 4096)
     assert not mhc.mhc_post_res_coeffs_pre_one_pass(64, 4, 7168)      # small B
     assert not mhc.mhc_post_res_coeffs_pre_one_pass(8192, 8, 4096)    # n = 8
     assert not mhc.mhc_post_res_coeffs_pre_one_pass(4096, 4, 8704)    # 17 steps per row
-    monkeypatch.setenv("MHC_FUSED_PRE", "0")
+    tune.setenv("MHC_FUSED_PRE", "0")
     assert not mhc.mhc_post_res_coeffs_pre_one_pass(16384, 4, 7168)
 
 
@@ -208,7 +208,7 @@ def test_workspace_contents(B, n, C, fill, route):
 
 
 @pytest.mark.parametrize("B", [16384, 65536], ids=["large", "B65536"])
-def test_two_routes_agree(monkeypatch, B):
+def test_two_routes_agree(tune, B):
     """The one-pass kernel and the two calls it replaces: X_next bitwise,
     coefficients up to summation order, F_pre within one bf16 step.  At
     B = 65536 every workgroup runs 228 steps of the record hand-off (57 at the
@@ -218,9 +218,9 @@ def test_two_routes_agree(monkeypatch, B):
     cur, nxt = _layers(cfg["n"], cfg["C"], cfg["B"], cfg["x_dist"], cfg["seed"])
     o = mhc.alloc_outputs(cfg["B"], cfg["n"], cfg["C"])
     _coeffs(cur, cur["X"], o)
-    monkeypatch.delenv("MHC_FUSED_PRE", raising=False)
+    tune.delenv("MHC_FUSED_PRE", raising=False)
     a = _call(cur, nxt, o["H"])
-    monkeypatch.setenv("MHC_FUSED_PRE", "0")
+    tune.setenv("MHC_FUSED_PRE", "0")
     b = _call(cur, nxt, o["H"])
     assert torch.equal(a["X_next"].view(torch.int16), b["X_next"].view(torch.int16))
     assert (a["H"] - b["H"]).abs().max().item() < 1e-4

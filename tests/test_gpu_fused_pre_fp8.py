@@ -50,13 +50,13 @@ def _gpu():
 
 
 @pytest.fixture(params=["default", "onepass", "twocalls"])
-def route(request, monkeypatch):
+def route(request, tune):
     for k in ("MHC_FUSED_PRE", "MHC_SMALL_MAX_B", "MHC_FUSED_FP8", "MHC_FUSED_FIXED"):
-        monkeypatch.delenv(k, raising=False)
+        tune.delenv(k, raising=False)
     if request.param == "onepass":
-        monkeypatch.setenv("MHC_SMALL_MAX_B", "0")
+        tune.setenv("MHC_SMALL_MAX_B", "0")
     elif request.param == "twocalls":
-        monkeypatch.setenv("MHC_FUSED_FP8", "0")
+        tune.setenv("MHC_FUSED_FP8", "0")
     return request.param
 
 
@@ -169,9 +169,9 @@ def test_named(name, route):
     _check(cur, nxt, o, ref, f, pre_own, _rows(cfg["B"]), name)
 
 
-def test_route_query(monkeypatch):
+def test_route_query(tune):
     for k in ("MHC_SMALL_MAX_B", "MHC_FUSED_PRE", "MHC_FUSED_FP8", "MHC_FUSED_FIXED"):
-        monkeypatch.delenv(k, raising=False)
+        tune.delenv(k, raising=False)
     q = mhc.mhc_post_res_coeffs_pre_fp8_one_pass
     assert q(16384, 4, 7168)
     assert q(4096, 4, 4096)
@@ -179,10 +179,10 @@ def test_route_query(monkeypatch):
     assert not q(8192, 8, 4096)     # n = 8
     assert not q(4096, 4, 8704)     # 17 steps per row
     assert not q(4096, 4, 7160)     # C % 32 != 0
-    monkeypatch.setenv("MHC_FUSED_FP8", "0")
+    tune.setenv("MHC_FUSED_FP8", "0")
     assert not q(16384, 4, 7168)
-    monkeypatch.setenv("MHC_FUSED_FP8", "1")
-    monkeypatch.setenv("MHC_FUSED_PRE", "0")
+    tune.setenv("MHC_FUSED_FP8", "1")
+    tune.setenv("MHC_FUSED_PRE", "0")
     assert not q(16384, 4, 7168)
 
 
@@ -216,7 +216,7 @@ def test_workspace_contents(B, n, C):
 
 
 @pytest.mark.parametrize("B", [16384, 65536], ids=["large", "B65536"])
-def test_two_routes_agree(monkeypatch, B):
+def test_two_routes_agree(tune, B):
     """The one-pass kernel and the two calls it replaces at n=4, C=7168 (the
     large workload, and B = 65536 for a long run of the record hand-off):
     X_next bitwise, coefficients up to summation order, F_pre codes at most
@@ -227,9 +227,9 @@ def test_two_routes_agree(monkeypatch, B):
     o = {}
     _coeffs(cur, cur["X"], o)
     for k in ("MHC_FUSED_PRE", "MHC_FUSED_FP8"):
-        monkeypatch.delenv(k, raising=False)
+        tune.delenv(k, raising=False)
     a = _call(cur, nxt, o["H"])
-    monkeypatch.setenv("MHC_FUSED_PRE", "0")
+    tune.setenv("MHC_FUSED_PRE", "0")
     b = _call(cur, nxt, o["H"])
     assert torch.equal(a["X_next"], b["X_next"])
     assert (a["H"] - b["H"]).abs().max().item() < 1e-4

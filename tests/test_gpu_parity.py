@@ -53,16 +53,16 @@ GEMM_ALGOS = ["lds", "reg", "small", "persist"]
 
 
 @pytest.fixture(params=GEMM_ALGOS)
-def gemm_algo(request, monkeypatch):
-    monkeypatch.delenv("MHC_GEMM_ALGO", raising=False)
+def gemm_algo(request, tune):
+    tune.delenv("MHC_GEMM_ALGO", raising=False)
     if request.param == "small":
-        monkeypatch.setenv("MHC_SMALL_MAX_B", str(1 << 30))
+        tune.setenv("MHC_SMALL_MAX_B", str(1 << 30))
     else:
-        monkeypatch.setenv("MHC_SMALL_MAX_B", "0")
+        tune.setenv("MHC_SMALL_MAX_B", "0")
         if request.param == "reg":
-            monkeypatch.setenv("MHC_GEMM_ALGO", "0")
+            tune.setenv("MHC_GEMM_ALGO", "0")
         elif request.param == "persist":
-            monkeypatch.setenv("MHC_GEMM_ALGO", "2")
+            tune.setenv("MHC_GEMM_ALGO", "2")
     return request.param
 
 
@@ -273,15 +273,15 @@ def test_bitwise_deterministic():
         assert torch.equal(a[k].view(torch.int8), b[k].view(torch.int8)), k
 
 
-def test_small_path_deterministic_and_matches_split(monkeypatch):
+def test_small_path_deterministic_and_matches_split(tune):
     _say("small path vs split path, decode")
     inp = synth.make_config("decode", device="cuda")
-    monkeypatch.setenv("MHC_SMALL_MAX_B", str(1 << 30))
+    tune.setenv("MHC_SMALL_MAX_B", str(1 << 30))
     a = run_forward(inp)
     b = run_forward(inp)
     for k in ("logits", "r", "H"):
         assert torch.equal(a[k].view(torch.int8), b[k].view(torch.int8)), k
-    monkeypatch.setenv("MHC_SMALL_MAX_B", "0")
+    tune.setenv("MHC_SMALL_MAX_B", "0")
     c = run_forward(inp)
     rel = (a["logits"] - c["logits"]).abs().max() / c["logits"].abs().max()
     assert rel.item() < 1e-5
@@ -290,11 +290,11 @@ def test_small_path_deterministic_and_matches_split(monkeypatch):
 
 
 @pytest.mark.parametrize("fill", ["zeros", "ones", "random", "near_done"])
-def test_small_path_any_workspace_contents(monkeypatch, fill):
+def test_small_path_any_workspace_contents(tune, fill):
     """The small-B kernel keeps per-tile counters in the workspace; whatever
     the workspace held before the call, the result is the same bits."""
     _say(f"small path, workspace filled with {fill}")
-    monkeypatch.setenv("MHC_SMALL_MAX_B", str(1 << 30))
+    tune.setenv("MHC_SMALL_MAX_B", str(1 << 30))
     inp = synth.make_inputs(4, 1024, 77, "normal", seed=4242, device="cuda")
     ref = run_forward(inp)
     B, n, C = inp["B"], inp["n"], inp["C"]
@@ -322,12 +322,12 @@ def test_small_path_any_workspace_contents(monkeypatch, fill):
             assert torch.equal(o[k].view(torch.int8), ref[k].view(torch.int8)), (fill, k)
 
 
-def test_split_k_invariance(monkeypatch, gemm_algo):
+def test_split_k_invariance(tune, gemm_algo):
     _say(f"split-K invariance decode gemm={gemm_algo}")
     inp = synth.make_config("decode", device="cuda")
     ref = None
     for s in ("1", "3", "17", "112"):
-        monkeypatch.setenv("MHC_SPLIT_K", s)
+        tune.setenv("MHC_SPLIT_K", s)
         o = run_forward(inp)
         if ref is None:
             ref = {k: v.clone() for k, v in o.items()}

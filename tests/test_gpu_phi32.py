@@ -47,10 +47,10 @@ def _gpu():
 
 
 @pytest.fixture(params=["small", "split"])
-def path(request, monkeypatch):
+def path(request, tune):
     for k in ("MHC_SMALL_MAX_B", "MHC_GEMM_ALGO"):
-        monkeypatch.delenv(k, raising=False)
-    monkeypatch.setenv("MHC_SMALL_MAX_B", str(1 << 30) if request.param == "small" else "0")
+        tune.delenv(k, raising=False)
+    tune.setenv("MHC_SMALL_MAX_B", str(1 << 30) if request.param == "small" else "0")
     return request.param
 
 
