@@ -116,13 +116,14 @@ def load():
 def _ptr(t, nbytes=None, esize=None, name="tensor"):
     """Device pointer of a tensor (None -> NULL; an int is taken as a raw
     address).  Raises ValueError on host or non-contiguous tensors and, when
-    the call's sizes are given, on a tensor of another element size or
-    smaller than the nbytes the library will touch, before anything runs."""
+    the call's sizes are given, on a tensor of another element size (uint8
+    tensors are taken as raw bytes) or smaller than the nbytes the library
+    will touch, before anything runs."""
     if t is None:
         return None
     if not isinstance(t, torch.Tensor):
         return int(t)  # raw address
-    if esize is not None and t.numel() > 0 and t.element_size() != esize:
+    if esize is not None and t.numel() > 0 and t.element_size() != esize and t.dtype != torch.uint8:
         raise ValueError(f"{name}: element size {t.element_size()} bytes, the call takes {esize}")
     if nbytes is not None and t.numel() * t.element_size() < nbytes:
         raise ValueError(f"{name}: {t.numel() * t.element_size()} bytes, the call needs {nbytes}")
@@ -148,6 +149,8 @@ class _Sizes:
         self.r = max(B, 0) * 4
         self.nb = n * 4                       # b_pre, b_post
         self.nr = n * n * 4                   # b_res
+        if B <= 0:  # B == 0 touches nothing (and B < 0 is the library's error to report)
+            self.x = self.f = self.phi = self.coef = self.r = self.nb = self.nr = 0
 
 
 def _coeff_args(z, phi, b_pre, b_post, b_res, logits, r, H):
