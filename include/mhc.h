@@ -230,6 +230,8 @@ int32_t mhc_post_res_coeffs_pre_one_pass(int64_t B, int32_t n, int64_t C);
  * `workspace` completed every wait of its one-pass route.  Synchronises
  * `stream` (the stream of that call) and reads one word of the workspace;
  * the workspace must still be the one the call used, not yet reused.
+ * workspace == NULL reads the word of mhc_post_res_coeffs_pre_noalloc's
+ * array on the current device instead (fp8 must then be 0).
  * Returns MHC_OK when no wait gave up (always for shapes that run the two
  * calls), MHC_ERR_INCOMPLETE when one did (F_pre_next then holds NaN -- the
  * E4M3 code 0x7F in the fp8 call -- in the vectors of the rows it gave up
@@ -237,6 +239,33 @@ int32_t mhc_post_res_coeffs_pre_one_pass(int64_t B, int32_t n, int64_t C);
  * usual argument errors and MHC_ERR_HIP otherwise. */
 int mhc_post_res_coeffs_pre_check(int64_t B, int32_t n, int64_t C, int32_t fp8,
                                   const void *workspace, size_t workspace_bytes, void *stream);
+
+/* mhc_post_res_coeffs_pre for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same call, results and routes, without the workspace
+ * argument.  Its workspace is a device array inside the library, of
+ * MHC_NOALLOC_SCRATCH_BYTES (32 MiB: the large workload n = 4, C = 7168,
+ * B = 16384 needs about 30.3 MB), one per GPU the library runs on, held until
+ * the process ends.  Shapes whose workspace (as
+ * mhc_post_res_coeffs_pre_workspace_size reports it) exceeds that return
+ * MHC_ERR_WORKSPACE before anything is launched.  The call allocates nothing:
+ * the first call on a device looks up the array's device address once.
+ * Every call on a GPU shares that GPU's array, so calls that overlap in time
+ * on one GPU (on different streams, or from different threads) race and must
+ * be ordered by the caller; calls on one stream are ordered by the stream.
+ * The array keeps whatever the last call left; each call clears what must
+ * start at zero with its own kernels.  The give-up word of the one-pass route
+ * is in the array too: mhc_post_res_coeffs_pre_check with workspace NULL
+ * reads it. */
+#define MHC_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+int mhc_post_res_coeffs_pre_noalloc(int64_t B, int32_t n, int64_t C,
+                                    const void *X_t, const void *F_out, const float *H,
+                                    void *X_next, const void *phi_next,
+                                    float alpha_pre, float alpha_post, float alpha_res,
+                                    const float *b_pre, const float *b_post, const float *b_res,
+                                    float *logits_next, float *r_next, float *H_next,
+                                    void *F_pre_next, void *stream);
 
 /* ------------------------------------------------------------------------
  * FP8 residual-stream variant.

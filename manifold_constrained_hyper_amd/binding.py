@@ -31,7 +31,9 @@ EXPORTED = ("mhc_status_string", "mhc_coeffs_workspace_size", "mhc_coeffs_split_
             "mhc_post_res_coeffs_pre", "mhc_post_res_coeffs_pre_one_pass",
             "mhc_post_res_coeffs_pre_fp8_workspace_size", "mhc_post_res_coeffs_pre_fp8",
             "mhc_post_res_coeffs_pre_fp8_one_pass", "mhc_post_res_coeffs_pre_check",
-            "mhc_tuning_set", "mhc_tuning_reset")
+            "mhc_tuning_set", "mhc_tuning_reset", "mhc_post_res_coeffs_pre_noalloc")
+
+MHC_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _lib = None
 
@@ -107,6 +109,9 @@ def load():
     lib.mhc_post_res_coeffs_pre_check.restype = ctypes.c_int
     lib.mhc_tuning_set.argtypes = [ctypes.c_char_p, i64]
     lib.mhc_tuning_set.restype = ctypes.c_int
+    lib.mhc_post_res_coeffs_pre_noalloc.argtypes = [i64, i32, i64, vp, vp, vp, vp, vp, f32, f32, f32,
+                                                    vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.mhc_post_res_coeffs_pre_noalloc.restype = ctypes.c_int
     lib.mhc_tuning_reset.argtypes = []
     lib.mhc_tuning_reset.restype = None
     _lib = lib
@@ -297,6 +302,23 @@ def mhc_post_res_coeffs_pre(B, n, C, X_t, F_out, H, X_next, phi_next, alpha_pre,
                   F_out, H, X_next, phi_next, alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res,
                   logits_next, r_next, H_next, F_pre_next, workspace, workspace_bytes, stream, check,
                   True)
+
+
+def mhc_post_res_coeffs_pre_noalloc(B, n, C, X_t, F_out, H, X_next, phi_next, alpha_pre,
+                                    alpha_post, alpha_res, b_pre, b_post, b_res, logits_next,
+                                    r_next, H_next, F_pre_next, stream=None, check=True):
+    """mhc_post_res_coeffs_pre with its workspace in the library's own device
+    array (no allocation; see include/mhc.h)."""
+    z = _Sizes(B, n, C, 2, 2)
+    pp, bp, bq, br, lg, rr, hh = _coeff_args(z, phi_next, b_pre, b_post, b_res, logits_next, r_next, H_next)
+    st = load().mhc_post_res_coeffs_pre_noalloc(
+        int(B), int(n), int(C), _ptr(X_t, z.x, 2, "X_t"), _ptr(F_out, z.f, 2, "F_out"),
+        _ptr(H, z.coef, 4, "H"), _ptr(X_next, z.x, 2, "X_next"), pp, float(alpha_pre),
+        float(alpha_post), float(alpha_res), bp, bq, br, lg, rr, hh,
+        _ptr(F_pre_next, z.f, 2, "F_pre_next"), _stream(stream))
+    if check:
+        _check(st, "mhc_post_res_coeffs_pre_noalloc")
+    return st
 
 
 def mhc_post_res_coeffs_pre_check(B, n, C, workspace, fp8=False, workspace_bytes=None, stream=None):

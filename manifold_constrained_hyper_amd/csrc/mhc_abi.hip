@@ -359,6 +359,32 @@ void tune_init() {
   }
 }
 
+// Workspace of mhc_post_res_coeffs_pre_noalloc: a device array of fixed size,
+// one copy per GPU, held until the process ends.  Host code never uses the
+// array's name as an address (in host code it names a host-side stand-in);
+// the device address comes from hipGetSymbolAddress, once per device, with
+// that device current.
+constexpr size_t kNoAllocScratchBytes = MHC_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices] = {};
+
+int noalloc_scratch(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MHC_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MHC_ERR_UNSUPPORTED;
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // Any thread that gets here resolves the same address; the first store wins.
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MHC_ERR_HIP;
+    void *expected = nullptr;
+    g_scratch_ptr[dev].compare_exchange_strong(expected, p, std::memory_order_acq_rel);
+    p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  }
+  *out = p;
+  return MHC_OK;
+}
+
 }  // namespace
 
 namespace mhc {
@@ -466,7 +492,15 @@ int mhc_post_res_coeffs_pre_check(int64_t B, int32_t n, int64_t C, int32_t fp8,
   if (st != MHC_OK) return st;
   if (C % 32 != 0) return MHC_ERR_UNSUPPORTED;
   if (B == 0 || !pre_fused(B, n, C, e)) return MHC_OK;  // the two calls never give up
-  if (!workspace) return MHC_ERR_INVALID_ARG;
+  if (!workspace) {  // the array of mhc_post_res_coeffs_pre_noalloc
+    if (fp8) return MHC_ERR_INVALID_ARG;
+    if (post_res_coeffs_pre_ws_bytes(B, n, C, e) > kNoAllocScratchBytes) return MHC_ERR_WORKSPACE;
+    void *ws = nullptr;
+    const int sst = noalloc_scratch(&ws);
+    if (sst != MHC_OK) return sst;
+    workspace = ws;
+    workspace_bytes = kNoAllocScratchBytes;
+  }
   if (workspace_bytes < post_res_coeffs_pre_ws_bytes(B, n, C, e)) return MHC_ERR_WORKSPACE;
   const mhc::FusedPlan plan = mhc::plan_post_res_next(B, n, C, true, e.fp8);
   uint32_t word = 0;
@@ -476,6 +510,25 @@ int mhc_post_res_coeffs_pre_check(int64_t B, int32_t n, int64_t C, int32_t fp8,
       hipStreamSynchronize(s) != hipSuccess)
     return MHC_ERR_HIP;
   return word == 0 ? MHC_OK : MHC_ERR_INCOMPLETE;
+}
+
+int mhc_post_res_coeffs_pre_noalloc(int64_t B, int32_t n, int64_t C, const void *X_t,
+                                    const void *F_out, const float *H, void *X_next,
+                                    const void *phi_next, float alpha_pre, float alpha_post,
+                                    float alpha_res, const float *b_pre, const float *b_post,
+                                    const float *b_res, float *logits_next, float *r_next,
+                                    float *H_next, void *F_pre_next, void *stream) {
+  int st = check_shape_elt(B, n, C, kBf16);
+  if (st != MHC_OK) return st;
+  if (C % 32 != 0) return MHC_ERR_UNSUPPORTED;
+  if (B == 0) return MHC_OK;
+  if (post_res_coeffs_pre_ws_bytes(B, n, C, kBf16) > kNoAllocScratchBytes) return MHC_ERR_WORKSPACE;
+  void *ws = nullptr;
+  st = noalloc_scratch(&ws);
+  if (st != MHC_OK) return st;
+  return post_res_coeffs_impl(kBf16, B, n, C, X_t, F_out, H, X_next, phi_next, alpha_pre,
+                              alpha_post, alpha_res, b_pre, b_post, b_res, logits_next, r_next,
+                              H_next, ws, kNoAllocScratchBytes, stream, true, F_pre_next);
 }
 
 int32_t mhc_post_res_coeffs_pre_one_pass(int64_t B, int32_t n, int64_t C) {

@@ -401,8 +401,10 @@ def test_binding_checks_tensor_sizes():
     X, H, F, Y, W = _addrs(5)
     with pytest.raises(ValueError, match="F_pre: 1792 bytes, the call needs 2048"):
         mhc.mhc_pre(B, n, C, X, H, torch.empty(B, C - 8, dtype=torch.bfloat16))
-    with pytest.raises(ValueError, match="X_t: element size 1"):
-        mhc.mhc_pre(B, n, C, torch.empty(B, 2 * n * C, dtype=torch.uint8), H, F)
+    with pytest.raises(ValueError, match="X_t: element size 4"):  # fp32 values to a bf16 call
+        mhc.mhc_pre(B, n, C, torch.empty(B, n * C, dtype=torch.float32), H, F)
+    with pytest.raises(ValueError, match="X_t: 4096 bytes, the call needs 8192"):  # raw bytes: size only
+        mhc.mhc_pre(B, n, C, torch.empty(B, n * C, dtype=torch.uint8), H, F)
     with pytest.raises(ValueError, match="X_t: element size 2"):  # a bf16 tensor to an E4M3 call
         mhc.mhc_pre_fp8(B, n, C, torch.empty(B, n * C, dtype=torch.bfloat16), H, F)
     with pytest.raises(ValueError, match="H: "):
@@ -428,7 +430,8 @@ def test_one_pass_grid_and_check():
     # argument errors
     assert mhc.mhc_post_res_coeffs_pre_check(16384, 3, 7168, A, stream=0) == mhc.MHC_ERR_UNSUPPORTED
     assert mhc.mhc_post_res_coeffs_pre_check(16384, 4, 7168, None, fp8=True, stream=0) == mhc.MHC_ERR_INVALID_ARG
-    assert mhc.mhc_post_res_coeffs_pre_check(16384, 4, 7168, None, stream=0) == mhc.MHC_ERR_INVALID_ARG
+    # NULL workspace: the no-alloc call's array, which holds at most MHC_NOALLOC_SCRATCH_BYTES
+    assert mhc.mhc_post_res_coeffs_pre_check(65536, 4, 7168, None, stream=0) == mhc.MHC_ERR_WORKSPACE
     need = mhc.mhc_post_res_coeffs_pre_workspace_size(16384, 4, 7168)
     assert mhc.mhc_post_res_coeffs_pre_check(16384, 4, 7168, A, workspace_bytes=need - 1,
                                              stream=0) == mhc.MHC_ERR_WORKSPACE
