@@ -19,6 +19,7 @@ Sources (cited by page title and section throughout):
 from .mhc_oracle import (  # noqa: F401
     SINKHORN_ITERS,
     bf16_bits_to_f64,
+    round_to_bf16,
     coefficient_logits,
     row_sum_squares,
     rms_scale,

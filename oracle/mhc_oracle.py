@@ -8,7 +8,8 @@ it ([mHC-cutile] = the page "mHC 算法分析 & cutile 高效实现"; [FreeNorm]
 PyTorch blog "Towards Free Normalization: Fusing Normalization into GEMM and
 Attention Kernels").  Arithmetic is numpy float64; bf16 inputs are widened
 exactly (bf16 -> fp32 is a 16-bit shift, fp32 -> fp64 is exact).  Outputs are
-never rounded back to a narrower type.
+never rounded back to a narrower type, except by round_to_bf16, which a test
+calls where one layer's X_next becomes the next layer's bf16 input.
 
 Notation (from [mHC-cutile] section 2):
   B  rows (batch x sequence),  n  expansion rate,  C  hidden size,
@@ -43,6 +44,22 @@ def bf16_bits_to_f64(bits):
     u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     with np.errstate(invalid="ignore"):
         return u.view(np.float32).astype(np.float64)
+
+
+def round_to_bf16(x):
+    """float64 -> the nearest bf16 value (ties to even), as float64.
+
+    [mHC-cutile] section 2.5 hands X_next to the next layer as that layer's
+    X_t, which is a bf16 tensor in every workload here; rounding to nearest,
+    ties to even, is the reading taken for that conversion.  bf16 keeps 8
+    significant bits (7 stored) and fp32's exponent range; values here are
+    far from its overflow and subnormal ranges, which this does not model.
+    Rounding straight from float64 (not through fp32) avoids double
+    rounding."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                  # x = m * 2^e, 0.5 <= |m| < 1
+    q = np.rint(m * 256.0) / 256.0      # 8 significant bits, ties to even
+    return np.ldexp(q, e)
 
 
 def coefficient_logits(x, phi):

@@ -292,10 +292,39 @@ def pin_chunking(m):
         _close(a[k], b[k], rtol=1e-13, atol=1e-14)
 
 
+def pin_bf16_rounding(m):
+    """round_to_bf16 against torch's fp32 -> bf16 conversion (nearest, ties to
+    even) on values exact in fp32, where rounding from fp32 or from fp64 must
+    agree; hand-made ties and near-ties; idempotence on bf16 values."""
+    import torch
+    rng = np.random.default_rng(31)
+    v = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-6, 6, 20000),
+                        rng.standard_t(4, 20000)]).astype(np.float32)
+    # every tie: the 16 dropped bits exactly 0x8000, both parities of the kept lsb
+    ties = ((rng.integers(0, 2**16, 4000, dtype=np.uint32) << 16) | 0x8000).astype(np.uint32)
+    ties = ties[((ties >> 23) & 0xFF) - 127 < 60]      # keep exponents in a sane range
+    ties = ties[((ties >> 23) & 0xFF) > 60]
+    v = np.concatenate([v, ties.view(np.float32)])
+    want = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    got = m.round_to_bf16(v.astype(np.float64))
+    assert np.array_equal(got, want)
+    # ties by hand: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7 (lsb of 1 is even)
+    assert m.round_to_bf16(1.0 + 2.0 ** -8) == 1.0
+    assert m.round_to_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6        # to the even neighbour above
+    assert m.round_to_bf16(-(1.0 + 3 * 2.0 ** -8)) == -(1.0 + 2.0 ** -6)
+    assert m.round_to_bf16(1.0 + 2.0 ** -8 + 2.0 ** -40) == 1.0 + 2.0 ** -7  # just past the tie: up
+    assert m.round_to_bf16(255.5) == 256.0 and m.round_to_bf16(254.5) == 254.0
+    # just below a tie whose even neighbour is above: fp32 would first round it
+    # onto the tie, which then goes up (double rounding); straight from fp64 it goes down
+    assert m.round_to_bf16(1.0 + 3 * 2.0 ** -8 - 2.0 ** -40) == 1.0 + 2.0 ** -7
+    b = m.round_to_bf16(rng.standard_normal(1000))
+    assert np.array_equal(m.round_to_bf16(b), b)
+
+
 PINS = [pin_brute_force, pin_one_hot_phi, pin_rms_closed_forms, pin_lazy_prenorm,
         pin_gates, pin_column_roles, pin_sinkhorn_scaling_form, pin_sinkhorn_column_last,
         pin_sinkhorn_closed_forms, pin_sinkhorn_invariants, pin_pre_one_hot,
-        pin_post_res_structure, pin_bf16_widening, pin_chunking]
+        pin_post_res_structure, pin_bf16_widening, pin_chunking, pin_bf16_rounding]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -387,7 +416,28 @@ ORACLE_GATES = ORACLE.gate_coefficients
 ORACLE_SCALE_BIAS = ORACLE.scale_bias
 ORACLE_PRE = ORACLE.pre_mix
 
+def _mut_round_truncate(x):
+    x = np.asarray(x, dtype=np.float64)
+    mm, e = np.frexp(x)
+    return np.ldexp(np.trunc(mm * 256.0) / 256.0, e)
+
+
+def _mut_round_half_up(x):
+    x = np.asarray(x, dtype=np.float64)
+    mm, e = np.frexp(x)
+    return np.ldexp(np.floor(mm * 256.0 + 0.5) / 256.0, e)
+
+
+def _mut_round_via_fp32(x):
+    return ORACLE_ROUND(np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64))
+
+
+ORACLE_ROUND = ORACLE.round_to_bf16
+
 MUTATIONS = [
+    ("round_to_bf16", _mut_round_truncate),
+    ("round_to_bf16", _mut_round_half_up),
+    ("round_to_bf16", _mut_round_via_fp32),
     ("sinkhorn_knopp", _mut_sinkhorn_cols_first),
     ("sinkhorn_knopp", _mut_sinkhorn_19),
     ("sinkhorn_knopp", _mut_exp_shift),
