@@ -443,7 +443,8 @@ int mhc_lazy_prenorm_gemm(int64_t M, int64_t N, int64_t K, const void *A, const 
  * fused calls' X_next and F_pre_next bitwise).  The workspace-size functions
  * answer for the routes selected at the time they are called, so set
  * overrides before sizing a workspace.  Not thread-safe against concurrent
- * calls.  mhc_tuning_set returns MHC_ERR_INVALID_ARG for an unknown key. */
+ * calls.  Values above 2^31 - 1 are taken as 2^31 - 1.  mhc_tuning_set
+ * returns MHC_ERR_INVALID_ARG for an unknown key. */
 int mhc_tuning_set(const char *name, int64_t value);
 void mhc_tuning_reset(void);
 

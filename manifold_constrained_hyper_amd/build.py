@@ -3,7 +3,9 @@
     python -m manifold_constrained_hyper_amd.build
 
 Compiles every HIP source under csrc/ into manifold_constrained_hyper_amd/
-libmhc.so.  Packed-fp32 instructions are disabled for all device code.
+libmhc.so, and the benchmark's bandwidth probes (probe/bw_probe.hip, not part
+of the library) into probe/libmhc_probe.so.  Packed-fp32 instructions are
+disabled for all device code.
 """
 
 import os
@@ -42,8 +44,26 @@ def _compile(src):
     return obj
 
 
+PROBE_SRC = os.path.join(PKG, "probe", "bw_probe.hip")
+PROBE_LIB = os.path.join(PKG, "probe", "libmhc_probe.so")
+
+
+def build_probe(verbose=True):
+    """The benchmark's bandwidth-probe library (not part of libmhc)."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, *COMPILE_FLAGS, "-shared", PROBE_SRC, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print(f"built {PROBE_LIB}")
+    return PROBE_LIB
+
+
 def build(verbose=True):
-    """Compile all sources and link libmhc.so (always rebuilds)."""
+    """Compile all sources and link libmhc.so (always rebuilds), then the
+    benchmark's probe library."""
     os.makedirs(OBJDIR, exist_ok=True)
     srcs = sources()
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
@@ -56,6 +76,7 @@ def build(verbose=True):
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    build_probe(verbose)
     return LIB
 
 

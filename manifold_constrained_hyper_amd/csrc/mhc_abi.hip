@@ -35,7 +35,8 @@ bool supported_n(int32_t n) { return n == 1 || n == 2 || n == 4 || n == 8; }
 int check_shape(int64_t B, int32_t n, int64_t C) {
   if (B < 0 || n < 1 || C < 1) return MHC_ERR_INVALID_ARG;
   if (!supported_n(n) || C % 8 != 0) return MHC_ERR_UNSUPPORTED;
-  if (B > kMaxB || (int64_t)n * C > kMaxK || (B > 0 && B > kMaxElems / ((int64_t)n * C)))
+  // C is compared before it is multiplied: n * C itself could overflow.
+  if (B > kMaxB || C > kMaxK / n || (B > 0 && B > kMaxElems / ((int64_t)n * C)))
     return MHC_ERR_UNSUPPORTED;
   return MHC_OK;
 }
@@ -413,7 +414,10 @@ int mhc_tuning_set(const char *name, int64_t value) {
   tune_init();
   for (const TuneName &t : kTuneNames)
     if (std::strcmp(t.name, name) == 0) {
-      g_tune[t.key].store(value < 0 ? -1 : value, std::memory_order_relaxed);
+      // Values are clamped to 2^31 - 1, far above any meaningful setting,
+      // so the launch-shape arithmetic they enter cannot overflow.
+      constexpr int64_t kMaxTune = (int64_t(1) << 31) - 1;
+      g_tune[t.key].store(value < 0 ? -1 : (value > kMaxTune ? kMaxTune : value), std::memory_order_relaxed);
       return MHC_OK;
     }
   return MHC_ERR_INVALID_ARG;

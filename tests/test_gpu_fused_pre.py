@@ -7,8 +7,10 @@ Checks, for every shape:
               H_next (the one-pass kernel forms H_pre from the same sums, in
               the same order, with the same gate);
   logits, r, H_next and F_pre_next against the fp64 oracle on the call's
-              X_next (tolerances of test_gpu_parity.py), on every row of the
-              small shapes and on sampled rows of the full-size workloads;
+              X_next (tolerances of test_gpu_parity.py), on every row;
+  at the large workload also an oracle-only chain: the oracle's X_next from
+              X_t and H, rounded to bf16 as the next layer's input, then the
+              oracle's coefficients and F_pre from that X_next;
   the coefficients against mhc_coeffs on X_next up to fp32 summation order.
 The next layer has its own phi and biases (a second seeded draw).
 
@@ -152,7 +154,12 @@ def test_named(name, route):
         pytest.skip("above 256 rows the default route already takes the one-pass kernel where it fits")
     cur, nxt = _layers(cfg["n"], cfg["C"], cfg["B"], cfg["x_dist"], cfg["seed"])
     o, ref, f, pre_own = _run(cur, nxt)
-    _check(cur, nxt, o, ref, f, pre_own, _rows(cfg["B"]), name)
+    # every row on the default route, in chunks (rows are independent);
+    # sampled rows on the others
+    chunks = ([list(range(lo, min(cfg["B"], lo + 1024))) for lo in range(0, cfg["B"], 1024)]
+              if route == "default" else [_rows(cfg["B"])])
+    for rows in chunks:
+        _check(cur, nxt, o, ref, f, pre_own, rows, f"{name} rows {rows[0]}..{rows[-1]}")
 
 
 def test_route_query(tune):
@@ -291,3 +298,42 @@ def test_guard_bands(route):
     torch.cuda.synchronize()
     for k, (buf, _) in bufs.items():
         assert (buf[:G] == 0x5A).all() and (buf[-G:] == 0x5A).all(), f"write outside {k}"
+
+
+def test_oracle_chain_large():
+    """The one-pass call at the large workload (n=4, C=7168, B=16384) against a
+    chain the oracle computes on its own: X_next = H_res X_t + H_post F_out
+    from the call's inputs ([mHC-cutile] section 2.5), rounded to bf16 as the
+    next layer's input; then the next layer's logits, r, H
+    (sections 2.1-2.4) and F_pre = sum_i H_pre[i] X_next[i] from that X_next.
+    Every row, at the parity tolerances."""
+    cfg = synth.CONFIGS["large"]
+    B, n, C = cfg["B"], cfg["n"], cfg["C"]
+    assert mhc.mhc_post_res_coeffs_pre_one_pass(B, n, C)
+    _say("post_res_coeffs_pre oracle chain, large")
+    cur, nxt = _layers(n, C, B, cfg["x_dist"], cfg["seed"])
+    o = mhc.alloc_outputs(B, n, C)
+    _coeffs(cur, cur["X"], o)           # this layer's H (an input of the call)
+    f = _call(cur, nxt, o["H"])
+    H = o["H"].double().cpu().numpy()
+    phi = _f64(nxt["phi"])
+    bp, bq, br = (nxt[k].double().cpu().numpy() for k in ("b_pre", "b_post", "b_res"))
+    for lo in range(0, B, 1024):
+        hi = min(B, lo + 1024)
+        lab = f"rows {lo}..{hi - 1}"
+        x = _f64(cur["X"][lo:hi])
+        _, hq, hr = oracle.split_h(H[lo:hi], n)
+        xn = oracle.post_res(x, _f64(cur["F_out"][lo:hi]), hq, hr, n, C)
+        gx = _f64(f["X_next"][lo:hi])
+        assert np.all(np.abs(gx - xn) <= 2e-2 + 1e-2 * np.abs(xn)), f"{lab}: X_next"
+        xb = oracle.round_to_bf16(xn)
+        co = oracle.coefficients(xb, phi, nxt["alpha_pre"], nxt["alpha_post"], nxt["alpha_res"],
+                                 bp, bq, br, n, C)
+        g = {k: f[k][lo:hi].double().cpu().numpy() for k in ("logits", "r", "H")}
+        row_err = np.abs(g["logits"] - co["logits"]).max(1)
+        assert np.all(row_err <= 2e-3 * np.abs(co["logits"]).max(1)), f"{lab}: logits"
+        assert np.all(np.abs(g["r"] - co["r"]) <= 2e-3 * co["r"]), f"{lab}: r"
+        assert np.abs(g["H"] - co["H"]).max() <= 1e-3, f"{lab}: H"
+        fo = oracle.pre_mix(xb, co["H"][:, :n], n, C)
+        gp = _f64(f["F_pre"][lo:hi])
+        assert np.all(np.abs(gp - fo) <= 2e-2 + 1e-2 * np.abs(fo)), f"{lab}: F_pre"

@@ -8,9 +8,10 @@ Tolerances (fixed for the method's outputs):
 Stricter checks on top: with the GPU's own H fed to the oracle's apply steps,
 the bf16 outputs must sit within one bf16 rounding of the fp64 value.
 
-Small shapes are compared on every output element; full-size workloads on
-sampled rows (rows are independent in every step, so the oracle computes
-exactly those rows) plus properties checked on all rows.
+Every output element is compared with the oracle, at the full-size workloads
+too (in chunks of rows: rows are independent in every step) on the default
+product, and on sampled rows for the alternative products, plus properties
+checked on all rows.
 """
 
 import os
@@ -159,15 +160,20 @@ def test_parity_full(name, gemm_algo):
 
 
 @pytest.mark.parametrize("name", ["prefill", "large", "wide"])
-def test_parity_sampled_and_properties(name, gemm_algo):
-    _say(f"parity sampled {name} gemm={gemm_algo}")
+def test_parity_every_row_and_properties(name, gemm_algo):
+    _say(f"parity every row {name} gemm={gemm_algo}")
     inp = synth.make_config(name, device="cuda")
     o = run_forward(inp)
     B, n, C = inp["B"], inp["n"], inp["C"]
-    rows = sample_rows(B, 48, seed=B)
-    g = gpu_rows(o, rows)
-    assert_parity(g, oracle_rows(inp, rows), name)
-    assert_apply_tight(inp, o, rows, g)
+    # every row against the oracle on the default product (in chunks of rows:
+    # rows are independent); the other products on sampled rows here, and on
+    # every row at the smaller shapes
+    chunks = ([list(range(lo, min(B, lo + 1024))) for lo in range(0, B, 1024)] if gemm_algo == "lds"
+              else [sample_rows(B, 48, seed=B)])
+    for rows in chunks:
+        g = gpu_rows(o, rows)
+        assert_parity(g, oracle_rows(inp, rows), f"{name} rows {rows[0]}..{rows[-1]}")
+        assert_apply_tight(inp, o, rows, g)
     # properties on every row
     H = o["H"].double()
     assert torch.isfinite(H).all() and torch.isfinite(o["logits"]).all()
