@@ -63,19 +63,29 @@ int check_shape_elt(int64_t B, int32_t n, int64_t C, Elt e) {
 }
 
 // Which kernels mhc_coeffs(_fp8) runs: the one-launch small-B kernel, the
-// split-K product (X staged through LDS, bf16 or E4M3) + combine, or (with
-// MHC_GEMM_ALGO=2) the persistent product kernel of mhc_post_res_fused.hip +
-// combine.  The
-// persistent kernel walks each stream in 32-channel k-steps, so it needs
-// C % 32 == 0; other hidden sizes take the small-B kernel at any B (it is
+// split-K product (X staged through LDS, bf16 or E4M3; or with
+// MHC_GEMM_ALGO=0 its register path) + combine, or the persistent product
+// kernel of mhc_post_res_fused.hip (product-only mode, fixed-slice layout) +
+// combine.  Above the small-B sizes, bf16 X at n <= 4 takes the persistent
+// kernel: measured on MI355X in the three-call sequence (after mhc_post_res,
+// before mhc_pre) at n=4, C=7168, B=16384 it takes 174.5 us per call against
+// 201-204 for the split-K product (its 16 waves per CU keep more loads in
+// flight than the split-K kernel's 4).  E4M3 X keeps the split-K product
+// (116-126 against 118-137 us) and n = 8 too (the persistent kernel cannot
+// hold 80-column phi operands in registers).  The persistent kernel walks
+// each stream in 32-channel k-steps, so it needs C % 32 == 0; with
+// MHC_GEMM_ALGO=2 other hidden sizes take the small-B kernel at any B (it is
 // correct for every shape, only slower at large B).
 enum class CoeffsPath { kSmall, kSplitK, kPersistent };
 
 CoeffsPath coeffs_path(int64_t B, int32_t n, int64_t C, Elt e) {
   if (mhc::use_coeffs_small(B, n, C)) return CoeffsPath::kSmall;
   if (e.phi32) return CoeffsPath::kSplitK;  // fp32 phi: small-B kernel or split-K through LDS
-  if (mhc::tune(mhc::kTuneGemmAlgo) != 2) return CoeffsPath::kSplitK;
-  return C % 32 == 0 ? CoeffsPath::kPersistent : CoeffsPath::kSmall;
+  const int64_t algo = mhc::tune(mhc::kTuneGemmAlgo);
+  if (algo == 2) return C % 32 == 0 ? CoeffsPath::kPersistent : CoeffsPath::kSmall;
+  if (algo == 0 || algo == 1) return CoeffsPath::kSplitK;
+  if (!e.fp8 && n <= 4 && C % 32 == 0 && mhc::fixed_layout_fits(n, C)) return CoeffsPath::kPersistent;
+  return CoeffsPath::kSplitK;
 }
 
 mhc::GemmPlan split_plan(int64_t B, int32_t n, int64_t C, Elt e) {
@@ -345,7 +355,8 @@ constexpr TuneName kTuneNames[] = {
     {"MHC_GEMM_MB", mhc::kTuneGemmMb},        {"MHC_FUSED_N8", mhc::kTuneFusedN8},
     {"MHC_FUSED_FP8", mhc::kTuneFusedFp8},    {"MHC_FUSED_FIXED", mhc::kTuneFusedFixed},
     {"MHC_FUSED_SPU", mhc::kTuneFusedSpu},    {"MHC_FUSED_WGS", mhc::kTuneFusedWgs},
-    {"MHC_FUSED_PRE", mhc::kTuneFusedPre},
+    {"MHC_FUSED_PRE", mhc::kTuneFusedPre},    {"MHC_LPN_ALGO", mhc::kTuneLpnAlgo},
+    {"MHC_GEMM_KC", mhc::kTuneGemmKc},        {"MHC_GEMM_STAGES", mhc::kTuneGemmStages},
 };
 static_assert(sizeof(kTuneNames) / sizeof(kTuneNames[0]) == mhc::kTuneCount, "one name per key");
 

@@ -67,7 +67,8 @@ struct LdsTile {
   static_assert(PIECES >= 16 && PIECES <= 64, "swizzle needs 16..64 pieces per row");
   static_assert(XI % 4 == 0 && PI % 4 == 0, "load instructions must split evenly over 4 waves");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-  static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
+  static_assert(STAGES >= 2 && STAGES <= 6, "pipeline depth");
+  static_assert((STAGES - 2) * (XI_W + PI_W) < 64, "vmcnt range");
 };
 
 // s_waitcnt with only the vector-memory counter constrained (expcnt and
@@ -112,17 +113,17 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
-// Wait until at most `later` chunks' loads of this wave are outstanding.
+// Wait until at most `later` chunks' loads of this wave are outstanding
+// (later <= STAGES - 2).
 template <int NS, int MB, int KC, int STAGES, int XB, int P2>
 __device__ __forceinline__ void wait_chunks(int later) {
   using L = LdsTile<NS, MB, KC, STAGES, XB, P2>;
-  if (STAGES >= 4 && later >= 2) {
-    wait_vmcnt<(STAGES >= 4 ? 2 : 0) * L::VM_PER_CHUNK>();
-  } else if (later >= 1) {
-    wait_vmcnt<L::VM_PER_CHUNK>();
-  } else {
-    wait_vmcnt<0>();
-  }
+  constexpr int V = L::VM_PER_CHUNK;
+  if (STAGES >= 6 && later >= 4) wait_vmcnt<(STAGES >= 6 ? 4 : 0) * V>();
+  else if (STAGES >= 5 && later >= 3) wait_vmcnt<(STAGES >= 5 ? 3 : 0) * V>();
+  else if (STAGES >= 4 && later >= 2) wait_vmcnt<(STAGES >= 4 ? 2 : 0) * V>();
+  else if (later >= 1) wait_vmcnt<V>();
+  else wait_vmcnt<0>();
 }
 
 template <int NS, int MB, int KC, int STAGES, int XB, int P2>
@@ -392,6 +393,13 @@ hipError_t launch_zero(void *p, size_t bytes, hipStream_t st) {
 
 // Instantiations used by the library (see plan_gemm in mhc_gemm_rms.hip).
 template hipError_t launch_gemm_lds_typed<1, 1, 256, 3, 2, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+// bf16 X in 128-k chunks, deeper rings (tuning: MHC_GEMM_KC = 128, MHC_GEMM_STAGES)
+template hipError_t launch_gemm_lds_typed<1, 1, 128, 5, 2, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<2, 1, 128, 5, 2, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<4, 1, 128, 5, 2, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<1, 1, 128, 6, 2, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<2, 1, 128, 6, 2, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<4, 1, 128, 6, 2, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
 template hipError_t launch_gemm_lds_typed<2, 1, 256, 3, 2, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
 template hipError_t launch_gemm_lds_typed<4, 1, 256, 3, 2, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
 template hipError_t launch_gemm_lds_typed<8, 1, 128, 4, 2, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);

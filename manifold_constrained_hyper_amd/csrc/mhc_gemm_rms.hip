@@ -256,8 +256,13 @@ hipError_t launch_n(const GemmPlan &p, int64_t B, int64_t C, const void *X, cons
     else return launch_gemm_lds_typed<NS, 1, 256, 4, 1, 1>(p, B, C, X, phi, ws, st);
   }
   if (p.algo == 1) {
-    if constexpr (NS == 8) return launch_gemm_lds_typed<NS, 1, 128, 4, 2, 1>(p, B, C, X, phi, ws, st);
-    else return launch_gemm_lds_typed<NS, 1, 256, 3, 2, 1>(p, B, C, X, phi, ws, st);
+    if constexpr (NS == 8) {
+      return launch_gemm_lds_typed<NS, 1, 128, 4, 2, 1>(p, B, C, X, phi, ws, st);
+    } else {
+      if (p.kc == 128 && p.stages == 5) return launch_gemm_lds_typed<NS, 1, 128, 5, 2, 1>(p, B, C, X, phi, ws, st);
+      if (p.kc == 128 && p.stages == 6) return launch_gemm_lds_typed<NS, 1, 128, 6, 2, 1>(p, B, C, X, phi, ws, st);
+      return launch_gemm_lds_typed<NS, 1, 256, 3, 2, 1>(p, B, C, X, phi, ws, st);
+    }
   }
   if (p.mb == 2) return launch_typed<NS, 2, kGemmKC, false, true>(p, B, C, X, phi, ws, st);
   return launch_typed<NS, 1, kGemmKC, false, true>(p, B, C, X, phi, ws, st);
@@ -325,9 +330,13 @@ GemmPlan plan_gemm(int64_t B, int n, int64_t C, bool fp8_x, bool phi32) {
     p.xb = 1;
     return p;
   }
-  const int kc = (n == 8) ? 128 : 256;
-  const int stages = (n == 8) ? 4 : 3;
-  if (tune(kTuneGemmAlgo) == 0)  // tuning override: the register path
+  int kc = (n == 8) ? 128 : 256;
+  int stages = (n == 8) ? 4 : 3;
+  if (n != 8 && tune(kTuneGemmKc) == 128 && (tune(kTuneGemmStages) == 5 || tune(kTuneGemmStages) == 6)) {
+    kc = 128;  // tuning: 128-k chunks in a 5- or 6-deep ring
+    stages = (int)tune(kTuneGemmStages);
+  }
+  if (tune(kTuneGemmAlgo) == 0)  // tuning override: the register path (1: the LDS path, the default here)
     return plan_gemm_custom(B, n, C, 0, (B >= 1024) ? 2 : 1, kGemmKC, 1, kGemmTargetWGs);
   const int64_t target = tune(kTuneGemmWgs) > 0 ? tune(kTuneGemmWgs) : 256;
   return plan_gemm_custom(B, n, C, 1, 1, kc, stages, target);

@@ -24,6 +24,9 @@ enum TuneKey : int {
   kTuneFusedSpu,       // 512-channel steps per unit of the fused kernel (> 0)
   kTuneFusedWgs,       // workgroups of the fused kernel (> 0; never above the resident count)
   kTuneFusedPre,       // 0: mhc_post_res_coeffs_pre(_fp8) as two calls
+  kTuneLpnAlgo,        // Lazy Pre-Norm GEMM: 0 eight-wave kernel, 1 four-wave kernel
+  kTuneGemmKc,         // 128: the bf16 split-K product in 128-k chunks (with kTuneGemmStages)
+  kTuneGemmStages,     // 5 or 6: its ring depth
   kTuneCount
 };
 // Current value of a key; -1 when unset.
@@ -98,6 +101,9 @@ struct FusedPlan {
 // layers): the E4M3 apply and both product-only modes run faster in it; the
 // bf16 apply after mhc_pre runs slower (393 vs 381 us).
 FusedPlan plan_post_res_next(int64_t B, int n, int64_t C, bool pre = false, bool prefer_fixed = false);
+// Whether the fixed-slice layout fits (n <= 4, one workgroup per slice at
+// least, packed phi addressable by 32-bit offsets).
+bool fixed_layout_fits(int n, int64_t C);
 // What the persistent kernel of mhc_post_res_fused.hip does per step.
 enum FusedMode : int {
   kFusedApplyBf16 = 0,     // bf16 X_t, F_out -> bf16 X_next, plus X_next . phi_next

@@ -379,10 +379,14 @@ def test_tuning_keys_and_no_environment(tune, monkeypatch):
         monkeypatch.setenv(k, v)
     assert (one(16384, 4, 7168), ws(16384, 4, 7168), mhc.mhc_coeffs_split_k(16384, 4, 7168),
             mhc.mhc_coeffs_workspace_size(64, 4, 7168)) == base
+    # the split-K product's slice count (the default product at n = 8)
+    s8 = mhc.mhc_coeffs_split_k(8192, 8, 4096)
     tune.setenv("MHC_SPLIT_K", 5)
-    assert mhc.mhc_coeffs_split_k(16384, 4, 7168) == 5
+    assert mhc.mhc_coeffs_split_k(8192, 8, 4096) == 5
+    assert mhc.mhc_coeffs_split_k(16384, 4, 7168) == base[2]   # the persistent product: one slice per 512 channels
     tune.delenv("MHC_SPLIT_K")
-    assert mhc.mhc_coeffs_split_k(16384, 4, 7168) == base[2]
+    assert mhc.mhc_coeffs_split_k(8192, 8, 4096) == s8
+    assert base[2] == 14
     tune.setenv("MHC_FUSED_PRE", 0)
     assert not one(16384, 4, 7168)
     mhc.mhc_tuning_reset()

@@ -41,16 +41,21 @@ def _gpu():
     yield
 
 
-# mhc_coeffs has three implementations, and every one must meet the bar:
+# mhc_coeffs has several implementations, and every one must meet the bar:
+#   default  whatever the call picks (above 256 rows: the persistent product
+#          for bf16 at n <= 4, the split-K product through LDS at n = 8);
 #   lds    split-K product with X staged through LDS by direct-to-LDS loads,
-#          then the combine kernel (the default above 256 rows);
+#          then the combine kernel (MHC_GEMM_ALGO=1);
 #   reg    the same with MFMA operands loaded straight from global memory
 #          (MHC_GEMM_ALGO=0);
 #   small  the one-launch small-B kernel (the default up to 256 rows; forced
 #          here for every size it supports with MHC_SMALL_MAX_B);
 #   persist  the product in the persistent kernel of mhc_post_res_coeffs
-#          (product only, MHC_GEMM_ALGO=2), then the combine kernel.
-GEMM_ALGOS = ["lds", "reg", "small", "persist"]
+#          (product only, MHC_GEMM_ALGO=2, also at n = 8), then the combine
+#          kernel.
+#   lds128x5, lds128x6  the LDS-staged product in 128-k chunks with a 5- or
+#          6-deep ring (MHC_GEMM_KC, MHC_GEMM_STAGES; bf16, n <= 4).
+GEMM_ALGOS = ["default", "lds", "reg", "small", "persist", "lds128x5", "lds128x6"]
 
 
 @pytest.fixture(params=GEMM_ALGOS)
@@ -62,8 +67,13 @@ def gemm_algo(request, tune):
         tune.setenv("MHC_SMALL_MAX_B", "0")
         if request.param == "reg":
             tune.setenv("MHC_GEMM_ALGO", "0")
+        elif request.param.startswith("lds"):
+            tune.setenv("MHC_GEMM_ALGO", "1")
         elif request.param == "persist":
             tune.setenv("MHC_GEMM_ALGO", "2")
+        if request.param.startswith("lds128x"):
+            tune.setenv("MHC_GEMM_KC", 128)
+            tune.setenv("MHC_GEMM_STAGES", int(request.param[-1]))
     return request.param
 
 
@@ -168,7 +178,7 @@ def test_parity_every_row_and_properties(name, gemm_algo):
     # every row against the oracle on the default product (in chunks of rows:
     # rows are independent); the other products on sampled rows here, and on
     # every row at the smaller shapes
-    chunks = ([list(range(lo, min(B, lo + 1024))) for lo in range(0, B, 1024)] if gemm_algo == "lds"
+    chunks = ([list(range(lo, min(B, lo + 1024))) for lo in range(0, B, 1024)] if gemm_algo == "default"
               else [sample_rows(B, 48, seed=B)])
     for rows in chunks:
         g = gpu_rows(o, rows)
