@@ -336,6 +336,263 @@ __global__ __launch_bounds__(512, 1) void lazy_prenorm_gemm_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Four-wave variant: the same 256 x 256 tiles and direct-to-LDS staging, but
+// one wave per SIMD, each owning 128 A rows x 128 W rows as 4 x 4 blocks of
+// v_mfma_f32_32x32x16_bf16 (256 accumulator registers, held in the AGPR half
+// of the 512-register file a lone wave gets).  Per 16-k step a wave reads
+// 4 + 4 operand vectors for 16 MFMAs: two thirds of the eight-wave layout's
+// LDS bytes per flop.
+//
+// With one wave per SIMD nothing hides a stall, so (measured on MI355X):
+//  * k moves in 32-wide chunks through four 32 KiB stages, three chunks
+//    ahead of the math (with two 64-wide stages, one chunk ahead, waiting
+//    for the DMA cost a third of the rate);
+//  * every instruction between two MFMAs delays the next one (a register-
+//    only loop of 32x32x16 MFMAs reaches 2.13 PFLOP/s from one wave per SIMD,
+//    16x16x32 ones only 1.48), so each step's MFMAs are issued in a fixed
+//    order with the other work placed between them, and the row sums of
+//    squares (v_dot2 on the A operands already in registers, no extra LDS
+//    reads) are split between the two waves that hold the same A rows.
+constexpr int kWaves4 = 4;
+constexpr int kKC4 = 32;                                   // k per chunk
+constexpr int kRB4 = kKC4 * 2;                             // 64 bytes per tile row per chunk
+constexpr int kTileBytes4 = kTile * kRB4;                  // 16 KiB
+constexpr int kStageBytes4 = 2 * kTileBytes4;              // A tile + W tile
+constexpr int kStages4 = 4;
+constexpr int kRowsPerInst4 = 1024 / kRB4;                 // 16 rows per DMA instruction
+constexpr int kInstPerWave4 = kTile / kRowsPerInst4 / kWaves4;  // 4 per operand
+constexpr int kLoadsPerWave4 = 2 * kInstPerWave4;          // vmcnt per chunk
+
+// 64-byte rows hold 4 pieces; piece p of row r sits in slot p ^ ((r >> 2) & 3),
+// so 16 consecutive rows read at one piece index cover all 64 banks once.
+__device__ __forceinline__ int swz4(int row) { return (row >> 2) & 3; }
+
+struct Operands4 {
+  bf16x8 a[4], w[4];
+};
+
+__global__ __launch_bounds__(256, 1) void lazy_prenorm_gemm4_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ W, uint16_t *__restrict__ Cout,
+    float *__restrict__ rstd_out, int M, int N, int K, float inv_k, float eps, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) char lds[kStages4 * kStageBytes4];
+  __shared__ float rs_lds[kTile];
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int j32 = lane & 31, g = lane >> 5;
+  const int wm = wave & 1, wn = wave >> 1;  // 2 x 2 waves
+
+  // Tile walk: as the eight-wave kernel (grouped order, one run per XCD).
+  const int T = tiles_m * tiles_n;
+  const int G = gridDim.x, bid = blockIdx.x;
+  const int x = bid & 7, jw = bid >> 3;
+  const int run0 = x * (T >> 3) + min(x, T & 7), runlen = (T >> 3) + (x < (T & 7) ? 1 : 0);
+  const int P = (G >> 3) + (x < (G & 7) ? 1 : 0);
+  const int ntiles = jw < runlen ? (runlen - 1 - jw) / P + 1 : 0;
+  auto tile_of = [&](int it, int &tm, int &tn) {
+    const int lin = run0 + jw + it * P;
+    const int group = lin / (kGroupM * tiles_n);
+    const int gm0 = group * kGroupM;
+    const int gsz = min(kGroupM, tiles_m - gm0);
+    const int within = lin - group * kGroupM * tiles_n;
+    tm = gm0 + within % gsz;
+    tn = within / gsz;
+  };
+
+  // DMA: wave w issues instructions 4 w .. 4 w + 3 of each operand; one
+  // instruction fills 16 rows of 64 bytes, lane l row 16 i + (l >> 2), slot
+  // l & 3 (piece slot ^ swz4(row)).  Rows past M (N) repeat the last row.
+  const uint32_t rowK2 = (uint32_t)K * 2u;
+  const int rsub = lane >> 2, slot = lane & 3;
+  const char *Ab = nullptr, *Wb = nullptr;
+  int dm0 = 0, dn0 = 0;
+  auto dma_tile = [&](int it) {
+    int tm, tn;
+    tile_of(it, tm, tn);
+    dm0 = tm * kTile;
+    dn0 = tn * kTile;
+    Ab = reinterpret_cast<const char *>(A) + (size_t)dm0 * rowK2;
+    Wb = reinterpret_cast<const char *>(W) + (size_t)dn0 * rowK2;
+  };
+  auto issue = [&](int stage, int k0) {
+    const uint32_t sb = lds_base + stage * kStageBytes4 + kInstPerWave4 * wave * 1024;
+    const char *ab = Ab + (size_t)k0 * 2, *wb = Wb + (size_t)k0 * 2;
+    auto off = [&](int jj, int base0, int lim, int &pc) {
+      const int r = kRowsPerInst4 * (kInstPerWave4 * wave + jj) + rsub;
+      pc = slot ^ swz4(r);
+      return (uint32_t)(min(base0 + r, lim - 1) - base0) * rowK2 + pc * 16;
+    };
+    if (k0 + kKC4 <= K) {
+#pragma unroll
+      for (int jj = 0; jj < kInstPerWave4; ++jj) {
+        int pc;
+        dma_saddr(ab, off(jj, dm0, M, pc), sb + jj * 1024);
+        dma_saddr(wb, off(jj, dn0, N, pc), sb + kTileBytes4 + jj * 1024);
+      }
+    } else {  // ragged last chunk: pieces past K read the zero block
+      const char *zero = reinterpret_cast<const char *>(g_lpn_zero);
+#pragma unroll
+      for (int jj = 0; jj < kInstPerWave4; ++jj) {
+        int pc;
+        const uint32_t oa = off(jj, dm0, M, pc), ow = off(jj, dn0, N, pc);
+        const bool in = k0 + pc * 8 < K;
+        dma_vaddr(in ? ab + oa : zero, sb + jj * 1024);
+        dma_vaddr(in ? wb + ow : zero, sb + kTileBytes4 + jj * 1024);
+      }
+    }
+  };
+  const int nchunks = (K + kKC4 - 1) / kKC4;
+  const int total = ntiles * nchunks;
+  int dit = 0, dc = 0;
+  auto issue_next = [&](int stage) {
+    if (dc == nchunks) {
+      dc = 0;
+      dma_tile(++dit);
+    }
+    issue(stage, dc * kKC4);
+    ++dc;
+  };
+
+  // Operand read r (0..3: a[r], 4..7: w[r-4]) of 16-k step t (0, 1) of a
+  // chunk: piece 2t + g of row j32 of each 32-row block (the 32x32x16 operand
+  // layout: lane l supplies k 8 (l >> 5) .. +7 of row l & 31).  The waves
+  // with wn = 1 hold their A blocks rotated by two (a[r] is block
+  // (r + 2 wn) & 3), so the blocks whose squares a wave sums are a[0] and
+  // a[1] in every wave: no selection in the MFMA stream.
+  const int sw = swz4(j32);
+  const int offw = kTileBytes4 + (wn * 128 + j32) * kRB4;
+  int offa[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) offa[r] = (wm * 128 + ((r + 2 * wn) & 3) * 32 + j32) * kRB4;
+  auto read_one = [&](Operands4 &o, int stage, int t, int r) {
+    const char *st = lds + stage * kStageBytes4;
+    const int sl = ((2 * t + g) ^ sw) * 16;
+    if (r < 4) o.a[r] = *reinterpret_cast<const bf16x8 *>(st + offa[r] + sl);
+    else o.w[r - 4] = *reinterpret_cast<const bf16x8 *>(st + offw + (r - 4) * 32 * kRB4 + sl);
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
+  // Sums of squares: each wave sums a[0] and a[1], i.e. A blocks 2 wn and
+  // 2 wn + 1 of its 128 rows (lane: row j32 of the block, k-half g).
+  float ssq[2] = {0.f, 0.f};
+  auto sq_slot = [&](const Operands4 &o, int i) {
+    if (i >= 8 && i < 12) {
+      const int b = (i - 8) >> 1, h = (i - 8) & 1;  // a[b], words 2 h, 2 h + 1
+      const u32x4 v = __builtin_bit_cast(u32x4, o.a[b]);
+      ssq[b] = dot2_sq_bf16(v[2 * h], ssq[b]);
+      ssq[b] = dot2_sq_bf16(v[2 * h + 1], ssq[b]);
+    }
+  };
+  // One 16-k step: its 16 MFMAs in a fixed order, `slot(i)` placing other
+  // work after MFMA i; scheduling barriers keep that order.
+  auto step = [&](const Operands4 &o, auto &&slotf) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int rb = i >> 2, cb = i & 3;
+      acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.w[cb], o.a[rb], acc[rb][cb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      slotf(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  if (total == 0) return;
+  dma_tile(0);
+#pragma unroll
+  for (int s = 0; s < kStages4; ++s)
+    if (s < total) issue_next(s);
+  // chunk 0 has landed for this wave, then for every wave
+  if (total >= 4) wait_vm<3 * kLoadsPerWave4>();
+  else if (total == 3) wait_vm<2 * kLoadsPerWave4>();
+  else if (total == 2) wait_vm<kLoadsPerWave4>();
+  else wait_vm<0>();
+  __builtin_amdgcn_s_barrier();
+  Operands4 o0, o1;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) read_one(o0, 0, 0, r);
+
+  int gc = 0;
+  for (int it = 0; it < ntiles; ++it) {
+    for (int c = 0; c < nchunks; ++c, ++gc) {
+      const int st = gc % kStages4;
+      // step 0: the reads of step 1 after MFMAs 0-7
+      step(o0, [&](int i) {
+        if (i < 8) read_one(o1, st, 1, i);
+        sq_slot(o0, i);
+      });
+      // step 1: after its first MFMA, wait until chunk gc+1 has landed and
+      // this wave's reads of chunk gc have returned, then the barrier: every
+      // wave is past chunk gc, so its stage takes chunk gc + 4.  The reads of
+      // chunk gc+1's first step follow MFMAs 8-15.
+      const int ahead = total - 1 - gc;  // chunks after this one
+      step(o1, [&](int i) {
+        if (i == 0) {
+          if (ahead >= 3) wait_vm<2 * kLoadsPerWave4>();
+          else if (ahead == 2) wait_vm<kLoadsPerWave4>();
+          else wait_vm<0>();
+          lds_barrier();
+          if (gc + kStages4 < total) issue_next(st);
+        }
+        if (i >= 8) read_one(o0, (gc + 1) % kStages4, 0, i - 8);  // past the stream's end: stale, unused
+        sq_slot(o1, i);
+      });
+    }
+
+    int tm, tn;
+    tile_of(it, tm, tn);
+    const int m0 = tm * kTile, n0 = tn * kTile;
+    // Row sums: the two k-halves of a row live in lanes j32 and j32 + 32.
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const float ss = ssq[b] + __shfl_xor(ssq[b], 32);
+      if (g == 0) rs_lds[wm * 128 + (2 * wn + b) * 32 + j32] = ss;
+      ssq[b] = 0.f;
+    }
+    lds_barrier();
+    if (tid < kTile) {
+      const float r = 1.0f / sqrtf(rs_lds[tid] * inv_k + eps);
+      if (tn == 0 && rstd_out != nullptr && m0 + tid < M) rstd_out[m0 + tid] = r;
+      rs_lds[tid] = r;
+    }
+    lds_barrier();
+
+    // Epilogue: block (rb, cb) of C^T; lane holds row j32 of A block rb and
+    // columns 8 q + 4 g .. +3 of W block cb; runs paired across lane halves
+    // by v_permlane32_swap, 16 bytes per lane.
+    const bool interior = (m0 + kTile <= M) && (n0 + kTile <= N);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int lr = wm * 128 + ((rb + 2 * wn) & 3) * 32 + j32;  // acc[rb] holds A block (rb + 2 wn) & 3
+      const int row = m0 + lr;
+      const float sc = rs_lds[lr];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const f32x16 v = acc[rb][cb];
+#pragma unroll
+        for (int qp = 0; qp < 4; qp += 2) {
+          const uint32_t a0 = pack_bf16x2(v[4 * qp] * sc, v[4 * qp + 1] * sc);
+          const uint32_t a1 = pack_bf16x2(v[4 * qp + 2] * sc, v[4 * qp + 3] * sc);
+          const uint32_t b0 = pack_bf16x2(v[4 * qp + 4] * sc, v[4 * qp + 5] * sc);
+          const uint32_t b1 = pack_bf16x2(v[4 * qp + 6] * sc, v[4 * qp + 7] * sc);
+          const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+          const u32x4 ov = {s0[0], s1[0], s0[1], s1[1]};
+          const int col = n0 + wn * 128 + cb * 32 + 8 * (qp + g);
+          if (interior || (row < M && col < N)) *reinterpret_cast<u32x4 *>(Cout + (size_t)row * N + col) = ov;
+        }
+        acc[rb][cb] = f32x16{};
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_lazy_prenorm_gemm(int64_t M, int64_t N, int64_t K, const void *A, const void *W,
@@ -345,9 +602,14 @@ hipError_t launch_lazy_prenorm_gemm(int64_t M, int64_t N, int64_t K, const void 
   // persistent: one workgroup per compute unit (the LDS stages allow one);
   // at least 8, so that each XCD run of the tile order has a workgroup
   const int64_t grid = std::min<int64_t>(tiles, std::max(device_cus(), 8));
-  lazy_prenorm_gemm_kernel<<<dim3((uint32_t)grid), kWaves * 64, 0, st>>>(
-      static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(W), static_cast<uint16_t *>(C),
-      rstd, (int)M, (int)N, (int)K, (float)(1.0 / (double)K), eps, tiles_m, tiles_n);
+  if (tune(kTuneLpnAlgo) == 1)
+    lazy_prenorm_gemm4_kernel<<<dim3((uint32_t)grid), kWaves4 * 64, 0, st>>>(
+        static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(W), static_cast<uint16_t *>(C),
+        rstd, (int)M, (int)N, (int)K, (float)(1.0 / (double)K), eps, tiles_m, tiles_n);
+  else
+    lazy_prenorm_gemm_kernel<<<dim3((uint32_t)grid), kWaves * 64, 0, st>>>(
+        static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(W), static_cast<uint16_t *>(C),
+        rstd, (int)M, (int)N, (int)K, (float)(1.0 / (double)K), eps, tiles_m, tiles_n);
   return hipGetLastError();
 }
 

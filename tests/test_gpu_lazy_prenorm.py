@@ -48,6 +48,13 @@ def _gpu():
     yield
 
 
+# Both kernels: the eight-wave one (MHC_LPN_ALGO 0) and the four-wave one (1).
+@pytest.fixture(autouse=True, params=[0, 1], ids=["w8", "w4"])
+def lpn_algo(request, tune):
+    tune.setenv("MHC_LPN_ALGO", request.param)
+    return request.param
+
+
 def _bf16_to_f64(t):
     return t.detach().to("cpu", torch.float32).double().numpy()
 
