@@ -283,7 +283,7 @@ int mhc_post_res_coeffs_pre_noalloc(int64_t B, int32_t n, int64_t C,
  * (no scale factors, as in the page's benchmark); inputs are widened exactly;
  * arithmetic is fp32 as in the bf16 calls; F_pre and X_next are rounded once
  * to E4M3, to nearest even, saturating at +-448 (torch's own cast returns NaN
- * past the range).  The product widens the E4M3 X exactly to bf16 for the
+ * past the range); a NaN (from a NaN input) stays NaN, as code 0x7F or 0xFF.  The product widens the E4M3 X exactly to bf16 for the
  * matrix core, so logits, r and H carry the bf16 calls' accuracy.
  *
  * Arguments, ownership, errors and workspace rules are those of the bf16

@@ -33,31 +33,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // FP8 E4M3 (the OCP "fn" encoding: bias 7, max 448, no infinities), four
 // values per 32-bit word, byte k holding element k.  gfx950's conversions use
 // this encoding and round to nearest even; narrowing would give NaN from
-// +-464 up, so values are clamped to +-448 first (saturation).  Widening to
-// fp32 (and from there to bf16) is exact.
+// +-464 up, so finite values are clamped to +-448 first (saturation).
+// Widening to fp32 (and from there to bf16) is exact.
 __device__ __forceinline__ f32x2 fp8_lo2(uint32_t w) {  // elements 0, 1
   return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
 }
 __device__ __forceinline__ f32x2 fp8_hi2(uint32_t w) {  // elements 2, 3
   return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
 }
-__device__ __forceinline__ float sat_e4m3(float x) { return __builtin_amdgcn_fmed3f(x, -448.0f, 448.0f); }
-// Byte k of w becomes the NaN code 0x7F where input k is NaN.
-__device__ __forceinline__ uint32_t fp8x4_nan_fix(uint32_t w, float a, float b, float c, float d) {
-  const uint32_t m = (a != a ? 0x000000ffu : 0u) | (b != b ? 0x0000ff00u : 0u) |
-                     (c != c ? 0x00ff0000u : 0u) | (d != d ? 0xff000000u : 0u);
-  return (w & ~m) | (0x7f7f7f7fu & m);
+// Saturation to +-448 with gfx950's NaN-propagating minimum / maximum
+// (v_minimum3_f32, v_maximum3_f32): a NaN stays NaN and converts to an E4M3
+// NaN code (S.1111.111), where the plain clamp (v_med3_f32) would turn it
+// into -448.  One instruction more per value than that clamp, no branch.
+__device__ __forceinline__ float sat_e4m3(float x) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_minimum(x, 448.0f), -448.0f);
 }
 __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
   const int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(a), sat_e4m3(b), 0, false);
-  const uint32_t r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(c), sat_e4m3(d), w, true);
-  // The clamp takes a NaN to -448; a NaN keeps the NaN code 0x7F instead.
-  // The sum is NaN when one of the four is (or when infinities of both signs
-  // meet, which the per-value test then sorts out), so the common case costs
-  // three adds and a compare.
-  const float s = (a + b) + (c + d);
-  if (__builtin_expect(s != s, 0)) return fp8x4_nan_fix(r, a, b, c, d);
-  return r;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(c), sat_e4m3(d), w, true);
 }
 // Eight E4M3 values (two words) -> the same eight values as bf16 (exact).
 // gfx950's scaled OCP conversion with scale 1.0 widens a pair straight to

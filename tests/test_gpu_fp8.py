@@ -294,10 +294,11 @@ def test_fp8_fused_deterministic(kernel, tune):
 
 
 def test_fp8_nan_codes():
-    """NaN inputs (E4M3 codes 0x7F and 0xFF) give the NaN code 0x7F in every
-    output they reach, as the oracle's encoding does (the saturating clamp
-    alone would turn them into -448), in the stand-alone apply and pre-mix;
-    every other code is the oracle's."""
+    """NaN inputs (E4M3 codes 0x7F and 0xFF) give a NaN code (S.1111.111:
+    0x7F, the oracle's, or 0xFF -- OCP E4M3 has the two and the pages fix no
+    sign for a NaN) in every output they reach and nowhere else (the plain
+    saturating clamp would turn them into -448), in the stand-alone apply and
+    pre-mix; every other code is the oracle's."""
     _say("fp8 NaN codes")
     B, n, C = 64, 4, 256
     N = n * n + 2 * n
@@ -322,8 +323,10 @@ def test_fp8_nan_codes():
     got_x, got_f = synth.e4m3_codes(o["X_next"]), synth.e4m3_codes(o["F_pre"])
     assert (want_x == 0x7F).sum() == 4 * 4 and (want_f == 0x7F).sum() == 3
     nan_x, nan_f = want_x == 0x7F, want_f == 0x7F
-    assert np.array_equal(got_x[nan_x], want_x[nan_x]) and (got_x[~nan_x] != 0x7F).all()
-    assert np.array_equal(got_f[nan_f], want_f[nan_f]) and (got_f[~nan_f] != 0x7F).all()
+    is_nan = lambda c: (c & 0x7F) == 0x7F  # noqa: E731
+    assert is_nan(got_x[nan_x]).all() and not is_nan(got_x[~nan_x]).any()
+    assert is_nan(got_f[nan_f]).all() and not is_nan(got_f[~nan_f]).any()
+    _say(f"NaN codes produced: {sorted(set(got_x[nan_x].tolist()) | set(got_f[nan_f].tolist()))}")
     exact_x = oracle.post_res(x, f, post, res, n, C)
     exact_f = oracle.pre_mix(x, pre, n, C)
     sx = fp32_slack_post(np.nan_to_num(x), np.nan_to_num(f), post, res, n, C)
