@@ -580,6 +580,31 @@ def _lazy_prenorm(mhc, torch, synth, stream, ev, steps=20, warmup=5):
     return out
 
 
+def _lpn_counters(mhc, torch, synth, launches=8):
+    """The square Lazy Pre-Norm workload for counter runs: `launches` calls of
+    the eight-wave kernel (the default), of the four-wave kernel
+    (MHC_LPN_ALGO = 1), then of torch's A @ W^T (the vendor GEMM, no norm) as
+    the library reference, each group followed by a device synchronisation."""
+    cfg = synth.LPN_CONFIGS["lpn_square"]
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    d = synth.make_lpn_inputs(M, N, K, seed=cfg["seed"], device="cuda")
+    C = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    r = torch.empty(M, dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream()
+    try:
+        for algo in (0, 1):
+            mhc.mhc_tuning_set("MHC_LPN_ALGO", algo)
+            for _ in range(launches):
+                mhc.mhc_lazy_prenorm_gemm(M, N, K, d["A"], d["W"], C, r, stream=s)
+            torch.cuda.synchronize()
+    finally:
+        mhc.mhc_tuning_set("MHC_LPN_ALGO", -1)
+    for _ in range(launches):
+        torch.matmul(d["A"], d["W"].t())
+    torch.cuda.synchronize()
+    print(json.dumps({"lpn_counters": {"shape": f"M={M} N={N} K={K}", "launches": launches}}), flush=True)
+
+
 SWEEP_SHAPES = [(4, 2048, 16384), (4, 4096, 16384), (4, 7168, 1024), (4, 7168, 4096),
                 (4, 7168, 16384), (4, 7168, 32768), (4, 7168, 65536), (4, 8192, 16384),
                 (2, 7168, 16384), (1, 7168, 16384)]
@@ -662,6 +687,9 @@ def main():
                     help="skip the E4M3 and other-workload sections (profiling runs of one workload)")
     ap.add_argument("--lazy-prenorm-only", action="store_true",
                     help="time only mhc_lazy_prenorm_gemm on its workloads (profiling runs)")
+    ap.add_argument("--lpn-counters", action="store_true",
+                    help="square Lazy Pre-Norm workload: a few launches of each kernel layout and of "
+                         "torch's A @ W^T (counter runs)")
     ap.add_argument("--shape-sweep", action="store_true",
                     help="time the one-pass layer call over a grid of shapes (one JSON line each)")
     args = ap.parse_args()
@@ -690,6 +718,9 @@ def main():
     mhc.load()  # raises if the HIP library is not built
     if args.shape_sweep:
         _shape_sweep(mhc, torch, synth)
+        return
+    if args.lpn_counters:
+        _lpn_counters(mhc, torch, synth)
         return
     if args.lazy_prenorm_only:
         lpn = _lazy_prenorm(mhc, torch, synth, torch.cuda.current_stream(),

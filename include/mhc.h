@@ -433,12 +433,17 @@ int mhc_lazy_prenorm_gemm(int64_t M, int64_t N, int64_t K, const void *A, const 
  *   MHC_SMALL_MAX_B  rows up to which the one-launch small-B coefficient
  *                    kernel runs (0: never)
  *   MHC_GEMM_ALGO    0: register-path product; 2: persistent product kernel
- *   MHC_SPLIT_K, MHC_GEMM_WGS, MHC_GEMM_MB   split-K product shape
+ *   MHC_SPLIT_K, MHC_GEMM_WGS, MHC_GEMM_MB, MHC_GEMM_WAVES   split-K
+ *                    product shape (K-slices, target workgroups, 16-row
+ *                    blocks per wave, 4 or 8 waves per workgroup)
+ *   MHC_GEMM_KC, MHC_GEMM_STAGES   128 with 5 or 6: the bf16 split-K product
+ *                    at n <= 4 in 128-k chunks with a deeper ring
  *   MHC_FUSED_N8     > 0: the fused kernel also at n = 8
  *   MHC_FUSED_FP8    0: E4M3 fused call as apply + product; > 0: fused kernel
  *   MHC_FUSED_FIXED  0 / 1: the fused kernel's fixed-slice layout off / on
  *   MHC_FUSED_SPU, MHC_FUSED_WGS   fused kernel's steps per unit, grid cap
  *   MHC_FUSED_PRE    0: mhc_post_res_coeffs_pre(_fp8) as two calls
+ *   MHC_LPN_ALGO     1: the four-wave Lazy Pre-Norm GEMM kernel
  * Every route computes the same results up to fp32 summation order (the
  * fused calls' X_next and F_pre_next bitwise).  The workspace-size functions
  * answer for the routes selected at the time they are called, so set

@@ -31,12 +31,24 @@
 // X.phi_hi + X.phi_lo, into the same fp32 accumulator (bf16 X times either
 // part is exact in fp32).
 //
-// Pipeline per workgroup (4 waves, 64*MB rows): the loads of chunks
+// Pipeline per workgroup (W waves, 16*MB*W rows): the loads of chunks
 // c+1 .. c+STAGES-1 are in flight while chunk c is multiplied.  Each wave
 // waits only for its own share of chunk c (s_waitcnt vmcnt), then one barrier
 // makes the whole chunk visible and frees the slot of chunk c-1 for refill.
+//
+// Why eight waves.  A wave's direct-to-LDS loads complete at about 6-7 GB/s
+// on MI355X whether they hit HBM or L2 (measured with plain streaming probes:
+// one 4-wave workgroup per CU moves 6.4 TB/s from HBM and only 7.3 TB/s from
+// an L2-resident buffer; 8 waves per CU move 15.4 TB/s, 16 waves 23 TB/s from
+// L2), so the chip-wide staging rate grows with the number of waves issuing
+// them.  With 4 waves the X + phi bytes staged per X byte (1.5 at n = 4, 2.25
+// at n = 8 with 64-row tiles) capped the X rate near 7.3 TB/s divided by that
+// ratio.  Eight waves per workgroup (128-row tiles) double the issuing waves
+// and halve phi's share.
 #include "mhc_device.h"
 #include "mhc_launch.h"
+
+#include <type_traits>
 
 namespace mhc {
 
@@ -44,13 +56,13 @@ namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int NS, int MB, int KC, int STAGES, int XB, int P2 = 1>
+template <int NS, int MB, int KC, int STAGES, int XB, int P2 = 1, int W = 4>
 struct LdsTile {
   static constexpr int N = NS * NS + 2 * NS;
   static constexpr int NP = N + 1;
   static constexpr int NB = (N + 15) / 16;
   static constexpr int PB = NB * P2;                 // packed phi blocks per 32-k step
-  static constexpr int RT = 64 * MB;                 // rows per workgroup
+  static constexpr int RT = 16 * MB * W;             // rows per workgroup
   static constexpr int T = KC / 32;                  // MFMA k-steps per chunk
   static constexpr int EPP = 16 / XB;                // X elements per 16-byte piece
   static constexpr int ROW_BYTES = KC * XB;          // one row of a chunk in LDS
@@ -58,17 +70,21 @@ struct LdsTile {
   static constexpr int RPI = 64 / PIECES;            // rows per load instruction
   static constexpr int XI = RT * PIECES / 64;        // X load instructions per chunk
   static constexpr int PI = T * PB;                  // phi load instructions per chunk
-  static constexpr int XI_W = XI / 4, PI_W = PI / 4; // ... per wave
-  static constexpr int VM_PER_CHUNK = XI_W + PI_W;
+  static constexpr int XI_W = XI / W;                // X loads per wave
+  // phi load j*W + w is wave w's j-th: waves below PI_REM issue PI_HI, the
+  // others PI_LO (equal when W divides PI).
+  static constexpr int PI_LO = PI / W, PI_REM = PI % W, PI_HI = PI_LO + (PI_REM ? 1 : 0);
+  static constexpr int VM_HI = XI_W + PI_HI, VM_LO = XI_W + PI_LO;  // loads per chunk per wave
   static constexpr int X_BYTES = RT * ROW_BYTES;
   static constexpr int P_BYTES = PI * 1024;
   static constexpr int STAGE_BYTES = X_BYTES + P_BYTES;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static_assert(W == 4 || W == 8, "four or eight waves");
   static_assert(PIECES >= 16 && PIECES <= 64, "swizzle needs 16..64 pieces per row");
-  static_assert(XI % 4 == 0 && PI % 4 == 0, "load instructions must split evenly over 4 waves");
+  static_assert(XI % W == 0, "X load instructions must split evenly over the waves");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(STAGES >= 2 && STAGES <= 6, "pipeline depth");
-  static_assert((STAGES - 2) * (XI_W + PI_W) < 64, "vmcnt range");
+  static_assert((STAGES - 2) * VM_HI < 64, "vmcnt range");
 };
 
 // s_waitcnt with only the vector-memory counter constrained (expcnt and
@@ -79,13 +95,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int NS, int MB, int KC, int STAGES, int XB, int P2>
+template <int NS, int MB, int KC, int STAGES, int XB, int P2, int W>
 __device__ __forceinline__ void issue_chunk(char *lds, int slot, int wave, int lane,
                                            const uint8_t *__restrict__ X,
                                            const uint16_t *__restrict__ phip,
                                            const uint16_t *__restrict__ zero, int row0, int B,
                                            int K, int k0) {
-  using L = LdsTile<NS, MB, KC, STAGES, XB, P2>;
+  using L = LdsTile<NS, MB, KC, STAGES, XB, P2, W>;
   char *xs = lds + slot * L::STAGE_BYTES;
   char *ps = xs + L::X_BYTES;
   const int slot_in_row = lane % L::PIECES;
@@ -102,10 +118,12 @@ __device__ __forceinline__ void issue_chunk(char *lds, int slot, int wave, int l
   }
   const int kstep0 = k0 / 32;
 #pragma unroll
-  for (int j = 0; j < L::PI_W; ++j) {
-    const int inst = wave * L::PI_W + j;                       // = t * PB + block
-    const uint16_t *src = phip + ((size_t)(kstep0 * L::PB + inst) * 64 + lane) * 8;
-    __builtin_amdgcn_global_load_lds(src, (lds_void *)(ps + inst * 1024), 16, 0, 0);
+  for (int j = 0; j < L::PI_HI; ++j) {
+    const int inst = j * W + wave;                             // = t * PB + block
+    if (j < L::PI_LO || wave < L::PI_REM) {                    // wave-uniform
+      const uint16_t *src = phip + ((size_t)(kstep0 * L::PB + inst) * 64 + lane) * 8;
+      __builtin_amdgcn_global_load_lds(src, (lds_void *)(ps + inst * 1024), 16, 0, 0);
+    }
   }
 }
 
@@ -114,11 +132,9 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
 }
 
 // Wait until at most `later` chunks' loads of this wave are outstanding
-// (later <= STAGES - 2).
-template <int NS, int MB, int KC, int STAGES, int XB, int P2>
-__device__ __forceinline__ void wait_chunks(int later) {
-  using L = LdsTile<NS, MB, KC, STAGES, XB, P2>;
-  constexpr int V = L::VM_PER_CHUNK;
+// (later <= STAGES - 2; V = this wave's loads per chunk).
+template <int STAGES, int V>
+__device__ __forceinline__ void wait_chunks_v(int later) {
   if (STAGES >= 6 && later >= 4) wait_vmcnt<(STAGES >= 6 ? 4 : 0) * V>();
   else if (STAGES >= 5 && later >= 3) wait_vmcnt<(STAGES >= 5 ? 3 : 0) * V>();
   else if (STAGES >= 4 && later >= 2) wait_vmcnt<(STAGES >= 4 ? 2 : 0) * V>();
@@ -126,13 +142,20 @@ __device__ __forceinline__ void wait_chunks(int later) {
   else wait_vmcnt<0>();
 }
 
-template <int NS, int MB, int KC, int STAGES, int XB, int P2>
-__global__ __launch_bounds__(256) void gemm_rms_lds_kernel(const uint8_t *__restrict__ X,
-                                                           const uint16_t *__restrict__ phip,
-                                                           const uint16_t *__restrict__ zero,
-                                                           float *__restrict__ ws, int B, int K,
-                                                           int kslice) {
-  using L = LdsTile<NS, MB, KC, STAGES, XB, P2>;
+template <int NS, int MB, int KC, int STAGES, int XB, int P2, int W>
+__device__ __forceinline__ void wait_chunks(int later, int wave) {
+  using L = LdsTile<NS, MB, KC, STAGES, XB, P2, W>;
+  if (L::PI_REM == 0 || wave < L::PI_REM) wait_chunks_v<STAGES, L::VM_HI>(later);  // wave-uniform
+  else wait_chunks_v<STAGES, L::VM_LO>(later);
+}
+
+template <int NS, int MB, int KC, int STAGES, int XB, int P2, int W>
+__global__ __launch_bounds__(W * 64) void gemm_rms_lds_kernel(const uint8_t *__restrict__ X,
+                                                              const uint16_t *__restrict__ phip,
+                                                              const uint16_t *__restrict__ zero,
+                                                              float *__restrict__ ws, int B, int K,
+                                                              int kslice) {
+  using L = LdsTile<NS, MB, KC, STAGES, XB, P2, W>;
   __shared__ __attribute__((aligned(1024))) char lds[L::LDS_BYTES];
 
   const int tid = threadIdx.x;
@@ -156,8 +179,8 @@ __global__ __launch_bounds__(256) void gemm_rms_lds_kernel(const uint8_t *__rest
 #pragma unroll
   for (int c = 0; c < STAGES - 1; ++c)
     if (c < nchunks)
-      issue_chunk<NS, MB, KC, STAGES, XB, P2>(lds, c, wave, lane, X, phip, zero, row0, B, K,
-                                      k_begin + c * KC);
+      issue_chunk<NS, MB, KC, STAGES, XB, P2, W>(lds, c, wave, lane, X, phip, zero, row0, B, K,
+                                         k_begin + c * KC);
 
   for (int c = 0; c < nchunks; ++c) {
     // This wave's loads of chunk c have landed and its LDS reads of chunk
@@ -165,45 +188,67 @@ __global__ __launch_bounds__(256) void gemm_rms_lds_kernel(const uint8_t *__rest
     // chunk c is complete and the slot of chunk c-1 may be refilled.  (A bare
     // s_barrier: a fenced __syncthreads would also wait for the loads still
     // in flight for the later chunks.)
-    wait_chunks<NS, MB, KC, STAGES, XB, P2>(min(STAGES - 2, nchunks - 1 - c));
+    wait_chunks<NS, MB, KC, STAGES, XB, P2, W>(min(STAGES - 2, nchunks - 1 - c), wave);
     wait_lgkmcnt0();
     asm volatile("" ::: "memory");  // no memory access moves across the barrier
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     const int cn = c + STAGES - 1;
     if (cn < nchunks)
-      issue_chunk<NS, MB, KC, STAGES, XB, P2>(lds, cn % STAGES, wave, lane, X, phip, zero, row0, B, K,
-                                      k_begin + cn * KC);
+      issue_chunk<NS, MB, KC, STAGES, XB, P2, W>(lds, cn % STAGES, wave, lane, X, phip, zero, row0, B,
+                                         K, k_begin + cn * KC);
     const char *xs = lds + (c % STAGES) * L::STAGE_BYTES;
     const char *ps = xs + L::X_BYTES;
-#pragma unroll
-    for (int t = 0; t < L::T; ++t) {
+    // The operands of k-step t+1 are read from LDS while the MFMAs of k-step
+    // t run (two register sets, the order pinned by scheduling barriers), so
+    // only the first k-step of a chunk waits for a full LDS round trip.  Left
+    // to itself the compiler reads two B operands at a time and waits for
+    // each pair, three round trips per k-step at n = 8.
+    using RawA = std::conditional_t<XB == 2, bf16x8, u32x2>;
+    struct Ops {
       bf16x8 b[L::PB];
+      RawA a[MB];
+    };
+    auto read_ops = [&](Ops &o, int t) {
 #pragma unroll
       for (int j = 0; j < L::PB; ++j)
-        b[j] = *reinterpret_cast<const bf16x8 *>(ps + (t * L::PB + j) * 1024 + lane * 16);
+        o.b[j] = *reinterpret_cast<const bf16x8 *>(ps + (t * L::PB + j) * 1024 + lane * 16);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const int rr = wave * 16 * MB + mb * 16 + m;
-        bf16x8 a;
         if constexpr (XB == 2) {
           const int slot = (4 * t + g) ^ m;  // rr & 15 == m
-          a = *reinterpret_cast<const bf16x8 *>(xs + rr * L::ROW_BYTES + slot * 16);
+          o.a[mb] = *reinterpret_cast<const bf16x8 *>(xs + rr * L::ROW_BYTES + slot * 16);
         } else {
-          // E4M3: k = 32t + 8g .. +7 is the (g & 1) half of piece 2t + g/2;
-          // it widens exactly to bf16.
+          // E4M3: k = 32t + 8g .. +7 is the (g & 1) half of piece 2t + g/2.
           const int slot = (2 * t + (g >> 1)) ^ m;
-          const u32x2 v = *reinterpret_cast<const u32x2 *>(xs + rr * L::ROW_BYTES + slot * 16 + (g & 1) * 8);
-          a = __builtin_bit_cast(bf16x8, fp8x8_to_bf16(v));
+          o.a[mb] = *reinterpret_cast<const u32x2 *>(xs + rr * L::ROW_BYTES + slot * 16 + (g & 1) * 8);
         }
+      }
+    };
+    auto mfma_ops = [&](const Ops &o) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        bf16x8 a;
+        if constexpr (XB == 2) a = o.a[mb];
+        else a = __builtin_bit_cast(bf16x8, fp8x8_to_bf16(o.a[mb]));  // exact widening
 #pragma unroll
         for (int nb = 0; nb < L::NB; ++nb) {
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[nb], acc[mb][nb], 0, 0, 0);
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, o.b[nb], acc[mb][nb], 0, 0, 0);
           if constexpr (P2 == 2)  // the low part of an fp32 phi
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[L::NB + nb], acc[mb][nb], 0, 0, 0);
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, o.b[L::NB + nb], acc[mb][nb], 0, 0, 0);
         }
         gram[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, a, gram[mb], 0, 0, 0);
       }
+    };
+    Ops ops[2];
+    read_ops(ops[0], 0);
+#pragma unroll
+    for (int t = 0; t < L::T; ++t) {
+      if (t + 1 < L::T) read_ops(ops[(t + 1) & 1], t + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_ops(ops[t & 1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -334,10 +379,11 @@ __global__ __launch_bounds__(256) void pack_phi32_kernel(const float *__restrict
 
 }  // namespace
 
-template <int NS, int MB, int KC, int STAGES, int XB, int P2>
+template <int NS, int MB, int KC, int STAGES, int XB, int P2, int W>
 hipError_t launch_gemm_lds_typed(const GemmPlan &p, int64_t B, int64_t C, const void *X,
                                  const void *phi, void *ws_base, hipStream_t st) {
-  using L = LdsTile<NS, MB, KC, STAGES, XB, P2>;
+  using L = LdsTile<NS, MB, KC, STAGES, XB, P2, W>;
+  if (p.row_tiles * L::RT < B) return hipErrorInvalidValue;  // the plan's tiles must cover B
   const int K = (int)(NS * C);
   char *base = static_cast<char *>(ws_base);
   uint16_t *phip = reinterpret_cast<uint16_t *>(base + p.phip_offset);
@@ -353,7 +399,7 @@ hipError_t launch_gemm_lds_typed(const GemmPlan &p, int64_t B, int64_t C, const 
   }
   if (e != hipSuccess) return e;
   const dim3 grid((uint32_t)p.row_tiles, (uint32_t)p.split);
-  gemm_rms_lds_kernel<NS, MB, KC, STAGES, XB, P2><<<grid, 256, 0, st>>>(
+  gemm_rms_lds_kernel<NS, MB, KC, STAGES, XB, P2, W><<<grid, W * 64, 0, st>>>(
       static_cast<const uint8_t *>(X), phip, zero, reinterpret_cast<float *>(base), (int)B, K,
       (int)p.kslice);
   return hipGetLastError();
@@ -402,6 +448,9 @@ template hipError_t launch_gemm_lds_typed<2, 1, 128, 6, 2, 1>(const GemmPlan &, 
 template hipError_t launch_gemm_lds_typed<4, 1, 128, 6, 2, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
 template hipError_t launch_gemm_lds_typed<2, 1, 256, 3, 2, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
 template hipError_t launch_gemm_lds_typed<4, 1, 256, 3, 2, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<8, 2, 128, 3, 2, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<8, 2, 256, 2, 1, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<8, 1, 256, 2, 2, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
 template hipError_t launch_gemm_lds_typed<8, 1, 128, 4, 2, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
 template hipError_t launch_gemm_lds_typed<1, 1, 256, 4, 1, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
 template hipError_t launch_gemm_lds_typed<2, 1, 256, 4, 1, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
@@ -410,6 +459,18 @@ template hipError_t launch_gemm_lds_typed<8, 1, 256, 2, 1, 1>(const GemmPlan &, 
 template hipError_t launch_gemm_lds_typed<1, 2, 256, 3, 1, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
 template hipError_t launch_gemm_lds_typed<2, 2, 256, 3, 1, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
 template hipError_t launch_gemm_lds_typed<4, 2, 256, 3, 1, 1>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+// eight waves per workgroup (128-row tiles)
+template hipError_t launch_gemm_lds_typed<1, 1, 128, 4, 2, 1, 8>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<2, 1, 128, 4, 2, 1, 8>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<4, 1, 128, 4, 2, 1, 8>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<1, 1, 256, 2, 2, 1, 8>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<2, 1, 256, 2, 2, 1, 8>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<4, 1, 256, 2, 2, 1, 8>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<8, 1, 128, 3, 2, 1, 8>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<1, 1, 256, 3, 1, 1, 8>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<2, 1, 256, 3, 1, 1, 8>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<4, 1, 256, 3, 1, 1, 8>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_lds_typed<8, 1, 256, 2, 1, 1, 8>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
 // fp32 phi (hi + lo parts)
 template hipError_t launch_gemm_lds_typed<1, 1, 128, 4, 2, 2>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
 template hipError_t launch_gemm_lds_typed<2, 1, 128, 4, 2, 2>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);

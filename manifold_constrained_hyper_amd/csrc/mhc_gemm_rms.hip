@@ -250,13 +250,26 @@ hipError_t launch_n(const GemmPlan &p, int64_t B, int64_t C, const void *X, cons
     if constexpr (NS == 8) return launch_gemm_lds_typed<NS, 1, 128, 2, 2, 2>(p, B, C, X, phi, ws, st);
     else return launch_gemm_lds_typed<NS, 1, 128, 4, 2, 2>(p, B, C, X, phi, ws, st);
   }
+  if (p.algo == 1 && p.xb == 1 && p.waves == 8) {
+    if constexpr (NS == 8) return launch_gemm_lds_typed<NS, 1, 256, 2, 1, 1, 8>(p, B, C, X, phi, ws, st);
+    else return launch_gemm_lds_typed<NS, 1, 256, 3, 1, 1, 8>(p, B, C, X, phi, ws, st);
+  }
+  if (p.algo == 1 && p.waves == 8) {
+    if constexpr (NS == 8) return launch_gemm_lds_typed<NS, 1, 128, 3, 2, 1, 8>(p, B, C, X, phi, ws, st);
+    else if (p.kc == 256) return launch_gemm_lds_typed<NS, 1, 256, 2, 2, 1, 8>(p, B, C, X, phi, ws, st);
+    else return launch_gemm_lds_typed<NS, 1, 128, 4, 2, 1, 8>(p, B, C, X, phi, ws, st);
+  }
   if (p.algo == 1 && p.xb == 1) {
-    if constexpr (NS == 8) return launch_gemm_lds_typed<NS, 1, 256, 2, 1, 1>(p, B, C, X, phi, ws, st);
-    else if (p.mb == 2) return launch_gemm_lds_typed<NS, 2, 256, 3, 1, 1>(p, B, C, X, phi, ws, st);
+    if constexpr (NS == 8) {
+      if (p.mb == 2) return launch_gemm_lds_typed<NS, 2, 256, 2, 1, 1>(p, B, C, X, phi, ws, st);
+      return launch_gemm_lds_typed<NS, 1, 256, 2, 1, 1>(p, B, C, X, phi, ws, st);
+    } else if (p.mb == 2) return launch_gemm_lds_typed<NS, 2, 256, 3, 1, 1>(p, B, C, X, phi, ws, st);
     else return launch_gemm_lds_typed<NS, 1, 256, 4, 1, 1>(p, B, C, X, phi, ws, st);
   }
   if (p.algo == 1) {
     if constexpr (NS == 8) {
+      if (p.mb == 2) return launch_gemm_lds_typed<NS, 2, 128, 3, 2, 1>(p, B, C, X, phi, ws, st);
+      if (p.kc == 256) return launch_gemm_lds_typed<NS, 1, 256, 2, 2, 1>(p, B, C, X, phi, ws, st);
       return launch_gemm_lds_typed<NS, 1, 128, 4, 2, 1>(p, B, C, X, phi, ws, st);
     } else {
       if (p.kc == 128 && p.stages == 5) return launch_gemm_lds_typed<NS, 1, 128, 5, 2, 1>(p, B, C, X, phi, ws, st);
@@ -271,8 +284,9 @@ hipError_t launch_n(const GemmPlan &p, int64_t B, int64_t C, const void *X, cons
 }  // namespace
 
 GemmPlan plan_gemm_custom(int64_t B, int n, int64_t C, int algo, int mb, int kc, int stages,
-                          int64_t target_wgs) {
+                          int64_t target_wgs, int waves) {
   GemmPlan p;
+  p.waves = algo == 1 ? waves : 4;
   const int64_t K = (int64_t)n * C;
   const int64_t N = (int64_t)n * n + 2 * n;
   const int64_t NB = (N + 15) / 16;
@@ -282,7 +296,8 @@ GemmPlan plan_gemm_custom(int64_t B, int n, int64_t C, int algo, int mb, int kc,
   p.kc = kc;
   p.mb = mb;
   p.stages = stages;
-  p.row_tiles = (B + 64 * p.mb - 1) / (64 * p.mb);
+  const int64_t rows = 16 * (int64_t)p.mb * p.waves;
+  p.row_tiles = (B + rows - 1) / rows;
   const int64_t kchunks = (K + p.kc - 1) / p.kc;
   int64_t want = (target_wgs + p.row_tiles - 1) / p.row_tiles;
   if (tune(kTuneSplitK) > 0) want = tune(kTuneSplitK);  // tuning override
@@ -316,20 +331,34 @@ GemmPlan plan_gemm(int64_t B, int n, int64_t C, bool fp8_x, bool phi32) {
     p.total_bytes = p.zero_offset + 256;
     return p;
   }
-  // X staged through LDS (algo 1), one 4-wave workgroup per CU at a time
-  // (the LDS ring is ~144 KiB); enough workgroups to fill the 256 CUs, and no
-  // more K-slices than that needs, since every slice adds (N+1)*4 bytes of
+  // X staged through LDS (algo 1), one workgroup per CU at a time (the LDS
+  // ring is 144-160 KiB); enough workgroups to fill the 256 CUs, and no more
+  // K-slices than that needs, since every slice adds (N+1)*4 bytes of
   // partials per row.  E4M3 X: 256-k chunks (16 pieces of 16 bytes per row),
-  // four stages (two at n = 8, whose phi blocks are larger).
+  // 128-row tiles, three stages (two at n = 8, whose phi blocks are larger).
+  const int64_t tw = tune(kTuneGemmWaves);
   if (fp8_x) {
+    // E4M3 X: eight waves per workgroup by default (measured at n = 8, C = 4096,
+    // B = 8192: 85 us against 90 us with four waves of two 16-row blocks and
+    // 107-129 us with four waves of one; at n = 4, C = 7168, B = 16384:
+    // 96 against 97-100 us).
+    const int waves = tw == 4 ? 4 : 8;
     const int64_t target = tune(kTuneGemmWgs) > 0 ? tune(kTuneGemmWgs) : 256;
     int mb = n == 8 ? 1 : 2;  // 128-row tiles: phi per X byte as for bf16 with 64 rows
     const int64_t v = tune(kTuneGemmMb);
-    if (v == 1 || (v == 2 && n != 8)) mb = (int)v;
-    GemmPlan p = plan_gemm_custom(B, n, C, 1, mb, 256, n == 8 ? 2 : (mb == 2 ? 3 : 4), target);
+    if (v == 1 || v == 2) mb = (int)v;
+    int stages = n == 8 ? 2 : (mb == 2 ? 3 : 4);
+    if (waves == 8) {  // 8 waves x 16 rows: 128-row tiles
+      mb = 1;
+      stages = n == 8 ? 2 : 3;
+    }
+    GemmPlan p = plan_gemm_custom(B, n, C, 1, mb, 256, stages, target, waves);
     p.xb = 1;
     return p;
   }
+  // bf16 X: four waves by default (eight measured no faster: 145 against
+  // 140-150 us at n = 8, C = 4096, B = 8192; 172 against 169 us at n = 4).
+  const int waves = tw == 8 ? 8 : 4;
   int kc = (n == 8) ? 128 : 256;
   int stages = (n == 8) ? 4 : 3;
   if (n != 8 && tune(kTuneGemmKc) == 128 && (tune(kTuneGemmStages) == 5 || tune(kTuneGemmStages) == 6)) {
@@ -339,7 +368,26 @@ GemmPlan plan_gemm(int64_t B, int n, int64_t C, bool fp8_x, bool phi32) {
   if (tune(kTuneGemmAlgo) == 0)  // tuning override: the register path (1: the LDS path, the default here)
     return plan_gemm_custom(B, n, C, 0, (B >= 1024) ? 2 : 1, kGemmKC, 1, kGemmTargetWGs);
   const int64_t target = tune(kTuneGemmWgs) > 0 ? tune(kTuneGemmWgs) : 256;
-  return plan_gemm_custom(B, n, C, 1, 1, kc, stages, target);
+  int mb = 1;
+  if (waves == 8) {  // 8 waves x 16 rows: 128-row tiles
+    if (n == 8) {
+      kc = 128;
+      stages = 3;
+    } else if (tune(kTuneGemmKc) == 256) {
+      kc = 256;
+      stages = 2;
+    } else {
+      kc = 128;
+      stages = 4;
+    }
+  } else if (n == 8 && tune(kTuneGemmMb) == 2) {
+    mb = 2;  // 128-row tiles at n = 8: half the phi operand traffic per X byte, three stages
+    stages = 3;
+  } else if (n == 8 && tune(kTuneGemmKc) == 256) {
+    kc = 256;  // 512-byte row pieces at n = 8, two stages
+    stages = 2;
+  }
+  return plan_gemm_custom(B, n, C, 1, mb, kc, stages, target, waves);
 }
 
 size_t gemm_workspace_bytes(const GemmPlan &p, int64_t B, int n) {

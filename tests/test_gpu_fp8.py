@@ -52,16 +52,21 @@ def _gpu():
 # (default above), and the persistent product kernel (MHC_GEMM_ALGO=2).  The
 # fused call is the fused kernel by default at n <= 4 (MHC_FUSED_FP8=0 gives
 # the apply + product instead, MHC_FUSED_FP8=1 the fused kernel also at n = 8
-# with MHC_FUSED_N8), all exercised here.
+# with MHC_FUSED_N8), all exercised here; the split-K product runs eight waves
+# per workgroup by default and is also run with four waves of one or two
+# 16-row blocks (split_w4mb1, split_w4mb2: MHC_GEMM_WAVES=4, MHC_GEMM_MB).
 # Every one must meet the bar at every size it supports.
-@pytest.fixture(params=["default", "small", "split", "persistent"])
+@pytest.fixture(params=["default", "small", "split", "persistent", "split_w4mb1", "split_w4mb2"])
 def path(request, tune):
     for k in ("MHC_SMALL_MAX_B", "MHC_GEMM_ALGO", "MHC_FUSED_N8"):
         tune.delenv(k, raising=False)
     if request.param == "small":
         tune.setenv("MHC_SMALL_MAX_B", str(1 << 30))
-    elif request.param == "split":
+    elif request.param.startswith("split"):
         tune.setenv("MHC_SMALL_MAX_B", "0")
+        if request.param.startswith("split_w4mb"):
+            tune.setenv("MHC_GEMM_WAVES", 4)
+            tune.setenv("MHC_GEMM_MB", int(request.param[-1]))
     elif request.param == "persistent":
         tune.setenv("MHC_SMALL_MAX_B", "0")
         tune.setenv("MHC_GEMM_ALGO", "2")

@@ -55,7 +55,15 @@ def _gpu():
 #          kernel.
 #   lds128x5, lds128x6  the LDS-staged product in 128-k chunks with a 5- or
 #          6-deep ring (MHC_GEMM_KC, MHC_GEMM_STAGES; bf16, n <= 4).
-GEMM_ALGOS = ["default", "lds", "reg", "small", "persist", "lds128x5", "lds128x6"]
+#   lds8, lds8k256  the LDS-staged product with eight waves per workgroup
+#          (128-row tiles; MHC_GEMM_WAVES=8), in 128-k chunks (four stages;
+#          three at n = 8) or 256-k chunks (two stages, n <= 4).
+#   ldsmb2  four waves with two 16-row blocks each (MHC_GEMM_MB=2; changes
+#          the shape at n = 8 only).
+#   ldsk256 four waves, 256-k chunks in two stages (MHC_GEMM_KC=256; changes
+#          the shape at n = 8 only).
+GEMM_ALGOS = ["default", "lds", "reg", "small", "persist", "lds128x5", "lds128x6", "lds8", "lds8k256",
+              "ldsmb2", "ldsk256"]
 
 
 @pytest.fixture(params=GEMM_ALGOS)
@@ -74,6 +82,14 @@ def gemm_algo(request, tune):
         if request.param.startswith("lds128x"):
             tune.setenv("MHC_GEMM_KC", 128)
             tune.setenv("MHC_GEMM_STAGES", int(request.param[-1]))
+        if request.param.startswith("lds8"):
+            tune.setenv("MHC_GEMM_WAVES", 8)
+            if request.param == "lds8k256":
+                tune.setenv("MHC_GEMM_KC", 256)
+        if request.param == "ldsmb2":
+            tune.setenv("MHC_GEMM_MB", 2)
+        if request.param == "ldsk256":
+            tune.setenv("MHC_GEMM_KC", 256)
     return request.param
 
 
