@@ -76,6 +76,11 @@ hipError_t launch_gemm_rms(const GemmPlan &p, int n, int64_t B, int64_t C,
 hipError_t launch_pack_phi(int n, int64_t K, int64_t ksteps, const void *phi, void *phip,
                            void *zero, hipStream_t st, void *clear = nullptr,
                            size_t clear_bytes = 0);
+// fp32 phi [K, N] -> per 32-k step the NB blocks of phi_hi = bf16(phi), then
+// the NB blocks of phi_lo = bf16(phi - phi_hi) (layout as above), plus the
+// zero block.
+hipError_t launch_pack_phi32(int n, int64_t K, int64_t ksteps, const void *phi, void *phip,
+                             void *zero, hipStream_t st);
 
 // Fused apply of this layer + coefficient product of the next (one pass).
 //
