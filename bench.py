@@ -46,7 +46,8 @@ Order of the run: the CPU baseline, the three separate calls, the two-call
 pipeline, then the headline loop (so the GPU runs at its working clocks when
 the timed region starts), then each headline call again between its own
 events (per-call mean, median, p10 and p90), the bandwidth probes, and the
-other sections.  "practical_ceiling" holds the rates of plain HIP read, write
+other sections.  The headline loop takes exactly W warm-up and K timed
+steps; the three-call, two-call and E4M3 loops take at least 40 and 50.  "practical_ceiling" holds the rates of plain HIP read, write
 and copy kernels (probe/bw_probe.hip) on 1 GiB buffers, and
 frac_of_practical_copy_ceiling relates a leg's bandwidth to the copy rate
 (the one-pass call reads and writes about equal bytes).
@@ -60,6 +61,8 @@ Other modes:
   --two-call-only  run only the two-call pipeline's loop (mhc_pre +
                  mhc_post_res_coeffs; for rocprofv3 counter runs of their kernels);
   --lazy-prenorm-only  time only the Lazy Pre-Norm GEMM workloads;
+  --lpn-counters  a few launches of each Lazy Pre-Norm kernel layout and of
+                 torch's A @ W^T on the square workload (counter runs);
   --shape-sweep  time the one-pass layer call (bf16 and E4M3) over a grid of
                  shapes around the headline one, one JSON line per shape
                  (steady state: ~60 ms of chained layers before ~60 ms timed).
@@ -119,6 +122,13 @@ def path_flops(B, n, C):
     """Algorithmic flops of one forward (product, sum of squares, pre, post/res)."""
     return product_flops(B, n, C) + B * (2 * n * C + 2 * (n * n + n) * C)
 
+
+# Legs other than the headline (the three-call and two-call pipelines, the
+# E4M3 pipelines) take at least this many warm-up and timed steps: the first
+# 20-40 back-to-back layers run slower while clocks and caches settle, and
+# these legs are reported as steady-state figures.
+SECONDARY_WARMUP = 40
+SECONDARY_STEPS = 50
 
 # kernels launched by each call (for the roofline record)
 KERNELS_OF_CALL = {"mhc_post_res": "post_res_kernel", "mhc_pre": "pre_kernel",
@@ -463,12 +473,13 @@ def _variants(args, mhc, torch, synth, stream, ev):
     B, n, C = (synth.CONFIGS[args.workload][k] for k in ("B", "n", "C"))
     fp8_inp = synth.make_config_fp8(args.workload, device="cuda")
     pf = Pipeline(mhc, torch, fp8_inp, fp8=True)
+    steps, warm = max(args.steps, SECONDARY_STEPS), max(args.warmup, SECONDARY_WARMUP)
     fp8_line = _summary(
-        B, n, C, 1, pf.time_loop(pf.layer, args.steps, args.warmup),
-        pf.time_loop(pf.three, args.steps, args.warmup),
+        B, n, C, 1, pf.time_loop(pf.layer, steps, warm),
+        pf.time_loop(pf.three, steps, warm),
         pf.per_call(pf.layer, ("mhc_pre_fp8", "mhc_post_res_coeffs_fp8"), args.steps),
         pf.per_call(pf.three, ("mhc_coeffs_fp8", "mhc_pre_fp8", "mhc_post_res_fp8"), args.steps),
-        ms_onepass=pf.time_loop(pf.onepass, args.steps, args.warmup))
+        ms_onepass=pf.time_loop(pf.onepass, steps, warm))
     fp8_line["onepass_route"] = ("one pass" if mhc.mhc_post_res_coeffs_pre_fp8_one_pass(B, n, C)
                                  else "mhc_post_res_coeffs_fp8 + mhc_pre_fp8")
     del pf, fp8_inp
@@ -668,8 +679,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     # Steady state: the first 20-40 back-to-back layers run slower (clocks and
-    # caches settling; 427 against 414 us per layer with 5 warm-up layers),
-    # so the default warm-up is 50 layers.  100 timed layers take ~45 ms.
+    # caches settling) unless other loops ran first, as they do here; the
+    # default warm-up is 50 layers.  100 timed layers take ~45 ms.
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
@@ -797,18 +808,20 @@ def main():
         if marks is not None:
             marks[3].record(stream)
 
-    def timed(fn):
-        for _ in range(args.warmup):
+    def timed(fn, warmup=None, steps=None):
+        warmup = args.warmup if warmup is None else warmup
+        steps = args.steps if steps is None else steps
+        for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
         e0, e1 = ev(), ev()
         w0 = time.perf_counter()
         e0.record(stream)
-        for _ in range(args.steps):
+        for _ in range(steps):
             fn()
         e1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps, time.perf_counter() - w0
+        return e0.elapsed_time(e1) / steps, time.perf_counter() - w0
 
     def per_call(fn, names):
         """Every call's ms, from an event before and after each call."""
@@ -821,6 +834,7 @@ def main():
                 for i, c in enumerate(names)}
 
     mean = lambda v: sum(v) / len(v)  # noqa: E731
+    sec_warm, sec_steps = max(args.warmup, SECONDARY_WARMUP), max(args.steps, SECONDARY_STEPS)
 
     if args.two_call_only:  # counter runs of the two-call pipeline's kernels
         timed(two_call_layer)
@@ -834,13 +848,14 @@ def main():
     ms_three = ms_two = None
     if not args.kernel_only:
         # The other bf16 pipelines first (the GPU is then at its working
-        # clocks when the headline loop starts).
+        # clocks when the headline loop starts), each with at least
+        # SECONDARY_WARMUP warm-up and SECONDARY_STEPS timed steps.
         # Three separate calls on a fixed X_t.
-        ms_three, _ = timed(three)
+        ms_three, _ = timed(three, sec_warm, sec_steps)
         three_calls = ("mhc_coeffs", "mhc_pre", "mhc_post_res")
         per_call3 = per_call(three, three_calls)
         # The two-call pipeline (mhc_pre + mhc_post_res_coeffs per layer).
-        ms_two, _ = timed(two_call_layer)
+        ms_two, _ = timed(two_call_layer, sec_warm, sec_steps)
         per_two = per_call(two_call_layer, ("mhc_pre", "mhc_post_res_coeffs"))
         mhc.mhc_pre(B, n, C, X[cur[0]], Hs[cur[0]], F_pre, stream=stream)
 
