@@ -438,6 +438,8 @@ int mhc_lazy_prenorm_gemm(int64_t M, int64_t N, int64_t K, const void *A, const 
  *                    blocks per wave, 4 or 8 waves per workgroup)
  *   MHC_GEMM_KC, MHC_GEMM_STAGES   128 with 5 or 6: the bf16 split-K product
  *                    at n <= 4 in 128-k chunks with a deeper ring
+ *   MHC_GEMM_XREG    2: the bf16 split-K product (n = 4, 8) with X and phi
+ *                    loaded through registers
  *   MHC_FUSED_N8     > 0: the fused kernel also at n = 8
  *   MHC_FUSED_FP8    0: E4M3 fused call as apply + product; > 0: fused kernel
  *   MHC_FUSED_FIXED  0 / 1: the fused kernel's fixed-slice layout off / on

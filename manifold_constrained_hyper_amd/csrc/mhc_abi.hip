@@ -357,7 +357,7 @@ constexpr TuneName kTuneNames[] = {
     {"MHC_FUSED_SPU", mhc::kTuneFusedSpu},    {"MHC_FUSED_WGS", mhc::kTuneFusedWgs},
     {"MHC_FUSED_PRE", mhc::kTuneFusedPre},    {"MHC_LPN_ALGO", mhc::kTuneLpnAlgo},
     {"MHC_GEMM_KC", mhc::kTuneGemmKc},        {"MHC_GEMM_STAGES", mhc::kTuneGemmStages},
-    {"MHC_GEMM_WAVES", mhc::kTuneGemmWaves},
+    {"MHC_GEMM_WAVES", mhc::kTuneGemmWaves},  {"MHC_GEMM_XREG", mhc::kTuneGemmXreg},
 };
 static_assert(sizeof(kTuneNames) / sizeof(kTuneNames[0]) == mhc::kTuneCount, "one name per key");
 

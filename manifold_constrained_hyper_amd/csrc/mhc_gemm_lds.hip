@@ -273,6 +273,173 @@ __global__ __launch_bounds__(W * 64) void gemm_rms_lds_kernel(const uint8_t *__r
   }
 }
 
+// The same product with X and phi through registers (bf16 X; the n = 8
+// route).  At n = 8 a 256-k chunk of phi is 40 KiB, so an LDS ring cannot
+// hold both enough X in flight and 512-byte row pieces (the 128-k chunks of
+// gemm_rms_lds_kernel read rows in 256-byte pieces, which HBM serves at about
+// 4 TB/s against 6 for 512-byte ones).  Here every wave loads its share of
+// chunk c+D (X rows row-contiguously, 1 KiB per instruction; phi blocks of
+// the packed copy) into one of D register sets while chunk c is multiplied,
+// and writes a set into single LDS slots (X XOR-swizzled as above) just
+// before the chunk's barrier.  All waits on those loads are the compiler's
+// own (register dependences), so D-1 chunks stay in flight at every point;
+// no direct-to-LDS load is used.
+template <int NS, int W, int KC>
+struct XrTile {
+  static constexpr int N = NS * NS + 2 * NS;
+  static constexpr int NP = N + 1;
+  static constexpr int NB = (N + 15) / 16;
+  static constexpr int PB = NB;
+  static constexpr int RT = 16 * W;                  // rows per workgroup (one 16-row block per wave)
+  static constexpr int T = KC / 32;                  // MFMA k-steps per chunk
+  static constexpr int PIECES = KC / 8;              // 16-byte pieces per row per chunk
+  static constexpr int RPI = 64 / PIECES;            // rows per load instruction
+  static constexpr int XI = RT * PIECES / 64;        // X load instructions per chunk
+  static constexpr int XI_W = XI / W;
+  static constexpr int PI = T * PB;                  // phi blocks (KiB) per chunk
+  static constexpr int PI_HI = (PI + W - 1) / W;     // ... loaded by a wave at most
+  static constexpr int ROW_BYTES = KC * 2;
+  static constexpr int X_BYTES = RT * ROW_BYTES;
+  static constexpr int P_BYTES = PI * 1024;
+  static constexpr int LDS_BYTES = X_BYTES + P_BYTES;
+  static_assert(PIECES >= 16 && PIECES <= 64, "swizzle needs 16..64 pieces per row");
+  static_assert(XI % W == 0, "X load instructions must split evenly over the waves");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+template <int NS, int W, int KC, int D>
+__global__ __launch_bounds__(W * 64) void gemm_rms_xreg_kernel(const uint16_t *__restrict__ X,
+                                                               const uint16_t *__restrict__ phip,
+                                                               const uint16_t *__restrict__ zero,
+                                                               float *__restrict__ ws, int B, int K,
+                                                               int kslice) {
+  using L = XrTile<NS, W, KC>;
+  __shared__ __attribute__((aligned(1024))) char lds[L::LDS_BYTES];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int m = lane & 15, g = lane >> 4;
+  const int s = blockIdx.y;
+  const int k_begin = s * kslice;
+  const int k_end = min(K, k_begin + kslice);
+  const int nchunks = (k_end - k_begin + KC - 1) / KC;
+  const int row0 = blockIdx.x * L::RT;
+
+  // This lane's X pieces: instruction j of the wave covers tile row
+  // rr(j) = rr0 + j * RPI, 16 bytes at piece `piece`; rows past B repeat row
+  // B-1 (not stored).  Addresses are formed at each use (holding them would
+  // cost 24 VGPRs).
+  const int piece = lane % L::PIECES;
+  const int rr0 = wave * L::XI_W * L::RPI + lane / L::PIECES;
+  const uint16_t *xlane = X + piece * 8;
+
+  u32x4 xr[D][L::XI_W], pr[D][L::PI_HI];
+  // Loads of chunk c (clamped to the last chunk, so every set is always
+  // filled; pieces past the slice end read the zero block).
+  auto load = [&](int set, int c) {
+    const int k0 = k_begin + min(c, nchunks - 1) * KC;
+    const int k = k0 + piece * 8;
+#pragma unroll
+    for (int j = 0; j < L::XI_W; ++j) {
+      const int row = min(row0 + rr0 + j * L::RPI, B - 1);
+      const uint16_t *src = k < k_end ? xlane + (size_t)row * K + k0 : zero;
+      xr[set][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src));
+    }
+    const int kstep0 = k0 / 32;
+#pragma unroll
+    for (int j = 0; j < L::PI_HI; ++j) {
+      const int inst = j * W + wave;
+      if (inst < L::PI)  // wave-uniform
+        pr[set][j] = load16(phip + ((size_t)(kstep0 * L::PB + inst) * 64 + lane) * 8);
+    }
+  };
+  auto stash = [&](int set) {
+#pragma unroll
+    for (int j = 0; j < L::XI_W; ++j) {
+      const int rr = rr0 + j * L::RPI;
+      *reinterpret_cast<u32x4 *>(lds + rr * L::ROW_BYTES + ((piece ^ (rr & 15)) * 16)) = xr[set][j];
+    }
+#pragma unroll
+    for (int j = 0; j < L::PI_HI; ++j) {
+      const int inst = j * W + wave;
+      if (inst < L::PI)
+        *reinterpret_cast<u32x4 *>(lds + L::X_BYTES + inst * 1024 + lane * 16) = pr[set][j];
+    }
+  };
+
+  f32x4 acc[L::NB], gram = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int nb = 0; nb < L::NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  struct Ops {
+    bf16x8 b[L::PB];
+    bf16x8 a;
+  };
+  const int rr_a = wave * 16 + m;
+  auto read_ops = [&](Ops &o, int t) {
+#pragma unroll
+    for (int j = 0; j < L::PB; ++j)
+      o.b[j] = *reinterpret_cast<const bf16x8 *>(lds + L::X_BYTES + (t * L::PB + j) * 1024 + lane * 16);
+    const int slot = (4 * t + g) ^ m;  // rr_a & 15 == m
+    o.a = *reinterpret_cast<const bf16x8 *>(lds + rr_a * L::ROW_BYTES + slot * 16);
+  };
+  auto mfma_ops = [&](const Ops &o) {
+#pragma unroll
+    for (int nb = 0; nb < L::NB; ++nb)
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.a, o.b[nb], acc[nb], 0, 0, 0);
+    gram = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.a, o.a, gram, 0, 0, 0);
+  };
+
+#pragma unroll
+  for (int d = 0; d < D; ++d) load(d, d);
+
+  for (int c = 0; c < nchunks; c += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int cc = c + d;
+      if (cc < nchunks) {  // workgroup-uniform
+        // Every wave has finished reading the slots (its MFMAs consumed the
+        // reads), so they may be overwritten.
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        stash(d);
+        wait_lgkmcnt0();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // chunk cc is in LDS
+        asm volatile("" ::: "memory");
+        load(d, cc + D);
+        Ops ops[2];
+        read_ops(ops[0], 0);
+#pragma unroll
+        for (int t = 0; t < L::T; ++t) {
+          if (t + 1 < L::T) read_ops(ops[(t + 1) & 1], t + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          mfma_ops(ops[t & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  }
+
+  // D layout of the 16x16 MFMA: lane (m, g) holds rows 4g..4g+3 of column m.
+  float *wsl = ws + (size_t)s * B * L::NP;
+  const int rbase = row0 + wave * 16;
+#pragma unroll
+  for (int nb = 0; nb < L::NB; ++nb) {
+    const int col = nb * 16 + m;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = rbase + 4 * g + v;
+      if (row < B && col < L::N) wsl[(size_t)row * L::NP + col] = acc[nb][v];
+    }
+  }
+  if (g == (m >> 2)) {  // Gram diagonal (m, m): lane (m, m/4), element m%4
+    const int row = rbase + m;
+    if (row < B) wsl[(size_t)row * L::NP + L::N] = gram[m & 3];
+  }
+}
+
 }  // namespace
 
 template <int NS, int MB, int KC, int STAGES, int XB, int P2, int W>
@@ -296,6 +463,24 @@ hipError_t launch_gemm_lds_typed(const GemmPlan &p, int64_t B, int64_t C, const 
   gemm_rms_lds_kernel<NS, MB, KC, STAGES, XB, P2, W><<<grid, W * 64, 0, st>>>(
       static_cast<const uint8_t *>(X), phip, zero, reinterpret_cast<float *>(base), (int)B, K,
       (int)p.kslice);
+  return hipGetLastError();
+}
+
+template <int NS, int W, int KC, int D>
+hipError_t launch_gemm_xreg_typed(const GemmPlan &p, int64_t B, int64_t C, const void *X, const void *phi,
+                                  void *ws_base, hipStream_t st) {
+  using L = XrTile<NS, W, KC>;
+  if (p.row_tiles * L::RT < B || p.kc != KC || p.kslice % KC != 0) return hipErrorInvalidValue;
+  const int K = (int)(NS * C);
+  char *base = static_cast<char *>(ws_base);
+  uint16_t *phip = reinterpret_cast<uint16_t *>(base + p.phip_offset);
+  uint16_t *zero = reinterpret_cast<uint16_t *>(base + p.zero_offset);
+  const int64_t ksteps = (int64_t)(p.phip_bytes / ((size_t)L::PB * 1024));
+  hipError_t e = launch_pack_phi(NS, K, ksteps, phi, phip, zero, st);
+  if (e != hipSuccess) return e;
+  const dim3 grid((uint32_t)p.row_tiles, (uint32_t)p.split);
+  gemm_rms_xreg_kernel<NS, W, KC, D><<<grid, W * 64, 0, st>>>(
+      static_cast<const uint16_t *>(X), phip, zero, reinterpret_cast<float *>(base), (int)B, K, (int)p.kslice);
   return hipGetLastError();
 }
 
@@ -333,6 +518,9 @@ template hipError_t launch_gemm_lds_typed<1, 1, 256, 3, 1, 1, 8>(const GemmPlan 
 template hipError_t launch_gemm_lds_typed<2, 1, 256, 3, 1, 1, 8>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
 template hipError_t launch_gemm_lds_typed<4, 1, 256, 3, 1, 1, 8>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
 template hipError_t launch_gemm_lds_typed<8, 1, 256, 2, 1, 1, 8>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+// X and phi through registers (bf16 X at n = 8)
+template hipError_t launch_gemm_xreg_typed<8, 8, 256, 2>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
+template hipError_t launch_gemm_xreg_typed<4, 8, 256, 2>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
 // fp32 phi (hi + lo parts)
 template hipError_t launch_gemm_lds_typed<1, 1, 128, 4, 2, 2>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);
 template hipError_t launch_gemm_lds_typed<2, 1, 128, 4, 2, 2>(const GemmPlan &, int64_t, int64_t, const void *, const void *, void *, hipStream_t);

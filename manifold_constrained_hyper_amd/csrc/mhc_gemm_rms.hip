@@ -250,6 +250,13 @@ hipError_t launch_n(const GemmPlan &p, int64_t B, int64_t C, const void *X, cons
     if constexpr (NS == 8) return launch_gemm_lds_typed<NS, 1, 128, 2, 2, 2>(p, B, C, X, phi, ws, st);
     else return launch_gemm_lds_typed<NS, 1, 128, 4, 2, 2>(p, B, C, X, phi, ws, st);
   }
+  if (p.algo == 1 && p.xreg > 0) {
+    if constexpr (NS == 8 || NS == 4) {
+      return launch_gemm_xreg_typed<NS, 8, 256, 2>(p, B, C, X, phi, ws, st);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   if (p.algo == 1 && p.xb == 1 && p.waves == 8) {
     if constexpr (NS == 8) return launch_gemm_lds_typed<NS, 1, 256, 2, 1, 1, 8>(p, B, C, X, phi, ws, st);
     else return launch_gemm_lds_typed<NS, 1, 256, 3, 1, 1, 8>(p, B, C, X, phi, ws, st);
@@ -287,6 +294,7 @@ GemmPlan plan_gemm_custom(int64_t B, int n, int64_t C, int algo, int mb, int kc,
                           int64_t target_wgs, int waves) {
   GemmPlan p;
   p.waves = algo == 1 ? waves : 4;
+  p.xreg = 0;
   const int64_t K = (int64_t)n * C;
   const int64_t N = (int64_t)n * n + 2 * n;
   const int64_t NB = (N + 15) / 16;
@@ -386,6 +394,12 @@ GemmPlan plan_gemm(int64_t B, int n, int64_t C, bool fp8_x, bool phi32) {
   } else if (n == 8 && tune(kTuneGemmKc) == 256) {
     kc = 256;  // 512-byte row pieces at n = 8, two stages
     stages = 2;
+  }
+  if (tune(kTuneGemmXreg) == 2 && (n == 8 || n == 4)) {
+    // X and phi through two register sets: eight waves, 256-k chunks, 128-row tiles
+    GemmPlan p = plan_gemm_custom(B, n, C, 1, 1, 256, 1, target, 8);
+    p.xreg = 2;
+    return p;
   }
   return plan_gemm_custom(B, n, C, 1, mb, kc, stages, target, waves);
 }

@@ -28,6 +28,7 @@ enum TuneKey : int {
   kTuneGemmKc,         // 128: the bf16 split-K product in 128-k chunks (with kTuneGemmStages)
   kTuneGemmStages,     // 5 or 6: its ring depth
   kTuneGemmWaves,      // 4 or 8: wavefronts per workgroup of the LDS-staged split-K product
+  kTuneGemmXreg,       // 2: bf16 split-K product with X and phi through two register sets (n = 4, 8)
   kTuneCount
 };
 // Current value of a key; -1 when unset.
@@ -46,6 +47,7 @@ struct GemmPlan {
   int algo;           // 0: MFMA A operands loaded from global memory; 1: X staged through LDS
   int mb;             // 16-row MFMA blocks per wavefront (rows per workgroup = 16 * mb * waves)
   int waves;          // wavefronts per workgroup: 4, or 8 (algo 1 only)
+  int xreg;           // 2: X and phi through two register sets (algo 1, bf16, n = 4 or 8, W = 8)
   int kc;             // K elements per chunk
   int stages;         // LDS ring depth (algo 1)
   int xb;             // bytes per X element: 2 (bf16) or 1 (E4M3, algo 1 only)
@@ -62,6 +64,10 @@ GemmPlan plan_gemm(int64_t B, int n, int64_t C, bool fp8_x = false, bool phi32 =
 GemmPlan plan_gemm_custom(int64_t B, int n, int64_t C, int algo, int mb, int kc, int stages,
                           int64_t target_wgs, int waves = 4);
 size_t gemm_workspace_bytes(const GemmPlan &p, int64_t B, int n);
+
+template <int NS, int W, int KC, int D>
+hipError_t launch_gemm_xreg_typed(const GemmPlan &p, int64_t B, int64_t C, const void *X, const void *phi,
+                                  void *ws_base, hipStream_t st);
 
 template <int NS, int MB, int KC, int STAGES, int XB, int P2, int W = 4>
 hipError_t launch_gemm_lds_typed(const GemmPlan &p, int64_t B, int64_t C, const void *X,

@@ -62,8 +62,10 @@ def _gpu():
 #          the shape at n = 8 only).
 #   ldsk256 four waves, 256-k chunks in two stages (MHC_GEMM_KC=256; changes
 #          the shape at n = 8 only).
+#   xreg   eight waves with X and phi through registers into single LDS slots
+#          (MHC_GEMM_XREG=2; n = 4 and 8, bf16).
 GEMM_ALGOS = ["default", "lds", "reg", "small", "persist", "lds128x5", "lds128x6", "lds8", "lds8k256",
-              "ldsmb2", "ldsk256"]
+              "ldsmb2", "ldsk256", "xreg"]
 
 
 @pytest.fixture(params=GEMM_ALGOS)
@@ -90,6 +92,9 @@ def gemm_algo(request, tune):
             tune.setenv("MHC_GEMM_MB", 2)
         if request.param == "ldsk256":
             tune.setenv("MHC_GEMM_KC", 256)
+        if request.param == "xreg":
+            tune.setenv("MHC_GEMM_ALGO", "1")
+            tune.setenv("MHC_GEMM_XREG", 2)
     return request.param
 
 
