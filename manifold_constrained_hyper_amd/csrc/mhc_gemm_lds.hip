@@ -36,15 +36,10 @@
 // waits only for its own share of chunk c (s_waitcnt vmcnt), then one barrier
 // makes the whole chunk visible and frees the slot of chunk c-1 for refill.
 //
-// Why eight waves.  A wave's direct-to-LDS loads complete at about 6-7 GB/s
-// on MI355X whether they hit HBM or L2 (measured with plain streaming probes:
-// one 4-wave workgroup per CU moves 6.4 TB/s from HBM and only 7.3 TB/s from
-// an L2-resident buffer; 8 waves per CU move 15.4 TB/s, 16 waves 23 TB/s from
-// L2), so the chip-wide staging rate grows with the number of waves issuing
-// them.  With 4 waves the X + phi bytes staged per X byte (1.5 at n = 4, 2.25
-// at n = 8 with 64-row tiles) capped the X rate near 7.3 TB/s divided by that
-// ratio.  Eight waves per workgroup (128-row tiles) double the issuing waves
-// and halve phi's share.
+// Eight waves (the E4M3 default) make 128-row tiles, so each chunk's phi
+// blocks are staged once per 128 rows instead of 64: at n = 8 the staged
+// phi bytes per X byte fall from 2.5 to 1.25 (E4M3), and two waves per SIMD
+// overlap one wave's LDS reads with the other's MFMAs.
 #include "mhc_device.h"
 #include "mhc_launch.h"
 
