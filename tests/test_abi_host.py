@@ -396,6 +396,28 @@ def test_tuning_keys_and_no_environment(tune, monkeypatch):
     assert ei.value.status == mhc.MHC_ERR_INVALID_ARG
 
 
+def test_every_documented_tuning_key(tune):
+    """Each key the header documents is accepted, and the split-K shape keys
+    reach the plan: at n = 8 (C = 4096, B = 8192) four waves of one 16-row
+    block make 64-row tiles and two K-slices; eight waves, or X through
+    registers, make 128-row tiles and four."""
+    hdr = open(os.path.join(ROOT, "include", "mhc.h")).read()
+    doc = hdr[hdr.index("Testing and tuning."):]
+    keys = sorted(set(re.findall(r"\bMHC_[A-Z0-9_]+\b", doc)) - {"MHC_H", "MHC_ERR_INVALID_ARG"})
+    assert {"MHC_GEMM_WAVES", "MHC_GEMM_XREG", "MHC_GEMM_KC", "MHC_LPN_ALGO"} <= set(keys)
+    for k in keys:
+        mhc.mhc_tuning_set(k, -1)
+    split = mhc.mhc_coeffs_split_k
+    assert split(8192, 8, 4096) == 2
+    tune.setenv("MHC_GEMM_WAVES", 8)
+    assert split(8192, 8, 4096) == 4
+    tune.delenv("MHC_GEMM_WAVES")
+    tune.setenv("MHC_GEMM_XREG", 2)
+    assert split(8192, 8, 4096) == 4
+    tune.delenv("MHC_GEMM_XREG")
+    assert split(8192, 8, 4096) == 2
+
+
 def test_binding_checks_tensor_sizes():
     """The binding rejects a tensor of the wrong element size, or smaller
     than the bytes the call touches, before anything reaches the library
