@@ -55,7 +55,7 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
 // Eight E4M3 values (two words) -> the same eight values as bf16 (exact).
 // gfx950's scaled OCP conversion with scale 1.0 widens a pair straight to
 // bf16: one instruction per pair, bitwise what widening to fp32 and packing
-// gives (checked on the box for all 65536 byte pairs, both word halves).
+// gives (checked on MI355X for all 65536 byte pairs, both word halves).
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, bool hi) {
   const bf16x2 v = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true)
                         : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false);
