@@ -162,6 +162,29 @@ def test_named(name, route):
         _check(cur, nxt, o, ref, f, pre_own, rows, f"{name} rows {rows[0]}..{rows[-1]}")
 
 
+def test_giveup_word_is_reported():
+    """mhc_post_res_coeffs_pre_check reports a set give-up word as
+    MHC_ERR_INCOMPLETE, and the next call clears the word before its kernel
+    runs.  The word (the last 16 bytes of the one-pass workspace) is set from
+    the host after a complete call: no wait is made to give up."""
+    B, n, C = 1024, 4, 1024
+    assert mhc.mhc_post_res_coeffs_pre_one_pass(B, n, C)
+    _say("post_res_coeffs_pre give-up word")
+    cur, nxt = _layers(n, C, B, "normal", 4242)
+    o = mhc.alloc_outputs(B, n, C)
+    _coeffs(cur, cur["X"], o)
+    need = mhc.mhc_post_res_coeffs_pre_workspace_size(B, n, C)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    _call(cur, nxt, o["H"], ws=ws)
+    assert mhc.mhc_post_res_coeffs_pre_check(B, n, C, ws) == mhc.MHC_OK
+    ws[need - 16:need - 12] = torch.tensor([1, 0, 0, 0], dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    assert mhc.mhc_post_res_coeffs_pre_check(B, n, C, ws) == mhc.MHC_ERR_INCOMPLETE
+    f = _call(cur, nxt, o["H"], ws=ws)
+    assert mhc.mhc_post_res_coeffs_pre_check(B, n, C, ws) == mhc.MHC_OK
+    assert not torch.isnan(f["F_pre"].float()).any()
+
+
 def test_route_query(tune):
     tune.delenv("MHC_SMALL_MAX_B", raising=False)
     tune.delenv("MHC_FUSED_PRE", raising=False)
