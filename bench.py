@@ -115,6 +115,7 @@ def path_bytes(B, n, C, eb=2):
         "mhc_post_res": post_res,
         "mhc_post_res_coeffs": post_res + K * N * 2 + coeff_out,
         "mhc_post_res_coeffs_pre": post_res + K * N * 2 + coeff_out + B * C * eb,
+        "mhc_coeffs_pre": x + K * N * 2 + coeff_out + B * C * eb,
     }
 
 
@@ -136,7 +137,9 @@ KERNELS_OF_CALL = {"mhc_post_res": "post_res_kernel", "mhc_pre": "pre_kernel",
                                  "layout) + coeff_sinkhorn_kernel",
                    "mhc_post_res_coeffs": "pack_phi_kernel + post_res_next_kernel + coeff_sinkhorn_kernel",
                    "mhc_post_res_coeffs_pre": "pack_phi_kernel + post_res_next_kernel<n, 4> (pre-mix mode) "
-                                              "+ coeff_sinkhorn_kernel (tree order)"}
+                                              "+ coeff_sinkhorn_kernel (tree order)",
+                   "mhc_coeffs_pre": "pack_phi_kernel + post_res_next_kernel<n, 6> (product-only pre-mix "
+                                     "mode) + coeff_sinkhorn_kernel (tree order)"}
 
 
 class Pipeline:
@@ -159,6 +162,8 @@ class Pipeline:
         ws_f = getattr(mhc, "mhc_post_res_coeffs" + sfx + "_workspace_size")(B, n, C)
         self.fused_pre = getattr(mhc, "mhc_post_res_coeffs_pre" + sfx)
         ws_f = max(ws_f, getattr(mhc, "mhc_post_res_coeffs_pre" + sfx + "_workspace_size")(B, n, C))
+        self.coeffs_pre = getattr(mhc, "mhc_coeffs_pre" + sfx)
+        ws_c = max(ws_c, getattr(mhc, "mhc_coeffs_pre" + sfx + "_workspace_size")(B, n, C))
         dev, st = "cuda", torch.uint8 if fp8 else torch.bfloat16
         self.X = [inp["X"], torch.empty_like(inp["X"])]
         self.H = [torch.empty(B, N, device=dev) for _ in range(2)]
@@ -197,6 +202,16 @@ class Pipeline:
         if marks is not None:
             marks[1].record(s)
         self.cur = 1 - a
+
+    def first(self, marks=None):
+        """The first layer's call (mhc_coeffs_pre) on the fixed X_t."""
+        B, n, C, s, inp = self.B, self.n, self.C, self.stream, self.inp
+        if marks is not None:
+            marks[0].record(s)
+        self.coeffs_pre(B, n, C, inp["X"], inp["phi"], *self.ab, self.logits, self.r, self.H[0],
+                        self.F_pre, self.ws_c, stream=s)
+        if marks is not None:
+            marks[1].record(s)
 
     def three(self, marks=None):
         B, n, C, s, inp = self.B, self.n, self.C, self.stream, self.inp
@@ -294,11 +309,17 @@ class Pipeline:
         return out
 
 
-def _summary(B, n, C, eb, ms_layer, ms_three, per_pipe=None, per_three=None, ms_onepass=None):
+def _summary(B, n, C, eb, ms_layer, ms_three, per_pipe=None, per_three=None, ms_onepass=None,
+             ms_first=None):
     b = path_bytes(B, n, C, eb)
     pipe = b["mhc_pre"] + b["mhc_post_res_coeffs"]
     three = b["mhc_coeffs"] + b["mhc_pre"] + b["mhc_post_res"]
     out = {}
+    if ms_first is not None:
+        first = b["mhc_coeffs_pre"]
+        out.update({"first_layer_us": round(ms_first * 1e3, 2),
+                    "first_layer_hbm_gbps": round(first / (ms_first * 1e-3) / 1e9, 1),
+                    "first_layer_algorithmic_bytes": first})
     if ms_onepass is not None:
         one = b["mhc_post_res_coeffs_pre"]
         out.update({"onepass_us_per_layer": round(ms_onepass * 1e3, 2),
@@ -479,7 +500,9 @@ def _variants(args, mhc, torch, synth, stream, ev):
         pf.time_loop(pf.three, steps, warm),
         pf.per_call(pf.layer, ("mhc_pre_fp8", "mhc_post_res_coeffs_fp8"), args.steps),
         pf.per_call(pf.three, ("mhc_coeffs_fp8", "mhc_pre_fp8", "mhc_post_res_fp8"), args.steps),
-        ms_onepass=pf.time_loop(pf.onepass, steps, warm))
+        ms_onepass=pf.time_loop(pf.onepass, steps, warm), ms_first=pf.time_loop(pf.first, steps, warm))
+    fp8_line["first_layer_route"] = ("one pass" if mhc.mhc_coeffs_pre_fp8_one_pass(B, n, C)
+                                     else "mhc_coeffs_fp8 + mhc_pre_fp8")
     fp8_line["onepass_route"] = ("one pass" if mhc.mhc_post_res_coeffs_pre_fp8_one_pass(B, n, C)
                                  else "mhc_post_res_coeffs_fp8 + mhc_pre_fp8")
     del pf, fp8_inp
@@ -499,7 +522,8 @@ def _variants(args, mhc, torch, synth, stream, ev):
             pw = Pipeline(mhc, torch, winp, fp8=fp8)
             res[dname] = _summary(wcfg["B"], wcfg["n"], wcfg["C"], 1 if fp8 else 2,
                                   pw.time_loop(pw.layer, wsteps, 10), pw.time_loop(pw.three, wsteps, 10),
-                                  ms_onepass=pw.time_loop(pw.onepass, wsteps, 10))
+                                  ms_onepass=pw.time_loop(pw.onepass, wsteps, 10),
+                                  ms_first=pw.time_loop(pw.first, wsteps, 10))
             if wname in ("tiny", "decode", "prefill"):  # launch-bound sizes: the same layers replayed from a graph
                 res[dname]["graph_onepass_us_per_layer"] = round(pw.time_graph(pw.onepass) * 1e3, 2)
             sfx = "_fp8" if fp8 else ""
@@ -808,6 +832,16 @@ def main():
         if marks is not None:
             marks[3].record(stream)
 
+    ws_cp = torch.empty(max(mhc.mhc_coeffs_pre_workspace_size(B, n, C), 16), dtype=torch.uint8, device="cuda")
+
+    def first(marks=None):
+        if marks is not None:
+            marks[0].record(stream)
+        mhc.mhc_coeffs_pre(B, n, C, X3, inp["phi"], *ab, out["logits"], out["r"], out["H"], out["F_pre"],
+                           ws_cp, stream=stream)
+        if marks is not None:
+            marks[1].record(stream)
+
     def timed(fn, warmup=None, steps=None):
         warmup = args.warmup if warmup is None else warmup
         steps = args.steps if steps is None else steps
@@ -858,6 +892,10 @@ def main():
         ms_two, _ = timed(two_call_layer, sec_warm, sec_steps)
         per_two = per_call(two_call_layer, ("mhc_pre", "mhc_post_res_coeffs"))
         mhc.mhc_pre(B, n, C, X[cur[0]], Hs[cur[0]], F_pre, stream=stream)
+        # The first layer's call on the fixed X_t, against mhc_coeffs +
+        # mhc_pre (the three calls' first two).
+        ms_first, _ = timed(first, sec_warm, sec_steps)
+        per_first = per_call(first, ("mhc_coeffs_pre",))
 
     # Timed region (the headline number): W warm-up layers, then K
     # back-to-back layers bracketed by two events and a device
@@ -873,7 +911,7 @@ def main():
     per_call_all = per_call(layer, pipe_calls)
     per_call_ms = {c: mean(v) for c, v in per_call_all.items()}
 
-    del X, Hs, out, X3
+    del X, Hs, out, X3, ws_cp
     torch.cuda.empty_cache()
     probe = bandwidth_probe(torch)
 
@@ -935,6 +973,14 @@ def main():
         "three_call": dict(leg(ms_three, three_bytes, per_call3), split_k=mhc.mhc_coeffs_split_k(B, n, C),
                            frac_of_practical_copy_ceiling=round(
                                three_bytes / (ms_three * 1e-3) / 1e9 / probe["copy_gbps"], 4)),
+        "first_layer": {
+            "call": "mhc_coeffs_pre", "kernel": KERNELS_OF_CALL["mhc_coeffs_pre"],
+            "route": "one pass" if mhc.mhc_coeffs_pre_one_pass(B, n, C) else "mhc_coeffs + mhc_pre",
+            **leg(ms_first, bytes_call["mhc_coeffs_pre"], per_first),
+            "vs_mhc_coeffs_plus_mhc_pre_us": round(
+                (mean(per_call3["mhc_coeffs"]) + mean(per_call3["mhc_pre"])) * 1e3, 2),
+            "frac_of_practical_copy_ceiling": round(
+                bytes_call["mhc_coeffs_pre"] / (ms_first * 1e-3) / 1e9 / probe["copy_gbps"], 4)},
         "practical_ceiling": probe,
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
         "roofline": roofline,

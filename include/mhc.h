@@ -47,7 +47,7 @@
  *    - workspace smaller than mhc_coeffs_workspace_size()    -> MHC_ERR_WORKSPACE
  *    - the HIP runtime reports a launch error                -> MHC_ERR_HIP
  *  B == 0 is valid and launches nothing.  MHC_ERR_INCOMPLETE is returned only
- *  by mhc_post_res_coeffs_pre_check (below).  Faults during asynchronous
+ *  by mhc_post_res_coeffs_pre_check and mhc_coeffs_pre_check (below).  Faults during asynchronous
  *  execution surface at the caller's next synchronisation, as in HIP.
  */
 #ifndef MHC_H
@@ -185,9 +185,10 @@ int mhc_post_res_coeffs(int64_t B, int32_t n, int64_t C,
  *   F_pre_next   out bf16 [B, C] = exactly what mhc_pre(X_next, H_next) writes
  *                (bitwise).
  *
- * A model runs mhc_coeffs and mhc_pre once for its first layer and then, per
- * layer, its layer F and this call: the residual stream is read once and
- * written once per layer (X_t and F_out in, X_next and F_pre_next out).
+ * A model runs mhc_coeffs_pre (or mhc_coeffs and mhc_pre) once for its first
+ * layer and then, per layer, its layer F and this call: the residual stream
+ * is read once and written once per layer (X_t and F_out in, X_next and
+ * F_pre_next out).
  *
  * Where the shape allows (n <= 4, B above 256, C % 32 == 0 and at most 16
  * 512-channel steps per row, i.e. C <= 8192) this runs as one persistent
@@ -266,6 +267,50 @@ int mhc_post_res_coeffs_pre_noalloc(int64_t B, int32_t n, int64_t C,
                                     const float *b_pre, const float *b_post, const float *b_res,
                                     float *logits_next, float *r_next, float *H_next,
                                     void *F_pre_next, void *stream);
+
+/* Steps (1)-(3) and step (4a) of one layer in one pass over X_t: the first
+ * layer's counterpart of mhc_post_res_coeffs_pre, for a stream that no apply
+ * produced (the layer-0 X_t built from the embeddings).
+ *
+ * [mHC-cutile] section 3.1 forms the product and the sum of squares in one
+ * pass over X_t, and section 2.5 (first step) needs F_pre = sum_i H_pre[i]
+ * X_t[i] once H_pre (sections 2.1-2.4) is known.  This call returns
+ *
+ *   logits, r, H = what mhc_coeffs(X_t, phi, alpha_*, b_*) computes, up to
+ *                  fp32 summation order (deterministic, no atomics);
+ *   F_pre    out bf16 [B, C] = exactly what mhc_pre(X_t, H) writes with the
+ *                  H this call returns (bitwise).
+ *
+ * Arguments as mhc_coeffs plus F_pre (16-byte aligned, must not overlap any
+ * other argument).  The workspace must hold mhc_coeffs_pre_workspace_size(B,
+ * n, C) bytes; its contents on entry do not matter.  Where
+ * mhc_post_res_coeffs_pre takes its one pass (and C % 32 == 0),
+ * mhc_coeffs_pre_one_pass() returns 1 and the call is the same persistent
+ * pass without the apply: X_t is read once, nothing is written back to it,
+ * and the residency rules, the give-up behaviour (F_pre NaN in the rows a
+ * wait gave up on; logits, r and H still complete) and the give-up word
+ * (read with mhc_coeffs_pre_check) are those of mhc_post_res_coeffs_pre.
+ * Other shapes run mhc_coeffs followed by mhc_pre, with the same results. */
+size_t mhc_coeffs_pre_workspace_size(int64_t B, int32_t n, int64_t C);
+
+int mhc_coeffs_pre(int64_t B, int32_t n, int64_t C,
+                   const void *X_t, const void *phi,
+                   float alpha_pre, float alpha_post, float alpha_res,
+                   const float *b_pre, const float *b_post, const float *b_res,
+                   float *logits, float *r, float *H, void *F_pre,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* 1 if mhc_coeffs_pre runs this shape as one pass, 0 otherwise (as
+ * mhc_post_res_coeffs_pre_one_pass, which it equals for C % 32 == 0). */
+int32_t mhc_coeffs_pre_one_pass(int64_t B, int32_t n, int64_t C);
+
+/* Whether the last mhc_coeffs_pre (fp8 == 0) or mhc_coeffs_pre_fp8 (fp8 != 0)
+ * call of shape (B, n, C) that used `workspace` completed every wait of its
+ * one-pass route; as mhc_post_res_coeffs_pre_check (synchronises `stream`,
+ * reads one word; workspace must not be NULL).  MHC_OK when no wait gave up
+ * (always for shapes that run the two calls), MHC_ERR_INCOMPLETE when one did. */
+int mhc_coeffs_pre_check(int64_t B, int32_t n, int64_t C, int32_t fp8,
+                         const void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * FP8 residual-stream variant.
@@ -355,6 +400,28 @@ int mhc_post_res_coeffs_pre_fp8(int64_t B, int32_t n, int64_t C,
 
 /* 1 if mhc_post_res_coeffs_pre_fp8 runs this shape as one pass, else 0. */
 int32_t mhc_post_res_coeffs_pre_fp8_one_pass(int64_t B, int32_t n, int64_t C);
+
+/* mhc_coeffs_pre on an E4M3 X_t: what mhc_coeffs_fp8 returns, plus
+ *
+ *   F_pre    out E4M3 [B, C] = exactly what mhc_pre_fp8(X_t, H) writes with
+ *            the H this call returns (bitwise).
+ *
+ * One pass where mhc_post_res_coeffs_pre_fp8 takes one (and C % 32 == 0),
+ * else mhc_coeffs_fp8 followed by mhc_pre_fp8; give-up behaviour as
+ * mhc_post_res_coeffs_pre_fp8 (mhc_coeffs_pre_check with fp8 = 1).  Requires
+ * C % 16 == 0; the workspace must hold mhc_coeffs_pre_fp8_workspace_size
+ * bytes. */
+size_t mhc_coeffs_pre_fp8_workspace_size(int64_t B, int32_t n, int64_t C);
+
+int mhc_coeffs_pre_fp8(int64_t B, int32_t n, int64_t C,
+                       const void *X_t, const void *phi,
+                       float alpha_pre, float alpha_post, float alpha_res,
+                       const float *b_pre, const float *b_post, const float *b_res,
+                       float *logits, float *r, float *H, void *F_pre,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* 1 if mhc_coeffs_pre_fp8 runs this shape as one pass, else 0. */
+int32_t mhc_coeffs_pre_fp8_one_pass(int64_t B, int32_t n, int64_t C);
 
 /* ------------------------------------------------------------------------
  * fp32 phi variant.

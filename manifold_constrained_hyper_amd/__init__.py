@@ -14,4 +14,6 @@ from .binding import (  # noqa: F401
     mhc_post_res_coeffs_phi32, mhc_post_res_coeffs_pre_workspace_size, mhc_post_res_coeffs_pre,
     mhc_post_res_coeffs_pre_one_pass, mhc_post_res_coeffs_pre_fp8_workspace_size,
     mhc_post_res_coeffs_pre_fp8, mhc_post_res_coeffs_pre_fp8_one_pass,
+    mhc_coeffs_pre_workspace_size, mhc_coeffs_pre, mhc_coeffs_pre_one_pass, mhc_coeffs_pre_check,
+    mhc_coeffs_pre_fp8_workspace_size, mhc_coeffs_pre_fp8, mhc_coeffs_pre_fp8_one_pass,
 )

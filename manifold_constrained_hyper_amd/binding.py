@@ -31,7 +31,10 @@ EXPORTED = ("mhc_status_string", "mhc_coeffs_workspace_size", "mhc_coeffs_split_
             "mhc_post_res_coeffs_pre", "mhc_post_res_coeffs_pre_one_pass",
             "mhc_post_res_coeffs_pre_fp8_workspace_size", "mhc_post_res_coeffs_pre_fp8",
             "mhc_post_res_coeffs_pre_fp8_one_pass", "mhc_post_res_coeffs_pre_check",
-            "mhc_tuning_set", "mhc_tuning_reset", "mhc_post_res_coeffs_pre_noalloc")
+            "mhc_tuning_set", "mhc_tuning_reset", "mhc_post_res_coeffs_pre_noalloc",
+            "mhc_coeffs_pre_workspace_size", "mhc_coeffs_pre", "mhc_coeffs_pre_one_pass",
+            "mhc_coeffs_pre_check", "mhc_coeffs_pre_fp8_workspace_size", "mhc_coeffs_pre_fp8",
+            "mhc_coeffs_pre_fp8_one_pass")
 
 MHC_NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -112,6 +115,16 @@ def load():
     lib.mhc_post_res_coeffs_pre_noalloc.argtypes = [i64, i32, i64, vp, vp, vp, vp, vp, f32, f32, f32,
                                                     vp, vp, vp, vp, vp, vp, vp, vp]
     lib.mhc_post_res_coeffs_pre_noalloc.restype = ctypes.c_int
+    for suffix in ("", "_fp8"):
+        getattr(lib, f"mhc_coeffs_pre{suffix}_workspace_size").argtypes = [i64, i32, i64]
+        getattr(lib, f"mhc_coeffs_pre{suffix}_workspace_size").restype = sz
+        getattr(lib, f"mhc_coeffs_pre{suffix}").argtypes = [i64, i32, i64, vp, vp, f32, f32, f32, vp, vp,
+                                                           vp, vp, vp, vp, vp, vp, sz, vp]
+        getattr(lib, f"mhc_coeffs_pre{suffix}").restype = ctypes.c_int
+        getattr(lib, f"mhc_coeffs_pre{suffix}_one_pass").argtypes = [i64, i32, i64]
+        getattr(lib, f"mhc_coeffs_pre{suffix}_one_pass").restype = i32
+    lib.mhc_coeffs_pre_check.argtypes = [i64, i32, i64, i32, vp, sz, vp]
+    lib.mhc_coeffs_pre_check.restype = ctypes.c_int
     lib.mhc_tuning_reset.argtypes = []
     lib.mhc_tuning_reset.restype = None
     _lib = lib
@@ -224,6 +237,61 @@ def mhc_coeffs(B, n, C, X_t, phi, alpha_pre, alpha_post, alpha_res, b_pre, b_pos
     """Steps (1)-(3): logits, r and H from X_t and phi (see include/mhc.h)."""
     return _coeffs(load().mhc_coeffs, "mhc_coeffs", 2, 2, B, n, C, X_t, phi, alpha_pre, alpha_post,
                    alpha_res, b_pre, b_post, b_res, logits, r, H, workspace, workspace_bytes, stream, check)
+
+
+def _coeffs_pre(fn, name, eb, B, n, C, X_t, phi, alpha_pre, alpha_post, alpha_res, b_pre, b_post,
+                b_res, logits, r, H, F_pre, workspace, workspace_bytes, stream, check):
+    z = _Sizes(B, n, C, eb, 2)
+    pp, bp, bq, br, lg, rr, hh = _coeff_args(z, phi, b_pre, b_post, b_res, logits, r, H)
+    wb = _ws_bytes(workspace, workspace_bytes)
+    st = fn(int(B), int(n), int(C), _ptr(X_t, z.x, eb, "X_t"), pp, float(alpha_pre), float(alpha_post),
+            float(alpha_res), bp, bq, br, lg, rr, hh, _ptr(F_pre, z.f, eb, "F_pre"),
+            _ptr(workspace, wb, None, "workspace"), wb, _stream(stream))
+    if check:
+        _check(st, name)
+    return st
+
+
+def mhc_coeffs_pre_workspace_size(B, n, C):
+    return int(load().mhc_coeffs_pre_workspace_size(int(B), int(n), int(C)))
+
+
+def mhc_coeffs_pre_one_pass(B, n, C):
+    return bool(load().mhc_coeffs_pre_one_pass(int(B), int(n), int(C)))
+
+
+def mhc_coeffs_pre(B, n, C, X_t, phi, alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res,
+                   logits, r, H, F_pre, workspace, workspace_bytes=None, stream=None, check=True):
+    """Steps (1)-(3) and (4a) of one layer: logits, r, H and F_pre from X_t, in
+    one pass where the shape allows (see include/mhc.h)."""
+    return _coeffs_pre(load().mhc_coeffs_pre, "mhc_coeffs_pre", 2, B, n, C, X_t, phi, alpha_pre,
+                       alpha_post, alpha_res, b_pre, b_post, b_res, logits, r, H, F_pre, workspace,
+                       workspace_bytes, stream, check)
+
+
+def mhc_coeffs_pre_check(B, n, C, workspace, fp8=False, workspace_bytes=None, stream=None):
+    """Status of the last one-pass mhc_coeffs_pre(_fp8) call of shape (B, n, C)
+    on `workspace`: MHC_OK, or MHC_ERR_INCOMPLETE if one of its waits gave up
+    (synchronises the stream).  Returns the status, never raises on it."""
+    wb = _ws_bytes(workspace, workspace_bytes)
+    return int(load().mhc_coeffs_pre_check(int(B), int(n), int(C), 1 if fp8 else 0,
+                                            _ptr(workspace, wb, None, "workspace"), wb, _stream(stream)))
+
+
+def mhc_coeffs_pre_fp8_workspace_size(B, n, C):
+    return int(load().mhc_coeffs_pre_fp8_workspace_size(int(B), int(n), int(C)))
+
+
+def mhc_coeffs_pre_fp8_one_pass(B, n, C):
+    return bool(load().mhc_coeffs_pre_fp8_one_pass(int(B), int(n), int(C)))
+
+
+def mhc_coeffs_pre_fp8(B, n, C, X_t, phi, alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res,
+                       logits, r, H, F_pre, workspace, workspace_bytes=None, stream=None, check=True):
+    """mhc_coeffs_pre on an E4M3 X_t (see include/mhc.h)."""
+    return _coeffs_pre(load().mhc_coeffs_pre_fp8, "mhc_coeffs_pre_fp8", 1, B, n, C, X_t, phi,
+                       alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res, logits, r, H, F_pre,
+                       workspace, workspace_bytes, stream, check)
 
 
 def _pre(fn, name, eb, B, n, C, X_t, H, F_pre, stream, check):

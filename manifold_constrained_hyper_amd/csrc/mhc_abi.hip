@@ -288,7 +288,8 @@ int post_res_coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t
     // grid from what the device and the stream's CUs hold, and run the two
     // calls instead when not even one row tile's slices fit together.
     grid = mhc::pre_mode_grid(plan.row_tiles * plan.split, plan.split,
-                              mhc::pre_mode_resident(n, e.fp8, s), mhc::tune(mhc::kTuneFusedWgs));
+                              mhc::pre_mode_resident(n, e.fp8 ? mhc::kFusedApplyPreFp8 : mhc::kFusedApplyPreBf16, s),
+                              mhc::tune(mhc::kTuneFusedWgs));
     if (grid == 0) {
       one_pass = false;
       // The give-up word then reports no give-up.
@@ -337,6 +338,94 @@ int post_res_coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t
   return from_hip(mhc::launch_coeff_sinkhorn(n, B, C, plan.split, static_cast<const float *>(workspace),
                                              alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res,
                                              logits_next, r_next, H_next, s));
+}
+
+// mhc_coeffs_pre(_fp8): the product-only pre-mix mode of the fused kernel
+// (X_t read once for the logits, the sums of squares and F_pre) wherever
+// mhc_post_res_coeffs_pre(_fp8) takes its one pass; otherwise mhc_coeffs(_fp8)
+// followed by mhc_pre(_fp8).  The workspace of a one-pass shape holds the
+// pre-mix layout (give-up word included) and also mhc_coeffs's workspace,
+// for the two calls that run when the grid cannot be resident.
+bool coeffs_pre_fused(int64_t B, int32_t n, int64_t C, Elt e) { return C % 32 == 0 && pre_fused(B, n, C, e); }
+
+size_t coeffs_pre_ws_bytes(int64_t B, int32_t n, int64_t C, Elt e) {
+  if (check_shape_elt(B, n, C, e) != MHC_OK || B == 0) return 0;
+  const size_t two = coeffs_ws_bytes(B, n, C, e);
+  if (!coeffs_pre_fused(B, n, C, e)) return two;
+  const size_t one = mhc::plan_post_res_next(B, n, C, true).total_bytes;
+  return one > two ? one : two;
+}
+
+int coeffs_pre_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t, const void *phi,
+                    float alpha_pre, float alpha_post, float alpha_res, const float *b_pre,
+                    const float *b_post, const float *b_res, float *logits, float *r, float *H,
+                    void *F_pre, void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_shape_elt(B, n, C, e);
+  if (st != MHC_OK) return st;
+  if (B == 0) return MHC_OK;
+  if (!X_t || !phi || !b_pre || !b_post || !b_res || !logits || !r || !H || !F_pre || !workspace)
+    return MHC_ERR_INVALID_ARG;
+  if (!aligned(X_t, 16) || !aligned(phi, 16) || !aligned(workspace, 16) || !aligned(F_pre, 16) ||
+      !aligned(b_pre, 4) || !aligned(b_post, 4) || !aligned(b_res, 4) || !aligned(logits, 4) ||
+      !aligned(r, 4) || !aligned(H, 4))
+    return MHC_ERR_UNSUPPORTED;
+  bool one_pass = coeffs_pre_fused(B, n, C, e);
+  const size_t ws_need = coeffs_pre_ws_bytes(B, n, C, e);
+  const int64_t N = ncoef(n), K = (int64_t)n * C;
+  const Span in[] = {span(X_t, (size_t)B * K * e.bytes()), span(phi, (size_t)K * N * e.phi_bytes()),
+                     span(b_pre, (size_t)n * 4), span(b_post, (size_t)n * 4),
+                     span(b_res, (size_t)n * n * 4)};
+  const Span out[] = {span(logits, (size_t)B * N * 4), span(r, (size_t)B * 4),
+                      span(H, (size_t)B * N * 4), span(workspace, ws_need),
+                      span(F_pre, (size_t)B * C * e.bytes())};
+  for (const Span &o : out)
+    for (const Span &i : in)
+      if (overlaps(o, i)) return MHC_ERR_INVALID_ARG;
+  for (int a = 0; a < 5; ++a)
+    for (int b = a + 1; b < 5; ++b)
+      if (overlaps(out[a], out[b])) return MHC_ERR_INVALID_ARG;
+  if (workspace_bytes < ws_need) return MHC_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int mode = e.fp8 ? mhc::kFusedCoeffsPreFp8 : mhc::kFusedCoeffsPreBf16;
+  if (one_pass) {
+    // As in mhc_post_res_coeffs_pre: a grid that can be resident at once,
+    // else the two calls (the give-up word then reports no give-up).
+    const mhc::FusedPlan plan = mhc::plan_post_res_next(B, n, C, true, e.fp8);
+    const int64_t grid = mhc::pre_mode_grid(plan.row_tiles * plan.split, plan.split,
+                                            mhc::pre_mode_resident(n, mode, s),
+                                            mhc::tune(mhc::kTuneFusedWgs));
+    if (grid > 0) {
+      const mhc::PreOut po{F_pre, b_pre, alpha_pre, grid};
+      st = from_hip(mhc::launch_post_res_next(plan, n, mode, B, C, X_t, nullptr, nullptr, nullptr, phi,
+                                              workspace, s, &po));
+      if (st != MHC_OK) return st;
+      return from_hip(mhc::launch_coeff_sinkhorn(n, B, C, plan.split, static_cast<const float *>(workspace),
+                                                 alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res,
+                                                 logits, r, H, s, /*tree=*/true));
+    }
+    one_pass = false;
+    st = from_hip(mhc::launch_zero(static_cast<char *>(workspace) + plan.flag_offset, 16, s));
+    if (st != MHC_OK) return st;
+  }
+  st = coeffs_impl(e, B, n, C, X_t, phi, alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res,
+                   logits, r, H, workspace, workspace_bytes, stream);
+  if (st != MHC_OK) return st;
+  return from_hip(e.fp8 ? mhc::launch_pre_fp8(n, B, C, X_t, H, F_pre, s)
+                        : mhc::launch_pre(n, B, C, X_t, H, F_pre, s));
+}
+
+// The give-up word of a one-pass workspace (pre-mix layout): MHC_OK while
+// zero, MHC_ERR_INCOMPLETE once a wait gave up.  Synchronises the stream.
+int read_giveup(int64_t B, int32_t n, int64_t C, Elt e, const void *workspace, void *stream) {
+  const mhc::FusedPlan plan = mhc::plan_post_res_next(B, n, C, true, e.fp8);
+  uint32_t word = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(&word, static_cast<const char *>(workspace) + plan.flag_offset, sizeof(word),
+                     hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return MHC_ERR_HIP;
+  return word == 0 ? MHC_OK : MHC_ERR_INCOMPLETE;
 }
 
 constexpr Elt kBf16{false, false}, kFp8{true, false}, kPhi32{false, true};
@@ -472,6 +561,23 @@ int mhc_post_res(int64_t B, int32_t n, int64_t C, const void *X_t, const void *F
   return post_res_impl(kBf16, B, n, C, X_t, F_out, H, X_next, stream);
 }
 
+size_t mhc_coeffs_pre_workspace_size(int64_t B, int32_t n, int64_t C) {
+  return coeffs_pre_ws_bytes(B, n, C, kBf16);
+}
+
+int mhc_coeffs_pre(int64_t B, int32_t n, int64_t C, const void *X_t, const void *phi,
+                   float alpha_pre, float alpha_post, float alpha_res, const float *b_pre,
+                   const float *b_post, const float *b_res, float *logits, float *r, float *H,
+                   void *F_pre, void *workspace, size_t workspace_bytes, void *stream) {
+  return coeffs_pre_impl(kBf16, B, n, C, X_t, phi, alpha_pre, alpha_post, alpha_res, b_pre, b_post,
+                         b_res, logits, r, H, F_pre, workspace, workspace_bytes, stream);
+}
+
+int32_t mhc_coeffs_pre_one_pass(int64_t B, int32_t n, int64_t C) {
+  if (check_shape(B, n, C) != MHC_OK || B == 0) return 0;
+  return coeffs_pre_fused(B, n, C, kBf16) ? 1 : 0;
+}
+
 size_t mhc_post_res_coeffs_workspace_size(int64_t B, int32_t n, int64_t C) {
   return post_res_coeffs_ws_bytes(B, n, C, kBf16);
 }
@@ -518,14 +624,18 @@ int mhc_post_res_coeffs_pre_check(int64_t B, int32_t n, int64_t C, int32_t fp8,
     workspace_bytes = kNoAllocScratchBytes;
   }
   if (workspace_bytes < post_res_coeffs_pre_ws_bytes(B, n, C, e)) return MHC_ERR_WORKSPACE;
-  const mhc::FusedPlan plan = mhc::plan_post_res_next(B, n, C, true, e.fp8);
-  uint32_t word = 0;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (hipMemcpyAsync(&word, static_cast<const char *>(workspace) + plan.flag_offset, sizeof(word),
-                     hipMemcpyDeviceToHost, s) != hipSuccess ||
-      hipStreamSynchronize(s) != hipSuccess)
-    return MHC_ERR_HIP;
-  return word == 0 ? MHC_OK : MHC_ERR_INCOMPLETE;
+  return read_giveup(B, n, C, e, workspace, stream);
+}
+
+int mhc_coeffs_pre_check(int64_t B, int32_t n, int64_t C, int32_t fp8, const void *workspace,
+                         size_t workspace_bytes, void *stream) {
+  const Elt e = fp8 ? kFp8 : kBf16;
+  const int st = check_shape_elt(B, n, C, e);
+  if (st != MHC_OK) return st;
+  if (B == 0 || !coeffs_pre_fused(B, n, C, e)) return MHC_OK;  // the two calls never give up
+  if (!workspace) return MHC_ERR_INVALID_ARG;
+  if (workspace_bytes < coeffs_pre_ws_bytes(B, n, C, e)) return MHC_ERR_WORKSPACE;
+  return read_giveup(B, n, C, e, workspace, stream);
 }
 
 int mhc_post_res_coeffs_pre_noalloc(int64_t B, int32_t n, int64_t C, const void *X_t,
@@ -573,6 +683,23 @@ int mhc_pre_fp8(int64_t B, int32_t n, int64_t C, const void *X_t, const float *H
 int mhc_post_res_fp8(int64_t B, int32_t n, int64_t C, const void *X_t, const void *F_out,
                      const float *H, void *X_next, void *stream) {
   return post_res_impl(kFp8, B, n, C, X_t, F_out, H, X_next, stream);
+}
+
+size_t mhc_coeffs_pre_fp8_workspace_size(int64_t B, int32_t n, int64_t C) {
+  return coeffs_pre_ws_bytes(B, n, C, kFp8);
+}
+
+int mhc_coeffs_pre_fp8(int64_t B, int32_t n, int64_t C, const void *X_t, const void *phi,
+                       float alpha_pre, float alpha_post, float alpha_res, const float *b_pre,
+                       const float *b_post, const float *b_res, float *logits, float *r, float *H,
+                       void *F_pre, void *workspace, size_t workspace_bytes, void *stream) {
+  return coeffs_pre_impl(kFp8, B, n, C, X_t, phi, alpha_pre, alpha_post, alpha_res, b_pre, b_post,
+                         b_res, logits, r, H, F_pre, workspace, workspace_bytes, stream);
+}
+
+int32_t mhc_coeffs_pre_fp8_one_pass(int64_t B, int32_t n, int64_t C) {
+  if (check_shape_elt(B, n, C, kFp8) != MHC_OK || B == 0) return 0;
+  return coeffs_pre_fused(B, n, C, kFp8) ? 1 : 0;
 }
 
 size_t mhc_post_res_coeffs_fp8_workspace_size(int64_t B, int32_t n, int64_t C) {

@@ -125,8 +125,13 @@ enum FusedMode : int {
   kFusedCoeffsBf16 = 3,    // X . phi only, X in bf16
   kFusedApplyPreBf16 = 4,  // kFusedApplyBf16, plus the next layer's F_pre (n <= 4)
   kFusedApplyPreFp8 = 5,   // kFusedApplyFp8, plus the next layer's F_pre in E4M3 (n <= 4)
+  kFusedCoeffsPreBf16 = 6, // kFusedCoeffsBf16, plus this layer's F_pre (n <= 4)
+  kFusedCoeffsPreFp8 = 7,  // kFusedCoeffsFp8, plus this layer's F_pre in E4M3 (n <= 4)
 };
-constexpr bool is_pre_mode(int mode) { return mode == kFusedApplyPreBf16 || mode == kFusedApplyPreFp8; }
+constexpr bool is_pre_mode(int mode) {
+  return mode == kFusedApplyPreBf16 || mode == kFusedApplyPreFp8 || mode == kFusedCoeffsPreBf16 ||
+         mode == kFusedCoeffsPreFp8;
+}
 // Kernel-side arguments of the pre-mix mode.  Its stores of partials,
 // records and F_pre, and its record loads, go through buffer resources, so a
 // store without a target is given an offset past the buffer and dropped by
@@ -146,11 +151,11 @@ struct PreArgs {
 // (a multiple of S workgroups) that fits the device, and partials and
 // records addressable by 32-bit buffer offsets.
 bool pre_mode_fits(int64_t B, int n, int64_t C);
-// Workgroups of the pre-mix kernel (n, E4M3 or bf16) that can be resident at
+// Workgroups of the pre-mix kernel (n, mode) that can be resident at
 // once for launches on `st`: the per-CU occupancy the runtime reports for the
 // kernel times the compute units the stream may use (its CU mask).  Cached
 // per device and kernel, except the mask, which is read per call.
-int64_t pre_mode_resident(int n, bool fp8, hipStream_t st);
+int64_t pre_mode_resident(int n, int mode, hipStream_t st);
 // Grid of the pre-mix mode: whole row tiles per round (a multiple of
 // `split`), at most `resident` workgroups (and at most `wgs_cap` when that is
 // positive), no more than the `units` there are; 0 when not even one row

@@ -87,6 +87,13 @@
 // up after about a second, writes NaN to its F_pre vector and sets the
 // give-up word of the workspace, which the caller can read back
 // (mhc_post_res_coeffs_pre_check).
+//
+// The first layer has no apply: its X_t is the stream built from the
+// embeddings.  The product-only pre-mix modes (kFusedCoeffsPreBf16 /
+// kFusedCoeffsPreFp8, mhc_coeffs_pre / mhc_coeffs_pre_fp8) run the same pass
+// on X_t itself: X_t goes into the tiles as read, nothing is written back,
+// and F_pre = sum_i H_pre[i] X_t[i] comes out of the same hand-off, so the
+// first layer also reads its stream once.
 #include "mhc_device.h"
 #include "mhc_finish.h"
 #include "mhc_launch.h"
@@ -164,7 +171,8 @@ struct Step {
 // What the kernel reads, writes and multiplies (FusedMode, mhc_launch.h).
 template <int MODE>
 struct FusedIO {
-  static constexpr bool FP8 = MODE == kFusedApplyFp8 || MODE == kFusedCoeffsFp8 || MODE == kFusedApplyPreFp8;
+  static constexpr bool FP8 = MODE == kFusedApplyFp8 || MODE == kFusedCoeffsFp8 || MODE == kFusedApplyPreFp8 ||
+                             MODE == kFusedCoeffsPreFp8;
   static constexpr bool PRE = is_pre_mode(MODE);
   static constexpr bool APPLY_BF16 = MODE == kFusedApplyBf16 || MODE == kFusedApplyPreBf16;
   static constexpr bool APPLY_FP8 = MODE == kFusedApplyFp8 || MODE == kFusedApplyPreFp8;
@@ -617,7 +625,7 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
     auto tile_vec = [&](int i) -> u32x4 {
       if constexpr (IO::APPLY_BF16) return out[i];
       else if constexpr (IO::APPLY_FP8) return fp8x8_to_bf16(out[i]);
-      else if constexpr (MODE == kFusedCoeffsFp8) return fp8x8_to_bf16(xv[i]);
+      else if constexpr (IO::FP8) return fp8x8_to_bf16(xv[i]);  // the product-only E4M3 modes
       else return xv[i];
     };
     // B operands of this wave's k-steps (global, L2-resident), in groups of
@@ -642,10 +650,12 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
     };
     char *my_lds_row = tile_of(t) + wave * T::ROW_BYTES;
     if constexpr (IO::PRE) {
-      uint8_t *yr = Y + (size_t)rr * NS * C * IO::EB;
+      if constexpr (IO::APPLY) {
+        uint8_t *yr = Y + (size_t)rr * NS * C * IO::EB;
 #pragma unroll
-      for (int i = 0; i < NS; ++i)
-        __builtin_nontemporal_store(out[i], reinterpret_cast<vec *>(yr + ((size_t)i * C + cst) * IO::EB));
+        for (int i = 0; i < NS; ++i)
+          __builtin_nontemporal_store(out[i], reinterpret_cast<vec *>(yr + ((size_t)i * C + cst) * IO::EB));
+      }
       // Keep the record check below the stores: the check's wait then covers
       // only loads issued at least a step ago (and the step's own stores).
       load_b(0);
@@ -661,8 +671,12 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
       pre_coeffs(rv, hp);
       emit(have ? t - 2 : 0, hp, poison, have, kv);
       if constexpr (IO::FP8) {
+        // This step's stream values (the apply's output, or X itself), emitted two steps on.
 #pragma unroll
-        for (int i = 0; i < NS; ++i) kv[i] = out[i];  // this step's output, emitted two steps on
+        for (int i = 0; i < NS; ++i) {
+          if constexpr (IO::APPLY) kv[i] = out[i];
+          else kv[i] = xv[i];
+        }
       }
 #pragma unroll
       for (int i = 0; i < NS; ++i)
@@ -924,31 +938,41 @@ int64_t pre_mode_grid(int64_t units, int64_t split, int64_t resident, int64_t wg
   return units < cap ? units : cap;
 }
 
-int64_t pre_mode_resident(int n, bool fp8, hipStream_t st) {
+namespace {
+template <int MODE>
+const void *pre_kernel_fn(int ni) {
+  switch (ni) {
+    case 0: return reinterpret_cast<const void *>(&post_res_next_kernel<1, MODE, true>);
+    case 1: return reinterpret_cast<const void *>(&post_res_next_kernel<2, MODE, true>);
+    default: return reinterpret_cast<const void *>(&post_res_next_kernel<4, MODE, true>);
+  }
+}
+}  // namespace
+
+int64_t pre_mode_resident(int n, int mode, hipStream_t st) {
   // Per-CU occupancy of the pre-mix kernel, cached per device and variant.
-  static std::atomic<int> occ_cache[64][3][2];
+  static std::atomic<int> occ_cache[64][3][4];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   const int ni = n == 1 ? 0 : (n == 2 ? 1 : (n == 4 ? 2 : -1));
-  if (ni < 0) return 0;
-  int occ = (dev >= 0 && dev < 64) ? occ_cache[dev][ni][fp8].load(std::memory_order_relaxed) : 0;
+  const int mi = mode == kFusedApplyPreBf16 ? 0
+               : mode == kFusedApplyPreFp8 ? 1
+               : mode == kFusedCoeffsPreBf16 ? 2
+               : mode == kFusedCoeffsPreFp8 ? 3 : -1;
+  if (ni < 0 || mi < 0) return 0;
+  int occ = (dev >= 0 && dev < 64) ? occ_cache[dev][ni][mi].load(std::memory_order_relaxed) : 0;
   if (occ <= 0) {
-    const void *fn = nullptr;
-    switch (ni * 2 + (fp8 ? 1 : 0)) {
-      case 0: fn = reinterpret_cast<const void *>(&post_res_next_kernel<1, kFusedApplyPreBf16, true>); break;
-      case 1: fn = reinterpret_cast<const void *>(&post_res_next_kernel<1, kFusedApplyPreFp8, true>); break;
-      case 2: fn = reinterpret_cast<const void *>(&post_res_next_kernel<2, kFusedApplyPreBf16, true>); break;
-      case 3: fn = reinterpret_cast<const void *>(&post_res_next_kernel<2, kFusedApplyPreFp8, true>); break;
-      case 4: fn = reinterpret_cast<const void *>(&post_res_next_kernel<4, kFusedApplyPreBf16, true>); break;
-      default: fn = reinterpret_cast<const void *>(&post_res_next_kernel<4, kFusedApplyPreFp8, true>); break;
-    }
+    const void *fn = mi == 0 ? pre_kernel_fn<kFusedApplyPreBf16>(ni)
+                   : mi == 1 ? pre_kernel_fn<kFusedApplyPreFp8>(ni)
+                   : mi == 2 ? pre_kernel_fn<kFusedCoeffsPreBf16>(ni)
+                             : pre_kernel_fn<kFusedCoeffsPreFp8>(ni);
     int v = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, fn, FusedTile<4, true>::THREADS, 0) != hipSuccess) {
       (void)hipGetLastError();  // leave no sticky error for the launch check
       return 0;
     }
     occ = v;
-    if (occ > 0 && dev >= 0 && dev < 64) occ_cache[dev][ni][fp8].store(occ, std::memory_order_relaxed);
+    if (occ > 0 && dev >= 0 && dev < 64) occ_cache[dev][ni][mi].store(occ, std::memory_order_relaxed);
   }
   int64_t cus = device_cus();
   if (st != nullptr) {
@@ -1017,6 +1041,8 @@ hipError_t launch_post_res_next(const FusedPlan &p, int n, int mode, int64_t B, 
     case kFusedCoeffsBf16: return launch_mode<kFusedCoeffsBf16>(n, p.fixed, B, C, spu, p.split, G, X, F, H, Y, phip, ws, dummy, pa, st);
     case kFusedApplyPreBf16: return launch_mode<kFusedApplyPreBf16>(n, p.fixed, B, C, spu, p.split, G, X, F, H, Y, phip, ws, dummy, pa, st);
     case kFusedApplyPreFp8: return launch_mode<kFusedApplyPreFp8>(n, p.fixed, B, C, spu, p.split, G, X, F, H, Y, phip, ws, dummy, pa, st);
+    case kFusedCoeffsPreBf16: return launch_mode<kFusedCoeffsPreBf16>(n, p.fixed, B, C, spu, p.split, G, X, F, H, Y, phip, ws, dummy, pa, st);
+    case kFusedCoeffsPreFp8: return launch_mode<kFusedCoeffsPreFp8>(n, p.fixed, B, C, spu, p.split, G, X, F, H, Y, phip, ws, dummy, pa, st);
     default: return hipErrorInvalidValue;
   }
 }

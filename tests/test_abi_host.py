@@ -245,6 +245,80 @@ def test_fused_pre_fp8_route_and_workspace(tune):
         mhc.mhc_post_res_coeffs_fp8_workspace_size(16384, 4, 7168)
 
 
+def _coeffs_pre(B=16, n=4, C=64, ws_bytes=None, fp8=False, **over):
+    names = ["X", "phi", "bp", "bq", "br", "logits", "r", "H", "Fp", "ws"]
+    p = dict(zip(names, _addrs(len(names))))
+    p.update(over)
+    size = mhc.mhc_coeffs_pre_fp8_workspace_size if fp8 else mhc.mhc_coeffs_pre_workspace_size
+    if ws_bytes is None:
+        ws_bytes = max(size(B, n, C), 16)
+    fn = mhc.mhc_coeffs_pre_fp8 if fp8 else mhc.mhc_coeffs_pre
+    return fn(B, n, C, p["X"], p["phi"], 0.01, 0.01, 0.01, p["bp"], p["bq"], p["br"], p["logits"],
+              p["r"], p["H"], p["Fp"], p["ws"], ws_bytes, stream=0, check=False)
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_coeffs_pre_validation(fp8):
+    eb = 1 if fp8 else 2
+    size = mhc.mhc_coeffs_pre_fp8_workspace_size if fp8 else mhc.mhc_coeffs_pre_workspace_size
+    assert _coeffs_pre(B=0, fp8=fp8) == mhc.MHC_OK
+    assert _coeffs_pre(B=0, X=None, Fp=None, ws=None, fp8=fp8) == mhc.MHC_OK
+    assert _coeffs_pre(n=3, fp8=fp8) == mhc.MHC_ERR_UNSUPPORTED
+    assert _coeffs_pre(C=36, fp8=fp8) == mhc.MHC_ERR_UNSUPPORTED              # C % 8 != 0
+    assert _coeffs_pre(B=-2, fp8=fp8) == mhc.MHC_ERR_INVALID_ARG
+    for k in ("X", "phi", "bp", "bq", "br", "logits", "r", "H", "Fp", "ws"):
+        assert _coeffs_pre(fp8=fp8, **{k: None}) == mhc.MHC_ERR_INVALID_ARG, k
+    assert _coeffs_pre(Fp=A + 16 * 4 * 64 * eb - 16, fp8=fp8) == mhc.MHC_ERR_INVALID_ARG  # F_pre overlaps X_t
+    assert _coeffs_pre(Fp=A + 7 * STEP, fp8=fp8) == mhc.MHC_ERR_INVALID_ARG   # F_pre overlaps H
+    assert _coeffs_pre(ws=A + 8 * STEP + 16 * 64 * eb - 16, fp8=fp8) == mhc.MHC_ERR_INVALID_ARG  # ws overlaps F_pre
+    assert _coeffs_pre(Fp=A + 8 * STEP + 8, fp8=fp8) == mhc.MHC_ERR_UNSUPPORTED  # F_pre needs 16-byte alignment
+    need = size(16, 4, 64)
+    assert need > 0 and _coeffs_pre(ws_bytes=need - 1, fp8=fp8) == mhc.MHC_ERR_WORKSPACE
+    # C % 32 != 0 is accepted (the two calls): the bf16 call at C = 40, the
+    # E4M3 call at C = 48; both sizes are mhc_coeffs's
+    C2 = 48 if fp8 else 40
+    coeffs_size = mhc.mhc_coeffs_fp8_workspace_size if fp8 else mhc.mhc_coeffs_workspace_size
+    assert size(16, 4, C2) == coeffs_size(16, 4, C2) > 0
+
+
+def test_coeffs_pre_route_and_workspace(tune):
+    for k in ("MHC_FUSED_PRE", "MHC_SMALL_MAX_B", "MHC_FUSED_FP8"):
+        tune.delenv(k, raising=False)
+    for one, size, coeffs_size in (
+            (mhc.mhc_coeffs_pre_one_pass, mhc.mhc_coeffs_pre_workspace_size, mhc.mhc_coeffs_workspace_size),
+            (mhc.mhc_coeffs_pre_fp8_one_pass, mhc.mhc_coeffs_pre_fp8_workspace_size,
+             mhc.mhc_coeffs_fp8_workspace_size)):
+        assert one(16384, 4, 7168) and one(4096, 4, 4096) and one(1000, 2, 4096) and one(300, 1, 1024)
+        assert not one(64, 4, 7168)          # small B: mhc_coeffs then mhc_pre
+        assert not one(8192, 8, 4096)        # n = 8
+        assert not one(4096, 4, 8704)        # 17 steps of 512 channels per row
+        assert not one(4096, 4, 7184)        # C % 32 != 0
+        assert not one(0, 4, 7168) and not one(16, 3, 64)
+        # one pass: the pre-mix layout of mhc_post_res_coeffs_pre (it also
+        # holds mhc_coeffs's workspace, for the two calls)
+        B, n, C = 16384, 4, 7168
+        assert size(B, n, C) == mhc.mhc_post_res_coeffs_pre_workspace_size(B, n, C)
+        assert size(B, n, C) >= coeffs_size(B, n, C)
+        assert size(8192, 8, 4096) == coeffs_size(8192, 8, 4096)
+    tune.setenv("MHC_FUSED_PRE", "0")
+    assert not mhc.mhc_coeffs_pre_one_pass(16384, 4, 7168)
+    assert mhc.mhc_coeffs_pre_workspace_size(16384, 4, 7168) == mhc.mhc_coeffs_workspace_size(16384, 4, 7168)
+
+
+def test_coeffs_pre_check_host():
+    """mhc_coeffs_pre_check answers without a device where no one-pass kernel
+    can have run, and rejects bad arguments."""
+    assert mhc.mhc_coeffs_pre_check(64, 4, 7168, A, workspace_bytes=1 << 20, stream=0) == mhc.MHC_OK
+    assert mhc.mhc_coeffs_pre_check(8192, 8, 4096, A, workspace_bytes=1 << 20, stream=0) == mhc.MHC_OK
+    assert mhc.mhc_coeffs_pre_check(4096, 4, 7184, A, workspace_bytes=1 << 30, stream=0) == mhc.MHC_OK
+    assert mhc.mhc_coeffs_pre_check(0, 4, 7168, None, stream=0) == mhc.MHC_OK
+    assert mhc.mhc_coeffs_pre_check(16384, 3, 7168, A, stream=0) == mhc.MHC_ERR_UNSUPPORTED
+    assert mhc.mhc_coeffs_pre_check(16384, 4, 7168, None, stream=0) == mhc.MHC_ERR_INVALID_ARG
+    need = mhc.mhc_coeffs_pre_workspace_size(16384, 4, 7168)
+    assert mhc.mhc_coeffs_pre_check(16384, 4, 7168, A, workspace_bytes=need - 1,
+                                    stream=0) == mhc.MHC_ERR_WORKSPACE
+
+
 def test_binding_raises_on_error_status():
     with pytest.raises(mhc.MhcError) as ei:
         mhc.mhc_pre(16, 3, 64, *_addrs(3), stream=0)
@@ -482,3 +556,7 @@ def test_no_device_is_mhc_err_hip():
     need = mhc.mhc_post_res_coeffs_pre_workspace_size(16384, 4, 7168)
     assert mhc.mhc_post_res_coeffs_pre_check(16384, 4, 7168, A, workspace_bytes=need,
                                              stream=0) == mhc.MHC_ERR_HIP
+    assert _coeffs_pre(B=16384, n=4, C=7168, **dict(zip(
+        ["X", "phi", "bp", "bq", "br", "logits", "r", "H", "Fp", "ws"],
+        [A + k * (1 << 36) for k in range(10)]))) == mhc.MHC_ERR_HIP
+    assert mhc.mhc_coeffs_pre_check(16384, 4, 7168, A, workspace_bytes=need, stream=0) == mhc.MHC_ERR_HIP
