@@ -133,13 +133,13 @@ SECONDARY_STEPS = 50
 
 # kernels launched by each call (for the roofline record)
 KERNELS_OF_CALL = {"mhc_post_res": "post_res_kernel", "mhc_pre": "pre_kernel",
-                   "mhc_coeffs": "pack_phi_kernel + post_res_next_kernel<n, 3> (product only, fixed-slice "
-                                 "layout) + coeff_sinkhorn_kernel",
+                   "mhc_coeffs": "post_res_next_kernel<n, 3> (product only, fixed-slice layout) + "
+                                 "coeff_sinkhorn_kernel",
                    "mhc_post_res_coeffs": "pack_phi_kernel + post_res_next_kernel + coeff_sinkhorn_kernel",
-                   "mhc_post_res_coeffs_pre": "pack_phi_kernel + post_res_next_kernel<n, 4> (pre-mix mode) "
-                                              "+ coeff_sinkhorn_kernel (tree order)",
-                   "mhc_coeffs_pre": "pack_phi_kernel + post_res_next_kernel<n, 6> (product-only pre-mix "
-                                     "mode) + coeff_sinkhorn_kernel (tree order)"}
+                   "mhc_post_res_coeffs_pre": "zero_kernel (records) + post_res_next_kernel<n, 4> (pre-mix "
+                                              "mode) + coeff_sinkhorn_kernel (tree order)",
+                   "mhc_coeffs_pre": "zero_kernel (records) + post_res_next_kernel<n, 6> (product-only "
+                                     "pre-mix mode) + coeff_sinkhorn_kernel (tree order)"}
 
 
 class Pipeline:
@@ -341,14 +341,15 @@ def _summary(B, n, C, eb, ms_layer, ms_three, per_pipe=None, per_three=None, ms_
 # Sources of the kernels each call runs on the large workload (n=4, C=7168,
 # B=16384, bf16): a recorded counter summary is used only while these match.
 CALL_SOURCES = {
-    "mhc_coeffs": ("mhc_pack.hip", "mhc_post_res_fused.hip", "mhc_coeff_sinkhorn.hip", "mhc_finish.h",
-                   "mhc_device.h"),
+    "mhc_coeffs": ("mhc_post_res_fused.hip", "mhc_coeff_sinkhorn.hip", "mhc_finish.h", "mhc_device.h"),
     "mhc_pre": ("mhc_stream.hip", "mhc_device.h"),
     "mhc_post_res": ("mhc_stream.hip", "mhc_device.h"),
     "mhc_post_res_coeffs": ("mhc_pack.hip", "mhc_post_res_fused.hip", "mhc_coeff_sinkhorn.hip",
                             "mhc_finish.h", "mhc_device.h"),
     "mhc_post_res_coeffs_pre": ("mhc_pack.hip", "mhc_post_res_fused.hip", "mhc_coeff_sinkhorn.hip",
                                 "mhc_finish.h", "mhc_device.h"),
+    "mhc_coeffs_pre": ("mhc_pack.hip", "mhc_post_res_fused.hip", "mhc_coeff_sinkhorn.hip",
+                       "mhc_finish.h", "mhc_device.h"),
     "mhc_lazy_prenorm_gemm": ("mhc_lazy_prenorm.hip", "mhc_device.h"),
     "mhc_coeffs_phi32": ("mhc_pack.hip", "mhc_gemm_lds.hip", "mhc_coeff_sinkhorn.hip", "mhc_finish.h",
                          "mhc_device.h"),

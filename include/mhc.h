@@ -246,7 +246,7 @@ int mhc_post_res_coeffs_pre_check(int64_t B, int32_t n, int64_t C, int32_t fp8,
  * hipMalloc): the same call, results and routes, without the workspace
  * argument.  Its workspace is a device array inside the library, of
  * MHC_NOALLOC_SCRATCH_BYTES (32 MiB: the large workload n = 4, C = 7168,
- * B = 16384 needs about 30.3 MB), one per GPU the library runs on, held until
+ * B = 16384 needs about 28.4 MB), one per GPU the library runs on, held until
  * the process ends.  Shapes whose workspace (as
  * mhc_post_res_coeffs_pre_workspace_size reports it) exceeds that return
  * MHC_ERR_WORKSPACE before anything is launched.  The call allocates nothing:

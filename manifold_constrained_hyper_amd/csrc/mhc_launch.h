@@ -115,7 +115,7 @@ struct FusedPlan {
 // bf16 apply after mhc_pre runs slower (393 vs 381 us).
 FusedPlan plan_post_res_next(int64_t B, int n, int64_t C, bool pre = false, bool prefer_fixed = false);
 // Whether the fixed-slice layout fits (n <= 4, one workgroup per slice at
-// least, packed phi addressable by 32-bit offsets).
+// least, phi itself addressable by 32-bit offsets).
 bool fixed_layout_fits(int n, int64_t C);
 // What the persistent kernel of mhc_post_res_fused.hip does per step.
 enum FusedMode : int {
@@ -141,7 +141,9 @@ struct PreArgs {
   uint32_t *rec;                  // records [B, split, PW]: fp32 bits, 0 = not yet written
   uint32_t rec_bytes;             // split * B * PW * 4 (< 2^31); PW = n+1 rounded up to even
   uint32_t partial_bytes;         // split * B * (N+1) * 4 (< 2^31)
-  uint32_t phip_bytes;            // packed phi (< 2^31; also set in the fixed-slice layout)
+  uint32_t phip_bytes;            // packed phi (< 2^31)
+  const uint16_t *phi;            // the fixed-slice layout: phi [K, N] itself (gathered once per run)
+  uint32_t phi_bytes;             // K * N * 2 (< 2^31)
   const float *b_pre;             // fp32 [n]
   float alpha_pre, inv_k;         // alpha_pre; 1 / (n C)
   uint32_t *giveup;               // set non-zero by a wave whose wait for records gave up

@@ -33,8 +33,9 @@
 //   product  the step's 16*n MFMA k-steps (32 channels of one stream each)
 //            are split over the 16 waves; each reads its A operands (16 rows x
 //            8 channels per lane) from LDS and its B operands from the packed
-//            copy of phi_{t+1} (see mhc_gemm_lds.hip; in the fixed-slice
-//            layout loaded once per run and held in registers) and
+//            copy of phi_{t+1} (see mhc_pack.hip; in the fixed-slice layout
+//            gathered from phi_{t+1} itself once per run and held in
+//            registers, with no packing launch) and
 //            accumulates v_mfma_f32_16x16x32_bf16 plus the Gram block for the
 //            sum of squares;
 //   flush    the 16 waves' accumulators are summed through LDS in wave order
@@ -234,15 +235,18 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
   [[maybe_unused]] __amdgpu_buffer_rsrc_t ws_rsrc, rec_rsrc, phi_rsrc;
   [[maybe_unused]] const uint32_t lane_off16 = (uint32_t)lane * 16u;
   if constexpr (FIX)
-    phi_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(phip), (short)0, (int)pa.phip_bytes, kRsrcWord3);
+    phi_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(pa.phi), (short)0, (int)pa.phi_bytes, kRsrcWord3);
   if constexpr (IO::PRE) {
     ws_rsrc = __builtin_amdgcn_make_buffer_rsrc(ws, (short)0, (int)pa.partial_bytes, kRsrcWord3);
     rec_rsrc = __builtin_amdgcn_make_buffer_rsrc(pa.rec, (short)0, (int)pa.rec_bytes, kRsrcWord3);
   }
 
   // In the fixed-slice layout (KB = KPW at n <= 4) the phi operands of each
-  // wave's k-steps are the same on every step: loaded once here (scalar
-  // block offset + the lane's 16 bytes) and held in registers.
+  // wave's k-steps are the same on every step: gathered once here straight
+  // from phi [K, N] and held in registers.  Lane (m, g) of k-step ks and
+  // column block nb takes phi[32 ks + 8 g + j][16 nb + m], j = 0..7 (the
+  // B operand layout of v_mfma_f32_16x16x32_bf16); columns past N read past
+  // the buffer, i.e. zero.
   [[maybe_unused]] bf16x8 bfix[FIX ? T::KB : 1][T::NB];
   if constexpr (FIX) {
     const int cb = pre_slot * kStepCh;
@@ -252,9 +256,18 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
       const int i = ks >> 4, ts = ks & 15;
       const int kstep = (i * C + min(cb + 32 * ts, C - 32)) >> 5;  // clamped in range; such steps add zero
 #pragma unroll
-      for (int nb = 0; nb < T::NB; ++nb)
-        bfix[q][nb] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-            phi_rsrc, lane_off16, uniform((kstep * T::NB + nb) * 1024), 0));
+      for (int nb = 0; nb < T::NB; ++nb) {
+        const int col = nb * 16 + m;
+        const uint32_t base = col < T::N ? (uint32_t)((kstep * 32 + 8 * g) * T::N + col) * 2u : 0x80000000u;
+        uint32_t w[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(phi_rsrc, base + (uint32_t)(2 * h * T::N * 2), 0, 0);
+          const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(phi_rsrc, base + (uint32_t)((2 * h + 1) * T::N * 2), 0, 0);
+          w[h] = lo | (hi << 16);
+        }
+        bfix[q][nb] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+      }
     }
   }
 
@@ -869,8 +882,8 @@ bool pre_mode_fits(int64_t B, int n, int64_t C) {
   const int64_t steps = (C + kStepCh - 1) / kStepCh;
   const int64_t N = (int64_t)n * n + 2 * n;
   const int64_t lim = int64_t(1) << 31;
-  const int64_t phip_bytes = ((int64_t)n * C + 31) / 32 * ((N + 15) / 16) * 1024;
-  return steps <= kRecordSlices && steps <= device_cus() && C * 2 < lim && phip_bytes < lim &&
+  const int64_t phi_bytes = (int64_t)n * C * N * 2;
+  return steps <= kRecordSlices && steps <= device_cus() && C * 2 < lim && phi_bytes < lim &&
          steps * B * ((n + 2) & ~1) * 4 < lim && steps * B * (N + 1) * 4 < lim;
 }
 
@@ -883,8 +896,8 @@ bool fixed_layout_fits(int n, int64_t C) {
   if (n != 1 && n != 2 && n != 4) return false;
   const int64_t steps = (C + kStepCh - 1) / kStepCh;
   const int64_t N = (int64_t)n * n + 2 * n;
-  const int64_t phip_bytes = ((int64_t)n * C + 31) / 32 * ((N + 15) / 16) * 1024;
-  return steps <= device_cus() && phip_bytes < (int64_t(1) << 31);
+  const int64_t phi_bytes = (int64_t)n * C * N * 2;  // phi itself, addressed by 32-bit buffer offsets
+  return steps <= device_cus() && phi_bytes < (int64_t(1) << 31);
 }
 
 FusedPlan plan_post_res_next(int64_t B, int n, int64_t C, bool pre, bool prefer_fixed) {
@@ -920,7 +933,7 @@ FusedPlan plan_post_res_next(int64_t B, int n, int64_t C, bool pre, bool prefer_
   p.dummy_offset = (p.partial_bytes + 1023) & ~(size_t)1023;
   p.dummy_bytes = (size_t)((16 * (N + 1) + 1023) / 1024) * 1024 * sizeof(float);
   p.phip_offset = p.dummy_offset + p.dummy_bytes;
-  p.phip_bytes = (size_t)p.ksteps * (size_t)NB * 1024;
+  p.phip_bytes = p.fixed ? 0 : (size_t)p.ksteps * (size_t)NB * 1024;  // the fixed layout reads phi itself
   p.zero_offset = p.phip_offset + p.phip_bytes;
   p.rec_offset = p.zero_offset + 256;
   p.rec_bytes = pre ? (size_t)p.split * (size_t)B * (size_t)((n + 2) & ~1) * 4 : 0;
@@ -998,10 +1011,15 @@ hipError_t launch_post_res_next(const FusedPlan &p, int n, int mode, int64_t B, 
   if (pre != p.pre || (pre && !pre_out)) return hipErrorInvalidValue;
   char *base = static_cast<char *>(ws_base);
   void *phip = base + p.phip_offset;
-  // The pre-mix mode's records and give-up word start from zero: the packing
-  // launch clears them.
-  hipError_t e = launch_pack_phi(n, (int64_t)n * C, p.ksteps, phi_next, phip, base + p.zero_offset, st,
-                                 pre ? base + p.rec_offset : nullptr, p.total_bytes - p.rec_offset);
+  // The fixed-slice layout gathers its phi operands from phi itself; the
+  // other layouts read the packed copy.  The pre-mix mode's records and
+  // give-up word start from zero.
+  hipError_t e = hipSuccess;
+  if (p.fixed)
+    e = pre ? launch_zero(base + p.rec_offset, p.total_bytes - p.rec_offset, st) : hipSuccess;
+  else
+    e = launch_pack_phi(n, (int64_t)n * C, p.ksteps, phi_next, phip, base + p.zero_offset, st,
+                        pre ? base + p.rec_offset : nullptr, p.total_bytes - p.rec_offset);
   if (e != hipSuccess) return e;
   float *ws = reinterpret_cast<float *>(base);
   float *dummy = reinterpret_cast<float *>(base + p.dummy_offset);
@@ -1030,7 +1048,8 @@ hipError_t launch_post_res_next(const FusedPlan &p, int n, int mode, int64_t B, 
   if (p.fixed) {
     // Whole row tiles per round (each workgroup keeps slice p(g) mod S).
     cap = (cap / p.split) * p.split;
-    pa.phip_bytes = (uint32_t)p.phip_bytes;
+    pa.phi = static_cast<const uint16_t *>(phi_next);
+    pa.phi_bytes = (uint32_t)((int64_t)n * C * (n * n + 2 * n) * 2);
   }
   if (cap < 1) return hipErrorInvalidValue;
   const int G = (int)(U < cap ? U : cap);
