@@ -720,6 +720,8 @@ def main():
                     help="run only the two-call pipeline's timed loop (counter runs of its kernels)")
     ap.add_argument("--three-call-only", action="store_true",
                     help="run only the three separate calls' timed loop (counter runs of their kernels)")
+    ap.add_argument("--first-layer-only", action="store_true",
+                    help="run only the first layer's call (mhc_coeffs_pre) in a timed loop (counter runs)")
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the E4M3 and other-workload sections (profiling runs of one workload)")
     ap.add_argument("--lazy-prenorm-only", action="store_true",
@@ -773,7 +775,8 @@ def main():
 
     # The CPU baseline samples the input before the chained loop overwrites it.
     cpu = None
-    if not args.no_cpu_baseline and not args.kernel_only and not args.two_call_only:
+    if (not args.no_cpu_baseline and not args.kernel_only and not args.two_call_only
+            and not args.three_call_only and not args.first_layer_only):
         cpu = _cpu_baseline(inp, args.cpu_rows, args.cpu_budget_s)
 
     # ---- headline: one call per layer, residual stream chained through layers
@@ -878,6 +881,10 @@ def main():
     if args.three_call_only:  # counter runs of the three calls' kernels
         timed(three)
         print(json.dumps({"three_call_only": True, "steps": args.steps}), flush=True)
+        return
+    if args.first_layer_only:  # counter runs of the first layer's call
+        timed(first)
+        print(json.dumps({"first_layer_only": True, "steps": args.steps}), flush=True)
         return
 
     ms_three = ms_two = None
