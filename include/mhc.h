@@ -326,9 +326,14 @@ int mhc_coeffs_pre_check(int64_t B, int32_t n, int64_t C, int32_t fp8,
  *
  * Readings (the page gives no conversion rules): values are used as they are
  * (no scale factors, as in the page's benchmark); inputs are widened exactly;
- * arithmetic is fp32 as in the bf16 calls; F_pre and X_next are rounded once
- * to E4M3, to nearest even, saturating at +-448 (torch's own cast returns NaN
- * past the range); a NaN (from a NaN input) stays NaN, as code 0x7F or 0xFF.  The product widens the E4M3 X exactly to bf16 for the
+ * arithmetic is fp32 as in the bf16 calls, except that at n = 4 the post/res
+ * mix of X_next runs on the matrix core with each coefficient carried as two
+ * bf16 parts (to 2^-18 relative; products exact, fp32 sums), which can move
+ * an E4M3 result only where the exact value lies within about 2^-17 of its
+ * terms' magnitude from a rounding midpoint; F_pre and X_next are rounded
+ * once to E4M3, to nearest even, saturating at +-448 (torch's own cast
+ * returns NaN past the range); a NaN (from a NaN input) stays NaN, as code
+ * 0x7F or 0xFF.  The product widens the E4M3 X exactly to bf16 for the
  * matrix core, so logits, r and H carry the bf16 calls' accuracy.
  *
  * Arguments, ownership, errors and workspace rules are those of the bf16

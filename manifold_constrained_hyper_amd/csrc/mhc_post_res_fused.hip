@@ -77,8 +77,9 @@
 //     column over 16 slice slots as a balanced tree (the order the combine
 //     kernel uses in this mode, so H_pre comes out bitwise as in H_next),
 //     forms the n gates and emits its row of F_pre from the tile exactly as
-//     pre_kernel would from X_{t+1} in HBM (E4M3: from the lane's own
-//     outputs of that step, kept in registers, as pre_fp8_kernel would).
+//     pre_kernel would from X_{t+1} in HBM (E4M3: the tile holds the E4M3
+//     values widened exactly, so the same chain gives pre_fp8_kernel's bits;
+//     the product-only E4M3 mode keeps its X values in registers instead).
 // No workgroup waits for one that has not started: a wait at step t+2 needs
 // only records published at the start of step t+1 by workgroups of the same
 // round, and every workgroup publishes before it waits (induction over t;
@@ -193,6 +194,9 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
   using IO = FusedIO<MODE>;
   using T = FusedTile<NS, IO::PRE>;
   using vec = typename IO::vec;
+  // F_pre from register-held E4M3 values (the product-only E4M3 pre-mix
+  // mode) rather than from the tile.
+  constexpr bool KV = IO::PRE && IO::FP8 && !IO::APPLY;
   static_assert(!IO::PRE || FIX, "the pre-mix mode runs the fixed-slice layout");
   static_assert(!FIX || T::KB == T::KPW, "the fixed-slice layout holds every k-step's operands");
   __shared__ __attribute__((aligned(1024))) char lds[T::LDS_BYTES];
@@ -416,13 +420,15 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
 #pragma unroll
     for (int i = 0; i < NS; ++i) hp[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gate), 16 * i));
   };
-  // F_pre of this wave's row of step q: bf16 from the row's tile, E4M3 from
-  // kv, this lane's own apply output of step q (kept in registers for two
-  // steps).  `real` false (before the first step) or a row past B gives the
-  // store an empty buffer (dropped); a given-up wait poisons the vector with
-  // NaN.  Lanes past the slice take the last in-range vector's tile slot
-  // (bf16) or computed the owning lane's values from clamped addresses
-  // (E4M3), so they store the owning lane's bytes to the owning lane's
+  // F_pre of this wave's row of step q, from the row's tile (bf16; in the
+  // E4M3 apply mode the E4M3 values widened exactly, so the fp32 chain below
+  // sees the values pre_fp8_kernel widens from E4M3), or in the product-only
+  // E4M3 mode (KV) from kv, this lane's own X values of step q (kept in
+  // registers for two steps).  `real` false (before the first step) or a row
+  // past B gives the store an empty buffer (dropped); a given-up wait
+  // poisons the vector with NaN.  Lanes past the slice take the last in-range
+  // vector's tile slot or computed the owning lane's values from clamped
+  // addresses, so they store the owning lane's bytes to the owning lane's
   // address.
   auto emit = [&](int q, const float (&hp)[NS], bool poison, bool real, const vec (&kv)[NS]) {
     const Step sp = step_at(q);
@@ -437,7 +443,7 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
     // fp32 FMA chain over the streams in stream order from zero, one rounding
     // at the end: pre_kernel's arithmetic (pre_fp8_kernel's for E4M3).
     float a[8];
-    if constexpr (IO::FP8) {
+    if constexpr (KV) {
       // The E4M3 values themselves, widened to fp32 (exact), two per instruction.
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
@@ -454,7 +460,7 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
         for (int k = 0; k < 4; ++k) a[4 * d + k] = s4[k];
       }
     } else {
-      // bf16: the lane's 16-byte slot of its row of the tile.
+      // The lane's 16-byte slot of its row of the tile.
       const int slot = (((cst - sp.c0) >> 3) ^ (wave & 15)) * 16;
       const char *src = tile_of(q) + wave * T::ROW_BYTES;
       u32x4 xv[NS];
@@ -572,10 +578,27 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
         }
       }
     } else if constexpr (IO::APPLY_FP8) {
-      // E4M3: each 8-byte vector is two words of four channels; the same FMA
-      // chain per element as post_res_fp8_kernel, then the E4M3 result is
-      // widened (exactly) for the tile.
-      if constexpr (NS <= 4) {
+      // E4M3: each 8-byte vector is two words of four channels; the same
+      // arithmetic per element as post_res_fp8_kernel (at n = 4 the mix on
+      // the matrix core, mix4_pair; otherwise an FMA chain), then the E4M3
+      // result is widened (exactly) for the tile.
+      if constexpr (NS == 4) {
+        // Row (lane & 3) of H_res and H_post[lane & 3] from the lanes of hv.
+        const int i4 = lane & 3;
+        auto bperm = [&](int src) { return __int_as_float(__builtin_amdgcn_ds_bpermute(src * 4, (int)hv[0])); };
+        const Mix4A ma = mix4_a(bperm(NS + i4 * NS), bperm(NS + i4 * NS + 1), bperm(NS + i4 * NS + 2),
+                                bperm(NS + i4 * NS + 3), bperm(i4));
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          f32x4 v0, v1;
+          mix4_pair(ma, xv[0][d], xv[1][d], xv[2][d], xv[3][d], fv[d], 0, v0, v1);
+#pragma unroll
+          for (int i = 0; i < NS; ++i) out[i][d] = pack_fp8x2_lo(v0[i], v1[i]);
+          mix4_pair(ma, xv[0][d], xv[1][d], xv[2][d], xv[3][d], fv[d], 2, v0, v1);
+#pragma unroll
+          for (int i = 0; i < NS; ++i) out[i][d] = pack_fp8x2_hi(out[i][d], v0[i], v1[i]);
+        }
+      } else if constexpr (NS <= 4) {
         float hpost[NS], hres[NS][NS];
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
@@ -683,13 +706,9 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
       float hp[NS];
       pre_coeffs(rv, hp);
       emit(have ? t - 2 : 0, hp, poison, have, kv);
-      if constexpr (IO::FP8) {
-        // This step's stream values (the apply's output, or X itself), emitted two steps on.
+      if constexpr (KV) {
 #pragma unroll
-        for (int i = 0; i < NS; ++i) {
-          if constexpr (IO::APPLY) kv[i] = out[i];
-          else kv[i] = xv[i];
-        }
+        for (int i = 0; i < NS; ++i) kv[i] = xv[i];  // this step's X, emitted two steps on
       }
 #pragma unroll
       for (int i = 0; i < NS; ++i)
@@ -754,8 +773,9 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
   };
 
   const int tl = nsteps - 1;
-  // The E4M3 pre-mix mode's own apply outputs of the last two steps, one set
-  // per register set (step t runs on set t & 1: ka for even t, kb for odd).
+  // The product-only E4M3 pre-mix mode's own X values of the last two steps,
+  // one set per register set (step t runs on set t & 1: ka for even t, kb
+  // for odd).
   [[maybe_unused]] vec ka[NS], kb[NS];
   if constexpr (NS >= 8) {
     // n = 8: one register set (two would not fit 128 VGPRs).
@@ -785,7 +805,7 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
   }
   if constexpr (IO::PRE) {
     // The last two steps' F_pre (their tiles are intact: nothing rewrote them;
-    // step q's own outputs are in ka or kb by the parity of q).
+    // with KV, step q's own values are in ka or kb by the parity of q).
     auto tail = [&](int q, const vec (&kv)[NS]) {
       u32x2 rv;
       rec_load(rv, q);

@@ -5,7 +5,10 @@
 // benchmark with every tensor in torch.float8_e4m3fn; the arithmetic is that of
 // section 2.5 (and the fused apply of section 3.4) as in mhc_stream.hip: fp32
 // accumulation of the widened inputs, one rounding to E4M3 at the end (to
-// nearest even, saturating at +-448).
+// nearest even, saturating at +-448).  At n = 4 the post/res mix runs on the
+// matrix core (mix4_pair, mhc_device.h: H carried to 2^-17 relative as two
+// bf16 parts, products exact, fp32 sums), as in the fused kernel's E4M3
+// apply, so both write the same bits.
 //
 // Layout of the work as in mhc_stream.hip: one wavefront per (row, chunk)
 // task, a chunk being 64 consecutive 16-byte vectors of 16 E4M3 channels, so
@@ -92,14 +95,40 @@ __global__ __launch_bounds__(64) void post_res_fp8_kernel(const uint8_t *__restr
   const uint8_t *xr = X + (size_t)row * xrow;
   const uint8_t *fr = F + (size_t)row * cvec * 16;
   uint8_t *yr = Y + (size_t)row * xrow;
-  const uint32_t v = chunk * 64u + (threadIdx.x & 63u);
-  if (v >= cvec) return;
+  const uint32_t v_raw = chunk * 64u + (threadIdx.x & 63u);
+  // At n = 4 the mix runs on the matrix core, whose 4x4x4 blocks take A rows
+  // from four neighbouring lanes: every lane stays, lanes past the row
+  // compute on its last vector and store nothing.
+  if (NS != 4 && v_raw >= cvec) return;
+  const uint32_t v = v_raw < cvec ? v_raw : cvec - 1;
   u32x4 xv[NS], fv;
 #pragma unroll
   for (int j = 0; j < NS; ++j)
     xv[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xr + ((size_t)j * cvec + v) * 16));
   fv = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(fr + (size_t)v * 16));
   u32x4 out[NS];
+  if constexpr (NS == 4) {
+    // Row (lane & 3) of H_res and H_post[lane & 3] (per-lane loads; H is only
+    // 4-byte aligned).
+    const int i4 = threadIdx.x & 3;
+    const float *hr = h + 2 * NS + i4 * NS;
+    const Mix4A ma = mix4_a(hr[0], hr[1], hr[2], hr[3], h[NS + i4]);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      f32x4 v0, v1;
+      mix4_pair(ma, xv[0][w], xv[1][w], xv[2][w], xv[3][w], fv[w], 0, v0, v1);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) out[i][w] = pack_fp8x2_lo(v0[i], v1[i]);
+      mix4_pair(ma, xv[0][w], xv[1][w], xv[2][w], xv[3][w], fv[w], 2, v0, v1);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) out[i][w] = pack_fp8x2_hi(out[i][w], v0[i], v1[i]);
+    }
+    if (v_raw >= cvec) return;
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+      __builtin_nontemporal_store(out[i], reinterpret_cast<u32x4 *>(yr + ((size_t)i * cvec + v) * 16));
+    return;
+  }
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     float f[4], x[NS][4];
