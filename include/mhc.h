@@ -203,8 +203,13 @@ int mhc_post_res_coeffs(int64_t B, int32_t n, int64_t C,
  * if they hold compute units so long that a wait for another workgroup
  * cannot complete within about a second, the wait gives up, writes NaN to the
  * affected F_pre_next vectors and sets a word in the workspace, which
- * mhc_post_res_coeffs_pre_check reads back.  Other shapes run
- * mhc_post_res_coeffs followed by mhc_pre on X_next, with the same results.
+ * mhc_post_res_coeffs_pre_check reads back.  Where all of a row's channels
+ * fit one 1024-channel slice (bf16, n <= 4, B <= 256, n*C <= 1024) it runs
+ * as one kernel with one workgroup per 16 rows: no workgroup waits for
+ * another and the workspace is not touched (its size is still required), and
+ * mhc_post_res_coeffs_pre_one_pass() reports 1 for these shapes too.  Other
+ * shapes run mhc_post_res_coeffs followed by mhc_pre on X_next, with the same
+ * results.
  *
  * Arguments as mhc_post_res_coeffs, plus F_pre_next (16-byte aligned, must
  * not overlap any other argument).  The workspace must hold
@@ -220,10 +225,11 @@ int mhc_post_res_coeffs_pre(int64_t B, int32_t n, int64_t C,
                             float *logits_next, float *r_next, float *H_next, void *F_pre_next,
                             void *workspace, size_t workspace_bytes, void *stream);
 
-/* 1 if mhc_post_res_coeffs_pre runs this shape as one pass, 0 if it runs the
- * two calls (or the shape is invalid).  (A stream whose CU mask leaves too
- * few compute units makes the call take the two calls even where this
- * returns 1.) */
+/* 1 if mhc_post_res_coeffs_pre runs this shape as one pass (the persistent
+ * pass, or the single-slice kernel at small shapes), 0 if it runs the two
+ * calls (or the shape is invalid).  (A stream whose CU mask leaves too few
+ * compute units makes the persistent pass's shapes take the two calls even
+ * where this returns 1.) */
 int32_t mhc_post_res_coeffs_pre_one_pass(int64_t B, int32_t n, int64_t C);
 
 /* Whether the last mhc_post_res_coeffs_pre (fp8 == 0) or
@@ -290,7 +296,10 @@ int mhc_post_res_coeffs_pre_noalloc(int64_t B, int32_t n, int64_t C,
  * and the residency rules, the give-up behaviour (F_pre NaN in the rows a
  * wait gave up on; logits, r and H still complete) and the give-up word
  * (read with mhc_coeffs_pre_check) are those of mhc_post_res_coeffs_pre.
- * Other shapes run mhc_coeffs followed by mhc_pre, with the same results. */
+ * Where mhc_post_res_coeffs_pre takes its single-slice kernel (bf16, n <= 4,
+ * B <= 256, n*C <= 1024; here also for C % 32 != 0, C % 8 == 0) this call
+ * takes the same kernel without the apply.  Other shapes run mhc_coeffs
+ * followed by mhc_pre, with the same results. */
 size_t mhc_coeffs_pre_workspace_size(int64_t B, int32_t n, int64_t C);
 
 int mhc_coeffs_pre(int64_t B, int32_t n, int64_t C,

@@ -233,6 +233,15 @@ bool pre_fused(int64_t B, int32_t n, int64_t C, Elt e) {
   return fused_route(B, n, C, e) == FusedRoute::kFused && mhc::pre_mode_fits(B, n, C);
 }
 
+// The single-slice route (mhc_layer_small.hip): bf16, n <= 4, the small-B
+// sizes, n*C <= 1024, wherever the one-pass calls are not turned off.  It
+// needs no workspace (the two calls' size is still asked for) and never waits.
+bool small_pass(int64_t B, int32_t n, int64_t C, Elt e) {
+  if (e.fp8 || e.phi32) return false;
+  if (mhc::tune(mhc::kTuneFusedPre) == 0) return false;
+  return mhc::layer_small_fits(B, n, C);
+}
+
 size_t post_res_coeffs_pre_ws_bytes(int64_t B, int32_t n, int64_t C, Elt e) {
   if (check_shape_elt(B, n, C, e) != MHC_OK || B == 0 || C % 32 != 0) return 0;
   if (pre_fused(B, n, C, e)) return mhc::plan_post_res_next(B, n, C, true).total_bytes;
@@ -282,6 +291,10 @@ int post_res_coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t
   if (workspace_bytes < ws_need) return MHC_ERR_WORKSPACE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (with_pre && small_pass(B, n, C, e))  // one kernel: apply, coefficients and F_pre
+    return from_hip(mhc::launch_layer_small(n, true, B, C, X_t, F_out, H, X_next, phi_next, alpha_pre, alpha_post,
+                                            alpha_res, b_pre, b_post, b_res, logits_next, r_next, H_next,
+                                            F_pre_next, s));
   int64_t grid = 0;
   if (one_pass) {
     // The pass needs every workgroup of a round resident at once: size the
@@ -388,6 +401,9 @@ int coeffs_pre_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t, con
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int mode = e.fp8 ? mhc::kFusedCoeffsPreFp8 : mhc::kFusedCoeffsPreBf16;
+  if (small_pass(B, n, C, e))  // one kernel: coefficients and F_pre
+    return from_hip(mhc::launch_layer_small(n, false, B, C, X_t, nullptr, nullptr, nullptr, phi, alpha_pre,
+                                            alpha_post, alpha_res, b_pre, b_post, b_res, logits, r, H, F_pre, s));
   if (one_pass) {
     // As in mhc_post_res_coeffs_pre: a grid that can be resident at once,
     // else the two calls (the give-up word then reports no give-up).
@@ -575,7 +591,7 @@ int mhc_coeffs_pre(int64_t B, int32_t n, int64_t C, const void *X_t, const void 
 
 int32_t mhc_coeffs_pre_one_pass(int64_t B, int32_t n, int64_t C) {
   if (check_shape(B, n, C) != MHC_OK || B == 0) return 0;
-  return coeffs_pre_fused(B, n, C, kBf16) ? 1 : 0;
+  return coeffs_pre_fused(B, n, C, kBf16) || small_pass(B, n, C, kBf16) ? 1 : 0;
 }
 
 size_t mhc_post_res_coeffs_workspace_size(int64_t B, int32_t n, int64_t C) {
@@ -613,7 +629,7 @@ int mhc_post_res_coeffs_pre_check(int64_t B, int32_t n, int64_t C, int32_t fp8,
   const int st = check_shape_elt(B, n, C, e);
   if (st != MHC_OK) return st;
   if (C % 32 != 0) return MHC_ERR_UNSUPPORTED;
-  if (B == 0 || !pre_fused(B, n, C, e)) return MHC_OK;  // the two calls never give up
+  if (B == 0 || !pre_fused(B, n, C, e)) return MHC_OK;  // the two calls and the single-slice kernel never give up
   if (!workspace) {  // the array of mhc_post_res_coeffs_pre_noalloc
     if (fp8) return MHC_ERR_INVALID_ARG;
     if (post_res_coeffs_pre_ws_bytes(B, n, C, e) > kNoAllocScratchBytes) return MHC_ERR_WORKSPACE;
@@ -632,7 +648,7 @@ int mhc_coeffs_pre_check(int64_t B, int32_t n, int64_t C, int32_t fp8, const voi
   const Elt e = fp8 ? kFp8 : kBf16;
   const int st = check_shape_elt(B, n, C, e);
   if (st != MHC_OK) return st;
-  if (B == 0 || !coeffs_pre_fused(B, n, C, e)) return MHC_OK;  // the two calls never give up
+  if (B == 0 || !coeffs_pre_fused(B, n, C, e)) return MHC_OK;  // the two calls and the single-slice kernel never give up
   if (!workspace) return MHC_ERR_INVALID_ARG;
   if (workspace_bytes < coeffs_pre_ws_bytes(B, n, C, e)) return MHC_ERR_WORKSPACE;
   return read_giveup(B, n, C, e, workspace, stream);
@@ -659,7 +675,7 @@ int mhc_post_res_coeffs_pre_noalloc(int64_t B, int32_t n, int64_t C, const void 
 
 int32_t mhc_post_res_coeffs_pre_one_pass(int64_t B, int32_t n, int64_t C) {
   if (check_shape(B, n, C) != MHC_OK || B == 0 || C % 32 != 0) return 0;
-  return pre_fused(B, n, C, kBf16) ? 1 : 0;
+  return pre_fused(B, n, C, kBf16) || small_pass(B, n, C, kBf16) ? 1 : 0;
 }
 
 size_t mhc_coeffs_fp8_workspace_size(int64_t B, int32_t n, int64_t C) {

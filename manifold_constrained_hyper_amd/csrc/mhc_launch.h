@@ -177,6 +177,18 @@ hipError_t launch_post_res_next(const FusedPlan &p, int n, int mode, int64_t B, 
                                 const void *phi_next, void *ws_base, hipStream_t st,
                                 const PreOut *pre_out = nullptr);
 
+// Single-slice layer calls in one kernel (mhc_layer_small.hip): the one-pass
+// mhc_post_res_coeffs_pre / mhc_coeffs_pre in bf16 for n in {1, 2, 4} at the
+// small-B sizes of mhc_coeffs when a row's n*C channels fit 1024 (C % 8 == 0).
+// One workgroup per 16-row tile; no workspace.
+bool layer_small_fits(int64_t B, int n, int64_t C);
+// apply: mhc_post_res_coeffs_pre (X = X_t, F = F_out, H, Y = X_next);
+// otherwise mhc_coeffs_pre (X = X_t; F, H, Y unused).
+hipError_t launch_layer_small(int n, bool apply, int64_t B, int64_t C, const void *X, const void *F,
+                              const float *H, void *Y, const void *phi, float ap, float aq, float ar,
+                              const float *bp, const float *bq, const float *br, float *logits, float *r,
+                              float *Hn, void *F_pre, hipStream_t st);
+
 // Zero-fill [p, p + bytes) (bytes a multiple of 16, p 16-byte aligned) with a
 // small kernel (no memset node if the caller captures a graph).
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t st);

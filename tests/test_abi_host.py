@@ -175,6 +175,11 @@ def test_fused_pre_route_and_workspace(tune):
     one = mhc.mhc_post_res_coeffs_pre_one_pass
     assert one(16384, 4, 7168) and one(4096, 4, 4096) and one(1000, 2, 4096) and one(300, 1, 1024)
     assert not one(64, 4, 7168)          # small B: the two calls
+    # small B with all n*C <= 1024 channels of a row in one slice: the single-slice kernel
+    assert one(64, 4, 256) and one(1, 2, 32) and one(256, 1, 1024) and one(16, 2, 512)
+    assert not one(64, 4, 288) and not one(64, 8, 96)
+    assert mhc.mhc_post_res_coeffs_pre_workspace_size(64, 4, 256) == \
+        mhc.mhc_post_res_coeffs_workspace_size(64, 4, 256)
     assert not one(8192, 8, 4096)        # n = 8: two tiles do not fit LDS
     assert not one(4096, 4, 8704)        # 17 steps of 512 channels per row
     assert not one(0, 4, 7168) and not one(16, 4, 40)
@@ -188,8 +193,11 @@ def test_fused_pre_route_and_workspace(tune):
     assert mhc.mhc_post_res_coeffs_pre_workspace_size(8192, 8, 4096) == \
         mhc.mhc_post_res_coeffs_workspace_size(8192, 8, 4096)
     tune.setenv("MHC_FUSED_PRE", "0")
-    assert not one(16384, 4, 7168)
+    assert not one(16384, 4, 7168) and not one(64, 4, 256)
     assert mhc.mhc_post_res_coeffs_pre_workspace_size(B, n, C) == mhc.mhc_post_res_coeffs_workspace_size(B, n, C)
+    tune.delenv("MHC_FUSED_PRE")
+    tune.setenv("MHC_SMALL_MAX_B", "0")  # no small-B routes: the persistent pass takes the small shape
+    assert one(64, 4, 256)
 
 
 def _fused_pre_fp8(B=16, n=4, C=64, ws_bytes=None, **over):
@@ -284,12 +292,17 @@ def test_coeffs_pre_validation(fp8):
 def test_coeffs_pre_route_and_workspace(tune):
     for k in ("MHC_FUSED_PRE", "MHC_SMALL_MAX_B", "MHC_FUSED_FP8"):
         tune.delenv(k, raising=False)
-    for one, size, coeffs_size in (
-            (mhc.mhc_coeffs_pre_one_pass, mhc.mhc_coeffs_pre_workspace_size, mhc.mhc_coeffs_workspace_size),
-            (mhc.mhc_coeffs_pre_fp8_one_pass, mhc.mhc_coeffs_pre_fp8_workspace_size,
+    for fp8, one, size, coeffs_size in (
+            (False, mhc.mhc_coeffs_pre_one_pass, mhc.mhc_coeffs_pre_workspace_size, mhc.mhc_coeffs_workspace_size),
+            (True, mhc.mhc_coeffs_pre_fp8_one_pass, mhc.mhc_coeffs_pre_fp8_workspace_size,
              mhc.mhc_coeffs_fp8_workspace_size)):
         assert one(16384, 4, 7168) and one(4096, 4, 4096) and one(1000, 2, 4096) and one(300, 1, 1024)
         assert not one(64, 4, 7168)          # small B: mhc_coeffs then mhc_pre
+        # small B, one slice (n*C <= 1024, C % 8 == 0): the single-slice kernel in bf16 only
+        for shape in ((64, 4, 256), (7, 4, 48), (256, 1, 1008)):
+            assert bool(one(*shape)) == (not fp8)
+            assert size(*shape) == coeffs_size(*shape)
+        assert not one(64, 4, 264) and not one(64, 8, 64)
         assert not one(8192, 8, 4096)        # n = 8
         assert not one(4096, 4, 8704)        # 17 steps of 512 channels per row
         assert not one(4096, 4, 7184)        # C % 32 != 0

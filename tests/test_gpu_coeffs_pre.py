@@ -12,8 +12,10 @@ Checks, for every shape, in bf16 and in E4M3:
   the coefficients against mhc_coeffs (mhc_coeffs_fp8) on X_t up to fp32
               summation order.
 
-Routes: "default" (one pass above 256 rows for n <= 4, C % 32 == 0 and at
-most sixteen 512-channel steps per row; mhc_coeffs then mhc_pre otherwise),
+Routes: "default" (bf16 up to 256 rows at n <= 4 with n*C <= 1024: the
+single-slice kernel of mhc_layer_small.hip; one pass above 256 rows for
+n <= 4, C % 32 == 0 and at most sixteen 512-channel steps per row; mhc_coeffs
+then mhc_pre otherwise),
 "onepass" (small-B limit 0, so the one-pass kernel also runs the small shapes
 it can take) and "twocalls" (MHC_FUSED_PRE=0).
 """
@@ -203,6 +205,8 @@ def test_route_query(tune):
         assert not q(8192, 8, 4096)     # n = 8
         assert not q(4096, 4, 8704)     # 17 steps per row
         assert not q(4096, 4, 7184)     # C % 32 != 0
+    assert mhc.mhc_coeffs_pre_one_pass(64, 4, 256)           # small B, one slice: bf16 only
+    assert not mhc.mhc_coeffs_pre_fp8_one_pass(64, 4, 256)
     tune.setenv("MHC_FUSED_PRE", "0")
     assert not mhc.mhc_coeffs_pre_one_pass(16384, 4, 7168)
     assert not mhc.mhc_coeffs_pre_fp8_one_pass(16384, 4, 7168)
@@ -212,7 +216,8 @@ def test_route_query(tune):
 # steps per row, n = 1, 2, 4; n = 8, C % 32 != 0 and 17 steps take the
 # two calls.
 RAGGED = [(77, 4, 544), (1, 4, 32), (33, 1, 64), (65, 2, 2080), (300, 4, 1536), (16, 2, 512),
-          (257, 4, 8192), (19, 4, 3104), (130, 8, 96), (21, 4, 8704), (513, 2, 4096), (300, 4, 1040)]
+          (257, 4, 8192), (19, 4, 3104), (130, 8, 96), (21, 4, 8704), (513, 2, 4096), (300, 4, 1040),
+          (7, 4, 48), (250, 1, 1008), (256, 2, 512)]
 
 
 @pytest.mark.parametrize("dt", ["bf16", "fp8"])

@@ -14,10 +14,11 @@ Checks, for every shape:
   the coefficients against mhc_coeffs on X_next up to fp32 summation order.
 The next layer has its own phi and biases (a second seeded draw).
 
-Routes: "default" (one pass above 256 rows for n <= 4 and at most sixteen
-512-channel steps per row; the two calls otherwise) and "onepass", which
-lowers the small-B limit to 0 so that the one-pass kernel also runs every
-small shape it can take.
+Routes: "default" (up to 256 rows at n <= 4 with n*C <= 1024 the
+single-slice kernel of mhc_layer_small.hip; one pass above 256 rows for
+n <= 4 and at most sixteen 512-channel steps per row; the two calls
+otherwise) and "onepass", which lowers the small-B limit to 0 so that the
+one-pass kernel also runs every small shape it can take.
 """
 
 import sys
@@ -191,6 +192,7 @@ def test_route_query(tune):
     assert mhc.mhc_post_res_coeffs_pre_one_pass(16384, 4, 7168)
     assert mhc.mhc_post_res_coeffs_pre_one_pass(4096, 4, 4096)
     assert not mhc.mhc_post_res_coeffs_pre_one_pass(64, 4, 7168)      # small B
+    assert mhc.mhc_post_res_coeffs_pre_one_pass(64, 4, 256)           # small B, one slice
     assert not mhc.mhc_post_res_coeffs_pre_one_pass(8192, 8, 4096)    # n = 8
     assert not mhc.mhc_post_res_coeffs_pre_one_pass(4096, 4, 8704)    # 17 steps per row
     tune.setenv("MHC_FUSED_PRE", "0")
@@ -202,7 +204,7 @@ def test_route_query(tune):
 # two-call route.
 RAGGED = [(77, 4, 544), (1, 4, 32), (33, 1, 64), (65, 2, 2080), (200, 4, 1056), (300, 4, 1536),
           (16, 2, 512), (5, 1, 1024), (257, 4, 8192), (40, 4, 8192), (19, 4, 3104), (130, 8, 96),
-          (21, 4, 8704), (513, 2, 4096)]
+          (21, 4, 8704), (513, 2, 4096), (256, 4, 256), (250, 1, 992)]
 
 
 @pytest.mark.parametrize("B,n,C", RAGGED, ids=[f"B{b}n{n}C{c}" for b, n, c in RAGGED])
