@@ -10,12 +10,15 @@
 // Grid: (16-row tiles) x (K-slices of `kslice` elements), 4 waves each.
 //   product  the workgroup stages its slice of phi [kslice, N] in LDS with
 //            16-byte loads (the rows of a slice are one contiguous block of
-//            phi, so no packed copy is needed); wave w takes k-steps
-//            w*KSW .. w*KSW+KSW-1 of the slice, with its A operands (16 rows x
-//            8 consecutive k per lane) loaded straight from X_t, all of them
-//            issued before the first multiply, and B operands gathered from
-//            LDS.  v_mfma_f32_16x16x32_bf16 accumulates the logits and the
-//            Gram block whose diagonal is the sum of squares.
+//            phi, so no packed copy is needed), transposed on the way in so
+//            that a column's k values are contiguous and each B operand is
+//            one 16-byte LDS read; wave w takes k-steps w*KSW .. w*KSW+KSW-1
+//            of the slice, with its A operands (16 rows x 8 consecutive k per
+//            lane) loaded straight from X_t, all of them issued before the
+//            first multiply.  v_mfma_f32_16x16x32_bf16 accumulates the logits
+//            and the Gram block whose diagonal is the sum of squares.  The
+//            biases are staged in LDS at the start, so the finish waits on
+//            no global load.
 //   partial  the 4 waves' sums are added through LDS in wave order and the
 //            tile's [16, N+1] partial is written to the workspace [S, B, N+1].
 //   arrival  each workgroup writes its partial with agent-scope stores (they
@@ -32,8 +35,9 @@
 //            read-modify-write, no fence that writes back the L2.
 //
 // fp32 phi (the *_phi32 calls): the slice is split while it is staged into
-// two bf16 arrays, phi_hi = bf16(phi) and phi_lo = bf16(phi - phi_hi), and
-// every block takes two MFMAs, X.phi_hi + X.phi_lo, into one accumulator.
+// two bf16 arrays, phi_hi = bf16(phi) and phi_lo = bf16(phi - phi_hi), kept
+// row-major (each B operand gathered from 8 two-byte LDS reads), and every
+// block takes two MFMAs, X.phi_hi + X.phi_lo, into one accumulator.
 //
 // The epoch is a process-wide 64-bit counter from a start that differs
 // between runs, so flags left in a workspace by earlier calls (or any other
@@ -60,10 +64,19 @@ struct SmallTile {
   static constexpr int RS = NB * 16 + 1;            // reduction row stride; Gram sum at NB*16
   static constexpr int KS = kSmallKSlice<NS>();     // K elements per slice (at most)
   static constexpr int KSW = KS / 128;              // k-steps per wave (4 waves x 32 k)
-  static constexpr int PIECES = KS * N / 8;           // 16-byte pieces of a phi slice
-  static constexpr int PPT = (PIECES + 255) / 256;     // ... per thread
   static constexpr int EPT = (16 * NP + 255) / 256;    // tile sums per thread in the combine
   static_assert(KS % 128 == 0, "slice splits evenly over 4 waves");
+  // Transposed bf16 staging: column col's k values at [col * LDK + k].  A unit
+  // is G consecutive k of CW columns: 8 columns (G = 4) when N % 8 == 0, one
+  // 16-byte piece per k row; otherwise all N columns of G = 8 rows (G*N/8
+  // contiguous pieces).
+  static constexpr int LDK = KS + 8;
+  static constexpr bool CHUNKED = N % 8 == 0;
+  static constexpr int G = CHUNKED ? 4 : 8;
+  static constexpr int CW = CHUNKED ? 8 : N;
+  static constexpr int UP = G * CW / 8;                  // 16-byte pieces per unit
+  static constexpr int UNITS = (KS / G) * (N / CW);
+  static constexpr int UPT = (UNITS + 255) / 256;        // units per thread
 };
 
 template <int NS, bool FP8X, bool P32>
@@ -74,9 +87,10 @@ __global__ __launch_bounds__(256) void coeffs_small_kernel(
     const float *__restrict__ b_res, float *__restrict__ logits, float *__restrict__ r_out,
     float *__restrict__ H, float *ws, unsigned long long *flags, unsigned long long epoch) {
   using T = SmallTile<NS>;
-  __shared__ __attribute__((aligned(16))) uint16_t phs[P32 ? 2 : 1][T::KS * T::N];
+  __shared__ __attribute__((aligned(16))) uint16_t phs[P32 ? 2 : 1][P32 ? T::KS * T::N : T::N * T::LDK];
   __shared__ float red[4 * 16 * T::RS];
   __shared__ float sums[16 * T::NP];
+  __shared__ float bsh[T::N];  // b_pre, b_post, b_res
   __shared__ int is_last;
 
   const int tid = threadIdx.x;
@@ -87,6 +101,7 @@ __global__ __launch_bounds__(256) void coeffs_small_kernel(
   const int row0 = tile * 16;
   const int k_lo = s * T::KS;
   const int k_hi = min(K, k_lo + T::KS);
+  if (tid < T::N) bsh[tid] = tid < NS ? b_pre[tid] : (tid < 2 * NS ? b_post[tid - NS] : b_res[tid - 2 * NS]);
 
   // A operands of this wave's k-steps: row row0+m (rows past B read row
   // B-1; their results are not written), k = step*32 + 8g .. +7 (zero past
@@ -107,22 +122,52 @@ __global__ __launch_bounds__(256) void coeffs_small_kernel(
   }
 
   // phi rows [k_lo, k_hi) into LDS, zero past k_hi.  (k_hi - k_lo) is a
-  // multiple of 8, so the valid bytes are a whole number of 16-byte pieces.
-  // All of a thread's loads are issued before the first LDS store.
+  // multiple of 8, so a unit's G rows lie wholly below k_hi or wholly past
+  // it.  All of a thread's loads are issued before the first LDS store.
   if constexpr (!P32) {
-    const int valid = (k_hi - k_lo) * T::N * 2;
-    const char *src = reinterpret_cast<const char *>(static_cast<const uint16_t *>(phi_v) + (size_t)k_lo * T::N);
-    char *dst = reinterpret_cast<char *>(phs[0]);
-    u32x4 v[T::PPT];
+    const uint16_t *src = static_cast<const uint16_t *>(phi_v) + (size_t)k_lo * T::N;
+    constexpr int CPR = T::N / T::CW;  // column chunks per k row
+    u32x4 v[T::UPT][T::UP];
 #pragma unroll
-    for (int q = 0; q < T::PPT; ++q) {
-      const int p = tid + 256 * q;
-      v[q] = load16(src + (size_t)min(p * 16, valid - 16));
+    for (int q = 0; q < T::UPT; ++q) {
+      const int u = min(tid + 256 * q, T::UNITS - 1);
+      const int kg = u / CPR, c0 = (u - kg * CPR) * T::CW;
+      const int k0 = k_lo + kg * T::G < k_hi ? kg * T::G : 0;  // units past k_hi read row 0 (zeroed below)
+#pragma unroll
+      for (int t = 0; t < T::UP; ++t) {
+        // CHUNKED: piece t is row k0+t, columns c0..c0+7; otherwise piece t
+        // of the G full rows from k0.
+        const size_t off = T::CHUNKED ? (size_t)(k0 + t) * T::N + c0 : (size_t)k0 * T::N + 8 * t;
+        v[q][t] = load16(src + off);
+      }
     }
 #pragma unroll
-    for (int q = 0; q < T::PPT; ++q) {
-      const int p = tid + 256 * q;
-      if (p < T::PIECES) *reinterpret_cast<u32x4 *>(dst + p * 16) = p * 16 < valid ? v[q] : u32x4{0u, 0u, 0u, 0u};
+    for (int q = 0; q < T::UPT; ++q) {
+      const int u = tid + 256 * q;
+      if (u < T::UNITS) {
+        const int kg = u / CPR, c0 = (u - kg * CPR) * T::CW;
+        const int k0 = kg * T::G;
+        const bool valid = k_lo + k0 < k_hi;
+#pragma unroll
+        for (int j = 0; j < T::CW; ++j) {
+          uint32_t w[T::G / 2];
+#pragma unroll
+          for (int t = 0; t < T::G / 2; ++t) {
+            // elements (k0 + 2t, c0 + j) and (k0 + 2t + 1, c0 + j) of the unit
+            const int el = T::CHUNKED ? (2 * t) * 8 + j : (2 * t) * T::N + j;
+            const int eh = T::CHUNKED ? (2 * t + 1) * 8 + j : (2 * t + 1) * T::N + j;
+            const uint32_t lo = (v[q][el >> 3][(el & 7) >> 1] >> (16 * (el & 1))) & 0xffffu;
+            const uint32_t hi = (v[q][eh >> 3][(eh & 7) >> 1] >> (16 * (eh & 1))) & 0xffffu;
+            w[t] = valid ? (lo | (hi << 16)) : 0u;
+          }
+          uint16_t *dst = phs[0] + (c0 + j) * T::LDK + k0;
+          if constexpr (T::G == 4) {
+            *reinterpret_cast<u32x2 *>(dst) = u32x2{w[0], w[1]};
+          } else {
+            *reinterpret_cast<u32x4 *>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+          }
+        }
+      }
     }
   } else {
     // fp32 phi: 16-byte pieces of 4 values, split into hi and lo halves of 8
@@ -167,17 +212,23 @@ __global__ __launch_bounds__(256) void coeffs_small_kernel(
 #pragma unroll
     for (int nb = 0; nb < T::NB; ++nb) {
       const int col = nb * 16 + m;
+      if constexpr (!P32) {
+        const u32x4 w = col < T::N ? *reinterpret_cast<const u32x4 *>(phs[0] + col * T::LDK + kk)
+                                   : u32x4{0u, 0u, 0u, 0u};
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q], __builtin_bit_cast(bf16x8, w), acc[nb], 0, 0, 0);
+      } else {
 #pragma unroll
-      for (int part = 0; part < (P32 ? 2 : 1); ++part) {
-        uint32_t w[4];
+        for (int part = 0; part < 2; ++part) {
+          uint32_t w[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t lo = col < T::N ? phs[part][(kk + 2 * j) * T::N + col] : 0u;
-          const uint32_t hi = col < T::N ? phs[part][(kk + 2 * j + 1) * T::N + col] : 0u;
-          w[j] = lo | (hi << 16);
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t lo = col < T::N ? phs[part][(kk + 2 * j) * T::N + col] : 0u;
+            const uint32_t hi = col < T::N ? phs[part][(kk + 2 * j + 1) * T::N + col] : 0u;
+            w[j] = lo | (hi << 16);
+          }
+          const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q], b, acc[nb], 0, 0, 0);
         }
-        const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q], b, acc[nb], 0, 0, 0);
       }
     }
     gram = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q], a[q], gram, 0, 0, 0);
@@ -209,7 +260,7 @@ __global__ __launch_bounds__(256) void coeffs_small_kernel(
     const int lr = tid / NS, i = tid % NS;
     if (lr < rows)
       finish_row<NS>(sums + lr * T::NP, row0 + lr, i, inv_k, alpha_pre, alpha_post, alpha_res,
-                     b_pre, b_post, b_res, r_out, H);
+                     bsh, bsh + NS, bsh + 2 * NS, r_out, H);
     return;
   }
   for (int e = tid; e < 16 * T::NP; e += 256) {
@@ -277,7 +328,7 @@ __global__ __launch_bounds__(256) void coeffs_small_kernel(
   const int lr = tid / NS, i = tid % NS;
   if (lr < rows)
     finish_row<NS>(sums + lr * T::NP, row0 + lr, i, inv_k, alpha_pre, alpha_post, alpha_res,
-                   b_pre, b_post, b_res, r_out, H);
+                   bsh, bsh + NS, bsh + 2 * NS, r_out, H);
 }
 
 // Process-wide call epoch, from a start that differs between runs.
