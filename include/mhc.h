@@ -526,6 +526,8 @@ int mhc_lazy_prenorm_gemm(int64_t M, int64_t N, int64_t K, const void *A, const 
  *   MHC_FUSED_FIXED  0 / 1: the fused kernel's fixed-slice layout off / on
  *   MHC_FUSED_SPU, MHC_FUSED_WGS   fused kernel's steps per unit, grid cap
  *   MHC_FUSED_PRE    0: mhc_post_res_coeffs_pre(_fp8) as two calls
+ *   MHC_APPLY_SMALL  0: small-B bf16 mhc_post_res_coeffs as the apply
+ *                    kernel, then the small-B coefficient kernel
  *   MHC_LPN_ALGO     1: the four-wave Lazy Pre-Norm GEMM kernel
  * Every route computes the same results up to fp32 summation order (the
  * fused calls' X_next and F_pre_next bitwise).  The workspace-size functions

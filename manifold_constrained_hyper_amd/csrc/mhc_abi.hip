@@ -329,6 +329,11 @@ int post_res_coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t
                           : mhc::launch_pre(n, B, C, X_next, H_next, F_pre_next, s));
   }
   if (route != FusedRoute::kFused) {
+    if (route == FusedRoute::kSmall && !e.fp8 && !e.phi32 && mhc::tune(mhc::kTuneApplySmall) != 0 &&
+        mhc::apply_coeffs_small_fits(B, n, C))  // the apply and the coefficients in one kernel
+      return from_hip(mhc::launch_apply_coeffs_small(mhc::plan_coeffs_small(B, n, C), n, B, C, X_t, F_out, H,
+                                                     X_next, phi_next, alpha_pre, alpha_post, alpha_res, b_pre,
+                                                     b_post, b_res, logits_next, r_next, H_next, workspace, s));
     st = from_hip(e.fp8 ? mhc::launch_post_res_fp8(n, B, C, X_t, F_out, H, X_next, s)
                         : mhc::launch_post_res(n, B, C, X_t, F_out, H, X_next, s));
     if (st != MHC_OK) return st;
@@ -463,6 +468,7 @@ constexpr TuneName kTuneNames[] = {
     {"MHC_FUSED_PRE", mhc::kTuneFusedPre},    {"MHC_LPN_ALGO", mhc::kTuneLpnAlgo},
     {"MHC_GEMM_KC", mhc::kTuneGemmKc},        {"MHC_GEMM_STAGES", mhc::kTuneGemmStages},
     {"MHC_GEMM_WAVES", mhc::kTuneGemmWaves},  {"MHC_GEMM_XREG", mhc::kTuneGemmXreg},
+    {"MHC_APPLY_SMALL", mhc::kTuneApplySmall},
 };
 static_assert(sizeof(kTuneNames) / sizeof(kTuneNames[0]) == mhc::kTuneCount, "one name per key");
 

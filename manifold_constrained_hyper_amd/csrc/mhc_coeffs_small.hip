@@ -331,8 +331,10 @@ __global__ __launch_bounds__(256) void coeffs_small_kernel(
                    bsh, bsh + NS, bsh + 2 * NS, r_out, H);
 }
 
+}  // namespace
+
 // Process-wide call epoch, from a start that differs between runs.
-unsigned long long next_epoch() {
+unsigned long long next_call_epoch() {
   static std::atomic<unsigned long long> counter{
       (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() * 0x9E3779B97F4A7C15ull};
   unsigned long long e;
@@ -341,6 +343,8 @@ unsigned long long next_epoch() {
   } while (e == 0);
   return e;
 }
+
+namespace {
 
 template <int NS, bool FP8X, bool P32>
 hipError_t launch_small_n(const SmallPlan &p, int64_t B, int64_t C, const void *X,
@@ -354,7 +358,7 @@ hipError_t launch_small_n(const SmallPlan &p, int64_t B, int64_t C, const void *
       static_cast<const uint8_t *>(X), phi, (int)B,
       (int)(NS * C), p.split, inv_k, ap, aq, ar, bp, bq, br, logits, r, H,
       reinterpret_cast<float *>(base), reinterpret_cast<unsigned long long *>(base + p.ctr_offset),
-      next_epoch());
+      next_call_epoch());
   return hipGetLastError();
 }
 

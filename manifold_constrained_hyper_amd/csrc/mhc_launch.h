@@ -29,6 +29,7 @@ enum TuneKey : int {
   kTuneGemmStages,     // 5 or 6: its ring depth
   kTuneGemmWaves,      // 4 or 8: wavefronts per workgroup of the LDS-staged split-K product
   kTuneGemmXreg,       // 2: bf16 split-K product with X and phi through two register sets (n = 4, 8)
+  kTuneApplySmall,     // 0: small-B bf16 mhc_post_res_coeffs as the apply kernel, then coeffs_small
   kTuneCount
 };
 // Current value of a key; -1 when unset.
@@ -227,6 +228,19 @@ hipError_t launch_coeffs_small(const SmallPlan &p, int n, bool fp8_x, int64_t B,
                                const float *b_res, float *logits, float *r, float *H, void *ws,
                                hipStream_t st,
                                bool phi32 = false);
+
+// mhc_post_res_coeffs at the small-B sizes in one kernel (mhc_layer_small.hip):
+// bf16, n in {1, 2, 4}, C % 8 == 0; the apply, then split-K over channel
+// ranges of all n streams with the last workgroup of a tile to arrive
+// finishing it.  Workspace and flags as coeffs_small (plan_coeffs_small gives
+// the same slice count, ceil(n*C / 1024)).
+bool apply_coeffs_small_fits(int64_t B, int n, int64_t C);
+hipError_t launch_apply_coeffs_small(const SmallPlan &p, int n, int64_t B, int64_t C, const void *X,
+                                     const void *F, const float *H, void *Y, const void *phi, float ap, float aq,
+                                     float ar, const float *bp, const float *bq, const float *br, float *logits,
+                                     float *r, float *Hn, void *ws, hipStream_t st);
+// Process-wide 64-bit call epoch of the small-B arrival flags (never 0).
+unsigned long long next_call_epoch();
 
 // tree: add the split partials as the 16-slot balanced tree (split <= 16,
 // n <= 4), the order of the fused kernel's pre-mix mode.

@@ -58,38 +58,34 @@ struct LayerTile {
   static_assert(NG <= 256 && (G * N) % 8 == 0, "phi staging groups");
 };
 
+// The part both kernels share, for the workgroup's 16-row tile (rows from
+// row0) and channels c0 .. c0 + CW-1 of every stream: loads, phi staged
+// transposed in LDS, the apply (APPLY: X_{t+1} into xn and stored to Y;
+// otherwise xn = X_t), the product and the four waves' partial sums in red
+// (row r, column col at red[(w*16 + r)*RS + col], the Gram sum at column
+// NB*16).  Ends with a barrier.
 template <int NS, bool APPLY>
-__global__ __launch_bounds__(256) void layer_small_kernel(
-    const uint16_t *__restrict__ X, const uint16_t *__restrict__ F, const float *__restrict__ H,
-    uint16_t *__restrict__ Y, const uint16_t *__restrict__ phi, int B, int C, float inv_k,
-    float alpha_pre, float alpha_post, float alpha_res, const float *__restrict__ b_pre,
-    const float *__restrict__ b_post, const float *__restrict__ b_res, float *__restrict__ logits,
-    float *__restrict__ r_out, float *__restrict__ Hn, uint16_t *__restrict__ F_pre) {
+__device__ __forceinline__ void layer_front(const uint16_t *__restrict__ X, const uint16_t *__restrict__ F,
+                                            const float *__restrict__ H, uint16_t *__restrict__ Y,
+                                            const uint16_t *__restrict__ phi, int B, int C, int row0, int c0,
+                                            uint16_t *phs, float *red, u32x4 (&xn)[LayerTile<NS>::TSW][NS],
+                                            int (&cl)[LayerTile<NS>::TSW]) {
   using T = LayerTile<NS>;
-  __shared__ __attribute__((aligned(16))) uint16_t phs[NS * T::N * T::LDK];  // [stream][column][channel]
-  __shared__ float red[4 * 16 * T::RS];
-  __shared__ float sums[16 * T::NP];
-  __shared__ float hpre[16 * NS];
-  __shared__ float bsh[T::N];  // b_pre, b_post, b_res
-
   const int tid = threadIdx.x;
   const int wave = uniform(tid >> 6);
   const int lane = tid & 63;
   const int m = lane & 15, g = lane >> 4;
-  const int row0 = blockIdx.x * 16;
   const int row = row0 + m;
   const int rr = min(row, B - 1);  // rows past B repeat row B-1 (nothing of theirs is stored)
   const int K = NS * C;
   const bool live = row < B;
-  if (tid < T::N) bsh[tid] = tid < NS ? b_pre[tid] : (tid < 2 * NS ? b_post[tid - NS] : b_res[tid - 2 * NS]);
 
   // ---- loads: this lane's X (and F_out, coefficients), then phi
   u32x4 xv[T::TSW][NS];
   [[maybe_unused]] u32x4 fv[T::TSW];
-  int cl[T::TSW];
 #pragma unroll
   for (int q = 0; q < T::TSW; ++q) {
-    const int c = 32 * (wave * T::TSW + q) + 8 * g;
+    const int c = c0 + 32 * (wave * T::TSW + q) + 8 * g;
     cl[q] = c;
     const int cc = min(c, C - 8);
 #pragma unroll
@@ -107,16 +103,17 @@ __global__ __launch_bounds__(256) void layer_small_kernel(
     }
   }
   {
-    // phi rows i*C .. i*C + C-1 of each stream, transposed into LDS: element
-    // (channel k, column col) of stream i goes to phs[(i*N + col)*LDK + k],
-    // zero for k >= C.  Thread t takes group t: G consecutive channels of one
-    // stream (G*N elements, GP contiguous 16-byte pieces), and writes each
-    // column's G channels with one 8- or 16-byte LDS store.  C % 8 == 0, so a
-    // group lies wholly below C or wholly past it.
+    // phi rows i*C + c0 .. i*C + c0 + CW-1 of each stream, transposed into
+    // LDS: element (channel c0 + k, column col) of stream i goes to
+    // phs[(i*N + col)*LDK + k], zero for c0 + k >= C.  Thread t takes group t:
+    // G consecutive channels of one stream (G*N elements, GP contiguous
+    // 16-byte pieces), and writes each column's G channels with one 8- or
+    // 16-byte LDS store.  C % 8 == 0, so a group lies wholly below C or wholly
+    // past it.
     const int gi = tid;
     const int i = min(gi / T::GPS, NS - 1), k0 = (gi - i * T::GPS) * T::G;
-    const bool gv = gi < T::NG && k0 < C;
-    const char *src = reinterpret_cast<const char *>(phi + ((size_t)i * C + (gv ? k0 : 0)) * T::N);
+    const bool gv = gi < T::NG && c0 + k0 < C;
+    const char *src = reinterpret_cast<const char *>(phi + ((size_t)i * C + c0 + (gv ? k0 : 0)) * T::N);
     u32x4 v[T::GP];
 #pragma unroll
     for (int q = 0; q < T::GP; ++q) v[q] = load16(src + 16 * q);
@@ -142,7 +139,6 @@ __global__ __launch_bounds__(256) void layer_small_kernel(
   }
 
   // ---- apply (post_res_kernel's arithmetic) and store X_{t+1}
-  u32x4 xn[T::TSW][NS];
 #pragma unroll
   for (int q = 0; q < T::TSW; ++q) {
     if constexpr (APPLY) {
@@ -207,6 +203,32 @@ __global__ __launch_bounds__(256) void layer_small_kernel(
     if (g == (m >> 2)) rw[m * T::RS + T::NB * 16] = gram[m & 3];
   }
   __syncthreads();
+}
+
+template <int NS, bool APPLY>
+__global__ __launch_bounds__(256) void layer_small_kernel(
+    const uint16_t *__restrict__ X, const uint16_t *__restrict__ F, const float *__restrict__ H,
+    uint16_t *__restrict__ Y, const uint16_t *__restrict__ phi, int B, int C, float inv_k,
+    float alpha_pre, float alpha_post, float alpha_res, const float *__restrict__ b_pre,
+    const float *__restrict__ b_post, const float *__restrict__ b_res, float *__restrict__ logits,
+    float *__restrict__ r_out, float *__restrict__ Hn, uint16_t *__restrict__ F_pre) {
+  using T = LayerTile<NS>;
+  __shared__ __attribute__((aligned(16))) uint16_t phs[NS * T::N * T::LDK];  // [stream][column][channel]
+  __shared__ float red[4 * 16 * T::RS];
+  __shared__ float sums[16 * T::NP];
+  __shared__ float hpre[16 * NS];
+  __shared__ float bsh[T::N];  // b_pre, b_post, b_res
+
+  const int tid = threadIdx.x;
+  const int m = tid & 15;
+  const int row0 = blockIdx.x * 16;
+  const int row = row0 + m;
+  const bool live = row < B;
+  if (tid < T::N) bsh[tid] = tid < NS ? b_pre[tid] : (tid < 2 * NS ? b_post[tid - NS] : b_res[tid - 2 * NS]);
+
+  u32x4 xn[T::TSW][NS];
+  int cl[T::TSW];
+  layer_front<NS, APPLY>(X, F, H, Y, phi, B, C, row0, 0, phs, red, xn, cl);
 
   // ---- sums: the four waves' partials, added in wave order
   for (int e = tid; e < 16 * T::NP; e += 256) {
@@ -254,6 +276,138 @@ __global__ __launch_bounds__(256) void layer_small_kernel(
                    bsh + 2 * NS, r_out, Hn);
 }
 
+// mhc_post_res_coeffs at the small-B sizes, split over K: workgroup (tile,
+// s) runs layer_front for channels s*CW .. s*CW + CW-1 of every stream
+// (X_{t+1} stored), writes its [16, N+1] partial to the workspace
+// [S, B, N+1] with agent-scope stores, waits for them, then writes the call's
+// epoch into its flag (one per tile and slice) and waits for that too.  Wave
+// 0 reads the tile's S flags; a workgroup that finds all of them carrying the
+// epoch adds the S partials in slice order 0..S-1, writes the logits, clears
+// the flags (so a replay of the same launch starts clean) and runs the finish.
+// Every workgroup's flag is complete before it reads the others', so the last
+// to arrive always sees all flags, and two that both see them write the same
+// bits.  No workgroup waits for another.  With one slice the workgroup
+// finishes from LDS.
+template <int NS>
+__global__ __launch_bounds__(256) void apply_coeffs_small_kernel(
+    const uint16_t *__restrict__ X, const uint16_t *__restrict__ F, const float *__restrict__ H,
+    uint16_t *__restrict__ Y, const uint16_t *__restrict__ phi, int B, int C, int S, float inv_k,
+    float alpha_pre, float alpha_post, float alpha_res, const float *__restrict__ b_pre,
+    const float *__restrict__ b_post, const float *__restrict__ b_res, float *__restrict__ logits,
+    float *__restrict__ r_out, float *__restrict__ Hn, float *__restrict__ ws,
+    unsigned long long *__restrict__ flags, unsigned long long epoch) {
+  using T = LayerTile<NS>;
+  constexpr int EPT = (16 * T::NP + 255) / 256;  // tile sums per thread in the combine
+  __shared__ __attribute__((aligned(16))) uint16_t phs[NS * T::N * T::LDK];  // [stream][column][channel]
+  __shared__ float red[4 * 16 * T::RS];
+  __shared__ float sums[16 * T::NP];
+  __shared__ float bsh[T::N];  // b_pre, b_post, b_res
+  __shared__ int is_last;
+
+  const int tid = threadIdx.x;
+  const int wave = uniform(tid >> 6);
+  const int lane = tid & 63;
+  const int tile = blockIdx.x, s = blockIdx.y;
+  const int row0 = tile * 16;
+  const int rows = min(16, B - row0);
+  if (tid < T::N) bsh[tid] = tid < NS ? b_pre[tid] : (tid < 2 * NS ? b_post[tid - NS] : b_res[tid - 2 * NS]);
+
+  u32x4 xn[T::TSW][NS];
+  int cl[T::TSW];
+  layer_front<NS, true>(X, F, H, Y, phi, B, C, row0, s * T::CW, phs, red, xn, cl);
+
+  const size_t slice = (size_t)B * T::NP;
+  if (S == 1) {
+    for (int e = tid; e < rows * T::NP; e += 256) {
+      const int r = e / T::NP, col = e - r * T::NP;
+      const int rcol = col < T::N ? col : T::NB * 16;
+      const float v = ((red[(0 * 16 + r) * T::RS + rcol] + red[(1 * 16 + r) * T::RS + rcol]) +
+                       red[(2 * 16 + r) * T::RS + rcol]) + red[(3 * 16 + r) * T::RS + rcol];
+      sums[e] = v;
+      if (col < T::N) logits[(size_t)(row0 + r) * T::N + col] = v;
+    }
+  } else {
+    for (int e = tid; e < 16 * T::NP; e += 256) {
+      const int r = e / T::NP, col = e - r * T::NP;
+      const int rcol = col < T::N ? col : T::NB * 16;
+      const float v = ((red[(0 * 16 + r) * T::RS + rcol] + red[(1 * 16 + r) * T::RS + rcol]) +
+                       red[(2 * 16 + r) * T::RS + rcol]) + red[(3 * 16 + r) * T::RS + rcol];
+      if (row0 + r < B)
+        __hip_atomic_store(ws + (size_t)s * slice + (size_t)(row0 + r) * T::NP + col, v, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // Arrival: this workgroup's partial is complete, then its flag is.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    unsigned long long *tflags = flags + (size_t)tile * S;
+    if (wave == 0) {
+      if (lane == 0) __hip_atomic_store(tflags + s, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      const unsigned long long f =
+          __hip_atomic_load(tflags + min(lane, S - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool arrived = lane >= S || f == epoch;
+      const unsigned long long missing = __builtin_amdgcn_ballot_w64(!arrived);  // whole wave votes
+      if (lane == 0) is_last = missing == 0;
+    }
+    __syncthreads();
+    if (!is_last) return;
+
+    // Last slice of the tile to arrive: the S partials in slice order (a
+    // thread's loads for 16 slices issued before any is added).
+    const float *base = ws + (size_t)row0 * T::NP;
+    const int nel = rows * T::NP;
+    float tot[EPT];
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) tot[q] = 0.f;
+    for (int s0 = 0; s0 < S; s0 += 16) {
+      float v[16][EPT];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+#pragma unroll
+        for (int q = 0; q < EPT; ++q)
+          v[j][q] = __hip_atomic_load(base + (size_t)min(s0 + j, S - 1) * slice + min(tid + 256 * q, nel - 1),
+                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+#pragma unroll
+        for (int q = 0; q < EPT; ++q)
+          if (s0 + j < S) tot[q] += v[j][q];
+    }
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      const int e = tid + 256 * q;
+      if (e < nel) {
+        sums[e] = tot[q];
+        const int r = e / T::NP, col = e - r * T::NP;
+        if (col < T::N) logits[(size_t)(row0 + r) * T::N + col] = tot[q];
+      }
+    }
+    // Every slice has arrived, so no workgroup reads the tile's flags any more.
+    if (wave == 0 && lane < S)
+      __hip_atomic_store(tflags + lane, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  const int lr = tid / NS, i = tid % NS;
+  if (lr < rows)
+    finish_row<NS>(sums + lr * T::NP, row0 + lr, i, inv_k, alpha_pre, alpha_post, alpha_res, bsh, bsh + NS,
+                   bsh + 2 * NS, r_out, Hn);
+}
+
+template <int NS>
+hipError_t launch_apply_coeffs_n(const SmallPlan &p, int64_t B, int64_t C, const void *X, const void *F,
+                                 const float *H, void *Y, const void *phi, float ap, float aq, float ar,
+                                 const float *bp, const float *bq, const float *br, float *logits, float *r,
+                                 float *Hn, void *ws_base, hipStream_t st) {
+  char *base = static_cast<char *>(ws_base);
+  const float inv_k = (float)(1.0 / (double)(NS * C));
+  apply_coeffs_small_kernel<NS><<<dim3((uint32_t)p.row_tiles, (uint32_t)p.split), 256, 0, st>>>(
+      static_cast<const uint16_t *>(X), static_cast<const uint16_t *>(F), H, static_cast<uint16_t *>(Y),
+      static_cast<const uint16_t *>(phi), (int)B, (int)C, p.split, inv_k, ap, aq, ar, bp, bq, br, logits, r, Hn,
+      reinterpret_cast<float *>(base), reinterpret_cast<unsigned long long *>(base + p.ctr_offset),
+      next_call_epoch());
+  return hipGetLastError();
+}
+
 template <int NS, bool APPLY>
 hipError_t launch_layer_n(int64_t B, int64_t C, const void *X, const void *F, const float *H, void *Y,
                           const void *phi, float ap, float aq, float ar, const float *bp, const float *bq,
@@ -271,6 +425,24 @@ hipError_t launch_layer_n(int64_t B, int64_t C, const void *X, const void *F, co
 bool layer_small_fits(int64_t B, int n, int64_t C) {
   if (n != 1 && n != 2 && n != 4) return false;
   return B >= 1 && C >= 8 && C % 8 == 0 && C * n <= 1024 && use_coeffs_small(B, n, C);
+}
+
+bool apply_coeffs_small_fits(int64_t B, int n, int64_t C) {
+  if (n != 1 && n != 2 && n != 4) return false;
+  return B >= 1 && C >= 8 && C % 8 == 0 && use_coeffs_small(B, n, C);
+}
+
+hipError_t launch_apply_coeffs_small(const SmallPlan &p, int n, int64_t B, int64_t C, const void *X,
+                                     const void *F, const float *H, void *Y, const void *phi, float ap, float aq,
+                                     float ar, const float *bp, const float *bq, const float *br, float *logits,
+                                     float *r, float *Hn, void *ws, hipStream_t st) {
+  if (!apply_coeffs_small_fits(B, n, C) || p.split != (int)((C * n + 1023) / 1024)) return hipErrorInvalidValue;
+  switch (n) {
+    case 1: return launch_apply_coeffs_n<1>(p, B, C, X, F, H, Y, phi, ap, aq, ar, bp, bq, br, logits, r, Hn, ws, st);
+    case 2: return launch_apply_coeffs_n<2>(p, B, C, X, F, H, Y, phi, ap, aq, ar, bp, bq, br, logits, r, Hn, ws, st);
+    case 4: return launch_apply_coeffs_n<4>(p, B, C, X, F, H, Y, phi, ap, aq, ar, bp, bq, br, logits, r, Hn, ws, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_layer_small(int n, bool apply, int64_t B, int64_t C, const void *X, const void *F,

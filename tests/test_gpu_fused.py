@@ -140,6 +140,28 @@ def test_fused_ragged(B, n, C, route):
     _check(cur, nxt, o, ref, f, list(range(B)), f"B{B}n{n}C{C}")
 
 
+SMALL_SHAPES = [(64, 4, 256), (64, 4, 7168), (77, 4, 544), (1, 4, 32), (33, 1, 64), (65, 2, 2080),
+                (200, 4, 1056), (16, 2, 512), (5, 1, 1024), (256, 4, 7168), (19, 1, 2976)]
+
+
+@pytest.mark.parametrize("apply_small", [1, 0], ids=["one_kernel", "apply_then_coeffs"])
+@pytest.mark.parametrize("B,n,C", SMALL_SHAPES, ids=[f"B{b}n{n}C{c}" for b, n, c in SMALL_SHAPES])
+def test_fused_small_routes(B, n, C, apply_small, tune):
+    """Both small-B routes of bf16 mhc_post_res_coeffs (n <= 4, up to 256 rows):
+    the kernel that applies and forms the coefficients in one launch (split
+    over channel ranges of all n streams, the last workgroup of a tile
+    finishing it), and the apply kernel followed by the small-B coefficient
+    kernel; every row against the oracle."""
+    tune.delenv("MHC_SMALL_MAX_B", raising=False)
+    tune.setenv("MHC_APPLY_SMALL", apply_small)
+    if C % 32:
+        pytest.skip("mhc_post_res_coeffs takes C % 32 == 0")
+    _say(f"fused small route B={B} n={n} C={C} apply_small={apply_small}")
+    cur, nxt = _layers(n, C, B, "student_t4" if B % 2 else "normal", B * 7 + C)
+    o, ref, f = _run(cur, nxt)
+    _check(cur, nxt, o, ref, f, list(range(B)), f"B{B}n{n}C{C} apply_small={apply_small}")
+
+
 def test_fused_deterministic():
     _say("fused determinism")
     cfg = synth.CONFIGS["prefill"]
