@@ -290,22 +290,24 @@ __global__ __launch_bounds__(256) void coeffs_small_kernel(
   if (!is_last) return;
 
   // Last slice of the tile: add the S partials in slice order.  A thread's
-  // loads for 16 slices of all its elements are issued before any is added.
+  // loads for kCombineBatch slices of all its elements are issued before any
+  // is added (one memory round trip up to 32 slices at n <= 4).
   const float *base = ws + (size_t)row0 * T::NP;
   const int nel = rows * T::NP;
+  constexpr int kCombineBatch = combine_batch(T::EPT);
   float tot[T::EPT];
 #pragma unroll
   for (int q = 0; q < T::EPT; ++q) tot[q] = 0.f;
-  for (int s0 = 0; s0 < S; s0 += 16) {
-    float v[16][T::EPT];
+  for (int s0 = 0; s0 < S; s0 += kCombineBatch) {
+    float v[kCombineBatch][T::EPT];
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
+    for (int j = 0; j < kCombineBatch; ++j)
 #pragma unroll
       for (int q = 0; q < T::EPT; ++q)
         v[j][q] = __hip_atomic_load(base + (size_t)min(s0 + j, S - 1) * slice + min(tid + 256 * q, nel - 1),
                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
+    for (int j = 0; j < kCombineBatch; ++j)
 #pragma unroll
       for (int q = 0; q < T::EPT; ++q)
         if (s0 + j < S) tot[q] += v[j][q];

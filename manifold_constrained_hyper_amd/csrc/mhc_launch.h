@@ -214,6 +214,8 @@ template <int NS>
 constexpr int kSmallKSlice() { return NS >= 8 ? 256 : 1024; }  // K per slice: phi slice <= 48 KiB of LDS
 constexpr int64_t kSmallMaxB = 256;     // rows up to which mhc_coeffs takes this path
 constexpr int64_t kSmallMaxSplit = 64;  // ... and K-slices up to which
+// Slices whose partials a small-B finisher loads at once (ept sums per thread).
+constexpr int combine_batch(int ept) { return ept <= 2 ? 32 : 16; }
 struct SmallPlan {
   int split;
   int64_t kslice, row_tiles;

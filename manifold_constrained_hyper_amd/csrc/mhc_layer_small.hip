@@ -298,6 +298,7 @@ __global__ __launch_bounds__(256) void apply_coeffs_small_kernel(
     unsigned long long *__restrict__ flags, unsigned long long epoch) {
   using T = LayerTile<NS>;
   constexpr int EPT = (16 * T::NP + 255) / 256;  // tile sums per thread in the combine
+  constexpr int kCombineBatch = combine_batch(EPT);
   __shared__ __attribute__((aligned(16))) uint16_t phs[NS * T::N * T::LDK];  // [stream][column][channel]
   __shared__ float red[4 * 16 * T::RS];
   __shared__ float sums[16 * T::NP];
@@ -353,22 +354,23 @@ __global__ __launch_bounds__(256) void apply_coeffs_small_kernel(
     if (!is_last) return;
 
     // Last slice of the tile to arrive: the S partials in slice order (a
-    // thread's loads for 16 slices issued before any is added).
+    // thread's loads for kCombineBatch slices issued before any is added:
+    // one memory round trip up to 32 slices at n <= 4).
     const float *base = ws + (size_t)row0 * T::NP;
     const int nel = rows * T::NP;
     float tot[EPT];
 #pragma unroll
     for (int q = 0; q < EPT; ++q) tot[q] = 0.f;
-    for (int s0 = 0; s0 < S; s0 += 16) {
-      float v[16][EPT];
+    for (int s0 = 0; s0 < S; s0 += kCombineBatch) {
+      float v[kCombineBatch][EPT];
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
+      for (int j = 0; j < kCombineBatch; ++j)
 #pragma unroll
         for (int q = 0; q < EPT; ++q)
           v[j][q] = __hip_atomic_load(base + (size_t)min(s0 + j, S - 1) * slice + min(tid + 256 * q, nel - 1),
                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
+      for (int j = 0; j < kCombineBatch; ++j)
 #pragma unroll
         for (int q = 0; q < EPT; ++q)
           if (s0 + j < S) tot[q] += v[j][q];
