@@ -9,10 +9,11 @@ captured.  This test captures three chained layers of mhc_post_res_coeffs_pre
 eager work refills the layer-0 inputs and overwrites every output and the
 workspace with garbage; each replay must reproduce the eager run bitwise.
 
-Shapes: the decode workload (the two-call route: apply, one-launch small-B
-coefficient kernel with its arrival flags, pre-mix) and a prefill-sized shape
-on the one-pass kernel (hand-off records cleared in-graph by the packing
-kernel).  The Lazy Pre-Norm GEMM (one persistent launch) is replayed the same
+Shapes: the decode workload (bf16: the apply and the split-K coefficients in
+one kernel with its arrival flags, then the pre-mix; E4M3: apply, one-launch
+small-B coefficient kernel, pre-mix), the tiny workload (bf16: the
+single-slice kernel, one launch per layer) and prefill-sized shapes on the
+one-pass kernel (hand-off records cleared in-graph by a fill kernel).  The Lazy Pre-Norm GEMM (one persistent launch) is replayed the same
 way.
 """
 
@@ -100,8 +101,8 @@ def _reset(inp, H0, bufs):
 
 
 @pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "e4m3"])
-@pytest.mark.parametrize("B,n,C", [(64, 4, 7168), (1024, 4, 4096), (600, 2, 2048)],
-                         ids=["decode", "one-pass", "one-pass-n2"])
+@pytest.mark.parametrize("B,n,C", [(64, 4, 7168), (1024, 4, 4096), (600, 2, 2048), (64, 4, 256)],
+                         ids=["decode", "one-pass", "one-pass-n2", "single-slice"])
 def test_graph_replay_matches_eager(B, n, C, fp8):
     route = (mhc.mhc_post_res_coeffs_pre_fp8_one_pass if fp8 else mhc.mhc_post_res_coeffs_pre_one_pass)(B, n, C)
     _say(f"graph replay B={B} n={n} C={C} fp8={fp8} one_pass={route}")
