@@ -513,7 +513,8 @@ int mhc_lazy_prenorm_gemm(int64_t M, int64_t N, int64_t K, const void *A, const 
  * the small-B kernel at any B.  Keys (value < 0 restores the default):
  *   MHC_SMALL_MAX_B  rows up to which the one-launch small-B coefficient
  *                    kernel runs (0: never)
- *   MHC_GEMM_ALGO    0: register-path product; 2: persistent product kernel
+ *   MHC_GEMM_ALGO    0: register-path product; 2: persistent product
+ *                    kernel; 3: the n = 8 pass (product only)
  *   MHC_SPLIT_K, MHC_GEMM_WGS, MHC_GEMM_MB, MHC_GEMM_WAVES   split-K
  *                    product shape (K-slices, target workgroups, 16-row
  *                    blocks per wave, 4 or 8 waves per workgroup)
@@ -521,7 +522,9 @@ int mhc_lazy_prenorm_gemm(int64_t M, int64_t N, int64_t K, const void *A, const 
  *                    at n <= 4 in 128-k chunks with a deeper ring
  *   MHC_GEMM_XREG    2: the bf16 split-K product (n = 4, 8) with X and phi
  *                    loaded through registers
- *   MHC_FUSED_N8     > 0: the fused kernel also at n = 8
+ *   MHC_FUSED_N8     0: n = 8 as the apply and the split-K product; > 0:
+ *                    the fused kernel (otherwise the n = 8 pass up to
+ *                    C = 4096)
  *   MHC_FUSED_FP8    0: E4M3 fused call as apply + product; > 0: fused kernel
  *   MHC_FUSED_FIXED  0 / 1: the fused kernel's fixed-slice layout off / on
  *   MHC_FUSED_SPU, MHC_FUSED_WGS   fused kernel's steps per unit, grid cap
@@ -529,6 +532,11 @@ int mhc_lazy_prenorm_gemm(int64_t M, int64_t N, int64_t K, const void *A, const 
  *   MHC_APPLY_SMALL  0: small-B bf16 mhc_post_res_coeffs as the apply
  *                    kernel, then the small-B coefficient kernel
  *   MHC_LPN_ALGO     1: the four-wave Lazy Pre-Norm GEMM kernel
+ *   MHC_PASS8_SETS   1 or 2: register sets of loads in flight per wave of
+ *                    the n = 8 one pass (mhc_post_res_coeffs_pre,
+ *                    mhc_coeffs_pre)
+ *   MHC_PASS8_PRE    1: those two calls at n = 8 in the n = 8 one pass
+ *                    (default: as two calls, measured faster)
  * Every route computes the same results up to fp32 summation order (the
  * fused calls' X_next and F_pre_next bitwise).  The workspace-size functions
  * answer for the routes selected at the time they are called, so set

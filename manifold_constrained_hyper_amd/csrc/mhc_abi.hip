@@ -76,7 +76,10 @@ int check_shape_elt(int64_t B, int32_t n, int64_t C, Elt e) {
 // each stream in 32-channel k-steps, so it needs C % 32 == 0; with
 // MHC_GEMM_ALGO=2 other hidden sizes take the small-B kernel at any B (it is
 // correct for every shape, only slower at large B).
-enum class CoeffsPath { kSmall, kSplitK, kPersistent };
+// At n = 8, bf16 X takes the product-only mode of the n = 8 pass
+// (mhc_onepass8.hip: phi held in registers per 128-channel slice) where it
+// fits (C <= 4096, C % 32 == 0).
+enum class CoeffsPath { kSmall, kSplitK, kPersistent, kPass8 };
 
 CoeffsPath coeffs_path(int64_t B, int32_t n, int64_t C, Elt e) {
   if (mhc::use_coeffs_small(B, n, C)) return CoeffsPath::kSmall;
@@ -84,8 +87,20 @@ CoeffsPath coeffs_path(int64_t B, int32_t n, int64_t C, Elt e) {
   const int64_t algo = mhc::tune(mhc::kTuneGemmAlgo);
   if (algo == 2) return C % 32 == 0 ? CoeffsPath::kPersistent : CoeffsPath::kSmall;
   if (algo == 0 || algo == 1) return CoeffsPath::kSplitK;
+  if (algo == 3) return n == 8 && !e.fp8 && mhc::onepass8_fits(B, C) ? CoeffsPath::kPass8 : CoeffsPath::kSplitK;
   if (!e.fp8 && n <= 4 && C % 32 == 0 && mhc::fixed_layout_fits(n, C)) return CoeffsPath::kPersistent;
+  if (!e.fp8 && n == 8 && mhc::onepass8_fits(B, C)) return CoeffsPath::kPass8;
   return CoeffsPath::kSplitK;
+}
+
+// Grid of the n = 8 pass without the hand-off: whole row tiles per round
+// (each workgroup keeps one slice), as many as can be resident; no workgroup
+// waits for another, so a grid larger than what is resident is only slower.
+int64_t pass8_grid(const mhc::FusedPlan &p, bool apply, hipStream_t s) {
+  const int64_t units = p.row_tiles * p.split;
+  int64_t g = mhc::pre_mode_grid(units, p.split, mhc::onepass8_resident(apply, false, s), mhc::tune(mhc::kTuneFusedWgs));
+  if (g == 0) g = p.split <= units ? p.split : units;
+  return g;
 }
 
 mhc::GemmPlan split_plan(int64_t B, int32_t n, int64_t C, Elt e) {
@@ -96,6 +111,7 @@ size_t coeffs_ws_bytes(int64_t B, int32_t n, int64_t C, Elt e) {
   switch (coeffs_path(B, n, C, e)) {
     case CoeffsPath::kSmall: return mhc::plan_coeffs_small(B, n, C).total_bytes;
     case CoeffsPath::kPersistent: return mhc::plan_post_res_next(B, n, C, false, true).total_bytes;
+    case CoeffsPath::kPass8: return mhc::plan_onepass8(B, C, false).total_bytes;
     default: return mhc::gemm_workspace_bytes(split_plan(B, n, C, e), B, n);
   }
 }
@@ -136,6 +152,15 @@ int coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t, const v
     return from_hip(mhc::launch_coeffs_small(mhc::plan_coeffs_small(B, n, C), n, e.fp8, B, C, X_t,
                                              phi, alpha_pre, alpha_post, alpha_res, b_pre, b_post,
                                              b_res, logits, r, H, workspace, s, e.phi32));
+  if (path == CoeffsPath::kPass8) {
+    const mhc::FusedPlan plan = mhc::plan_onepass8(B, C, false);
+    st = from_hip(mhc::launch_onepass8(plan, false, B, C, X_t, nullptr, nullptr, nullptr, phi, workspace,
+                                       pass8_grid(plan, false, s), s, nullptr));
+    if (st != MHC_OK) return st;
+    return from_hip(mhc::launch_coeff_sinkhorn(n, B, C, plan.split, static_cast<const float *>(workspace),
+                                               alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res,
+                                               logits, r, H, s, /*tree=*/true));
+  }
   if (path == CoeffsPath::kPersistent) {
     const mhc::FusedPlan plan = mhc::plan_post_res_next(B, n, C, false, true);
     st = from_hip(mhc::launch_post_res_next(plan, n, e.fp8 ? mhc::kFusedCoeffsFp8 : mhc::kFusedCoeffsBf16,
@@ -199,12 +224,18 @@ int post_res_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t, const
 //          call, 371 vs 383 us per layer with pre_fp8, chained layers at
 //          n=4, C=7168, B=16384).  MHC_FUSED_FP8=1 forces the fused kernel,
 //          MHC_FUSED_FP8=0 the two passes.
-enum class FusedRoute { kSmall, kTwoPass, kFused };
+//   n = 8, bf16: the n = 8 pass (mhc_onepass8.hip) where it fits (C <= 4096);
+//          MHC_FUSED_N8=0 forces the two passes.
+enum class FusedRoute { kSmall, kTwoPass, kFused, kPass8 };
 
 FusedRoute fused_route(int64_t B, int32_t n, int64_t C, Elt e) {
   if (mhc::use_coeffs_small(B, n, C)) return FusedRoute::kSmall;
   if (e.phi32) return FusedRoute::kTwoPass;  // the fused kernel takes bf16 phi only
-  if (n == 8 && mhc::tune(mhc::kTuneFusedN8) <= 0) return FusedRoute::kTwoPass;
+  if (n == 8) {
+    const int64_t v = mhc::tune(mhc::kTuneFusedN8);
+    if (v < 0 && !e.fp8 && mhc::onepass8_fits(B, C)) return FusedRoute::kPass8;
+    if (v <= 0) return FusedRoute::kTwoPass;
+  }
   if (e.fp8) {
     const int64_t v = mhc::tune(mhc::kTuneFusedFp8);
     if (v >= 0) return v == 0 ? FusedRoute::kTwoPass : FusedRoute::kFused;
@@ -218,6 +249,7 @@ size_t post_res_coeffs_ws_bytes(int64_t B, int32_t n, int64_t C, Elt e) {
   switch (fused_route(B, n, C, e)) {
     case FusedRoute::kSmall: return mhc::plan_coeffs_small(B, n, C).total_bytes;
     case FusedRoute::kTwoPass: return mhc::gemm_workspace_bytes(split_plan(B, n, C, e), B, n);
+    case FusedRoute::kPass8: return mhc::plan_onepass8(B, C, false).total_bytes;
     default: return mhc::plan_post_res_next(B, n, C, false, e.fp8).total_bytes;
   }
 }
@@ -230,7 +262,17 @@ size_t post_res_coeffs_ws_bytes(int64_t B, int32_t n, int64_t C, Elt e) {
 bool pre_fused(int64_t B, int32_t n, int64_t C, Elt e) {
   if (e.phi32) return false;
   if (mhc::tune(mhc::kTuneFusedPre) == 0) return false;
-  return fused_route(B, n, C, e) == FusedRoute::kFused && mhc::pre_mode_fits(B, n, C);
+  const FusedRoute route = fused_route(B, n, C, e);
+  // n = 8: the pass with the hand-off (one register set of loads beside it)
+  // measured slower than its two calls at n=8, C=4096, B=8192 (461-546
+  // against 360-392 us per layer), so it runs only with MHC_PASS8_PRE=1.
+  if (route == FusedRoute::kPass8) return mhc::tune(mhc::kTunePass8Pre) > 0;
+  return route == FusedRoute::kFused && mhc::pre_mode_fits(B, n, C);
+}
+
+// Workspace layout of a one-pass shape (records and give-up word included).
+mhc::FusedPlan pre_plan(int64_t B, int32_t n, int64_t C, Elt e) {
+  return n == 8 ? mhc::plan_onepass8(B, C, true) : mhc::plan_post_res_next(B, n, C, true, e.fp8);
 }
 
 // The single-slice route (mhc_layer_small.hip): bf16, n <= 4, the small-B
@@ -244,7 +286,7 @@ bool small_pass(int64_t B, int32_t n, int64_t C, Elt e) {
 
 size_t post_res_coeffs_pre_ws_bytes(int64_t B, int32_t n, int64_t C, Elt e) {
   if (check_shape_elt(B, n, C, e) != MHC_OK || B == 0 || C % 32 != 0) return 0;
-  if (pre_fused(B, n, C, e)) return mhc::plan_post_res_next(B, n, C, true).total_bytes;
+  if (pre_fused(B, n, C, e)) return pre_plan(B, n, C, e).total_bytes;
   return post_res_coeffs_ws_bytes(B, n, C, e);
 }
 
@@ -270,7 +312,8 @@ int post_res_coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t
     return MHC_ERR_UNSUPPORTED;
   const FusedRoute route = fused_route(B, n, C, e);
   bool one_pass = with_pre && pre_fused(B, n, C, e);
-  const mhc::FusedPlan plan = mhc::plan_post_res_next(B, n, C, one_pass, e.fp8);
+  const mhc::FusedPlan plan = route == FusedRoute::kPass8 ? mhc::plan_onepass8(B, C, one_pass)
+                                                           : mhc::plan_post_res_next(B, n, C, one_pass, e.fp8);
   const size_t ws_need = with_pre ? post_res_coeffs_pre_ws_bytes(B, n, C, e) : post_res_coeffs_ws_bytes(B, n, C, e);
   const int64_t N = ncoef(n), K = (int64_t)n * C;
   const size_t eb = e.bytes();
@@ -301,7 +344,9 @@ int post_res_coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t
     // grid from what the device and the stream's CUs hold, and run the two
     // calls instead when not even one row tile's slices fit together.
     grid = mhc::pre_mode_grid(plan.row_tiles * plan.split, plan.split,
-                              mhc::pre_mode_resident(n, e.fp8 ? mhc::kFusedApplyPreFp8 : mhc::kFusedApplyPreBf16, s),
+                              route == FusedRoute::kPass8
+                                  ? mhc::onepass8_resident(true, true, s)
+                                  : mhc::pre_mode_resident(n, e.fp8 ? mhc::kFusedApplyPreFp8 : mhc::kFusedApplyPreBf16, s),
                               mhc::tune(mhc::kTuneFusedWgs));
     if (grid == 0) {
       one_pass = false;
@@ -312,8 +357,11 @@ int post_res_coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t
   }
   if (one_pass) {
     const mhc::PreOut po{F_pre_next, b_pre, alpha_pre, grid};
-    st = from_hip(mhc::launch_post_res_next(plan, n, e.fp8 ? mhc::kFusedApplyPreFp8 : mhc::kFusedApplyPreBf16,
-                                            B, C, X_t, F_out, H, X_next, phi_next, workspace, s, &po));
+    if (route == FusedRoute::kPass8)
+      st = from_hip(mhc::launch_onepass8(plan, true, B, C, X_t, F_out, H, X_next, phi_next, workspace, grid, s, &po));
+    else
+      st = from_hip(mhc::launch_post_res_next(plan, n, e.fp8 ? mhc::kFusedApplyPreFp8 : mhc::kFusedApplyPreBf16,
+                                              B, C, X_t, F_out, H, X_next, phi_next, workspace, s, &po));
     if (st != MHC_OK) return st;
     return from_hip(mhc::launch_coeff_sinkhorn(n, B, C, plan.split, static_cast<const float *>(workspace),
                                                alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res,
@@ -327,6 +375,14 @@ int post_res_coeffs_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t
     if (st != MHC_OK) return st;
     return from_hip(e.fp8 ? mhc::launch_pre_fp8(n, B, C, X_next, H_next, F_pre_next, s)
                           : mhc::launch_pre(n, B, C, X_next, H_next, F_pre_next, s));
+  }
+  if (route == FusedRoute::kPass8) {
+    st = from_hip(mhc::launch_onepass8(plan, true, B, C, X_t, F_out, H, X_next, phi_next, workspace,
+                                       pass8_grid(plan, true, s), s, nullptr));
+    if (st != MHC_OK) return st;
+    return from_hip(mhc::launch_coeff_sinkhorn(n, B, C, plan.split, static_cast<const float *>(workspace),
+                                               alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res,
+                                               logits_next, r_next, H_next, s, /*tree=*/true));
   }
   if (route != FusedRoute::kFused) {
     if (route == FusedRoute::kSmall && !e.fp8 && !e.phi32 && mhc::tune(mhc::kTuneApplySmall) != 0 &&
@@ -370,7 +426,7 @@ size_t coeffs_pre_ws_bytes(int64_t B, int32_t n, int64_t C, Elt e) {
   if (check_shape_elt(B, n, C, e) != MHC_OK || B == 0) return 0;
   const size_t two = coeffs_ws_bytes(B, n, C, e);
   if (!coeffs_pre_fused(B, n, C, e)) return two;
-  const size_t one = mhc::plan_post_res_next(B, n, C, true).total_bytes;
+  const size_t one = pre_plan(B, n, C, e).total_bytes;
   return one > two ? one : two;
 }
 
@@ -412,14 +468,19 @@ int coeffs_pre_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t, con
   if (one_pass) {
     // As in mhc_post_res_coeffs_pre: a grid that can be resident at once,
     // else the two calls (the give-up word then reports no give-up).
-    const mhc::FusedPlan plan = mhc::plan_post_res_next(B, n, C, true, e.fp8);
+    const mhc::FusedPlan plan = pre_plan(B, n, C, e);
     const int64_t grid = mhc::pre_mode_grid(plan.row_tiles * plan.split, plan.split,
-                                            mhc::pre_mode_resident(n, mode, s),
+                                            n == 8 ? mhc::onepass8_resident(false, true, s)
+                                                   : mhc::pre_mode_resident(n, mode, s),
                                             mhc::tune(mhc::kTuneFusedWgs));
     if (grid > 0) {
       const mhc::PreOut po{F_pre, b_pre, alpha_pre, grid};
-      st = from_hip(mhc::launch_post_res_next(plan, n, mode, B, C, X_t, nullptr, nullptr, nullptr, phi,
-                                              workspace, s, &po));
+      if (n == 8)
+        st = from_hip(mhc::launch_onepass8(plan, false, B, C, X_t, nullptr, nullptr, nullptr, phi, workspace,
+                                           grid, s, &po));
+      else
+        st = from_hip(mhc::launch_post_res_next(plan, n, mode, B, C, X_t, nullptr, nullptr, nullptr, phi,
+                                                workspace, s, &po));
       if (st != MHC_OK) return st;
       return from_hip(mhc::launch_coeff_sinkhorn(n, B, C, plan.split, static_cast<const float *>(workspace),
                                                  alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res,
@@ -439,7 +500,7 @@ int coeffs_pre_impl(Elt e, int64_t B, int32_t n, int64_t C, const void *X_t, con
 // The give-up word of a one-pass workspace (pre-mix layout): MHC_OK while
 // zero, MHC_ERR_INCOMPLETE once a wait gave up.  Synchronises the stream.
 int read_giveup(int64_t B, int32_t n, int64_t C, Elt e, const void *workspace, void *stream) {
-  const mhc::FusedPlan plan = mhc::plan_post_res_next(B, n, C, true, e.fp8);
+  const mhc::FusedPlan plan = pre_plan(B, n, C, e);
   uint32_t word = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (hipMemcpyAsync(&word, static_cast<const char *>(workspace) + plan.flag_offset, sizeof(word),
@@ -469,6 +530,7 @@ constexpr TuneName kTuneNames[] = {
     {"MHC_GEMM_KC", mhc::kTuneGemmKc},        {"MHC_GEMM_STAGES", mhc::kTuneGemmStages},
     {"MHC_GEMM_WAVES", mhc::kTuneGemmWaves},  {"MHC_GEMM_XREG", mhc::kTuneGemmXreg},
     {"MHC_APPLY_SMALL", mhc::kTuneApplySmall},
+    {"MHC_PASS8_SETS", mhc::kTunePass8Sets},  {"MHC_PASS8_PRE", mhc::kTunePass8Pre},
 };
 static_assert(sizeof(kTuneNames) / sizeof(kTuneNames[0]) == mhc::kTuneCount, "one name per key");
 
@@ -561,6 +623,7 @@ int32_t mhc_coeffs_split_k(int64_t B, int32_t n, int64_t C) {
   switch (coeffs_path(B, n, C, kBf16)) {
     case CoeffsPath::kSmall: return mhc::plan_coeffs_small(B, n, C).split;
     case CoeffsPath::kPersistent: return mhc::plan_post_res_next(B, n, C, false, true).split;
+    case CoeffsPath::kPass8: return mhc::plan_onepass8(B, C, false).split;
     default: return mhc::plan_gemm(B, n, C).split;
   }
 }

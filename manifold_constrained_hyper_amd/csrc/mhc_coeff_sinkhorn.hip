@@ -27,7 +27,9 @@
 //            With TREE (at most 16 slices) the slices are instead added as
 //            the balanced binary tree over 16 slots, zero past S
 //            (tree16_sum_serial), the order in which the pre-mix mode of the
-//            fused kernel sums the same partials for its H_pre.
+//            fused kernel sums the same partials for its H_pre; at n = 8 (at
+//            most 32 slices) the trees of slots 0-15 and 16-31, then their
+//            sum, the order of the n = 8 pass (mhc_onepass8.hip).
 //   phase 2  finish_row (mhc_finish.h): lane i computes gate i of the pre
 //            and post blocks, then the Sinkhorn iteration on row i of the res
 //            matrix, with column sums by a DPP butterfly over the row's lanes.
@@ -99,19 +101,30 @@ __global__ __launch_bounds__(ONE_ROW ? 256 : kMultiRowThreads) void coeff_sinkho
 #pragma unroll
     for (int q = 0; q < EPT; ++q) acc[q] = 0.f;
     if constexpr (TREE) {
-      // Slots past S are zero (no load); the tree is the same for any S.
+      // Slots past S are zero (no load); the tree is the same for any S.  At
+      // n = 8 there are 32 slots: the 16-slot trees of slots 0-15 and 16-31,
+      // then their sum.
+      constexpr int TS = NS >= 8 ? 32 : 16;
 #pragma unroll
       for (int q = 0; q < EPT; ++q) {
         const int e = tid + q * TH;
-        float v[16];
+        float part[TS / 16];
 #pragma unroll
-        for (int sb = 0; sb < 16; ++sb) v[sb] = 0.f;
-        if (e < nel) {
+        for (int h = 0; h < TS / 16; ++h) {
+          float v[16];
 #pragma unroll
-          for (int sb = 0; sb < 16; ++sb)
-            if (sb < split) v[sb] = base[(size_t)sb * slice + e];
+          for (int sb = 0; sb < 16; ++sb) v[sb] = 0.f;
+          if (e < nel) {
+#pragma unroll
+            for (int sb = 0; sb < 16; ++sb)
+              if (16 * h + sb < split) v[sb] = base[(size_t)(16 * h + sb) * slice + e];
+          }
+          part[h] = tree16_sum_serial(v);
         }
-        acc[q] = tree16_sum_serial(v);
+        if constexpr (TS == 32)
+          acc[q] = part[0] + part[1];
+        else
+          acc[q] = part[0];
       }
     }
     for (int s0 = 0; s0 < (TREE ? 0 : split); s0 += SB) {
@@ -176,7 +189,7 @@ hipError_t launch_coeff_sinkhorn(int n, int64_t B, int64_t C, int split, const f
                                  float alpha_pre, float alpha_post, float alpha_res,
                                  const float *b_pre, const float *b_post, const float *b_res,
                                  float *logits, float *r, float *H, hipStream_t st, bool tree) {
-  if (tree && (split > 16 || n == 8)) return hipErrorInvalidValue;
+  if (tree && split > (n == 8 ? kMaxSlices8 : 16)) return hipErrorInvalidValue;
   switch (n) {
     case 1: launch_n<1>(B, C, split, ws, alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res, logits, r, H, st, tree); break;
     case 2: launch_n<2>(B, C, split, ws, alpha_pre, alpha_post, alpha_res, b_pre, b_post, b_res, logits, r, H, st, tree); break;

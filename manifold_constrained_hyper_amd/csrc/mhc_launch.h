@@ -30,6 +30,8 @@ enum TuneKey : int {
   kTuneGemmWaves,      // 4 or 8: wavefronts per workgroup of the LDS-staged split-K product
   kTuneGemmXreg,       // 2: bf16 split-K product with X and phi through two register sets (n = 4, 8)
   kTuneApplySmall,     // 0: small-B bf16 mhc_post_res_coeffs as the apply kernel, then coeffs_small
+  kTunePass8Sets,      // 1 or 2: register sets of loads of the n = 8 pass with the hand-off
+  kTunePass8Pre,       // 1: mhc_post_res_coeffs_pre and mhc_coeffs_pre at n = 8 in one pass (default: two calls)
   kTuneCount
 };
 // Current value of a key; -1 when unset.
@@ -164,6 +166,9 @@ int64_t pre_mode_resident(int n, int mode, hipStream_t st);
 // positive), no more than the `units` there are; 0 when not even one row
 // tile's `split` workgroups can be resident together (the mode must not run).
 int64_t pre_mode_grid(int64_t units, int64_t split, int64_t resident, int64_t wgs_cap);
+// Compute units a launch on `st` may use: the device's, or the stream's CU
+// mask where it has one.
+int64_t stream_cus(hipStream_t st);
 // pre_out: F_pre (bf16 or E4M3 [B, C], the element type of the mode), the
 // next layer's b_pre / alpha_pre and the grid (pre_mode_grid) for the
 // pre-mix modes, else null.
@@ -177,6 +182,24 @@ hipError_t launch_post_res_next(const FusedPlan &p, int n, int mode, int64_t B, 
                                 const void *X, const void *F, const float *H, void *Y,
                                 const void *phi_next, void *ws_base, hipStream_t st,
                                 const PreOut *pre_out = nullptr);
+
+// The n = 8 pass (mhc_onepass8.hip): bf16, one workgroup per 128-channel
+// slice of all 8 streams and row tile, phi held in registers.  apply: X_t,
+// F_out, H -> X_next (mhc_post_res's bits) and the next layer's partials;
+// otherwise the partials of X_t itself.  With plan.pre also the records and
+// F_pre (pre_out).  Workspace: the FusedPlan of plan_onepass8 (partials
+// [S, B, 81]; with pre, records [B, 9, S] and the give-up word, zero-filled
+// by the launch).  The combine is launch_coeff_sinkhorn(..., tree = true).
+constexpr int kMaxSlices8 = 32;  // slices per row: C <= 4096
+bool onepass8_fits(int64_t B, int64_t C);
+FusedPlan plan_onepass8(int64_t B, int64_t C, bool pre);
+// Workgroups that can be resident at once for launches on `st`.
+int64_t onepass8_resident(bool apply, bool pre, hipStream_t st);
+// grid: a multiple of plan.split, at most the row tiles times the split, all
+// resident (pre_mode_grid with onepass8_resident).
+hipError_t launch_onepass8(const FusedPlan &p, bool apply, int64_t B, int64_t C, const void *X,
+                           const void *F, const float *H, void *Y, const void *phi, void *ws_base,
+                           int64_t grid, hipStream_t st, const PreOut *pre_out);
 
 // Single-slice layer calls in one kernel (mhc_layer_small.hip): the one-pass
 // mhc_post_res_coeffs_pre / mhc_coeffs_pre in bf16 for n in {1, 2, 4} at the
@@ -244,8 +267,10 @@ hipError_t launch_apply_coeffs_small(const SmallPlan &p, int n, int64_t B, int64
 // Process-wide 64-bit call epoch of the small-B arrival flags (never 0).
 unsigned long long next_call_epoch();
 
-// tree: add the split partials as the 16-slot balanced tree (split <= 16,
-// n <= 4), the order of the fused kernel's pre-mix mode.
+// tree: add the split partials as the balanced tree over 16 slots (split <=
+// 16, n <= 4), the order of the fused kernel's pre-mix mode, or at n = 8 over
+// 32 slots (split <= 32: two 16-slot trees, then their sum), the order of the
+// n = 8 pass.
 hipError_t launch_coeff_sinkhorn(int n, int64_t B, int64_t C, int split, const float *ws,
                                  float alpha_pre, float alpha_post, float alpha_res,
                                  const float *b_pre, const float *b_post, const float *b_res,

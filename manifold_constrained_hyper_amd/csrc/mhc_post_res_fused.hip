@@ -1007,6 +1007,10 @@ int64_t pre_mode_resident(int n, int mode, hipStream_t st) {
     occ = v;
     if (occ > 0 && dev >= 0 && dev < 64) occ_cache[dev][ni][mi].store(occ, std::memory_order_relaxed);
   }
+  return (int64_t)occ * stream_cus(st);
+}
+
+int64_t stream_cus(hipStream_t st) {
   int64_t cus = device_cus();
   if (st != nullptr) {
     // A stream created with a CU mask runs on the masked CUs only.
@@ -1020,7 +1024,7 @@ int64_t pre_mode_resident(int n, int mode, hipStream_t st) {
       (void)hipGetLastError();
     }
   }
-  return (int64_t)occ * cus;
+  return cus;
 }
 
 hipError_t launch_post_res_next(const FusedPlan &p, int n, int mode, int64_t B, int64_t C,

@@ -159,9 +159,9 @@ int main(int argc, char **argv) {
   // Tuning keys.
   CHECK(mhc_tuning_set(nullptr, 1) == MHC_ERR_INVALID_ARG);
   CHECK(mhc_tuning_set("MHC_NOPE", 1) == MHC_ERR_INVALID_ARG);
-  const int32_t s0 = mhc_coeffs_split_k(8192, 8, 4096);  // the split-K product (the default at n = 8)
-  CHECK(mhc_tuning_set("MHC_SPLIT_K", 5) == MHC_OK && mhc_coeffs_split_k(8192, 8, 4096) == 5);
-  CHECK(mhc_tuning_set("MHC_SPLIT_K", INT64_MAX) == MHC_OK && mhc_coeffs_split_k(8192, 8, 4096) >= 1);
+  const int32_t s0 = mhc_coeffs_split_k(8192, 8, 4224);  // the split-K product (the default at n = 8 above C = 4096)
+  CHECK(mhc_tuning_set("MHC_SPLIT_K", 5) == MHC_OK && mhc_coeffs_split_k(8192, 8, 4224) == 5);
+  CHECK(mhc_tuning_set("MHC_SPLIT_K", INT64_MAX) == MHC_OK && mhc_coeffs_split_k(8192, 8, 4224) >= 1);
   CHECK(mhc_tuning_set("MHC_FUSED_PRE", 0) == MHC_OK && !mhc_post_res_coeffs_pre_one_pass(16384, 4, 7168));
   for (const char *k : {"MHC_SMALL_MAX_B", "MHC_GEMM_ALGO", "MHC_GEMM_WGS", "MHC_GEMM_MB", "MHC_FUSED_N8",
                         "MHC_FUSED_FP8", "MHC_FUSED_FIXED", "MHC_FUSED_SPU", "MHC_FUSED_WGS", "MHC_LPN_ALGO",
@@ -175,7 +175,7 @@ int main(int argc, char **argv) {
     CHECK(mhc_tuning_set(k, -5) == MHC_OK);
   }
   mhc_tuning_reset();
-  CHECK(mhc_coeffs_split_k(8192, 8, 4096) == s0 && mhc_post_res_coeffs_pre_one_pass(16384, 4, 7168));
+  CHECK(mhc_coeffs_split_k(8192, 8, 4224) == s0 && mhc_post_res_coeffs_pre_one_pass(16384, 4, 7168));
 
   // The one-pass grid: whole row tiles per round within what is resident.
   CHECK(mhc::pre_mode_grid(1024 * 14, 14, 256, -1) == 252);

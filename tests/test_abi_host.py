@@ -180,7 +180,7 @@ def test_fused_pre_route_and_workspace(tune):
     assert not one(64, 4, 288) and not one(64, 8, 96)
     assert mhc.mhc_post_res_coeffs_pre_workspace_size(64, 4, 256) == \
         mhc.mhc_post_res_coeffs_workspace_size(64, 4, 256)
-    assert not one(8192, 8, 4096)        # n = 8: two tiles do not fit LDS
+    assert not one(8192, 8, 4096)        # n = 8: two calls (the n = 8 apply pass, then mhc_pre)
     assert not one(4096, 4, 8704)        # 17 steps of 512 channels per row
     assert not one(0, 4, 7168) and not one(16, 4, 40)
     # one pass: partials [S, B, N+1] fp32 + packed phi + records [B, S, PW] of 4 bytes
@@ -189,9 +189,29 @@ def test_fused_pre_route_and_workspace(tune):
     ws = mhc.mhc_post_res_coeffs_pre_workspace_size(B, n, C)
     assert ws >= S * B * (N + 1) * 4 + S * B * PW * 4
     assert ws <= S * B * (N + 1) * 4 + S * B * PW * 4 + (n * C // 32) * 2 * 1024 + 8192
+    # the n = 8 apply pass: partials [S, B, 81], S = C / 128
+    B8, C8 = 8192, 4096
+    S8 = C8 // 128
+    assert S8 * B8 * 81 * 4 <= mhc.mhc_post_res_coeffs_workspace_size(B8, 8, C8) <= S8 * B8 * 81 * 4 + 1024
+    # ... and its one pass (MHC_PASS8_PRE=1): + records [B, 9, S] + the give-up word
+    tune.setenv("MHC_PASS8_PRE", 1)
+    assert one(8192, 8, 4096) and one(300, 8, 160)
+    assert not one(8192, 8, 4224)        # n = 8 with 33 slices per row
+    ws8 = mhc.mhc_post_res_coeffs_pre_workspace_size(B8, 8, C8)
+    assert S8 * B8 * 81 * 4 + B8 * 9 * S8 * 4 <= ws8 <= S8 * B8 * 81 * 4 + B8 * 9 * S8 * 4 + 2048
+    tune.delenv("MHC_PASS8_PRE")
     # the two-call routes need what mhc_post_res_coeffs needs
     assert mhc.mhc_post_res_coeffs_pre_workspace_size(8192, 8, 4096) == \
         mhc.mhc_post_res_coeffs_workspace_size(8192, 8, 4096)
+    assert mhc.mhc_post_res_coeffs_pre_workspace_size(8192, 8, 4224) == \
+        mhc.mhc_post_res_coeffs_workspace_size(8192, 8, 4224)
+    tune.setenv("MHC_FUSED_N8", "0")     # n = 8 as the apply and the split-K product
+    tune.setenv("MHC_PASS8_PRE", 1)      # (no n = 8 pass to run in one pass)
+    assert not one(8192, 8, 4096)
+    assert mhc.mhc_post_res_coeffs_pre_workspace_size(8192, 8, 4096) == \
+        mhc.mhc_post_res_coeffs_workspace_size(8192, 8, 4096)
+    tune.delenv("MHC_FUSED_N8")
+    tune.delenv("MHC_PASS8_PRE")
     tune.setenv("MHC_FUSED_PRE", "0")
     assert not one(16384, 4, 7168) and not one(64, 4, 256)
     assert mhc.mhc_post_res_coeffs_pre_workspace_size(B, n, C) == mhc.mhc_post_res_coeffs_workspace_size(B, n, C)
@@ -303,7 +323,8 @@ def test_coeffs_pre_route_and_workspace(tune):
             assert bool(one(*shape)) == (not fp8)
             assert size(*shape) == coeffs_size(*shape)
         assert not one(64, 4, 264) and not one(64, 8, 64)
-        assert not one(8192, 8, 4096)        # n = 8
+        assert not one(8192, 8, 4096)        # n = 8: two calls by default
+        assert not one(8192, 8, 4224)        # n = 8 with 33 slices per row
         assert not one(4096, 4, 8704)        # 17 steps of 512 channels per row
         assert not one(4096, 4, 7184)        # C % 32 != 0
         assert not one(0, 4, 7168) and not one(16, 3, 64)
@@ -312,7 +333,16 @@ def test_coeffs_pre_route_and_workspace(tune):
         B, n, C = 16384, 4, 7168
         assert size(B, n, C) == mhc.mhc_post_res_coeffs_pre_workspace_size(B, n, C)
         assert size(B, n, C) >= coeffs_size(B, n, C)
+        assert size(8192, 8, 4224) == coeffs_size(8192, 8, 4224)
         assert size(8192, 8, 4096) == coeffs_size(8192, 8, 4096)
+        tune.setenv("MHC_PASS8_PRE", 1)      # the n = 8 pass in one pass (bf16 only)
+        assert bool(one(8192, 8, 4096)) == (not fp8)
+        if not fp8:
+            tune.setenv("MHC_FUSED_PRE", 1)
+            assert size(8192, 8, 4096) == mhc.mhc_post_res_coeffs_pre_workspace_size(8192, 8, 4096)
+            assert size(8192, 8, 4096) >= coeffs_size(8192, 8, 4096)
+            tune.delenv("MHC_FUSED_PRE")
+        tune.delenv("MHC_PASS8_PRE")
     tune.setenv("MHC_FUSED_PRE", "0")
     assert not mhc.mhc_coeffs_pre_one_pass(16384, 4, 7168)
     assert mhc.mhc_coeffs_pre_workspace_size(16384, 4, 7168) == mhc.mhc_coeffs_workspace_size(16384, 4, 7168)
@@ -322,7 +352,7 @@ def test_coeffs_pre_check_host():
     """mhc_coeffs_pre_check answers without a device where no one-pass kernel
     can have run, and rejects bad arguments."""
     assert mhc.mhc_coeffs_pre_check(64, 4, 7168, A, workspace_bytes=1 << 20, stream=0) == mhc.MHC_OK
-    assert mhc.mhc_coeffs_pre_check(8192, 8, 4096, A, workspace_bytes=1 << 20, stream=0) == mhc.MHC_OK
+    assert mhc.mhc_coeffs_pre_check(8192, 8, 4224, A, workspace_bytes=1 << 20, stream=0) == mhc.MHC_OK
     assert mhc.mhc_coeffs_pre_check(4096, 4, 7184, A, workspace_bytes=1 << 30, stream=0) == mhc.MHC_OK
     assert mhc.mhc_coeffs_pre_check(0, 4, 7168, None, stream=0) == mhc.MHC_OK
     assert mhc.mhc_coeffs_pre_check(16384, 3, 7168, A, stream=0) == mhc.MHC_ERR_UNSUPPORTED
@@ -466,11 +496,17 @@ def test_tuning_keys_and_no_environment(tune, monkeypatch):
         monkeypatch.setenv(k, v)
     assert (one(16384, 4, 7168), ws(16384, 4, 7168), mhc.mhc_coeffs_split_k(16384, 4, 7168),
             mhc.mhc_coeffs_workspace_size(64, 4, 7168)) == base
-    # the split-K product's slice count (the default product at n = 8)
+    # the n = 8 pass: one slice per 128 channels
+    assert mhc.mhc_coeffs_split_k(8192, 8, 4096) == 32
+    # the split-K product's slice count (MHC_GEMM_ALGO=1 forces it at n = 8)
+    tune.setenv("MHC_GEMM_ALGO", 1)
     s8 = mhc.mhc_coeffs_split_k(8192, 8, 4096)
     tune.setenv("MHC_SPLIT_K", 5)
     assert mhc.mhc_coeffs_split_k(8192, 8, 4096) == 5
+    tune.delenv("MHC_GEMM_ALGO")
     assert mhc.mhc_coeffs_split_k(16384, 4, 7168) == base[2]   # the persistent product: one slice per 512 channels
+    assert mhc.mhc_coeffs_split_k(8192, 8, 4096) == 32         # ... and the n = 8 pass: one per 128
+    tune.setenv("MHC_GEMM_ALGO", 1)
     tune.delenv("MHC_SPLIT_K")
     assert mhc.mhc_coeffs_split_k(8192, 8, 4096) == s8
     assert base[2] == 14
@@ -485,9 +521,10 @@ def test_tuning_keys_and_no_environment(tune, monkeypatch):
 
 def test_every_documented_tuning_key(tune):
     """Each key the header documents is accepted, and the split-K shape keys
-    reach the plan: at n = 8 (C = 4096, B = 8192) four waves of one 16-row
-    block make 64-row tiles and two K-slices; eight waves, or X through
-    registers, make 128-row tiles and four."""
+    reach the plan: at n = 8 (C = 4096, B = 8192; the split-K product forced
+    over the n = 8 pass) four waves of one 16-row block make 64-row tiles and
+    two K-slices; eight waves, or X through registers, make 128-row tiles and
+    four."""
     hdr = open(os.path.join(ROOT, "include", "mhc.h")).read()
     doc = hdr[hdr.index("Testing and tuning."):]
     keys = sorted(set(re.findall(r"\bMHC_[A-Z0-9_]+\b", doc)) - {"MHC_H", "MHC_ERR_INVALID_ARG"})
@@ -495,6 +532,8 @@ def test_every_documented_tuning_key(tune):
     for k in keys:
         mhc.mhc_tuning_set(k, -1)
     split = mhc.mhc_coeffs_split_k
+    assert split(8192, 8, 4096) == 32     # the n = 8 pass
+    tune.setenv("MHC_GEMM_ALGO", 1)       # the split-K product
     assert split(8192, 8, 4096) == 2
     tune.setenv("MHC_GEMM_WAVES", 8)
     assert split(8192, 8, 4096) == 4
@@ -538,7 +577,7 @@ def test_one_pass_grid_and_check():
     without a device where no one-pass kernel can have run."""
     # the shapes that run two calls never give up: no device access needed
     assert mhc.mhc_post_res_coeffs_pre_check(64, 4, 7168, A, workspace_bytes=1 << 20, stream=0) == mhc.MHC_OK
-    assert mhc.mhc_post_res_coeffs_pre_check(8192, 8, 4096, A, workspace_bytes=1 << 20, stream=0) == mhc.MHC_OK
+    assert mhc.mhc_post_res_coeffs_pre_check(8192, 8, 4224, A, workspace_bytes=1 << 20, stream=0) == mhc.MHC_OK
     assert mhc.mhc_post_res_coeffs_pre_check(0, 4, 7168, None, stream=0) == mhc.MHC_OK
     # argument errors
     assert mhc.mhc_post_res_coeffs_pre_check(16384, 3, 7168, A, stream=0) == mhc.MHC_ERR_UNSUPPORTED

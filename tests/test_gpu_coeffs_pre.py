@@ -47,15 +47,24 @@ def _gpu():
     yield
 
 
-@pytest.fixture(params=["default", "onepass", "twocalls"])
+# "pass8pre": the n = 8 pass in one pass (MHC_PASS8_PRE=1, bf16 n = 8 shapes
+# only; by default n = 8 runs as the two calls).
+@pytest.fixture(params=["default", "onepass", "twocalls", "pass8pre"])
 def route(request, tune):
-    for k in ("MHC_FUSED_PRE", "MHC_SMALL_MAX_B", "MHC_FUSED_FP8"):
+    for k in ("MHC_FUSED_PRE", "MHC_SMALL_MAX_B", "MHC_FUSED_FP8", "MHC_PASS8_PRE"):
         tune.delenv(k, raising=False)
     if request.param == "onepass":
         tune.setenv("MHC_SMALL_MAX_B", "0")
     elif request.param == "twocalls":
         tune.setenv("MHC_FUSED_PRE", "0")
+    elif request.param == "pass8pre":
+        tune.setenv("MHC_PASS8_PRE", "1")
     return request.param
+
+
+def _only_pass8(route, n, dt="bf16"):
+    if route == "pass8pre" and (n != 8 or dt != "bf16"):
+        pytest.skip("MHC_PASS8_PRE changes bf16 n = 8 only")
 
 
 class _Api:
@@ -183,6 +192,7 @@ def _rows(B):
 def test_named(name, dt, route):
     api = APIS[dt]
     cfg = synth.CONFIGS[name]
+    _only_pass8(route, cfg["n"], dt)
     one = api.one_pass(cfg["B"], cfg["n"], cfg["C"])
     _say(f"coeffs_pre {dt} {name} route={route} one_pass={one}")
     if route == "onepass" and cfg["B"] > 256:
@@ -202,27 +212,35 @@ def test_route_query(tune):
         assert q(16384, 4, 7168)
         assert q(4096, 2, 4096)
         assert not q(64, 4, 7168)       # small B
-        assert not q(8192, 8, 4096)     # n = 8
+        assert not q(8192, 8, 4224)     # n = 8 above 32 slices of 128 channels
         assert not q(4096, 4, 8704)     # 17 steps per row
         assert not q(4096, 4, 7184)     # C % 32 != 0
     assert mhc.mhc_coeffs_pre_one_pass(64, 4, 256)           # small B, one slice: bf16 only
     assert not mhc.mhc_coeffs_pre_fp8_one_pass(64, 4, 256)
+    assert not mhc.mhc_coeffs_pre_one_pass(8192, 8, 4096)    # n = 8: two calls by default
+    tune.setenv("MHC_PASS8_PRE", "1")
+    assert mhc.mhc_coeffs_pre_one_pass(8192, 8, 4096)        # ... the n = 8 pass on request, bf16 only
+    assert not mhc.mhc_coeffs_pre_fp8_one_pass(8192, 8, 4096)
+    tune.delenv("MHC_PASS8_PRE")
     tune.setenv("MHC_FUSED_PRE", "0")
     assert not mhc.mhc_coeffs_pre_one_pass(16384, 4, 7168)
     assert not mhc.mhc_coeffs_pre_fp8_one_pass(16384, 4, 7168)
 
 
 # (B, n, C): ragged row tiles, a ragged last 512-channel step, one to sixteen
-# steps per row, n = 1, 2, 4; n = 8, C % 32 != 0 and 17 steps take the
-# two calls.
+# steps per row, n = 1, 2, 4; n = 8 (bf16) in the n = 8 pass: a ragged last
+# 128-channel slice, 1 to 32 slices; n = 8 above 32 slices, C % 32 != 0 and
+# 17 steps take the two calls.
 RAGGED = [(77, 4, 544), (1, 4, 32), (33, 1, 64), (65, 2, 2080), (300, 4, 1536), (16, 2, 512),
           (257, 4, 8192), (19, 4, 3104), (130, 8, 96), (21, 4, 8704), (513, 2, 4096), (300, 4, 1040),
-          (7, 4, 48), (250, 1, 1008), (256, 2, 512)]
+          (7, 4, 48), (250, 1, 1008), (256, 2, 512), (300, 8, 160), (257, 8, 4096), (1000, 8, 1056),
+          (40, 8, 4224)]
 
 
 @pytest.mark.parametrize("dt", ["bf16", "fp8"])
 @pytest.mark.parametrize("B,n,C", RAGGED, ids=[f"B{b}n{n}C{c}" for b, n, c in RAGGED])
 def test_ragged(B, n, C, dt, route):
+    _only_pass8(route, n, dt)
     api = APIS[dt]
     _say(f"coeffs_pre {dt} ragged B={B} n={n} C={C} route={route} one_pass={api.one_pass(B, n, C)}")
     inp = api.inputs(n, C, B, "student_t4" if B % 2 else "normal", B * 37 + C)

@@ -35,15 +35,21 @@ def _gpu():
 
 
 # Up to 256 rows mhc_post_res_coeffs runs the stand-alone apply and the
-# one-launch small-B coefficient kernel, and at n = 8 the apply and the
-# split-K product; "fused" forces the fused kernel at every size and n (in
-# its default layout: several 512-channel steps per unit, slices changing
-# from round to round), and "fused_fixed" the same kernel in its fixed-slice
-# layout (n <= 4: one step per unit, each workgroup keeping one slice).
-@pytest.fixture(params=["default", "fused", "fused_fixed"])
+# one-launch small-B coefficient kernel; above, at n = 8, the n = 8 pass
+# (mhc_onepass8.hip) up to C = 4096 and the apply with the split-K product
+# beyond; "fused" forces the fused kernel of mhc_post_res_fused.hip at every
+# size and n (in its default layout: several 512-channel steps per unit,
+# slices changing from round to round), "fused_fixed" the same kernel in its
+# fixed-slice layout (n <= 4: one step per unit, each workgroup keeping one
+# slice), and "two_pass" the apply and the split-K product at n = 8
+# (MHC_FUSED_N8=0).
+@pytest.fixture(params=["default", "fused", "fused_fixed", "two_pass"])
 def route(request, tune):
     tune.delenv("MHC_FUSED_FIXED", raising=False)
-    if request.param in ("fused", "fused_fixed"):
+    if request.param == "two_pass":
+        tune.delenv("MHC_SMALL_MAX_B", raising=False)
+        tune.setenv("MHC_FUSED_N8", "0")
+    elif request.param in ("fused", "fused_fixed"):
         tune.setenv("MHC_SMALL_MAX_B", "0")
         tune.setenv("MHC_FUSED_N8", "1")
         if request.param == "fused_fixed":
@@ -118,6 +124,8 @@ def test_fused_named(name, route):
         pytest.skip("above 256 rows (n < 8) the default route is the fused kernel")
     if route == "fused_fixed" and synth.CONFIGS[name]["n"] == 8:
         pytest.skip("the fixed-slice layout is for n <= 4")
+    if route == "two_pass" and synth.CONFIGS[name]["n"] != 8:
+        pytest.skip("MHC_FUSED_N8 changes n = 8 only")
     _say(f"fused {name} route={route}")
     cfg = synth.CONFIGS[name]
     cur, nxt = _layers(cfg["n"], cfg["C"], cfg["B"], cfg["x_dist"], cfg["seed"])
@@ -134,11 +142,14 @@ def test_fused_named(name, route):
 
 
 FUSED_RAGGED = [(77, 4, 544), (1, 4, 32), (130, 8, 96), (33, 1, 64), (65, 2, 2080), (200, 4, 1056),
-                (17, 8, 32), (300, 4, 1536), (16, 2, 512), (5, 1, 1024)]
+                (17, 8, 32), (300, 4, 1536), (16, 2, 512), (5, 1, 1024), (300, 8, 160), (257, 8, 4096),
+                (1000, 8, 1056), (40, 8, 4224), (513, 8, 32)]
 
 
 @pytest.mark.parametrize("B,n,C", FUSED_RAGGED, ids=[f"B{b}n{n}C{c}" for b, n, c in FUSED_RAGGED])
 def test_fused_ragged(B, n, C, route):
+    if route == "two_pass" and n != 8:
+        pytest.skip("MHC_FUSED_N8 changes n = 8 only")
     _say(f"fused ragged B={B} n={n} C={C} route={route}")
     cur, nxt = _layers(n, C, B, "student_t4" if B % 2 else "normal", B * 13 + C)
     o, ref, f = _run(cur, nxt)
@@ -177,9 +188,11 @@ def test_fused_deterministic():
         assert torch.equal(a[k].view(torch.int8), b[k].view(torch.int8)), k
 
 
-def test_fused_guard_bands(route):
-    _say(f"fused guard bands route={route}")
-    B, n, C = 77, 4, 544
+@pytest.mark.parametrize("B,n,C", [(77, 4, 544), (300, 8, 160)], ids=["n4", "n8"])
+def test_fused_guard_bands(route, B, n, C):
+    if route == "two_pass" and n != 8:
+        pytest.skip("MHC_FUSED_N8 changes n = 8 only")
+    _say(f"fused guard bands B={B} n={n} C={C} route={route}")
     N = n * n + 2 * n
     cur, nxt = _layers(n, C, B, "normal", 11)
     o = mhc.alloc_outputs(B, n, C)

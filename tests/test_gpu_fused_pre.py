@@ -16,9 +16,10 @@ The next layer has its own phi and biases (a second seeded draw).
 
 Routes: "default" (up to 256 rows at n <= 4 with n*C <= 1024 the
 single-slice kernel of mhc_layer_small.hip; one pass above 256 rows for
-n <= 4 and at most sixteen 512-channel steps per row; the two calls
+n <= 4 and at most sixteen 512-channel steps per row, and at n = 8 for at
+most thirty-two 128-channel slices per row (mhc_onepass8.hip); the two calls
 otherwise) and "onepass", which lowers the small-B limit to 0 so that the
-one-pass kernel also runs every small shape it can take.
+one-pass kernels also run every small shape they can take.
 """
 
 import sys
@@ -47,14 +48,24 @@ def _gpu():
     yield
 
 
-@pytest.fixture(params=["default", "onepass"])
+# "pass8pre": the n = 8 pass in one pass (MHC_PASS8_PRE=1; n = 8 shapes only,
+# which by default run as the two calls).
+@pytest.fixture(params=["default", "onepass", "pass8pre"])
 def route(request, tune):
     tune.delenv("MHC_FUSED_PRE", raising=False)
+    tune.delenv("MHC_PASS8_PRE", raising=False)
     if request.param == "onepass":
         tune.setenv("MHC_SMALL_MAX_B", "0")
     else:
         tune.delenv("MHC_SMALL_MAX_B", raising=False)
+    if request.param == "pass8pre":
+        tune.setenv("MHC_PASS8_PRE", "1")
     return request.param
+
+
+def _only_pass8(route, n):
+    if route == "pass8pre" and n != 8:
+        pytest.skip("MHC_PASS8_PRE changes n = 8 only")
 
 
 def _f64(t):
@@ -149,6 +160,7 @@ def _rows(B):
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "large", "wide"])
 def test_named(name, route):
     cfg = synth.CONFIGS[name]
+    _only_pass8(route, cfg["n"])
     one = mhc.mhc_post_res_coeffs_pre_one_pass(cfg["B"], cfg["n"], cfg["C"])
     _say(f"post_res_coeffs_pre {name} route={route} one_pass={one}")
     if route == "onepass" and cfg["B"] > 256:
@@ -163,14 +175,17 @@ def test_named(name, route):
         _check(cur, nxt, o, ref, f, pre_own, rows, f"{name} rows {rows[0]}..{rows[-1]}")
 
 
-def test_giveup_word_is_reported():
+@pytest.mark.parametrize("n", [4, 8])
+def test_giveup_word_is_reported(n, tune):
     """mhc_post_res_coeffs_pre_check reports a set give-up word as
     MHC_ERR_INCOMPLETE, and the next call clears the word before its kernel
     runs.  The word (the last 16 bytes of the one-pass workspace) is set from
     the host after a complete call: no wait is made to give up."""
-    B, n, C = 1024, 4, 1024
+    B, C = 1024, 1024
+    if n == 8:
+        tune.setenv("MHC_PASS8_PRE", "1")
     assert mhc.mhc_post_res_coeffs_pre_one_pass(B, n, C)
-    _say("post_res_coeffs_pre give-up word")
+    _say(f"post_res_coeffs_pre give-up word n={n}")
     cur, nxt = _layers(n, C, B, "normal", 4242)
     o = mhc.alloc_outputs(B, n, C)
     _coeffs(cur, cur["X"], o)
@@ -193,22 +208,29 @@ def test_route_query(tune):
     assert mhc.mhc_post_res_coeffs_pre_one_pass(4096, 4, 4096)
     assert not mhc.mhc_post_res_coeffs_pre_one_pass(64, 4, 7168)      # small B
     assert mhc.mhc_post_res_coeffs_pre_one_pass(64, 4, 256)           # small B, one slice
-    assert not mhc.mhc_post_res_coeffs_pre_one_pass(8192, 8, 4096)    # n = 8
+    assert not mhc.mhc_post_res_coeffs_pre_one_pass(8192, 8, 4096)    # n = 8: two calls by default
+    tune.setenv("MHC_PASS8_PRE", "1")
+    assert mhc.mhc_post_res_coeffs_pre_one_pass(8192, 8, 4096)        # ... the n = 8 pass on request
+    assert not mhc.mhc_post_res_coeffs_pre_one_pass(8192, 8, 4224)    # n = 8, 33 slices per row
+    tune.delenv("MHC_PASS8_PRE")
     assert not mhc.mhc_post_res_coeffs_pre_one_pass(4096, 4, 8704)    # 17 steps per row
     tune.setenv("MHC_FUSED_PRE", "0")
     assert not mhc.mhc_post_res_coeffs_pre_one_pass(16384, 4, 7168)
 
 
 # (B, n, C): ragged row tiles, a ragged last 512-channel step (C % 512 != 0),
-# one to sixteen steps per row, n = 1, 2, 4; n = 8 and 17 steps take the
-# two-call route.
+# one to sixteen steps per row, n = 1, 2, 4; at n = 8 (the n = 8 pass) a
+# ragged last 128-channel slice and 1 to 32 slices per row; n = 8 above 32
+# slices and 17 steps take the two-call route.
 RAGGED = [(77, 4, 544), (1, 4, 32), (33, 1, 64), (65, 2, 2080), (200, 4, 1056), (300, 4, 1536),
           (16, 2, 512), (5, 1, 1024), (257, 4, 8192), (40, 4, 8192), (19, 4, 3104), (130, 8, 96),
-          (21, 4, 8704), (513, 2, 4096), (256, 4, 256), (250, 1, 992)]
+          (21, 4, 8704), (513, 2, 4096), (256, 4, 256), (250, 1, 992), (300, 8, 160), (257, 8, 4096),
+          (1000, 8, 1056), (40, 8, 4224), (513, 8, 32), (17, 8, 4096)]
 
 
 @pytest.mark.parametrize("B,n,C", RAGGED, ids=[f"B{b}n{n}C{c}" for b, n, c in RAGGED])
 def test_ragged(B, n, C, route):
+    _only_pass8(route, n)
     _say(f"post_res_coeffs_pre ragged B={B} n={n} C={C} route={route} "
          f"one_pass={mhc.mhc_post_res_coeffs_pre_one_pass(B, n, C)}")
     cur, nxt = _layers(n, C, B, "student_t4" if B % 2 else "normal", B * 31 + C)
@@ -231,8 +253,9 @@ def _rand_fill(ws):
 
 
 @pytest.mark.parametrize("fill", [_tag_fill, _rand_fill], ids=["tags", "random"])
-@pytest.mark.parametrize("B,n,C", [(300, 4, 1536), (600, 4, 7168), (1000, 2, 4096)])
+@pytest.mark.parametrize("B,n,C", [(300, 4, 1536), (600, 4, 7168), (1000, 2, 4096), (600, 8, 4096)])
 def test_workspace_contents(B, n, C, fill, route):
+    _only_pass8(route, n)
     _say(f"post_res_coeffs_pre workspace {fill.__name__} B={B} n={n} C={C} route={route}")
     cur, nxt = _layers(n, C, B, "normal", B + n + C)
     o, ref, f, pre_own = _run(cur, nxt, fill=fill)

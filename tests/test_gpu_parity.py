@@ -43,7 +43,10 @@ def _gpu():
 
 # mhc_coeffs has several implementations, and every one must meet the bar:
 #   default  whatever the call picks (above 256 rows: the persistent product
-#          for bf16 at n <= 4, the split-K product through LDS at n = 8);
+#          for bf16 at n <= 4; at n = 8 the product-only mode of the n = 8
+#          pass up to C = 4096 (C % 32 == 0), the split-K product through LDS
+#          otherwise);
+#   pass8  the n = 8 pass (MHC_GEMM_ALGO=3; n = 8 shapes only);
 #   lds    split-K product with X staged through LDS by direct-to-LDS loads,
 #          then the combine kernel (MHC_GEMM_ALGO=1);
 #   reg    the same with MFMA operands loaded straight from global memory
@@ -65,7 +68,12 @@ def _gpu():
 #   xreg   eight waves with X and phi through registers into single LDS slots
 #          (MHC_GEMM_XREG=2; n = 4 and 8, bf16).
 GEMM_ALGOS = ["default", "lds", "reg", "small", "persist", "lds128x5", "lds128x6", "lds8", "lds8k256",
-              "ldsmb2", "ldsk256", "xreg"]
+              "ldsmb2", "ldsk256", "xreg", "pass8"]
+
+
+def _only_n8(gemm_algo, n, C=0):
+    if gemm_algo == "pass8" and (n != 8 or C % 32):
+        pytest.skip("the n = 8 pass takes n = 8, C % 32 == 0")
 
 
 @pytest.fixture(params=GEMM_ALGOS)
@@ -81,6 +89,8 @@ def gemm_algo(request, tune):
             tune.setenv("MHC_GEMM_ALGO", "1")
         elif request.param == "persist":
             tune.setenv("MHC_GEMM_ALGO", "2")
+        elif request.param == "pass8":
+            tune.setenv("MHC_GEMM_ALGO", "3")
         if request.param.startswith("lds128x"):
             tune.setenv("MHC_GEMM_KC", 128)
             tune.setenv("MHC_GEMM_STAGES", int(request.param[-1]))
@@ -181,6 +191,7 @@ def sample_rows(B, k=64, seed=0):
 
 @pytest.mark.parametrize("name", ["tiny", "decode"])
 def test_parity_full(name, gemm_algo):
+    _only_n8(gemm_algo, synth.CONFIGS[name]["n"])
     _say(f"parity full {name} gemm={gemm_algo}")
     inp = synth.make_config(name, device="cuda")
     o = run_forward(inp)
@@ -192,6 +203,7 @@ def test_parity_full(name, gemm_algo):
 
 @pytest.mark.parametrize("name", ["prefill", "large", "wide"])
 def test_parity_every_row_and_properties(name, gemm_algo):
+    _only_n8(gemm_algo, synth.CONFIGS[name]["n"])
     _say(f"parity every row {name} gemm={gemm_algo}")
     inp = synth.make_config(name, device="cuda")
     o = run_forward(inp)
@@ -233,11 +245,13 @@ def test_parity_every_row_and_properties(name, gemm_algo):
 # ----------------------------------------------------------------------------
 
 RAGGED = [(77, 4, 264), (1, 4, 8), (130, 8, 72), (33, 1, 24), (65, 2, 40), (200, 4, 2056),
-          (3, 8, 8), (129, 2, 8), (1000, 1, 8), (64, 4, 64), (257, 4, 520)]
+          (3, 8, 8), (129, 2, 8), (1000, 1, 8), (64, 4, 64), (257, 4, 520), (300, 8, 160),
+          (257, 8, 4096), (1000, 8, 1056), (40, 8, 4224)]
 
 
 @pytest.mark.parametrize("B,n,C", RAGGED, ids=[f"B{b}n{n}C{c}" for b, n, c in RAGGED])
 def test_parity_ragged(B, n, C, gemm_algo):
+    _only_n8(gemm_algo, n, C)
     _say(f"parity ragged B={B} n={n} C={C} gemm={gemm_algo}")
     inp = synth.make_inputs(n, C, B, "student_t4" if B % 2 else "normal", seed=B * 31 + C,
                             device="cuda")
@@ -360,6 +374,7 @@ def test_small_path_any_workspace_contents(tune, fill):
 
 
 def test_split_k_invariance(tune, gemm_algo):
+    _only_n8(gemm_algo, synth.CONFIGS["decode"]["n"])
     _say(f"split-K invariance decode gemm={gemm_algo}")
     inp = synth.make_config("decode", device="cuda")
     ref = None
