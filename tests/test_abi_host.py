@@ -496,16 +496,17 @@ def test_tuning_keys_and_no_environment(tune, monkeypatch):
         monkeypatch.setenv(k, v)
     assert (one(16384, 4, 7168), ws(16384, 4, 7168), mhc.mhc_coeffs_split_k(16384, 4, 7168),
             mhc.mhc_coeffs_workspace_size(64, 4, 7168)) == base
-    # the n = 8 pass: one slice per 128 channels
+    # the n = 8 pass's product (MHC_GEMM_ALGO=3): one slice per 128 channels
+    tune.setenv("MHC_GEMM_ALGO", 3)
     assert mhc.mhc_coeffs_split_k(8192, 8, 4096) == 32
-    # the split-K product's slice count (MHC_GEMM_ALGO=1 forces it at n = 8)
+    # the split-K product's slice count (the default product at n = 8)
     tune.setenv("MHC_GEMM_ALGO", 1)
     s8 = mhc.mhc_coeffs_split_k(8192, 8, 4096)
     tune.setenv("MHC_SPLIT_K", 5)
     assert mhc.mhc_coeffs_split_k(8192, 8, 4096) == 5
     tune.delenv("MHC_GEMM_ALGO")
     assert mhc.mhc_coeffs_split_k(16384, 4, 7168) == base[2]   # the persistent product: one slice per 512 channels
-    assert mhc.mhc_coeffs_split_k(8192, 8, 4096) == 32         # ... and the n = 8 pass: one per 128
+    assert mhc.mhc_coeffs_split_k(8192, 8, 4096) == 5          # the default at n = 8: the split-K product
     tune.setenv("MHC_GEMM_ALGO", 1)
     tune.delenv("MHC_SPLIT_K")
     assert mhc.mhc_coeffs_split_k(8192, 8, 4096) == s8
@@ -521,10 +522,9 @@ def test_tuning_keys_and_no_environment(tune, monkeypatch):
 
 def test_every_documented_tuning_key(tune):
     """Each key the header documents is accepted, and the split-K shape keys
-    reach the plan: at n = 8 (C = 4096, B = 8192; the split-K product forced
-    over the n = 8 pass) four waves of one 16-row block make 64-row tiles and
-    two K-slices; eight waves, or X through registers, make 128-row tiles and
-    four."""
+    reach the plan: at n = 8 (C = 4096, B = 8192) four waves of one 16-row
+    block make 64-row tiles and two K-slices; eight waves, or X through
+    registers, make 128-row tiles and four."""
     hdr = open(os.path.join(ROOT, "include", "mhc.h")).read()
     doc = hdr[hdr.index("Testing and tuning."):]
     keys = sorted(set(re.findall(r"\bMHC_[A-Z0-9_]+\b", doc)) - {"MHC_H", "MHC_ERR_INVALID_ARG"})
@@ -532,8 +532,10 @@ def test_every_documented_tuning_key(tune):
     for k in keys:
         mhc.mhc_tuning_set(k, -1)
     split = mhc.mhc_coeffs_split_k
-    assert split(8192, 8, 4096) == 32     # the n = 8 pass
-    tune.setenv("MHC_GEMM_ALGO", 1)       # the split-K product
+    assert split(8192, 8, 4096) == 2      # the split-K product
+    tune.setenv("MHC_GEMM_ALGO", 3)       # the n = 8 pass's product
+    assert split(8192, 8, 4096) == 32
+    tune.setenv("MHC_GEMM_ALGO", 1)       # the split-K product, forced
     assert split(8192, 8, 4096) == 2
     tune.setenv("MHC_GEMM_WAVES", 8)
     assert split(8192, 8, 4096) == 4

@@ -43,10 +43,9 @@ def _gpu():
 
 # mhc_coeffs has several implementations, and every one must meet the bar:
 #   default  whatever the call picks (above 256 rows: the persistent product
-#          for bf16 at n <= 4; at n = 8 the product-only mode of the n = 8
-#          pass up to C = 4096 (C % 32 == 0), the split-K product through LDS
-#          otherwise);
-#   pass8  the n = 8 pass (MHC_GEMM_ALGO=3; n = 8 shapes only);
+#          for bf16 at n <= 4, the split-K product through LDS at n = 8);
+#   pass8  the product-only mode of the n = 8 pass (MHC_GEMM_ALGO=3; n = 8
+#          shapes only);
 #   lds    split-K product with X staged through LDS by direct-to-LDS loads,
 #          then the combine kernel (MHC_GEMM_ALGO=1);
 #   reg    the same with MFMA operands loaded straight from global memory
