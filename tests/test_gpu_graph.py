@@ -101,9 +101,21 @@ def _reset(inp, H0, bufs):
 
 
 @pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "e4m3"])
-@pytest.mark.parametrize("B,n,C", [(64, 4, 7168), (1024, 4, 4096), (600, 2, 2048), (64, 4, 256)],
-                         ids=["decode", "one-pass", "one-pass-n2", "single-slice"])
+@pytest.mark.parametrize("B,n,C", [(64, 4, 7168), (1024, 4, 4096), (600, 2, 2048), (64, 4, 256), (600, 8, 1024)],
+                         ids=["decode", "one-pass", "one-pass-n2", "single-slice", "n8"])
 def test_graph_replay_matches_eager(B, n, C, fp8):
+    _replay_check(B, n, C, fp8)
+
+
+def test_graph_replay_n8_one_pass(tune):
+    """The n = 8 pass with the record hand-off (MHC_PASS8_PRE=1): a zero-fill
+    kernel and the pass, replayed."""
+    tune.setenv("MHC_PASS8_PRE", "1")
+    assert mhc.mhc_post_res_coeffs_pre_one_pass(600, 8, 1024)
+    _replay_check(600, 8, 1024, False)
+
+
+def _replay_check(B, n, C, fp8):
     route = (mhc.mhc_post_res_coeffs_pre_fp8_one_pass if fp8 else mhc.mhc_post_res_coeffs_pre_one_pass)(B, n, C)
     _say(f"graph replay B={B} n={n} C={C} fp8={fp8} one_pass={route}")
     inp, H0, bufs, call = _setup(n, C, B, fp8)

@@ -58,8 +58,9 @@ def _args(cur, nxt, H, o):
 
 
 # (B, n, C): one-pass route at a prefill-like size, then a smaller one-pass
-# shape with a ragged row tile, then a shape that takes the two calls.
-SHAPES = [(4096, 4, 4096), (333, 4, 1024), (200, 4, 512)]
+# shape with a ragged row tile, then a shape that takes the two calls, then
+# n = 8 (the n = 8 pass and mhc_pre) with a ragged last slice.
+SHAPES = [(4096, 4, 4096), (333, 4, 1024), (200, 4, 512), (300, 8, 160)]
 
 
 def test_noalloc_matches_caller_workspace():
