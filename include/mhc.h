@@ -163,7 +163,10 @@ int mhc_post_res(int64_t B, int32_t n, int64_t C, const void *X_t,
  * (X_t, F_out, H, X_next) and mhc_coeffs (phi_next, alpha_*, b_*, logits_next,
  * r_next, H_next, workspace).  Additionally requires C % 32 == 0
  * (else MHC_ERR_UNSUPPORTED); the workspace must hold
- * mhc_post_res_coeffs_workspace_size(B, n, C) bytes. */
+ * mhc_post_res_coeffs_workspace_size(B, n, C) bytes.  At n = 8 (B above
+ * 256, C <= 4096) the pass splits each row into C/128 slices of 128 channels
+ * of all eight streams, so the workspace holds fp32 partials [C/128, B, 81]
+ * (85 MB at B = 8192, C = 4096). */
 size_t mhc_post_res_coeffs_workspace_size(int64_t B, int32_t n, int64_t C);
 
 int mhc_post_res_coeffs(int64_t B, int32_t n, int64_t C,
@@ -209,7 +212,8 @@ int mhc_post_res_coeffs(int64_t B, int32_t n, int64_t C,
  * another and the workspace is not touched (its size is still required), and
  * mhc_post_res_coeffs_pre_one_pass() reports 1 for these shapes too.  Other
  * shapes run mhc_post_res_coeffs followed by mhc_pre on X_next, with the same
- * results.
+ * results; at n = 8 that is the default (a one pass at n = 8 exists, for
+ * C <= 4096, behind the MHC_PASS8_PRE tuning key below: measured slower).
  *
  * Arguments as mhc_post_res_coeffs, plus F_pre_next (16-byte aligned, must
  * not overlap any other argument).  The workspace must hold
