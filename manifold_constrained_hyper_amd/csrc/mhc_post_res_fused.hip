@@ -479,9 +479,12 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
       }
     }
     // The row's own buffer; a row without a target (past B, or before the
-    // first step) gets an empty one, so the store is dropped.  Stores use
-    // the default cache policy: measured 412-417 against 439-442 us per call
-    // with the non-temporal bit (bf16, n=4, C=7168, B=16384).
+    // first step) gets an empty one, so the store is dropped.  Cache policy
+    // by mode, as measured at n=4, C=7168, B=16384: after the apply the
+    // default one (412-417 against 439-442 us per call with the streaming
+    // bit); in the product-only modes (the first layer) the streaming one
+    // (217.5-218.2 against 223.8-225.1 us in bf16; E4M3 unchanged).
+    constexpr int kFpreAux = IO::APPLY ? 0 : 2;
     const bool tgt = real && row < B;  // wave-uniform
     const __amdgpu_buffer_rsrc_t frow = __builtin_amdgcn_make_buffer_rsrc(
         static_cast<uint8_t *>(pa.F_pre) + (size_t)min(row, B - 1) * C * IO::EB, (short)0,
@@ -489,13 +492,13 @@ __global__ __launch_bounds__(1024) void post_res_next_kernel(
     if constexpr (IO::FP8) {
       u32x2 o{pack_fp8x4(a[0], a[1], a[2], a[3]), pack_fp8x4(a[4], a[5], a[6], a[7])};
       if (poison) o = u32x2{0x7f7f7f7fu, 0x7f7f7f7fu};  // E4M3 NaN
-      __builtin_amdgcn_raw_buffer_store_b64(o, frow, (uint32_t)cst, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(o, frow, (uint32_t)cst, 0, kFpreAux);
     } else {
       u32x4 o;
 #pragma unroll
       for (int w = 0; w < 4; ++w) o[w] = pack_bf16x2(a[2 * w], a[2 * w + 1]);
       if (poison) o = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
-      __builtin_amdgcn_raw_buffer_store_b128(o, frow, (uint32_t)cst * 2u, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(o, frow, (uint32_t)cst * 2u, 0, kFpreAux);
     }
   };
 
