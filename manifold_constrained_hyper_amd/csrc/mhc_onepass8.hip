@@ -14,14 +14,14 @@
 // slice's phi block in registers.  At n = 8 that block is 4096 k x 80
 // columns (640 KiB), more than a CU's registers; streaming it from L2 for
 // every 16-row tile moves five times the X bytes.  Here a slice is 128
-// channels of all 8 streams: 1024 k, a phi block of 160 KiB, 40-44 VGPRs per
+// channels of all 8 streams: 1024 k, a phi block of 160 KiB, 44 VGPRs per
 // lane over 15 waves, gathered once per run and kept for every row tile the
 // workgroup visits (the fixed-slice layout).
 //
 // Work decomposition.  S = ceil(C / 128) slices per row (at most 32);
-// a persistent grid of G workgroups (G a multiple of S, all resident: the
-// host sizes G from the occupancy the runtime reports and the stream's CUs)
-// of 16 waves each.  Workgroup p (dealt so that each XCD takes a contiguous
+// a persistent grid of G workgroups of 16 waves each, G a multiple of S
+// (with the hand-off below all resident at once: the host sizes G from the
+// occupancy the runtime reports and the stream's CUs).  Workgroup p (dealt so that each XCD takes a contiguous
 // run of p, i.e. whole row tiles) keeps slice p mod S and visits row tiles
 // p / S, p / S + G/S, ...  A step is one 16-row tile of its slice:
 //   apply    wave w owns tile row w; lane l owns channels c0 + 2l, c0 + 2l + 1
@@ -37,11 +37,15 @@
 //            v_mfma_f32_16x16x32_bf16; the column-block-0 wave of each group
 //            also forms the Gram block A A^T of its k-steps, whose diagonal
 //            is the rows' sum of squares over them;
-//   flush    at the start of the next step the three k-group sums of each
-//            (row, column) are added in k-group order (deterministic) and
-//            stored as the slice's partials fp32 [S, B, 81]; the combine
+//   flush    in the next step, after its apply, the three k-group sums of
+//            each (row, column) are added in k-group order (deterministic)
+//            and stored as the slice's partials fp32 [S, B, 81]; the combine
 //            kernel (coeff_sinkhorn_kernel, 32-slot tree order) turns them
 //            into the next layer's logits, r and H.
+// Each wave keeps the loads of the next two steps in flight (two register
+// sets; one with the hand-off, whose records and gates leave no room for a
+// second beside phi), and the step applies first so that the refill of its
+// set is issued early.  Three LDS tiles: a step's rows stay until step t+3.
 // Pre-mix (PRE): the flush also publishes, per (row, slice), the 8 pre
 // logits and the sum of squares as 4-byte records [B][9][S] (zero until
 // written, never zero when written: +0.0 is stored as -0.0; buffer stores
@@ -57,7 +61,11 @@
 // and sets the give-up word (mhc_post_res_coeffs_pre_check reads it).
 //
 // Without APPLY the tile takes X itself (the first layer: mhc_coeffs_pre and
-// mhc_coeffs at n = 8); without PRE no records and no F_pre.
+// mhc_coeffs at n = 8); without PRE no records and no F_pre.  Routes: the
+// apply without the hand-off is mhc_post_res_coeffs at n = 8 (C <= 4096);
+// the hand-off (one pass for mhc_post_res_coeffs_pre / mhc_coeffs_pre) and
+// the product alone run only on request (MHC_PASS8_PRE, MHC_GEMM_ALGO=3):
+// measured slower than the calls they replace at n=8, C=4096, B=8192.
 #include "mhc_device.h"
 #include "mhc_finish.h"
 #include "mhc_launch.h"
