@@ -259,7 +259,12 @@ int mhc_post_res_coeffs_pre_check(int64_t B, int32_t n, int64_t C, int32_t fp8,
  * B = 16384 needs about 28.4 MB), one per GPU the library runs on, held until
  * the process ends.  Shapes whose workspace (as
  * mhc_post_res_coeffs_pre_workspace_size reports it) exceeds that return
- * MHC_ERR_WORKSPACE before anything is launched.  The call allocates nothing:
+ * MHC_ERR_WORKSPACE before anything is launched, except at n = 8: where the
+ * n = 8 pass's partials would not fit (C/128 slices x B x 81 fp32, above
+ * B = 3236 at C = 4096) the call takes the apply and split-K product route,
+ * whose workspace does, so the coefficients may differ from the workspace
+ * call's in fp32 summation order (X_next and F_pre_next bitwise as always
+ * against mhc_post_res and mhc_pre).  The call allocates nothing:
  * the first call on a device looks up the array's device address once.
  * Every call on a GPU shares that GPU's array, so calls that overlap in time
  * on one GPU (on different streams, or from different threads) race and must

@@ -51,6 +51,9 @@ int from_hip(hipError_t e) { return e == hipSuccess ? MHC_OK : MHC_ERR_HIP; }
 struct Elt {
   bool fp8;
   bool phi32;
+  // The workspace is the array of mhc_post_res_coeffs_pre_noalloc: routes
+  // whose workspace would not fit it give way to ones that do.
+  bool capped = false;
   size_t bytes() const { return fp8 ? 1 : 2; }
   size_t phi_bytes() const { return phi32 ? 4 : 2; }
 };
@@ -233,7 +236,9 @@ FusedRoute fused_route(int64_t B, int32_t n, int64_t C, Elt e) {
   if (e.phi32) return FusedRoute::kTwoPass;  // the fused kernel takes bf16 phi only
   if (n == 8) {
     const int64_t v = mhc::tune(mhc::kTuneFusedN8);
-    if (v < 0 && !e.fp8 && mhc::onepass8_fits(B, C)) return FusedRoute::kPass8;
+    if (v < 0 && !e.fp8 && mhc::onepass8_fits(B, C) &&
+        !(e.capped && mhc::plan_onepass8(B, C, false).total_bytes > (size_t)MHC_NOALLOC_SCRATCH_BYTES))
+      return FusedRoute::kPass8;
     if (v <= 0) return FusedRoute::kTwoPass;
   }
   if (e.fp8) {
@@ -511,6 +516,7 @@ int read_giveup(int64_t B, int32_t n, int64_t C, Elt e, const void *workspace, v
 }
 
 constexpr Elt kBf16{false, false}, kFp8{true, false}, kPhi32{false, true};
+constexpr Elt kBf16Capped{false, false, true};  // bf16 in the no-alloc array
 
 // Route and launch-shape overrides (mhc_tuning_set): -1 = unset.
 std::atomic<int64_t> g_tune[mhc::kTuneCount] = {};
@@ -694,7 +700,7 @@ int mhc_post_res_coeffs_pre(int64_t B, int32_t n, int64_t C, const void *X_t, co
 
 int mhc_post_res_coeffs_pre_check(int64_t B, int32_t n, int64_t C, int32_t fp8,
                                   const void *workspace, size_t workspace_bytes, void *stream) {
-  const Elt e = fp8 ? kFp8 : kBf16;
+  const Elt e = fp8 ? kFp8 : (workspace ? kBf16 : kBf16Capped);
   const int st = check_shape_elt(B, n, C, e);
   if (st != MHC_OK) return st;
   if (C % 32 != 0) return MHC_ERR_UNSUPPORTED;
@@ -733,11 +739,11 @@ int mhc_post_res_coeffs_pre_noalloc(int64_t B, int32_t n, int64_t C, const void 
   if (st != MHC_OK) return st;
   if (C % 32 != 0) return MHC_ERR_UNSUPPORTED;
   if (B == 0) return MHC_OK;
-  if (post_res_coeffs_pre_ws_bytes(B, n, C, kBf16) > kNoAllocScratchBytes) return MHC_ERR_WORKSPACE;
+  if (post_res_coeffs_pre_ws_bytes(B, n, C, kBf16Capped) > kNoAllocScratchBytes) return MHC_ERR_WORKSPACE;
   void *ws = nullptr;
   st = noalloc_scratch(&ws);
   if (st != MHC_OK) return st;
-  return post_res_coeffs_impl(kBf16, B, n, C, X_t, F_out, H, X_next, phi_next, alpha_pre,
+  return post_res_coeffs_impl(kBf16Capped, B, n, C, X_t, F_out, H, X_next, phi_next, alpha_pre,
                               alpha_post, alpha_res, b_pre, b_post, b_res, logits_next, r_next,
                               H_next, ws, kNoAllocScratchBytes, stream, true, F_pre_next);
 }

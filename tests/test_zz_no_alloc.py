@@ -80,6 +80,27 @@ def test_noalloc_matches_caller_workspace():
         assert mhc.mhc_post_res_coeffs_pre_check(B, n, C, ws) == mhc.MHC_OK
 
 
+def test_noalloc_n8_beyond_the_array(tune):
+    """At n = 8 the n = 8 pass's partials outgrow the array above B = 3236
+    (C = 4096): the call then runs the apply and split-K product route, the
+    workspace call's route with MHC_FUSED_N8=0 (bitwise the same results)."""
+    B, n, C = 4096, 8, 4096
+    assert mhc.mhc_post_res_coeffs_pre_workspace_size(B, n, C) > mhc.MHC_NOALLOC_SCRATCH_BYTES
+    _say(f"no-alloc call beyond the array: B={B} n={n} C={C}")
+    cur, nxt, H = _layer(B, n, C, seed=777)
+    ref, got = _outputs(B, n, C), _outputs(B, n, C)
+    mhc.mhc_post_res_coeffs_pre_noalloc(B, n, C, *_args(cur, nxt, H, got))
+    assert mhc.mhc_post_res_coeffs_pre_check(B, n, C, None) == mhc.MHC_OK
+    tune.setenv("MHC_FUSED_N8", "0")
+    ws = torch.empty(mhc.mhc_post_res_coeffs_pre_workspace_size(B, n, C), dtype=torch.uint8, device="cuda")
+    mhc.mhc_post_res_coeffs_pre(B, n, C, *_args(cur, nxt, H, ref), ws)
+    torch.cuda.synchronize()
+    for name in ("X_next", "logits", "r", "H", "F_pre"):
+        assert torch.equal(got[name].view(torch.int16 if got[name].dtype == torch.bfloat16 else torch.int32),
+                           ref[name].view(torch.int16 if ref[name].dtype == torch.bfloat16 else torch.int32)), \
+            f"{name} differs from the split-K route's workspace call"
+
+
 def test_noalloc_rejects_oversized_shape():
     B, n, C = 65536, 4, 7168
     assert mhc.mhc_post_res_coeffs_pre_workspace_size(B, n, C) > mhc.MHC_NOALLOC_SCRATCH_BYTES
